@@ -1,0 +1,38 @@
+"""Plain, slow CPU oracle for the fused W4 dequantize-and-multiply GEMV.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import or call anything in this package.  The product library never
+imports it, and this package never imports the product library: the two share no code.
+
+What it computes (all in numpy fp64 unless a storage format fixes the precision):
+
+* ``nf4_codebook``   -- the 16 NormalFloat code points.  The pages fix only that there are 16
+  unevenly spaced codes for normally distributed weights, stored fp32 (LLM Quantization on RTX 4060,
+  sections "Standard Expectation from Quantization" and "Kernel Implementation"); the values come
+  from the standard NormalFloat construction, written out in ``nf4.py``.
+* ``quantize_nf4``   -- blockwise absmax NF4, block 64 along K, one fp32 absmax per block, two
+  nibbles per byte with element 2i in the high nibble (same page, same sections).
+* ``quantize_int4``  -- symmetric INT4 with a +8 zero point (My Triton Kernel Ties bitsandbytes,
+  section "The kernels", first bug), one bf16 scale per 128-column group, round half to even
+  (LLM Compressor 0.14, section "Details worth knowing").
+* ``dequant_*``      -- the decoded weights, exact in fp64.
+* ``gemv_reference`` -- y = x . W_hat^T and T = |x| . |W_hat|^T in fp64: the fused kernel only moves
+  where dequantization happens (LLM Quantization on RTX 4060, section "Kernel Implementation"), so
+  its result is this plain definition.
+* ``accept``         -- the per-element bound |y - y_ref| <= 2e-3 T + 1e-5.
+
+Pins: every function is checked against facts fixed by the pages or by mathematics in the
+``-m "not gpu"`` tests (``tests/test_oracle_*.py``).  No function here is "parity unpinned".
+"""
+from .bits import bf16_bits_to_f64, f16_bits_to_f64, f32_to_bf16_rne_bits, x_bits_to_f64
+from .nf4 import NF4_BLOCK, dequant_nf4, nf4_codebook, nf4_midpoints, quantize_nf4
+from .int4 import INT4_GROUP, dequant_int4, quantize_int4
+from .gemv import accept, dequant, gemv_reference, unpack_nibbles, violation_ratio
+
+__all__ = [
+    "NF4_BLOCK", "INT4_GROUP",
+    "nf4_codebook", "nf4_midpoints", "quantize_nf4", "dequant_nf4",
+    "quantize_int4", "dequant_int4",
+    "unpack_nibbles", "dequant", "gemv_reference", "accept", "violation_ratio",
+    "f16_bits_to_f64", "bf16_bits_to_f64", "x_bits_to_f64", "f32_to_bf16_rne_bits",
+]
