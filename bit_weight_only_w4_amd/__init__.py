@@ -1,0 +1,227 @@
+"""Python binding of the W4 C ABI (include/w4.h).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libw4.so``.  PyTorch supplies device memory and the current stream.  There is no fallback:
+if the library is not built, every call raises ``RuntimeError``.
+
+Formats are named ``"nf4_f16"``, ``"nf4_bf16"``, ``"int4_f16"`` and ``"int4_bf16"`` (weight format
+x activation dtype).  Scales are fp32 ``[N, K/64]`` for NF4 and bf16 bit patterns stored in an
+int16 tensor ``[N, K/128]`` for INT4.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4.so")
+
+FORMATS = {"nf4_f16": 1, "nf4_bf16": 2, "int4_f16": 3, "int4_bf16": 4}
+PATHS = {"auto": 0, "gemv": 1, "splitk": 2, "mfma": 3, "twopass": 4}
+PATH_NAMES = {v: k for k, v in PATHS.items()}
+STATUS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "FORMAT", -5: "NONFINITE",
+          -6: "WORKSPACE", -7: "PATH", -8: "HIP", -9: "ALIAS"}
+MAX_BATCH = 256
+MAX_SPLIT_K = 64
+
+_lib = None
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class W4ValueError(W4Error, ValueError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libw4.so``; raises RuntimeError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"W4 HIP library not built ({LIB_PATH} missing); run "
+                "`python -m bit_weight_only_w4_amd.build` on a machine with ROCm")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.w4_quantize_nf4.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.w4_quantize_int4.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.w4_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
+        L.w4_gemm_smallbatch.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
+        L.w4_matmul_ex.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, ci, ci, vp, sz, vp]
+        L.w4_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ci]
+        L.w4_workspace_bytes.restype = sz
+        L.w4_auto_path.argtypes = [ci, i64, i64, i64, sz, ctypes.POINTER(ci)]
+        ip = ctypes.POINTER(ci)
+        L.w4_gemv_plan.argtypes = [ci, i64, i64, i64, ci, ip, ip, ip, ip]
+        L.w4_nf4_codebook.restype = ctypes.POINTER(ctypes.c_float)
+        L.w4_status_string.argtypes = [ci]
+        L.w4_status_string.restype = ctypes.c_char_p
+        L.w4_probe_read.argtypes = [vp, sz, vp, vp]
+        L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
+        for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_gemv", "w4_gemm_smallbatch",
+                     "w4_matmul_ex", "w4_auto_path", "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy"):
+            getattr(L, name).restype = ci
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().w4_status_string(int(status)).decode()
+
+
+def check(status: int, what: str = "w4") -> None:
+    if status == 0:
+        return
+    msg = f"{what}: {STATUS.get(status, status)} ({status_string(status)})"
+    if status == -8:
+        raise W4Error(status, msg)
+    raise W4ValueError(status, msg)
+
+
+def nf4_codebook():
+    """The 16 fp32 NF4 code points the kernels decode with (host copy from the library)."""
+    p = lib().w4_nf4_codebook()
+    return [p[i] for i in range(16)]
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, int):
+        return fmt
+    try:
+        return FORMATS[fmt]
+    except KeyError:
+        raise ValueError(f"unknown format {fmt!r}; expected one of {sorted(FORMATS)}") from None
+
+
+def _stream(stream=None) -> int:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def quantize_nf4(w, stream=None):
+    """fp32 [N, K] device weights -> (packed uint8 [N, K/2], absmax fp32 [N, K/64])."""
+    import torch
+
+    _need_cuda(w)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    absmax = torch.empty((n, max(k // 64, 1)), dtype=torch.float32, device=w.device)
+    check(lib().w4_quantize_nf4(_ptr(w), n, k, _ptr(packed), _ptr(absmax), _stream(stream)),
+          "w4_quantize_nf4")
+    return packed, absmax
+
+
+def quantize_int4(w, stream=None):
+    """fp32 [N, K] device weights -> (packed uint8 [N, K/2], bf16 scale bits int16 [N, K/128])."""
+    import torch
+
+    _need_cuda(w)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n, max(k // 128, 1)), dtype=torch.int16, device=w.device)
+    check(lib().w4_quantize_int4(_ptr(w), n, k, _ptr(packed), _ptr(scale), _stream(stream)),
+          "w4_quantize_int4")
+    return packed, scale
+
+
+def _mm_shapes(x, packed):
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    b, k = x.shape
+    n = packed.shape[0]
+    return x, n, k, b
+
+
+def gemv(x, packed, scales, fmt, y=None, stream=None):
+    """y[B, N] = x[B, K] . W_hat^T via the fused single-pass GEMV (B <= 8)."""
+    import torch
+
+    x, n, k, b = _mm_shapes(x, packed)
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _need_cuda(x, packed, scales, y)
+    check(lib().w4_gemv(_ptr(x), _ptr(packed), _ptr(scales), _fmt(fmt), n, k, b, _ptr(y),
+                        _stream(stream)), "w4_gemv")
+    return y
+
+
+def gemm_smallbatch(x, packed, scales, fmt, y=None, stream=None):
+    """y[B, N] = x[B, K] . W_hat^T for B <= 256, GEMV or MFMA path chosen by the library."""
+    import torch
+
+    x, n, k, b = _mm_shapes(x, packed)
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _need_cuda(x, packed, scales, y)
+    check(lib().w4_gemm_smallbatch(_ptr(x), _ptr(packed), _ptr(scales), _fmt(fmt), n, k, b,
+                                   _ptr(y), _stream(stream)), "w4_gemm_smallbatch")
+    return y
+
+
+def workspace_bytes(fmt, n, k, b, path="auto", split_k=0) -> int:
+    return int(lib().w4_workspace_bytes(_fmt(fmt), n, k, b, PATHS[path], split_k))
+
+
+def auto_path(fmt, n, k, b, workspace_bytes=0):
+    """(path name, split count) that the automatic choice would run."""
+    sk = ctypes.c_int(0)
+    r = lib().w4_auto_path(_fmt(fmt), n, k, b, workspace_bytes, ctypes.byref(sk))
+    if r < 0:
+        check(r, "w4_auto_path")
+    return PATH_NAMES[r], sk.value
+
+
+def gemv_plan(fmt, n, k, b, split_k=1):
+    """dict(team, iters, chunks_per_split, grid_x) of the fused GEMV launch for these arguments."""
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    r = lib().w4_gemv_plan(_fmt(fmt), n, k, b, split_k, *[ctypes.byref(v) for v in vals])
+    check(r, "w4_gemv_plan")
+    return dict(zip(("team", "iters", "chunks_per_split", "grid_x"), (v.value for v in vals)))
+
+
+def matmul_ex(x, packed, scales, fmt, path="auto", split_k=0, workspace=None, y=None,
+              stream=None):
+    """The same product with an explicit path, split count and workspace (a uint8 tensor)."""
+    import torch
+
+    x, n, k, b = _mm_shapes(x, packed)
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _need_cuda(x, packed, scales, y, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().w4_matmul_ex(_ptr(x), _ptr(packed), _ptr(scales), _fmt(fmt), n, k, b, _ptr(y),
+                             PATHS[path], int(split_k), _ptr(workspace), wbytes, _stream(stream)),
+          f"w4_matmul_ex[{path}]")
+    return y
+
+
+def probe_read(src, sink, stream=None):
+    _need_cuda(src, sink)
+    check(lib().w4_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                              _stream(stream)), "w4_probe_read")
+
+
+def probe_copy(src, dst, stream=None):
+    _need_cuda(src, dst)
+    check(lib().w4_probe_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                              _stream(stream)), "w4_probe_copy")

@@ -1,0 +1,358 @@
+// C ABI of the W4 library: host-side validation, path and launch-shape selection, dispatch.
+// Every check runs before any launch; nothing here allocates device memory or synchronizes a
+// stream except the quantizers (which read back the device-side non-finite flag).
+#include <string.h>
+
+#include <algorithm>
+
+#include "w4_common.h"
+
+namespace w4 {
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      cus = 256;
+    }
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+namespace {
+
+struct CodebookInit {
+  float v[16];
+  CodebookInit() {
+    const uint32_t bits[16] = W4_NF4_CODE_BITS;
+    memcpy(v, bits, sizeof(v));
+  }
+};
+const CodebookInit g_codebook;
+
+bool valid_fmt(int fmt) {
+  return fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_BF16 || fmt == W4_INT4_X_F16 ||
+         fmt == W4_INT4_X_BF16;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+// Common matmul validation; returns W4_OK or the first failing check.
+int validate(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+             int64_t k, int64_t b, const float* y) {
+  if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
+  if (!x || !packed || !scales || !y) return W4_ERR_NULL;
+  const int64_t g = fmt_group(fmt);
+  if (n < 1 || k < g || k % g != 0 || b < 1 || b > W4_MAX_BATCH || n >= kMaxDim || k >= kMaxDim)
+    return W4_ERR_SHAPE;
+  if (n > ((int64_t)1 << 62) / k) return W4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 4)) return W4_ERR_ALIGN;
+  if (!aligned(scales, fmt_weight(fmt) == kNF4 ? 4 : 2)) return W4_ERR_ALIGN;
+  const size_t ybytes = (size_t)(b * n) * 4;
+  const size_t sbytes = (size_t)(n * (k / g)) * (fmt_weight(fmt) == kNF4 ? 4 : 2);
+  if (overlaps(y, ybytes, x, (size_t)(b * k) * 2) || overlaps(y, ybytes, packed, (size_t)(n * k / 2)) ||
+      overlaps(y, ybytes, scales, sbytes))
+    return W4_ERR_ALIAS;
+  return W4_OK;
+}
+
+// Launch shape of the fused GEMV for (K, B) over `splits` K ranges.  Chooses the team width
+// (lanes per row) with the least idle lanes among those whose per-lane chunk count fits the
+// register budget of batch b; a team wider than one wave costs an LDS exchange per row, so it
+// is taken only when it saves idle lanes.
+bool plan_gemv(int64_t n, int64_t k, int b, int splits, GemvPlan* out) {
+  const int cpr = (int)(k / 32);
+  if (splits < 1 || splits > cpr) return false;
+  const int cps = (cpr + splits - 1) / splits;
+  if ((int64_t)(splits - 1) * cps >= cpr) return false;  // every split must own a chunk
+  const int itmax = gemv_max_iters(b);
+  double best = 1e9;
+  GemvPlan p{};
+  for (int team = 16; team <= kGemvThreads; team *= 2) {
+    const int it = (cps + team - 1) / team;
+    if (it > itmax) continue;
+    const double waste = (double)(team * it - cps) / (double)(team * it);
+    const double cost = waste + (team > 64 ? 0.05 : 0.0) + (it > 5 ? 0.01 * (it - 5) : 0.0);
+    if (cost < best) {
+      best = cost;
+      p.team = team;
+      p.iters = it;
+    }
+  }
+  if (best > 1e8) return false;
+  p.splits = splits;
+  p.cps = cps;
+  const int64_t rows_per_wg = kGemvThreads / p.team;
+  const int64_t nrb = (n + rows_per_wg - 1) / rows_per_wg;
+  // Two 64 KiB decode tables fit in one CU's LDS; more resident workgroups than that would only
+  // queue, so the grid is capped at two per CU and each workgroup loops over row blocks.
+  const int64_t cap = std::max<int64_t>(1, 2 * (int64_t)device_cu_count() / splits);
+  p.grid_x = (int)std::min<int64_t>(nrb, cap);
+  *out = p;
+  return true;
+}
+
+// Split count the automatic path uses: split only when one pass would leave CUs idle.
+int auto_splits(int64_t n, int64_t k, int b) {
+  GemvPlan p;
+  if (!plan_gemv(n, k, b, 1, &p)) return 1;
+  const int64_t rows_per_wg = kGemvThreads / p.team;
+  const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
+  const int64_t target = 2 * (int64_t)device_cu_count();
+  if (wgs >= target) return 1;
+  int s = 1;
+  while (s < W4_MAX_SPLIT_K && wgs * s * 2 <= target * 2 && (k / 32) / (s * 2) >= 32) s *= 2;
+  return s;
+}
+
+size_t splitk_bytes(int64_t n, int64_t b, int s) { return (size_t)s * (size_t)b * (size_t)n * 4; }
+
+int run_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+             int64_t k, int64_t b, float* y, int splits, void* ws, hipStream_t st) {
+  GemvPlan p;
+  if (b > kMaxGemvBatch || !plan_gemv(n, k, (int)b, splits, &p)) return W4_ERR_PATH;
+  GemvArgs a;
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.packed = packed;
+  a.scales = scales;
+  a.out = splits == 1 ? y : reinterpret_cast<float*>(ws);
+  a.n = n;
+  a.k = k;
+  a.cpr = (int)(k / 32);
+  a.cps = p.cps;
+  a.team = p.team;
+  a.iters = p.iters;
+  if (launch_gemv(fmt, (int)b, a, p, st) != hipSuccess) return W4_ERR_HIP;
+  if (splits > 1) {
+    if (launch_splitk_reduce(reinterpret_cast<const float*>(ws), y, b * n, splits, st) != hipSuccess)
+      return W4_ERR_HIP;
+  }
+  return W4_OK;
+}
+
+int run_twopass(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+                int64_t k, int64_t b, float* y, void* ws, hipStream_t st) {
+  uint16_t* w_hat = reinterpret_cast<uint16_t*>(ws);
+  if (launch_dequant_f16(fmt, packed, scales, n, k, w_hat, st) != hipSuccess) return W4_ERR_HIP;
+  if (launch_dense_gemv(fmt, reinterpret_cast<const uint16_t*>(x), w_hat, n, k, b, y, st) !=
+      hipSuccess)
+    return W4_ERR_HIP;
+  return W4_OK;
+}
+
+int run_mfma(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+             int64_t k, int64_t b, float* y, hipStream_t st) {
+  const hipError_t e = launch_mfma(fmt, reinterpret_cast<const uint16_t*>(x), packed, scales, n, k,
+                                   b, y, st);
+  if (e == hipErrorNotSupported) return W4_ERR_PATH;
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+// Batch size from which the automatic path prefers the MFMA kernel.
+constexpr int64_t kMfmaFromBatch = 9;
+
+}  // namespace
+}  // namespace w4
+
+using namespace w4;
+
+extern "C" {
+
+int w4_version(void) { return 1; }
+
+const float* w4_nf4_codebook(void) { return g_codebook.v; }
+
+const char* w4_status_string(int status) {
+  switch (status) {
+    case W4_OK: return "ok";
+    case W4_ERR_NULL: return "null pointer argument";
+    case W4_ERR_SHAPE: return "invalid shape (N, K, B) for this format";
+    case W4_ERR_ALIGN: return "misaligned pointer";
+    case W4_ERR_FORMAT: return "unknown weight/activation format";
+    case W4_ERR_NONFINITE: return "non-finite weight passed to quantize";
+    case W4_ERR_WORKSPACE: return "workspace missing or too small";
+    case W4_ERR_PATH: return "path not available for these arguments";
+    case W4_ERR_HIP: return "HIP runtime error";
+    case W4_ERR_ALIAS: return "output overlaps an input or the workspace";
+  }
+  return "unknown status";
+}
+
+int w4_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* packed, float* absmax,
+                    void* stream) {
+  if (!w || !packed || !absmax) return W4_ERR_NULL;
+  if (n < 1 || k < 64 || k % 64 != 0 || n >= kMaxDim || k >= kMaxDim) return W4_ERR_SHAPE;
+  if (!aligned(w, 8) || !aligned(packed, 16) || !aligned(absmax, 4)) return W4_ERR_ALIGN;
+  if (overlaps(w, (size_t)(n * k) * 4, packed, (size_t)(n * k / 2)) ||
+      overlaps(w, (size_t)(n * k) * 4, absmax, (size_t)(n * k / 64) * 4) ||
+      overlaps(packed, (size_t)(n * k / 2), absmax, (size_t)(n * k / 64) * 4))
+    return W4_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
+  if (launch_quantize_nf4(w, n, k, packed, absmax, s) != hipSuccess) return W4_ERR_HIP;
+  int flag = 0;
+  if (quantize_error_read(&flag, s) != hipSuccess) return W4_ERR_HIP;
+  return flag ? W4_ERR_NONFINITE : W4_OK;
+}
+
+int w4_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* packed, uint16_t* scale,
+                     void* stream) {
+  if (!w || !packed || !scale) return W4_ERR_NULL;
+  if (n < 1 || k < 128 || k % 128 != 0 || n >= kMaxDim || k >= kMaxDim) return W4_ERR_SHAPE;
+  if (!aligned(w, 8) || !aligned(packed, 16) || !aligned(scale, 2)) return W4_ERR_ALIGN;
+  if (overlaps(w, (size_t)(n * k) * 4, packed, (size_t)(n * k / 2)) ||
+      overlaps(w, (size_t)(n * k) * 4, scale, (size_t)(n * k / 128) * 2) ||
+      overlaps(packed, (size_t)(n * k / 2), scale, (size_t)(n * k / 128) * 2))
+    return W4_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
+  if (launch_quantize_int4(w, n, k, packed, scale, s) != hipSuccess) return W4_ERR_HIP;
+  int flag = 0;
+  if (quantize_error_read(&flag, s) != hipSuccess) return W4_ERR_HIP;
+  return flag ? W4_ERR_NONFINITE : W4_OK;
+}
+
+size_t w4_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b, int path, int split_k) {
+  if (!valid_fmt(fmt)) return 0;
+  const int64_t g = fmt_group(fmt);
+  if (n < 1 || k < g || k % g || b < 1 || b > W4_MAX_BATCH || n >= kMaxDim || k >= kMaxDim) return 0;
+  switch (path) {
+    case W4_PATH_SPLITK: {
+      const int s = split_k > 0 ? split_k : auto_splits(n, k, (int)b);
+      if (s < 2) return splitk_bytes(n, b, 2);
+      return splitk_bytes(n, b, s);
+    }
+    case W4_PATH_TWOPASS: return (size_t)n * (size_t)k * 2;
+    case W4_PATH_AUTO: {
+      if (b > kMaxGemvBatch) return 0;
+      const int s = auto_splits(n, k, (int)b);
+      return s > 1 ? splitk_bytes(n, b, s) : 0;
+    }
+    default: return 0;
+  }
+}
+
+int w4_gemv_plan(int fmt, int64_t n, int64_t k, int64_t b, int split_k, int* team, int* iters,
+                 int* chunks_per_split, int* grid_x) {
+  if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
+  const int64_t g = fmt_group(fmt);
+  if (n < 1 || k < g || k % g || b < 1 || b > W4_MAX_BATCH || n >= kMaxDim || k >= kMaxDim)
+    return W4_ERR_SHAPE;
+  GemvPlan p;
+  if (b > kMaxGemvBatch || split_k < 1 || !plan_gemv(n, k, (int)b, split_k, &p)) return W4_ERR_PATH;
+  if (team) *team = p.team;
+  if (iters) *iters = p.iters;
+  if (chunks_per_split) *chunks_per_split = p.cps;
+  if (grid_x) *grid_x = p.grid_x;
+  return W4_OK;
+}
+
+int w4_auto_path(int fmt, int64_t n, int64_t k, int64_t b, size_t workspace_bytes, int* split_k) {
+  if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
+  const int64_t g = fmt_group(fmt);
+  if (n < 1 || k < g || k % g || b < 1 || b > W4_MAX_BATCH || n >= kMaxDim || k >= kMaxDim)
+    return W4_ERR_SHAPE;
+  int s = 1;
+  int path;
+  GemvPlan p;
+  if (b >= kMfmaFromBatch || !plan_gemv(n, k, (int)b, 1, &p)) {
+    path = W4_PATH_MFMA;
+  } else {
+    s = auto_splits(n, k, (int)b);
+    if (s > 1 && workspace_bytes >= splitk_bytes(n, b, s)) {
+      path = W4_PATH_SPLITK;
+    } else {
+      s = 1;
+      path = W4_PATH_GEMV;
+    }
+  }
+  if (split_k) *split_k = s;
+  return path;
+}
+
+int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+                 int64_t k, int64_t b, float* y, int path, int split_k, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int st = validate(x, packed, scales, fmt, n, k, b, y);
+  if (st != W4_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (workspace && !aligned(workspace, 16)) return W4_ERR_ALIGN;
+  if (workspace && overlaps(y, (size_t)(b * n) * 4, workspace, workspace_bytes)) return W4_ERR_ALIAS;
+  if (path == W4_PATH_AUTO) {
+    int sk = 1;
+    path = w4_auto_path(fmt, n, k, b, workspace ? workspace_bytes : 0, &sk);
+    if (path < 0) return path;
+    split_k = sk;
+  }
+  switch (path) {
+    case W4_PATH_GEMV:
+      return run_gemv(x, packed, scales, fmt, n, k, b, y, 1, nullptr, s);
+    case W4_PATH_SPLITK: {
+      if (b > kMaxGemvBatch) return W4_ERR_PATH;
+      if (split_k == 0) split_k = std::max(2, auto_splits(n, k, (int)b));
+      if (split_k < 2 || split_k > W4_MAX_SPLIT_K || split_k > k / 32) return W4_ERR_PATH;
+      if (!workspace || workspace_bytes < splitk_bytes(n, b, split_k)) return W4_ERR_WORKSPACE;
+      return run_gemv(x, packed, scales, fmt, n, k, b, y, split_k, workspace, s);
+    }
+    case W4_PATH_MFMA:
+      return run_mfma(x, packed, scales, fmt, n, k, b, y, s);
+    case W4_PATH_TWOPASS: {
+      if (!workspace || workspace_bytes < (size_t)n * (size_t)k * 2) return W4_ERR_WORKSPACE;
+      if (overlaps(workspace, workspace_bytes, x, (size_t)(b * k) * 2) ||
+          overlaps(workspace, workspace_bytes, packed, (size_t)(n * k / 2)))
+        return W4_ERR_ALIAS;
+      return run_twopass(x, packed, scales, fmt, n, k, b, y, workspace, s);
+    }
+  }
+  return W4_ERR_PATH;
+}
+
+int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n, int64_t k,
+            int64_t b, float* y, void* stream) {
+  int st = validate(x, packed, scales, fmt, n, k, b, y);
+  if (st != W4_OK) return st;
+  if (b > kMaxGemvBatch) return W4_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  GemvPlan p;
+  if (!plan_gemv(n, k, (int)b, 1, &p)) return run_mfma(x, packed, scales, fmt, n, k, b, y, s);
+  return run_gemv(x, packed, scales, fmt, n, k, b, y, 1, nullptr, s);
+}
+
+int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+                       int64_t k, int64_t b, float* y, void* stream) {
+  return w4_matmul_ex(x, packed, scales, fmt, n, k, b, y, W4_PATH_AUTO, 0, nullptr, 0, stream);
+}
+
+int w4_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return W4_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return W4_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return W4_ERR_ALIGN;
+  return launch_probe_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? W4_OK
+             : W4_ERR_HIP;
+}
+
+int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return W4_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return W4_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return W4_ERR_ALIGN;
+  if (overlaps(src, bytes, dst, bytes)) return W4_ERR_ALIAS;
+  return launch_probe_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? W4_OK
+             : W4_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Offline quantizers: fp32 weights -> packed nibbles + per-block scales, decided in fp64.
+//
+// NF4 (LLM Quantization on RTX 4060: Where 4-bit Decode Falls Behind FP16, "Standard Expectation
+// from Quantization"): blocks of 64 along K, absmax A stored as fp32, nibble = nearest code to
+// w / A.  The decision compares the fp64 quotient w / A with the fp64 midpoints of neighbouring
+// codes: a non-zero gap between the exact ratio and a midpoint is far larger than the fp64
+// quotient's rounding error, and an exact tie yields the midpoint itself, which goes to the lower
+// index.  An fp32 quotient is not enough: it flips a few nibbles per billion weights.
+//
+// INT4 (My Triton Kernel Ties bitsandbytes, "The kernels": +8 zero point; LLM Compressor 0.14,
+// "Details worth knowing": rint): groups of 128, s = bf16_RNE(fp32(A / 7)), q = clamp(rint(w / s),
+// -8, 7) against the rounded s, nibble = q + 8.  fp32(A / 7) is taken as the fp64 quotient rounded
+// to fp32, which equals the correctly rounded fp32 quotient (53 >= 2 * 24 + 2).
+//
+// One lane handles one pair of weights (one output byte): element 2i goes to the high nibble.
+// Absmax is an integer max over |bits| (the order of non-negative floats), reduced across the 32
+// lanes of an NF4 block or the 64 lanes of an INT4 group with cross-lane shuffles.
+#include "w4_common.h"
+
+namespace w4 {
+
+// Set to a non-zero value by a quantize kernel that meets a NaN or Inf weight.  Reset and read
+// back by the host around every quantize call.
+__device__ int g_w4_nonfinite;
+
+namespace {
+
+__constant__ uint32_t c_nf4_code_bits[16] = W4_NF4_CODE_BITS;
+
+__device__ inline uint32_t nf4_index(double r, const double (&mid)[15]) {
+  uint32_t idx = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) idx += (r > mid[i]) ? 1u : 0u;
+  return idx;
+}
+
+__global__ void __launch_bounds__(256) quant_nf4_kernel(const float* __restrict__ w, int64_t pairs,
+                                                         uint8_t* __restrict__ packed,
+                                                         float* __restrict__ absmax) {
+  const int64_t p = blockIdx.x * 256ll + threadIdx.x;
+  const bool valid = p < pairs;  // pairs is a multiple of 32: a whole block is valid or not
+  const float2 v = reinterpret_cast<const float2*>(w)[valid ? p : 0];
+  const uint32_t a0 = __float_as_uint(v.x) & 0x7FFFFFFFu;
+  const uint32_t a1 = __float_as_uint(v.y) & 0x7FFFFFFFu;
+  if (valid && (a0 >= 0x7F800000u || a1 >= 0x7F800000u)) g_w4_nonfinite = 1;
+  uint32_t m = a0 > a1 ? a0 : a1;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)m, off);
+    m = o > m ? o : m;
+  }
+  const float amax = __uint_as_float(m);
+  uint32_t i0 = 7, i1 = 7;
+  if (m != 0) {
+    double mid[15];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+      mid[i] = ((double)__uint_as_float(c_nf4_code_bits[i]) +
+                (double)__uint_as_float(c_nf4_code_bits[i + 1])) * 0.5;
+    }
+    const double a = (double)amax;
+    i0 = nf4_index((double)v.x / a, mid);
+    i1 = nf4_index((double)v.y / a, mid);
+  }
+  if (valid) {
+    packed[p] = (uint8_t)((i0 << 4) | i1);
+    if ((threadIdx.x & 31) == 0) absmax[p >> 5] = amax;
+  }
+}
+
+__global__ void __launch_bounds__(256) quant_int4_kernel(const float* __restrict__ w, int64_t pairs,
+                                                          uint8_t* __restrict__ packed,
+                                                          uint16_t* __restrict__ scale) {
+  const int64_t p = blockIdx.x * 256ll + threadIdx.x;
+  const bool valid = p < pairs;  // pairs is a multiple of 64: a whole group is valid or not
+  const float2 v = reinterpret_cast<const float2*>(w)[valid ? p : 0];
+  const uint32_t a0 = __float_as_uint(v.x) & 0x7FFFFFFFu;
+  const uint32_t a1 = __float_as_uint(v.y) & 0x7FFFFFFFu;
+  if (valid && (a0 >= 0x7F800000u || a1 >= 0x7F800000u)) g_w4_nonfinite = 1;
+  uint32_t m = a0 > a1 ? a0 : a1;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)m, off);
+    m = o > m ? o : m;
+  }
+  const float s32 = (float)((double)__uint_as_float(m) / 7.0);
+  const uint32_t u = __float_as_uint(s32);
+  const uint32_t sb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // bf16, nearest even
+  const double s = (double)__uint_as_float(sb << 16);
+  uint32_t n0 = 8, n1 = 8;
+  if (s != 0.0) {
+    double q0 = rint((double)v.x / s), q1 = rint((double)v.y / s);
+    q0 = q0 < -8.0 ? -8.0 : (q0 > 7.0 ? 7.0 : q0);
+    q1 = q1 < -8.0 ? -8.0 : (q1 > 7.0 ? 7.0 : q1);
+    n0 = (uint32_t)((int)q0 + 8);
+    n1 = (uint32_t)((int)q1 + 8);
+  }
+  if (valid) {
+    packed[p] = (uint8_t)((n0 << 4) | n1);
+    if ((threadIdx.x & 63) == 0) scale[p >> 6] = (uint16_t)sb;
+  }
+}
+
+}  // namespace
+
+hipError_t quantize_error_reset(hipStream_t s) {
+  const int zero = 0;
+  return hipMemcpyToSymbolAsync(HIP_SYMBOL(g_w4_nonfinite), &zero, sizeof(int), 0,
+                                hipMemcpyHostToDevice, s);
+}
+
+hipError_t quantize_error_read(int* flag, hipStream_t s) {
+  hipError_t e = hipMemcpyFromSymbolAsync(flag, HIP_SYMBOL(g_w4_nonfinite), sizeof(int), 0,
+                                          hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(s);
+}
+
+hipError_t launch_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* packed,
+                               float* absmax, hipStream_t s) {
+  const int64_t pairs = n * (k / 2);
+  const int64_t blocks = (pairs + 255) / 256;
+  hipLaunchKernelGGL(quant_nf4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, pairs, packed,
+                     absmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* packed,
+                                uint16_t* scale, hipStream_t s) {
+  const int64_t pairs = n * (k / 2);
+  const int64_t blocks = (pairs + 255) / 256;
+  hipLaunchKernelGGL(quant_int4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, pairs, packed,
+                     scale);
+  return hipGetLastError();
+}
+
+}  // namespace w4

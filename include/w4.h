@@ -1,0 +1,181 @@
+/*
+ * w4.h -- C ABI of the MI355X (gfx950) fused 4-bit weight-only dequantize-and-multiply library.
+ *
+ * The operation: y[b, n] = sum_k x[b, k] * W_hat[n, k], where W_hat is decoded on chip from packed
+ * 4-bit weights and per-block scales, with fp32 accumulation, and never written back to memory
+ * (LLM Quantization on RTX 4060: Where 4-bit Decode Falls Behind FP16, sections "Fused Kernel:
+ * Moving Dequantization On-Chip" and "Kernel Implementation").
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer named as "device" is HIP device memory owned by the caller; the library never
+ *     allocates, frees or keeps a device pointer beyond the call.
+ *   - All arrays are dense and row-major; there are no stride arguments.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Matmul calls are
+ *     asynchronous on it and make no allocation and no synchronization, so they can be captured
+ *     in a HIP graph.  Quantize calls synchronize the stream (they report device-detected errors).
+ *   - Arguments are validated on the host before anything is launched; a failing check returns a
+ *     negative w4_status_t and launches nothing.  After a launch, a HIP launch error is reported
+ *     as W4_ERR_HIP.
+ *   - Packed weights: uint8 [N, K/2]; byte i of a row holds element 2i in its high nibble and
+ *     element 2i+1 in its low nibble (same page, "Kernel Implementation").
+ *   - The library has no global mutable state except the quantizers' device-side error word;
+ *     calls on different streams may run concurrently as long as their buffers do not overlap.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight format x activation dtype.  y is always fp32 [B, N].
+ *   NF4 : 16-entry NormalFloat codebook, blocks of 64 along K, one fp32 absmax per block,
+ *         scales = float[N, K/64]  (LLM Quantization on RTX 4060, "Standard Expectation from
+ *         Quantization").
+ *   INT4: symmetric, stored nibble = q + 8 (My Triton Kernel Ties bitsandbytes, "The kernels"),
+ *         groups of 128 along K, scales = bf16 bit patterns uint16[N, K/128]. */
+typedef enum {
+  W4_NF4_X_F16 = 1,
+  W4_NF4_X_BF16 = 2,
+  W4_INT4_X_F16 = 3,
+  W4_INT4_X_BF16 = 4
+} w4_format_t;
+
+typedef enum {
+  W4_OK = 0,
+  W4_ERR_NULL = -1,      /* a required pointer is NULL                                        */
+  W4_ERR_SHAPE = -2,     /* N, K or B out of range, or K not a multiple of 64 (NF4) / 128 (INT4) */
+  W4_ERR_ALIGN = -3,     /* packed or x not 16-byte aligned, scales or y not element aligned  */
+  W4_ERR_FORMAT = -4,    /* unknown w4_format_t                                               */
+  W4_ERR_NONFINITE = -5, /* quantize met a NaN or Inf weight (outputs are then meaningless)   */
+  W4_ERR_WORKSPACE = -6, /* workspace missing or smaller than w4_workspace_bytes()            */
+  W4_ERR_PATH = -7,      /* unknown path, or a path that does not support this batch size     */
+  W4_ERR_HIP = -8,       /* a HIP runtime call failed                                         */
+  W4_ERR_ALIAS = -9      /* y overlaps an input or the workspace                              */
+} w4_status_t;
+
+/* Execution paths of the matmul. */
+typedef enum {
+  W4_PATH_AUTO = 0,    /* pick by (format, N, K, B) from a fixed table                        */
+  W4_PATH_GEMV = 1,    /* fused streaming GEMV, one pass, B <= 8                              */
+  W4_PATH_SPLITK = 2,  /* fused GEMV over split_k disjoint K ranges into an fp32 workspace,
+                          then a fixed-order sum that overwrites y (deterministic, no atomics;
+                          My Triton Kernel Ties bitsandbytes, "The kernels", v3 and its
+                          stale-output bug)                                                  */
+  W4_PATH_MFMA = 3,    /* dequantize W tiles on chip, MFMA against x, B >= 1 (meant for B >= 16) */
+  W4_PATH_TWOPASS = 4  /* ablation: dequantize W to fp16 in the workspace, then a dense GEMV/GEMM
+                          (the out-of-place path of LLM Quantization on RTX 4060, "The
+                          Quantization Tax: A Byte-Accounting Model")                        */
+} w4_path_t;
+
+#define W4_MAX_BATCH 256
+#define W4_MAX_SPLIT_K 64
+
+/* ---------------------------------------------------------------- quantizers (offline) ----- */
+
+/* w4_quantize_nf4: blockwise absmax NF4 (LLM Quantization on RTX 4060, "Standard Expectation
+ * from Quantization").  Per row and 64-block: absmax A = max |w| (stored as fp32, not re-
+ * quantized); nibble = index of the code nearest to w / A, decided exactly (fp64 quotient
+ * against fp64 midpoints; a value exactly on a midpoint takes the lower index); a block with
+ * A == 0 stores A = 0 and nibble 7 (the 0.0 code).
+ *   w       device float[N, K], read only
+ *   N, K    N >= 1, K >= 64, K % 64 == 0
+ *   packed  device uint8[N, K/2], written; 16-byte aligned
+ *   absmax  device float[N, K/64], written; 4-byte aligned
+ * Synchronizes `stream`.  Returns W4_ERR_NONFINITE if any weight is NaN or Inf. */
+int w4_quantize_nf4(const float* w, int64_t N, int64_t K, uint8_t* packed, float* absmax,
+                    void* stream);
+
+/* w4_quantize_int4: symmetric INT4 with a +8 zero point (My Triton Kernel Ties bitsandbytes,
+ * "The kernels"), round half to even (LLM Compressor 0.14, "Details worth knowing").  Per row and
+ * 128-group: s = bf16_RNE(fp32(absmax / 7)); q = clamp(rint(w / s), -8, 7) with the quotient
+ * taken against the rounded s; nibble = q + 8; a group whose s is 0 stores s = 0, nibbles 8.
+ *   w           device float[N, K], read only
+ *   N, K        N >= 1, K >= 128, K % 128 == 0
+ *   packed      device uint8[N, K/2], written; 16-byte aligned
+ *   scale_bf16  device uint16[N, K/128] (bf16 bit patterns), written; 2-byte aligned
+ * Synchronizes `stream`.  Returns W4_ERR_NONFINITE if any weight is NaN or Inf. */
+int w4_quantize_int4(const float* w, int64_t N, int64_t K, uint8_t* packed, uint16_t* scale_bf16,
+                     void* stream);
+
+/* -------------------------------------------------------------------------- matmul --------- */
+
+/* w4_gemv: fused dequantize-and-multiply, y = x . W_hat^T, B <= 8 (decode; LLM Quantization on
+ * RTX 4060, "Kernel Implementation": unpack, codebook, block scale, fp32 accumulation).
+ *   x       device [B, K] fp16 or bf16 (per fmt) bit patterns; 16-byte aligned
+ *   packed  device uint8[N, K/2]; 16-byte aligned
+ *   scales  device float[N, K/64] (NF4) or uint16 bf16 bits [N, K/128] (INT4)
+ *   fmt     w4_format_t
+ *   N, K, B N >= 1; K as for the format; 1 <= B <= 8
+ *   y       device float[B, N]; fully overwritten, never accumulated into; must not overlap inputs
+ * Single pass, no workspace.  Asynchronous on `stream`. */
+int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t N,
+            int64_t K, int64_t B, float* y, void* stream);
+
+/* w4_gemm_smallbatch: the same operation for 1 <= B <= W4_MAX_BATCH (decode batches; Do
+ * Quantization and Sparsity make LLM Inference Faster?, "NF4: fast at batch 1, slower at larger
+ * batches").  Picks the fused GEMV for small B and the MFMA dequantize-in-LDS path for larger B;
+ * never materializes W_hat.  Arguments as for w4_gemv.  No workspace.  Asynchronous. */
+int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt,
+                       int64_t N, int64_t K, int64_t B, float* y, void* stream);
+
+/* w4_matmul_ex: the same operation with an explicit path, split count and workspace (tests and
+ * the ablation benchmark).  path = W4_PATH_AUTO also considers split-K when a workspace is given.
+ *   split_k          number of K ranges for W4_PATH_SPLITK (2..W4_MAX_SPLIT_K); 0 = library choice;
+ *                    ignored by the other paths
+ *   workspace        device memory of at least w4_workspace_bytes(...) bytes, 16-byte aligned;
+ *                    may be NULL when that size is 0.  Its contents are scratch on entry and exit.
+ *                    Two calls in flight must not share one workspace.
+ * Returns W4_ERR_WORKSPACE when the workspace is missing or too small for the requested path. */
+int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t N,
+                 int64_t K, int64_t B, float* y, int path, int split_k, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace w4_matmul_ex needs for (fmt, N, K, B, path, split_k): split-K needs
+ * 4 * S * B * N, two-pass 2 * N * K, the single-pass paths 0; W4_PATH_AUTO reports the split-K
+ * size it would use.  Returns 0 for invalid arguments. */
+size_t w4_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t B, int path, int split_k);
+
+/* The path (w4_path_t) and split count W4_PATH_AUTO would run for these arguments when given
+ * `workspace_bytes` of workspace; negative w4_status_t on invalid arguments. */
+int w4_auto_path(int fmt, int64_t N, int64_t K, int64_t B, size_t workspace_bytes, int* split_k);
+
+/* ------------------------------------------------------------------ introspection --------- */
+
+/* Launch shape the fused GEMV uses for (fmt, N, K, B) over `split_k` K ranges (1 = single pass):
+ * lanes per output row, 16-byte chunks per lane, chunks per split and workgroups along N.  Any
+ * output pointer may be NULL.  Returns W4_OK, or W4_ERR_SHAPE / W4_ERR_PATH when the GEMV path
+ * cannot run these arguments. */
+int w4_gemv_plan(int fmt, int64_t N, int64_t K, int64_t B, int split_k, int* team, int* iters,
+                 int* chunks_per_split, int* grid_x);
+
+/* Host pointer to the 16 NF4 code points (fp32, ascending) the kernels decode with.  Static
+ * storage owned by the library; never NULL. */
+const float* w4_nf4_codebook(void);
+
+/* Static, human-readable text for a w4_status_t; never NULL. */
+const char* w4_status_string(int status);
+
+/* Library ABI version (this header: 1). */
+int w4_version(void);
+
+/* ------------------------------------------------------------------ measurement probes ------ */
+
+/* Streaming-read ceiling probe: reads `bytes` (multiple of 16) from device `src` with 128-bit
+ * loads, folds them, and writes one uint32 per workgroup to device `sink` (>= 4096 entries).
+ * Used to measure the achievable HBM read bandwidth next to the GEMV (My Triton Kernel Ties
+ * bitsandbytes, "The roofline first": measured, not spec-sheet, bandwidth).  Asynchronous. */
+int w4_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/* Copy probe: dst[0:bytes] = src[0:bytes] with 128-bit loads and stores; bytes % 16 == 0;
+ * the ranges must not overlap.  Asynchronous. */
+int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

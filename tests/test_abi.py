@@ -1,0 +1,108 @@
+"""The C ABI library loads on the host, exports every function include/w4.h declares, and rejects
+invalid arguments on the host before any launch.  No compute call is made (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+
+def _lib():
+    import bit_weight_only_w4_amd as w4
+
+    if not os.path.exists(w4.LIB_PATH):
+        pytest.fail("libw4.so is not built; run `python -m bit_weight_only_w4_amd.build`")
+    return w4, w4.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for required in ("w4_quantize_nf4", "w4_quantize_int4", "w4_gemv", "w4_gemm_smallbatch",
+                     "w4_matmul_ex", "w4_workspace_bytes"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    _, L = _lib()
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_codebook_matches_oracle_bitwise():
+    w4, _ = _lib()
+    lib_code = np.array(w4.nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_code.view(np.uint32), oracle.nf4_codebook().view(np.uint32))
+
+
+def test_version_and_status_strings():
+    w4, L = _lib()
+    assert L.w4_version() == 1
+    for st in range(0, -10, -1):
+        assert w4.status_string(st) not in ("", "unknown status")
+    assert w4.status_string(-42) == "unknown status"
+
+
+FAKE = 0x10000  # a non-null, well-aligned address that is never dereferenced
+
+
+def _gemv(L, x=FAKE, p=FAKE * 2, s=FAKE * 3, fmt=1, n=64, k=256, b=1, y=FAKE * 4):
+    vp = ctypes.c_void_p
+    return L.w4_gemv(vp(x), vp(p), vp(s), fmt, n, k, b, vp(y), None)
+
+
+def test_host_validation_codes():
+    _, L = _lib()
+    assert _gemv(L, x=0) == -1
+    assert _gemv(L, y=0) == -1
+    assert _gemv(L, fmt=0) == -4
+    assert _gemv(L, fmt=5) == -4
+    assert _gemv(L, n=0) == -2
+    assert _gemv(L, k=96) == -2  # NF4 needs K % 64
+    assert _gemv(L, fmt=3, k=192) == -2  # INT4 needs K % 128
+    assert _gemv(L, b=0) == -2
+    assert _gemv(L, b=9) == -2  # w4_gemv is the B <= 8 entry point
+    assert _gemv(L, x=FAKE + 8) == -3  # x must be 16-byte aligned
+    assert _gemv(L, p=FAKE + 4) == -3
+    assert _gemv(L, y=FAKE + 2) == -3
+    assert _gemv(L, y=FAKE * 2) == -9  # y overlaps the packed weights
+    vp = ctypes.c_void_p
+    # split-K without a workspace; two-pass without a workspace; unknown path
+    assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 1, vp(FAKE * 4), 2, 4,
+                          None, 0, None) == -6
+    assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 1, vp(FAKE * 4), 4, 0,
+                          None, 0, None) == -6
+    assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 1, vp(FAKE * 4), 9, 0,
+                          None, 0, None) == -7
+    assert L.w4_quantize_nf4(None, 4, 64, vp(FAKE), vp(FAKE * 2), None) == -1
+    assert L.w4_quantize_nf4(vp(FAKE), 4, 96, vp(FAKE * 8), vp(FAKE * 9), None) == -2
+    assert L.w4_quantize_int4(vp(FAKE), 4, 64, vp(FAKE * 8), vp(FAKE * 9), None) == -2
+    assert L.w4_probe_read(vp(FAKE), 24, vp(FAKE * 2), None) == -2
+
+
+def test_workspace_and_plan_logic():
+    w4, _ = _lib()
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 1, "splitk", 4) == 4 * 1536 * 4
+    assert w4.workspace_bytes("nf4_f16", 8960, 1536, 2, "twopass") == 8960 * 1536 * 2
+    assert w4.workspace_bytes("nf4_f16", 8960, 1536, 1, "gemv") == 0
+    assert w4.workspace_bytes("nf4_f16", 8960, 100, 1, "gemv") == 0  # invalid K
+    plan = w4.gemv_plan("nf4_f16", 8960, 1536, 1)
+    assert plan["team"] * plan["iters"] >= 1536 // 32
+    assert plan["chunks_per_split"] == 1536 // 32
+    plan = w4.gemv_plan("int4_bf16", 1536, 8960, 1, split_k=4)
+    assert plan["chunks_per_split"] * 4 >= 8960 // 32
+    with pytest.raises(ValueError):
+        w4.gemv_plan("nf4_f16", 64, 256, 9)
+    assert w4.auto_path("nf4_f16", 8960, 1536, 1) == ("gemv", 1)
+    assert w4.auto_path("nf4_f16", 8960, 1536, 64)[0] == "mfma"

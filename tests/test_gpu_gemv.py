@@ -1,0 +1,188 @@
+"""Fused GEMV / split-K / two-pass / small-batch paths against the oracle's fp64 reference,
+per element, within |y - y_ref| <= 2e-3 * sum_k |x_k w_k| + 1e-5.
+
+Every case quantizes on the GPU, checks the packed data bit for bit against the oracle, and then
+checks y computed from it, so the oracle's reference is built from the oracle's own packed data.
+"""
+import numpy as np
+import pytest
+
+import synth_inputs
+from tests import gpu_util as g
+
+pytestmark = pytest.mark.gpu
+
+ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16"]
+
+
+def _case(fmt, n, k, b, seed, sigma=0.02):
+    w = synth_inputs.weights(n, k, sigma=sigma, seed=seed)
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=seed + 1000)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    g.assert_quant_equal(fmt, p, s, pr, sr)
+    return x, g.to_dev_x(x, g.XDT[fmt]), p, s, pr, sr
+
+
+def _workspace(nbytes):
+    import torch
+
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=g.device())
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("n,k,b", [(256, 1536, 1), (37, 384, 1), (1, 128, 1), (300, 1536, 2),
+                                   (129, 8960, 1), (77, 8192, 3), (64, 28672, 1), (200, 1536, 4),
+                                   (45, 1024, 5), (96, 2048, 8), (33, 640, 7), (250, 256, 6)])
+def test_gemv_parity(fmt, n, k, b):
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n + k + b)
+    y = w4.gemv(xd, p, s, fmt)
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_single_gemv_workload(fmt):
+    """W[256 x 1536] ~ N(0, 0.02) drawn first, then x, seed 0 (the single-GEMV workload)."""
+    import bit_weight_only_w4_amd as w4
+
+    w, x = synth_inputs.single_gemv_case(seed=0, dtype=g.XDT[fmt])
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    g.assert_quant_equal(fmt, p, s, pr, sr)
+    y = w4.gemv(g.to_dev_x(x, g.XDT[fmt]), p, s, fmt)
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("splits", [2, 3, 4, 8, 16])
+def test_splitk_parity_down_shape(fmt, splits):
+    """Split-K on the 1536 x 8960 down projection, B = 1 and 8."""
+    import bit_weight_only_w4_amd as w4
+
+    for b in (1, 8):
+        x, xd, p, s, pr, sr = _case(fmt, 1536, 8960, b, seed=40 + splits)
+        ws = _workspace(w4.workspace_bytes(fmt, 1536, 8960, b, "splitk", splits))
+        y = w4.matmul_ex(xd, p, s, fmt, path="splitk", split_k=splits, workspace=ws)
+        g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
+def test_splitk_deterministic_and_overwrites(fmt):
+    """y pre-filled with NaN and called twice with a dirty workspace: bitwise identical results,
+    nothing accumulated into y (the stale-output bug of an atomic split-K under autotuning)."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, 1536, 8960, 2, seed=77)
+    ws = _workspace(w4.workspace_bytes(fmt, 1536, 8960, 2, "splitk", 8))
+    ws.fill_(0x7F)
+    y1 = torch.full((2, 1536), float("nan"), device=g.device())
+    w4.matmul_ex(xd, p, s, fmt, path="splitk", split_k=8, workspace=ws, y=y1)
+    y2 = torch.full((2, 1536), float("nan"), device=g.device())
+    w4.matmul_ex(xd, p, s, fmt, path="splitk", split_k=8, workspace=ws, y=y2)
+    assert torch.equal(y1, y2)
+    g.assert_y_close(fmt, y1, x, pr, sr)
+    y3 = w4.gemv(xd, p, s, fmt)
+    y4 = w4.gemv(xd, p, s, fmt)
+    assert torch.equal(y3, y4)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("n,k,b", [(256, 1536, 1), (129, 8960, 3), (40, 384, 17)])
+def test_twopass_parity(fmt, n, k, b):
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=5 * n + b)
+    ws = _workspace(w4.workspace_bytes(fmt, n, k, b, "twopass"))
+    y = w4.matmul_ex(xd, p, s, fmt, path="twopass", workspace=ws)
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_batch_rows_match_single_calls(fmt):
+    """Each row of a B = 5 product equals (within the bound) the B = 1 product of that row."""
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, 513, 1536, 5, seed=3)
+    y = w4.gemv(xd, p, s, fmt)
+    for i in range(5):
+        yi = w4.gemv(xd[i:i + 1].contiguous(), p, s, fmt)
+        g.assert_y_close(fmt, yi, x[i:i + 1], pr, sr)
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_one_hot_and_zero_activations(fmt):
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    n, k = 96, 1536
+    w = synth_inputs.weights(n, k, seed=8)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    x = np.zeros((2, k), dtype=np.uint16)
+    x[0, 700] = 0x3C00 if g.XDT[fmt] == "f16" else 0x3F80  # 1.0
+    y = w4.gemv(g.to_dev_x(x, g.XDT[fmt]), p, s, fmt).cpu().numpy().astype(np.float64)
+    import oracle
+
+    w_hat = oracle.dequant(g.WFMT[fmt], pr, sr)
+    assert np.all(y[1] == 0)
+    assert np.allclose(y[0], w_hat[:, 700], rtol=3.5e-4 if fmt == "nf4_f16" else 1e-6, atol=0)
+    assert torch.isfinite(torch.as_tensor(y)).all()
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
+def test_decode_shapes_full_and_sampled(fmt):
+    """The five Qwen2.5-1.5B decode shapes at B = 1, the path the decode step uses (auto with a
+    workspace); lm_head checked on sampled rows."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    shapes = [(1536, 1536), (256, 1536), (8960, 1536), (1536, 8960), (151936, 1536)]
+    for n, k in shapes:
+        w = synth_inputs.weights(n, k, seed=n ^ k)
+        x = synth_inputs.activations(1, k, g.XDT[fmt], seed=11)
+        p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+        rows = None if n <= 9000 else np.sort(np.random.default_rng(n).choice(n, 200, replace=False))
+        pr, sr = g.oracle_quantize(fmt, w if rows is None else w[rows])
+        g.assert_quant_equal(fmt, p, s, pr, sr, rows=rows)
+        ws = torch.empty(1 << 22, dtype=torch.uint8, device=g.device())
+        y = w4.matmul_ex(g.to_dev_x(x, g.XDT[fmt]), p, s, fmt, path="auto", workspace=ws)
+        if rows is None:
+            g.assert_y_close(fmt, y, x, pr, sr)
+        else:
+            g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
+
+
+def test_error_codes_on_device_pointers():
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case("nf4_f16", 64, 256, 1, seed=1)
+    y = torch.empty((1, 64), device=g.device())
+    L = w4.lib()
+    import ctypes
+
+    vp = ctypes.c_void_p
+    st = L.w4_gemv(vp(xd.data_ptr() + 2), vp(p.data_ptr()), vp(s.data_ptr()), 1, 64, 256, 1,
+                   vp(y.data_ptr()), None)
+    assert st == -3  # misaligned x
+    st = L.w4_gemv(vp(xd.data_ptr()), vp(p.data_ptr()), vp(s.data_ptr()), 1, 64, 192 + 32, 1,
+                   vp(y.data_ptr()), None)
+    assert st == -2  # K not a multiple of 64
+    st = L.w4_gemv(vp(xd.data_ptr()), vp(p.data_ptr()), vp(s.data_ptr()), 3, 64, 192, 1,
+                   vp(y.data_ptr()), None)
+    assert st == -2  # INT4 needs K % 128
+    st = L.w4_gemv(vp(xd.data_ptr()), vp(p.data_ptr()), vp(s.data_ptr()), 1, 64, 256, 1,
+                   vp(xd.data_ptr()), None)
+    assert st == -9  # y aliases x
+    st = L.w4_matmul_ex(vp(xd.data_ptr()), vp(p.data_ptr()), vp(s.data_ptr()), 1, 64, 256, 1,
+                        vp(y.data_ptr()), 2, 4, None, 0, None)
+    assert st == -6  # split-K without workspace
+    assert torch.cuda.synchronize() is None

@@ -1,0 +1,72 @@
+"""GPU quantizers against the oracle, bit for bit (packed nibbles and scales)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs
+from tests import gpu_util as g
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["nf4_f16", "int4_f16"]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k,seed", [(256, 1536, 0), (37, 384, 1), (1, 128, 2), (1536, 8960, 3),
+                                      (129, 8192, 4)])
+def test_quantize_bitexact_gaussian(fmt, n, k, seed):
+    w = synth_inputs.weights(n, k, seed=seed)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    g.assert_quant_equal(fmt, p, s, *g.oracle_quantize(fmt, w))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_edge_values(fmt):
+    """Zero blocks, -0.0, denormals, huge magnitudes, constant blocks, exact ties."""
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((12, 256)) * 0.02).astype(np.float32)
+    w[0] = 0.0
+    w[1, :128] = -0.0
+    w[2] = rng.standard_normal(256).astype(np.float32) * np.float32(1e-39)  # fp32 denormals
+    w[3] = rng.standard_normal(256).astype(np.float32) * np.float32(1e37)
+    w[4] = np.float32(0.75)
+    w[5, ::2] = np.float32(2.0 ** -140)
+    w[5, 1::2] = -np.float32(2.0 ** -141)
+    # NF4 ties: absmax 1 and representable midpoints; INT4 ties: s = 1 and half-integers
+    mids = [m for m in oracle.nf4_midpoints() if float(np.float32(m)) == m]
+    w[6] = 0.0
+    w[6, 0] = 1.0
+    w[6, 1:1 + len(mids)] = mids
+    w[6, 128] = 7.0
+    w[6, 129:137] = [0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 6.5]
+    w[7] = rng.integers(-7, 8, 256).astype(np.float32) * np.float32(2.0 ** -5)
+    w[7, ::128] = 7 * 2.0 ** -5
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    g.assert_quant_equal(fmt, p, s, *g.oracle_quantize(fmt, w))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_rejects_nonfinite(fmt):
+    import bit_weight_only_w4_amd as w4
+
+    for bad in (np.nan, np.inf, -np.inf):
+        w = synth_inputs.weights(4, 256, seed=5)
+        w[2, 77] = bad
+        with pytest.raises(w4.W4ValueError) as e:
+            g.gpu_quantize(fmt, g.to_dev_f32(w))
+        assert e.value.status == -5
+    # the error word is cleared by the next call
+    w = synth_inputs.weights(4, 256, seed=5)
+    g.gpu_quantize(fmt, g.to_dev_f32(w))
+
+
+def test_quantize_lm_head_sampled_rows():
+    """Full 151936 x 1536 matrix quantized on the GPU; 96 sampled rows compared bit for bit."""
+    n, k = synth_inputs.QWEN15_LM_HEAD[1:]
+    w = synth_inputs.weights(n, k, seed=999)
+    wd = g.to_dev_f32(w)
+    rows = np.sort(np.random.default_rng(1).choice(n, 94, replace=False))
+    rows = np.concatenate([[0], rows, [n - 1]])
+    for fmt in FMTS:
+        p, s = g.gpu_quantize(fmt, wd)
+        g.assert_quant_equal(fmt, p, s, *g.oracle_quantize(fmt, w[rows]), rows=rows)
