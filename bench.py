@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the fused W4 GEMV library on one MI355X.
+
+One step = the 197 weight GEMVs of a Qwen2.5-1.5B decode step at batch 1 (28 layers x {q, k, v, o,
+gate, up, down} + lm_head; Do Quantization and Sparsity make LLM Inference Faster?, "What we
+did"), NF4 blocksize 64 with fp32 absmax and fp16 activations, every matrix distinct (872 MB of
+packed weights and scales, more than the 256 MB last-level cache, so every step streams from
+HBM).  Weights are synthetic N(0, 0.02), quantized on the GPU before timing; activations N(0, 1).
+The step is captured once as a HIP graph and replayed.
+
+stdout: ONE JSON line (the driver contract).  Details go to stderr and to --report.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--fmt", default="nf4_f16", choices=["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16"])
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--kernel-reps", type=int, default=5, help="eager passes timed per launch")
+    ap.add_argument("--report", default=None, help="write a detailed JSON report here")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(fmt: str, n: int, k: int, b: int) -> int:
+    """Bytes the method itself must move for one GEMV: packed weights + scales + x + y."""
+    scale_bytes = n * k // 16 if fmt.startswith("nf4") else n * k // 64
+    return n * k // 2 + scale_bytes + 2 * b * k + 4 * b * n
+
+
+class Step:
+    """The 197 GEMVs with their inputs resident in HBM and prebuilt C-ABI arguments."""
+
+    def __init__(self, fmt, b, path, dev):
+        import ctypes
+
+        import torch
+
+        import bit_weight_only_w4_amd as w4
+        import synth_inputs
+
+        self.w4, self.fmt, self.b, self.path = w4, fmt, b, path
+        self.shapes = synth_inputs.decode_step_shapes()
+        self.fmt_id = w4.FORMATS[fmt]
+        xdt = torch.float16 if fmt.endswith("_f16") else torch.bfloat16
+        gen = torch.Generator(device=dev).manual_seed(7)
+        self.x = {k: torch.randn(b, k, generator=gen, device=dev).to(xdt).contiguous()
+                  for k in sorted({k for _, _, k in self.shapes})}
+        self.mats, self.ys = [], []
+        t0 = time.time()
+        for i, (name, n, k) in enumerate(self.shapes):
+            if name == "lm_head":
+                seed = 999
+            else:
+                layer, j = i // 7, i % 7
+                seed = 1000 + 8 * layer + j
+            g = torch.Generator(device=dev).manual_seed(seed)
+            w = torch.randn(n, k, generator=g, device=dev) * synth_inputs.QWEN15_SIGMA
+            packed, scales = (w4.quantize_nf4(w) if fmt.startswith("nf4") else w4.quantize_int4(w))
+            del w
+            self.mats.append((packed, scales))
+            self.ys.append(torch.empty(b, n, device=dev))
+        torch.cuda.synchronize()
+        log(f"[bench] quantized {len(self.shapes)} matrices in {time.time() - t0:.1f}s")
+        self.ws_bytes = max(w4.workspace_bytes(fmt, n, k, b, path) for _, n, k in self.shapes)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.plans = []
+        vp = ctypes.c_void_p
+        self.args = []
+        for (name, n, k), (p, s), y in zip(self.shapes, self.mats, self.ys):
+            ap, sk = w4.auto_path(fmt, n, k, b, self.ws_bytes) if path == "auto" else (path, 0)
+            self.plans.append((ap, sk))
+            self.args.append((vp(self.x[k].data_ptr()), vp(p.data_ptr()), vp(s.data_ptr()),
+                              self.fmt_id, n, k, b, vp(y.data_ptr()), w4.PATHS[ap], sk,
+                              vp(self.ws.data_ptr()), self.ws.numel()))
+        self.bytes = [algorithmic_bytes(fmt, n, k, b) for _, n, k in self.shapes]
+
+    def launch(self, i, stream_handle):
+        r = self.w4.lib().w4_matmul_ex(*self.args[i], stream_handle)
+        if r != 0:
+            self.w4.check(r, f"gemv {self.shapes[i][0]}")
+
+    def run(self, stream_handle):
+        for i in range(len(self.args)):
+            self.launch(i, stream_handle)
+
+    def kernel_key(self, i):
+        """Name of the kernel instantiation launch i runs (matches the profiler's kernel names)."""
+        name, n, k = self.shapes[i]
+        path, sk = self.plans[i]
+        if path in ("gemv", "splitk"):
+            plan = self.w4.gemv_plan(self.fmt, n, k, self.b, max(sk, 1))
+            fmt_i = 0 if self.fmt.startswith("nf4") else 1
+            xt = 0 if self.fmt.endswith("_f16") else 1
+            key = f"gemv_kernel<{fmt_i}, {xt}, {self.b}, {plan['iters']}>"
+            return key + (f"+splitk_reduce(S={sk})" if path == "splitk" else "")
+        return path
+
+
+def time_graph(step, steps, warmup, dev):
+    import torch
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run(side.cuda_stream)  # one eager pass on the capture stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step.run(side.cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, graph
+
+
+def time_launches(step, reps):
+    """Per-launch device time: each launch bracketed by an event pair on the stream it runs on,
+    launched eagerly so that the pair brackets that kernel alone.  Returns ms per launch (mean
+    over `reps` passes)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    n = len(step.args)
+    acc = [0.0] * n
+    for _ in range(reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            step.launch(i, h)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(n):
+            acc[i] += ev[i][0].elapsed_time(ev[i][1])
+    return [a / reps for a in acc]
+
+
+def measure_ceilings(dev, nbytes=2 << 30, reps=10):
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    dst = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
+    w4.probe_read(src, sink)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        w4.probe_read(src, sink)
+    e.record()
+    torch.cuda.synchronize()
+    read_gbs = nbytes * reps / (s.elapsed_time(e) / 1e3) / 1e9
+    half = src[: nbytes // 2]
+    w4.probe_copy(half, dst)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        w4.probe_copy(half, dst)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (nbytes // 2) * reps / (s.elapsed_time(e) / 1e3) / 1e9
+    del src, dst
+    return read_gbs, copy_gbs
+
+
+def cpu_baseline(fmt, b, seconds):
+    """The oracle (fp64 dequantize + dot products) timed on the host cores on a bounded sample of
+    the decode step -- layer 0's q, gate and down matrices -- scaled to a whole step by weight
+    count.  Weights are drawn and quantized on the CPU (untimed); only dequant + GEMV is timed."""
+    import numpy as np
+
+    import oracle
+    import synth_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    wf = "nf4" if fmt.startswith("nf4") else "int4"
+    xd = "f16" if fmt.endswith("_f16") else "bf16"
+    sample = [("q", 1536, 1536, 1000), ("gate", 8960, 1536, 1004), ("down", 1536, 8960, 1006)]
+    mats = []
+    for name, n, k, seed in sample:
+        w = synth_inputs.weights(n, k, seed=seed)
+        q = oracle.quantize_nf4(w) if wf == "nf4" else oracle.quantize_int4(w)
+        mats.append((q, synth_inputs.activations(b, k, xd, seed=7)))
+    sample_weights = sum(n * k for _, n, k, _ in sample)
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        for (p, s), x in mats:
+            oracle.gemv_reference(x, xd, oracle.dequant(wf, p, s))
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 50:
+            break
+    per_pass = el / passes
+    step_weights = sum(n * k for _, n, k in synth_inputs.decode_step_shapes())
+    step_s = per_pass * step_weights / sample_weights
+    try:
+        model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
+    except Exception:
+        model = "unknown"
+    return {
+        "value": round(b / step_s, 4),
+        "unit": "tok/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"layer-0 q 1536x1536, gate 8960x1536, down 1536x8960 ({sample_weights} weights), "
+                   f"{passes} passes in {el:.1f}s, scaled by weight count to the 197-GEMV step "
+                   f"({step_weights} weights): {step_s:.2f} s/step; CPU {model}"),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w4.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    step = Step(args.fmt, args.batch, args.path, dev)
+    total_bytes = sum(step.bytes)
+
+    ms, _graph = time_graph(step, args.steps, args.warmup, dev)
+    tok_s = args.batch * 1e3 / ms
+    step_gbs = total_bytes / (ms / 1e3) / 1e9
+    log(f"[bench] step {ms * 1e3:.1f} us -> {tok_s:.1f} tok/s; algorithmic {total_bytes / 1e6:.1f} MB "
+        f"-> {step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+
+    per = time_launches(step, args.kernel_reps)
+    by_key = {}
+    for i, t in enumerate(per):
+        key = step.kernel_key(i)
+        d = by_key.setdefault(key, {"launches": 0, "ms": 0.0, "bytes": 0})
+        d["launches"] += 1
+        d["ms"] += t
+        d["bytes"] += step.bytes[i]
+    dom_key = max(by_key, key=lambda kk: by_key[kk]["ms"])
+    dom = by_key[dom_key]
+    avg_ms = dom["ms"] / dom["launches"]
+    avg_bytes = dom["bytes"] / dom["launches"]
+    achieved = avg_bytes / (avg_ms / 1e3) / 1e9
+    shapes_report = {}
+    for i, (name, n, k) in enumerate(step.shapes):
+        kind = name.split(".")[-1]
+        r = shapes_report.setdefault(kind, {"n": n, "k": k, "count": 0, "us": 0.0,
+                                            "bytes": step.bytes[i], "path": step.plans[i][0],
+                                            "split_k": step.plans[i][1]})
+        r["count"] += 1
+        r["us"] += per[i] * 1e3
+    for kind, r in shapes_report.items():
+        r["us"] /= r["count"]
+        r["gbs"] = r["bytes"] / (r["us"] / 1e6) / 1e9
+        log(f"[bench] {kind:8s} {r['n']:6d}x{r['k']:5d} {r['path']:6s} S={r['split_k']:2d} "
+            f"{r['us']:8.2f} us {r['gbs']:8.0f} GB/s")
+    for key, d in sorted(by_key.items(), key=lambda kv: -kv[1]["ms"]):
+        log(f"[bench] kernel {key}: {d['launches']} launches, avg {d['ms'] / d['launches'] * 1e3:.2f} us, "
+            f"{d['bytes'] / (d['ms'] / 1e3) / 1e9:.0f} GB/s")
+
+    read_gbs, copy_gbs = measure_ceilings(dev)
+    log(f"[bench] ceilings: streaming read {read_gbs:.0f} GB/s, copy {copy_gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.fmt, args.batch, args.cpu_seconds)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    line = {
+        "metric": "W4 GEMV achieved HBM GB/s & % roofline; decode-step tok/s (197 GEMVs, B=1)",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if args.fmt.endswith("_f16") else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"Qwen2.5-1.5B decode step: 197 distinct GEMVs (28x q,k,v,o,gate,up,down + "
+                         f"lm_head), {args.fmt.split('_')[0].upper()} "
+                         f"{'bs64 fp32 absmax' if args.fmt.startswith('nf4') else 'g128 bf16 scale'}, "
+                         f"{args.fmt.split('_')[1]} x, fp32 accumulate and output"),
+            "format": args.fmt,
+            "batch": args.batch,
+            "path": args.path,
+            "algorithmic_bytes_per_step": total_bytes,
+            "step_gbs": round(step_gbs, 1),
+            "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+            "measured_read_ceiling_gbs": round(read_gbs, 1),
+            "measured_copy_ceiling_gbs": round(copy_gbs, 1),
+            "step_frac_of_measured_read": round(step_gbs / read_gbs, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom_key,
+            "launches_per_step": dom["launches"],
+            "avg_launch_us": round(avg_ms * 1e3, 3),
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump({"line": line, "shapes": shapes_report, "kernels": by_key}, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -69,54 +69,62 @@ int validate(const void* x, const uint8_t* packed, const void* scales, int fmt, 
   return W4_OK;
 }
 
-// Launch shape of the fused GEMV for (K, B) over `splits` K ranges.  Chooses the team width
-// (lanes per row) with the least idle lanes among those whose per-lane chunk count fits the
-// register budget of batch b; a team wider than one wave costs an LDS exchange per row, so it
-// is taken only when it saves idle lanes.
+int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// Launch shape of the fused GEMV for (N, K, B) over `splits` K ranges.
+//
+// The rules follow measurements on MI355X (graph replays of one shape over rotated copies):
+//  * small matrices are latency-bound: give each lane as few 16-byte chunks as possible (one,
+//    when a row has at most 64 chunks, else up to three) so that the first row block finishes
+//    soon after its data lands;
+//  * large matrices (>= 64 MiB of packed bytes) are bandwidth-bound: use narrow teams (16 lanes,
+//    several rows per wave) and at most 256 workgroups of 512 threads that each stream many row
+//    blocks, which keeps the per-lane activation footprint and the number of table fills small;
+//  * at most two workgroups fit in one CU (64 KiB decode table each), so grids beyond two per CU
+//    only queue.
 bool plan_gemv(int64_t n, int64_t k, int b, int splits, GemvPlan* out) {
   const int cpr = (int)(k / 32);
   if (splits < 1 || splits > cpr) return false;
   const int cps = (cpr + splits - 1) / splits;
   if ((int64_t)(splits - 1) * cps >= cpr) return false;  // every split must own a chunk
   const int itmax = gemv_max_iters(b);
-  double best = 1e9;
-  GemvPlan p{};
-  for (int team = 16; team <= kGemvThreads; team *= 2) {
-    const int it = (cps + team - 1) / team;
-    if (it > itmax) continue;
-    const double waste = (double)(team * it - cps) / (double)(team * it);
-    const double cost = waste + (team > 64 ? 0.05 : 0.0) + (it > 5 ? 0.01 * (it - 5) : 0.0);
-    if (cost < best) {
-      best = cost;
-      p.team = team;
-      p.iters = it;
-    }
+  const bool large = (n * (k / 2)) / splits >= ((int64_t)64 << 20);
+  int team;
+  if (large) {
+    team = std::max(16, next_pow2((cps + 2) / 3));
+  } else if (cps <= 64) {
+    team = std::max(16, next_pow2(cps));
+  } else {
+    team = std::max(64, next_pow2((cps + 2) / 3));
   }
-  if (best > 1e8) return false;
+  while (team < kGemvMaxThreads && (cps + team - 1) / team > itmax) team *= 2;
+  const int iters = (cps + team - 1) / team;
+  if (iters > itmax) return false;
+  GemvPlan p{};
+  p.team = team;
+  p.iters = iters;
+  p.threads = (team >= 128 && !large) ? 256 : kGemvMaxThreads;
+  if (p.threads < team) p.threads = team;
   p.splits = splits;
   p.cps = cps;
-  const int64_t rows_per_wg = kGemvThreads / p.team;
+  const int64_t rows_per_wg = p.threads / p.team;
   const int64_t nrb = (n + rows_per_wg - 1) / rows_per_wg;
-  // Two 64 KiB decode tables fit in one CU's LDS; more resident workgroups than that would only
-  // queue, so the grid is capped at two per CU and each workgroup loops over row blocks.
-  const int64_t cap = std::max<int64_t>(1, 2 * (int64_t)device_cu_count() / splits);
+  const int64_t cus = device_cu_count();
+  const int64_t cap = std::max<int64_t>(1, (large ? cus : 2 * cus) / splits);
   p.grid_x = (int)std::min<int64_t>(nrb, cap);
   *out = p;
   return true;
 }
 
-// Split count the automatic path uses: split only when one pass would leave CUs idle.
-int auto_splits(int64_t n, int64_t k, int b) {
-  GemvPlan p;
-  if (!plan_gemv(n, k, b, 1, &p)) return 1;
-  const int64_t rows_per_wg = kGemvThreads / p.team;
-  const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
-  const int64_t target = 2 * (int64_t)device_cu_count();
-  if (wgs >= target) return 1;
-  int s = 1;
-  while (s < W4_MAX_SPLIT_K && wgs * s * 2 <= target * 2 && (k / 32) / (s * 2) >= 32) s *= 2;
-  return s;
-}
+// Split count the automatic path uses.  Measured on the 1536 x 8960 down projection, one pass
+// with 128-lane teams beats every split-K configuration (the extra reduce launch costs more than
+// the parallelism it adds), so the automatic choice is a single pass; split-K stays available
+// explicitly through W4_PATH_SPLITK.
+int auto_splits(int64_t, int64_t, int) { return 1; }
 
 size_t splitk_bytes(int64_t n, int64_t b, int s) { return (size_t)s * (size_t)b * (size_t)n * 4; }
 
@@ -230,11 +238,7 @@ size_t w4_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b, int path, in
   const int64_t g = fmt_group(fmt);
   if (n < 1 || k < g || k % g || b < 1 || b > W4_MAX_BATCH || n >= kMaxDim || k >= kMaxDim) return 0;
   switch (path) {
-    case W4_PATH_SPLITK: {
-      const int s = split_k > 0 ? split_k : auto_splits(n, k, (int)b);
-      if (s < 2) return splitk_bytes(n, b, 2);
-      return splitk_bytes(n, b, s);
-    }
+    case W4_PATH_SPLITK: return splitk_bytes(n, b, split_k > 1 ? split_k : 4);
     case W4_PATH_TWOPASS: return (size_t)n * (size_t)k * 2;
     case W4_PATH_AUTO: {
       if (b > kMaxGemvBatch) return 0;
@@ -302,7 +306,7 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
       return run_gemv(x, packed, scales, fmt, n, k, b, y, 1, nullptr, s);
     case W4_PATH_SPLITK: {
       if (b > kMaxGemvBatch) return W4_ERR_PATH;
-      if (split_k == 0) split_k = std::max(2, auto_splits(n, k, (int)b));
+      if (split_k == 0) split_k = 4;
       if (split_k < 2 || split_k > W4_MAX_SPLIT_K || split_k > k / 32) return W4_ERR_PATH;
       if (!workspace || workspace_bytes < splitk_bytes(n, b, split_k)) return W4_ERR_WORKSPACE;
       return run_gemv(x, packed, scales, fmt, n, k, b, y, split_k, workspace, s);

@@ -36,7 +36,8 @@ inline int64_t fmt_group(int fmt) { return fmt_weight(fmt) == kNF4 ? 64 : 128; }
 
 // Shape of one fused-GEMV launch (host-chosen; see choose_gemv in w4_api.cpp).
 struct GemvPlan {
-  int team;     // lanes that share one output row (16..512, power of two)
+  int threads;  // threads per workgroup (64, 128, 256 or 512)
+  int team;     // lanes that share one output row (16..512, power of two, <= threads)
   int iters;    // 16-byte chunks each lane streams per row (<= the instantiated maximum)
   int splits;   // number of disjoint K ranges (grid.y); 1 = single pass
   int cps;      // chunks per split
@@ -56,7 +57,7 @@ struct GemvArgs {
   int iters;
 };
 
-constexpr int kGemvThreads = 512;  // 8 wave64s per workgroup
+constexpr int kGemvMaxThreads = 512;
 constexpr int kMaxGemvBatch = 8;
 
 // Largest per-lane chunk count instantiated for batch b (x is held in registers:

@@ -1,0 +1,365 @@
+// Fused 4-bit dequantize-and-multiply GEMV for gfx950 (CDNA4), batch 1..8 (kernel templates; one
+// translation unit per weight x activation format instantiates them).
+//
+// Operation (LLM Quantization on RTX 4060: Where 4-bit Decode Falls Behind FP16, "Kernel
+// Implementation"): y[b, n] = sum_k x[b, k] * code(nibble[n, k]) * scale[n, block(k)], reading each
+// packed byte once from HBM, decoding on chip and accumulating in fp32.
+//
+// Layout of the work:
+//   * A "team" of T lanes (16..512) owns one output row.  Lane t of a team streams the 16-byte
+//     chunks t, t + T, t + 2T, ... of the row (one global_load_dwordx4 each; consecutive lanes on
+//     consecutive chunks).  A chunk is 32 weights: half an NF4 block or a quarter of an INT4
+//     group, so each chunk needs exactly one scale.
+//   * The lane keeps the activations of its chunks in VGPRs for the whole launch and walks the
+//     row blocks of its workgroup (grid-stride) with the next two row blocks' packed bytes and
+//     scales already in flight.  The loop is unrolled three times so that the three buffers rotate
+//     by register renaming: no copy of a loaded register, hence no wait on an outstanding load,
+//     until the data is consumed.
+//   * Every load is unconditional and in bounds (out-of-range chunks and row blocks are clamped
+//     to valid ones and skipped by index when computing), so no branch joins force early waits.
+//   * Decode: a 256-entry table in LDS maps a packed byte to the pair (value of the high nibble,
+//     value of the low nibble) in the activation's 16-bit type; one ds_read_b32 decodes two
+//     weights.  The table holds 64 copies of each entry, copy c in bank c, and lane L reads copy L,
+//     so the lookups of a wave never conflict.  Its LDS address, byte value * 256 + lane * 4, is
+//     built by one v_perm_b32.  The table is written while the first loads are in flight.
+//   * Multiply: v_dot2_f32_f16 / v_dot2_f32_bf16 of the decoded pair with the activation pair
+//     into fp32 (products of two 16-bit values are exact in fp32), then one fp32 FMA per chunk with
+//     the block scale.  NF4 with bf16 activations splits each code into two bf16 terms (8-byte
+//     entries, 32 copies): a single bf16 code is not accurate enough.
+//   * Reduction over a team: DPP within 16 lanes, cross-row shuffles up to 64, and an LDS exchange
+//     between the waves of a team wider than one wave.
+#pragma once
+#include "w4_common.h"
+
+namespace w4 {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+constexpr int kTableBytes = 65536;  // 256 entries x 256 bytes
+
+__device__ inline uint32_t f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ inline uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Lane q (q < 16) receives the fp32 bits of NF4 code q; the constants go lane by lane from scalar
+// registers, so building the table needs no memory access.
+__device__ inline uint32_t nf4_codes_in_lanes() {
+  constexpr uint32_t k[16] = W4_NF4_CODE_BITS;
+  uint32_t v = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(k[q]), "i"(q));
+  return v;
+}
+
+// The decoded 16-bit value(s) of nibble (lane & 15), meaningful in lanes 0..15: the fp16 code
+// (NF4 x fp16), the bf16 hi/lo split of the code (NF4 x bf16), or q - 8 in the activation type
+// (INT4, exact).
+template <int FMT, int XT>
+__device__ inline void lane_decode(uint32_t& v1, uint32_t& v2) {
+  v2 = 0;
+  if (FMT == kNF4) {
+    const float c = __uint_as_float(nf4_codes_in_lanes());
+    if (XT == kF16) {
+      v1 = f16_bits(c);
+    } else {
+      v1 = bf16_rne_bits(c);
+      v2 = bf16_rne_bits(c - __uint_as_float(v1 << 16));
+    }
+  } else {
+    const float v = (float)((int)(threadIdx.x & 15u) - 8);
+    v1 = XT == kF16 ? f16_bits(v) : (__float_as_uint(v) >> 16);
+  }
+}
+
+// Write the 64 KiB table.  Thread t writes 16-byte slots t, t + NT, ...; slot i belongs to entry
+// i >> 4, whose high nibble (i >> 8) is the same for the whole wave (read with v_readlane) and
+// whose low nibble ((i >> 4) & 15) is fixed per lane when NT >= 256.
+template <int FMT, int XT, int NT>
+__device__ inline void fill_table(uint32_t* tab) {
+  uint32_t v1, v2;
+  lane_decode<FMT, XT>(v1, v2);
+  constexpr bool kSplit = (FMT == kNF4 && XT == kBF16);
+  uint4* t4 = reinterpret_cast<uint4*>(tab);
+  const int tid = threadIdx.x;
+  uint32_t lo1 = 0, lo2 = 0;
+  if (NT >= 256) {
+    lo1 = (uint32_t)__shfl((int)v1, (tid >> 4) & 15) << 16;
+    if (kSplit) lo2 = (uint32_t)__shfl((int)v2, (tid >> 4) & 15) << 16;
+  }
+#pragma unroll 4
+  for (int j = 0; j < kTableBytes / 16 / NT; ++j) {
+    const int i = tid + NT * j;
+    const int hi = __builtin_amdgcn_readfirstlane(i >> 8);
+    if (NT < 256) {
+      lo1 = (uint32_t)__shfl((int)v1, (i >> 4) & 15) << 16;
+      if (kSplit) lo2 = (uint32_t)__shfl((int)v2, (i >> 4) & 15) << 16;
+    }
+    const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane((int)v1, hi) | lo1;
+    if (kSplit) {
+      const uint32_t p2 = (uint32_t)__builtin_amdgcn_readlane((int)v2, hi) | lo2;
+      t4[i] = make_uint4(p1, p2, p1, p2);
+    } else {
+      t4[i] = make_uint4(p1, p1, p1, p1);
+    }
+  }
+}
+
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
+
+// Sum over a team of `team` (16..64) lanes inside one wave; every lane of the team gets the total.
+__device__ inline float team_sum_wave(float v, int team) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror: all 16 lanes of a row hold the row sum
+  if (team >= 32) v += __shfl_xor(v, 16);
+  if (team >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <int FMT>
+__device__ inline float load_scale(const void* scales, int64_t row, int64_t k, int chunk) {
+  if (FMT == kNF4) {
+    return reinterpret_cast<const float*>(scales)[row * (k >> 6) + (chunk >> 1)];
+  } else {
+    const uint16_t s = reinterpret_cast<const uint16_t*>(scales)[row * (k >> 7) + (chunk >> 2)];
+    return __uint_as_float((uint32_t)s << 16);
+  }
+}
+
+template <int FMT, int XT, int B, int ITM, int NT>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) gemv_kernel(GemvArgs a) {
+  __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
+  __shared__ float xwave[NT / 64][B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int team = a.team;
+  const int tshift = __builtin_ctz((unsigned)team);
+  const int tl = tid & (team - 1);
+  const int team_id = tid >> tshift;
+  const int teams_per_wg = NT >> tshift;
+  const int c0 = blockIdx.y * a.cps;
+  const int nck = min(a.cps, a.cpr - c0);
+  const int64_t n = a.n, k = a.k;
+  const int64_t nrb = (n + teams_per_wg - 1) / teams_per_wg;
+  const int64_t grid = gridDim.x;
+  const int64_t rb0 = blockIdx.x;  // < nrb: the host never launches more workgroups than blocks
+  const int64_t rb_last = rb0 + grid * ((nrb - 1 - rb0) / grid);
+
+  // Chunk index of slot i for this lane, clamped into the split's range.
+  auto chunk_of = [&](int i) {
+    const int c = tl + (i << tshift);
+    return c < nck ? c : nck - 1;
+  };
+  auto load_rb = [&](int64_t rbv, uint4 (&p)[ITM], float (&s)[ITM]) {
+    rbv = rbv < rb_last ? rbv : rb_last;
+    int64_t row = rbv * teams_per_wg + team_id;
+    row = row < n ? row : n - 1;
+    const uint4* prow = reinterpret_cast<const uint4*>(a.packed + row * (k >> 1)) + c0;
+#pragma unroll
+    for (int i = 0; i < ITM; ++i) {
+      const int c = chunk_of(i);
+      p[i] = load_stream16(prow + c);
+      s[i] = load_scale<FMT>(a.scales, row, k, c0 + c);
+    }
+  };
+
+  // --- first row block, then this lane's activations, then the second row block
+  uint4 pA[ITM], pB[ITM], pC[ITM];
+  float sA[ITM], sB[ITM], sC[ITM];
+  load_rb(rb0, pA, sA);
+  uint32_t xr[ITM][B][16];
+#pragma unroll
+  for (int i = 0; i < ITM; ++i) {
+    const int c = chunk_of(i);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const uint4* xb = reinterpret_cast<const uint4*>(a.x + b * k) + (int64_t)(c0 + c) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = xb[q];
+        xr[i][b][4 * q + 0] = v.x;
+        xr[i][b][4 * q + 1] = v.y;
+        xr[i][b][4 * q + 2] = v.z;
+        xr[i][b][4 * q + 3] = v.w;
+      }
+    }
+  }
+  load_rb(rb0 + grid, pB, sB);
+
+  // --- decode table, written while the loads above are in flight
+  fill_table<FMT, XT, NT>(tab);
+  __syncthreads();
+
+  constexpr bool kSplitCode = (FMT == kNF4 && XT == kBF16);
+  const uint32_t laneoff = kSplitCode ? (uint32_t)(lane & 31) * 8u : (uint32_t)lane * 4u;
+  const char* tabc = reinterpret_cast<const char*>(tab);
+  const int wave = tid >> 6;
+  const int waves_per_team = team > 64 ? team >> 6 : 1;
+
+  auto compute_store = [&](int64_t rbv, const uint4 (&pk)[ITM], const float (&sc)[ITM]) {
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < ITM; ++i) {
+      const int c = tl + (i << tshift);
+      if (i < a.iters && c < nck) {
+        float d[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) d[b] = 0.0f;
+        const uint32_t wv[4] = {pk[i].x, pk[i].y, pk[i].z, pk[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            // LDS byte address: lane offset in byte 0, the packed byte in byte 1.
+            const uint32_t addr =
+                __builtin_amdgcn_perm(wv[j], laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb) << 8));
+            const int m = 4 * j + kb;  // byte index in the chunk = activation pair index
+            if (kSplitCode) {
+              const uint2 t = *reinterpret_cast<const uint2*>(tabc + addr);
+#pragma unroll
+              for (int b = 0; b < B; ++b) {
+                const bf162_t xv = __builtin_bit_cast(bf162_t, xr[i][b][m]);
+                d[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, t.x), xv, d[b], false);
+                d[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, t.y), xv, d[b], false);
+              }
+            } else {
+              const uint32_t t = *reinterpret_cast<const uint32_t*>(tabc + addr);
+#pragma unroll
+              for (int b = 0; b < B; ++b) {
+                if (XT == kF16) {
+                  d[b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, t),
+                                                __builtin_bit_cast(half2_t, xr[i][b][m]), d[b], false);
+                } else {
+                  d[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, t),
+                                                         __builtin_bit_cast(bf162_t, xr[i][b][m]),
+                                                         d[b], false);
+                }
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(d[b], sc[i], acc[b]);
+      }
+    }
+
+    const int64_t row = rbv * teams_per_wg + team_id;
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = team_sum_wave(acc[b], team);
+    float* out = a.out + (int64_t)blockIdx.y * B * n;
+    if (waves_per_team == 1) {
+      if (tl == 0 && row < n) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) out[b * n + row] = acc[b];
+      }
+    } else {
+      if (lane == 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) xwave[wave][b] = acc[b];
+      }
+      __syncthreads();
+      if (tl == 0 && row < n) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float v = 0.0f;
+          for (int w = 0; w < waves_per_team; ++w) v += xwave[wave + w][b];
+          out[b * n + row] = v;
+        }
+      }
+      __syncthreads();
+    }
+  };
+
+  // --- main loop: three row blocks per trip, buffers rotating A -> B -> C, no early exit; the
+  // last one or two row blocks are already loaded when the loop ends.
+  const int64_t count = (rb_last - rb0) / grid + 1;  // row blocks of this workgroup
+  int64_t rb = rb0;
+  int64_t t = 0;
+  for (; t + 3 <= count; t += 3) {
+    load_rb(rb + 2 * grid, pC, sC);
+    compute_store(rb, pA, sA);
+    load_rb(rb + 3 * grid, pA, sA);
+    compute_store(rb + grid, pB, sB);
+    load_rb(rb + 4 * grid, pB, sB);
+    compute_store(rb + 2 * grid, pC, sC);
+    rb += 3 * grid;
+  }
+  if (t < count) compute_store(rb, pA, sA);
+  if (t + 1 < count) compute_store(rb + grid, pB, sB);
+}
+
+template <int FMT, int XT, int B, int ITM>
+hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
+  const dim3 grid(p.grid_x, p.splits);
+  switch (p.threads) {
+    case 256: hipLaunchKernelGGL((gemv_kernel<FMT, XT, B, ITM, 256>), grid, dim3(256), 0, s, a); break;
+    case 512: hipLaunchKernelGGL((gemv_kernel<FMT, XT, B, ITM, 512>), grid, dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, int XT, int B>
+hipError_t launch_b(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
+  const int it = p.iters;
+  if constexpr (B == 1) {
+    switch (it) {
+      case 1: return launch_one<FMT, XT, B, 1>(a, p, s);
+      case 2: return launch_one<FMT, XT, B, 2>(a, p, s);
+      case 3: return launch_one<FMT, XT, B, 3>(a, p, s);
+      case 4: return launch_one<FMT, XT, B, 4>(a, p, s);
+      case 5: return launch_one<FMT, XT, B, 5>(a, p, s);
+      case 6: return launch_one<FMT, XT, B, 6>(a, p, s);
+      case 7: return launch_one<FMT, XT, B, 7>(a, p, s);
+      case 8: return launch_one<FMT, XT, B, 8>(a, p, s);
+    }
+  } else if constexpr (B == 2) {
+    switch (it) {
+      case 1: return launch_one<FMT, XT, B, 1>(a, p, s);
+      case 2: return launch_one<FMT, XT, B, 2>(a, p, s);
+      case 3: return launch_one<FMT, XT, B, 3>(a, p, s);
+      case 4: return launch_one<FMT, XT, B, 4>(a, p, s);
+    }
+  } else if constexpr (B <= 4) {
+    switch (it) {
+      case 1: return launch_one<FMT, XT, B, 1>(a, p, s);
+      case 2: return launch_one<FMT, XT, B, 2>(a, p, s);
+    }
+  } else {
+    if (it == 1) return launch_one<FMT, XT, B, 1>(a, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FMT, int XT>
+hipError_t launch_fx(int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
+  switch (b) {
+    case 1: return launch_b<FMT, XT, 1>(a, p, s);
+    case 2: return launch_b<FMT, XT, 2>(a, p, s);
+    case 3: return launch_b<FMT, XT, 3>(a, p, s);
+    case 4: return launch_b<FMT, XT, 4>(a, p, s);
+    case 5: return launch_b<FMT, XT, 5>(a, p, s);
+    case 6: return launch_b<FMT, XT, 6>(a, p, s);
+    case 7: return launch_b<FMT, XT, 7>(a, p, s);
+    case 8: return launch_b<FMT, XT, 8>(a, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace w4

@@ -1,0 +1,8 @@
+// Instantiation of the fused GEMV for one weight x activation format (nf4_bf16).
+#include "w4_gemv_impl.h"
+
+namespace w4 {
+hipError_t launch_gemv_nf4_bf16(int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
+  return launch_fx<kNF4, kBF16>(b, a, p, s);
+}
+}  // namespace w4
