@@ -1,0 +1,54 @@
+"""MFMA small-batch path against the oracle's fp64 reference (per element, 2e-3 T + 1e-5)."""
+import pytest
+
+import synth_inputs
+from tests import gpu_util as g
+
+pytestmark = pytest.mark.gpu
+
+ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16"]
+
+
+def _case(fmt, n, k, b, seed):
+    w = synth_inputs.weights(n, k, seed=seed)
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=seed + 17)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    g.assert_quant_equal(fmt, p, s, pr, sr)
+    return x, g.to_dev_x(x, g.XDT[fmt]), p, s, pr, sr
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("n,k,b", [(64, 256, 16), (37, 384, 9), (100, 1536, 32), (256, 1536, 17),
+                                   (130, 8960, 64), (513, 1536, 128), (65, 2048, 129),
+                                   (96, 1024, 200), (200, 8192, 48)])
+def test_mfma_parity(fmt, n, k, b):
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n * 7 + b)
+    y = w4.matmul_ex(xd, p, s, fmt, path="mfma")
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
+def test_smallbatch_auto_uses_both_paths(fmt):
+    """w4_gemm_smallbatch at B = 8 (GEMV) and B = 32 (MFMA) on the gate shape."""
+    import bit_weight_only_w4_amd as w4
+
+    for b in (8, 32):
+        x, xd, p, s, pr, sr = _case(fmt, 8960, 1536, b, seed=b)
+        assert w4.auto_path(fmt, 8960, 1536, b)[0] == ("gemv" if b <= 8 else "mfma")
+        y = w4.gemm_smallbatch(xd, p, s, fmt)
+        g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "nf4_bf16"])
+def test_mfma_deterministic(fmt):
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, 300, 1536, 40, seed=3)
+    y1 = w4.matmul_ex(xd, p, s, fmt, path="mfma")
+    y2 = w4.matmul_ex(xd, p, s, fmt, path="mfma")
+    assert torch.equal(y1, y2)
