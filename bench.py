@@ -31,7 +31,8 @@ def parse_args():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--kernel-reps", type=int, default=5, help="eager passes timed per launch")
+    ap.add_argument("--schedule", default="serial", choices=["serial", "dag"],
+                    help="serial: one chain of 197 launches; dag: q|k|v and gate|up as branches")
     ap.add_argument("--report", default=None, help="write a detailed JSON report here")
     return ap.parse_args()
 
@@ -110,24 +111,66 @@ class Step:
             plan = self.w4.gemv_plan(self.fmt, n, k, self.b, max(sk, 1))
             fmt_i = 0 if self.fmt.startswith("nf4") else 1
             xt = 0 if self.fmt.endswith("_f16") else 1
-            key = f"gemv_kernel<{fmt_i}, {xt}, {self.b}, {plan['iters']}>"
+            key = f"gemv_kernel<{fmt_i}, {xt}, {self.b}, {plan['iters']}, {plan['threads']}>"
             return key + (f"+splitk_reduce(S={sk})" if path == "splitk" else "")
         return path
 
 
-def time_graph(step, steps, warmup, dev):
+def capture(step, dev, indices=None, schedule="serial"):
+    """Capture launches `indices` (default: the whole step) into one HIP graph.
+
+    schedule "serial": every launch depends on the previous one (one stream).
+    schedule "dag": the dependency structure of a real decode step -- q, k and v of a layer read
+    the same activations and run on three branches, gate and up on two, everything else in
+    order -- still one kernel launch per GEMV."""
     import torch
 
-    side = torch.cuda.Stream(device=dev)
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step.run(side.cuda_stream)  # one eager pass on the capture stream before capture
-    torch.cuda.current_stream().wait_stream(side)
+    idx = list(range(len(step.args))) if indices is None else list(indices)
+    s0 = torch.cuda.Stream(device=dev)
+    s0.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s0):
+        for i in idx:  # warm every launch once on the capture stream
+            step.launch(i, s0.cuda_stream)
     torch.cuda.synchronize()
+    side = [torch.cuda.Stream(device=dev) for _ in range(2)]
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        step.run(side.cuda_stream)
+    with torch.cuda.graph(graph, stream=s0):
+        pos = 0
+        while pos < len(idx):
+            i = idx[pos]
+            group = [i]
+            if schedule == "dag":
+                kind = step.shapes[i][0].split(".")[-1]
+                want = {"q": ["k", "v"], "gate": ["up"]}.get(kind, [])
+                while want and pos + len(group) < len(idx):
+                    j = idx[pos + len(group)]
+                    if step.shapes[j][0].split(".")[-1] != want[0]:
+                        break
+                    group.append(j)
+                    want.pop(0)
+            if len(group) == 1:
+                step.launch(i, s0.cuda_stream)
+            else:
+                fork = torch.cuda.Event()
+                fork.record(s0)
+                for b, j in enumerate(group[1:]):
+                    side[b].wait_event(fork)
+                    step.launch(j, side[b].cuda_stream)
+                step.launch(group[0], s0.cuda_stream)
+                for b in range(len(group) - 1):
+                    join = torch.cuda.Event()
+                    join.record(side[b])
+                    s0.wait_event(join)
+            pos += len(group)
     torch.cuda.synchronize()
+    return graph
+
+
+def time_replays(graph, steps, warmup):
+    """ms per replay: `warmup` untimed replays, then `steps` replays between two events on the
+    current stream (the stream the graph's kernels run on)."""
+    import torch
+
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -138,30 +181,43 @@ def time_graph(step, steps, warmup, dev):
         graph.replay()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps, graph
+    return start.elapsed_time(end) / steps
 
 
-def time_launches(step, reps):
-    """Per-launch device time: each launch bracketed by an event pair on the stream it runs on,
-    launched eagerly so that the pair brackets that kernel alone.  Returns ms per launch (mean
-    over `reps` passes)."""
-    import torch
+def time_kernel_classes(step, dev, reps=50):
+    """Average launch time of every kernel instantiation the step uses, measured the way the step
+    runs: a graph holding only that kernel's launches, in step order, timed with HIP events over
+    `reps` replays.  Returns {kernel: {"launches", "us", "bytes"}} per step."""
+    classes = {}
+    for i in range(len(step.args)):
+        classes.setdefault(step.kernel_key(i), []).append(i)
+    out = {}
+    for key, idx in classes.items():
+        g = capture(step, dev, idx, "serial")
+        ms = time_replays(g, reps, 5)
+        out[key] = {"launches": len(idx), "us": ms * 1e3 / len(idx),
+                    "bytes": sum(step.bytes[i] for i in idx) / len(idx)}
+        del g
+    return out
 
-    stream = torch.cuda.current_stream()
-    h = stream.cuda_stream
-    n = len(step.args)
-    acc = [0.0] * n
-    for _ in range(reps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        for i in range(n):
-            ev[i][0].record(stream)
-            step.launch(i, h)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        for i in range(n):
-            acc[i] += ev[i][0].elapsed_time(ev[i][1])
-    return [a / reps for a in acc]
+
+def time_shape_kinds(step, dev, reps=50):
+    """Average launch time per projection kind (q, k, ..., lm_head) inside the step, from a graph
+    of that kind's launches only."""
+    kinds = {}
+    for i, (name, _, _) in enumerate(step.shapes):
+        kinds.setdefault(name.split(".")[-1], []).append(i)
+    out = {}
+    for kind, idx in kinds.items():
+        g = capture(step, dev, idx, "serial")
+        ms = time_replays(g, reps, 5)
+        _, n, k = step.shapes[idx[0]]
+        out[kind] = {"n": n, "k": k, "count": len(idx), "us": ms * 1e3 / len(idx),
+                     "bytes": step.bytes[idx[0]], "path": step.plans[idx[0]][0],
+                     "kernel": step.kernel_key(idx[0])}
+        out[kind]["gbs"] = out[kind]["bytes"] / (out[kind]["us"] / 1e6) / 1e9
+        del g
+    return out
 
 
 def measure_ceilings(dev, nbytes=2 << 30, reps=10):
@@ -264,41 +320,30 @@ def main():
     step = Step(args.fmt, args.batch, args.path, dev)
     total_bytes = sum(step.bytes)
 
-    ms, _graph = time_graph(step, args.steps, args.warmup, dev)
+    other = "dag" if args.schedule == "serial" else "serial"
+    g_main = capture(step, dev, None, args.schedule)
+    ms = time_replays(g_main, args.steps, args.warmup)
+    del g_main
+    g_other = capture(step, dev, None, other)
+    ms_other = time_replays(g_other, args.steps, args.warmup)
+    del g_other
     tok_s = args.batch * 1e3 / ms
     step_gbs = total_bytes / (ms / 1e3) / 1e9
-    log(f"[bench] step {ms * 1e3:.1f} us -> {tok_s:.1f} tok/s; algorithmic {total_bytes / 1e6:.1f} MB "
-        f"-> {step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    log(f"[bench] step ({args.schedule}) {ms * 1e3:.1f} us -> {tok_s:.1f} tok/s; algorithmic "
+        f"{total_bytes / 1e6:.1f} MB -> {step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    log(f"[bench] step ({other}) {ms_other * 1e3:.1f} us -> {args.batch * 1e3 / ms_other:.1f} tok/s")
 
-    per = time_launches(step, args.kernel_reps)
-    by_key = {}
-    for i, t in enumerate(per):
-        key = step.kernel_key(i)
-        d = by_key.setdefault(key, {"launches": 0, "ms": 0.0, "bytes": 0})
-        d["launches"] += 1
-        d["ms"] += t
-        d["bytes"] += step.bytes[i]
-    dom_key = max(by_key, key=lambda kk: by_key[kk]["ms"])
-    dom = by_key[dom_key]
-    avg_ms = dom["ms"] / dom["launches"]
-    avg_bytes = dom["bytes"] / dom["launches"]
-    achieved = avg_bytes / (avg_ms / 1e3) / 1e9
-    shapes_report = {}
-    for i, (name, n, k) in enumerate(step.shapes):
-        kind = name.split(".")[-1]
-        r = shapes_report.setdefault(kind, {"n": n, "k": k, "count": 0, "us": 0.0,
-                                            "bytes": step.bytes[i], "path": step.plans[i][0],
-                                            "split_k": step.plans[i][1]})
-        r["count"] += 1
-        r["us"] += per[i] * 1e3
-    for kind, r in shapes_report.items():
-        r["us"] /= r["count"]
-        r["gbs"] = r["bytes"] / (r["us"] / 1e6) / 1e9
-        log(f"[bench] {kind:8s} {r['n']:6d}x{r['k']:5d} {r['path']:6s} S={r['split_k']:2d} "
-            f"{r['us']:8.2f} us {r['gbs']:8.0f} GB/s")
-    for key, d in sorted(by_key.items(), key=lambda kv: -kv[1]["ms"]):
-        log(f"[bench] kernel {key}: {d['launches']} launches, avg {d['ms'] / d['launches'] * 1e3:.2f} us, "
-            f"{d['bytes'] / (d['ms'] / 1e3) / 1e9:.0f} GB/s")
+    kernels = time_kernel_classes(step, dev)
+    shapes = time_shape_kinds(step, dev)
+    for kind, r in shapes.items():
+        log(f"[bench] {kind:8s} {r['n']:6d}x{r['k']:5d} {r['path']:6s} {r['us']:8.2f} us/launch "
+            f"{r['gbs']:8.0f} GB/s  [{r['kernel']}]")
+    for key, d in sorted(kernels.items(), key=lambda kv: -kv[1]["us"] * kv[1]["launches"]):
+        log(f"[bench] kernel {key}: {d['launches']} launches/step, {d['us']:.2f} us/launch, "
+            f"{d['bytes'] / (d['us'] / 1e6) / 1e9:.0f} GB/s")
+    dom_key = max(kernels, key=lambda kk: kernels[kk]["us"] * kernels[kk]["launches"])
+    dom = kernels[dom_key]
+    achieved = dom["bytes"] / (dom["us"] / 1e6) / 1e9
 
     read_gbs, copy_gbs = measure_ceilings(dev)
     log(f"[bench] ceilings: streaming read {read_gbs:.0f} GB/s, copy {copy_gbs:.0f} GB/s")
@@ -308,6 +353,7 @@ def main():
         cpu = cpu_baseline(args.fmt, args.batch, args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu}")
 
+    wfmt = args.fmt.split("_")[0].upper()
     line = {
         "metric": "W4 GEMV achieved HBM GB/s & % roofline; decode-step tok/s (197 GEMVs, B=1)",
         "value": round(tok_s, 2),
@@ -322,25 +368,29 @@ def main():
         "dtype": "f16" if args.fmt.endswith("_f16") else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"Qwen2.5-1.5B decode step: 197 distinct GEMVs (28x q,k,v,o,gate,up,down + "
-                         f"lm_head), {args.fmt.split('_')[0].upper()} "
-                         f"{'bs64 fp32 absmax' if args.fmt.startswith('nf4') else 'g128 bf16 scale'}, "
-                         f"{args.fmt.split('_')[1]} x, fp32 accumulate and output"),
+            "workload": (f"Qwen2.5-1.5B decode step: 197 distinct GEMV launches (28x q,k,v,o,gate,"
+                         f"up,down + lm_head), {wfmt} "
+                         f"{'bs64 fp32 absmax' if wfmt == 'NF4' else 'g128 bf16 scale'}, "
+                         f"{args.fmt.split('_')[1]} x, batch {args.batch}, fp32 accumulate/output"),
             "format": args.fmt,
             "batch": args.batch,
             "path": args.path,
+            "schedule": args.schedule,
+            "other_schedule": {other: {"ms_per_step": round(ms_other, 5),
+                                       "tok_s": round(args.batch * 1e3 / ms_other, 2)}},
             "algorithmic_bytes_per_step": total_bytes,
             "step_gbs": round(step_gbs, 1),
             "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
             "measured_read_ceiling_gbs": round(read_gbs, 1),
             "measured_copy_ceiling_gbs": round(copy_gbs, 1),
             "step_frac_of_measured_read": round(step_gbs / read_gbs, 4),
+            "per_shape_us": {kk: round(r["us"], 3) for kk, r in shapes.items()},
         },
         "roofline": {
             "bound": "hbm",
             "kernel": dom_key,
             "launches_per_step": dom["launches"],
-            "avg_launch_us": round(avg_ms * 1e3, 3),
+            "avg_launch_us": round(dom["us"], 3),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -351,7 +401,7 @@ def main():
     }
     if args.report:
         with open(args.report, "w") as f:
-            json.dump({"line": line, "shapes": shapes_report, "kernels": by_key}, f, indent=1)
+            json.dump({"line": line, "shapes": shapes, "kernels": kernels}, f, indent=1)
     print(json.dumps(line), flush=True)
 
 

@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
         L.w4_workspace_bytes.restype = sz
         L.w4_auto_path.argtypes = [ci, i64, i64, i64, sz, ctypes.POINTER(ci)]
         ip = ctypes.POINTER(ci)
-        L.w4_gemv_plan.argtypes = [ci, i64, i64, i64, ci, ip, ip, ip, ip]
+        L.w4_gemv_plan.argtypes = [ci, i64, i64, i64, ci, ip, ip, ip, ip, ip]
         L.w4_nf4_codebook.restype = ctypes.POINTER(ctypes.c_float)
         L.w4_status_string.argtypes = [ci]
         L.w4_status_string.restype = ctypes.c_char_p
@@ -192,11 +192,12 @@ def auto_path(fmt, n, k, b, workspace_bytes=0):
 
 
 def gemv_plan(fmt, n, k, b, split_k=1):
-    """dict(team, iters, chunks_per_split, grid_x) of the fused GEMV launch for these arguments."""
-    vals = [ctypes.c_int(0) for _ in range(4)]
+    """dict(threads, team, iters, chunks_per_split, grid_x) of the fused GEMV launch."""
+    vals = [ctypes.c_int(0) for _ in range(5)]
     r = lib().w4_gemv_plan(_fmt(fmt), n, k, b, split_k, *[ctypes.byref(v) for v in vals])
     check(r, "w4_gemv_plan")
-    return dict(zip(("team", "iters", "chunks_per_split", "grid_x"), (v.value for v in vals)))
+    return dict(zip(("threads", "team", "iters", "chunks_per_split", "grid_x"),
+                    (v.value for v in vals)))
 
 
 def matmul_ex(x, packed, scales, fmt, path="auto", split_k=0, workspace=None, y=None,

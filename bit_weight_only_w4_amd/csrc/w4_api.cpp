@@ -249,14 +249,15 @@ size_t w4_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b, int path, in
   }
 }
 
-int w4_gemv_plan(int fmt, int64_t n, int64_t k, int64_t b, int split_k, int* team, int* iters,
-                 int* chunks_per_split, int* grid_x) {
+int w4_gemv_plan(int fmt, int64_t n, int64_t k, int64_t b, int split_k, int* threads, int* team,
+                 int* iters, int* chunks_per_split, int* grid_x) {
   if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
   const int64_t g = fmt_group(fmt);
   if (n < 1 || k < g || k % g || b < 1 || b > W4_MAX_BATCH || n >= kMaxDim || k >= kMaxDim)
     return W4_ERR_SHAPE;
   GemvPlan p;
   if (b > kMaxGemvBatch || split_k < 1 || !plan_gemv(n, k, (int)b, split_k, &p)) return W4_ERR_PATH;
+  if (threads) *threads = p.threads;
   if (team) *team = p.team;
   if (iters) *iters = p.iters;
   if (chunks_per_split) *chunks_per_split = p.cps;

@@ -146,11 +146,11 @@ int w4_auto_path(int fmt, int64_t N, int64_t K, int64_t B, size_t workspace_byte
 /* ------------------------------------------------------------------ introspection --------- */
 
 /* Launch shape the fused GEMV uses for (fmt, N, K, B) over `split_k` K ranges (1 = single pass):
- * lanes per output row, 16-byte chunks per lane, chunks per split and workgroups along N.  Any
- * output pointer may be NULL.  Returns W4_OK, or W4_ERR_SHAPE / W4_ERR_PATH when the GEMV path
- * cannot run these arguments. */
-int w4_gemv_plan(int fmt, int64_t N, int64_t K, int64_t B, int split_k, int* team, int* iters,
-                 int* chunks_per_split, int* grid_x);
+ * threads per workgroup, lanes per output row, 16-byte chunks per lane, chunks per split and
+ * workgroups along N.  Any output pointer may be NULL.  Returns W4_OK, or W4_ERR_SHAPE /
+ * W4_ERR_PATH when the GEMV path cannot run these arguments. */
+int w4_gemv_plan(int fmt, int64_t N, int64_t K, int64_t B, int split_k, int* threads, int* team,
+                 int* iters, int* chunks_per_split, int* grid_x);
 
 /* Host pointer to the 16 NF4 code points (fp32, ascending) the kernels decode with.  Static
  * storage owned by the library; never NULL. */
