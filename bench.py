@@ -31,6 +31,8 @@ def parse_args():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--kernel-reps", type=int, default=50,
+                    help="graph replays per kernel class / shape kind when timing launches")
     ap.add_argument("--schedule", default="serial", choices=["serial", "dag"],
                     help="serial: one chain of 197 launches; dag: q|k|v and gate|up as branches")
     ap.add_argument("--report", default=None, help="write a detailed JSON report here")
@@ -333,8 +335,8 @@ def main():
         f"{total_bytes / 1e6:.1f} MB -> {step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
     log(f"[bench] step ({other}) {ms_other * 1e3:.1f} us -> {args.batch * 1e3 / ms_other:.1f} tok/s")
 
-    kernels = time_kernel_classes(step, dev)
-    shapes = time_shape_kinds(step, dev)
+    kernels = time_kernel_classes(step, dev, args.kernel_reps)
+    shapes = time_shape_kinds(step, dev, args.kernel_reps)
     for kind, r in shapes.items():
         log(f"[bench] {kind:8s} {r['n']:6d}x{r['k']:5d} {r['path']:6s} {r['us']:8.2f} us/launch "
             f"{r['gbs']:8.0f} GB/s  [{r['kernel']}]")

@@ -143,6 +143,7 @@ int run_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, 
   a.cps = p.cps;
   a.team = p.team;
   a.iters = p.iters;
+  a.nrb = (int)((n + p.threads / p.team - 1) / (p.threads / p.team));
   if (launch_gemv(fmt, (int)b, a, p, st) != hipSuccess) return W4_ERR_HIP;
   if (splits > 1) {
     if (launch_splitk_reduce(reinterpret_cast<const float*>(ws), y, b * n, splits, st) != hipSuccess)

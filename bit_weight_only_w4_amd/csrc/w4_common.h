@@ -55,6 +55,7 @@ struct GemvArgs {
   int cps;               // chunks per split
   int team;
   int iters;
+  int nrb;               // row blocks = ceil(N / (threads / team)), computed on the host
 };
 
 constexpr int kGemvMaxThreads = 512;

@@ -153,20 +153,24 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
   const int c0 = blockIdx.y * a.cps;
   const int nck = min(a.cps, a.cpr - c0);
   const int64_t n = a.n, k = a.k;
-  const int64_t nrb = (n + teams_per_wg - 1) / teams_per_wg;
-  const int64_t grid = gridDim.x;
-  const int64_t rb0 = blockIdx.x;  // < nrb: the host never launches more workgroups than blocks
-  const int64_t rb_last = rb0 + grid * ((nrb - 1 - rb0) / grid);
+  // 32-bit index arithmetic for row blocks (the host guarantees N < 2^31); one 32-bit division
+  // gives this workgroup's trip count.
+  const uint32_t nrb = (uint32_t)a.nrb;
+  const uint32_t grid = gridDim.x;
+  const uint32_t rb0 = blockIdx.x;  // < nrb: the host never launches more workgroups than blocks
+  const uint32_t count = (nrb - 1u - rb0) / grid + 1u;  // row blocks of this workgroup
+  const uint32_t rb_last = rb0 + grid * (count - 1u);
 
   // Chunk index of slot i for this lane, clamped into the split's range.
   auto chunk_of = [&](int i) {
     const int c = tl + (i << tshift);
     return c < nck ? c : nck - 1;
   };
-  auto load_rb = [&](int64_t rbv, uint4 (&p)[ITM], float (&s)[ITM]) {
+  auto load_rb = [&](uint32_t rbv, uint4 (&p)[ITM], float (&s)[ITM]) {
     rbv = rbv < rb_last ? rbv : rb_last;
-    int64_t row = rbv * teams_per_wg + team_id;
-    row = row < n ? row : n - 1;
+    uint32_t row32 = rbv * (uint32_t)teams_per_wg + (uint32_t)team_id;
+    row32 = row32 < (uint32_t)n ? row32 : (uint32_t)n - 1u;
+    const int64_t row = row32;
     const uint4* prow = reinterpret_cast<const uint4*>(a.packed + row * (k >> 1)) + c0;
 #pragma unroll
     for (int i = 0; i < ITM; ++i) {
@@ -209,7 +213,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
   const int wave = tid >> 6;
   const int waves_per_team = team > 64 ? team >> 6 : 1;
 
-  auto compute_store = [&](int64_t rbv, const uint4 (&pk)[ITM], const float (&sc)[ITM]) {
+  auto compute_store = [&](uint32_t rbv, const uint4 (&pk)[ITM], const float (&sc)[ITM]) {
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
@@ -258,7 +262,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
       }
     }
 
-    const int64_t row = rbv * teams_per_wg + team_id;
+    const int64_t row = (int64_t)rbv * teams_per_wg + team_id;
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = team_sum_wave(acc[b], team);
     float* out = a.out + (int64_t)blockIdx.y * B * n;
@@ -287,9 +291,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
 
   // --- main loop: three row blocks per trip, buffers rotating A -> B -> C, no early exit; the
   // last one or two row blocks are already loaded when the loop ends.
-  const int64_t count = (rb_last - rb0) / grid + 1;  // row blocks of this workgroup
-  int64_t rb = rb0;
-  int64_t t = 0;
+  uint32_t rb = rb0;
+  uint32_t t = 0;
   for (; t + 3 <= count; t += 3) {
     load_rb(rb + 2 * grid, pC, sC);
     compute_store(rb, pA, sA);
