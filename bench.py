@@ -31,6 +31,8 @@ def parse_args():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--suite", default="decode", choices=["decode", "shapes"],
+                    help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per kernel class / shape kind when timing launches")
     ap.add_argument("--schedule", default="serial", choices=["serial", "dag"],
@@ -304,8 +306,125 @@ def cpu_baseline(fmt, b, seconds):
     }
 
 
+def time_shape(fmt, n, k, b, path, split_k, dev, min_bytes=600 << 20, reps=5):
+    """Average launch time of one (format, N, K, B, path) over rotated weight copies (together
+    larger than the last-level cache, so the weights stream from HBM), as a HIP graph of launches
+    timed with events.  Returns (us per launch, None) or (None, error text)."""
+    import ctypes
+
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    wb = n * k // 2 + (n * k // 16 if fmt.startswith("nf4") else n * k // 64)
+    copies = max(1, min(4096, -(-min_bytes // wb)))
+    xdt = torch.float16 if fmt.endswith("_f16") else torch.bfloat16
+    gen = torch.Generator(device=dev).manual_seed(n * 31 + k)
+    mats = []
+    for c in range(copies):
+        w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+        mats.append(w4.quantize_nf4(w) if fmt.startswith("nf4") else w4.quantize_int4(w))
+        del w
+    x = torch.randn(b, k, generator=gen, device=dev).to(xdt)
+    y = torch.empty(b, n, device=dev)
+    wsb = w4.workspace_bytes(fmt, n, k, b, path, split_k) if path in ("splitk", "twopass") else 0
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    launches = max(copies, 16)
+    vp = ctypes.c_void_p
+    L = w4.lib()
+
+    def run(stream):
+        for r in range(launches):
+            p_, s_ = mats[r % copies]
+            st = L.w4_matmul_ex(vp(x.data_ptr()), vp(p_.data_ptr()), vp(s_.data_ptr()), w4.FORMATS[fmt],
+                                n, k, b, vp(y.data_ptr()), w4.PATHS[path], split_k,
+                                vp(ws.data_ptr()), ws.numel(), stream.cuda_stream)
+            if st != 0:
+                return w4.status_string(st)
+        return None
+
+    s0 = torch.cuda.Stream(device=dev)
+    s0.wait_stream(torch.cuda.current_stream())
+    err = run(s0)
+    torch.cuda.synchronize()
+    if err:
+        return None, err
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s0):
+        run(s0)
+    ms = time_replays(g, reps, 2)
+    del g, mats, ws
+    torch.cuda.empty_cache()
+    return ms * 1e3 / launches, None
+
+
+def shapes_suite(args, dev):
+    """Per-shape table for the other workloads: INT4 decode steps (B = 1, 8) and split-K vs one
+    pass on down; small-batch GEMM on gate / down / lm_head at B = 1, 8, 32, 128 for the GEMV,
+    MFMA and two-pass paths; the larger single-GPU model's shapes at B = 1, 4, 16."""
+    import synth_inputs
+
+    rows = []
+
+    def add(group, fmt, name, n, k, b, path, split_k=0):
+        us, err = time_shape(fmt, n, k, b, path, split_k, dev)
+        ab = algorithmic_bytes(fmt, n, k, b)
+        r = {"group": group, "fmt": fmt, "shape": name, "n": n, "k": k, "b": b, "path": path,
+             "split_k": split_k, "algorithmic_bytes": ab}
+        if us is None:
+            r["error"] = err
+        else:
+            r["us"] = round(us, 3)
+            r["gbs"] = round(ab / us / 1e3, 1)
+            r["frac_hbm"] = round(ab / us / 1e3 / HBM_PEAK_GBS, 4)
+            r["tflops"] = round(2.0 * n * k * b / us / 1e6, 2)
+        rows.append(r)
+        log(f"[shapes] {group:10s} {fmt:9s} {name:8s} {n:6d}x{k:5d} B={b:3d} {path:7s} S={split_k:2d} "
+            + (f"{r['us']:9.2f} us {r['gbs']:8.0f} GB/s {r['tflops']:7.2f} TFLOP/s" if us else f"ERR {err}"))
+
+    # INT4 g128, bf16 x: the five decode shapes at B = 1 and 8; split-K vs one pass on down
+    for b in (1, 8):
+        for name, n, k in (("q/o", 1536, 1536), ("k/v", 256, 1536), ("gate/up", 8960, 1536),
+                           ("down", 1536, 8960), ("lm_head", 151936, 1536)):
+            add("int4-step", "int4_bf16", name, n, k, b, "auto")
+        for sk in (2, 4, 8, 16):
+            add("int4-splitk", "int4_bf16", "down", 1536, 8960, b, "splitk", sk)
+    for sk in (2, 4, 8, 16):
+        add("nf4-splitk", "nf4_f16", "down", 1536, 8960, 1, "splitk", sk)
+    # NF4 fp16 small-batch GEMM: GEMV path (B <= 8), MFMA, two-pass
+    for name, n, k in (("gate", 8960, 1536), ("down", 1536, 8960), ("lm_head", 151936, 1536)):
+        for b in (1, 8, 32, 128):
+            if b <= 8:
+                add("nf4-gemm", "nf4_f16", name, n, k, b, "gemv")
+            add("nf4-gemm", "nf4_f16", name, n, k, b, "mfma")
+            add("nf4-gemm", "nf4_f16", name, n, k, b, "twopass")
+    # larger single-GPU model
+    for fmt in ("nf4_f16", "int4_f16"):
+        for name, n, k in synth_inputs.LARGE_SHAPES:
+            if name == "up":
+                continue
+            for b in (1, 4, 16):
+                add("large", fmt, name, n, k, b, "auto")
+    return rows
+
+
 def main():
     args = parse_args()
+    if args.suite == "shapes":
+        import torch
+
+        import bit_weight_only_w4_amd as w4
+
+        w4.lib()
+        dev = torch.device("cuda:0")
+        rows = shapes_suite(args, dev)
+        if args.report:
+            with open(args.report, "w") as f:
+                json.dump(rows, f, indent=1)
+        ok = [r for r in rows if "us" in r]
+        print(json.dumps({"metric": "per-shape fused W4 GEMV/GEMM table", "rows": len(rows),
+                          "measured": len(ok), "report": args.report}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
