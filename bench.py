@@ -38,6 +38,9 @@ def parse_args():
     ap.add_argument("--schedule", default="serial", choices=["serial", "dag"],
                     help="serial: one chain of 197 launches; dag: q|k|v and gate|up as branches")
     ap.add_argument("--report", default=None, help="write a detailed JSON report here")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="CPU only: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script into the stored per-kernel HBM traffic, then exit")
     return ap.parse_args()
 
 
@@ -109,15 +112,134 @@ class Step:
 
     def kernel_key(self, i):
         """Name of the kernel instantiation launch i runs (matches the profiler's kernel names)."""
-        name, n, k = self.shapes[i]
+        _, n, k = self.shapes[i]
         path, sk = self.plans[i]
-        if path in ("gemv", "splitk"):
-            plan = self.w4.gemv_plan(self.fmt, n, k, self.b, max(sk, 1))
-            fmt_i = 0 if self.fmt.startswith("nf4") else 1
-            xt = 0 if self.fmt.endswith("_f16") else 1
-            key = f"gemv_kernel<{fmt_i}, {xt}, {self.b}, {plan['iters']}, {plan['threads']}>"
-            return key + (f"+splitk_reduce(S={sk})" if path == "splitk" else "")
-        return path
+        return plan_kernel(self.w4, self.fmt, n, k, self.b, path, sk)[0]
+
+
+def plan_kernel(w4, fmt, n, k, b, path, sk):
+    """(kernel name, grid size in work-items) of one launch, from the library's own host-side plan.
+    Names match the profiler's kernel names; the grid size is the profiler's Grid_Size."""
+    if path in ("gemv", "splitk"):
+        plan = w4.gemv_plan(fmt, n, k, b, max(sk, 1))
+        fmt_i = 0 if fmt.startswith("nf4") else 1
+        xt = 0 if fmt.endswith("_f16") else 1
+        key = f"gemv_kernel<{fmt_i}, {xt}, {b}, {plan['iters']}, {plan['threads']}>"
+        if path == "splitk":
+            key += f"+splitk_reduce(S={sk})"
+        return key, plan["grid_x"] * plan["threads"]
+    return path, None
+
+
+def step_launch_mix(w4, fmt, b, path):
+    """Per launch of the decode step: (kernel name, grid work-items, algorithmic bytes).  Host-only:
+    the same path choice and plans as Step, without touching the GPU."""
+    import synth_inputs
+
+    shapes = synth_inputs.decode_step_shapes()
+    ws = max(w4.workspace_bytes(fmt, n, k, b, path) for _, n, k in shapes)
+    mix = []
+    for _, n, k in shapes:
+        ap, sk = w4.auto_path(fmt, n, k, b, ws) if path == "auto" else (path, 0)
+        key, grid = plan_kernel(w4, fmt, n, k, b, ap, sk)
+        mix.append((key, grid, algorithmic_bytes(fmt, n, k, b)))
+    return mix
+
+
+def kernel_source_digest():
+    """sha256 over the library's HIP/C++ sources and its build script: a stored counter reading
+    belongs to the kernels it was taken on and to nothing built since."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    pkg = os.path.join(root, "bit_weight_only_w4_amd")
+    h = hashlib.sha256()
+    files = [os.path.join("csrc", f) for f in sorted(os.listdir(os.path.join(pkg, "csrc")))]
+    for rel in files + ["build.py"]:
+        h.update(rel.encode())
+        with open(os.path.join(pkg, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(fmt, b, path):
+    root = os.path.dirname(os.path.abspath(__file__))
+    return os.path.join(root, "profiles", f"traffic_decode_{fmt}_b{b}_{path}.json")
+
+
+def traffic_from_counters(fetch_dir, write_dir, fmt, b, path, out):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, in KiB per
+    dispatch) into HBM bytes per launch for every kernel of the decode step.
+
+    Each counter is scaled by what it reads for the library's plain copy kernel (1 GiB read and
+    1 GiB written per dispatch, launched by the same run); per kernel, the readings are averaged
+    per grid size and weighted by how often the step launches that grid.  CPU-only."""
+    import collections
+    import csv
+
+    import bit_weight_only_w4_amd as w4
+
+    def load(d):
+        agg = collections.defaultdict(list)
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                agg[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return agg
+
+    def mean(v):
+        return sum(v) / len(v)
+
+    fetch, write = load(fetch_dir), load(write_dir)
+    copy_bytes = 1 << 30
+    cf = [v for (n, _), vs in fetch.items() if "probe_copy" in n for v in vs]
+    cw = [v for (n, _), vs in write.items() if "probe_copy" in n for v in vs]
+    if not cf or not cw:
+        raise SystemExit("traffic: the copy probe is missing from the counter runs")
+    f_fac = copy_bytes / (mean(cf) * 1024)
+    w_fac = copy_bytes / (mean(cw) * 1024)
+    mix = step_launch_mix(w4, fmt, b, path)
+    kernels = {}
+    for key in sorted({m[0] for m in mix}):
+        launches = [m for m in mix if m[0] == key]
+        tot_f = tot_w = 0.0
+        for _, grid, _ in launches:
+            fv = [v for (n, g), vs in fetch.items() if key in n and g == grid for v in vs]
+            wv = [v for (n, g), vs in write.items() if key in n and g == grid for v in vs]
+            if not fv or not wv:
+                raise SystemExit(f"traffic: no counter reading for {key} at grid {grid}")
+            tot_f += mean(fv) * 1024 * f_fac
+            tot_w += mean(wv) * 1024 * w_fac
+        cnt = len(launches)
+        kernels[key] = {"launches_per_step": cnt,
+                        "fetch_bytes": round(tot_f / cnt), "write_bytes": round(tot_w / cnt),
+                        "traffic_bytes": round((tot_f + tot_w) / cnt),
+                        "algorithmic_bytes": round(sum(m[2] for m in launches) / cnt)}
+        kernels[key]["traffic_over_algorithmic"] = round(
+            kernels[key]["traffic_bytes"] / kernels[key]["algorithmic_bytes"], 4)
+    rec = {"workload": f"decode step {fmt} batch {b} path {path}", "format": fmt, "batch": b,
+           "path": path, "sources_sha256": kernel_source_digest(),
+           "calibration": {"copy_bytes_per_dispatch": copy_bytes,
+                           "fetch_kib_per_copy": round(mean(cf), 3),
+                           "write_kib_per_copy": round(mean(cw), 3),
+                           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+           "kernels": kernels}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def stored_traffic(fmt, b, path, key):
+    """HBM bytes per launch of kernel `key` from the stored counter reading, or None when there is
+    none or the library's sources have changed since it was taken."""
+    p = traffic_path(fmt, b, path)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("sources_sha256") != kernel_source_digest() or key not in rec.get("kernels", {}):
+        return None
+    return rec["kernels"][key]["traffic_bytes"]
 
 
 def capture(step, dev, indices=None, schedule="serial"):
@@ -410,6 +532,12 @@ def shapes_suite(args, dev):
 
 def main():
     args = parse_args()
+    if args.traffic_from:
+        out = traffic_path(args.fmt, args.batch, args.path)
+        rec = traffic_from_counters(*args.traffic_from, args.fmt, args.batch, args.path, out)
+        print(json.dumps({"traffic": out, "kernels": {k: v["traffic_bytes"]
+                                                      for k, v in rec["kernels"].items()}}))
+        return
     if args.suite == "shapes":
         import torch
 
@@ -516,7 +644,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(args.fmt, args.batch, args.path, dom_key),
         },
         "cpu_baseline": cpu,
     }
