@@ -35,8 +35,10 @@ def parse_args():
                     help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per kernel class / shape kind when timing launches")
-    ap.add_argument("--schedule", default="serial", choices=["serial", "dag"],
-                    help="serial: one chain of 197 launches; dag: q|k|v and gate|up as branches")
+    ap.add_argument("--schedule", default="serial", choices=["serial", "grouped", "dag"],
+                    help="serial: one chain of 197 launches; grouped: one chain of 113 launches, "
+                         "q|k|v and gate|up each in one grouped launch; dag: 197 launches with "
+                         "q|k|v and gate|up as graph branches")
     ap.add_argument("--report", default=None, help="write a detailed JSON report here")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="CPU only: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
@@ -52,6 +54,27 @@ def algorithmic_bytes(fmt: str, n: int, k: int, b: int) -> int:
     """Bytes the method itself must move for one GEMV: packed weights + scales + x + y."""
     scale_bytes = n * k // 16 if fmt.startswith("nf4") else n * k // 64
     return n * k // 2 + scale_bytes + 2 * b * k + 4 * b * n
+
+
+GROUPS = {"q": ("q", "k", "v"), "gate": ("gate", "up")}  # projections that read the same x
+
+
+def step_units(shapes, schedule):
+    """Launch units of one step: tuples of GEMV indices that share one kernel launch.  "serial"
+    and "dag" launch every GEMV on its own; "grouped" launches a layer's q, k and v together and
+    its gate and up together (they read the same activations), 113 launches for the 197 GEMVs."""
+    if schedule != "grouped":
+        return [(i,) for i in range(len(shapes))]
+    units, i = [], 0
+    while i < len(shapes):
+        members = GROUPS.get(shapes[i][0].split(".")[-1])
+        if members and tuple(sh[0].split(".")[-1] for sh in shapes[i:i + len(members)]) == members:
+            units.append(tuple(range(i, i + len(members))))
+            i += len(members)
+        else:
+            units.append((i,))
+            i += 1
+    return units
 
 
 class Step:
@@ -100,21 +123,44 @@ class Step:
                               self.fmt_id, n, k, b, vp(y.data_ptr()), w4.PATHS[ap], sk,
                               vp(self.ws.data_ptr()), self.ws.numel()))
         self.bytes = [algorithmic_bytes(fmt, n, k, b) for _, n, k in self.shapes]
+        self.group_args = {}
 
     def launch(self, i, stream_handle):
         r = self.w4.lib().w4_matmul_ex(*self.args[i], stream_handle)
         if r != 0:
             self.w4.check(r, f"gemv {self.shapes[i][0]}")
 
-    def run(self, stream_handle):
-        for i in range(len(self.args)):
-            self.launch(i, stream_handle)
+    def launch_unit(self, unit, stream_handle):
+        if len(unit) == 1:
+            self.launch(unit[0], stream_handle)
+            return
+        if unit not in self.group_args:
+            k = self.shapes[unit[0]][2]
+            arrays = self.w4.grouped_args(self.x[k], [self.mats[i][0] for i in unit],
+                                          [self.mats[i][1] for i in unit],
+                                          [self.ys[i] for i in unit])
+            self.group_args[unit] = (self.args[unit[0]][0], len(unit)) + arrays + (
+                self.fmt_id, k, self.b)
+        r = self.w4.lib().w4_gemv_grouped(*self.group_args[unit], stream_handle)
+        if r != 0:
+            self.w4.check(r, f"grouped gemv {[self.shapes[i][0] for i in unit]}")
 
-    def kernel_key(self, i):
-        """Name of the kernel instantiation launch i runs (matches the profiler's kernel names)."""
-        _, n, k = self.shapes[i]
-        path, sk = self.plans[i]
-        return plan_kernel(self.w4, self.fmt, n, k, self.b, path, sk)[0]
+    def unit_key(self, unit):
+        """Name of the kernel instantiation a launch unit runs (the profiler's kernel names)."""
+        if len(unit) == 1:
+            _, n, k = self.shapes[unit[0]]
+            path, sk = self.plans[unit[0]]
+            return plan_kernel(self.w4, self.fmt, n, k, self.b, path, sk)[0]
+        n = sum(self.shapes[i][1] for i in unit)
+        return plan_kernel(self.w4, self.fmt, n, self.shapes[unit[0]][2], self.b, "gemv", 1)[0]
+
+    def unit_kind(self, unit):
+        return "|".join(self.shapes[i][0].split(".")[-1] for i in unit)
+
+    def unit_bytes(self, unit):
+        """Algorithmic bytes of one launch unit: every member's weights, scales and y, x once."""
+        x_bytes = 2 * self.b * self.shapes[unit[0]][2]
+        return sum(self.bytes[i] - x_bytes for i in unit) + x_bytes
 
 
 def plan_kernel(w4, fmt, n, k, b, path, sk):
@@ -131,18 +177,32 @@ def plan_kernel(w4, fmt, n, k, b, path, sk):
     return path, None
 
 
-def step_launch_mix(w4, fmt, b, path):
+def step_launch_mix(w4, fmt, b, path, schedule):
     """Per launch of the decode step: (kernel name, grid work-items, algorithmic bytes).  Host-only:
-    the same path choice and plans as Step, without touching the GPU."""
+    the same units, path choice and plans as Step, without touching the GPU."""
     import synth_inputs
 
     shapes = synth_inputs.decode_step_shapes()
     ws = max(w4.workspace_bytes(fmt, n, k, b, path) for _, n, k in shapes)
     mix = []
-    for _, n, k in shapes:
-        ap, sk = w4.auto_path(fmt, n, k, b, ws) if path == "auto" else (path, 0)
-        key, grid = plan_kernel(w4, fmt, n, k, b, ap, sk)
-        mix.append((key, grid, algorithmic_bytes(fmt, n, k, b)))
+    for unit in step_units(shapes, schedule):
+        k = shapes[unit[0]][2]
+        if len(unit) == 1:
+            n = shapes[unit[0]][1]
+            ap, sk = w4.auto_path(fmt, n, k, b, ws) if path == "auto" else (path, 0)
+            key, grid = plan_kernel(w4, fmt, n, k, b, ap, sk)
+            mix.append((key, grid, algorithmic_bytes(fmt, n, k, b)))
+        else:
+            ns = [shapes[i][1] for i in unit]
+            key, _ = plan_kernel(w4, fmt, sum(ns), k, b, "gemv", 1)
+            plan = w4.gemv_plan(fmt, sum(ns), k, b)
+            rows = plan["threads"] // plan["team"]
+            nrb = sum((n + rows - 1) // rows for n in ns)  # row blocks never span two members
+            full = (sum(ns) + rows - 1) // rows
+            # either the grid cap binds (and still does for nrb >= full), or every block gets one
+            grid = (plan["grid_x"] if plan["grid_x"] < full else nrb) * plan["threads"]
+            x_bytes = 2 * b * k
+            mix.append((key, grid, sum(algorithmic_bytes(fmt, n, k, b) - x_bytes for n in ns) + x_bytes))
     return mix
 
 
@@ -162,12 +222,12 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def traffic_path(fmt, b, path):
+def traffic_path(fmt, b, path, schedule):
     root = os.path.dirname(os.path.abspath(__file__))
-    return os.path.join(root, "profiles", f"traffic_decode_{fmt}_b{b}_{path}.json")
+    return os.path.join(root, "profiles", f"traffic_decode_{fmt}_b{b}_{path}_{schedule}.json")
 
 
-def traffic_from_counters(fetch_dir, write_dir, fmt, b, path, out):
+def traffic_from_counters(fetch_dir, write_dir, fmt, b, path, schedule, out):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, in KiB per
     dispatch) into HBM bytes per launch for every kernel of the decode step.
 
@@ -197,7 +257,7 @@ def traffic_from_counters(fetch_dir, write_dir, fmt, b, path, out):
         raise SystemExit("traffic: the copy probe is missing from the counter runs")
     f_fac = copy_bytes / (mean(cf) * 1024)
     w_fac = copy_bytes / (mean(cw) * 1024)
-    mix = step_launch_mix(w4, fmt, b, path)
+    mix = step_launch_mix(w4, fmt, b, path, schedule)
     kernels = {}
     for key in sorted({m[0] for m in mix}):
         launches = [m for m in mix if m[0] == key]
@@ -216,8 +276,9 @@ def traffic_from_counters(fetch_dir, write_dir, fmt, b, path, out):
                         "algorithmic_bytes": round(sum(m[2] for m in launches) / cnt)}
         kernels[key]["traffic_over_algorithmic"] = round(
             kernels[key]["traffic_bytes"] / kernels[key]["algorithmic_bytes"], 4)
-    rec = {"workload": f"decode step {fmt} batch {b} path {path}", "format": fmt, "batch": b,
-           "path": path, "sources_sha256": kernel_source_digest(),
+    rec = {"workload": f"decode step {fmt} batch {b} path {path} schedule {schedule}",
+           "format": fmt, "batch": b, "path": path, "schedule": schedule,
+           "sources_sha256": kernel_source_digest(),
            "calibration": {"copy_bytes_per_dispatch": copy_bytes,
                            "fetch_kib_per_copy": round(mean(cf), 3),
                            "write_kib_per_copy": round(mean(cw), 3),
@@ -229,10 +290,10 @@ def traffic_from_counters(fetch_dir, write_dir, fmt, b, path, out):
     return rec
 
 
-def stored_traffic(fmt, b, path, key):
+def stored_traffic(fmt, b, path, schedule, key):
     """HBM bytes per launch of kernel `key` from the stored counter reading, or None when there is
     none or the library's sources have changed since it was taken."""
-    p = traffic_path(fmt, b, path)
+    p = traffic_path(fmt, b, path, schedule)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -242,47 +303,45 @@ def stored_traffic(fmt, b, path, key):
     return rec["kernels"][key]["traffic_bytes"]
 
 
-def capture(step, dev, indices=None, schedule="serial"):
-    """Capture launches `indices` (default: the whole step) into one HIP graph.
+def capture(step, dev, units, schedule="serial"):
+    """Capture the launch units `units` (tuples of GEMV indices; see step_units) into one HIP graph.
 
-    schedule "serial": every launch depends on the previous one (one stream).
-    schedule "dag": the dependency structure of a real decode step -- q, k and v of a layer read
-    the same activations and run on three branches, gate and up on two, everything else in
-    order -- still one kernel launch per GEMV."""
+    "serial" and "grouped": every launch depends on the previous one (one stream).
+    "dag": the dependency structure of a real decode step -- q, k and v of a layer read the same
+    activations and run on three branches, gate and up on two, everything else in order -- still
+    one kernel launch per GEMV."""
     import torch
 
-    idx = list(range(len(step.args))) if indices is None else list(indices)
+    units = list(units)
     s0 = torch.cuda.Stream(device=dev)
     s0.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s0):
-        for i in idx:  # warm every launch once on the capture stream
-            step.launch(i, s0.cuda_stream)
+        for u in units:  # warm every launch once on the capture stream
+            step.launch_unit(u, s0.cuda_stream)
     torch.cuda.synchronize()
     side = [torch.cuda.Stream(device=dev) for _ in range(2)]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s0):
         pos = 0
-        while pos < len(idx):
-            i = idx[pos]
-            group = [i]
-            if schedule == "dag":
-                kind = step.shapes[i][0].split(".")[-1]
-                want = {"q": ["k", "v"], "gate": ["up"]}.get(kind, [])
-                while want and pos + len(group) < len(idx):
-                    j = idx[pos + len(group)]
-                    if step.shapes[j][0].split(".")[-1] != want[0]:
+        while pos < len(units):
+            group = [units[pos]]
+            if schedule == "dag" and len(units[pos]) == 1:
+                want = list(GROUPS.get(step.shapes[units[pos][0]][0].split(".")[-1], ())[1:])
+                while want and pos + len(group) < len(units):
+                    nxt = units[pos + len(group)]
+                    if len(nxt) != 1 or step.shapes[nxt[0]][0].split(".")[-1] != want[0]:
                         break
-                    group.append(j)
+                    group.append(nxt)
                     want.pop(0)
             if len(group) == 1:
-                step.launch(i, s0.cuda_stream)
+                step.launch_unit(group[0], s0.cuda_stream)
             else:
                 fork = torch.cuda.Event()
                 fork.record(s0)
-                for b, j in enumerate(group[1:]):
+                for b, u in enumerate(group[1:]):
                     side[b].wait_event(fork)
-                    step.launch(j, side[b].cuda_stream)
-                step.launch(group[0], s0.cuda_stream)
+                    step.launch_unit(u, side[b].cuda_stream)
+                step.launch_unit(group[0], s0.cuda_stream)
                 for b in range(len(group) - 1):
                     join = torch.cuda.Event()
                     join.record(side[b])
@@ -310,37 +369,38 @@ def time_replays(graph, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-def time_kernel_classes(step, dev, reps=50):
+def time_kernel_classes(step, dev, units, reps=50):
     """Average launch time of every kernel instantiation the step uses, measured the way the step
     runs: a graph holding only that kernel's launches, in step order, timed with HIP events over
     `reps` replays.  Returns {kernel: {"launches", "us", "bytes"}} per step."""
     classes = {}
-    for i in range(len(step.args)):
-        classes.setdefault(step.kernel_key(i), []).append(i)
+    for u in units:
+        classes.setdefault(step.unit_key(u), []).append(u)
     out = {}
-    for key, idx in classes.items():
-        g = capture(step, dev, idx, "serial")
+    for key, us in classes.items():
+        g = capture(step, dev, us, "serial")
         ms = time_replays(g, reps, 5)
-        out[key] = {"launches": len(idx), "us": ms * 1e3 / len(idx),
-                    "bytes": sum(step.bytes[i] for i in idx) / len(idx)}
+        out[key] = {"launches": len(us), "us": ms * 1e3 / len(us),
+                    "bytes": sum(step.unit_bytes(u) for u in us) / len(us)}
         del g
     return out
 
 
-def time_shape_kinds(step, dev, reps=50):
-    """Average launch time per projection kind (q, k, ..., lm_head) inside the step, from a graph
-    of that kind's launches only."""
+def time_shape_kinds(step, dev, units, reps=50):
+    """Average launch time per launch kind (q, k, ..., lm_head, or q|k|v and gate|up when grouped)
+    inside the step, from a graph of that kind's launches only."""
     kinds = {}
-    for i, (name, _, _) in enumerate(step.shapes):
-        kinds.setdefault(name.split(".")[-1], []).append(i)
+    for u in units:
+        kinds.setdefault(step.unit_kind(u), []).append(u)
     out = {}
-    for kind, idx in kinds.items():
-        g = capture(step, dev, idx, "serial")
+    for kind, us in kinds.items():
+        g = capture(step, dev, us, "serial")
         ms = time_replays(g, reps, 5)
-        _, n, k = step.shapes[idx[0]]
-        out[kind] = {"n": n, "k": k, "count": len(idx), "us": ms * 1e3 / len(idx),
-                     "bytes": step.bytes[idx[0]], "path": step.plans[idx[0]][0],
-                     "kernel": step.kernel_key(idx[0])}
+        u0 = us[0]
+        out[kind] = {"n": sum(step.shapes[i][1] for i in u0), "k": step.shapes[u0[0]][2],
+                     "count": len(us), "us": ms * 1e3 / len(us), "bytes": step.unit_bytes(u0),
+                     "path": "grouped" if len(u0) > 1 else step.plans[u0[0]][0],
+                     "kernel": step.unit_key(u0)}
         out[kind]["gbs"] = out[kind]["bytes"] / (out[kind]["us"] / 1e6) / 1e9
         del g
     return out
@@ -533,8 +593,9 @@ def shapes_suite(args, dev):
 def main():
     args = parse_args()
     if args.traffic_from:
-        out = traffic_path(args.fmt, args.batch, args.path)
-        rec = traffic_from_counters(*args.traffic_from, args.fmt, args.batch, args.path, out)
+        out = traffic_path(args.fmt, args.batch, args.path, args.schedule)
+        rec = traffic_from_counters(*args.traffic_from, args.fmt, args.batch, args.path,
+                                    args.schedule, out)
         print(json.dumps({"traffic": out, "kernels": {k: v["traffic_bytes"]
                                                       for k, v in rec["kernels"].items()}}))
         return
@@ -569,23 +630,25 @@ def main():
     step = Step(args.fmt, args.batch, args.path, dev)
     total_bytes = sum(step.bytes)
 
-    other = "dag" if args.schedule == "serial" else "serial"
-    g_main = capture(step, dev, None, args.schedule)
-    ms = time_replays(g_main, args.steps, args.warmup)
-    del g_main
-    g_other = capture(step, dev, None, other)
-    ms_other = time_replays(g_other, args.steps, args.warmup)
-    del g_other
+    # every schedule of the same 197 GEMVs, the selected one first
+    timed = {}
+    for sched in [args.schedule] + [x for x in ("serial", "grouped", "dag") if x != args.schedule]:
+        g = capture(step, dev, step_units(step.shapes, sched), sched)
+        timed[sched] = time_replays(g, args.steps, args.warmup)
+        del g
+        log(f"[bench] step ({sched}) {timed[sched] * 1e3:.1f} us -> "
+            f"{args.batch * 1e3 / timed[sched]:.1f} tok/s")
+    ms = timed[args.schedule]
     tok_s = args.batch * 1e3 / ms
     step_gbs = total_bytes / (ms / 1e3) / 1e9
-    log(f"[bench] step ({args.schedule}) {ms * 1e3:.1f} us -> {tok_s:.1f} tok/s; algorithmic "
-        f"{total_bytes / 1e6:.1f} MB -> {step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
-    log(f"[bench] step ({other}) {ms_other * 1e3:.1f} us -> {args.batch * 1e3 / ms_other:.1f} tok/s")
+    log(f"[bench] selected {args.schedule}: algorithmic {total_bytes / 1e6:.1f} MB -> "
+        f"{step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
 
-    kernels = time_kernel_classes(step, dev, args.kernel_reps)
-    shapes = time_shape_kinds(step, dev, args.kernel_reps)
+    units = step_units(step.shapes, args.schedule)
+    kernels = time_kernel_classes(step, dev, units, args.kernel_reps)
+    shapes = time_shape_kinds(step, dev, units, args.kernel_reps)
     for kind, r in shapes.items():
-        log(f"[bench] {kind:8s} {r['n']:6d}x{r['k']:5d} {r['path']:6s} {r['us']:8.2f} us/launch "
+        log(f"[bench] {kind:10s} {r['n']:6d}x{r['k']:5d} {r['path']:7s} {r['us']:8.2f} us/launch "
             f"{r['gbs']:8.0f} GB/s  [{r['kernel']}]")
     for key, d in sorted(kernels.items(), key=lambda kv: -kv[1]["us"] * kv[1]["launches"]):
         log(f"[bench] kernel {key}: {d['launches']} launches/step, {d['us']:.2f} us/launch, "
@@ -617,16 +680,18 @@ def main():
         "dtype": "f16" if args.fmt.endswith("_f16") else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"Qwen2.5-1.5B decode step: 197 distinct GEMV launches (28x q,k,v,o,gate,"
-                         f"up,down + lm_head), {wfmt} "
+            "workload": (f"Qwen2.5-1.5B decode step: 197 distinct GEMVs (28x q,k,v,o,gate,"
+                         f"up,down + lm_head) in {len(units)} launches, {wfmt} "
                          f"{'bs64 fp32 absmax' if wfmt == 'NF4' else 'g128 bf16 scale'}, "
                          f"{args.fmt.split('_')[1]} x, batch {args.batch}, fp32 accumulate/output"),
             "format": args.fmt,
             "batch": args.batch,
             "path": args.path,
             "schedule": args.schedule,
-            "other_schedule": {other: {"ms_per_step": round(ms_other, 5),
-                                       "tok_s": round(args.batch * 1e3 / ms_other, 2)}},
+            "launches_per_step": len(units),
+            "other_schedule": {sc: {"ms_per_step": round(t, 5),
+                                    "tok_s": round(args.batch * 1e3 / t, 2)}
+                               for sc, t in timed.items() if sc != args.schedule},
             "algorithmic_bytes_per_step": total_bytes,
             "step_gbs": round(step_gbs, 1),
             "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
@@ -644,7 +709,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(args.fmt, args.batch, args.path, dom_key),
+            "traffic": stored_traffic(args.fmt, args.batch, args.path, args.schedule, dom_key),
         },
         "cpu_baseline": cpu,
     }

@@ -60,10 +60,13 @@ def lib() -> ctypes.CDLL:
         L.w4_nf4_codebook.restype = ctypes.POINTER(ctypes.c_float)
         L.w4_status_string.argtypes = [ci]
         L.w4_status_string.restype = ctypes.c_char_p
+        vpp = ctypes.POINTER(vp)
+        L.w4_gemv_grouped.argtypes = [vp, ci, vpp, vpp, ctypes.POINTER(i64), vpp, ci, i64, i64, vp]
         L.w4_probe_read.argtypes = [vp, sz, vp, vp]
         L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
         for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_gemv", "w4_gemm_smallbatch",
-                     "w4_matmul_ex", "w4_auto_path", "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy"):
+                     "w4_matmul_ex", "w4_auto_path", "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
+                     "w4_gemv_grouped"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -163,6 +166,34 @@ def gemv(x, packed, scales, fmt, y=None, stream=None):
     check(lib().w4_gemv(_ptr(x), _ptr(packed), _ptr(scales), _fmt(fmt), n, k, b, _ptr(y),
                         _stream(stream)), "w4_gemv")
     return y
+
+
+def grouped_args(x, packed, scales, ys):
+    """ctypes arrays for w4_gemv_grouped: (packed**, scales**, N*, y**) over the members."""
+    g = len(packed)
+    vp = ctypes.c_void_p
+    return ((vp * g)(*[p.data_ptr() for p in packed]), (vp * g)(*[s.data_ptr() for s in scales]),
+            (ctypes.c_int64 * g)(*[p.shape[0] for p in packed]),
+            (vp * g)(*[y.data_ptr() for y in ys]))
+
+
+def gemv_grouped(x, packed, scales, fmt, ys=None, stream=None):
+    """[y_g] = [x . W_hat_g^T] for weight matrices that share x, in one fused-GEMV launch.
+    packed / scales are equal-length lists (at most 4 members); returns the list of y_g [B, N_g]."""
+    import torch
+
+    if len(packed) != len(scales) or (ys is not None and len(ys) != len(packed)):
+        raise ValueError("packed, scales and ys must have one entry per member")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    b, k = x.shape
+    if ys is None:
+        ys = [torch.empty((b, p.shape[0]), dtype=torch.float32, device=x.device) for p in packed]
+    _need_cuda(x, *packed, *scales, *ys)
+    pp, sp, n, yp = grouped_args(x, packed, scales, ys)
+    check(lib().w4_gemv_grouped(_ptr(x), len(packed), pp, sp, n, yp, _fmt(fmt), k, b,
+                                _stream(stream)), "w4_gemv_grouped")
+    return ys
 
 
 def gemm_smallbatch(x, packed, scales, fmt, y=None, stream=None):

@@ -17,8 +17,10 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw4.so")
 SOURCES = ["w4_api.cpp", "w4_gemv.hip", "w4_gemv_nf4_f16.hip", "w4_gemv_nf4_bf16.hip",
-           "w4_gemv_int4_f16.hip", "w4_gemv_int4_bf16.hip", "w4_quant.hip", "w4_twopass.hip",
-           "w4_mfma.hip", "w4_probe.hip"]
+           "w4_gemv_int4_f16.hip", "w4_gemv_int4_bf16.hip", "w4_gemv_nf4_f16_grouped.hip",
+           "w4_gemv_nf4_bf16_grouped.hip", "w4_gemv_int4_f16_grouped.hip",
+           "w4_gemv_int4_bf16_grouped.hip", "w4_quant.hip", "w4_twopass.hip", "w4_mfma.hip",
+           "w4_probe.hip"]
 ARCH = "gfx950"
 
 

@@ -86,12 +86,15 @@ int next_pow2(int v) {
 //    blocks, which keeps the per-lane activation footprint and the number of table fills small;
 //  * at most two workgroups fit in one CU (64 KiB decode table each), so grids beyond two per CU
 //    only queue.
-bool plan_gemv(int64_t n, int64_t k, int b, int splits, GemvPlan* out) {
+bool plan_gemv(int64_t n, int64_t k, int b, int splits, GemvPlan* out, bool grouped = false) {
   const int cpr = (int)(k / 32);
   if (splits < 1 || splits > cpr) return false;
+  // The kernel addresses a row block, the activations and their scales with 32-bit byte offsets
+  // inside range-checked buffer resources: keep 32 rows of packed bytes below 2^31.
+  if (k >= ((int64_t)1 << 26)) return false;
   const int cps = (cpr + splits - 1) / splits;
   if ((int64_t)(splits - 1) * cps >= cpr) return false;  // every split must own a chunk
-  const int itmax = gemv_max_iters(b);
+  const int itmax = gemv_max_iters(b, grouped);
   const bool large = (n * (k / 2)) / splits >= ((int64_t)64 << 20);
   int team;
   if (large) {
@@ -115,6 +118,7 @@ bool plan_gemv(int64_t n, int64_t k, int b, int splits, GemvPlan* out) {
   const int64_t nrb = (n + rows_per_wg - 1) / rows_per_wg;
   const int64_t cus = device_cu_count();
   const int64_t cap = std::max<int64_t>(1, (large ? cus : 2 * cus) / splits);
+  p.cap = (int)cap;
   p.grid_x = (int)std::min<int64_t>(nrb, cap);
   *out = p;
   return true;
@@ -128,28 +132,51 @@ int auto_splits(int64_t, int64_t, int) { return 1; }
 
 size_t splitk_bytes(int64_t n, int64_t b, int s) { return (size_t)s * (size_t)b * (size_t)n * 4; }
 
-int run_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
-             int64_t k, int64_t b, float* y, int splits, void* ws, hipStream_t st) {
+// One fused-GEMV launch over `groups` members that share x and K (splits > 1 only for a single
+// member), then the split-K reduction if any.
+int run_gemv_members(const void* x, int groups, const uint8_t* const* packed,
+                     const void* const* scales, const int64_t* n, float* const* y, int fmt,
+                     int64_t k, int64_t b, int splits, void* ws, hipStream_t st) {
+  int64_t n_total = 0;
+  for (int g = 0; g < groups; ++g) n_total += n[g];
   GemvPlan p;
-  if (b > kMaxGemvBatch || !plan_gemv(n, k, (int)b, splits, &p)) return W4_ERR_PATH;
+  if (b > kMaxGemvBatch || !plan_gemv(n_total, k, (int)b, splits, &p, groups > 1)) return W4_ERR_PATH;
+  const int64_t rows_per_wg = p.threads / p.team;
   GemvArgs a;
+  memset(&a, 0, sizeof(a));
   a.x = reinterpret_cast<const uint16_t*>(x);
-  a.packed = packed;
-  a.scales = scales;
-  a.out = splits == 1 ? y : reinterpret_cast<float*>(ws);
-  a.n = n;
+  int64_t nrb_sum = 0, nrb_max = 0;
+  for (int g = 0; g < groups; ++g) {
+    const int64_t nrb = (n[g] + rows_per_wg - 1) / rows_per_wg;
+    a.m[g].packed = packed[g];
+    a.m[g].scales = scales[g];
+    a.m[g].out = splits == 1 ? y[g] : reinterpret_cast<float*>(ws);
+    a.m[g].n = (uint32_t)n[g];
+    a.m[g].nrb = (uint32_t)nrb;
+    nrb_sum += nrb;
+    nrb_max = std::max(nrb_max, nrb);
+  }
   a.k = k;
   a.cpr = (int)(k / 32);
   a.cps = p.cps;
   a.team = p.team;
   a.iters = p.iters;
-  a.nrb = (int)((n + p.threads / p.team - 1) / (p.threads / p.team));
-  if (launch_gemv(fmt, (int)b, a, p, st) != hipSuccess) return W4_ERR_HIP;
+  // Workgroups along x per member: the largest member's share of the cap, so that the grid as a
+  // whole stays within the cap; smaller members leave their surplus workgroups idle.
+  const int64_t share = std::max<int64_t>(1, (p.cap * nrb_max + nrb_sum - 1) / nrb_sum);
+  p.grid_x = (int)std::min<int64_t>(nrb_max, share);
+  if (launch_gemv(fmt, (int)b, a, groups, p, st) != hipSuccess) return W4_ERR_HIP;
   if (splits > 1) {
-    if (launch_splitk_reduce(reinterpret_cast<const float*>(ws), y, b * n, splits, st) != hipSuccess)
+    if (launch_splitk_reduce(reinterpret_cast<const float*>(ws), y[0], b * n[0], splits, st) !=
+        hipSuccess)
       return W4_ERR_HIP;
   }
   return W4_OK;
+}
+
+int run_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+             int64_t k, int64_t b, float* y, int splits, void* ws, hipStream_t st) {
+  return run_gemv_members(x, 1, &packed, &scales, &n, &y, fmt, k, b, splits, ws, st);
 }
 
 int run_twopass(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
@@ -335,6 +362,43 @@ int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, i
   GemvPlan p;
   if (!plan_gemv(n, k, (int)b, 1, &p)) return run_mfma(x, packed, scales, fmt, n, k, b, y, s);
   return run_gemv(x, packed, scales, fmt, n, k, b, y, 1, nullptr, s);
+}
+
+int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
+                    const void* const* scales, const int64_t* n, float* const* y, int fmt,
+                    int64_t k, int64_t b, void* stream) {
+  if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
+  if (groups < 1 || groups > W4_MAX_GROUP) return W4_ERR_SHAPE;
+  if (!packed || !scales || !n || !y) return W4_ERR_NULL;
+  int64_t n_total = 0;
+  for (int g = 0; g < groups; ++g) {
+    const int st = validate(x, packed[g], scales[g], fmt, n[g], k, b, y[g]);
+    if (st != W4_OK) return st;
+    n_total += n[g];
+  }
+  if (n_total >= kMaxDim) return W4_ERR_SHAPE;
+  if (b > kMaxGemvBatch) return W4_ERR_SHAPE;
+  const size_t sdiv = (size_t)fmt_group(fmt), ssz = fmt_weight(fmt) == kNF4 ? 4 : 2;
+  for (int g = 0; g < groups; ++g) {
+    const size_t yb = (size_t)(b * n[g]) * 4;
+    for (int h = 0; h < groups; ++h) {
+      if (h == g) continue;
+      if (overlaps(y[g], yb, y[h], (size_t)(b * n[h]) * 4) ||
+          overlaps(y[g], yb, packed[h], (size_t)(n[h] * k / 2)) ||
+          overlaps(y[g], yb, scales[h], (size_t)(n[h] * (k / (int64_t)sdiv)) * ssz))
+        return W4_ERR_ALIAS;
+    }
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  GemvPlan p;
+  if (!plan_gemv(n_total, k, (int)b, 1, &p, groups > 1)) {  // no GEMV shape: MFMA per member
+    for (int g = 0; g < groups; ++g) {
+      const int st = run_mfma(x, packed[g], scales[g], fmt, n[g], k, b, y[g], s);
+      if (st != W4_OK) return st;
+    }
+    return W4_OK;
+  }
+  return run_gemv_members(x, groups, packed, scales, n, y, fmt, k, b, 1, nullptr, s);
 }
 
 int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,

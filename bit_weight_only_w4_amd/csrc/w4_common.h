@@ -27,6 +27,51 @@ __device__ inline uint4 load_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer-resource loads.  A raw buffer resource (base, byte size) makes the hardware range-check
+// every access: a load at an offset past the size returns zero and issues no memory request, so
+// prefetches of row blocks that do not exist and lanes with no chunk to read cost nothing and need
+// no branch.  Word 3 is the gfx9 raw-buffer configuration (32-bit data, no swizzle).
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;  // past every resource the kernels build
+
+// `off` for lanes that `have` their element, else an offset past the resource.  The select is
+// computed as a value (kept opaque to the optimizer) so that the load after it stays a single,
+// unconditional instruction: split into branches it would force a wait for all loads in flight.
+__device__ inline uint32_t offset_or_oob(bool have, uint32_t off) {
+  uint32_t r = have ? off : kOutOfRange;
+  asm volatile("" : "+v"(r));
+  return r;
+}
+
+// `base` and `bytes` must be uniform over the wave; readfirstlane states that to the compiler,
+// which otherwise may not prove it and wraps every load in a loop over distinct resources.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t n = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                           (short)0, (int)n, 0x00020000);
+}
+
+// 16 bytes, non-temporal (streamed once).
+__device__ inline uint4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline uint32_t buffer_load32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+__device__ inline uint32_t buffer_load16bit(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 enum Fmt { kNF4 = 0, kINT4 = 1 };
 enum XType { kF16 = 0, kBF16 = 1 };
 
@@ -34,38 +79,60 @@ inline int fmt_weight(int fmt) { return (fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_
 inline int fmt_xtype(int fmt) { return (fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16) ? kF16 : kBF16; }
 inline int64_t fmt_group(int fmt) { return fmt_weight(fmt) == kNF4 ? 64 : 128; }
 
-// Shape of one fused-GEMV launch (host-chosen; see choose_gemv in w4_api.cpp).
+// Shape of one fused-GEMV launch (host-chosen; see plan_gemv in w4_api.cpp).
 struct GemvPlan {
-  int threads;  // threads per workgroup (64, 128, 256 or 512)
+  int threads;  // threads per workgroup (256 or 512)
   int team;     // lanes that share one output row (16..512, power of two, <= threads)
   int iters;    // 16-byte chunks each lane streams per row (<= the instantiated maximum)
   int splits;   // number of disjoint K ranges (grid.y); 1 = single pass
   int cps;      // chunks per split
   int grid_x;   // workgroups along the row dimension
+  int cap;      // largest useful grid_x for this shape class (grid_x = min(row blocks, cap))
 };
 
-struct GemvArgs {
-  const uint16_t* x;     // [B, K] activations (bits)
-  const uint8_t* packed; // [N, K/2]
-  const void* scales;    // NF4 float[N, K/64] | INT4 uint16[N, K/128]
-  float* out;            // y [B, N] (splits == 1) or partials [splits, B, N]
-  int64_t n;
+// Matrices of one launch.  A launch covers 1..kMaxGroup weight matrices ("members") that share
+// the activations x and K.  Member g is processed by the workgroups with blockIdx.z == g, which
+// walk its row blocks grid-stride along x.
+constexpr int kMaxGroup = W4_MAX_GROUP;
+
+struct GemvMember {
+  const uint8_t* packed;  // [N_g, K/2]
+  const void* scales;     // NF4 float[N_g, K/64] | INT4 uint16[N_g, K/128]
+  float* out;             // y [B, N_g] (splits == 1) or partials [splits, B, N_g]
+  uint32_t n;             // rows N_g
+  uint32_t nrb;           // row blocks of this member = ceil(N_g / rows per workgroup)
+};
+
+// Kernel arguments for launches of up to G members (the single-member kernels take G = 1, which
+// keeps their argument block at 64 contiguous bytes: the prologue fetches it with one batch of
+// scalar loads; a layout that made the compiler split the fetch into two dependent batches cost
+// ~0.2 us per launch).
+template <int G>
+struct GemvArgsT {
+  GemvMember m[G];
+  const uint16_t* x;  // [B, K] activations (bits), shared by every member
   int64_t k;
-  int cpr;               // 16-byte chunks per row = K / 32
-  int cps;               // chunks per split
+  int cpr;            // 16-byte chunks per row = K / 32
+  int cps;            // chunks per split
   int team;
   int iters;
-  int nrb;               // row blocks = ceil(N / (threads / team)), computed on the host
 };
+using GemvArgs = GemvArgsT<kMaxGroup>;
 
 constexpr int kGemvMaxThreads = 512;
 constexpr int kMaxGemvBatch = 8;
 
 // Largest per-lane chunk count instantiated for batch b (x is held in registers:
-// 16 dwords per chunk per batch row).
-inline int gemv_max_iters(int b) { return b == 1 ? 8 : b == 2 ? 4 : b <= 4 ? 2 : 1; }
+// 16 dwords per chunk per batch row).  Grouped launches (several members) are instantiated up to
+// 4 chunks per lane, rows of up to 64 Ki weights at 512 lanes per row.
+constexpr int gemv_max_iters(int b, bool grouped) {
+  return b == 1 ? (grouped ? 4 : 8) : b == 2 ? 4 : b <= 4 ? 2 : 1;
+}
 
-hipError_t launch_gemv(int fmt, int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s);
+// One fused-GEMV launch over `groups` members (a.m[0 .. groups-1]); groups > 1 selects the grouped
+// kernels, launched with grid.z = groups.
+hipError_t launch_gemv(int fmt, int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                       hipStream_t s);
 hipError_t launch_splitk_reduce(const float* partial, float* y, int64_t count, int splits,
                                 hipStream_t s);
 hipError_t launch_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* packed,

@@ -3,10 +3,22 @@
 
 namespace w4 {
 
-hipError_t launch_gemv_nf4_f16(int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s);
-hipError_t launch_gemv_nf4_bf16(int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s);
-hipError_t launch_gemv_int4_f16(int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s);
-hipError_t launch_gemv_int4_bf16(int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s);
+hipError_t launch_gemv_nf4_f16(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                               hipStream_t s);
+hipError_t launch_gemv_nf4_bf16(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                hipStream_t s);
+hipError_t launch_gemv_int4_f16(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                hipStream_t s);
+hipError_t launch_gemv_int4_bf16(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                 hipStream_t s);
+hipError_t launch_gemv_nf4_f16_grouped(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                       hipStream_t s);
+hipError_t launch_gemv_nf4_bf16_grouped(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                        hipStream_t s);
+hipError_t launch_gemv_int4_f16_grouped(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                        hipStream_t s);
+hipError_t launch_gemv_int4_bf16_grouped(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                         hipStream_t s);
 
 namespace {
 
@@ -24,12 +36,22 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ partial, float* _
 
 }  // namespace
 
-hipError_t launch_gemv(int fmt, int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
+hipError_t launch_gemv(int fmt, int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                       hipStream_t s) {
+  if (groups > 1) {
+    switch (fmt) {
+      case W4_NF4_X_F16: return launch_gemv_nf4_f16_grouped(b, a, groups, p, s);
+      case W4_NF4_X_BF16: return launch_gemv_nf4_bf16_grouped(b, a, groups, p, s);
+      case W4_INT4_X_F16: return launch_gemv_int4_f16_grouped(b, a, groups, p, s);
+      case W4_INT4_X_BF16: return launch_gemv_int4_bf16_grouped(b, a, groups, p, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (fmt) {
-    case W4_NF4_X_F16: return launch_gemv_nf4_f16(b, a, p, s);
-    case W4_NF4_X_BF16: return launch_gemv_nf4_bf16(b, a, p, s);
-    case W4_INT4_X_F16: return launch_gemv_int4_f16(b, a, p, s);
-    case W4_INT4_X_BF16: return launch_gemv_int4_bf16(b, a, p, s);
+    case W4_NF4_X_F16: return launch_gemv_nf4_f16(b, a, groups, p, s);
+    case W4_NF4_X_BF16: return launch_gemv_nf4_bf16(b, a, groups, p, s);
+    case W4_INT4_X_F16: return launch_gemv_int4_f16(b, a, groups, p, s);
+    case W4_INT4_X_BF16: return launch_gemv_int4_bf16(b, a, groups, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -128,18 +128,24 @@ __device__ inline float team_sum_wave(float v, int team) {
   return v;
 }
 
+// Bytes of one row's scales, and the byte offset of chunk `chunk`'s scale within the row.
 template <int FMT>
-__device__ inline float load_scale(const void* scales, int64_t row, int64_t k, int chunk) {
-  if (FMT == kNF4) {
-    return reinterpret_cast<const float*>(scales)[row * (k >> 6) + (chunk >> 1)];
-  } else {
-    const uint16_t s = reinterpret_cast<const uint16_t*>(scales)[row * (k >> 7) + (chunk >> 2)];
-    return __uint_as_float((uint32_t)s << 16);
-  }
+__device__ inline uint32_t scale_pitch(int64_t k) {
+  return FMT == kNF4 ? (uint32_t)(k >> 6) * 4u : (uint32_t)(k >> 7) * 2u;
+}
+template <int FMT>
+__device__ inline uint32_t scale_offset(int chunk) {
+  return FMT == kNF4 ? (uint32_t)(chunk >> 1) * 4u : (uint32_t)(chunk >> 2) * 2u;
+}
+template <int FMT>
+__device__ inline float load_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if (FMT == kNF4) return __uint_as_float(buffer_load32(r, off));
+  return __uint_as_float(buffer_load16bit(r, off) << 16);  // bf16 bits -> fp32, exact
 }
 
-template <int FMT, int XT, int B, int ITM, int NT>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) gemv_kernel(GemvArgs a) {
+template <int FMT, int XT, int B, int ITM, int NT, bool GROUPED>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
+gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
   __shared__ float xwave[NT / 64][B];
 
@@ -152,31 +158,56 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
   const int teams_per_wg = NT >> tshift;
   const int c0 = blockIdx.y * a.cps;
   const int nck = min(a.cps, a.cpr - c0);
-  const int64_t n = a.n, k = a.k;
+  const int64_t k = a.k;
+  // This workgroup's member (grouped launches: one member per blockIdx.z).
+  const GemvMember mm = a.m[GROUPED ? blockIdx.z : 0];
   // 32-bit index arithmetic for row blocks (the host guarantees N < 2^31); one 32-bit division
   // gives this workgroup's trip count.
-  const uint32_t nrb = (uint32_t)a.nrb;
+  const uint32_t nrb = mm.nrb;
   const uint32_t grid = gridDim.x;
-  const uint32_t rb0 = blockIdx.x;  // < nrb: the host never launches more workgroups than blocks
-  const uint32_t count = (nrb - 1u - rb0) / grid + 1u;  // row blocks of this workgroup
-  const uint32_t rb_last = rb0 + grid * (count - 1u);
+  const uint32_t rb0 = blockIdx.x;
+  // Row blocks of this workgroup: none when its member is smaller than the grid is wide (grouped
+  // launches).  Such a workgroup still runs the prologue with every load out of range, rather
+  // than branching out early: an early exit would make the prologue wait for the member
+  // descriptor before fetching the rest of its arguments.
+  const uint32_t count = rb0 < nrb ? (nrb - 1u - rb0) / grid + 1u : 0u;
+  const uint32_t rb_last = count ? rb0 + grid * (count - 1u) : rb0;
 
-  // Chunk index of slot i for this lane, clamped into the split's range.
-  auto chunk_of = [&](int i) {
-    const int c = tl + (i << tshift);
-    return c < nck ? c : nck - 1;
+  // Chunk index of slot i for this lane within the split, and whether the lane has that chunk.
+  auto chunk_at = [&](int i) { return tl + (i << tshift); };
+  // Member descriptor of row block rbv and the block's first row.
+  struct Where {
+    const uint8_t* packed;
+    const void* scales;
+    float* out;
+    uint32_t n;
+    uint32_t row0;
   };
+  auto where = [&](uint32_t rbv) {
+    return Where{mm.packed, mm.scales, mm.out, mm.n, rbv * (uint32_t)teams_per_wg};
+  };
+  // Row block rbv's packed bytes and scales for this lane, through buffer resources that span
+  // exactly the block's existing rows: rows past N and chunks past the split read as zero
+  // without touching memory, and need no clamping or branch.
+  const uint32_t pitch = (uint32_t)(k >> 1);  // packed bytes per row
+  const uint32_t spitch = scale_pitch<FMT>(k);
   auto load_rb = [&](uint32_t rbv, uint4 (&p)[ITM], float (&s)[ITM]) {
-    rbv = rbv < rb_last ? rbv : rb_last;
-    uint32_t row32 = rbv * (uint32_t)teams_per_wg + (uint32_t)team_id;
-    row32 = row32 < (uint32_t)n ? row32 : (uint32_t)n - 1u;
-    const int64_t row = row32;
-    const uint4* prow = reinterpret_cast<const uint4*>(a.packed + row * (k >> 1)) + c0;
+    // A prefetch past this workgroup's last row block re-reads that block (an L2 hit) rather
+    // than switching the resource off, which would need a per-block select of its size.
+    const Where w = where(rbv < rb_last ? rbv : rb_last);
+    uint32_t rows = w.n > w.row0 ? w.n - w.row0 : 0u;
+    rows = rows < (uint32_t)teams_per_wg ? rows : (uint32_t)teams_per_wg;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(w.packed + (int64_t)w.row0 * pitch, rows * pitch);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+        reinterpret_cast<const char*>(w.scales) + (int64_t)w.row0 * spitch, rows * spitch);
 #pragma unroll
     for (int i = 0; i < ITM; ++i) {
-      const int c = chunk_of(i);
-      p[i] = load_stream16(prow + c);
-      s[i] = load_scale<FMT>(a.scales, row, k, c0 + c);
+      const int c = chunk_at(i);
+      const bool have = c < nck;
+      p[i] = buffer_load16_stream(
+          rp, offset_or_oob(have, (uint32_t)team_id * pitch + (uint32_t)(c0 + c) * 16u));
+      s[i] = load_scale<FMT>(
+          rs, offset_or_oob(have, (uint32_t)team_id * spitch + scale_offset<FMT>(c0 + c)));
     }
   };
 
@@ -185,15 +216,17 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
   float sA[ITM], sB[ITM], sC[ITM];
   load_rb(rb0, pA, sA);
   uint32_t xr[ITM][B][16];
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(B * k * 2));
 #pragma unroll
   for (int i = 0; i < ITM; ++i) {
-    const int c = chunk_of(i);
+    const int c = chunk_at(i);
+    const bool have = c < nck;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const uint4* xb = reinterpret_cast<const uint4*>(a.x + b * k) + (int64_t)(c0 + c) * 4;
+      const uint32_t xo = offset_or_oob(have, (uint32_t)(b * k + (int64_t)(c0 + c) * 32) * 2u);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = xb[q];
+        const uint4 v = buffer_load16(rx, xo + 16u * q);
         xr[i][b][4 * q + 0] = v.x;
         xr[i][b][4 * q + 1] = v.y;
         xr[i][b][4 * q + 2] = v.z;
@@ -262,12 +295,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
       }
     }
 
-    const int64_t row = (int64_t)rbv * teams_per_wg + team_id;
+    const Where w = where(rbv);
+    const uint32_t row = w.row0 + (uint32_t)team_id;
+    const int64_t n = w.n;
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = team_sum_wave(acc[b], team);
-    float* out = a.out + (int64_t)blockIdx.y * B * n;
+    float* out = w.out + (int64_t)blockIdx.y * B * n;
     if (waves_per_team == 1) {
-      if (tl == 0 && row < n) {
+      if (tl == 0 && row < w.n) {
 #pragma unroll
         for (int b = 0; b < B; ++b) out[b * n + row] = acc[b];
       }
@@ -277,7 +312,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
         for (int b = 0; b < B; ++b) xwave[wave][b] = acc[b];
       }
       __syncthreads();
-      if (tl == 0 && row < n) {
+      if (tl == 0 && row < w.n) {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           float v = 0.0f;
@@ -289,8 +324,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
     }
   };
 
-  // --- main loop: three row blocks per trip, buffers rotating A -> B -> C, no early exit; the
-  // last one or two row blocks are already loaded when the loop ends.
+  // --- main loop: three row blocks per trip, buffers rotating A -> B -> C, two row blocks in
+  // flight behind the one being computed, no early exit; the last one or two row blocks are
+  // already loaded when the loop ends.  (Requesting the third block before the table fill instead
+  // measured slower on small matrices.)
   uint32_t rb = rb0;
   uint32_t t = 0;
   for (; t + 3 <= count; t += 3) {
@@ -306,60 +343,58 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
   if (t + 1 < count) compute_store(rb + grid, pB, sB);
 }
 
-template <int FMT, int XT, int B, int ITM>
-hipError_t launch_one(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
-  const dim3 grid(p.grid_x, p.splits);
+template <int FMT, int XT, int B, int ITM, bool GROUPED>
+hipError_t launch_one(const GemvArgs& full, int groups, const GemvPlan& p, hipStream_t s) {
+  constexpr int G = GROUPED ? kMaxGroup : 1;
+  GemvArgsT<G> a;
+  a.x = full.x;
+  a.k = full.k;
+  a.cpr = full.cpr;
+  a.cps = full.cps;
+  a.team = full.team;
+  a.iters = full.iters;
+  for (int g = 0; g < G; ++g) a.m[g] = full.m[g];
+  const dim3 grid(p.grid_x, p.splits, GROUPED ? groups : 1);
   switch (p.threads) {
-    case 256: hipLaunchKernelGGL((gemv_kernel<FMT, XT, B, ITM, 256>), grid, dim3(256), 0, s, a); break;
-    case 512: hipLaunchKernelGGL((gemv_kernel<FMT, XT, B, ITM, 512>), grid, dim3(512), 0, s, a); break;
+    case 256:
+      hipLaunchKernelGGL((gemv_kernel<FMT, XT, B, ITM, 256, GROUPED>), grid, dim3(256), 0, s, a);
+      break;
+    case 512:
+      hipLaunchKernelGGL((gemv_kernel<FMT, XT, B, ITM, 512, GROUPED>), grid, dim3(512), 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int FMT, int XT, int B>
-hipError_t launch_b(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
-  const int it = p.iters;
-  if constexpr (B == 1) {
-    switch (it) {
-      case 1: return launch_one<FMT, XT, B, 1>(a, p, s);
-      case 2: return launch_one<FMT, XT, B, 2>(a, p, s);
-      case 3: return launch_one<FMT, XT, B, 3>(a, p, s);
-      case 4: return launch_one<FMT, XT, B, 4>(a, p, s);
-      case 5: return launch_one<FMT, XT, B, 5>(a, p, s);
-      case 6: return launch_one<FMT, XT, B, 6>(a, p, s);
-      case 7: return launch_one<FMT, XT, B, 7>(a, p, s);
-      case 8: return launch_one<FMT, XT, B, 8>(a, p, s);
-    }
-  } else if constexpr (B == 2) {
-    switch (it) {
-      case 1: return launch_one<FMT, XT, B, 1>(a, p, s);
-      case 2: return launch_one<FMT, XT, B, 2>(a, p, s);
-      case 3: return launch_one<FMT, XT, B, 3>(a, p, s);
-      case 4: return launch_one<FMT, XT, B, 4>(a, p, s);
-    }
-  } else if constexpr (B <= 4) {
-    switch (it) {
-      case 1: return launch_one<FMT, XT, B, 1>(a, p, s);
-      case 2: return launch_one<FMT, XT, B, 2>(a, p, s);
-    }
-  } else {
-    if (it == 1) return launch_one<FMT, XT, B, 1>(a, p, s);
+// Chunks per lane instantiated for batch B: up to gemv_max_iters(B, GROUPED).
+template <int FMT, int XT, int B, bool GROUPED>
+hipError_t launch_b(const GemvArgs& a, int groups, const GemvPlan& p, hipStream_t s) {
+  constexpr int kMax = gemv_max_iters(B, GROUPED);
+  switch (p.iters) {
+    case 1: return launch_one<FMT, XT, B, 1, GROUPED>(a, groups, p, s);
+    case 2: if constexpr (kMax >= 2) return launch_one<FMT, XT, B, 2, GROUPED>(a, groups, p, s); break;
+    case 3: if constexpr (kMax >= 3) return launch_one<FMT, XT, B, 3, GROUPED>(a, groups, p, s); break;
+    case 4: if constexpr (kMax >= 4) return launch_one<FMT, XT, B, 4, GROUPED>(a, groups, p, s); break;
+    case 5: if constexpr (kMax >= 5) return launch_one<FMT, XT, B, 5, GROUPED>(a, groups, p, s); break;
+    case 6: if constexpr (kMax >= 6) return launch_one<FMT, XT, B, 6, GROUPED>(a, groups, p, s); break;
+    case 7: if constexpr (kMax >= 7) return launch_one<FMT, XT, B, 7, GROUPED>(a, groups, p, s); break;
+    case 8: if constexpr (kMax >= 8) return launch_one<FMT, XT, B, 8, GROUPED>(a, groups, p, s); break;
   }
   return hipErrorInvalidValue;
 }
 
-template <int FMT, int XT>
-hipError_t launch_fx(int b, const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
+template <int FMT, int XT, bool GROUPED>
+hipError_t launch_fx(int b, const GemvArgs& a, int groups, const GemvPlan& p, hipStream_t s) {
   switch (b) {
-    case 1: return launch_b<FMT, XT, 1>(a, p, s);
-    case 2: return launch_b<FMT, XT, 2>(a, p, s);
-    case 3: return launch_b<FMT, XT, 3>(a, p, s);
-    case 4: return launch_b<FMT, XT, 4>(a, p, s);
-    case 5: return launch_b<FMT, XT, 5>(a, p, s);
-    case 6: return launch_b<FMT, XT, 6>(a, p, s);
-    case 7: return launch_b<FMT, XT, 7>(a, p, s);
-    case 8: return launch_b<FMT, XT, 8>(a, p, s);
+    case 1: return launch_b<FMT, XT, 1, GROUPED>(a, groups, p, s);
+    case 2: return launch_b<FMT, XT, 2, GROUPED>(a, groups, p, s);
+    case 3: return launch_b<FMT, XT, 3, GROUPED>(a, groups, p, s);
+    case 4: return launch_b<FMT, XT, 4, GROUPED>(a, groups, p, s);
+    case 5: return launch_b<FMT, XT, 5, GROUPED>(a, groups, p, s);
+    case 6: return launch_b<FMT, XT, 6, GROUPED>(a, groups, p, s);
+    case 7: return launch_b<FMT, XT, 7, GROUPED>(a, groups, p, s);
+    case 8: return launch_b<FMT, XT, 8, GROUPED>(a, groups, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -73,6 +73,7 @@ typedef enum {
 
 #define W4_MAX_BATCH 256
 #define W4_MAX_SPLIT_K 64
+#define W4_MAX_GROUP 4
 
 /* ---------------------------------------------------------------- quantizers (offline) ----- */
 
@@ -114,6 +115,28 @@ int w4_quantize_int4(const float* w, int64_t N, int64_t K, uint8_t* packed, uint
  * Single pass, no workspace.  Asynchronous on `stream`. */
 int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t N,
             int64_t K, int64_t B, float* y, void* stream);
+
+/* w4_gemv_grouped: G weight matrices that read the same activations (a layer's q, k and v
+ * projections, or its gate and up projections) in ONE launch of the fused GEMV:
+ * y_g = x . W_hat_g^T for g = 0 .. G-1.  Stacking modules that share their input so that one
+ * launch covers them gives fewer, fuller launches (LLM Compressor 0.14: GPTQ's 15x speedup is one
+ * fused loop, section "Batching layers"); at decode sizes the launch itself is a large share of a
+ * small GEMV's time (My Triton Kernel Ties bitsandbytes, "The numbers" and "What's next").
+ *   x        device [B, K] fp16 or bf16 bit patterns, shared by every member; 16-byte aligned
+ *   groups   G, 1 <= G <= W4_MAX_GROUP
+ *   packed   host array of G device pointers, member g: uint8[N_g, K/2]; 16-byte aligned
+ *   scales   host array of G device pointers, member g: as for w4_gemv with N = N_g
+ *   N        host array of G row counts, N_g >= 1, sum of N_g < 2^31
+ *   y        host array of G device pointers, member g: float[B, N_g], fully overwritten; no y_g
+ *            may overlap another y_h or any input
+ *   fmt, K, B  as for w4_gemv, shared by every member (B <= 8)
+ * The host arrays are read during the call only.  Each y_g satisfies the same accuracy bound as
+ * w4_gemv on that member alone, and is bitwise equal to it when both calls get the same launch
+ * shape (w4_gemv_plan with N = N_g and with N = sum of N_g report the same threads, team and
+ * iters).  No workspace.  Asynchronous on `stream`. */
+int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
+                    const void* const* scales, const int64_t* N, float* const* y, int fmt,
+                    int64_t K, int64_t B, void* stream);
 
 /* w4_gemm_smallbatch: the same operation for 1 <= B <= W4_MAX_BATCH (decode batches; Do
  * Quantization and Sparsity make LLM Inference Faster?, "NF4: fast at batch 1, slower at larger

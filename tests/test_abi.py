@@ -106,3 +106,35 @@ def test_workspace_and_plan_logic():
         w4.gemv_plan("nf4_f16", 64, 256, 9)
     assert w4.auto_path("nf4_f16", 8960, 1536, 1) == ("gemv", 1)
     assert w4.auto_path("nf4_f16", 8960, 1536, 64)[0] == "mfma"
+
+
+def _grouped(L, n=(64, 32, 32), x=FAKE, p=None, s=None, y=None, fmt=1, k=256, b=1, groups=None):
+    vp = ctypes.c_void_p
+    g = len(n)
+    p = p if p is not None else [FAKE * (10 + i) for i in range(g)]
+    s = s if s is not None else [FAKE * (20 + i) for i in range(g)]
+    y = y if y is not None else [FAKE * (30 + i) for i in range(g)]
+    return L.w4_gemv_grouped(vp(x), g if groups is None else groups, (vp * g)(*p), (vp * g)(*s),
+                             (ctypes.c_int64 * g)(*n), (vp * g)(*y), fmt, k, b, None)
+
+
+def test_grouped_validation_codes():
+    _, L = _lib()
+    vp = ctypes.c_void_p
+    assert _grouped(L, groups=0) == -2
+    assert _grouped(L, n=(8,) * 5) == -2  # more members than W4_MAX_GROUP
+    assert L.w4_gemv_grouped(vp(FAKE), 1, None, None, None, None, 1, 256, 1, None) == -1
+    assert _grouped(L, x=0) == -1
+    assert _grouped(L, y=[FAKE * 30, 0, FAKE * 32]) == -1
+    assert _grouped(L, n=(64, 0, 32)) == -2
+    assert _grouped(L, k=96) == -2
+    assert _grouped(L, b=9) == -2
+    assert _grouped(L, fmt=7) == -4
+    assert _grouped(L, p=[FAKE * 10, FAKE * 11 + 4, FAKE * 12]) == -3
+    # y of member 1 overlaps y of member 0 (64 rows x 4 bytes from FAKE * 30)
+    assert _grouped(L, y=[FAKE * 30, FAKE * 30 + 128, FAKE * 32]) == -9
+    # y of member 2 overlaps the packed weights of member 0
+    assert _grouped(L, y=[FAKE * 30, FAKE * 31, FAKE * 10]) == -9
+    # the sum of N must stay below 2^31 (addresses 1 TiB apart so that nothing overlaps)
+    far = [1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44, 1 << 45]
+    assert _grouped(L, n=(1 << 30, 1 << 30), k=64, p=far[0:2], s=far[2:4], y=far[4:6]) == -2

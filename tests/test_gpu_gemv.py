@@ -189,3 +189,67 @@ def test_error_codes_on_device_pointers():
                         vp(y.data_ptr()), 2, 4, None, 0, None)
     assert st == -6  # split-K without workspace
     assert torch.cuda.synchronize() is None
+
+
+def _grouped_case(fmt, ns, k, b, seed):
+    members = []
+    for i, n in enumerate(ns):
+        w = synth_inputs.weights(n, k, sigma=0.02, seed=seed + 17 * i)
+        p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+        pr, sr = g.oracle_quantize(fmt, w)
+        g.assert_quant_equal(fmt, p, s, pr, sr)
+        members.append((p, s, pr, sr))
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=seed + 999)
+    return x, g.to_dev_x(x, g.XDT[fmt]), members
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("ns,k,b", [((1536, 256, 256), 1536, 1), ((8960, 8960), 1536, 1),
+                                    ((1, 7, 300, 65), 1536, 1), ((37, 100), 384, 2),
+                                    ((129, 64, 1), 8960, 1), ((70, 200, 33), 640, 4),
+                                    ((96, 40), 2048, 8), ((500,), 1024, 3)])
+def test_grouped_parity(fmt, ns, k, b):
+    """Each member of a grouped launch against the oracle; ragged member sizes that end inside a
+    row block, single-row members, and up to four members."""
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, members = _grouped_case(fmt, ns, k, b, seed=sum(ns) + k + b)
+    ys = w4.gemv_grouped(xd, [m[0] for m in members], [m[1] for m in members], fmt)
+    for (p, s, pr, sr), y in zip(members, ys):
+        g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("ns,b", [((1536, 256, 256), 1), ((8960, 8960), 1), ((1536, 256, 256), 4)])
+def test_grouped_bitwise_equals_solo(fmt, ns, b):
+    """When the grouped launch gets the same launch shape as each member alone, every y_g is
+    bitwise equal to w4_gemv on that member (same per-row arithmetic, only the row mapping
+    differs); y buffers pre-filled with NaN, so every element must be written."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    k = 1536
+    x, xd, members = _grouped_case(fmt, ns, k, b, seed=5 + b)
+    plan_all = w4.gemv_plan(fmt, sum(ns), k, b)
+    ys = [torch.full((b, n), float("nan"), device=g.device()) for n in ns]
+    w4.gemv_grouped(xd, [m[0] for m in members], [m[1] for m in members], fmt, ys=ys)
+    for n, (p, s, pr, sr), y in zip(ns, members, ys):
+        plan_one = w4.gemv_plan(fmt, n, k, b)
+        y_solo = w4.gemv(xd, p, s, fmt)
+        assert not torch.isnan(y).any()
+        if all(plan_one[f] == plan_all[f] for f in ("threads", "team", "iters")):
+            assert torch.equal(y, y_solo)
+        g.assert_y_close(fmt, y, x, pr, sr)
+
+
+def test_grouped_long_rows_at_b8_fall_back_per_member():
+    """B = 8 with K = 28672 has no GEMV launch shape; the grouped call then runs each member on
+    the MFMA path and still meets the bound."""
+    import bit_weight_only_w4_amd as w4
+
+    fmt = "nf4_f16"
+    x, xd, members = _grouped_case(fmt, (40, 24), 28672, 8, seed=3)
+    ys = w4.gemv_grouped(xd, [m[0] for m in members], [m[1] for m in members], fmt)
+    for (p, s, pr, sr), y in zip(members, ys):
+        g.assert_y_close(fmt, y, x, pr, sr)
