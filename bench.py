@@ -8,6 +8,11 @@ packed weights and scales, more than the 256 MB last-level cache, so every step 
 HBM).  Weights are synthetic N(0, 0.02), quantized on the GPU before timing; activations N(0, 1).
 The step is captured once as a HIP graph and replayed.
 
+Schedules of the same 197 GEMVs: "grouped" (default) launches each layer's q, k, v together and
+its gate, up together through w4_gemv_grouped, as a model whose projections share their input
+runs them (113 launches); "serial" launches every GEMV on its own (197 launches); "dag" puts
+q|k|v and gate|up on parallel graph branches.  Every schedule is timed and reported.
+
 stdout: ONE JSON line (the driver contract).  Details go to stderr and to --report.
 """
 from __future__ import annotations
@@ -35,7 +40,7 @@ def parse_args():
                     help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per kernel class / shape kind when timing launches")
-    ap.add_argument("--schedule", default="serial", choices=["serial", "grouped", "dag"],
+    ap.add_argument("--schedule", default="grouped", choices=["serial", "grouped", "dag"],
                     help="serial: one chain of 197 launches; grouped: one chain of 113 launches, "
                          "q|k|v and gate|up each in one grouped launch; dag: 197 launches with "
                          "q|k|v and gate|up as graph branches")
