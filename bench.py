@@ -156,8 +156,8 @@ class Step:
             _, n, k = self.shapes[unit[0]]
             path, sk = self.plans[unit[0]]
             return plan_kernel(self.w4, self.fmt, n, k, self.b, path, sk)[0]
-        n = sum(self.shapes[i][1] for i in unit)
-        return plan_kernel(self.w4, self.fmt, n, self.shapes[unit[0]][2], self.b, "gemv", 1)[0]
+        return grouped_kernel(self.w4, self.fmt, [self.shapes[i][1] for i in unit],
+                              self.shapes[unit[0]][2], self.b)[0]
 
     def unit_kind(self, unit):
         return "|".join(self.shapes[i][0].split(".")[-1] for i in unit)
@@ -168,18 +168,29 @@ class Step:
         return sum(self.bytes[i] - x_bytes for i in unit) + x_bytes
 
 
+def _gemv_name(fmt, b, iters, threads, grouped):
+    fmt_i = 0 if fmt.startswith("nf4") else 1
+    xt = 0 if fmt.endswith("_f16") else 1
+    return f"gemv_kernel<{fmt_i}, {xt}, {b}, {iters}, {threads}, {'true' if grouped else 'false'}>"
+
+
 def plan_kernel(w4, fmt, n, k, b, path, sk):
     """(kernel name, grid size in work-items) of one launch, from the library's own host-side plan.
     Names match the profiler's kernel names; the grid size is the profiler's Grid_Size."""
     if path in ("gemv", "splitk"):
         plan = w4.gemv_plan(fmt, n, k, b, max(sk, 1))
-        fmt_i = 0 if fmt.startswith("nf4") else 1
-        xt = 0 if fmt.endswith("_f16") else 1
-        key = f"gemv_kernel<{fmt_i}, {xt}, {b}, {plan['iters']}, {plan['threads']}>"
+        key = _gemv_name(fmt, b, plan["iters"], plan["threads"], False)
         if path == "splitk":
             key += f"+splitk_reduce(S={sk})"
-        return key, plan["grid_x"] * plan["threads"]
+        return key, plan["grid_x"] * plan["threads"] * max(sk, 1)
     return path, None
+
+
+def grouped_kernel(w4, fmt, ns, k, b):
+    """(kernel name, grid size in work-items) of one grouped launch over members of ns rows."""
+    plan = w4.gemv_grouped_plan(fmt, ns, k, b)
+    return (_gemv_name(fmt, b, plan["iters"], plan["threads"], True),
+            plan["grid_x"] * plan["grid_z"] * plan["threads"])
 
 
 def step_launch_mix(w4, fmt, b, path, schedule):
@@ -199,13 +210,7 @@ def step_launch_mix(w4, fmt, b, path, schedule):
             mix.append((key, grid, algorithmic_bytes(fmt, n, k, b)))
         else:
             ns = [shapes[i][1] for i in unit]
-            key, _ = plan_kernel(w4, fmt, sum(ns), k, b, "gemv", 1)
-            plan = w4.gemv_plan(fmt, sum(ns), k, b)
-            rows = plan["threads"] // plan["team"]
-            nrb = sum((n + rows - 1) // rows for n in ns)  # row blocks never span two members
-            full = (sum(ns) + rows - 1) // rows
-            # either the grid cap binds (and still does for nrb >= full), or every block gets one
-            grid = (plan["grid_x"] if plan["grid_x"] < full else nrb) * plan["threads"]
+            key, grid = grouped_kernel(w4, fmt, ns, k, b)
             x_bytes = 2 * b * k
             mix.append((key, grid, sum(algorithmic_bytes(fmt, n, k, b) - x_bytes for n in ns) + x_bytes))
     return mix

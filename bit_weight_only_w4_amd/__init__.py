@@ -62,11 +62,12 @@ def lib() -> ctypes.CDLL:
         L.w4_status_string.restype = ctypes.c_char_p
         vpp = ctypes.POINTER(vp)
         L.w4_gemv_grouped.argtypes = [vp, ci, vpp, vpp, ctypes.POINTER(i64), vpp, ci, i64, i64, vp]
+        L.w4_gemv_grouped_plan.argtypes = [ci, ci, ctypes.POINTER(i64), i64, i64, ip, ip, ip, ip, ip]
         L.w4_probe_read.argtypes = [vp, sz, vp, vp]
         L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
         for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_gemv", "w4_gemm_smallbatch",
                      "w4_matmul_ex", "w4_auto_path", "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
-                     "w4_gemv_grouped"):
+                     "w4_gemv_grouped", "w4_gemv_grouped_plan"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -229,6 +230,16 @@ def gemv_plan(fmt, n, k, b, split_k=1):
     check(r, "w4_gemv_plan")
     return dict(zip(("threads", "team", "iters", "chunks_per_split", "grid_x"),
                     (v.value for v in vals)))
+
+
+def gemv_grouped_plan(fmt, ns, k, b):
+    """dict(threads, team, iters, grid_x, grid_z) of the grouped fused-GEMV launch over members
+    of ns rows."""
+    vals = [ctypes.c_int(0) for _ in range(5)]
+    arr = (ctypes.c_int64 * len(ns))(*ns)
+    r = lib().w4_gemv_grouped_plan(_fmt(fmt), len(ns), arr, k, b, *[ctypes.byref(v) for v in vals])
+    check(r, "w4_gemv_grouped_plan")
+    return dict(zip(("threads", "team", "iters", "grid_x", "grid_z"), (v.value for v in vals)))
 
 
 def matmul_ex(x, packed, scales, fmt, path="auto", split_k=0, workspace=None, y=None,

@@ -132,39 +132,50 @@ int auto_splits(int64_t, int64_t, int) { return 1; }
 
 size_t splitk_bytes(int64_t n, int64_t b, int s) { return (size_t)s * (size_t)b * (size_t)n * 4; }
 
+// Launch shape of one fused-GEMV launch over `groups` members that share K: the plan of their
+// summed rows, each member's row blocks, and the workgroups along x per member (the largest
+// member's share of the grid cap, so that the whole grid stays within the cap; smaller members
+// leave their surplus workgroups idle).
+bool plan_members(int groups, const int64_t* n, int64_t k, int b, int splits, bool grouped,
+                  GemvPlan* p, int64_t* nrb) {
+  int64_t n_total = 0;
+  for (int g = 0; g < groups; ++g) n_total += n[g];
+  if (b > kMaxGemvBatch || !plan_gemv(n_total, k, b, splits, p, grouped)) return false;
+  const int64_t rows_per_wg = p->threads / p->team;
+  int64_t nrb_sum = 0, nrb_max = 0;
+  for (int g = 0; g < groups; ++g) {
+    nrb[g] = (n[g] + rows_per_wg - 1) / rows_per_wg;
+    nrb_sum += nrb[g];
+    nrb_max = std::max(nrb_max, nrb[g]);
+  }
+  const int64_t share = std::max<int64_t>(1, (p->cap * nrb_max + nrb_sum - 1) / nrb_sum);
+  p->grid_x = (int)std::min<int64_t>(nrb_max, share);
+  return true;
+}
+
 // One fused-GEMV launch over `groups` members that share x and K (splits > 1 only for a single
 // member), then the split-K reduction if any.
 int run_gemv_members(const void* x, int groups, const uint8_t* const* packed,
                      const void* const* scales, const int64_t* n, float* const* y, int fmt,
                      int64_t k, int64_t b, int splits, void* ws, hipStream_t st) {
-  int64_t n_total = 0;
-  for (int g = 0; g < groups; ++g) n_total += n[g];
   GemvPlan p;
-  if (b > kMaxGemvBatch || !plan_gemv(n_total, k, (int)b, splits, &p, groups > 1)) return W4_ERR_PATH;
-  const int64_t rows_per_wg = p.threads / p.team;
+  int64_t nrb[kMaxGroup];
+  if (!plan_members(groups, n, k, (int)b, splits, groups > 1, &p, nrb)) return W4_ERR_PATH;
   GemvArgs a;
   memset(&a, 0, sizeof(a));
   a.x = reinterpret_cast<const uint16_t*>(x);
-  int64_t nrb_sum = 0, nrb_max = 0;
   for (int g = 0; g < groups; ++g) {
-    const int64_t nrb = (n[g] + rows_per_wg - 1) / rows_per_wg;
     a.m[g].packed = packed[g];
     a.m[g].scales = scales[g];
     a.m[g].out = splits == 1 ? y[g] : reinterpret_cast<float*>(ws);
     a.m[g].n = (uint32_t)n[g];
-    a.m[g].nrb = (uint32_t)nrb;
-    nrb_sum += nrb;
-    nrb_max = std::max(nrb_max, nrb);
+    a.m[g].nrb = (uint32_t)nrb[g];
   }
   a.k = k;
   a.cpr = (int)(k / 32);
   a.cps = p.cps;
   a.team = p.team;
   a.iters = p.iters;
-  // Workgroups along x per member: the largest member's share of the cap, so that the grid as a
-  // whole stays within the cap; smaller members leave their surplus workgroups idle.
-  const int64_t share = std::max<int64_t>(1, (p.cap * nrb_max + nrb_sum - 1) / nrb_sum);
-  p.grid_x = (int)std::min<int64_t>(nrb_max, share);
   if (launch_gemv(fmt, (int)b, a, groups, p, st) != hipSuccess) return W4_ERR_HIP;
   if (splits > 1) {
     if (launch_splitk_reduce(reinterpret_cast<const float*>(ws), y[0], b * n[0], splits, st) !=
@@ -293,6 +304,30 @@ int w4_gemv_plan(int fmt, int64_t n, int64_t k, int64_t b, int split_k, int* thr
   return W4_OK;
 }
 
+int w4_gemv_grouped_plan(int fmt, int groups, const int64_t* n, int64_t k, int64_t b,
+                         int* threads, int* team, int* iters, int* grid_x, int* grid_z) {
+  if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
+  if (groups < 1 || groups > W4_MAX_GROUP) return W4_ERR_SHAPE;
+  if (!n) return W4_ERR_NULL;
+  const int64_t g = fmt_group(fmt);
+  int64_t n_total = 0;
+  for (int i = 0; i < groups; ++i) {
+    if (n[i] < 1 || n[i] >= kMaxDim) return W4_ERR_SHAPE;
+    n_total += n[i];
+  }
+  if (n_total >= kMaxDim || k < g || k % g || k >= kMaxDim || b < 1 || b > W4_MAX_BATCH)
+    return W4_ERR_SHAPE;
+  GemvPlan p;
+  int64_t nrb[kMaxGroup];
+  if (!plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb)) return W4_ERR_PATH;
+  if (threads) *threads = p.threads;
+  if (team) *team = p.team;
+  if (iters) *iters = p.iters;
+  if (grid_x) *grid_x = p.grid_x;
+  if (grid_z) *grid_z = groups;
+  return W4_OK;
+}
+
 int w4_auto_path(int fmt, int64_t n, int64_t k, int64_t b, size_t workspace_bytes, int* split_k) {
   if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
   const int64_t g = fmt_group(fmt);
@@ -391,7 +426,8 @@ int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   GemvPlan p;
-  if (!plan_gemv(n_total, k, (int)b, 1, &p, groups > 1)) {  // no GEMV shape: MFMA per member
+  int64_t nrb[kMaxGroup];
+  if (!plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb)) {  // no GEMV shape: MFMA each
     for (int g = 0; g < groups; ++g) {
       const int st = run_mfma(x, packed[g], scales[g], fmt, n[g], k, b, y[g], s);
       if (st != W4_OK) return st;

@@ -166,12 +166,16 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   const uint32_t nrb = mm.nrb;
   const uint32_t grid = gridDim.x;
   const uint32_t rb0 = blockIdx.x;
-  // Row blocks of this workgroup: none when its member is smaller than the grid is wide (grouped
-  // launches).  Such a workgroup still runs the prologue with every load out of range, rather
-  // than branching out early: an early exit would make the prologue wait for the member
-  // descriptor before fetching the rest of its arguments.
-  const uint32_t count = rb0 < nrb ? (nrb - 1u - rb0) / grid + 1u : 0u;
-  const uint32_t rb_last = count ? rb0 + grid * (count - 1u) : rb0;
+  if constexpr (GROUPED) {
+    // A member smaller than the grid is wide leaves workgroups with no row block: they leave
+    // before the table fill.  Every argument the kernel uses is fetched before that branch (the
+    // empty asm consumes them), so the fetch stays one batch of scalar loads.
+    asm volatile("" ::"s"(a.x), "s"(a.k), "s"(a.cpr), "s"(a.cps), "s"(a.team), "s"(a.iters),
+                 "s"(mm.packed), "s"(mm.scales), "s"(mm.out), "s"(mm.n), "s"(grid));
+    if (rb0 >= nrb) return;
+  }
+  const uint32_t count = (nrb - 1u - rb0) / grid + 1u;  // row blocks of this workgroup (>= 1)
+  const uint32_t rb_last = rb0 + grid * (count - 1u);
 
   // Chunk index of slot i for this lane within the split, and whether the lane has that chunk.
   auto chunk_at = [&](int i) { return tl + (i << tshift); };
@@ -195,7 +199,7 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
     // A prefetch past this workgroup's last row block re-reads that block (an L2 hit) rather
     // than switching the resource off, which would need a per-block select of its size.
     const Where w = where(rbv < rb_last ? rbv : rb_last);
-    uint32_t rows = w.n > w.row0 ? w.n - w.row0 : 0u;
+    uint32_t rows = w.n - w.row0;  // w.row0 < w.n: every row block up to rb_last exists
     rows = rows < (uint32_t)teams_per_wg ? rows : (uint32_t)teams_per_wg;
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(w.packed + (int64_t)w.row0 * pitch, rows * pitch);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(

@@ -175,6 +175,14 @@ int w4_auto_path(int fmt, int64_t N, int64_t K, int64_t B, size_t workspace_byte
 int w4_gemv_plan(int fmt, int64_t N, int64_t K, int64_t B, int split_k, int* threads, int* team,
                  int* iters, int* chunks_per_split, int* grid_x);
 
+/* Launch shape of w4_gemv_grouped for members of N[0 .. groups-1] rows sharing (fmt, K, B):
+ * threads per workgroup, lanes per output row, 16-byte chunks per lane, workgroups along N per
+ * member (grid_x) and members (grid_z; one grid slice per member).  Any output pointer may be
+ * NULL.  Returns W4_OK, or W4_ERR_SHAPE / W4_ERR_PATH when the grouped GEMV cannot run these
+ * arguments (w4_gemv_grouped then runs each member on the MFMA path). */
+int w4_gemv_grouped_plan(int fmt, int groups, const int64_t* N, int64_t K, int64_t B, int* threads,
+                         int* team, int* iters, int* grid_x, int* grid_z);
+
 /* Host pointer to the 16 NF4 code points (fp32, ascending) the kernels decode with.  Static
  * storage owned by the library; never NULL. */
 const float* w4_nf4_codebook(void);

@@ -138,3 +138,22 @@ def test_grouped_validation_codes():
     # the sum of N must stay below 2^31 (addresses 1 TiB apart so that nothing overlaps)
     far = [1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44, 1 << 45]
     assert _grouped(L, n=(1 << 30, 1 << 30), k=64, p=far[0:2], s=far[2:4], y=far[4:6]) == -2
+
+
+def test_grouped_plan_logic():
+    """Host-side plan of a grouped launch: one grid slice per member, the shared per-row shape of
+    the summed rows, and a grid that stays within the single-launch cap."""
+    w4, L = _lib()
+    p = w4.gemv_grouped_plan("nf4_f16", [1536, 256, 256], 1536, 1)
+    solo = w4.gemv_plan("nf4_f16", 2048, 1536, 1)
+    assert p["grid_z"] == 3
+    assert (p["threads"], p["team"], p["iters"]) == (solo["threads"], solo["team"], solo["iters"])
+    rows = p["threads"] // p["team"]
+    assert p["grid_x"] <= (1536 + rows - 1) // rows  # never wider than the largest member
+    p2 = w4.gemv_grouped_plan("int4_bf16", [8960, 8960], 1536, 2)
+    assert p2["grid_z"] == 2 and p2["grid_x"] * 2 <= 2 * 512  # within 2 workgroups per CU
+    with pytest.raises(ValueError):
+        w4.gemv_grouped_plan("nf4_f16", [64] * 5, 256, 1)
+    with pytest.raises(ValueError):
+        w4.gemv_grouped_plan("nf4_f16", [64, 0], 256, 1)
+    assert L.w4_gemv_grouped_plan(1, 2, None, 256, 1, None, None, None, None, None) == -1
