@@ -217,14 +217,16 @@ def step_launch_mix(w4, fmt, b, path, schedule):
 
 
 def kernel_source_digest():
-    """sha256 over the library's HIP/C++ sources and its build script: a stored counter reading
-    belongs to the kernels it was taken on and to nothing built since."""
+    """sha256 over the sources of the decode step's kernels (the fused GEMV, its launch planning
+    and the build flags): a stored counter reading belongs to the kernels it was taken on and to
+    nothing built since."""
     import hashlib
 
     root = os.path.dirname(os.path.abspath(__file__))
     pkg = os.path.join(root, "bit_weight_only_w4_amd")
     h = hashlib.sha256()
-    files = [os.path.join("csrc", f) for f in sorted(os.listdir(os.path.join(pkg, "csrc")))]
+    files = [os.path.join("csrc", f) for f in sorted(os.listdir(os.path.join(pkg, "csrc")))
+             if f.startswith("w4_gemv") or f in ("w4_common.h", "w4_api.cpp")]
     for rel in files + ["build.py"]:
         h.update(rel.encode())
         with open(os.path.join(pkg, rel), "rb") as f:
@@ -553,7 +555,8 @@ def time_shape(fmt, n, k, b, path, split_k, dev, min_bytes=600 << 20, reps=5):
 def shapes_suite(args, dev):
     """Per-shape table for the other workloads: INT4 decode steps (B = 1, 8) and split-K vs one
     pass on down; small-batch GEMM on gate / down / lm_head at B = 1, 8, 32, 128 for the GEMV,
-    MFMA and two-pass paths; the larger single-GPU model's shapes at B = 1, 4, 16."""
+    MFMA and two-pass paths, and GEMV against MFMA at B = 2..6; the larger single-GPU model's
+    shapes at B = 1, 4, 16."""
     import synth_inputs
 
     rows = []
@@ -590,6 +593,11 @@ def shapes_suite(args, dev):
                 add("nf4-gemm", "nf4_f16", name, n, k, b, "gemv")
             add("nf4-gemm", "nf4_f16", name, n, k, b, "mfma")
             add("nf4-gemm", "nf4_f16", name, n, k, b, "twopass")
+    # GEMV against MFMA at small batches (where the automatic path switches)
+    for name, n, k in (("gate", 8960, 1536), ("down", 1536, 8960), ("lm_head", 151936, 1536)):
+        for b in (2, 3, 4, 6):
+            add("crossover", "nf4_f16", name, n, k, b, "gemv")
+            add("crossover", "nf4_f16", name, n, k, b, "mfma")
     # larger single-GPU model
     for fmt in ("nf4_f16", "int4_f16"):
         for name, n, k in synth_inputs.LARGE_SHAPES:

@@ -43,9 +43,9 @@ typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTableBytes = 65536;
-constexpr int kThreads = 512;       // 8 waves
-constexpr int kXBytes = 96 * 1024;  // x window; the table takes the other 64 KiB of the 160 KiB
+constexpr int kTableBytes = 32768;   // 256 entries x 128 bytes
+constexpr int kThreads = 512;        // 8 waves
+constexpr int kXBytes = 128 * 1024;  // x window; the table takes the other 32 KiB of the 160 KiB
 constexpr int kQuad = 256;          // weights per quad
 constexpr int kMaxTiles = 8;        // up to 128 activation rows per launch
 
@@ -66,7 +66,9 @@ __device__ inline uint32_t nf4_codes_in_lanes() {
   return v;
 }
 
-// The byte -> decoded pair table (64 copies of 256 entries, as in the GEMV kernel).
+// The byte -> decoded pair table, as in the GEMV kernel but with 32 copies of each 4-byte entry
+// (16 of each 8-byte NF4 x bf16 entry): 128 bytes per entry, lane L reading copy L % 32 (L % 16).
+// Half the GEMV's LDS, which leaves room for a larger x window.
 template <int FMT, int XT>
 __device__ inline void fill_table(uint32_t* tab) {
   uint32_t v1, v2 = 0;
@@ -85,12 +87,14 @@ __device__ inline void fill_table(uint32_t* tab) {
   constexpr bool kSplit = (FMT == kNF4 && XT == kBF16);
   uint4* t4 = reinterpret_cast<uint4*>(tab);
   const int tid = threadIdx.x;
-  const uint32_t lo1 = (uint32_t)__shfl((int)v1, (tid >> 4) & 15) << 16;
-  const uint32_t lo2 = kSplit ? (uint32_t)__shfl((int)v2, (tid >> 4) & 15) << 16 : 0u;
+  // 16-byte slot i belongs to entry i >> 3: high nibble i >> 7 (uniform over a wave), low nibble
+  // (i >> 3) & 15 (the same for every slot of a thread).
+  const uint32_t lo1 = (uint32_t)__shfl((int)v1, (tid >> 3) & 15) << 16;
+  const uint32_t lo2 = kSplit ? (uint32_t)__shfl((int)v2, (tid >> 3) & 15) << 16 : 0u;
 #pragma unroll 4
   for (int j = 0; j < kTableBytes / 16 / kThreads; ++j) {
     const int i = tid + kThreads * j;
-    const int hi = __builtin_amdgcn_readfirstlane(i >> 8);
+    const int hi = __builtin_amdgcn_readfirstlane(i >> 7);
     const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane((int)v1, hi) | lo1;
     if (kSplit) {
       const uint32_t p2 = (uint32_t)__builtin_amdgcn_readlane((int)v2, hi) | lo2;
@@ -119,7 +123,7 @@ struct MfmaArgs {
   const void* scales;     // NF4 float[N, K/64] | INT4 uint16[N, K/128]
   float* y;               // [B, N]
   int64_t n, k;
-  int b;       // activation rows in this launch (<= 16 * T)
+  int b;       // activation rows in all; slice blockIdx.y takes rows [16 T y, 16 T (y + 1))
   int qpk;     // quads per K group
   int qpp;     // quads per K group in one x window (one phase)
   int xrow;    // bytes per activation row of the x window: KW * qpp * 512 + 16
@@ -167,7 +171,12 @@ mfma_kernel(MfmaArgs a) {
   const int64_t nblocks = k / KC;
   const uint32_t pitch = (uint32_t)(k >> 1);
   const uint32_t spitch = (uint32_t)(nblocks * SB);
-  const __amdgpu_buffer_rsrc_t rx_ = make_rsrc(a.x, (uint32_t)(a.b * k * 2));
+  // This workgroup's batch slice: activation rows [16 T y, 16 T y + bsl).
+  const int64_t b0 = (int64_t)blockIdx.y * 16 * T;
+  const int bsl = (int)min((int64_t)16 * T, (int64_t)a.b - b0);
+  const uint16_t* xsl = a.x + b0 * k;
+  float* ysl = a.y + b0 * n;
+  const __amdgpu_buffer_rsrc_t rx_ = make_rsrc(xsl, (uint32_t)(bsl * k * 2));
 
   // The workgroup's row tiles: blockIdx.x, blockIdx.x + gridDim.x, ...  A workgroup runs several
   // tiles (a persistent grid) only when the whole of x fits one window and KW == 1; otherwise the
@@ -234,15 +243,15 @@ mfma_kernel(MfmaArgs a) {
   // col = s % (rowp + 1) of row r = s / (rowp + 1), the last piece of a row being the padding.
   const int xrow = a.xrow;
   const int seg = a.qpp * (kQuad / 8);  // 16-byte pieces of one K group's segment of a row
-  const int rowp = KW * seg;            // data pieces per window row (<= 352)
+  const int rowp = KW * seg;            // data pieces per window row (<= 480)
   const int slots = 16 * T * (rowp + 1);
   const int nphase = (nq + a.qpp - 1) / a.qpp;
-  // Integer quotients through float reciprocals: s < 6144 and, after the + 0.5 offset, s / (rowp
-  // + 1) and col / seg stay at least 1 / 706 away from an integer, far above the error of the fp32
+  // Integer quotients through float reciprocals: s < 8192 and, after the + 0.5 offset, s / (rowp
+  // + 1) and col / seg stay at least 1 / 962 away from an integer, far above the error of the fp32
   // reciprocal and product.
   const float inv_row = 1.0f / (float)(rowp + 1);
   const float inv_seg = 1.0f / (float)seg;
-  constexpr int kXPer = kXBytes / 16 / kThreads;  // 12 slots per thread cover the whole area
+  constexpr int kXPer = kXBytes / 16 / kThreads;  // 16 slots per thread cover the whole area
   auto load_x = [&](int p) __attribute__((always_inline)) {
     const int64_t kbase = (int64_t)p * a.qpp * kQuad;
     // Recomputed at each window rather than kept live across the main loop (registers).
@@ -256,7 +265,7 @@ mfma_kernel(MfmaArgs a) {
       const int kk = (int)(((float)col + 0.5f) * inv_seg);
       const int pc = col - kk * seg;
       const int64_t kpos = (int64_t)kk * a.qpk * kQuad + kbase + (int64_t)pc * 8;
-      const bool have = sl < slots && col < rowp && r < a.b && kpos < k;
+      const bool have = sl < slots && col < rowp && r < bsl && kpos < k;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx_, (__attribute__((address_space(3))) void*)(xs + (j * kThreads + wave * 64) * 16), 16,
           (int)offset_or_oob(have, (uint32_t)((r * k + kpos) * 2)), 0, 0, 0);
@@ -289,7 +298,8 @@ mfma_kernel(MfmaArgs a) {
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t laneoff = kSplit ? (uint32_t)(lane & 31) * 8u : (uint32_t)lane * 4u;
+  // Twice this lane's byte offset in a table entry (see the lookup below).
+  const uint32_t laneoff = kSplit ? (uint32_t)(lane & 15) * 16u : (uint32_t)(lane & 31) * 8u;
   const char* tabc = reinterpret_cast<const char*>(tab);
   const uint8_t* xw = xs + kg * (seg * 16) + m * xrow;  // this lane's B row (tile 0), K group kg
 
@@ -328,9 +338,10 @@ mfma_kernel(MfmaArgs a) {
         uint32_t p1[4], p2[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          // LDS byte address: lane offset in byte 0, the packed byte in byte 1.
+          // LDS byte address = byte * 128 + lane offset: the perm builds byte * 256 + 2 * lane
+          // offset (the packed byte into byte 1), halved by the shift.
           const uint32_t addr =
-              __builtin_amdgcn_perm(wb[c][s], laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb) << 8));
+              __builtin_amdgcn_perm(wb[c][s], laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb) << 8)) >> 1;
           if (kSplit) {
             const uint2 tv = *reinterpret_cast<const uint2*>(tabc + addr);
             p1[kb] = tv.x;
@@ -388,8 +399,8 @@ mfma_kernel(MfmaArgs a) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int b = 16 * t + m;
-        if (b < a.b) {
-          float* yr = a.y + (int64_t)b * n;
+        if (b < bsl) {
+          float* yr = ysl + (int64_t)b * n;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (row_d + i < n) yr[row_d + i] = acc[t][i];
@@ -447,7 +458,9 @@ constexpr int max_kw(int t) { return t == 1 ? 8 : t == 2 ? 4 : t == 4 ? 2 : 1; }
 
 template <int FMT, int XT, int T, int KW>
 hipError_t launch_kw(const MfmaArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((mfma_kernel<FMT, XT, T, KW>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  const unsigned slices = (unsigned)((a.b + 16 * T - 1) / (16 * T));
+  hipLaunchKernelGGL((mfma_kernel<FMT, XT, T, KW>), dim3((unsigned)grid, slices), dim3(kThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -476,17 +489,18 @@ hipError_t launch_fx(const MfmaArgs& a, int tiles, int kw, int grid, hipStream_t
 
 }  // namespace
 
-// Launch shape of the MFMA kernel for (N, K, B <= 128): batch tiles, K groups, quads per K group
-// and per x window.  K groups split K inside a workgroup when N alone gives too few workgroups:
-// the smallest KW of 1, 2, 4, 8 that gives at least one workgroup per CU, within what the x
-// window holds.  Byte offsets are 32-bit: the activations (B * K * 2) must stay below 2^31.
-bool plan_mfma(int64_t n, int64_t k, int64_t b, int* tiles, int* kw, int* qpk, int* qpp,
-               int* xrow, int* ntiles, int* grid) {
-  if (b < 1 || b > 16 * kMaxTiles || b * k * 2 >= ((int64_t)1 << 31)) return false;
-  const int need = (int)((b + 15) / 16);
-  const int t = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+// Launch shape of the MFMA kernel for one batch slice of T tiles: K groups, quads per K group and
+// per x window, row tiles and workgroups along x.  K groups split K inside a workgroup when N alone
+// gives too few workgroups: the smallest KW of 1, 2, 4, 8 that gives at least one workgroup per CU
+// (counting the `slices` batch slices), within what the x window holds.
+struct MfmaPlan {
+  int tiles, kw, qpk, qpp, xrow, ntiles, grid, slices;
+};
+
+bool plan_slice(int64_t n, int64_t k, int64_t b, int t, MfmaPlan* p) {
   const int64_t quads = (k + kQuad - 1) / kQuad;
   const int64_t cus = device_cu_count();
+  const int slices = (int)((b + 16 * t - 1) / (16 * t));
   const int row_budget = kXBytes / (16 * t);          // window bytes per activation row
   const int max_q = (row_budget - 16) / (kQuad * 2);  // quads per window row, all K groups
   if (max_q < 1) return false;
@@ -495,52 +509,78 @@ bool plan_mfma(int64_t n, int64_t k, int64_t b, int* tiles, int* kw, int* qpk, i
     if (c > max_q || c > quads) break;
     best = c;
     const int64_t rows = 16 * (8 / c);
-    if ((n + rows - 1) / rows >= cus) break;
+    if ((n + rows - 1) / rows * slices >= cus) break;
   }
   const int64_t per_kg = (quads + best - 1) / best;
   const int per_phase = std::max(1, max_q / best);
-  *tiles = t;
-  *kw = best;
-  *qpk = (int)per_kg;
-  *qpp = (int)std::min<int64_t>(per_kg, per_phase);
-  *xrow = best * *qpp * kQuad * 2 + 16;
+  p->tiles = t;
+  p->kw = best;
+  p->qpk = (int)per_kg;
+  p->qpp = (int)std::min<int64_t>(per_kg, per_phase);
+  p->xrow = best * p->qpp * kQuad * 2 + 16;
   // Row tiles and workgroups: one workgroup per CU walks several tiles when x fits one window and
   // K is not split (the window and the table are then filled once per workgroup, and each wave's
   // stream of quads runs across its tiles without a pipeline restart); else one per tile.
   const int64_t rows = 16 * (8 / best);
   const int64_t ntile = (n + rows - 1) / rows;
-  *ntiles = (int)ntile;
-  *grid = (best == 1 && *qpp >= per_kg) ? (int)std::min<int64_t>(ntile, cus) : (int)ntile;
+  p->ntiles = (int)ntile;
+  p->grid = (best == 1 && p->qpp >= per_kg)
+                ? (int)std::min<int64_t>(ntile, std::max<int64_t>(1, cus / slices))
+                : (int)ntile;
+  p->slices = slices;
   return true;
 }
 
-// Runs the batch in slices of at most 128 activation rows; each slice re-reads the weights.
+// Batch tiles per slice: the largest T (8, 4, 2, 1; at most what B needs) whose launch has at
+// least half a workgroup per CU; slices beyond the first re-read the weights (mostly from L2).
+// Byte offsets are 32-bit: a slice's activations (16 T * K * 2 bytes) must stay below 2^31.
+bool plan_mfma(int64_t n, int64_t k, int64_t b, MfmaPlan* out) {
+  if (b < 1 || b > W4_MAX_BATCH || 16 * kMaxTiles * k * 2 >= ((int64_t)1 << 31)) return false;
+  const int64_t cus = device_cu_count();
+  const int need = (int)std::min<int64_t>((b + 15) / 16, kMaxTiles);
+  const int tmax = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  bool found = false;
+  MfmaPlan best{};
+  for (int t = tmax; t >= 1; t /= 2) {
+    MfmaPlan p;
+    if (!plan_slice(n, k, b, t, &p)) continue;
+    if (!found || (int64_t)p.grid * p.slices > (int64_t)best.grid * best.slices) {
+      best = p;
+      found = true;
+    }
+    if ((int64_t)p.grid * p.slices * 2 >= cus) {
+      best = p;
+      break;
+    }
+  }
+  if (found) *out = best;
+  return found;
+}
+
+// One launch over all B rows of x: grid.y = batch slices of up to 16 T rows.
 hipError_t launch_mfma(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
                        int64_t n, int64_t k, int64_t b, float* y, hipStream_t s) {
-  const int64_t per = 16 * kMaxTiles;
-  for (int64_t b0 = 0; b0 < b; b0 += per) {
-    MfmaArgs a;
-    a.x = x + b0 * k;
-    a.packed = packed;
-    a.scales = scales;
-    a.y = y + b0 * n;
-    a.n = n;
-    a.k = k;
-    a.b = (int)std::min<int64_t>(per, b - b0);
-    int tiles, kw, grid;
-    if (!plan_mfma(n, k, a.b, &tiles, &kw, &a.qpk, &a.qpp, &a.xrow, &a.tiles, &grid))
-      return hipErrorNotSupported;
-    hipError_t e;
-    switch (fmt) {
-      case W4_NF4_X_F16: e = launch_fx<kNF4, kF16>(a, tiles, kw, grid, s); break;
-      case W4_NF4_X_BF16: e = launch_fx<kNF4, kBF16>(a, tiles, kw, grid, s); break;
-      case W4_INT4_X_F16: e = launch_fx<kINT4, kF16>(a, tiles, kw, grid, s); break;
-      case W4_INT4_X_BF16: e = launch_fx<kINT4, kBF16>(a, tiles, kw, grid, s); break;
-      default: return hipErrorInvalidValue;
-    }
-    if (e != hipSuccess) return e;
+  MfmaPlan p;
+  if (!plan_mfma(n, k, b, &p)) return hipErrorNotSupported;
+  MfmaArgs a;
+  a.x = x;
+  a.packed = packed;
+  a.scales = scales;
+  a.y = y;
+  a.n = n;
+  a.k = k;
+  a.b = (int)b;
+  a.qpk = p.qpk;
+  a.qpp = p.qpp;
+  a.xrow = p.xrow;
+  a.tiles = p.ntiles;
+  switch (fmt) {
+    case W4_NF4_X_F16: return launch_fx<kNF4, kF16>(a, p.tiles, p.kw, p.grid, s);
+    case W4_NF4_X_BF16: return launch_fx<kNF4, kBF16>(a, p.tiles, p.kw, p.grid, s);
+    case W4_INT4_X_F16: return launch_fx<kINT4, kF16>(a, p.tiles, p.kw, p.grid, s);
+    case W4_INT4_X_BF16: return launch_fx<kINT4, kBF16>(a, p.tiles, p.kw, p.grid, s);
   }
-  return hipSuccess;
+  return hipErrorInvalidValue;
 }
 
 }  // namespace w4

@@ -65,7 +65,8 @@ typedef enum {
                           then a fixed-order sum that overwrites y (deterministic, no atomics;
                           My Triton Kernel Ties bitsandbytes, "The kernels", v3 and its
                           stale-output bug)                                                  */
-  W4_PATH_MFMA = 3,    /* dequantize W tiles on chip, MFMA against x, B >= 1 (meant for B >= 16) */
+  W4_PATH_MFMA = 3,    /* decode W on chip, MFMA against x, 1 <= B <= W4_MAX_BATCH (W4_PATH_AUTO
+                          takes it from B = 7, or B = 4 for matrices of 64 MiB and more)   */
   W4_PATH_TWOPASS = 4  /* ablation: dequantize W to fp16 in the workspace, then a dense GEMV/GEMM
                           (the out-of-place path of LLM Quantization on RTX 4060, "The
                           Quantization Tax: A Byte-Accounting Model")                        */
