@@ -45,7 +45,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTableBytes = 32768;   // 256 entries x 128 bytes
 constexpr int kThreads = 512;        // 8 waves
-constexpr int kXBytes = 128 * 1024;  // x window; the table takes the other 32 KiB of the 160 KiB
+constexpr int kLdsBytes = 160 * 1024;  // LDS of a CU: table, reduction area and x window
 constexpr int kQuad = 256;          // weights per quad
 constexpr int kMaxTiles = 8;        // up to 128 activation rows per launch
 
@@ -122,12 +122,15 @@ struct MfmaArgs {
   const uint8_t* packed;  // [N, K/2]
   const void* scales;     // NF4 float[N, K/64] | INT4 uint16[N, K/128]
   float* y;               // [B, N]
-  int64_t n, k;
-  int b;       // activation rows in all; slice blockIdx.y takes rows [16 T y, 16 T (y + 1))
-  int qpk;     // quads per K group
-  int qpp;     // quads per K group in one x window (one phase)
-  int xrow;    // bytes per activation row of the x window: KW * qpp * 512 + 16
-  int tiles;   // row tiles (16 * RW rows each) in all
+  uint32_t n, k;
+  uint32_t b;          // activation rows in all; slice blockIdx.y takes rows [16 T y, 16 T (y + 1))
+  uint32_t qpk;        // quads per K group
+  uint32_t qpp;        // quads per K group in one x window (one phase)
+  uint32_t xrow;       // bytes per activation row of the x window: (KW * 32 qpp + 1) * 16
+  uint32_t red_bytes;  // LDS bytes of the K-group reduction area (0 when KW == 1)
+  uint32_t tiles;      // row tiles (16 RW rows each) in all
+  uint32_t tiles_base;  // tiles per workgroup: tiles_base, plus one for blockIdx.x < tiles_rem
+  uint32_t tiles_rem;
 };
 
 // One quad in this lane's registers: 32 packed bytes of its A row (two 16-byte loads), and the
@@ -152,38 +155,42 @@ __device__ inline float row_bcast(uint32_t v) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + I, 0xF, 0xF, false));
 }
 
+// Waves per SIMD the kernel is compiled for: four (two workgroups per CU, <= 128 VGPRs) for one
+// batch tile, two above.
+constexpr int min_waves(int t) { return t == 1 ? 4 : 2; }
+
 template <int FMT, int XT, int T, int KW>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
-mfma_kernel(MfmaArgs a) {
+__global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a) {
   constexpr int RW = 8 / KW;
   constexpr int KC = FMT == kNF4 ? 64 : 128;  // weights per scale block
   constexpr int QC = kQuad / KC;              // blocks per quad
   constexpr int STEPS = KC / 32;              // MFMA steps per block
   constexpr int SB = FMT == kNF4 ? 4 : 2;     // bytes per scale
   constexpr bool kSplit = (FMT == kNF4 && XT == kBF16);
-  __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
-  __shared__ __align__(16) uint8_t xs[kXBytes];
+  // Dynamic LDS: the decode table, the K-group reduction area, then the x window.
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* tab = reinterpret_cast<uint32_t*>(smem);
+  float4_t* red = reinterpret_cast<float4_t*>(smem + kTableBytes);  // [KW - 1][RW][T][64 lanes]
+  uint8_t* xs = smem + kTableBytes + a.red_bytes;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rg = wave % RW, kg = wave / RW;
   const int g = lane >> 4, m = lane & 15;
-  const int64_t n = a.n, k = a.k;
-  const int64_t nblocks = k / KC;
-  const uint32_t pitch = (uint32_t)(k >> 1);
-  const uint32_t spitch = (uint32_t)(nblocks * SB);
-  // This workgroup's batch slice: activation rows [16 T y, 16 T y + bsl).
-  const int64_t b0 = (int64_t)blockIdx.y * 16 * T;
-  const int bsl = (int)min((int64_t)16 * T, (int64_t)a.b - b0);
-  const uint16_t* xsl = a.x + b0 * k;
-  float* ysl = a.y + b0 * n;
-  const __amdgpu_buffer_rsrc_t rx_ = make_rsrc(xsl, (uint32_t)(bsl * k * 2));
+  const uint32_t n = a.n, k = a.k;
+  const uint32_t nblocks = k / KC;
+  const uint32_t pitch = k >> 1;
+  const uint32_t spitch = nblocks * SB;
+  // This workgroup's batch slice: activation rows [16 T y, 16 T y + bsl); the window holds them.
+  const uint32_t b0 = blockIdx.y * 16u * T;
+  const uint32_t bsl = min(16u * T, a.b - b0);
+  const uint16_t* xsl = a.x + (size_t)b0 * k;
+  float* ysl = a.y + (size_t)b0 * n;
+  const __amdgpu_buffer_rsrc_t rx_ = make_rsrc(xsl, bsl * k * 2u);
 
-  // The workgroup's row tiles: blockIdx.x, blockIdx.x + gridDim.x, ...  A workgroup runs several
-  // tiles (a persistent grid) only when the whole of x fits one window and KW == 1; otherwise the
-  // grid has one workgroup per tile.
-  const int ntiles = ((int)a.tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int nq = a.qpk;               // quads per tile and wave
-  const int64_t len = (int64_t)ntiles * nq;  // this wave's stream of (tile, quad) positions
+  // The workgroup's row tiles: blockIdx.x, blockIdx.x + gridDim.x, ... (ntiles of them).
+  const int ntiles = (int)(a.tiles_base + (blockIdx.x < a.tiles_rem ? 1u : 0u));
+  const int nq = (int)a.qpk;         // quads per tile and wave
+  const int len = ntiles * nq;       // this wave's stream of (tile, quad) positions
 
   // Per-lane byte offsets inside a row tile: the A bytes of row m / lane group g, and the scale
   // row 4 g + (m & 3) (see Quad).
@@ -197,11 +204,11 @@ mfma_kernel(MfmaArgs a) {
     __amdgpu_buffer_rsrc_t rw, rs;
   };
   auto set_tile = [&](Cursor& c) __attribute__((always_inline)) {
-    const int64_t row_base = ((int64_t)(blockIdx.x + (int64_t)c.ti * gridDim.x) * RW + rg) * 16;
-    const int64_t rows_left = c.ti < ntiles ? n - row_base : 0;
-    const uint32_t rows = rows_left <= 0 ? 0u : rows_left >= 16 ? 16u : (uint32_t)rows_left;
-    c.rw = make_rsrc(a.packed + row_base * pitch, rows * pitch);
-    c.rs = make_rsrc(reinterpret_cast<const char*>(a.scales) + row_base * spitch, rows * spitch);
+    const uint32_t row_base = ((blockIdx.x + (uint32_t)c.ti * gridDim.x) * RW + rg) * 16u;
+    const uint32_t rows_left = c.ti < ntiles && row_base < n ? n - row_base : 0u;
+    const uint32_t rows = rows_left >= 16u ? 16u : rows_left;
+    c.rw = make_rsrc(a.packed + (size_t)row_base * pitch, rows * pitch);
+    c.rs = make_rsrc(reinterpret_cast<const char*>(a.scales) + (size_t)row_base * spitch, rows * spitch);
   };
   // (Branch-free: the counters stay scalar values the compiler can keep in registers.)
   auto advance = [&](Cursor& c) __attribute__((always_inline)) {
@@ -215,13 +222,13 @@ mfma_kernel(MfmaArgs a) {
   // bytes lie inside one block.
   const int lblk = FMT == kNF4 ? (g >> 1) : 0;  // block of this lane's bytes within a load
   auto load_quad = [&](const Cursor& cur, Quad<FMT>& d) __attribute__((always_inline)) {
-    const uint32_t qb = (uint32_t)((kg * a.qpk + cur.q) * QC);
+    const uint32_t qb = ((uint32_t)kg * a.qpk + (uint32_t)cur.q) * QC;
     const uint32_t wbase = wlane + qb * (KC / 2);
     const uint32_t sbase = slane + qb * SB;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int blk = FMT == kNF4 ? 2 * h + lblk : h;
-      const bool have = (int64_t)qb + blk < nblocks;
+      const bool have = qb + blk < nblocks;
       const uint4 v = buffer_load16_stream(cur.rw, offset_or_oob(have, wbase + 64u * h));
       d.w[h][0] = v.x;
       d.w[h][1] = v.y;
@@ -230,45 +237,43 @@ mfma_kernel(MfmaArgs a) {
     }
 #pragma unroll
     for (int c = 0; c < QC; ++c) {
-      const bool have = (int64_t)qb + c < nblocks;
+      const bool have = qb + c < nblocks;
       const uint32_t so = offset_or_oob(have, sbase) + (uint32_t)(c * SB);
       d.s[c] = FMT == kNF4 ? buffer_load32(cur.rs, so) : buffer_load16bit(cur.rs, so) << 16;
     }
   };
 
-  // x window of phase p: for every batch row r < 16 T and K group kk, its quads
-  // kk * qpk + p * qpp .. + qpp - 1; rows past B and k past K are zero.  The window is copied
-  // straight from global memory into LDS (buffer loads with the LDS destination): 16-byte slot
-  // s = tid + 512 j of the window area receives lane (s % 64)'s load, so slot s holds piece
-  // col = s % (rowp + 1) of row r = s / (rowp + 1), the last piece of a row being the padding.
-  const int xrow = a.xrow;
-  const int seg = a.qpp * (kQuad / 8);  // 16-byte pieces of one K group's segment of a row
-  const int rowp = KW * seg;            // data pieces per window row (<= 480)
-  const int slots = 16 * T * (rowp + 1);
-  const int nphase = (nq + a.qpp - 1) / a.qpp;
-  // Integer quotients through float reciprocals: s < 8192 and, after the + 0.5 offset, s / (rowp
-  // + 1) and col / seg stay at least 1 / 962 away from an integer, far above the error of the fp32
-  // reciprocal and product.
-  const float inv_row = 1.0f / (float)(rowp + 1);
+  // x window of phase p: for every batch row r < bsl and K group kk, the quads
+  // kk * qpk + p * qpp .. + qpp - 1 that the K group has (other pieces read as zero).  The window
+  // is copied straight from global memory into LDS (buffer loads with the LDS destination): the
+  // 16-byte slot s = base + tid receives thread tid's load, so slot s holds piece
+  // col = s % P of row r = s / P, P = KW * seg + 1 pieces per row, the last one padding (it puts
+  // consecutive rows four banks apart).  Only the slots of the bsl rows are loaded.
+  const uint32_t seg = a.qpp * 32u;  // 16-byte pieces of one K group's segment of a row
+  const uint32_t P = (uint32_t)KW * seg + 1u;
+  const uint32_t slots = bsl * P;
+  const uint32_t nphase = (a.qpk + a.qpp - 1) / a.qpp;
+  // Row of slot s and K group of piece col through float reciprocals: with the + 0.5 offset,
+  // (s + 0.5) / P is at least 1 / (2 P) away from an integer, and bsl * P <= 8192 (the window fits
+  // 128 KiB) keeps the fp32 error, at most bsl * 2^-23, far below that; likewise (col + 0.5) / seg
+  // (error at most KW * 2^-23, margin 1 / (2 seg) >= 2^-14).
+  const float inv_p = 1.0f / (float)P;
   const float inv_seg = 1.0f / (float)seg;
-  constexpr int kXPer = kXBytes / 16 / kThreads;  // 16 slots per thread cover the whole area
-  auto load_x = [&](int p) __attribute__((always_inline)) {
-    const int64_t kbase = (int64_t)p * a.qpp * kQuad;
-    // Recomputed at each window rather than kept live across the main loop (registers).
-    int t0 = tid;
-    asm volatile("" : "+v"(t0));
-#pragma unroll
-    for (int j = 0; j < kXPer; ++j) {
-      const int sl = t0 + j * kThreads;
-      const int r = (int)(((float)sl + 0.5f) * inv_row);
-      const int col = sl - r * (rowp + 1);
-      const int kk = (int)(((float)col + 0.5f) * inv_seg);
-      const int pc = col - kk * seg;
-      const int64_t kpos = (int64_t)kk * a.qpk * kQuad + kbase + (int64_t)pc * 8;
-      const bool have = sl < slots && col < rowp && r < bsl && kpos < k;
+  auto load_x = [&](uint32_t p) __attribute__((always_inline)) {
+    const uint32_t q0 = p * a.qpp;  // first quad of the phase inside each K group
+    for (uint32_t base = 0; base < slots; base += kThreads) {
+      uint32_t sl = base + (uint32_t)tid;
+      asm volatile("" : "+v"(sl));
+      const uint32_t r = (uint32_t)(((float)sl + 0.5f) * inv_p);
+      const uint32_t col = sl - r * P;
+      const uint32_t kk = (uint32_t)(((float)col + 0.5f) * inv_seg);
+      const uint32_t pc = col - kk * seg;
+      const uint32_t ql = q0 + (pc >> 5);  // quad inside the K group
+      const uint32_t kpos = (kk * a.qpk + ql) * kQuad + (pc & 31u) * 8u;
+      const bool have = sl < slots && kk < (uint32_t)KW && ql < a.qpk && kpos < k;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx_, (__attribute__((address_space(3))) void*)(xs + (j * kThreads + wave * 64) * 16), 16,
-          (int)offset_or_oob(have, (uint32_t)((r * k + kpos) * 2)), 0, 0, 0);
+          rx_, (__attribute__((address_space(3))) void*)(xs + (base + (uint32_t)wave * 64u) * 16u), 16,
+          (int)offset_or_oob(have, (r * k + kpos) * 2u), 0, 0, 0);
     }
   };
 
@@ -301,7 +306,7 @@ mfma_kernel(MfmaArgs a) {
   // Twice this lane's byte offset in a table entry (see the lookup below).
   const uint32_t laneoff = kSplit ? (uint32_t)(lane & 15) * 16u : (uint32_t)(lane & 31) * 8u;
   const char* tabc = reinterpret_cast<const char*>(tab);
-  const uint8_t* xw = xs + kg * (seg * 16) + m * xrow;  // this lane's B row (tile 0), K group kg
+  const uint8_t* xw = xs + (uint32_t)kg * (seg * 16u);  // this K group's part of the window
 
   // k offset (in the block) of the first of this lane's weights for MFMA step 0 (see Quad).
   const int klane = FMT == kNF4 ? 32 * (g & 1) + 16 * (g >> 1) : 32 * g;
@@ -328,6 +333,14 @@ mfma_kernel(MfmaArgs a) {
       }
     }
     const uint8_t* xq = xw + (wq * kQuad + klane) * 2;
+    // This lane's B rows: activation row 16 t + m of the slice, or the last one held when the
+    // slice is shorter (those columns of D are never stored).  Recomputed per quad (the opaque
+    // copy of the limit keeps the compiler from holding T offsets across the main loop).
+    uint32_t blim = bsl - 1u;
+    asm volatile("" : "+s"(blim));
+    uint32_t xrowoff[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xrowoff[t] = min((uint32_t)(16 * t + m), blim) * a.xrow;
 #pragma unroll
     for (int c = 0; c < QC; ++c) {
       float4_t dd[T];
@@ -353,8 +366,7 @@ mfma_kernel(MfmaArgs a) {
         const uint4 a1 = make_uint4(p1[0], p1[1], p1[2], p1[3]);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          const uint4 bv =
-              *reinterpret_cast<const uint4*>(xq + 16 * t * xrow + (c * KC + s * 8) * 2);
+          const uint4 bv = *reinterpret_cast<const uint4*>(xq + xrowoff[t] + (c * KC + s * 8) * 2);
           dd[t] = mfma<XT>(a1, bv, dd[t]);
           if (kSplit) dd[t] = mfma<XT>(make_uint4(p2[0], p2[1], p2[2], p2[3]), bv, dd[t]);
         }
@@ -372,13 +384,12 @@ mfma_kernel(MfmaArgs a) {
     }
   };
 
-  // y rows of tile ti: after its last quad, K groups add up (KW > 1, one tile per workgroup) and
+  // y rows of tile ti: after its last quad, K groups add up in the reduction area (KW > 1) and
   // kg == 0 stores; lane (g, m) holds y[16 t + m][row_d + i], i = 0..3.
   auto finish_tile = [&](int ti) __attribute__((always_inline)) {
-    const int64_t row_d = ((int64_t)(blockIdx.x + (int64_t)ti * gridDim.x) * RW + rg) * 16 + 4 * g;
+    const uint32_t row_d = ((blockIdx.x + (uint32_t)ti * gridDim.x) * RW + rg) * 16u + 4u * g;
     if constexpr (KW > 1) {
-      float4_t* red = reinterpret_cast<float4_t*>(xs);  // [KW - 1][RW][T][64 lanes]
-      __syncthreads();
+      __syncthreads();  // the previous tile's sums have been read
       if (kg > 0) {
 #pragma unroll
         for (int t = 0; t < T; ++t) red[(((kg - 1) * RW + rg) * T + t) * 64 + lane] = acc[t];
@@ -398,9 +409,9 @@ mfma_kernel(MfmaArgs a) {
     if (kg == 0) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const int b = 16 * t + m;
+        const uint32_t b = 16u * t + m;
         if (b < bsl) {
-          float* yr = ysl + (int64_t)b * n;
+          float* yr = ysl + (size_t)b * n;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (row_d + i < n) yr[row_d + i] = acc[t][i];
@@ -412,17 +423,17 @@ mfma_kernel(MfmaArgs a) {
     for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
   };
 
-  // One stream position with the quad in d: a new x window at every multiple of qpp quads (only
-  // when the tile needs several windows, i.e. one tile per workgroup), the multiply, the refill of
-  // d R positions ahead, and the end of the tile after its last quad.
+  // One stream position with the quad in d: a new x window at every multiple of qpp quads when a
+  // K group needs several windows (also back to phase 0 at each new tile), the multiply, the
+  // refill of d R positions ahead, and the end of the tile after its last quad.
   int ct = 0, cq = 0;
   auto step = [&](Quad<FMT>& d) __attribute__((always_inline)) {
-    if (nphase > 1 && cq > 0 && cq % a.qpp == 0) {
+    if (nphase > 1 && (cq > 0 || ct > 0) && cq % a.qpp == 0) {
       __syncthreads();  // every wave is done with the old window
-      load_x(cq / a.qpp);
+      load_x((uint32_t)cq / a.qpp);
       __syncthreads();
     }
-    compute(nphase > 1 ? cq % a.qpp : cq, d);
+    compute(nphase > 1 ? cq % (int)a.qpp : cq, d);
     load_quad(ld, d);
     advance(ld);
     const bool last = cq == nq - 1;
@@ -433,7 +444,7 @@ mfma_kernel(MfmaArgs a) {
 
   // Main loop: R positions per trip, the register sets rotating without copies; the last
   // positions are already loaded when it ends.
-  int64_t j = 0;
+  int j = 0;
   if constexpr (R == 4) {
     for (; j + 4 <= len; j += 4) {
       step(P0);
@@ -453,89 +464,138 @@ mfma_kernel(MfmaArgs a) {
   }
 }
 
-// K groups the x window allows for T batch tiles (plan_mfma never asks for more): 8 / 4 / 2 / 1.
+// K groups instantiated for T batch tiles: 8 / 4 / 2 / 1.
 constexpr int max_kw(int t) { return t == 1 ? 8 : t == 2 ? 4 : t == 4 ? 2 : 1; }
 
+// Workgroups of one instantiation that fit a CU with `lds` bytes of dynamic LDS (registers and
+// LDS), from the runtime; the dynamic LDS limit is raised once per instantiation.
 template <int FMT, int XT, int T, int KW>
-hipError_t launch_kw(const MfmaArgs& a, int grid, hipStream_t s) {
-  const unsigned slices = (unsigned)((a.b + 16 * T - 1) / (16 * T));
-  hipLaunchKernelGGL((mfma_kernel<FMT, XT, T, KW>), dim3((unsigned)grid, slices), dim3(kThreads), 0,
-                     s, a);
+int resident_kw(int lds) {
+  static bool raised = false;
+  if (!raised) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_kernel<FMT, XT, T, KW>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    raised = true;
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &nb, reinterpret_cast<const void*>(&mfma_kernel<FMT, XT, T, KW>), kThreads, lds) !=
+      hipSuccess)
+    return 0;
+  return nb;
+}
+
+template <int FMT, int XT, int T, int KW>
+hipError_t launch_kw(const MfmaArgs& a, int lds, int grid, int slices, hipStream_t s) {
+  hipLaunchKernelGGL((mfma_kernel<FMT, XT, T, KW>), dim3((unsigned)grid, (unsigned)slices),
+                     dim3(kThreads), (unsigned)lds, s, a);
   return hipGetLastError();
 }
 
+// Instantiation dispatch: op 0 = resident workgroups per CU (returned in *out), op 1 = launch.
 template <int FMT, int XT, int T>
-hipError_t launch_t(const MfmaArgs& a, int kw, int grid, hipStream_t s) {
+hipError_t dispatch_t(int op, const MfmaArgs& a, int kw, int lds, int grid, int slices, int* out,
+                      hipStream_t s) {
   if (kw > max_kw(T)) return hipErrorInvalidValue;
-  switch (kw) {
-    case 1: return launch_kw<FMT, XT, T, 1>(a, grid, s);
-    case 2: if constexpr (max_kw(T) >= 2) return launch_kw<FMT, XT, T, 2>(a, grid, s); break;
-    case 4: if constexpr (max_kw(T) >= 4) return launch_kw<FMT, XT, T, 4>(a, grid, s); break;
-    case 8: if constexpr (max_kw(T) >= 8) return launch_kw<FMT, XT, T, 8>(a, grid, s); break;
+#define W4_MFMA_KW(KWV)                                                    \
+  if (kw == KWV) {                                                         \
+    if constexpr (max_kw(T) >= KWV) {                                      \
+      if (op == 0) {                                                       \
+        *out = resident_kw<FMT, XT, T, KWV>(lds);                          \
+        return hipSuccess;                                                 \
+      }                                                                    \
+      return launch_kw<FMT, XT, T, KWV>(a, lds, grid, slices, s);          \
+    }                                                                      \
   }
+  W4_MFMA_KW(1)
+  W4_MFMA_KW(2)
+  W4_MFMA_KW(4)
+  W4_MFMA_KW(8)
+#undef W4_MFMA_KW
   return hipErrorInvalidValue;
 }
 
 template <int FMT, int XT>
-hipError_t launch_fx(const MfmaArgs& a, int tiles, int kw, int grid, hipStream_t s) {
+hipError_t dispatch_fx(int op, const MfmaArgs& a, int tiles, int kw, int lds, int grid, int slices,
+                       int* out, hipStream_t s) {
   switch (tiles) {
-    case 1: return launch_t<FMT, XT, 1>(a, kw, grid, s);
-    case 2: return launch_t<FMT, XT, 2>(a, kw, grid, s);
-    case 4: return launch_t<FMT, XT, 4>(a, kw, grid, s);
-    case 8: return launch_t<FMT, XT, 8>(a, kw, grid, s);
+    case 1: return dispatch_t<FMT, XT, 1>(op, a, kw, lds, grid, slices, out, s);
+    case 2: return dispatch_t<FMT, XT, 2>(op, a, kw, lds, grid, slices, out, s);
+    case 4: return dispatch_t<FMT, XT, 4>(op, a, kw, lds, grid, slices, out, s);
+    case 8: return dispatch_t<FMT, XT, 8>(op, a, kw, lds, grid, slices, out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch(int op, int fmt, const MfmaArgs& a, int tiles, int kw, int lds, int grid,
+                    int slices, int* out, hipStream_t s) {
+  switch (fmt) {
+    case W4_NF4_X_F16: return dispatch_fx<kNF4, kF16>(op, a, tiles, kw, lds, grid, slices, out, s);
+    case W4_NF4_X_BF16: return dispatch_fx<kNF4, kBF16>(op, a, tiles, kw, lds, grid, slices, out, s);
+    case W4_INT4_X_F16: return dispatch_fx<kINT4, kF16>(op, a, tiles, kw, lds, grid, slices, out, s);
+    case W4_INT4_X_BF16: return dispatch_fx<kINT4, kBF16>(op, a, tiles, kw, lds, grid, slices, out, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Launch shape of the MFMA kernel for one batch slice of T tiles: K groups, quads per K group and
-// per x window, row tiles and workgroups along x.  K groups split K inside a workgroup when N alone
-// gives too few workgroups: the smallest KW of 1, 2, 4, 8 that gives at least one workgroup per CU
-// (counting the `slices` batch slices), within what the x window holds.
+// Launch shape of the MFMA kernel for one batch slice of T tiles.  K groups split K inside a
+// workgroup when N alone gives too few row tiles: the smallest KW of 1, 2, 4, 8 that gives a row
+// tile per CU (counting the batch slices).  The x window holds the slice's rows and as many quads
+// per K group as fit the LDS next to the table and the reduction area, in phases of equal size.
+// Every workgroup of the launch is resident at once: the grid is at most what fits the GPU (from
+// the runtime's occupancy for the LDS in use), and a workgroup walks several row tiles when there
+// are more tiles than that.
 struct MfmaPlan {
-  int tiles, kw, qpk, qpp, xrow, ntiles, grid, slices;
+  int tiles, kw, qpk, qpp, xrow, red, lds, ntiles, slices;
 };
 
 bool plan_slice(int64_t n, int64_t k, int64_t b, int t, MfmaPlan* p) {
   const int64_t quads = (k + kQuad - 1) / kQuad;
   const int64_t cus = device_cu_count();
   const int slices = (int)((b + 16 * t - 1) / (16 * t));
-  const int row_budget = kXBytes / (16 * t);          // window bytes per activation row
-  const int max_q = (row_budget - 16) / (kQuad * 2);  // quads per window row, all K groups
-  if (max_q < 1) return false;
-  int best = 1;
-  for (int c = 1; c <= 8; c *= 2) {
-    if (c > max_q || c > quads) break;
-    best = c;
+  const int64_t rows_held = std::min<int64_t>(16 * t, b);
+  int kw = 1;
+  for (int c = 1; c <= max_kw(t); c *= 2) {
+    if (c > quads) break;
+    kw = c;
     const int64_t rows = 16 * (8 / c);
     if ((n + rows - 1) / rows * slices >= cus) break;
   }
-  const int64_t per_kg = (quads + best - 1) / best;
-  const int per_phase = std::max(1, max_q / best);
+  const int64_t qpk = (quads + kw - 1) / kw;
+  const int64_t red = kw > 1 ? (int64_t)(kw - 1) * (8 / kw) * t * 1024 : 0;
+  const int64_t budget = kLdsBytes - kTableBytes - red;
+  int64_t qpp = qpk;
+  // Window bytes, rounded up to whole rounds of 512 16-byte slots (each thread's last load may land
+  // past the slots in use, inside the allocation).
+  auto window = [&](int64_t q) {
+    const int64_t slots = rows_held * ((int64_t)kw * 32 * q + 1);
+    return (slots + kThreads - 1) / kThreads * kThreads * 16;
+  };
+  while (qpp > 1 && window(qpp) > budget) --qpp;
+  if (window(qpp) > budget) return false;
+  const int64_t nphase = (qpk + qpp - 1) / qpp;
+  qpp = (qpk + nphase - 1) / nphase;  // the same number of phases, balanced
   p->tiles = t;
-  p->kw = best;
-  p->qpk = (int)per_kg;
-  p->qpp = (int)std::min<int64_t>(per_kg, per_phase);
-  p->xrow = best * p->qpp * kQuad * 2 + 16;
-  // Row tiles and workgroups: one workgroup per CU walks several tiles when x fits one window and
-  // K is not split (the window and the table are then filled once per workgroup, and each wave's
-  // stream of quads runs across its tiles without a pipeline restart); else one per tile.
-  const int64_t rows = 16 * (8 / best);
-  const int64_t ntile = (n + rows - 1) / rows;
-  p->ntiles = (int)ntile;
-  p->grid = (best == 1 && p->qpp >= per_kg)
-                ? (int)std::min<int64_t>(ntile, std::max<int64_t>(1, cus / slices))
-                : (int)ntile;
+  p->kw = kw;
+  p->qpk = (int)qpk;
+  p->qpp = (int)qpp;
+  p->xrow = (int)(((int64_t)kw * 32 * qpp + 1) * 16);
+  p->red = (int)red;
+  p->lds = (int)(kTableBytes + red + window(qpp));
+  p->ntiles = (int)((n + 16 * (8 / kw) - 1) / (16 * (8 / kw)));
   p->slices = slices;
   return true;
 }
 
 // Batch tiles per slice: the largest T (8, 4, 2, 1; at most what B needs) whose launch has at
-// least half a workgroup per CU; slices beyond the first re-read the weights (mostly from L2).
-// Byte offsets are 32-bit: a slice's activations (16 T * K * 2 bytes) must stay below 2^31.
+// least half a row tile per CU; slices beyond the first re-read the weights (mostly from L2).
+// Offsets are 32-bit: a slice's activations (16 T K 2 bytes) and K itself are bounded below.
 bool plan_mfma(int64_t n, int64_t k, int64_t b, MfmaPlan* out) {
-  if (b < 1 || b > W4_MAX_BATCH || 16 * kMaxTiles * k * 2 >= ((int64_t)1 << 31)) return false;
+  if (b < 1 || b > W4_MAX_BATCH || k >= ((int64_t)1 << 22) || n >= ((int64_t)1 << 31) ||
+      16 * kMaxTiles * k * 2 >= ((int64_t)1 << 31))
+    return false;
   const int64_t cus = device_cu_count();
   const int need = (int)std::min<int64_t>((b + 15) / 16, kMaxTiles);
   const int tmax = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
@@ -544,11 +604,11 @@ bool plan_mfma(int64_t n, int64_t k, int64_t b, MfmaPlan* out) {
   for (int t = tmax; t >= 1; t /= 2) {
     MfmaPlan p;
     if (!plan_slice(n, k, b, t, &p)) continue;
-    if (!found || (int64_t)p.grid * p.slices > (int64_t)best.grid * best.slices) {
+    if (!found || (int64_t)p.ntiles * p.slices > (int64_t)best.ntiles * best.slices) {
       best = p;
       found = true;
     }
-    if ((int64_t)p.grid * p.slices * 2 >= cus) {
+    if ((int64_t)p.ntiles * p.slices * 2 >= cus) {
       best = p;
       break;
     }
@@ -567,20 +627,23 @@ hipError_t launch_mfma(int fmt, const uint16_t* x, const uint8_t* packed, const 
   a.packed = packed;
   a.scales = scales;
   a.y = y;
-  a.n = n;
-  a.k = k;
-  a.b = (int)b;
-  a.qpk = p.qpk;
-  a.qpp = p.qpp;
-  a.xrow = p.xrow;
-  a.tiles = p.ntiles;
-  switch (fmt) {
-    case W4_NF4_X_F16: return launch_fx<kNF4, kF16>(a, p.tiles, p.kw, p.grid, s);
-    case W4_NF4_X_BF16: return launch_fx<kNF4, kBF16>(a, p.tiles, p.kw, p.grid, s);
-    case W4_INT4_X_F16: return launch_fx<kINT4, kF16>(a, p.tiles, p.kw, p.grid, s);
-    case W4_INT4_X_BF16: return launch_fx<kINT4, kBF16>(a, p.tiles, p.kw, p.grid, s);
-  }
-  return hipErrorInvalidValue;
+  a.n = (uint32_t)n;
+  a.k = (uint32_t)k;
+  a.b = (uint32_t)b;
+  a.qpk = (uint32_t)p.qpk;
+  a.qpp = (uint32_t)p.qpp;
+  a.xrow = (uint32_t)p.xrow;
+  a.red_bytes = (uint32_t)p.red;
+  a.tiles = (uint32_t)p.ntiles;
+  int resident = 0;
+  hipError_t e = dispatch(0, fmt, a, p.tiles, p.kw, p.lds, 0, 0, &resident, s);
+  if (e != hipSuccess) return e;
+  if (resident < 1) return hipErrorNotSupported;
+  const int64_t fit = std::max<int64_t>(1, (int64_t)device_cu_count() * resident / p.slices);
+  const int grid = (int)std::min<int64_t>(p.ntiles, fit);
+  a.tiles_base = (uint32_t)(p.ntiles / grid);
+  a.tiles_rem = (uint32_t)(p.ntiles % grid);
+  return dispatch(1, fmt, a, p.tiles, p.kw, p.lds, grid, p.slices, nullptr, s);
 }
 
 }  // namespace w4

@@ -52,3 +52,30 @@ def test_mfma_deterministic(fmt):
     y1 = w4.matmul_ex(xd, p, s, fmt, path="mfma")
     y2 = w4.matmul_ex(xd, p, s, fmt, path="mfma")
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("fmt,n,k,b", [("nf4_f16", 151936, 1536, 8), ("nf4_bf16", 151936, 1536, 128),
+                                       ("int4_f16", 1536, 8960, 8), ("int4_bf16", 8960, 1536, 32),
+                                       ("nf4_f16", 28672, 8192, 16)])
+def test_mfma_full_size_sampled(fmt, n, k, b):
+    """Full-size matrices (persistent grids with several row tiles per workgroup, K groups, x
+    windows in several phases): weights drawn on the GPU, quantized there, and 160 sampled rows
+    (the first and the last among them) checked against the oracle."""
+    import numpy as np
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    dev = g.device()
+    gen = torch.Generator(device=dev).manual_seed(n + 3 * k + b)
+    w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+    p, s = g.gpu_quantize(fmt, w)
+    rng = np.random.default_rng(n + b)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 158, replace=False)]))
+    w_rows = w[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    del w
+    pr, sr = g.oracle_quantize(fmt, w_rows)
+    g.assert_quant_equal(fmt, p, s, pr, sr, rows=rows)
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=b + 5)
+    y = w4.matmul_ex(g.to_dev_x(x, g.XDT[fmt]), p, s, fmt, path="mfma")
+    g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
