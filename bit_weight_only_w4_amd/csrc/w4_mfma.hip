@@ -235,11 +235,21 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
       d.w[h][2] = v.z;
       d.w[h][3] = v.w;
     }
+    // NF4: the quad's four fp32 scales of this lane's row are contiguous (dword aligned), one
+    // 16-byte load; blocks past K are zeroed here (inside the matrix their bytes are the next
+    // row's).  INT4: two bf16 scales, 2-byte aligned, two loads.
+    if constexpr (FMT == kNF4) {
+      const uint4 sv = buffer_load16(cur.rs, offset_or_oob(qb < nblocks, sbase));
+      d.s[0] = sv.x;
+      d.s[1] = qb + 1 < nblocks ? sv.y : 0u;
+      d.s[2] = qb + 2 < nblocks ? sv.z : 0u;
+      d.s[3] = qb + 3 < nblocks ? sv.w : 0u;
+    } else {
 #pragma unroll
-    for (int c = 0; c < QC; ++c) {
-      const bool have = qb + c < nblocks;
-      const uint32_t so = offset_or_oob(have, sbase) + (uint32_t)(c * SB);
-      d.s[c] = FMT == kNF4 ? buffer_load32(cur.rs, so) : buffer_load16bit(cur.rs, so) << 16;
+      for (int c = 0; c < QC; ++c) {
+        const bool have = qb + c < nblocks;
+        d.s[c] = buffer_load16bit(cur.rs, offset_or_oob(have, sbase) + (uint32_t)(c * SB)) << 16;
+      }
     }
   };
 
@@ -284,20 +294,22 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   ld.ti = 0;
   ld.q = 0;
   set_tile(ld);
+  // Two quads go out before the window and the table, the other two after the barrier (which
+  // waits for every load in flight): the prologue's loads stay few.
   Quad<FMT> P0, P1, P2, P3;
   load_quad(ld, P0);
   advance(ld);
   load_quad(ld, P1);
   advance(ld);
+  load_x(0);
+  fill_table<FMT, XT>(tab);
+  __syncthreads();
   if constexpr (R == 4) {
     load_quad(ld, P2);
     advance(ld);
     load_quad(ld, P3);
     advance(ld);
   }
-  load_x(0);
-  fill_table<FMT, XT>(tab);
-  __syncthreads();
 
   float4_t acc[T];
 #pragma unroll
