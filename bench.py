@@ -36,8 +36,9 @@ def parse_args():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--suite", default="decode", choices=["decode", "shapes"],
-                    help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table")
+    ap.add_argument("--suite", default="decode", choices=["decode", "shapes", "counters"],
+                    help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table; "
+                         "counters: a few launches of each path, for rocprofv3 --pmc runs")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per kernel class / shape kind when timing launches")
     ap.add_argument("--schedule", default="grouped", choices=["serial", "grouped", "dag"],
@@ -45,6 +46,9 @@ def parse_args():
                          "q|k|v and gate|up each in one grouped launch; dag: 197 launches with "
                          "q|k|v and gate|up as graph branches")
     ap.add_argument("--report", default=None, help="write a detailed JSON report here")
+    ap.add_argument("--counters-from", nargs="+", metavar="PMC_DIR", default=None,
+                    help="CPU only: turn rocprofv3 --pmc runs of --suite counters into per-path "
+                         "instruction counts (profiles/counters_paths.json), then exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="CPU only: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script into the stored per-kernel HBM traffic, then exit")
@@ -552,6 +556,34 @@ def time_shape(fmt, n, k, b, path, split_k, dev, min_bytes=600 << 20, reps=5):
     return ms * 1e3 / launches, None
 
 
+def time_read_probe(nbytes, dev, min_bytes=600 << 20, reps=5):
+    """Size-matched streaming-read ceiling: the library's read probe over `nbytes` per launch,
+    rotated over enough buffers to exceed the last-level cache, as a graph of launches timed like
+    time_shape.  Returns us per launch."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    nbytes = (nbytes + 15) // 16 * 16
+    copies = max(1, min(4096, -(-min_bytes // nbytes)))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    launches = max(copies, 16)
+    s0 = torch.cuda.Stream(device=dev)
+    s0.wait_stream(torch.cuda.current_stream())
+    for r in range(launches):
+        w4.probe_read(bufs[r % copies], sink, stream=s0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s0):
+        for r in range(launches):
+            w4.probe_read(bufs[r % copies], sink, stream=s0)
+    ms = time_replays(g, reps, 2)
+    del g, bufs
+    torch.cuda.empty_cache()
+    return ms * 1e3 / launches
+
+
 def shapes_suite(args, dev):
     """Per-shape table for the other workloads: INT4 decode steps (B = 1, 8) and split-K vs one
     pass on down; small-batch GEMM on gate / down / lm_head at B = 1, 8, 32, 128 for the GEMV,
@@ -560,10 +592,13 @@ def shapes_suite(args, dev):
     import synth_inputs
 
     rows = []
+    probe_us = {}
 
     def add(group, fmt, name, n, k, b, path, split_k=0):
         us, err = time_shape(fmt, n, k, b, path, split_k, dev)
         ab = algorithmic_bytes(fmt, n, k, b)
+        if ab not in probe_us:
+            probe_us[ab] = time_read_probe(ab, dev)
         r = {"group": group, "fmt": fmt, "shape": name, "n": n, "k": k, "b": b, "path": path,
              "split_k": split_k, "algorithmic_bytes": ab}
         if us is None:
@@ -573,9 +608,13 @@ def shapes_suite(args, dev):
             r["gbs"] = round(ab / us / 1e3, 1)
             r["frac_hbm"] = round(ab / us / 1e3 / HBM_PEAK_GBS, 4)
             r["tflops"] = round(2.0 * n * k * b / us / 1e6, 2)
+            # the same bytes through the streaming-read probe, launched the same way
+            r["read_probe_us"] = round(probe_us[ab], 3)
+            r["frac_size_matched_read"] = round(probe_us[ab] / us, 4)
         rows.append(r)
         log(f"[shapes] {group:10s} {fmt:9s} {name:8s} {n:6d}x{k:5d} B={b:3d} {path:7s} S={split_k:2d} "
-            + (f"{r['us']:9.2f} us {r['gbs']:8.0f} GB/s {r['tflops']:7.2f} TFLOP/s" if us else f"ERR {err}"))
+            + (f"{r['us']:9.2f} us {r['gbs']:8.0f} GB/s {r['tflops']:7.2f} TFLOP/s "
+               f"(read probe {r['read_probe_us']:.2f} us)" if us else f"ERR {err}"))
 
     # INT4 g128, bf16 x: the five decode shapes at B = 1 and 8; split-K vs one pass on down
     for b in (1, 8):
@@ -608,14 +647,140 @@ def shapes_suite(args, dev):
     return rows
 
 
+# Launches whose instruction mix the counter runs record: (name, format, N, K, B, path).
+COUNTER_CASES = [
+    ("gemv nf4 gate B=1", "nf4_f16", 8960, 1536, 1, "gemv"),
+    ("gemv nf4 down B=1", "nf4_f16", 1536, 8960, 1, "gemv"),
+    ("gemv nf4 lm_head B=1", "nf4_f16", 151936, 1536, 1, "gemv"),
+    ("gemv int4 gate B=1", "int4_bf16", 8960, 1536, 1, "gemv"),
+    ("gemv nf4 gate B=4", "nf4_f16", 8960, 1536, 4, "gemv"),
+    ("mfma nf4 gate B=8", "nf4_f16", 8960, 1536, 8, "mfma"),
+    ("mfma nf4 gate B=32", "nf4_f16", 8960, 1536, 32, "mfma"),
+    ("mfma nf4 gate B=128", "nf4_f16", 8960, 1536, 128, "mfma"),
+    ("mfma nf4 lm_head B=8", "nf4_f16", 151936, 1536, 8, "mfma"),
+    ("mfma nf4 lm_head B=32", "nf4_f16", 151936, 1536, 32, "mfma"),
+    ("mfma nf4 lm_head B=128", "nf4_f16", 151936, 1536, 128, "mfma"),
+    ("twopass nf4 gate B=1", "nf4_f16", 8960, 1536, 1, "twopass"),
+]
+COUNTER_LAUNCHES = 3
+COUNTER_KERNELS = ("gemv_kernel", "mfma_kernel", "dequant", "dense")
+
+
+def counters_suite(dev):
+    """COUNTER_LAUNCHES launches of every COUNTER_CASES entry, in order, after all inputs are
+    made (so that the only library launches in the run are these)."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    made = []
+    for name, fmt, n, k, b, path in COUNTER_CASES:
+        gen = torch.Generator(device=dev).manual_seed(n + k)
+        w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+        p, sc = w4.quantize_nf4(w) if fmt.startswith("nf4") else w4.quantize_int4(w)
+        del w
+        xdt = torch.float16 if fmt.endswith("_f16") else torch.bfloat16
+        x = torch.randn(b, k, generator=gen, device=dev).to(xdt)
+        ws = None
+        if path == "twopass":
+            ws = torch.empty(w4.workspace_bytes(fmt, n, k, b, path, 0), dtype=torch.uint8, device=dev)
+        made.append((p, sc, x, ws))
+    torch.cuda.synchronize()
+    for (name, fmt, n, k, b, path), (p, sc, x, ws) in zip(COUNTER_CASES, made):
+        for _ in range(COUNTER_LAUNCHES):
+            w4.matmul_ex(x, p, sc, fmt, path=path, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"[counters] {name}: {COUNTER_LAUNCHES} launches")
+
+
+def counters_from(dirs):
+    """Per-launch SQ/GRBM counter averages of every COUNTER_CASES entry from rocprofv3 --pmc runs
+    of --suite counters (one counter set per directory), with VALU instructions per MAC
+    (64 lanes * SQ_INSTS_VALU / (B N K)) and MFMA busy cycles per MFMA instruction.  CPU-only."""
+    import collections
+    import csv
+
+    per_case = [collections.defaultdict(list) for _ in COUNTER_CASES]
+    meta = [dict() for _ in COUNTER_CASES]
+    for d in dirs:
+        disp = collections.OrderedDict()
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if not any(kw in r["Kernel_Name"] for kw in COUNTER_KERNELS):
+                    continue
+                e = disp.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"],
+                                                            "grid": int(r["Grid_Size"]),
+                                                            "vgpr": int(r["VGPR_Count"]),
+                                                            "lds": int(r["LDS_Block_Size"]),
+                                                            "c": {}})
+                e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        ids = sorted(disp)
+        pos = 0
+        for ci, (name, fmt, n, k, b, path) in enumerate(COUNTER_CASES):
+            per_launch = 2 if path == "twopass" else 1
+            for _ in range(COUNTER_LAUNCHES):
+                group = [disp[i] for i in ids[pos:pos + per_launch]]
+                pos += per_launch
+                if len(group) != per_launch:
+                    raise SystemExit(f"counters: {d} ends before case {name!r}")
+                tot = collections.Counter()
+                for e in group:
+                    tot.update(e["c"])
+                for cname, v in tot.items():
+                    per_case[ci][cname].append(v)
+                meta[ci] = {"kernels": [e["kernel"].replace("void ", "").replace(
+                    "w4::(anonymous namespace)::", "").split("(")[0] for e in group],
+                    "grid": [e["grid"] for e in group], "vgpr": [e["vgpr"] for e in group],
+                    "lds": [e["lds"] for e in group]}
+        if pos != len(ids):
+            raise SystemExit(f"counters: {d} has {len(ids) - pos} library dispatches past the cases")
+    out = []
+    for ci, (name, fmt, n, k, b, path) in enumerate(COUNTER_CASES):
+        c = {cn: sum(v) / len(v) for cn, v in per_case[ci].items()}
+        rec = {"case": name, "fmt": fmt, "n": n, "k": k, "b": b, "path": path, **meta[ci],
+               "counters_per_launch": {cn: round(v, 1) for cn, v in sorted(c.items())}}
+        macs = float(b) * n * k
+        if "SQ_INSTS_VALU" in c:
+            rec["valu_insts_per_mac"] = round(64.0 * c["SQ_INSTS_VALU"] / macs, 4)
+        if "SQ_INSTS_LDS" in c:
+            rec["lds_insts_per_mac"] = round(64.0 * c["SQ_INSTS_LDS"] / macs, 4)
+        if c.get("SQ_INSTS_MFMA"):
+            rec["mfma_insts"] = round(c["SQ_INSTS_MFMA"], 1)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                rec["mfma_busy_cycles_per_mfma_inst"] = round(
+                    c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_INSTS_MFMA"], 2)
+        out.append(rec)
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "counters_paths.json")
+    with open(path, "w") as f:
+        json.dump({"launches_per_case": COUNTER_LAUNCHES, "sources": sorted(dirs), "cases": out},
+                  f, indent=1)
+        f.write("\n")
+    return path, out
+
+
 def main():
     args = parse_args()
+    if args.counters_from:
+        path, out = counters_from(args.counters_from)
+        print(json.dumps({"counters": path, "cases": len(out)}))
+        return
     if args.traffic_from:
         out = traffic_path(args.fmt, args.batch, args.path, args.schedule)
         rec = traffic_from_counters(*args.traffic_from, args.fmt, args.batch, args.path,
                                     args.schedule, out)
         print(json.dumps({"traffic": out, "kernels": {k: v["traffic_bytes"]
                                                       for k, v in rec["kernels"].items()}}))
+        return
+    if args.suite == "counters":
+        import torch
+
+        import bit_weight_only_w4_amd as w4
+
+        w4.lib()
+        counters_suite(torch.device("cuda:0"))
+        print(json.dumps({"suite": "counters", "cases": len(COUNTER_CASES),
+                          "launches_per_case": COUNTER_LAUNCHES}), flush=True)
         return
     if args.suite == "shapes":
         import torch
