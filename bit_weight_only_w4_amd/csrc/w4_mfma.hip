@@ -146,7 +146,7 @@ template <int FMT>
 struct Quad {
   static constexpr int QC = FMT == kNF4 ? 4 : 2;  // scale blocks per quad
   uint32_t w[2][4];
-  uint32_t s[QC];  // fp32 bits (INT4: bf16 bits shifted to the high half)
+  uint32_t s[QC];  // fp32 bits (INT4: bf16 bits in the low half)
 };
 
 // Lane i of each row of 16 lanes, broadcast to the row.
@@ -167,13 +167,16 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   constexpr int STEPS = KC / 32;              // MFMA steps per block
   constexpr int SB = FMT == kNF4 ? 4 : 2;     // bytes per scale
   constexpr bool kSplit = (FMT == kNF4 && XT == kBF16);
-  // Dynamic LDS: the decode table, the K-group reduction area, then the x window.
+  // LDS: the decode table (static, at address 0, so a lookup address needs no base), then the
+  // dynamic part: the K-group reduction area and the x window.
+  __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
   extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t* tab = reinterpret_cast<uint32_t*>(smem);
-  float4_t* red = reinterpret_cast<float4_t*>(smem + kTableBytes);  // [KW - 1][RW][T][64 lanes]
-  uint8_t* xs = smem + kTableBytes + a.red_bytes;
+  float4_t* red = reinterpret_cast<float4_t*>(smem);  // [KW - 1][RW][T][64 lanes]
+  uint8_t* xs = smem + a.red_bytes;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index through readfirstlane: everything derived from it stays in scalar registers.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave % RW, kg = wave / RW;
   const int g = lane >> 4, m = lane & 15;
   const uint32_t n = a.n, k = a.k;
@@ -210,12 +213,14 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
     c.rw = make_rsrc(a.packed + (size_t)row_base * pitch, rows * pitch);
     c.rs = make_rsrc(reinterpret_cast<const char*>(a.scales) + (size_t)row_base * spitch, rows * spitch);
   };
-  // (Branch-free: the counters stay scalar values the compiler can keep in registers.)
+  // The resources change only at a new tile (a uniform branch).
   auto advance = [&](Cursor& c) __attribute__((always_inline)) {
     const bool wrap = c.q + 1 == nq;
     c.q = wrap ? 0 : c.q + 1;
-    c.ti += wrap ? 1 : 0;
-    set_tile(c);
+    if (wrap) {
+      c.ti += 1;
+      set_tile(c);
+    }
   };
   // The quad at the cursor: blocks qb .. qb + QC - 1 of the K group, qb = (kg * qpk + q) * QC.
   // Blocks past K read as zero (their weights and scales), which adds nothing.  Each lane's 16
@@ -236,19 +241,21 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
       d.w[h][3] = v.w;
     }
     // NF4: the quad's four fp32 scales of this lane's row are contiguous (dword aligned), one
-    // 16-byte load; blocks past K are zeroed here (inside the matrix their bytes are the next
-    // row's).  INT4: two bf16 scales, 2-byte aligned, two loads.
+    // 16-byte load; of a quad that ends past K, the blocks past K are zeroed when the quad is
+    // multiplied (inside the matrix their bytes are the next row's; zeroing them here would make
+    // the loop wait for the load).  INT4: two bf16 scales, 2-byte aligned, two loads, moved to the
+    // high half when multiplied (for the same reason).
     if constexpr (FMT == kNF4) {
       const uint4 sv = buffer_load16(cur.rs, offset_or_oob(qb < nblocks, sbase));
       d.s[0] = sv.x;
-      d.s[1] = qb + 1 < nblocks ? sv.y : 0u;
-      d.s[2] = qb + 2 < nblocks ? sv.z : 0u;
-      d.s[3] = qb + 3 < nblocks ? sv.w : 0u;
+      d.s[1] = sv.y;
+      d.s[2] = sv.z;
+      d.s[3] = sv.w;
     } else {
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
         const bool have = qb + c < nblocks;
-        d.s[c] = buffer_load16bit(cur.rs, offset_or_oob(have, sbase) + (uint32_t)(c * SB)) << 16;
+        d.s[c] = buffer_load16bit(cur.rs, offset_or_oob(have, sbase) + (uint32_t)(c * SB));
       }
     }
   };
@@ -323,8 +330,9 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   // k offset (in the block) of the first of this lane's weights for MFMA step 0 (see Quad).
   const int klane = FMT == kNF4 ? 32 * (g & 1) + 16 * (g >> 1) : 32 * g;
 
-  // Multiply the quad held in d; wq = its index inside the current x window.
-  auto compute = [&](int wq, const Quad<FMT>& d) __attribute__((always_inline)) {
+  // Multiply the quad held in d: quad q of the K group, wq = its index inside the current window.
+  auto compute = [&](int q, int wq, const Quad<FMT>& d) __attribute__((always_inline)) {
+    const uint32_t qb = ((uint32_t)kg * a.qpk + (uint32_t)q) * QC;  // its first scale block
     // this lane's 2 (NF4) or 4 (INT4) dwords of packed bytes per block
     uint32_t wb[QC][STEPS];
     if constexpr (FMT == kNF4) {
@@ -386,8 +394,9 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
         // step (they would not fit the registers left by the accumulators).
         if constexpr (T == 8) __builtin_amdgcn_sched_barrier(0);
       }
-      const float sc[4] = {row_bcast<0>(d.s[c]), row_bcast<1>(d.s[c]), row_bcast<2>(d.s[c]),
-                           row_bcast<3>(d.s[c])};
+      const uint32_t sraw = FMT == kNF4 ? ((c > 0 && qb + c >= nblocks) ? 0u : d.s[c]) : d.s[c] << 16;
+      const float sc[4] = {row_bcast<0>(sraw), row_bcast<1>(sraw), row_bcast<2>(sraw),
+                           row_bcast<3>(sraw)};
 #pragma unroll
       for (int t = 0; t < T; ++t) {
 #pragma unroll
@@ -424,9 +433,14 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
         const uint32_t b = 16u * t + m;
         if (b < bsl) {
           float* yr = ysl + (size_t)b * n;
+          if ((n & 3u) == 0 && row_d + 3 < n) {
+            // the lane's four rows are consecutive in y: one 16-byte store
+            *reinterpret_cast<float4_t*>(yr + row_d) = acc[t];
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (row_d + i < n) yr[row_d + i] = acc[t][i];
+            for (int i = 0; i < 4; ++i) {
+              if (row_d + i < n) yr[row_d + i] = acc[t][i];
+            }
           }
         }
       }
@@ -445,7 +459,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
       load_x((uint32_t)cq / a.qpp);
       __syncthreads();
     }
-    compute(nphase > 1 ? cq % (int)a.qpp : cq, d);
+    compute(cq, nphase > 1 ? cq % (int)a.qpp : cq, d);
     load_quad(ld, d);
     advance(ld);
     const bool last = cq == nq - 1;
@@ -486,7 +500,7 @@ int resident_kw(int lds) {
   static bool raised = false;
   if (!raised) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_kernel<FMT, XT, T, KW>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes - kTableBytes);
     raised = true;
   }
   int nb = 0;
@@ -577,7 +591,7 @@ bool plan_slice(int64_t n, int64_t k, int64_t b, int t, MfmaPlan* p) {
   }
   const int64_t qpk = (quads + kw - 1) / kw;
   const int64_t red = kw > 1 ? (int64_t)(kw - 1) * (8 / kw) * t * 1024 : 0;
-  const int64_t budget = kLdsBytes - kTableBytes - red;
+  const int64_t budget = kLdsBytes - kTableBytes - red;  // the table is static LDS
   int64_t qpp = qpk;
   // Window bytes, rounded up to whole rounds of 512 16-byte slots (each thread's last load may land
   // past the slots in use, inside the allocation).
@@ -595,7 +609,7 @@ bool plan_slice(int64_t n, int64_t k, int64_t b, int t, MfmaPlan* p) {
   p->qpp = (int)qpp;
   p->xrow = (int)(((int64_t)kw * 32 * qpp + 1) * 16);
   p->red = (int)red;
-  p->lds = (int)(kTableBytes + red + window(qpp));
+  p->lds = (int)(red + window(qpp));  // dynamic LDS
   p->ntiles = (int)((n + 16 * (8 / kw) - 1) / (16 * (8 / kw)));
   p->slices = slices;
   return true;
