@@ -208,12 +208,12 @@ int run_mfma(const void* x, const uint8_t* packed, const void* scales, int fmt, 
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
-// Batch size from which the automatic path prefers the MFMA kernel: 5, or 3 for matrices of 64 MiB
-// of packed bytes and more.  Measured on MI355X (NF4 x fp16): the MFMA kernel's time hardly moves
-// between B = 1 and 16, the GEMV's grows with B (one dot2 per weight pair and activation row); on
-// 8960 x 1536 and 1536 x 8960 the two are even at B = 4 and the GEMV is slower from B = 5, on
+// Batch size from which the automatic path prefers the MFMA kernel: 4, or 3 for matrices of 64 MiB
+// of packed bytes and more.  Measured on MI355X (NF4 x fp16, INT4 x bf16): the MFMA kernel's time
+// hardly moves between B = 1 and 16, the GEMV's grows with B (one dot2 per weight pair and
+// activation row); on 8960 x 1536 the GEMV is still faster at B = 3 and slower from B = 4, on
 // 151936 x 1536 slower from B = 3.
-constexpr int64_t kMfmaFromBatch = 5;
+constexpr int64_t kMfmaFromBatch = 4;
 constexpr int64_t kMfmaFromBatchLarge = 3;
 
 bool prefer_mfma(int64_t n, int64_t k, int64_t b) {

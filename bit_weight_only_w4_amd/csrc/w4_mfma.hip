@@ -133,12 +133,17 @@ struct MfmaArgs {
   uint32_t tiles_rem;
 };
 
-// One quad in this lane's registers: 32 packed bytes of its A row (two 16-byte loads), and the
-// scale of one D row per block: lane (g, m) holds row 4 g + (m & 3), and lane (g, n) gets the
-// scales of its rows 4 g + i from lanes (g, i) by a DPP row broadcast.
-//   INT4 (2 blocks of 64 bytes): load c holds bytes [16 g, 16 g + 16) of block c.
-//   NF4 (4 blocks of 32 bytes): load h holds bytes [16 g, 16 g + 16) of the 64 bytes of blocks
-//   2 h, 2 h + 1, so lane groups 0, 1 hold block 2 h and groups 2, 3 block 2 h + 1.  Two
+// One quad in this lane's registers: 32 packed bytes of the 128-byte quad segments of the tile's
+// rows (two 16-byte loads), and the scale of one D row per block: lane (g, m) holds row 4 g + (m & 3),
+// and lane (g, n) gets the scales of its rows 4 g + i from lanes (g, i) by a DPP row broadcast.
+//   The loads read whole 128-byte lines: load h covers rows 8 h .. 8 h + 7, each row by 8 lanes,
+//   its own lanes (g, m) and those of its partner row m ^ 8.  In load h, lane (g, m) takes chunk g
+//   of its own row when m >> 3 == h, else chunk g + 4 of the partner row; a DPP rotation by 8
+//   lanes swaps the partner chunks when the quad is multiplied, so that lane (g, m) then holds
+//   chunks g and g + 4 (bytes [16 g, 16 g + 16) and [64 + 16 g, 80 + 16 g)) of row m.
+//   INT4 (2 blocks of 64 bytes): those are bytes [16 g, 16 g + 16) of blocks 0 and 1.
+//   NF4 (4 blocks of 32 bytes): bytes [16 g, 16 g + 16) of the 64 bytes of blocks 0, 1 and of
+//   blocks 2, 3, so lane groups 0, 1 hold blocks 0 / 2 and groups 2, 3 blocks 1 / 3.  Two
 //   v_permlane32_swap give every lane 8 bytes of each block: lane group L then holds the bytes
 //   [16 g0, 16 g0 + 8) of both blocks' lane-group-(L & 1) halves, g0 = L & 1, offset by 8 bytes
 //   for L >= 2, i.e. the 16 weights from 32 (L & 1) + 16 (L >> 1) of each block.
@@ -197,7 +202,11 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
 
   // Per-lane byte offsets inside a row tile: the A bytes of row m / lane group g, and the scale
   // row 4 g + (m & 3) (see Quad).
-  const uint32_t wlane = (uint32_t)m * pitch + (uint32_t)(g * 16);
+  // This lane's two weight loads (see Quad): row and 16-byte chunk inside the quad segment.
+  const int chunk0 = m < 8 ? g : g + 4, chunk1 = m < 8 ? g + 4 : g;
+  const uint32_t wl0 = (uint32_t)(m & 7) * pitch + (uint32_t)(chunk0 * 16);
+  const uint32_t wl1 = (uint32_t)(8 + (m & 7)) * pitch + (uint32_t)(chunk1 * 16);
+  const uint32_t wblk0 = (uint32_t)(chunk0 / (KC / 32)), wblk1 = (uint32_t)(chunk1 / (KC / 32));
   const uint32_t slane = (uint32_t)(4 * g + (m & 3)) * spitch;
 
   // A cursor over this wave's stream of (tile ti, quad q) positions, with the buffer resources of
@@ -225,16 +234,14 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   // The quad at the cursor: blocks qb .. qb + QC - 1 of the K group, qb = (kg * qpk + q) * QC.
   // Blocks past K read as zero (their weights and scales), which adds nothing.  Each lane's 16
   // bytes lie inside one block.
-  const int lblk = FMT == kNF4 ? (g >> 1) : 0;  // block of this lane's bytes within a load
   auto load_quad = [&](const Cursor& cur, Quad<FMT>& d) __attribute__((always_inline)) {
     const uint32_t qb = ((uint32_t)kg * a.qpk + (uint32_t)cur.q) * QC;
-    const uint32_t wbase = wlane + qb * (KC / 2);
+    const uint32_t wq = qb * (KC / 2);  // byte offset of the quad segment in a row
     const uint32_t sbase = slane + qb * SB;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int blk = FMT == kNF4 ? 2 * h + lblk : h;
-      const bool have = qb + blk < nblocks;
-      const uint4 v = buffer_load16_stream(cur.rw, offset_or_oob(have, wbase + 64u * h));
+      const bool have = qb + (h ? wblk1 : wblk0) < nblocks;
+      const uint4 v = buffer_load16_stream(cur.rw, offset_or_oob(have, (h ? wl1 : wl0) + wq));
       d.w[h][0] = v.x;
       d.w[h][1] = v.y;
       d.w[h][2] = v.z;
@@ -334,12 +341,20 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   auto compute = [&](int q, int wq, const Quad<FMT>& d) __attribute__((always_inline)) {
     const uint32_t qb = ((uint32_t)kg * a.qpk + (uint32_t)q) * QC;  // its first scale block
     // this lane's 2 (NF4) or 4 (INT4) dwords of packed bytes per block
+    // Chunks g and g + 4 of row m: keep the own one, take the partner's by a rotation of 8 lanes.
+    uint32_t wh[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t send = m < 8 ? d.w[1][i] : d.w[0][i];
+      wh[0][i] = m < 8 ? d.w[0][i] : d.w[1][i];
+      wh[1][i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0x128, 0xF, 0xF, false);  // row_ror:8
+    }
     uint32_t wb[QC][STEPS];
     if constexpr (FMT == kNF4) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const auto s0 = __builtin_amdgcn_permlane32_swap(d.w[h][0], d.w[h][2], false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(d.w[h][1], d.w[h][3], false, false);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(wh[h][0], wh[h][2], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(wh[h][1], wh[h][3], false, false);
         wb[2 * h][0] = s0[0];
         wb[2 * h][1] = s1[0];
         wb[2 * h + 1][0] = s0[1];
@@ -349,7 +364,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) wb[c][s] = d.w[c][s];
+        for (int s = 0; s < STEPS; ++s) wb[c][s] = wh[c][s];
       }
     }
     const uint8_t* xq = xw + (wq * kQuad + klane) * 2;

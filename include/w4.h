@@ -66,7 +66,7 @@ typedef enum {
                           My Triton Kernel Ties bitsandbytes, "The kernels", v3 and its
                           stale-output bug)                                                  */
   W4_PATH_MFMA = 3,    /* decode W on chip, MFMA against x, 1 <= B <= W4_MAX_BATCH (W4_PATH_AUTO
-                          takes it from B = 5, or B = 3 for matrices of 64 MiB and more)   */
+                          takes it from B = 4, or B = 3 for matrices of 64 MiB and more)   */
   W4_PATH_TWOPASS = 4  /* ablation: dequantize W to fp16 in the workspace, then a dense GEMV/GEMM
                           (the out-of-place path of LLM Quantization on RTX 4060, "The
                           Quantization Tax: A Byte-Accounting Model")                        */

@@ -105,8 +105,8 @@ def test_workspace_and_plan_logic():
     with pytest.raises(ValueError):
         w4.gemv_plan("nf4_f16", 64, 256, 9)
     assert w4.auto_path("nf4_f16", 8960, 1536, 1) == ("gemv", 1)
-    assert w4.auto_path("nf4_f16", 8960, 1536, 4)[0] == "gemv"
-    assert w4.auto_path("nf4_f16", 8960, 1536, 5)[0] == "mfma"
+    assert w4.auto_path("nf4_f16", 8960, 1536, 3)[0] == "gemv"
+    assert w4.auto_path("nf4_f16", 8960, 1536, 4)[0] == "mfma"
     assert w4.auto_path("nf4_f16", 8960, 1536, 64)[0] == "mfma"
     assert w4.auto_path("nf4_f16", 151936, 1536, 2)[0] == "gemv"  # 116 MB: MFMA from B = 3
     assert w4.auto_path("nf4_f16", 151936, 1536, 3)[0] == "mfma"

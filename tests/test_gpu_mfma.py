@@ -32,12 +32,12 @@ def test_mfma_parity(fmt, n, k, b):
 
 @pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
 def test_smallbatch_auto_uses_both_paths(fmt):
-    """w4_gemm_smallbatch at B = 4 (GEMV) and B = 5, 32 (MFMA) on the gate shape."""
+    """w4_gemm_smallbatch at B = 3 (GEMV) and B = 4, 32 (MFMA) on the gate shape."""
     import bit_weight_only_w4_amd as w4
 
-    for b in (4, 5, 32):
+    for b in (3, 4, 32):
         x, xd, p, s, pr, sr = _case(fmt, 8960, 1536, b, seed=b)
-        assert w4.auto_path(fmt, 8960, 1536, b)[0] == ("gemv" if b <= 4 else "mfma")
+        assert w4.auto_path(fmt, 8960, 1536, b)[0] == ("gemv" if b <= 3 else "mfma")
         y = w4.gemm_smallbatch(xd, p, s, fmt)
         g.assert_y_close(fmt, y, x, pr, sr)
 
