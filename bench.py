@@ -36,9 +36,10 @@ def parse_args():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--suite", default="decode", choices=["decode", "shapes", "counters"],
+    ap.add_argument("--suite", default="decode", choices=["decode", "shapes", "counters", "steps"],
                     help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table; "
-                         "counters: a few launches of each path, for rocprofv3 --pmc runs")
+                         "counters: a few launches of each path, for rocprofv3 --pmc runs; "
+                         "steps: the decode step in the other formats and at batch 8")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per kernel class / shape kind when timing launches")
     ap.add_argument("--schedule", default="grouped", choices=["serial", "grouped", "dag"],
@@ -584,6 +585,38 @@ def time_read_probe(nbytes, dev, min_bytes=600 << 20, reps=5):
     return ms * 1e3 / launches
 
 
+# Decode steps besides the benchmark line's: (format, batch).
+OTHER_STEPS = [("int4_bf16", 1), ("int4_bf16", 8), ("nf4_f16", 8), ("nf4_bf16", 1), ("int4_f16", 1)]
+
+
+def steps_suite(args, dev):
+    """The 197-GEMV step in each OTHER_STEPS format and batch, automatic paths: the serial chain,
+    and the grouped schedule where its grouped launches run the GEMV (batch below the MFMA
+    threshold).  Returns rows of ms per step and tok/s."""
+    import torch
+
+    rows = []
+    for fmt, b in OTHER_STEPS:
+        step = Step(fmt, b, "auto", dev)
+        total = sum(step.bytes)
+        r = {"format": fmt, "batch": b, "algorithmic_bytes_per_step": total,
+             "paths": sorted({p for p, _ in step.plans})}
+        scheds = ["serial"] + (["grouped"] if all(p == "gemv" for p, _ in step.plans) else [])
+        for sched in scheds:
+            g = capture(step, dev, step_units(step.shapes, sched), sched)
+            ms = time_replays(g, args.steps, args.warmup)
+            del g
+            r[sched] = {"ms_per_step": round(ms, 5), "tok_s": round(b * 1e3 / ms, 2),
+                        "gbs": round(total / (ms / 1e3) / 1e9, 1),
+                        "launches": len(step_units(step.shapes, sched))}
+            log(f"[steps] {fmt} B={b} {sched}: {ms * 1e3:.1f} us/step, {b * 1e3 / ms:.1f} tok/s, "
+                f"{total / (ms / 1e3) / 1e9:.0f} GB/s")
+        rows.append(r)
+        del step
+        torch.cuda.empty_cache()
+    return rows
+
+
 def shapes_suite(args, dev):
     """Per-shape table for the other workloads: INT4 decode steps (B = 1, 8) and split-K vs one
     pass on down; small-batch GEMM on gate / down / lm_head at B = 1, 8, 32, 128 for the GEMV,
@@ -781,6 +814,19 @@ def main():
         counters_suite(torch.device("cuda:0"))
         print(json.dumps({"suite": "counters", "cases": len(COUNTER_CASES),
                           "launches_per_case": COUNTER_LAUNCHES}), flush=True)
+        return
+    if args.suite == "steps":
+        import torch
+
+        import bit_weight_only_w4_amd as w4
+
+        w4.lib()
+        rows = steps_suite(args, torch.device("cuda:0"))
+        if args.report:
+            with open(args.report, "w") as f:
+                json.dump(rows, f, indent=1)
+        print(json.dumps({"metric": "decode step in other formats and batches", "rows": rows}),
+              flush=True)
         return
     if args.suite == "shapes":
         import torch
