@@ -62,12 +62,14 @@ def lib() -> ctypes.CDLL:
         L.w4_status_string.restype = ctypes.c_char_p
         vpp = ctypes.POINTER(vp)
         L.w4_gemv_grouped.argtypes = [vp, ci, vpp, vpp, ctypes.POINTER(i64), vpp, ci, i64, i64, vp]
+        L.w4_gemm_smallbatch_grouped.argtypes = [vp, ci, vpp, vpp, ctypes.POINTER(i64), vpp, ci, i64,
+                                                 i64, vp]
         L.w4_gemv_grouped_plan.argtypes = [ci, ci, ctypes.POINTER(i64), i64, i64, ip, ip, ip, ip, ip]
         L.w4_probe_read.argtypes = [vp, sz, vp, vp]
         L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
         for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_gemv", "w4_gemm_smallbatch",
                      "w4_matmul_ex", "w4_auto_path", "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
-                     "w4_gemv_grouped", "w4_gemv_grouped_plan"):
+                     "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -178,9 +180,7 @@ def grouped_args(x, packed, scales, ys):
             (vp * g)(*[y.data_ptr() for y in ys]))
 
 
-def gemv_grouped(x, packed, scales, fmt, ys=None, stream=None):
-    """[y_g] = [x . W_hat_g^T] for weight matrices that share x, in one fused-GEMV launch.
-    packed / scales are equal-length lists (at most 4 members); returns the list of y_g [B, N_g]."""
+def _grouped_call(entry, x, packed, scales, fmt, ys, stream):
     import torch
 
     if len(packed) != len(scales) or (ys is not None and len(ys) != len(packed)):
@@ -192,9 +192,21 @@ def gemv_grouped(x, packed, scales, fmt, ys=None, stream=None):
         ys = [torch.empty((b, p.shape[0]), dtype=torch.float32, device=x.device) for p in packed]
     _need_cuda(x, *packed, *scales, *ys)
     pp, sp, n, yp = grouped_args(x, packed, scales, ys)
-    check(lib().w4_gemv_grouped(_ptr(x), len(packed), pp, sp, n, yp, _fmt(fmt), k, b,
-                                _stream(stream)), "w4_gemv_grouped")
+    check(getattr(lib(), entry)(_ptr(x), len(packed), pp, sp, n, yp, _fmt(fmt), k, b,
+                                _stream(stream)), entry)
     return ys
+
+
+def gemv_grouped(x, packed, scales, fmt, ys=None, stream=None):
+    """[y_g] = [x . W_hat_g^T] for weight matrices that share x, in one fused-GEMV launch.
+    packed / scales are equal-length lists (at most 4 members); returns the list of y_g [B, N_g]."""
+    return _grouped_call("w4_gemv_grouped", x, packed, scales, fmt, ys, stream)
+
+
+def gemm_smallbatch_grouped(x, packed, scales, fmt, ys=None, stream=None):
+    """gemv_grouped for batches up to W4_MAX_BATCH: one launch of the kernel the automatic path
+    picks for the members' summed rows (the fused GEMV, or the MFMA kernel for larger batches)."""
+    return _grouped_call("w4_gemm_smallbatch_grouped", x, packed, scales, fmt, ys, stream)
 
 
 def gemm_smallbatch(x, packed, scales, fmt, y=None, stream=None):

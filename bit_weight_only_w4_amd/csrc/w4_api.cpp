@@ -221,6 +221,51 @@ bool prefer_mfma(int64_t n, int64_t k, int64_t b) {
   return b >= (large ? kMfmaFromBatchLarge : kMfmaFromBatch);
 }
 
+// Arguments of a grouped call: every member valid on its own, the members' summed rows in range,
+// and no member's y overlapping another member's y, packed bytes or scales.
+int validate_group(const void* x, int groups, const uint8_t* const* packed,
+                   const void* const* scales, const int64_t* n, float* const* y, int fmt,
+                   int64_t k, int64_t b) {
+  if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
+  if (groups < 1 || groups > W4_MAX_GROUP) return W4_ERR_SHAPE;
+  if (!packed || !scales || !n || !y) return W4_ERR_NULL;
+  int64_t n_total = 0;
+  for (int g = 0; g < groups; ++g) {
+    const int st = validate(x, packed[g], scales[g], fmt, n[g], k, b, y[g]);
+    if (st != W4_OK) return st;
+    n_total += n[g];
+  }
+  if (n_total >= kMaxDim) return W4_ERR_SHAPE;
+  const size_t sdiv = (size_t)fmt_group(fmt), ssz = fmt_weight(fmt) == kNF4 ? 4 : 2;
+  for (int g = 0; g < groups; ++g) {
+    const size_t yb = (size_t)(b * n[g]) * 4;
+    for (int h = 0; h < groups; ++h) {
+      if (h == g) continue;
+      if (overlaps(y[g], yb, y[h], (size_t)(b * n[h]) * 4) ||
+          overlaps(y[g], yb, packed[h], (size_t)(n[h] * k / 2)) ||
+          overlaps(y[g], yb, scales[h], (size_t)(n[h] * (k / (int64_t)sdiv)) * ssz))
+        return W4_ERR_ALIAS;
+    }
+  }
+  return W4_OK;
+}
+
+// A validated group: one MFMA launch over all members (mfma), else one fused-GEMV launch, or an
+// MFMA launch when the GEMV has no launch shape for (K, B).
+int run_group(const void* x, int groups, const uint8_t* const* packed, const void* const* scales,
+              const int64_t* n, float* const* y, int fmt, int64_t k, int64_t b, bool mfma,
+              hipStream_t s) {
+  GemvPlan p;
+  int64_t nrb[kMaxGroup];
+  if (mfma || !plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb)) {
+    const hipError_t e = launch_mfma_members(fmt, reinterpret_cast<const uint16_t*>(x), groups,
+                                             packed, scales, n, y, k, b, s);
+    if (e == hipErrorNotSupported) return W4_ERR_PATH;
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+  }
+  return run_gemv_members(x, groups, packed, scales, n, y, fmt, k, b, 1, nullptr, s);
+}
+
 }  // namespace
 }  // namespace w4
 
@@ -412,39 +457,23 @@ int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, i
 int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
                     const void* const* scales, const int64_t* n, float* const* y, int fmt,
                     int64_t k, int64_t b, void* stream) {
-  if (!valid_fmt(fmt)) return W4_ERR_FORMAT;
-  if (groups < 1 || groups > W4_MAX_GROUP) return W4_ERR_SHAPE;
-  if (!packed || !scales || !n || !y) return W4_ERR_NULL;
-  int64_t n_total = 0;
-  for (int g = 0; g < groups; ++g) {
-    const int st = validate(x, packed[g], scales[g], fmt, n[g], k, b, y[g]);
-    if (st != W4_OK) return st;
-    n_total += n[g];
-  }
-  if (n_total >= kMaxDim) return W4_ERR_SHAPE;
+  int st = validate_group(x, groups, packed, scales, n, y, fmt, k, b);
+  if (st != W4_OK) return st;
   if (b > kMaxGemvBatch) return W4_ERR_SHAPE;
-  const size_t sdiv = (size_t)fmt_group(fmt), ssz = fmt_weight(fmt) == kNF4 ? 4 : 2;
-  for (int g = 0; g < groups; ++g) {
-    const size_t yb = (size_t)(b * n[g]) * 4;
-    for (int h = 0; h < groups; ++h) {
-      if (h == g) continue;
-      if (overlaps(y[g], yb, y[h], (size_t)(b * n[h]) * 4) ||
-          overlaps(y[g], yb, packed[h], (size_t)(n[h] * k / 2)) ||
-          overlaps(y[g], yb, scales[h], (size_t)(n[h] * (k / (int64_t)sdiv)) * ssz))
-        return W4_ERR_ALIAS;
-    }
-  }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  GemvPlan p;
-  int64_t nrb[kMaxGroup];
-  if (!plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb)) {  // no GEMV shape: MFMA each
-    for (int g = 0; g < groups; ++g) {
-      const int st = run_mfma(x, packed[g], scales[g], fmt, n[g], k, b, y[g], s);
-      if (st != W4_OK) return st;
-    }
-    return W4_OK;
-  }
-  return run_gemv_members(x, groups, packed, scales, n, y, fmt, k, b, 1, nullptr, s);
+  return run_group(x, groups, packed, scales, n, y, fmt, k, b, false,
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
+int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* packed,
+                               const void* const* scales, const int64_t* n, float* const* y,
+                               int fmt, int64_t k, int64_t b, void* stream) {
+  int st = validate_group(x, groups, packed, scales, n, y, fmt, k, b);
+  if (st != W4_OK) return st;
+  int64_t n_total = 0;
+  for (int g = 0; g < groups; ++g) n_total += n[g];
+  return run_group(x, groups, packed, scales, n, y, fmt, k, b,
+                   b > kMaxGemvBatch || prefer_mfma(n_total, k, b),
+                   reinterpret_cast<hipStream_t>(stream));
 }
 
 int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,

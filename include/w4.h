@@ -134,17 +134,31 @@ int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, i
  * The host arrays are read during the call only.  Each y_g satisfies the same accuracy bound as
  * w4_gemv on that member alone, and is bitwise equal to it when both calls get the same launch
  * shape (w4_gemv_plan with N = N_g and with N = sum of N_g report the same threads, team and
- * iters).  No workspace.  Asynchronous on `stream`. */
+ * iters).  When the fused GEMV has no launch shape for (K, B) (B = 8 with rows of more than 8192
+ * values), the members run in one launch of the MFMA kernel instead.  No workspace.
+ * Asynchronous on `stream`. */
 int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
                     const void* const* scales, const int64_t* N, float* const* y, int fmt,
                     int64_t K, int64_t B, void* stream);
 
 /* w4_gemm_smallbatch: the same operation for 1 <= B <= W4_MAX_BATCH (decode batches; Do
  * Quantization and Sparsity make LLM Inference Faster?, "NF4: fast at batch 1, slower at larger
- * batches").  Picks the fused GEMV for small B and the MFMA dequantize-in-LDS path for larger B;
- * never materializes W_hat.  Arguments as for w4_gemv.  No workspace.  Asynchronous. */
+ * batches").  Picks the fused GEMV for small B and the MFMA path (weights decoded on chip into
+ * the matrix-core operands) for larger B; never materializes W_hat.  Arguments as for w4_gemv.
+ * No workspace.  Asynchronous. */
 int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt,
                        int64_t N, int64_t K, int64_t B, float* y, void* stream);
+
+/* w4_gemm_smallbatch_grouped: w4_gemv_grouped for 1 <= B <= W4_MAX_BATCH.  The members run in ONE
+ * launch of the kernel w4_gemm_smallbatch would pick for a matrix of sum-of-N_g rows: the fused
+ * GEMV (as w4_gemv_grouped) for small B, the MFMA kernel over the row tiles of every member for
+ * larger B (LLM Compressor 0.14: GPTQ's 15x speedup is one fused loop, section "Batching
+ * layers").  Arguments, ownership and errors as for w4_gemv_grouped, with B up to
+ * W4_MAX_BATCH.  Each y_g meets w4_gemm_smallbatch's accuracy bound on that member.  No
+ * workspace.  Asynchronous on `stream`. */
+int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* packed,
+                               const void* const* scales, const int64_t* N, float* const* y,
+                               int fmt, int64_t K, int64_t B, void* stream);
 
 /* w4_matmul_ex: the same operation with an explicit path, split count and workspace (tests and
  * the ablation benchmark).  path = W4_PATH_AUTO also considers split-K when a workspace is given.

@@ -112,13 +112,14 @@ def test_workspace_and_plan_logic():
     assert w4.auto_path("nf4_f16", 151936, 1536, 3)[0] == "mfma"
 
 
-def _grouped(L, n=(64, 32, 32), x=FAKE, p=None, s=None, y=None, fmt=1, k=256, b=1, groups=None):
+def _grouped(L, n=(64, 32, 32), x=FAKE, p=None, s=None, y=None, fmt=1, k=256, b=1, groups=None,
+             entry="w4_gemv_grouped"):
     vp = ctypes.c_void_p
     g = len(n)
     p = p if p is not None else [FAKE * (10 + i) for i in range(g)]
     s = s if s is not None else [FAKE * (20 + i) for i in range(g)]
     y = y if y is not None else [FAKE * (30 + i) for i in range(g)]
-    return L.w4_gemv_grouped(vp(x), g if groups is None else groups, (vp * g)(*p), (vp * g)(*s),
+    return getattr(L, entry)(vp(x), g if groups is None else groups, (vp * g)(*p), (vp * g)(*s),
                              (ctypes.c_int64 * g)(*n), (vp * g)(*y), fmt, k, b, None)
 
 
@@ -142,6 +143,23 @@ def test_grouped_validation_codes():
     # the sum of N must stay below 2^31 (addresses 1 TiB apart so that nothing overlaps)
     far = [1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44, 1 << 45]
     assert _grouped(L, n=(1 << 30, 1 << 30), k=64, p=far[0:2], s=far[2:4], y=far[4:6]) == -2
+
+
+def test_grouped_smallbatch_validation_codes():
+    """w4_gemm_smallbatch_grouped rejects what w4_gemv_grouped rejects, but takes B up to
+    W4_MAX_BATCH = 256 (every case here fails validation, before any launch)."""
+    _, L = _lib()
+    e = "w4_gemm_smallbatch_grouped"
+    assert _grouped(L, groups=0, entry=e) == -2
+    assert _grouped(L, n=(8,) * 5, entry=e) == -2
+    assert _grouped(L, x=0, b=32, entry=e) == -1
+    assert _grouped(L, n=(64, 0, 32), b=32, entry=e) == -2
+    assert _grouped(L, k=96, b=32, entry=e) == -2
+    assert _grouped(L, b=257, entry=e) == -2
+    assert _grouped(L, fmt=7, b=32, entry=e) == -4
+    assert _grouped(L, y=[FAKE * 30, FAKE * 30 + 128, FAKE * 32], b=1, entry=e) == -9
+    # with B = 32 each y_g is 32 rows: y_1 placed inside y_0
+    assert _grouped(L, y=[FAKE * 30, FAKE * 30 + 64 * 4 * 8, FAKE * 32], b=32, entry=e) == -9
 
 
 def test_grouped_plan_logic():

@@ -243,9 +243,9 @@ def test_grouped_bitwise_equals_solo(fmt, ns, b):
         g.assert_y_close(fmt, y, x, pr, sr)
 
 
-def test_grouped_long_rows_at_b8_fall_back_per_member():
-    """B = 8 with K = 28672 has no GEMV launch shape; the grouped call then runs each member on
-    the MFMA path and still meets the bound."""
+def test_grouped_long_rows_at_b8_fall_back_to_mfma():
+    """B = 8 with K = 28672 has no GEMV launch shape; the grouped call then runs the members in
+    one launch of the MFMA kernel and still meets the bound."""
     import bit_weight_only_w4_amd as w4
 
     fmt = "nf4_f16"

@@ -79,3 +79,49 @@ def test_mfma_full_size_sampled(fmt, n, k, b):
     x = synth_inputs.activations(b, k, g.XDT[fmt], seed=b + 5)
     y = w4.matmul_ex(g.to_dev_x(x, g.XDT[fmt]), p, s, fmt, path="mfma")
     g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("ns,k,b", [((1536, 256, 256), 1536, 8), ((300, 1000), 2048, 32),
+                                    ((64, 40, 100, 17), 384, 129), ((8960, 8960), 1536, 4),
+                                    ((130, 70), 8960, 16)])
+def test_smallbatch_grouped_parity(fmt, ns, k, b):
+    """One launch over members sharing x (the MFMA kernel over every member's row tiles from the
+    MFMA threshold on): each y_g against the oracle on that member."""
+    import bit_weight_only_w4_amd as w4
+
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=b + k)
+    xd = g.to_dev_x(x, g.XDT[fmt])
+    packed, scales, refs = [], [], []
+    for i, n in enumerate(ns):
+        w = synth_inputs.weights(n, k, seed=n * 13 + i)
+        p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+        pr, sr = g.oracle_quantize(fmt, w)
+        g.assert_quant_equal(fmt, p, s, pr, sr)
+        packed.append(p)
+        scales.append(s)
+        refs.append((pr, sr))
+    ys = w4.gemm_smallbatch_grouped(xd, packed, scales, fmt)
+    for y, (pr, sr) in zip(ys, refs):
+        g.assert_y_close(fmt, y, x, pr, sr)
+
+
+def test_smallbatch_grouped_below_threshold_is_the_grouped_gemv():
+    """Below the MFMA threshold the grouped small-batch call runs the grouped fused GEMV: bitwise
+    the same outputs as w4_gemv_grouped."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    fmt, k, b = "nf4_f16", 1536, 2
+    x = synth_inputs.activations(b, k, "f16", seed=5)
+    xd = g.to_dev_x(x, "f16")
+    packed, scales = [], []
+    for i, n in enumerate((1536, 256, 256)):
+        p, s = g.gpu_quantize(fmt, g.to_dev_f32(synth_inputs.weights(n, k, seed=40 + i)))
+        packed.append(p)
+        scales.append(s)
+    a = w4.gemm_smallbatch_grouped(xd, packed, scales, fmt)
+    c = w4.gemv_grouped(xd, packed, scales, fmt)
+    for ya, yc in zip(a, c):
+        assert torch.equal(ya, yc)
