@@ -133,23 +133,32 @@ int auto_splits(int64_t, int64_t, int) { return 1; }
 size_t splitk_bytes(int64_t n, int64_t b, int s) { return (size_t)s * (size_t)b * (size_t)n * 4; }
 
 // Launch shape of one fused-GEMV launch over `groups` members that share K: the plan of their
-// summed rows, each member's row blocks, and the workgroups along x per member (the largest
-// member's share of the grid cap, so that the whole grid stays within the cap; smaller members
-// leave their surplus workgroups idle).
+// summed rows, each member's row blocks, and each member's workgroups along x (its share of the
+// grid cap, at most its row blocks; grouped launches give the members consecutive ranges of x, so
+// no workgroup is without work).
 bool plan_members(int groups, const int64_t* n, int64_t k, int b, int splits, bool grouped,
-                  GemvPlan* p, int64_t* nrb) {
+                  GemvPlan* p, int64_t* nrb, int64_t* grid_g) {
   int64_t n_total = 0;
   for (int g = 0; g < groups; ++g) n_total += n[g];
   if (b > kMaxGemvBatch || !plan_gemv(n_total, k, b, splits, p, grouped)) return false;
   const int64_t rows_per_wg = p->threads / p->team;
-  int64_t nrb_sum = 0, nrb_max = 0;
+  int64_t nrb_sum = 0;
   for (int g = 0; g < groups; ++g) {
     nrb[g] = (n[g] + rows_per_wg - 1) / rows_per_wg;
     nrb_sum += nrb[g];
-    nrb_max = std::max(nrb_max, nrb[g]);
   }
-  const int64_t share = std::max<int64_t>(1, (p->cap * nrb_max + nrb_sum - 1) / nrb_sum);
-  p->grid_x = (int)std::min<int64_t>(nrb_max, share);
+  if (groups == 1) {
+    grid_g[0] = std::min<int64_t>(nrb[0], p->cap);
+    p->grid_x = (int)grid_g[0];
+    return true;
+  }
+  int64_t total = 0;
+  for (int g = 0; g < groups; ++g) {
+    const int64_t share = (p->cap * nrb[g] + nrb_sum / 2) / nrb_sum;
+    grid_g[g] = std::max<int64_t>(1, std::min<int64_t>(nrb[g], share));
+    total += grid_g[g];
+  }
+  p->grid_x = (int)total;
   return true;
 }
 
@@ -159,17 +168,22 @@ int run_gemv_members(const void* x, int groups, const uint8_t* const* packed,
                      const void* const* scales, const int64_t* n, float* const* y, int fmt,
                      int64_t k, int64_t b, int splits, void* ws, hipStream_t st) {
   GemvPlan p;
-  int64_t nrb[kMaxGroup];
-  if (!plan_members(groups, n, k, (int)b, splits, groups > 1, &p, nrb)) return W4_ERR_PATH;
+  int64_t nrb[kMaxGroup], grid_g[kMaxGroup];
+  if (!plan_members(groups, n, k, (int)b, splits, groups > 1, &p, nrb, grid_g)) return W4_ERR_PATH;
   GemvArgs a;
   memset(&a, 0, sizeof(a));
   a.x = reinterpret_cast<const uint16_t*>(x);
+  uint32_t wg0 = 0;
+  for (int g = 0; g < kMaxGroup; ++g) a.m[g].wg0 = 0xFFFFFFFFu;  // unused slots match no workgroup
   for (int g = 0; g < groups; ++g) {
     a.m[g].packed = packed[g];
     a.m[g].scales = scales[g];
     a.m[g].out = splits == 1 ? y[g] : reinterpret_cast<float*>(ws);
     a.m[g].n = (uint32_t)n[g];
     a.m[g].nrb = (uint32_t)nrb[g];
+    a.m[g].wg0 = wg0;
+    a.m[g].grid = (uint32_t)grid_g[g];
+    wg0 += (uint32_t)grid_g[g];
   }
   a.k = k;
   a.cpr = (int)(k / 32);
@@ -256,8 +270,8 @@ int run_group(const void* x, int groups, const uint8_t* const* packed, const voi
               const int64_t* n, float* const* y, int fmt, int64_t k, int64_t b, bool mfma,
               hipStream_t s) {
   GemvPlan p;
-  int64_t nrb[kMaxGroup];
-  if (mfma || !plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb)) {
+  int64_t nrb[kMaxGroup], grid_g[kMaxGroup];
+  if (mfma || !plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb, grid_g)) {
     const hipError_t e = launch_mfma_members(fmt, reinterpret_cast<const uint16_t*>(x), groups,
                                              packed, scales, n, y, k, b, s);
     if (e == hipErrorNotSupported) return W4_ERR_PATH;
@@ -373,13 +387,13 @@ int w4_gemv_grouped_plan(int fmt, int groups, const int64_t* n, int64_t k, int64
   if (n_total >= kMaxDim || k < g || k % g || k >= kMaxDim || b < 1 || b > W4_MAX_BATCH)
     return W4_ERR_SHAPE;
   GemvPlan p;
-  int64_t nrb[kMaxGroup];
-  if (!plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb)) return W4_ERR_PATH;
+  int64_t nrb[kMaxGroup], grid_g[kMaxGroup];
+  if (!plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb, grid_g)) return W4_ERR_PATH;
   if (threads) *threads = p.threads;
   if (team) *team = p.team;
   if (iters) *iters = p.iters;
   if (grid_x) *grid_x = p.grid_x;
-  if (grid_z) *grid_z = groups;
+  if (grid_z) *grid_z = 1;
   return W4_OK;
 }
 

@@ -91,8 +91,8 @@ struct GemvPlan {
 };
 
 // Matrices of one launch.  A launch covers 1..kMaxGroup weight matrices ("members") that share
-// the activations x and K.  Member g is processed by the workgroups with blockIdx.z == g, which
-// walk its row blocks grid-stride along x.
+// the activations x and K.  Member g is processed by its own range of workgroups along x,
+// [wg0, wg0 + grid), which walk its row blocks grid-stride (a single-member launch: all of x).
 constexpr int kMaxGroup = W4_MAX_GROUP;
 
 struct GemvMember {
@@ -101,6 +101,8 @@ struct GemvMember {
   float* out;             // y [B, N_g] (splits == 1) or partials [splits, B, N_g]
   uint32_t n;             // rows N_g
   uint32_t nrb;           // row blocks of this member = ceil(N_g / rows per workgroup)
+  uint32_t wg0;           // grouped launches: first workgroup (unused slots: 0xFFFFFFFF)
+  uint32_t grid;          // grouped launches: workgroups of this member (<= nrb)
 };
 
 // Kernel arguments for launches of up to G members (the single-member kernels take G = 1, which

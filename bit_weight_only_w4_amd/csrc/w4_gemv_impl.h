@@ -159,21 +159,35 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   const int c0 = blockIdx.y * a.cps;
   const int nck = min(a.cps, a.cpr - c0);
   const int64_t k = a.k;
-  // This workgroup's member (grouped launches: one member per blockIdx.z).
-  const GemvMember mm = a.m[GROUPED ? blockIdx.z : 0];
+  // This workgroup's member: grouped launches give each member its own range of workgroups
+  // along x, found by selects over the member slots (every slot is fetched in the one batch of
+  // scalar loads; indexing the slots by a loaded value would add a second, dependent batch).
+  GemvMember mm = a.m[0];
+  if constexpr (GROUPED) {
+    // (The empty asm statements take every slot's fields first, so that the compiler fetches them
+    // in one batch instead of loading the chosen slot after comparing.)
+#pragma unroll
+    for (int i = 0; i < (GROUPED ? kMaxGroup : 1); ++i) {
+      asm volatile("" ::"s"(a.m[i].packed), "s"(a.m[i].scales), "s"(a.m[i].out), "s"(a.m[i].n),
+                   "s"(a.m[i].nrb), "s"(a.m[i].wg0), "s"(a.m[i].grid));
+    }
+#pragma unroll
+    for (int i = 1; i < (GROUPED ? kMaxGroup : 1); ++i) {
+      const bool take = blockIdx.x >= a.m[i].wg0;
+      mm.packed = take ? a.m[i].packed : mm.packed;
+      mm.scales = take ? a.m[i].scales : mm.scales;
+      mm.out = take ? a.m[i].out : mm.out;
+      mm.n = take ? a.m[i].n : mm.n;
+      mm.nrb = take ? a.m[i].nrb : mm.nrb;
+      mm.wg0 = take ? a.m[i].wg0 : mm.wg0;
+      mm.grid = take ? a.m[i].grid : mm.grid;
+    }
+  }
   // 32-bit index arithmetic for row blocks (the host guarantees N < 2^31); one 32-bit division
   // gives this workgroup's trip count.
   const uint32_t nrb = mm.nrb;
-  const uint32_t grid = gridDim.x;
-  const uint32_t rb0 = blockIdx.x;
-  if constexpr (GROUPED) {
-    // A member smaller than the grid is wide leaves workgroups with no row block: they leave
-    // before the table fill.  Every argument the kernel uses is fetched before that branch (the
-    // empty asm consumes them), so the fetch stays one batch of scalar loads.
-    asm volatile("" ::"s"(a.x), "s"(a.k), "s"(a.cpr), "s"(a.cps), "s"(a.team), "s"(a.iters),
-                 "s"(mm.packed), "s"(mm.scales), "s"(mm.out), "s"(mm.n), "s"(grid));
-    if (rb0 >= nrb) return;
-  }
+  const uint32_t grid = GROUPED ? mm.grid : gridDim.x;
+  const uint32_t rb0 = GROUPED ? blockIdx.x - mm.wg0 : blockIdx.x;
   const uint32_t count = (nrb - 1u - rb0) / grid + 1u;  // row blocks of this workgroup (>= 1)
   const uint32_t rb_last = rb0 + grid * (count - 1u);
 
@@ -358,7 +372,8 @@ hipError_t launch_one(const GemvArgs& full, int groups, const GemvPlan& p, hipSt
   a.team = full.team;
   a.iters = full.iters;
   for (int g = 0; g < G; ++g) a.m[g] = full.m[g];
-  const dim3 grid(p.grid_x, p.splits, GROUPED ? groups : 1);
+  (void)groups;
+  const dim3 grid(p.grid_x, p.splits, 1);
   switch (p.threads) {
     case 256:
       hipLaunchKernelGGL((gemv_kernel<FMT, XT, B, ITM, 256, GROUPED>), grid, dim3(256), 0, s, a);

@@ -191,10 +191,11 @@ int w4_gemv_plan(int fmt, int64_t N, int64_t K, int64_t B, int split_k, int* thr
                  int* iters, int* chunks_per_split, int* grid_x);
 
 /* Launch shape of w4_gemv_grouped for members of N[0 .. groups-1] rows sharing (fmt, K, B):
- * threads per workgroup, lanes per output row, 16-byte chunks per lane, workgroups along N per
- * member (grid_x) and members (grid_z; one grid slice per member).  Any output pointer may be
- * NULL.  Returns W4_OK, or W4_ERR_SHAPE / W4_ERR_PATH when the grouped GEMV cannot run these
- * arguments (w4_gemv_grouped then runs each member on the MFMA path). */
+ * threads per workgroup, lanes per output row, 16-byte chunks per lane, workgroups along N for all
+ * members together (grid_x: each member gets a consecutive range, its share of the grid, at most
+ * one workgroup per row block of its own) and grid_z (always 1).  Any output pointer may be NULL.
+ * Returns W4_OK, or W4_ERR_SHAPE / W4_ERR_PATH when the grouped GEMV cannot run these arguments
+ * (w4_gemv_grouped then runs the members in one launch of the MFMA kernel). */
 int w4_gemv_grouped_plan(int fmt, int groups, const int64_t* N, int64_t K, int64_t B, int* threads,
                          int* team, int* iters, int* grid_x, int* grid_z);
 

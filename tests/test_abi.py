@@ -163,17 +163,19 @@ def test_grouped_smallbatch_validation_codes():
 
 
 def test_grouped_plan_logic():
-    """Host-side plan of a grouped launch: one grid slice per member, the shared per-row shape of
-    the summed rows, and a grid that stays within the single-launch cap."""
+    """Host-side plan of a grouped launch: the shared per-row shape of the summed rows, and one
+    range of workgroups per member along x, never more than the member's row blocks (no idle
+    workgroups) and together within the single-launch cap."""
     w4, L = _lib()
     p = w4.gemv_grouped_plan("nf4_f16", [1536, 256, 256], 1536, 1)
     solo = w4.gemv_plan("nf4_f16", 2048, 1536, 1)
-    assert p["grid_z"] == 3
+    assert p["grid_z"] == 1
     assert (p["threads"], p["team"], p["iters"]) == (solo["threads"], solo["team"], solo["iters"])
     rows = p["threads"] // p["team"]
-    assert p["grid_x"] <= (1536 + rows - 1) // rows  # never wider than the largest member
+    blocks = sum((n + rows - 1) // rows for n in (1536, 256, 256))
+    assert p["grid_x"] == blocks  # 192 + 32 + 32 row blocks, within the cap: one workgroup each
     p2 = w4.gemv_grouped_plan("int4_bf16", [8960, 8960], 1536, 2)
-    assert p2["grid_z"] == 2 and p2["grid_x"] * 2 <= 2 * 512  # within 2 workgroups per CU
+    assert p2["grid_z"] == 1 and p2["grid_x"] <= 2 * 256  # within 2 workgroups per CU
     with pytest.raises(ValueError):
         w4.gemv_grouped_plan("nf4_f16", [64] * 5, 256, 1)
     with pytest.raises(ValueError):
