@@ -17,11 +17,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4.so")
 
 FORMATS = {"nf4_f16": 1, "nf4_bf16": 2, "int4_f16": 3, "int4_bf16": 4}
-PATHS = {"auto": 0, "gemv": 1, "splitk": 2, "mfma": 3, "twopass": 4}
+PATHS = {"auto": 0, "gemv": 1, "splitk": 2, "mfma": 3, "twopass": 4, "tiled": 5}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 STATUS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "FORMAT", -5: "NONFINITE",
           -6: "WORKSPACE", -7: "PATH", -8: "HIP", -9: "ALIAS"}
-MAX_BATCH = 256
+MAX_BATCH = 4096
+TILED_FROM_BATCH = 128
 MAX_SPLIT_K = 64
 
 _lib = None
@@ -51,6 +52,7 @@ def lib() -> ctypes.CDLL:
         L.w4_quantize_int4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.w4_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_smallbatch.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
+        L.w4_gemm_prefill.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_matmul_ex.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, ci, ci, vp, sz, vp]
         L.w4_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ci]
         L.w4_workspace_bytes.restype = sz
@@ -69,7 +71,8 @@ def lib() -> ctypes.CDLL:
         L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
         for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_gemv", "w4_gemm_smallbatch",
                      "w4_matmul_ex", "w4_auto_path", "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
-                     "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped"):
+                     "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped",
+                     "w4_gemm_prefill"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -210,7 +213,8 @@ def gemm_smallbatch_grouped(x, packed, scales, fmt, ys=None, stream=None):
 
 
 def gemm_smallbatch(x, packed, scales, fmt, y=None, stream=None):
-    """y[B, N] = x[B, K] . W_hat^T for B <= 256, GEMV or MFMA path chosen by the library."""
+    """y[B, N] = x[B, K] . W_hat^T for B <= MAX_BATCH, GEMV, MFMA or tiled path chosen by the
+    library."""
     import torch
 
     x, n, k, b = _mm_shapes(x, packed)
@@ -219,6 +223,19 @@ def gemm_smallbatch(x, packed, scales, fmt, y=None, stream=None):
     _need_cuda(x, packed, scales, y)
     check(lib().w4_gemm_smallbatch(_ptr(x), _ptr(packed), _ptr(scales), _fmt(fmt), n, k, b,
                                    _ptr(y), _stream(stream)), "w4_gemm_smallbatch")
+    return y
+
+
+def gemm_prefill(x, packed, scales, fmt, y=None, stream=None):
+    """y[B, N] = x[B, K] . W_hat^T through the tiled GEMM (prefill: B = prompt tokens)."""
+    import torch
+
+    x, n, k, b = _mm_shapes(x, packed)
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    _need_cuda(x, packed, scales, y)
+    check(lib().w4_gemm_prefill(_ptr(x), _ptr(packed), _ptr(scales), _fmt(fmt), n, k, b,
+                                _ptr(y), _stream(stream)), "w4_gemm_prefill")
     return y
 
 

@@ -222,6 +222,14 @@ int run_mfma(const void* x, const uint8_t* packed, const void* scales, int fmt, 
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
+int run_tiled(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+              int64_t k, int64_t b, float* y, hipStream_t st) {
+  const hipError_t e = launch_gemm(fmt, reinterpret_cast<const uint16_t*>(x), packed, scales, n, k,
+                                   b, y, st);
+  if (e == hipErrorNotSupported) return W4_ERR_PATH;
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
 // Batch size from which the automatic path prefers the MFMA kernel: 4, or 3 for matrices of 64 MiB
 // of packed bytes and more.  Measured on MI355X (NF4 x fp16, INT4 x bf16): the MFMA kernel's time
 // hardly moves between B = 1 and 16, the GEMV's grows with B (one dot2 per weight pair and
@@ -264,11 +272,19 @@ int validate_group(const void* x, int groups, const uint8_t* const* packed,
   return W4_OK;
 }
 
-// A validated group: one MFMA launch over all members (mfma), else one fused-GEMV launch, or an
-// MFMA launch when the GEMV has no launch shape for (K, B).
+// A validated group: one tiled-GEMM launch per member from B = W4_TILED_FROM_BATCH, else one MFMA
+// launch over all members (mfma), else one fused-GEMV launch, or an MFMA launch when the GEMV has
+// no launch shape for (K, B).
 int run_group(const void* x, int groups, const uint8_t* const* packed, const void* const* scales,
               const int64_t* n, float* const* y, int fmt, int64_t k, int64_t b, bool mfma,
               hipStream_t s) {
+  if (mfma && b >= W4_TILED_FROM_BATCH) {
+    for (int g = 0; g < groups; ++g) {
+      const int st = run_tiled(x, packed[g], scales[g], fmt, n[g], k, b, y[g], s);
+      if (st != W4_OK) return st;
+    }
+    return W4_OK;
+  }
   GemvPlan p;
   int64_t nrb[kMaxGroup], grid_g[kMaxGroup];
   if (mfma || !plan_members(groups, n, k, (int)b, 1, groups > 1, &p, nrb, grid_g)) {
@@ -405,7 +421,9 @@ int w4_auto_path(int fmt, int64_t n, int64_t k, int64_t b, size_t workspace_byte
   int s = 1;
   int path;
   GemvPlan p;
-  if (prefer_mfma(n, k, b) || !plan_gemv(n, k, (int)b, 1, &p)) {
+  if (b >= W4_TILED_FROM_BATCH) {
+    path = W4_PATH_TILED;
+  } else if (prefer_mfma(n, k, b) || !plan_gemv(n, k, (int)b, 1, &p)) {
     path = W4_PATH_MFMA;
   } else {
     s = auto_splits(n, k, (int)b);
@@ -446,6 +464,8 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
     }
     case W4_PATH_MFMA:
       return run_mfma(x, packed, scales, fmt, n, k, b, y, s);
+    case W4_PATH_TILED:
+      return run_tiled(x, packed, scales, fmt, n, k, b, y, s);
     case W4_PATH_TWOPASS: {
       if (!workspace || workspace_bytes < (size_t)n * (size_t)k * 2) return W4_ERR_WORKSPACE;
       if (overlaps(workspace, workspace_bytes, x, (size_t)(b * k) * 2) ||
@@ -493,6 +513,13 @@ int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* 
 int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
                        int64_t k, int64_t b, float* y, void* stream) {
   return w4_matmul_ex(x, packed, scales, fmt, n, k, b, y, W4_PATH_AUTO, 0, nullptr, 0, stream);
+}
+
+int w4_gemm_prefill(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+                    int64_t k, int64_t b, float* y, void* stream) {
+  const int st = validate(x, packed, scales, fmt, n, k, b, y);
+  if (st != W4_OK) return st;
+  return run_tiled(x, packed, scales, fmt, n, k, b, y, reinterpret_cast<hipStream_t>(stream));
 }
 
 int w4_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {

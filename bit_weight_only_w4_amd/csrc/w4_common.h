@@ -152,6 +152,8 @@ hipError_t launch_mfma(int fmt, const uint16_t* x, const uint8_t* packed, const 
 hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
                                const void* const* scales, const int64_t* ns, float* const* y,
                                int64_t k, int64_t b, hipStream_t s);
+hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
+                       int64_t n, int64_t k, int64_t m, float* y, hipStream_t s);
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 

@@ -1,0 +1,369 @@
+// Prefill-size GEMM: y[m, n] = sum_k x[m, k] * W_hat[n, k] for hundreds to thousands of activation
+// rows (the tokens of a prompt), the weights decoded on chip and multiplied on the matrix cores.
+//
+// A GEMV kernel run once per token makes prefill an order of magnitude slower than a GEMM (LLM
+// Quantization on RTX 4060, "Why Only 16%", item 3); the dequantize-then-dense-GEMM route rebuilds
+// the fp16 matrix on every call (Do Quantization and Sparsity make LLM Inference Faster?, "NF4:
+// fast at batch 1, slower at larger batches").  Here each workgroup owns an output tile of
+// TN weight rows x TM activation rows and walks K one 64-weight block at a time, so every decoded
+// weight is reused by TM activation rows and every activation by TN weight rows: the work is
+// bound by the matrix cores, not by memory.
+//
+// Work layout.  A K group is 256 threads = 4 waves in a 2 x 2 grid over the tile; wave (wn, wm)
+// owns WN row tiles x WM column tiles of 16 x 16 outputs (TN = 32 WN, TM = 32 WM).  A workgroup has
+// KW K groups that split the K blocks between them and add their sums through LDS at the end in a
+// fixed order (small grids: twice the waves per tile and half the blocks per wave).
+//   * A operand (16 weight rows x 32 k per MFMA step): lane l = 16 g + r takes row r and the 8
+//     consecutive weights 16 g + 8 s .. 16 g + 8 s + 7 of the block in step s = 0, 1: bytes
+//     [8 g, 8 g + 8) of the row's 32-byte block, one 8-byte load per row tile, decoded pairwise
+//     through the byte -> pair table in LDS.  Both steps lie inside one scale block, so the block
+//     scale is applied exactly, in fp32, to the block's fresh partial sums: acc += scale * D.
+//     INT4 groups of 128 are two such blocks under one scale.
+//   * B operand (32 k x 16 activation rows): lane l = 16 g + r takes activation row r of the
+//     column tile and the same 8 k positions, one ds_read_b128 from the x stage in LDS.
+//   * x stages: the tile's TM activation rows x 64 k (128 bytes per row, padded to 144 so that
+//     the 16 lanes of a read hit distinct banks), double-buffered in LDS per K group.  Stage kb + 2 is
+//     loaded into registers when block kb starts (two register sets) and written to LDS at the
+//     end of block kb + 1; one barrier per block.
+//   * Weights and scales run four blocks ahead of the multiply (four register sets, rotating by
+//     unrolling): a block's loads have three blocks of matrix work to land.
+//   * D (16 x 16 fp32): lane l = 16 g + r holds weight rows 4 g .. 4 g + 3 of activation row r,
+//     consecutive in y[m, :] (one 16-byte store).
+//   * Workgroups are numbered so that the ones the dispatcher places on one XCD (every eighth)
+//     take consecutive tiles, the activation-row tiles of one weight-row tile first: a weight tile
+//     is read from HBM once and then served by that XCD's L2.
+#include "w4_mfma_common.h"
+
+namespace w4 {
+
+struct GemmArgs {
+  const uint16_t* x;      // [M, K] activations (bits)
+  const uint8_t* packed;  // [N, K/2]
+  const void* scales;     // NF4 float[N, K/64] | INT4 uint16[N, K/128]
+  float* y;               // [M, N]
+  uint32_t m, n, k;
+  uint32_t mt;            // activation-row tiles (TM rows each)
+  uint32_t tiles;         // mt * weight-row tiles
+};
+
+namespace {
+
+constexpr int kGroupThreads = 256;            // one K group: 4 waves in a 2 x 2 grid
+constexpr int kXPitch = 144;                  // LDS bytes per activation row of a stage
+constexpr int kXcds = 8;
+constexpr int kDepth = 4;                     // weight blocks in flight (register sets)
+
+template <int WM>
+constexpr int stage_bytes() { return 32 * WM * kXPitch; }
+
+// Weights and scales of one block for this lane: two dwords of packed bytes per row tile, and the
+// scale of D row 4 g + (r & 3) of each row tile (fp32 bits; INT4: bf16 bits in the low half).
+template <int WN>
+struct Block {
+  uint32_t w[WN][2];
+  uint32_t s[WN];
+};
+
+template <int FMT, int XT, int WN, int WM, int KW>
+__global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a) {
+  constexpr int TN = 32 * WN, TM = 32 * WM;
+  constexpr bool kSplit = FMT == kNF4 && XT == kBF16;
+  constexpr int SB = FMT == kNF4 ? 4 : 2;  // bytes per scale
+  // LDS: the decode table (static, at address 0, so a lookup address needs no base), then the two
+  // x stages of each K group (dynamic), reused at the end for the K groups' sums.
+  __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
+  extern __shared__ __align__(16) uint8_t xs[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = (wave >> 1) & 1, kg = wave >> 2;
+  const int gt = tid & (kGroupThreads - 1);  // thread index inside the K group
+  const int g = lane >> 4, r = lane & 15;
+
+  // This workgroup's tile: every eighth workgroup shares an XCD; those take consecutive tiles.
+  const uint32_t id = blockIdx.x, tiles = a.tiles;
+  const uint32_t xcd = id % kXcds, per = tiles / kXcds, extra = tiles % kXcds;
+  const uint32_t tile = xcd * per + min(xcd, extra) + id / kXcds;
+  const uint32_t tn = tile / a.mt, tm = tile - tn * a.mt;
+  const uint32_t n0 = tn * TN, m0 = tm * TM;
+
+  const uint32_t k = a.k;
+  const uint32_t nb = k / 64;        // 64-weight blocks along K
+  // K group kg takes blocks [kbase, kbase + cnt); every group runs `steps` block steps (the
+  // barriers are shared), the ones past its range on zero-filled loads, which add nothing.
+  const uint32_t steps = (nb + KW - 1) / KW;
+  const uint32_t kbase = (uint32_t)kg * steps;
+  const uint32_t cnt = kbase < nb ? min(steps, nb - kbase) : 0u;
+  const uint32_t pitch = k >> 1;     // packed bytes per weight row
+  const uint32_t spitch = (k / (FMT == kNF4 ? 64 : 128)) * SB;
+
+  // Buffer resources: this wave's WN * 16 weight rows (rows past N read as zero), and the
+  // workgroup's TM activation rows (rows past M read as zero).
+  const uint32_t wrow0 = n0 + (uint32_t)wn * 16u * WN;
+  const uint32_t wrows = wrow0 < a.n ? min(16u * WN, a.n - wrow0) : 0u;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.packed + (size_t)wrow0 * pitch, wrows * pitch);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(reinterpret_cast<const char*>(a.scales) + (size_t)wrow0 * spitch, wrows * spitch);
+  const uint32_t xrows = min((uint32_t)TM, a.m - m0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)m0 * k, xrows * k * 2u);
+
+  // Per-lane offsets: packed bytes of row r, lane group g; the scale row 4 g + (r & 3).
+  const uint32_t woff = (uint32_t)r * pitch + 8u * (uint32_t)g;
+  const uint32_t soff = (uint32_t)(4 * g + (r & 3)) * spitch;
+
+  auto load_block = [&](uint32_t i, Block<WN>& d) __attribute__((always_inline)) {
+    const bool have = i < cnt;
+    const uint32_t kb = kbase + i;
+#pragma unroll
+    for (int t = 0; t < WN; ++t) {
+      const uint32_t off = offset_or_oob(have, woff + (uint32_t)t * 16u * pitch + kb * 32u);
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)off, 0, 0);
+      d.w[t][0] = v.x;
+      d.w[t][1] = v.y;
+    }
+#pragma unroll
+    for (int t = 0; t < WN; ++t) {
+      const uint32_t row = soff + (uint32_t)t * 16u * spitch;
+      if constexpr (FMT == kNF4) {
+        d.s[t] = buffer_load32(rs, offset_or_oob(have, row + kb * 4u));
+      } else {
+        d.s[t] = buffer_load16bit(rs, offset_or_oob(have, row + (kb >> 1) * 2u));
+      }
+    }
+  };
+
+  // x stage of the group's block i: group thread gt moves 16-byte chunks c = gt + 256 j (row
+  // c / 8, chunk c % 8) into the group's own two stages.
+  uint8_t* xg = xs + (uint32_t)kg * 2u * stage_bytes<WM>();
+  auto load_x = [&](uint32_t i, uint4 (&xr)[WM]) __attribute__((always_inline)) {
+    const uint32_t kb = kbase + i;
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      const uint32_t c = (uint32_t)gt + (uint32_t)kGroupThreads * j;
+      const uint32_t row = c >> 3, col = c & 7u;
+      xr[j] = buffer_load16(rx, offset_or_oob(i < cnt, row * k * 2u + kb * 128u + col * 16u));
+    }
+  };
+  auto store_x = [&](int buf, const uint4 (&xr)[WM]) __attribute__((always_inline)) {
+    uint8_t* st = xg + buf * stage_bytes<WM>();
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      const uint32_t c = (uint32_t)gt + (uint32_t)kGroupThreads * j;
+      *reinterpret_cast<uint4*>(st + (c >> 3) * kXPitch + (c & 7u) * 16u) = xr[j];
+    }
+  };
+
+  // Prologue.  Weights run kDepth blocks ahead of the multiply (kDepth register sets), activations
+  // two stages ahead (two register sets feeding the two LDS stages).  The loads go out in the
+  // loop's steady-state order (weights of blocks 0 .. kDepth - 2, stage 1, weights of block
+  // kDepth - 1), so that the waits the compiler derives for the loop entry match its back edge.
+  Block<WN> D[kDepth];
+  uint4 X0[WM], X1[WM];
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) load_block((uint32_t)i, D[i]);
+  load_x(0, X0);
+  fill_table<FMT, XT, kGroupThreads * KW>(tab);
+  store_x(0, X0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(1, X1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_block(kDepth - 1, D[kDepth - 1]);
+  __syncthreads();
+
+  float4_t acc[WN][WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i) {
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Twice this lane's byte offset in a table entry (see the lookup below).
+  const uint32_t laneoff = kSplit ? (uint32_t)(lane & 15) * 16u : (uint32_t)(lane & 31) * 8u;
+  const char* tabc = reinterpret_cast<const char*>(tab);
+  // This lane's B fragment offset inside a stage: activation row wm * 16 WM + r, bytes 32 g.
+  const uint32_t xoff = ((uint32_t)wm * 16u * WM + (uint32_t)r) * kXPitch + 32u * (uint32_t)g;
+
+  auto compute = [&](int buf, const Block<WN>& d) __attribute__((always_inline)) {
+    const uint8_t* st = xg + buf * stage_bytes<WM>() + xoff;
+    uint4 bf[2][WM];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int j = 0; j < WM; ++j)
+        bf[s][j] = *reinterpret_cast<const uint4*>(st + j * 16 * kXPitch + s * 16);
+    }
+#pragma unroll
+    for (int t = 0; t < WN; ++t) {
+      float4_t dd[WM];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        uint32_t p1[4], p2[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          // LDS byte address = byte * 128 + lane offset: the perm builds byte * 256 + 2 * lane
+          // offset (the packed byte into byte 1), halved by the shift.
+          const uint32_t addr =
+              __builtin_amdgcn_perm(d.w[t][s], laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb) << 8)) >> 1;
+          if (kSplit) {
+            const uint2 tv = *reinterpret_cast<const uint2*>(tabc + addr);
+            p1[kb] = tv.x;
+            p2[kb] = tv.y;
+          } else {
+            p1[kb] = *reinterpret_cast<const uint32_t*>(tabc + addr);
+          }
+        }
+        const uint4 a1 = make_uint4(p1[0], p1[1], p1[2], p1[3]);
+#pragma unroll
+        for (int j = 0; j < WM; ++j) {
+          dd[j] = mfma<XT>(a1, bf[s][j], s == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : dd[j]);
+          if (kSplit) dd[j] = mfma<XT>(make_uint4(p2[0], p2[1], p2[2], p2[3]), bf[s][j], dd[j]);
+        }
+      }
+      const uint32_t sraw = FMT == kNF4 ? d.s[t] : d.s[t] << 16;
+      const float sc[4] = {row_bcast<0>(sraw), row_bcast<1>(sraw), row_bcast<2>(sraw),
+                           row_bcast<3>(sraw)};
+#pragma unroll
+      for (int j = 0; j < WM; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][j][i] = __builtin_fmaf(dd[j][i], sc[i], acc[t][j][i]);
+      }
+    }
+  };
+
+  // Block kb (stage kb % 2, weights in d): fetch stage kb + 2 into the free register set xn
+  // (stage kb went to LDS one block ago), multiply, publish stage kb + 1 (register set xp, loaded
+  // one block ago) to the other LDS stage, fetch the weights of block kb + kDepth into d.  The
+  // barrier ends the reads of stage kb % 2 and makes stage kb + 1 visible.  The x loads are kept
+  // ahead of the weight loads (the scheduler would otherwise mix them, and the wait before the LDS
+  // store would then also wait for weights fetched later).
+  auto step = [&](uint32_t kb, Block<WN>& d, uint4 (&xn)[WM], const uint4 (&xp)[WM])
+                  __attribute__((always_inline)) {
+    load_x(kb + 2, xn);
+    __builtin_amdgcn_sched_barrier(0);
+    compute((int)(kb & 1u), d);
+    store_x((int)((kb + 1) & 1u), xp);
+    __builtin_amdgcn_sched_barrier(0);
+    load_block(kb + kDepth, d);
+    __syncthreads();
+  };
+
+  uint32_t kb = 0;
+  for (; kb + 4 <= steps; kb += 4) {
+    step(kb, D[0], X0, X1);
+    step(kb + 1, D[1], X1, X0);
+    step(kb + 2, D[2], X0, X1);
+    step(kb + 3, D[3], X1, X0);
+  }
+  if (kb < steps) step(kb, D[0], X0, X1);
+  if (kb + 1 < steps) step(kb + 1, D[1], X1, X0);
+  if (kb + 2 < steps) step(kb + 2, D[2], X0, X1);
+
+  // K groups 1 .. KW - 1 hand their sums to group 0 through LDS (the x stages are free after the
+  // last barrier), which adds them in the fixed order kg = 1, 2, ...: bitwise reproducible.
+  if constexpr (KW > 1) {
+    float4_t* red = reinterpret_cast<float4_t*>(xs);
+    const int wg4 = wave & 3;
+    if (kg > 0) {
+#pragma unroll
+      for (int t = 0; t < WN; ++t) {
+#pragma unroll
+        for (int j = 0; j < WM; ++j)
+          red[((((kg - 1) * 4 + wg4) * WN + t) * WM + j) * 64 + lane] = acc[t][j];
+      }
+    }
+    __syncthreads();
+    if (kg > 0) return;
+    for (int q = 1; q < KW; ++q) {
+#pragma unroll
+      for (int t = 0; t < WN; ++t) {
+#pragma unroll
+        for (int j = 0; j < WM; ++j) {
+          const float4_t v = red[((((q - 1) * 4 + wg4) * WN + t) * WM + j) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][j][i] += v[i];
+        }
+      }
+    }
+  }
+
+  // Stores: lane (g, r) holds y[m0 + wm * 16 WM + 16 j + r][wrow0 + 16 t + 4 g + i].
+  const uint32_t n = a.n;
+#pragma unroll
+  for (int j = 0; j < WM; ++j) {
+    const uint32_t mrow = m0 + (uint32_t)wm * 16u * WM + 16u * j + (uint32_t)r;
+    if (mrow >= a.m) continue;
+    float* yr = a.y + (size_t)mrow * n;
+#pragma unroll
+    for (int t = 0; t < WN; ++t) {
+      const uint32_t col = wrow0 + 16u * t + 4u * (uint32_t)g;
+      if ((n & 3u) == 0 && col + 3 < n) {
+        *reinterpret_cast<float4_t*>(yr + col) = acc[t][j];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (col + i < n) yr[col + i] = acc[t][j][i];
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int XT, int WN, int WM, int KW>
+hipError_t launch_wm(const GemmArgs& a, hipStream_t s) {
+  static bool raised = false;
+  constexpr int lds = KW * 2 * stage_bytes<WM>();
+  static_assert(KW == 1 || (KW - 1) * 4 * WN * WM * 64 * 16 <= lds, "K-group sums fit the stages");
+  if (!raised) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<FMT, XT, WN, WM, KW>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    raised = true;
+  }
+  hipLaunchKernelGGL((gemm_kernel<FMT, XT, WN, WM, KW>), dim3(a.tiles), dim3(kGroupThreads * KW),
+                     lds, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int XT>
+hipError_t launch_fx(const GemmArgs& a, int wn, int wm, int kw, hipStream_t s) {
+  if (wn == 2 && wm == 4 && kw == 2) return launch_wm<FMT, XT, 2, 4, 2>(a, s);
+  if (wn == 4 && wm == 4 && kw == 1) return launch_wm<FMT, XT, 4, 4, 1>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
+                       int64_t n, int64_t k, int64_t m, float* y, hipStream_t s) {
+  if (m < 1 || n < 1 || k < 64 || k % 64 != 0) return hipErrorInvalidValue;
+  // 32-bit offsets inside the buffer resources: 128 activation rows and 64 weight rows of K.
+  if (128 * k * 2 >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31) || m >= ((int64_t)1 << 31))
+    return hipErrorNotSupported;
+  const int64_t cus = device_cu_count();
+  const int wm = 4;
+  const int64_t mt = (m + 32 * wm - 1) / (32 * wm);
+  // Two workgroups of 128 x 128 per CU when there are that many tiles; else 64 x 128 tiles with
+  // two K groups (twice the waves per tile, half the blocks per wave).
+  const bool full = ((n + 127) / 128) * mt >= 2 * cus;
+  const int wn = full ? 4 : 2, kw = full ? 1 : 2;
+  const int64_t nt = (n + 32 * wn - 1) / (32 * wn);
+  if (nt * mt >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  GemmArgs a;
+  a.x = x;
+  a.packed = packed;
+  a.scales = scales;
+  a.y = y;
+  a.m = (uint32_t)m;
+  a.n = (uint32_t)n;
+  a.k = (uint32_t)k;
+  a.mt = (uint32_t)mt;
+  a.tiles = (uint32_t)(nt * mt);
+  switch (fmt) {
+    case W4_NF4_X_F16: return launch_fx<kNF4, kF16>(a, wn, wm, kw, s);
+    case W4_NF4_X_BF16: return launch_fx<kNF4, kBF16>(a, wn, wm, kw, s);
+    case W4_INT4_X_F16: return launch_fx<kINT4, kF16>(a, wn, wm, kw, s);
+    case W4_INT4_X_BF16: return launch_fx<kINT4, kBF16>(a, wn, wm, kw, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w4

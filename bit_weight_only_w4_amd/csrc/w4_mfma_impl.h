@@ -36,7 +36,7 @@
 
 #include <algorithm>
 
-#include "w4_common.h"
+#include "w4_mfma_common.h"
 
 namespace w4 {
 
@@ -67,84 +67,10 @@ struct MfmaArgs {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kTableBytes = 32768;   // 256 entries x 128 bytes
 constexpr int kThreads = 512;        // 8 waves
 constexpr int kLdsBytes = 160 * 1024;  // LDS of a CU: table, reduction area and x window
 constexpr int kQuad = 256;          // weights per quad
 constexpr int kMaxTiles = 8;        // up to 128 activation rows per launch
-
-__device__ inline uint32_t f16_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-__device__ inline uint32_t bf16_rne_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ inline uint32_t nf4_codes_in_lanes() {
-  constexpr uint32_t k[16] = W4_NF4_CODE_BITS;
-  uint32_t v = 0;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(k[q]), "i"(q));
-  return v;
-}
-
-// The byte -> decoded pair table, as in the GEMV kernel but with 32 copies of each 4-byte entry
-// (16 of each 8-byte NF4 x bf16 entry): 128 bytes per entry, lane L reading copy L % 32 (L % 16).
-// Half the GEMV's LDS, which leaves room for a larger x window.
-template <int FMT, int XT>
-__device__ inline void fill_table(uint32_t* tab) {
-  uint32_t v1, v2 = 0;
-  if (FMT == kNF4) {
-    const float c = __uint_as_float(nf4_codes_in_lanes());
-    if (XT == kF16) {
-      v1 = f16_bits(c);
-    } else {
-      v1 = bf16_rne_bits(c);
-      v2 = bf16_rne_bits(c - __uint_as_float(v1 << 16));
-    }
-  } else {
-    const float v = (float)((int)(threadIdx.x & 15u) - 8);
-    v1 = XT == kF16 ? f16_bits(v) : (__float_as_uint(v) >> 16);
-  }
-  constexpr bool kSplit = (FMT == kNF4 && XT == kBF16);
-  uint4* t4 = reinterpret_cast<uint4*>(tab);
-  const int tid = threadIdx.x;
-  // 16-byte slot i belongs to entry i >> 3: high nibble i >> 7 (uniform over a wave), low nibble
-  // (i >> 3) & 15 (the same for every slot of a thread).
-  const uint32_t lo1 = (uint32_t)__shfl((int)v1, (tid >> 3) & 15) << 16;
-  const uint32_t lo2 = kSplit ? (uint32_t)__shfl((int)v2, (tid >> 3) & 15) << 16 : 0u;
-#pragma unroll 4
-  for (int j = 0; j < kTableBytes / 16 / kThreads; ++j) {
-    const int i = tid + kThreads * j;
-    const int hi = __builtin_amdgcn_readfirstlane(i >> 7);
-    const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane((int)v1, hi) | lo1;
-    if (kSplit) {
-      const uint32_t p2 = (uint32_t)__builtin_amdgcn_readlane((int)v2, hi) | lo2;
-      t4[i] = make_uint4(p1, p2, p1, p2);
-    } else {
-      t4[i] = make_uint4(p1, p1, p1, p1);
-    }
-  }
-}
-
-// One 16x16x32 MFMA on 8-value 16-bit fragments (one uint4 each), fp32 accumulate.
-template <int XT>
-__device__ inline float4_t mfma(const uint4& a, const uint4& b, float4_t c) {
-  if constexpr (XT == kF16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
-                                                   __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, a),
-                                                    __builtin_bit_cast(bf168_t, b), c, 0, 0, 0);
-  }
-}
 
 // One quad in this lane's registers: 32 packed bytes of the 128-byte quad segments of the tile's
 // rows (two 16-byte loads), and the scale of one D row per block: lane (g, m) holds row 4 g + (m & 3),
@@ -166,12 +92,6 @@ struct Quad {
   uint32_t w[2][4];
   uint32_t s[QC];  // fp32 bits (INT4: bf16 bits in the low half)
 };
-
-// Lane i of each row of 16 lanes, broadcast to the row.
-template <int I>
-__device__ inline float row_bcast(uint32_t v) {
-  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + I, 0xF, 0xF, false));
-}
 
 // Waves per SIMD the kernel is compiled for: four (two workgroups per CU, <= 128 VGPRs) for one
 // batch tile, two above.
@@ -342,7 +262,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   load_quad(ld, P1);
   advance(ld);
   load_x(0);
-  fill_table<FMT, XT>(tab);
+  fill_table<FMT, XT, kThreads>(tab);
   __syncthreads();
   if constexpr (R == 4) {
     load_quad(ld, P2);

@@ -67,12 +67,18 @@ typedef enum {
                           stale-output bug)                                                  */
   W4_PATH_MFMA = 3,    /* decode W on chip, MFMA against x, 1 <= B <= W4_MAX_BATCH (W4_PATH_AUTO
                           takes it from B = 4, or B = 3 for matrices of 64 MiB and more)   */
-  W4_PATH_TWOPASS = 4  /* ablation: dequantize W to fp16 in the workspace, then a dense GEMV/GEMM
+  W4_PATH_TWOPASS = 4, /* ablation: dequantize W to fp16 in the workspace, then a dense GEMV/GEMM
                           (the out-of-place path of LLM Quantization on RTX 4060, "The
                           Quantization Tax: A Byte-Accounting Model")                        */
+  W4_PATH_TILED = 5    /* prefill-size GEMM: output tiles of 128 weight rows x 128 activation
+                          rows, K walked one 64-weight block at a time, weights decoded on chip
+                          into the matrix-core operands (LLM Quantization on RTX 4060, "Why Only
+                          16%", item 3: prefill needs a GEMM, not a GEMV per token); any B, meant
+                          for B >= W4_TILED_FROM_BATCH                                       */
 } w4_path_t;
 
-#define W4_MAX_BATCH 256
+#define W4_MAX_BATCH 4096
+#define W4_TILED_FROM_BATCH 128
 #define W4_MAX_SPLIT_K 64
 #define W4_MAX_GROUP 4
 
@@ -143,11 +149,22 @@ int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
 
 /* w4_gemm_smallbatch: the same operation for 1 <= B <= W4_MAX_BATCH (decode batches; Do
  * Quantization and Sparsity make LLM Inference Faster?, "NF4: fast at batch 1, slower at larger
- * batches").  Picks the fused GEMV for small B and the MFMA path (weights decoded on chip into
- * the matrix-core operands) for larger B; never materializes W_hat.  Arguments as for w4_gemv.
+ * batches").  Picks the fused GEMV for small B, the MFMA path (weights decoded on chip into
+ * the matrix-core operands) for larger B, and the tiled GEMM from B = W4_TILED_FROM_BATCH;
+ * never materializes W_hat.  Arguments as for w4_gemv, with 1 <= B <= W4_MAX_BATCH.
  * No workspace.  Asynchronous. */
 int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt,
                        int64_t N, int64_t K, int64_t B, float* y, void* stream);
+
+/* w4_gemm_prefill: the same operation through the tiled GEMM (W4_PATH_TILED) whatever B: the
+ * prompt of a prefill step, B = tokens (LLM Quantization on RTX 4060, "Why Only 16%", item 3).
+ *   x       device [B, K] fp16 or bf16 bit patterns, row-major; 16-byte aligned
+ *   packed, scales, fmt, N, K, y   as for w4_gemv
+ *   B       1 <= B <= W4_MAX_BATCH
+ * Returns W4_ERR_PATH when K is 2^22 or more (32-bit offsets inside one tile).  y[b, n] meets the
+ * same accuracy bound as w4_gemv.  No workspace.  Asynchronous on `stream`. */
+int w4_gemm_prefill(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t N,
+                    int64_t K, int64_t B, float* y, void* stream);
 
 /* w4_gemm_smallbatch_grouped: w4_gemv_grouped for 1 <= B <= W4_MAX_BATCH.  The members run in ONE
  * launch of the kernel w4_gemm_smallbatch would pick for a matrix of sum-of-N_g rows: the fused

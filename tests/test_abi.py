@@ -91,6 +91,33 @@ def test_host_validation_codes():
     assert L.w4_probe_read(vp(FAKE), 24, vp(FAKE * 2), None) == -2
 
 
+def _prefill(L, x=FAKE, p=FAKE * 2, s=FAKE * 3, fmt=1, n=64, k=256, b=512, y=FAKE * 64):
+    vp = ctypes.c_void_p
+    return L.w4_gemm_prefill(vp(x), vp(p), vp(s), fmt, n, k, b, vp(y), None)
+
+
+def test_prefill_validation_codes():
+    """w4_gemm_prefill takes 1 <= B <= W4_MAX_BATCH = 4096 and checks like w4_gemv (every case
+    here fails validation, before any launch)."""
+    import bit_weight_only_w4_amd as w4
+
+    _, L = _lib()
+    assert w4.MAX_BATCH == 4096
+    assert _prefill(L, x=0) == -1
+    assert _prefill(L, s=0) == -1
+    assert _prefill(L, fmt=0) == -4
+    assert _prefill(L, b=0) == -2
+    assert _prefill(L, b=4097) == -2
+    assert _prefill(L, k=96) == -2
+    assert _prefill(L, fmt=4, k=192) == -2
+    assert _prefill(L, p=FAKE + 8) == -3
+    assert _prefill(L, y=FAKE + 4) == -9  # y [512, 64] floats overlaps x
+    vp = ctypes.c_void_p
+    # the explicit tiled path validates the same way
+    assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 4097, vp(FAKE * 64), 5,
+                          0, None, 0, None) == -2
+
+
 def test_workspace_and_plan_logic():
     w4, _ = _lib()
     assert w4.workspace_bytes("nf4_f16", 1536, 8960, 1, "splitk", 4) == 4 * 1536 * 4
@@ -110,6 +137,10 @@ def test_workspace_and_plan_logic():
     assert w4.auto_path("nf4_f16", 8960, 1536, 64)[0] == "mfma"
     assert w4.auto_path("nf4_f16", 151936, 1536, 2)[0] == "gemv"  # 116 MB: MFMA from B = 3
     assert w4.auto_path("nf4_f16", 151936, 1536, 3)[0] == "mfma"
+    assert w4.auto_path("nf4_f16", 8960, 1536, w4.TILED_FROM_BATCH - 1)[0] == "mfma"
+    assert w4.auto_path("nf4_f16", 8960, 1536, w4.TILED_FROM_BATCH)[0] == "tiled"
+    assert w4.auto_path("int4_bf16", 151936, 1536, 4096)[0] == "tiled"
+    assert w4.workspace_bytes("nf4_f16", 8960, 1536, 512, "tiled") == 0
 
 
 def _grouped(L, n=(64, 32, 32), x=FAKE, p=None, s=None, y=None, fmt=1, k=256, b=1, groups=None,
@@ -147,7 +178,7 @@ def test_grouped_validation_codes():
 
 def test_grouped_smallbatch_validation_codes():
     """w4_gemm_smallbatch_grouped rejects what w4_gemv_grouped rejects, but takes B up to
-    W4_MAX_BATCH = 256 (every case here fails validation, before any launch)."""
+    W4_MAX_BATCH = 4096 (every case here fails validation, before any launch)."""
     _, L = _lib()
     e = "w4_gemm_smallbatch_grouped"
     assert _grouped(L, groups=0, entry=e) == -2
@@ -155,7 +186,7 @@ def test_grouped_smallbatch_validation_codes():
     assert _grouped(L, x=0, b=32, entry=e) == -1
     assert _grouped(L, n=(64, 0, 32), b=32, entry=e) == -2
     assert _grouped(L, k=96, b=32, entry=e) == -2
-    assert _grouped(L, b=257, entry=e) == -2
+    assert _grouped(L, b=4097, entry=e) == -2
     assert _grouped(L, fmt=7, b=32, entry=e) == -4
     assert _grouped(L, y=[FAKE * 30, FAKE * 30 + 128, FAKE * 32], b=1, entry=e) == -9
     # with B = 32 each y_g is 32 rows: y_1 placed inside y_0

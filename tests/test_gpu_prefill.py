@@ -1,0 +1,112 @@
+"""Tiled prefill GEMM (W4_PATH_TILED, w4_gemm_prefill) against the oracle's fp64 reference, per
+element within 2e-3 T + 1e-5 (T = sum over k of |x * w_hat|), as for every other path."""
+import pytest
+
+import synth_inputs
+from tests import gpu_util as g
+
+pytestmark = pytest.mark.gpu
+
+ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16"]
+
+
+def _case(fmt, n, k, b, seed):
+    w = synth_inputs.weights(n, k, seed=seed)
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=seed + 17)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    g.assert_quant_equal(fmt, p, s, pr, sr)
+    return x, g.to_dev_x(x, g.XDT[fmt]), p, s, pr, sr
+
+
+# Tiles are 128 (or 64) weight rows x 128 activation rows over 64-weight blocks of K: the cases
+# cover one block (K = 128 for INT4's group), an odd block count (K = 384, 8960 / 64 = 140 even,
+# 320 / 64 = 5 odd for NF4), ragged N and B in both tile directions, B = 1, and several tiles.
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("n,k,b", [(64, 128, 128), (37, 384, 130), (300, 1536, 512), (129, 8960, 200),
+                                   (1000, 2048, 257), (96, 1024, 1), (65, 128, 33), (260, 640, 300)])
+def test_tiled_parity(fmt, n, k, b):
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n * 5 + b)
+    y = w4.matmul_ex(xd, p, s, fmt, path="tiled")
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "nf4_bf16"])
+def test_tiled_odd_block_count(fmt):
+    """K = 320: five NF4 blocks, so the block loop ends on its remainder step."""
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, 200, 320, 150, seed=9)
+    y = w4.matmul_ex(xd, p, s, fmt, path="tiled")
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
+def test_prefill_entry_auto_and_determinism(fmt):
+    """w4_gemm_prefill, the explicit tiled path and the automatic path at B >= W4_TILED_FROM_BATCH
+    give bitwise the same y; a second call repeats it bitwise."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    b = 512
+    x, xd, p, s, pr, sr = _case(fmt, 8960, 1536, b, seed=2)
+    assert w4.auto_path(fmt, 8960, 1536, b)[0] == "tiled"
+    y1 = w4.gemm_prefill(xd, p, s, fmt)
+    y2 = w4.matmul_ex(xd, p, s, fmt, path="tiled")
+    y3 = w4.gemm_smallbatch(xd, p, s, fmt)
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    g.assert_y_close(fmt, y1, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt,n,k,b", [("nf4_f16", 151936, 1536, 512), ("int4_bf16", 151936, 1536, 512),
+                                       ("nf4_bf16", 1536, 8960, 512), ("int4_f16", 28672, 8192, 512),
+                                       ("nf4_f16", 8960, 1536, 4096)])
+def test_tiled_full_size_sampled(fmt, n, k, b):
+    """Full-size prefill matrices at 512 tokens (and 4096, the largest batch): weights drawn on the
+    GPU, quantized there, and 160 sampled rows (the first and the last among them) checked
+    against the oracle over every activation row."""
+    import numpy as np
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    dev = g.device()
+    gen = torch.Generator(device=dev).manual_seed(n + 5 * k + b)
+    w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+    p, s = g.gpu_quantize(fmt, w)
+    rng = np.random.default_rng(n + b)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 158, replace=False)]))
+    w_rows = w[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    del w
+    pr, sr = g.oracle_quantize(fmt, w_rows)
+    g.assert_quant_equal(fmt, p, s, pr, sr, rows=rows)
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=b + 11)
+    y = w4.gemm_prefill(g.to_dev_x(x, g.XDT[fmt]), p, s, fmt)
+    g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
+def test_grouped_at_prefill_batch(fmt):
+    """w4_gemm_smallbatch_grouped from W4_TILED_FROM_BATCH on: each member through the tiled
+    GEMM, bitwise equal to w4_gemm_prefill on that member."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    k, b = 1536, 160
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=77)
+    xd = g.to_dev_x(x, g.XDT[fmt])
+    packed, scales, refs = [], [], []
+    for i, n in enumerate((1536, 256, 256)):
+        w = synth_inputs.weights(n, k, seed=60 + i)
+        p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+        packed.append(p)
+        scales.append(s)
+        refs.append(g.oracle_quantize(fmt, w))
+    ys = w4.gemm_smallbatch_grouped(xd, packed, scales, fmt)
+    for y, p, s, (pr, sr) in zip(ys, packed, scales, refs):
+        assert torch.equal(y, w4.gemm_prefill(xd, p, s, fmt))
+        g.assert_y_close(fmt, y, x, pr, sr)
