@@ -37,10 +37,11 @@ def parse_args():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--suite", default="decode", choices=["decode", "shapes", "counters", "steps"],
+    ap.add_argument("--suite", default="decode", choices=["decode", "shapes", "counters", "steps", "prefill"],
                     help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table; "
                          "counters: a few launches of each path, for rocprofv3 --pmc runs; "
-                         "steps: the decode step in the other formats and at batch 8")
+                         "steps: the decode step in the other formats and at batch 8; "
+                         "prefill: the 197 GEMMs of a 512-token prompt and a per-shape GEMM table")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per kernel class / shape kind when timing launches")
     ap.add_argument("--schedule", default="grouped", choices=["serial", "grouped", "dag"],
@@ -620,6 +621,81 @@ def steps_suite(args, dev):
     return rows
 
 
+PREFILL_TOKENS = 512
+PREFILL_FMTS = ("nf4_f16", "int4_bf16", "nf4_bf16", "int4_f16")
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_suite(args, dev):
+    """Prefill of a 512-token prompt (LLM Quantization on RTX 4060, "Why Only 16%", item 3): the
+    197 matrix multiplications of one Qwen2.5-1.5B forward pass at B = 512 activation rows, through
+    the automatic paths (tiled GEMM for the large-N matrices, MFMA for the rest), as one HIP graph
+    per schedule; and a per-shape table at B = 512 of the tiled and MFMA paths, with the fp16 dense
+    GEMM of the decoded matrix (torch.matmul on an fp16 copy, no 4-bit decode) as context.
+    Returns dict(steps=[...], shapes=[...])."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+    import synth_inputs
+
+    b = PREFILL_TOKENS
+    out = {"tokens": b, "steps": [], "shapes": []}
+    for fmt in PREFILL_FMTS:
+        step = Step(fmt, b, "auto", dev)
+        flops = sum(2.0 * n * k * b for _, n, k in step.shapes)
+        r = {"format": fmt, "tokens": b, "flop_per_step": flops,
+             "paths": sorted({p for p, _ in step.plans})}
+        for sched in ("serial", "grouped"):
+            g = capture(step, dev, step_units(step.shapes, sched), sched)
+            ms = time_replays(g, max(3, args.steps // 10), max(2, args.warmup // 5))
+            del g
+            r[sched] = {"ms_per_step": round(ms, 4), "tok_s": round(b * 1e3 / ms, 1),
+                        "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+                        "frac_fp16_mfma_peak": round(flops / (ms / 1e3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+                        "launches": len(step_units(step.shapes, sched))}
+            log(f"[prefill] {fmt} {b} tokens {sched}: {ms:.3f} ms/step, {b * 1e3 / ms:.0f} tok/s, "
+                f"{flops / (ms / 1e3) / 1e12:.0f} TFLOP/s")
+        out["steps"].append(r)
+        del step
+        torch.cuda.empty_cache()
+    shapes = [("q/o", 1536, 1536), ("k/v", 256, 1536), ("gate/up", 8960, 1536), ("down", 1536, 8960),
+              ("lm_head", 151936, 1536)] + [(f"L.{nm}", n, k) for nm, n, k in synth_inputs.LARGE_SHAPES
+                                             if nm != "up"]
+    for fmt in ("nf4_f16", "int4_bf16"):
+        for name, n, k in shapes:
+            row = {"format": fmt, "shape": name, "n": n, "k": k, "b": b,
+                   "auto": w4.auto_path(fmt, n, k, b)[0]}
+            for path in ("tiled", "mfma"):
+                us, err = time_shape(fmt, n, k, b, path, 0, dev, min_bytes=256 << 20, reps=3)
+                if us is None:
+                    row[path] = {"error": err}
+                    continue
+                tf = 2.0 * n * k * b / us / 1e6
+                row[path] = {"us": round(us, 2), "tflops": round(tf, 1),
+                             "frac_fp16_mfma_peak": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
+            if fmt == "nf4_f16":
+                w = torch.randn(n, k, device=dev, dtype=torch.float16)
+                x = torch.randn(b, k, device=dev, dtype=torch.float16)
+                for _ in range(3):
+                    y = x @ w.t()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(20):
+                    y = x @ w.t()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / 20
+                row["fp16_dense_torch"] = {"us": round(us, 2), "tflops": round(2.0 * n * k * b / us / 1e6, 1)}
+                del w, x, y
+                torch.cuda.empty_cache()
+            out["shapes"].append(row)
+            log(f"[prefill] {fmt} {name} {n}x{k} B={b}: " +
+                ", ".join(f"{p} {row[p]['us']} us" for p in ("tiled", "mfma", "fp16_dense_torch")
+                          if p in row and "us" in row[p]))
+    return out
+
+
 def shapes_suite(args, dev):
     """Per-shape table for the other workloads: INT4 decode steps (B = 1, 8) and split-K vs one
     pass on down; small-batch GEMM on gate / down / lm_head at B = 1, 8, 32, 128 for the GEMV,
@@ -830,6 +906,19 @@ def main():
                 json.dump(rows, f, indent=1)
         print(json.dumps({"metric": "decode step in other formats and batches", "rows": rows}),
               flush=True)
+        return
+    if args.suite == "prefill":
+        import torch
+
+        import bit_weight_only_w4_amd as w4
+
+        w4.lib()
+        res = prefill_suite(args, torch.device("cuda:0"))
+        if args.report:
+            with open(args.report, "w") as f:
+                json.dump(res, f, indent=1)
+        print(json.dumps({"metric": "prefill step (512 tokens) and per-shape GEMM table",
+                          "steps": res["steps"]}), flush=True)
         return
     if args.suite == "shapes":
         import torch

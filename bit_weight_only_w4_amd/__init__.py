@@ -23,6 +23,7 @@ STATUS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "FORMAT", -5: "NONF
           -6: "WORKSPACE", -7: "PATH", -8: "HIP", -9: "ALIAS"}
 MAX_BATCH = 4096
 TILED_FROM_BATCH = 128
+TILED_FROM_ROWS = 4096
 MAX_SPLIT_K = 64
 
 _lib = None

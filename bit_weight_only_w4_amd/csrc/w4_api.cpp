@@ -243,6 +243,13 @@ bool prefer_mfma(int64_t n, int64_t k, int64_t b) {
   return b >= (large ? kMfmaFromBatchLarge : kMfmaFromBatch);
 }
 
+// The tiled GEMM from W4_TILED_FROM_BATCH activation rows, for matrices of W4_TILED_FROM_ROWS rows
+// and more.  Measured on MI355X at 512 activation rows (NF4 x fp16, INT4 x bf16): tiled against
+// MFMA 48 / 57 us on 8960 x 1536, 437 / 500 us on 151936 x 1536, 403 / 519 us on 28672 x 8192;
+// with 1536 or 2048 rows the tiles do not fill the CUs and the MFMA path is faster (17 / 14 us on
+// 1536 x 1536, 66 / 57 us on 1536 x 8960).
+bool prefer_tiled(int64_t n, int64_t b) { return b >= W4_TILED_FROM_BATCH && n >= W4_TILED_FROM_ROWS; }
+
 // Arguments of a grouped call: every member valid on its own, the members' summed rows in range,
 // and no member's y overlapping another member's y, packed bytes or scales.
 int validate_group(const void* x, int groups, const uint8_t* const* packed,
@@ -272,18 +279,36 @@ int validate_group(const void* x, int groups, const uint8_t* const* packed,
   return W4_OK;
 }
 
-// A validated group: one tiled-GEMM launch per member from B = W4_TILED_FROM_BATCH, else one MFMA
-// launch over all members (mfma), else one fused-GEMV launch, or an MFMA launch when the GEMV has
-// no launch shape for (K, B).
+// A validated group: from B = W4_TILED_FROM_BATCH a tiled-GEMM launch per member of at least
+// W4_TILED_FROM_ROWS rows and one MFMA launch over the others; below it one MFMA launch over all
+// members (mfma), else one fused-GEMV launch, or an MFMA launch when the GEMV has no launch shape
+// for (K, B).
 int run_group(const void* x, int groups, const uint8_t* const* packed, const void* const* scales,
               const int64_t* n, float* const* y, int fmt, int64_t k, int64_t b, bool mfma,
               hipStream_t s) {
   if (mfma && b >= W4_TILED_FROM_BATCH) {
+    const uint8_t* rp[kMaxGroup];
+    const void* rs[kMaxGroup];
+    int64_t rn[kMaxGroup];
+    float* ry[kMaxGroup];
+    int rest = 0;
     for (int g = 0; g < groups; ++g) {
-      const int st = run_tiled(x, packed[g], scales[g], fmt, n[g], k, b, y[g], s);
-      if (st != W4_OK) return st;
+      if (prefer_tiled(n[g], b)) {
+        const int st = run_tiled(x, packed[g], scales[g], fmt, n[g], k, b, y[g], s);
+        if (st != W4_OK) return st;
+      } else {
+        rp[rest] = packed[g];
+        rs[rest] = scales[g];
+        rn[rest] = n[g];
+        ry[rest] = y[g];
+        ++rest;
+      }
     }
-    return W4_OK;
+    if (rest == 0) return W4_OK;
+    const hipError_t e = launch_mfma_members(fmt, reinterpret_cast<const uint16_t*>(x), rest, rp, rs,
+                                             rn, ry, k, b, s);
+    if (e == hipErrorNotSupported) return W4_ERR_PATH;
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
   }
   GemvPlan p;
   int64_t nrb[kMaxGroup], grid_g[kMaxGroup];
@@ -421,7 +446,7 @@ int w4_auto_path(int fmt, int64_t n, int64_t k, int64_t b, size_t workspace_byte
   int s = 1;
   int path;
   GemvPlan p;
-  if (b >= W4_TILED_FROM_BATCH) {
+  if (prefer_tiled(n, b)) {
     path = W4_PATH_TILED;
   } else if (prefer_mfma(n, k, b) || !plan_gemv(n, k, (int)b, 1, &p)) {
     path = W4_PATH_MFMA;

@@ -73,12 +73,15 @@ typedef enum {
   W4_PATH_TILED = 5    /* prefill-size GEMM: output tiles of 128 weight rows x 128 activation
                           rows, K walked one 64-weight block at a time, weights decoded on chip
                           into the matrix-core operands (LLM Quantization on RTX 4060, "Why Only
-                          16%", item 3: prefill needs a GEMM, not a GEMV per token); any B, meant
-                          for B >= W4_TILED_FROM_BATCH                                       */
+                          16%", item 3: prefill needs a GEMM, not a GEMV per token); any B.
+                          W4_PATH_AUTO takes it from B = W4_TILED_FROM_BATCH for matrices of
+                          N >= W4_TILED_FROM_ROWS (fewer rows leave too few tiles: the MFMA path
+                          is faster there)                                                   */
 } w4_path_t;
 
 #define W4_MAX_BATCH 4096
 #define W4_TILED_FROM_BATCH 128
+#define W4_TILED_FROM_ROWS 4096
 #define W4_MAX_SPLIT_K 64
 #define W4_MAX_GROUP 4
 
@@ -150,8 +153,8 @@ int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
 /* w4_gemm_smallbatch: the same operation for 1 <= B <= W4_MAX_BATCH (decode batches; Do
  * Quantization and Sparsity make LLM Inference Faster?, "NF4: fast at batch 1, slower at larger
  * batches").  Picks the fused GEMV for small B, the MFMA path (weights decoded on chip into
- * the matrix-core operands) for larger B, and the tiled GEMM from B = W4_TILED_FROM_BATCH;
- * never materializes W_hat.  Arguments as for w4_gemv, with 1 <= B <= W4_MAX_BATCH.
+ * the matrix-core operands) for larger B, and the tiled GEMM from B = W4_TILED_FROM_BATCH when
+ * N >= W4_TILED_FROM_ROWS; never materializes W_hat.  Arguments as for w4_gemv, with 1 <= B <= W4_MAX_BATCH.
  * No workspace.  Asynchronous. */
 int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt,
                        int64_t N, int64_t K, int64_t B, float* y, void* stream);
@@ -170,7 +173,9 @@ int w4_gemm_prefill(const void* x, const uint8_t* packed, const void* scales, in
  * launch of the kernel w4_gemm_smallbatch would pick for a matrix of sum-of-N_g rows: the fused
  * GEMV (as w4_gemv_grouped) for small B, the MFMA kernel over the row tiles of every member for
  * larger B (LLM Compressor 0.14: GPTQ's 15x speedup is one fused loop, section "Batching
- * layers").  Arguments, ownership and errors as for w4_gemv_grouped, with B up to
+ * layers").  From B = W4_TILED_FROM_BATCH each member of N_g >= W4_TILED_FROM_ROWS runs as its
+ * own tiled-GEMM launch (bitwise equal to w4_gemm_prefill on it) and the others share one MFMA
+ * launch.  Arguments, ownership and errors as for w4_gemv_grouped, with B up to
  * W4_MAX_BATCH.  Each y_g meets w4_gemm_smallbatch's accuracy bound on that member.  No
  * workspace.  Asynchronous on `stream`. */
 int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* packed,

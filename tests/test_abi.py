@@ -140,6 +140,8 @@ def test_workspace_and_plan_logic():
     assert w4.auto_path("nf4_f16", 8960, 1536, w4.TILED_FROM_BATCH - 1)[0] == "mfma"
     assert w4.auto_path("nf4_f16", 8960, 1536, w4.TILED_FROM_BATCH)[0] == "tiled"
     assert w4.auto_path("int4_bf16", 151936, 1536, 4096)[0] == "tiled"
+    assert w4.auto_path("nf4_f16", 1536, 8960, 512)[0] == "mfma"  # too few rows for the tiles
+    assert w4.auto_path("nf4_f16", w4.TILED_FROM_ROWS, 1536, 512)[0] == "tiled"
     assert w4.workspace_bytes("nf4_f16", 8960, 1536, 512, "tiled") == 0
 
 

@@ -43,6 +43,27 @@ def test_tiled_odd_block_count(fmt):
     g.assert_y_close(fmt, y, x, pr, sr)
 
 
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_tiled_scale_range_fallback(fmt):
+    """Rows whose block scales fall outside the range where fp16 holds every scaled code (tiny,
+    huge, and zero rows) next to ordinary rows: with fp16 activations their blocks take the exact
+    fp32 form, the others the folded fp16 form; all within the bound."""
+    import numpy as np
+
+    import bit_weight_only_w4_amd as w4
+
+    n, k, b = 300, 1536, 200
+    w = synth_inputs.weights(n, k, seed=31)
+    factors = np.array([1.0, 1e-3, 1.0, 1e6, 1e-7, 1.0, 0.0, 1.0], dtype=np.float32)
+    w = (w * factors[np.arange(n) % len(factors)][:, None]).astype(np.float32)
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=32)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    g.assert_quant_equal(fmt, p, s, pr, sr)
+    y = w4.matmul_ex(g.to_dev_x(x, g.XDT[fmt]), p, s, fmt, path="tiled")
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
 @pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
 def test_prefill_entry_auto_and_determinism(fmt):
     """w4_gemm_prefill, the explicit tiled path and the automatic path at B >= W4_TILED_FROM_BATCH
@@ -90,8 +111,9 @@ def test_tiled_full_size_sampled(fmt, n, k, b):
 
 @pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
 def test_grouped_at_prefill_batch(fmt):
-    """w4_gemm_smallbatch_grouped from W4_TILED_FROM_BATCH on: each member through the tiled
-    GEMM, bitwise equal to w4_gemm_prefill on that member."""
+    """w4_gemm_smallbatch_grouped from W4_TILED_FROM_BATCH on: members of W4_TILED_FROM_ROWS rows
+    and more through the tiled GEMM (bitwise equal to w4_gemm_prefill on them), the others in one
+    MFMA launch; every member against the oracle."""
     import torch
 
     import bit_weight_only_w4_amd as w4
@@ -99,14 +121,14 @@ def test_grouped_at_prefill_batch(fmt):
     k, b = 1536, 160
     x = synth_inputs.activations(b, k, g.XDT[fmt], seed=77)
     xd = g.to_dev_x(x, g.XDT[fmt])
-    packed, scales, refs = [], [], []
-    for i, n in enumerate((1536, 256, 256)):
+    packed, scales, refs, ns = [], [], [], (w4.TILED_FROM_ROWS + 100, 1536, 256)
+    for i, n in enumerate(ns):
         w = synth_inputs.weights(n, k, seed=60 + i)
         p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
         packed.append(p)
         scales.append(s)
         refs.append(g.oracle_quantize(fmt, w))
     ys = w4.gemm_smallbatch_grouped(xd, packed, scales, fmt)
-    for y, p, s, (pr, sr) in zip(ys, packed, scales, refs):
-        assert torch.equal(y, w4.gemm_prefill(xd, p, s, fmt))
+    assert torch.equal(ys[0], w4.gemm_prefill(xd, packed[0], scales[0], fmt))
+    for y, (pr, sr) in zip(ys, refs):
         g.assert_y_close(fmt, y, x, pr, sr)
