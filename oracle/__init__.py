@@ -15,6 +15,10 @@ What it computes (all in numpy fp64 unless a storage format fixes the precision)
 * ``quantize_int4``  -- symmetric INT4 with a +8 zero point (My Triton Kernel Ties bitsandbytes,
   section "The kernels", first bug), one bf16 scale per 128-column group, round half to even
   (LLM Compressor 0.14, section "Details worth knowing").
+* ``quantize_fp4``   -- FP4 (E2M1) codes through a 16-entry table, block 64, fp32 scale
+  absmax / 6, the pages' ladder of thresholds with ties to the even code (LLM Compressor 0.14,
+  section "Details worth knowing"; the FP4-named fused kernel of My Triton Kernel Ties
+  bitsandbytes, section "The kernels").
 * ``dequant_*``      -- the decoded weights, exact in fp64.
 * ``gemv_reference`` -- y = x . W_hat^T and T = |x| . |W_hat|^T in fp64: the fused kernel only moves
   where dequantization happens (LLM Quantization on RTX 4060, section "Kernel Implementation"), so
@@ -27,12 +31,14 @@ Pins: every function is checked against facts fixed by the pages or by mathemati
 from .bits import bf16_bits_to_f64, f16_bits_to_f64, f32_to_bf16_rne_bits, x_bits_to_f64
 from .nf4 import NF4_BLOCK, dequant_nf4, nf4_codebook, nf4_midpoints, quantize_nf4
 from .int4 import INT4_GROUP, dequant_int4, quantize_int4
+from .fp4 import FP4_BLOCK, FP4_GRID, dequant_fp4, fp4_codebook, fp4_magnitude_index, quantize_fp4
 from .gemv import accept, dequant, gemv_reference, unpack_nibbles, violation_ratio
 
 __all__ = [
     "NF4_BLOCK", "INT4_GROUP",
     "nf4_codebook", "nf4_midpoints", "quantize_nf4", "dequant_nf4",
     "quantize_int4", "dequant_int4",
+    "FP4_BLOCK", "FP4_GRID", "fp4_codebook", "fp4_magnitude_index", "quantize_fp4", "dequant_fp4",
     "unpack_nibbles", "dequant", "gemv_reference", "accept", "violation_ratio",
     "f16_bits_to_f64", "bf16_bits_to_f64", "x_bits_to_f64", "f32_to_bf16_rne_bits",
 ]
