@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4.so")
 
-FORMATS = {"nf4_f16": 1, "nf4_bf16": 2, "int4_f16": 3, "int4_bf16": 4}
+FORMATS = {"nf4_f16": 1, "nf4_bf16": 2, "int4_f16": 3, "int4_bf16": 4, "fp4_f16": 5, "fp4_bf16": 6}
 PATHS = {"auto": 0, "gemv": 1, "splitk": 2, "mfma": 3, "twopass": 4, "tiled": 5}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 STATUS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "FORMAT", -5: "NONFINITE",
@@ -51,6 +51,7 @@ def lib() -> ctypes.CDLL:
         i64, vp, sz, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         L.w4_quantize_nf4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.w4_quantize_int4.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.w4_quantize_fp4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.w4_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_smallbatch.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_prefill.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
@@ -70,7 +71,8 @@ def lib() -> ctypes.CDLL:
         L.w4_gemv_grouped_plan.argtypes = [ci, ci, ctypes.POINTER(i64), i64, i64, ip, ip, ip, ip, ip]
         L.w4_probe_read.argtypes = [vp, sz, vp, vp]
         L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
-        for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_gemv", "w4_gemm_smallbatch",
+        for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_quantize_fp4", "w4_gemv",
+                     "w4_gemm_smallbatch",
                      "w4_matmul_ex", "w4_auto_path", "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
                      "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped",
                      "w4_gemm_prefill"):
@@ -138,6 +140,21 @@ def quantize_nf4(w, stream=None):
           "w4_quantize_nf4")
     return packed, absmax
 
+
+
+def quantize_fp4(w, stream=None):
+    """fp32 [N, K] device weights -> (packed uint8 [N, K/2], scale fp32 [N, K/64]) in FP4 (E2M1)."""
+    import torch
+
+    _need_cuda(w)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n, max(k // 64, 1)), dtype=torch.float32, device=w.device)
+    check(lib().w4_quantize_fp4(_ptr(w), n, k, _ptr(packed), _ptr(scale), _stream(stream)),
+          "w4_quantize_fp4")
+    return packed, scale
 
 def quantize_int4(w, stream=None):
     """fp32 [N, K] device weights -> (packed uint8 [N, K/2], bf16 scale bits int16 [N, K/128])."""

@@ -37,7 +37,7 @@ const CodebookInit g_codebook;
 
 bool valid_fmt(int fmt) {
   return fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_BF16 || fmt == W4_INT4_X_F16 ||
-         fmt == W4_INT4_X_BF16;
+         fmt == W4_INT4_X_BF16 || fmt == W4_FP4_X_F16 || fmt == W4_FP4_X_BF16;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -60,9 +60,9 @@ int validate(const void* x, const uint8_t* packed, const void* scales, int fmt, 
     return W4_ERR_SHAPE;
   if (n > ((int64_t)1 << 62) / k) return W4_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 4)) return W4_ERR_ALIGN;
-  if (!aligned(scales, fmt_weight(fmt) == kNF4 ? 4 : 2)) return W4_ERR_ALIGN;
+  if (!aligned(scales, fmt_scale_bytes(fmt))) return W4_ERR_ALIGN;
   const size_t ybytes = (size_t)(b * n) * 4;
-  const size_t sbytes = (size_t)(n * (k / g)) * (fmt_weight(fmt) == kNF4 ? 4 : 2);
+  const size_t sbytes = (size_t)(n * (k / g)) * fmt_scale_bytes(fmt);
   if (overlaps(y, ybytes, x, (size_t)(b * k) * 2) || overlaps(y, ybytes, packed, (size_t)(n * k / 2)) ||
       overlaps(y, ybytes, scales, sbytes))
     return W4_ERR_ALIAS;
@@ -265,7 +265,7 @@ int validate_group(const void* x, int groups, const uint8_t* const* packed,
     n_total += n[g];
   }
   if (n_total >= kMaxDim) return W4_ERR_SHAPE;
-  const size_t sdiv = (size_t)fmt_group(fmt), ssz = fmt_weight(fmt) == kNF4 ? 4 : 2;
+  const size_t sdiv = (size_t)fmt_group(fmt), ssz = fmt_scale_bytes(fmt);
   for (int g = 0; g < groups; ++g) {
     const size_t yb = (size_t)(b * n[g]) * 4;
     for (int h = 0; h < groups; ++h) {
@@ -360,6 +360,23 @@ int w4_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* packed, float
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
   if (launch_quantize_nf4(w, n, k, packed, absmax, s) != hipSuccess) return W4_ERR_HIP;
+  int flag = 0;
+  if (quantize_error_read(&flag, s) != hipSuccess) return W4_ERR_HIP;
+  return flag ? W4_ERR_NONFINITE : W4_OK;
+}
+
+int w4_quantize_fp4(const float* w, int64_t n, int64_t k, uint8_t* packed, float* scale,
+                    void* stream) {
+  if (!w || !packed || !scale) return W4_ERR_NULL;
+  if (n < 1 || k < 64 || k % 64 != 0 || n >= kMaxDim || k >= kMaxDim) return W4_ERR_SHAPE;
+  if (!aligned(w, 8) || !aligned(packed, 16) || !aligned(scale, 4)) return W4_ERR_ALIGN;
+  if (overlaps(w, (size_t)(n * k) * 4, packed, (size_t)(n * k / 2)) ||
+      overlaps(w, (size_t)(n * k) * 4, scale, (size_t)(n * k / 64) * 4) ||
+      overlaps(packed, (size_t)(n * k / 2), scale, (size_t)(n * k / 64) * 4))
+    return W4_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
+  if (launch_quantize_fp4(w, n, k, packed, scale, s) != hipSuccess) return W4_ERR_HIP;
   int flag = 0;
   if (quantize_error_read(&flag, s) != hipSuccess) return W4_ERR_HIP;
   return flag ? W4_ERR_NONFINITE : W4_OK;

@@ -19,6 +19,13 @@ namespace w4 {
    0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u, 0x3ee1a4b5u, 0x3f1007a9u, \
    0x3f3913b0u, 0x3f800000u}
 
+// FP4 (E2M1) table, fp32: nibbles 0-7 the magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}, 8-15 their
+// negatives (bit 3 is the sign), as LLM Compressor 0.14, "Details worth knowing" gives the grid.
+#define W4_FP4_CODE_BITS                                                                    \
+  {0x00000000u, 0x3f000000u, 0x3f800000u, 0x3fc00000u, 0x40000000u, 0x40400000u, 0x40800000u, \
+   0x40c00000u, 0x80000000u, 0xbf000000u, 0xbf800000u, 0xbfc00000u, 0xc0000000u, 0xc0400000u, \
+   0xc0800000u, 0xc0c00000u}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // 128-bit streaming load marked non-temporal (the data is read once).
@@ -72,12 +79,21 @@ __device__ inline uint32_t buffer_load16bit(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 
-enum Fmt { kNF4 = 0, kINT4 = 1 };
+// Weight formats.  NF4 and FP4 share the layout (blocks of 64, fp32 scale) and differ only in the
+// 16-entry table; INT4 has groups of 128 with a bf16 scale.
+enum Fmt { kNF4 = 0, kINT4 = 1, kFP4 = 2 };
 enum XType { kF16 = 0, kBF16 = 1 };
 
-inline int fmt_weight(int fmt) { return (fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_BF16) ? kNF4 : kINT4; }
-inline int fmt_xtype(int fmt) { return (fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16) ? kF16 : kBF16; }
-inline int64_t fmt_group(int fmt) { return fmt_weight(fmt) == kNF4 ? 64 : 128; }
+inline int fmt_weight(int fmt) {
+  return (fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_BF16)   ? kNF4
+         : (fmt == W4_FP4_X_F16 || fmt == W4_FP4_X_BF16) ? kFP4
+                                                         : kINT4;
+}
+inline int fmt_xtype(int fmt) {
+  return (fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16 || fmt == W4_FP4_X_F16) ? kF16 : kBF16;
+}
+inline int64_t fmt_group(int fmt) { return fmt_weight(fmt) == kINT4 ? 128 : 64; }
+inline size_t fmt_scale_bytes(int fmt) { return fmt_weight(fmt) == kINT4 ? 2 : 4; }
 
 // Shape of one fused-GEMV launch (host-chosen; see plan_gemv in w4_api.cpp).
 struct GemvPlan {
@@ -141,6 +157,8 @@ hipError_t launch_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* pa
                                float* absmax, hipStream_t s);
 hipError_t launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* packed,
                                 uint16_t* scale, hipStream_t s);
+hipError_t launch_quantize_fp4(const float* w, int64_t n, int64_t k, uint8_t* packed, float* scale,
+                               hipStream_t s);
 hipError_t quantize_error_reset(hipStream_t s);
 hipError_t quantize_error_read(int* flag, hipStream_t s);
 hipError_t launch_dequant_f16(int fmt, const uint8_t* packed, const void* scales, int64_t n,

@@ -68,7 +68,7 @@ template <int FMT, int XT, int WN, int WM, int KW>
 __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a) {
   constexpr int TN = 32 * WN, TM = 32 * WM;
   constexpr bool kSplit = FMT == kNF4 && XT == kBF16;
-  constexpr int SB = FMT == kNF4 ? 4 : 2;  // bytes per scale
+  constexpr int SB = FMT != kINT4 ? 4 : 2;  // bytes per scale
   // LDS: the decode table (static, at address 0, so a lookup address needs no base), then the two
   // x stages of each K group (dynamic), reused at the end for the K groups' sums.
   __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   const uint32_t kbase = (uint32_t)kg * steps;
   const uint32_t cnt = kbase < nb ? min(steps, nb - kbase) : 0u;
   const uint32_t pitch = k >> 1;     // packed bytes per weight row
-  const uint32_t spitch = (k / (FMT == kNF4 ? 64 : 128)) * SB;
+  const uint32_t spitch = (k / (FMT != kINT4 ? 64 : 128)) * SB;
 
   // Buffer resources: this wave's WN * 16 weight rows (rows past N read as zero), and the
   // workgroup's TM activation rows (rows past M read as zero).
@@ -124,7 +124,7 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
 #pragma unroll
     for (int t = 0; t < WN; ++t) {
       const uint32_t row = soff + (uint32_t)t * 16u * spitch;
-      if constexpr (FMT == kNF4) {
+      if constexpr (FMT != kINT4) {
         d.s[t] = buffer_load32(rs, offset_or_oob(have, row + kb * 4u));
       } else {
         d.s[t] = buffer_load16bit(rs, offset_or_oob(have, row + (kb >> 1) * 2u));
@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
           if (kSplit) dd[j] = mfma<XT>(make_uint4(p2[0], p2[1], p2[2], p2[3]), bf[s][j], dd[j]);
         }
       }
-      const uint32_t sraw = FMT == kNF4 ? d.s[t] : d.s[t] << 16;
+      const uint32_t sraw = FMT != kINT4 ? d.s[t] : d.s[t] << 16;
       const float sc[4] = {row_bcast<0>(sraw), row_bcast<1>(sraw), row_bcast<2>(sraw),
                            row_bcast<3>(sraw)};
 #pragma unroll
@@ -362,6 +362,8 @@ hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const 
     case W4_NF4_X_BF16: return launch_fx<kNF4, kBF16>(a, wn, wm, kw, s);
     case W4_INT4_X_F16: return launch_fx<kINT4, kF16>(a, wn, wm, kw, s);
     case W4_INT4_X_BF16: return launch_fx<kINT4, kBF16>(a, wn, wm, kw, s);
+    case W4_FP4_X_F16: return launch_fx<kFP4, kF16>(a, wn, wm, kw, s);
+    case W4_FP4_X_BF16: return launch_fx<kFP4, kBF16>(a, wn, wm, kw, s);
   }
   return hipErrorInvalidValue;
 }

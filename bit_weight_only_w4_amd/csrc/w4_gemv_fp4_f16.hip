@@ -1,0 +1,10 @@
+// Instantiation of the fused GEMV for one weight x activation format (fp4_f16), one member
+// per launch.
+#include "w4_gemv_impl.h"
+
+namespace w4 {
+hipError_t launch_gemv_fp4_f16(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                               hipStream_t s) {
+  return launch_fx<kFP4, kF16, false>(b, a, groups, p, s);
+}
+}  // namespace w4

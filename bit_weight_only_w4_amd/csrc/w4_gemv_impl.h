@@ -8,7 +8,7 @@
 // Layout of the work:
 //   * A "team" of T lanes (16..512) owns one output row.  Lane t of a team streams the 16-byte
 //     chunks t, t + T, t + 2T, ... of the row (one global_load_dwordx4 each; consecutive lanes on
-//     consecutive chunks).  A chunk is 32 weights: half an NF4 block or a quarter of an INT4
+//     consecutive chunks).  A chunk is 32 weights: half an NF4/FP4 block or a quarter of an INT4
 //     group, so each chunk needs exactly one scale.
 //   * The lane keeps the activations of its chunks in VGPRs for the whole launch and walks the
 //     row blocks of its workgroup (grid-stride) with the next two row blocks' packed bytes and
@@ -48,24 +48,30 @@ __device__ inline uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Lane q (q < 16) receives the fp32 bits of NF4 code q; the constants go lane by lane from scalar
-// registers, so building the table needs no memory access.
-__device__ inline uint32_t nf4_codes_in_lanes() {
-  constexpr uint32_t k[16] = W4_NF4_CODE_BITS;
+// Lane q (q < 16) receives the fp32 bits of table entry q of the NF4 or FP4 format; the constants
+// go lane by lane from scalar registers, so building the table needs no memory access.
+template <int FMT>
+__device__ inline uint32_t codes_in_lanes() {
+  constexpr uint32_t kn[16] = W4_NF4_CODE_BITS;
+  constexpr uint32_t kf[16] = W4_FP4_CODE_BITS;
   uint32_t v = 0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(k[q]), "i"(q));
+  for (int q = 0; q < 16; ++q)
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(FMT == kFP4 ? kf[q] : kn[q]), "i"(q));
   return v;
 }
 
 // The decoded 16-bit value(s) of nibble (lane & 15), meaningful in lanes 0..15: the fp16 code
-// (NF4 x fp16), the bf16 hi/lo split of the code (NF4 x bf16), or q - 8 in the activation type
-// (INT4, exact).
+// (NF4 x fp16), the bf16 hi/lo split of the code (NF4 x bf16), the FP4 code (exact in both 16-bit
+// types), or q - 8 in the activation type (INT4, exact).
 template <int FMT, int XT>
 __device__ inline void lane_decode(uint32_t& v1, uint32_t& v2) {
   v2 = 0;
-  if (FMT == kNF4) {
-    const float c = __uint_as_float(nf4_codes_in_lanes());
+  if (FMT == kFP4) {
+    const float c = __uint_as_float(codes_in_lanes<kFP4>());
+    v1 = XT == kF16 ? f16_bits(c) : (__float_as_uint(c) >> 16);
+  } else if (FMT == kNF4) {
+    const float c = __uint_as_float(codes_in_lanes<kNF4>());
     if (XT == kF16) {
       v1 = f16_bits(c);
     } else {
@@ -131,15 +137,15 @@ __device__ inline float team_sum_wave(float v, int team) {
 // Bytes of one row's scales, and the byte offset of chunk `chunk`'s scale within the row.
 template <int FMT>
 __device__ inline uint32_t scale_pitch(int64_t k) {
-  return FMT == kNF4 ? (uint32_t)(k >> 6) * 4u : (uint32_t)(k >> 7) * 2u;
+  return FMT != kINT4 ? (uint32_t)(k >> 6) * 4u : (uint32_t)(k >> 7) * 2u;
 }
 template <int FMT>
 __device__ inline uint32_t scale_offset(int chunk) {
-  return FMT == kNF4 ? (uint32_t)(chunk >> 1) * 4u : (uint32_t)(chunk >> 2) * 2u;
+  return FMT != kINT4 ? (uint32_t)(chunk >> 1) * 4u : (uint32_t)(chunk >> 2) * 2u;
 }
 template <int FMT>
 __device__ inline float load_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if (FMT == kNF4) return __uint_as_float(buffer_load32(r, off));
+  if (FMT != kINT4) return __uint_as_float(buffer_load32(r, off));
   return __uint_as_float(buffer_load16bit(r, off) << 16);  // bf16 bits -> fp32, exact
 }
 

@@ -25,11 +25,15 @@ __device__ inline uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ inline uint32_t nf4_codes_in_lanes() {
-  constexpr uint32_t k[16] = W4_NF4_CODE_BITS;
+// Lane q (q < 16) receives the fp32 bits of table entry q of the NF4 or FP4 format.
+template <int FMT>
+__device__ inline uint32_t codes_in_lanes() {
+  constexpr uint32_t kn[16] = W4_NF4_CODE_BITS;
+  constexpr uint32_t kf[16] = W4_FP4_CODE_BITS;
   uint32_t v = 0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(k[q]), "i"(q));
+  for (int q = 0; q < 16; ++q)
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(FMT == kFP4 ? kf[q] : kn[q]), "i"(q));
   return v;
 }
 
@@ -40,8 +44,11 @@ __device__ inline uint32_t nf4_codes_in_lanes() {
 template <int FMT, int XT, int THREADS>
 __device__ inline void fill_table(uint32_t* tab) {
   uint32_t v1, v2 = 0;
-  if (FMT == kNF4) {
-    const float c = __uint_as_float(nf4_codes_in_lanes());
+  if (FMT == kFP4) {
+    const float c = __uint_as_float(codes_in_lanes<kFP4>());  // exact in both 16-bit types
+    v1 = XT == kF16 ? f16_bits(c) : (__float_as_uint(c) >> 16);
+  } else if (FMT == kNF4) {
+    const float c = __uint_as_float(codes_in_lanes<kNF4>());
     if (XT == kF16) {
       v1 = f16_bits(c);
     } else {

@@ -88,7 +88,7 @@ constexpr int kMaxTiles = 8;        // up to 128 activation rows per launch
 //   for L >= 2, i.e. the 16 weights from 32 (L & 1) + 16 (L >> 1) of each block.
 template <int FMT>
 struct Quad {
-  static constexpr int QC = FMT == kNF4 ? 4 : 2;  // scale blocks per quad
+  static constexpr int QC = FMT != kINT4 ? 4 : 2;  // scale blocks per quad
   uint32_t w[2][4];
   uint32_t s[QC];  // fp32 bits (INT4: bf16 bits in the low half)
 };
@@ -100,10 +100,10 @@ constexpr int min_waves(int t) { return t == 1 ? 4 : 2; }
 template <int FMT, int XT, int T, int KW, bool GROUPED>
 __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a) {
   constexpr int RW = 8 / KW;
-  constexpr int KC = FMT == kNF4 ? 64 : 128;  // weights per scale block
+  constexpr int KC = FMT != kINT4 ? 64 : 128;  // weights per scale block
   constexpr int QC = kQuad / KC;              // blocks per quad
   constexpr int STEPS = KC / 32;              // MFMA steps per block
-  constexpr int SB = FMT == kNF4 ? 4 : 2;     // bytes per scale
+  constexpr int SB = FMT != kINT4 ? 4 : 2;     // bytes per scale
   constexpr bool kSplit = (FMT == kNF4 && XT == kBF16);
   // LDS: the decode table (static, at address 0, so a lookup address needs no base), then the
   // dynamic part: the K-group reduction area and the x window.
@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
     // multiplied (inside the matrix their bytes are the next row's; zeroing them here would make
     // the loop wait for the load).  INT4: two bf16 scales, 2-byte aligned, two loads, moved to the
     // high half when multiplied (for the same reason).
-    if constexpr (FMT == kNF4) {
+    if constexpr (FMT != kINT4) {
       const uint4 sv = buffer_load16(cur.rs, offset_or_oob(qb < nblocks, sbase));
       d.s[0] = sv.x;
       d.s[1] = sv.y;
@@ -281,7 +281,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   const uint8_t* xw = xs + (uint32_t)kg * (seg * 16u);  // this K group's part of the window
 
   // k offset (in the block) of the first of this lane's weights for MFMA step 0 (see Quad).
-  const int klane = FMT == kNF4 ? 32 * (g & 1) + 16 * (g >> 1) : 32 * g;
+  const int klane = FMT != kINT4 ? 32 * (g & 1) + 16 * (g >> 1) : 32 * g;
 
   // Multiply the quad held in d: quad q of the K group, wq = its index inside the current window.
   auto compute = [&](int q, int wq, const Quad<FMT>& d) __attribute__((always_inline)) {
@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
       wh[1][i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0x128, 0xF, 0xF, false);  // row_ror:8
     }
     uint32_t wb[QC][STEPS];
-    if constexpr (FMT == kNF4) {
+    if constexpr (FMT != kINT4) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const auto s0 = __builtin_amdgcn_permlane32_swap(wh[h][0], wh[h][2], false, false);
@@ -355,7 +355,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
         // step (they would not fit the registers left by the accumulators).
         if constexpr (T == 8) __builtin_amdgcn_sched_barrier(0);
       }
-      const uint32_t sraw = FMT == kNF4 ? ((c > 0 && qb + c >= nblocks) ? 0u : d.s[c]) : d.s[c] << 16;
+      const uint32_t sraw = FMT != kINT4 ? ((c > 0 && qb + c >= nblocks) ? 0u : d.s[c]) : d.s[c] << 16;
       const float sc[4] = {row_bcast<0>(sraw), row_bcast<1>(sraw), row_bcast<2>(sraw),
                            row_bcast<3>(sraw)};
 #pragma unroll
@@ -526,6 +526,8 @@ hipError_t dispatch(int op, int fmt, const MfmaArgs& a, int tiles, int kw, int l
     case W4_NF4_X_BF16: return dispatch_fx<kNF4, kBF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
     case W4_INT4_X_F16: return dispatch_fx<kINT4, kF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
     case W4_INT4_X_BF16: return dispatch_fx<kINT4, kBF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
+    case W4_FP4_X_F16: return dispatch_fx<kFP4, kF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
+    case W4_FP4_X_BF16: return dispatch_fx<kFP4, kBF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
   }
   return hipErrorInvalidValue;
 }

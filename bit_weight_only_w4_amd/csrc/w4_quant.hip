@@ -12,6 +12,12 @@
 // -8, 7) against the rounded s, nibble = q + 8.  fp32(A / 7) is taken as the fp64 quotient rounded
 // to fp32, which equals the correctly rounded fp32 quotient (53 >= 2 * 24 + 2).
 //
+// FP4 (LLM Compressor 0.14, "Details worth knowing": a ladder of thresholds onto the magnitudes
+// {0, 0.5, 1, 1.5, 2, 3, 4, 6}, alternating <= and < so that ties go to the even code): blocks of
+// 64, s = fp32(A / 6) (the fp64 quotient rounded to fp32, as for INT4), magnitude index = the
+// ladder applied to the fp64 quotient |w| / s, sign bit = (w < 0); the thresholds are dyadic, so
+// the fp64 quotient of two fp32 values is on the same side of each as the exact ratio.
+//
 // One lane handles one pair of weights (one output byte): element 2i goes to the high nibble.
 // Absmax is an integer max over |bits| (the order of non-negative floats), reduced across the 32
 // lanes of an NF4 block or the 64 lanes of an INT4 group with cross-lane shuffles.
@@ -101,6 +107,41 @@ __global__ void __launch_bounds__(256) quant_int4_kernel(const float* __restrict
   }
 }
 
+// FP4 magnitude index of y = |w| / s >= 0: one step past each threshold crossed; a value on
+// 0.25, 1.25, 2.5 or 5 stays below, one on 0.75, 1.75 or 3.5 goes above (the even index).
+__device__ inline uint32_t fp4_magnitude(double y) {
+  return (y > 0.25 ? 1u : 0u) + (y >= 0.75 ? 1u : 0u) + (y > 1.25 ? 1u : 0u) + (y >= 1.75 ? 1u : 0u) +
+         (y > 2.5 ? 1u : 0u) + (y >= 3.5 ? 1u : 0u) + (y > 5.0 ? 1u : 0u);
+}
+
+__global__ void __launch_bounds__(256) quant_fp4_kernel(const float* __restrict__ w, int64_t pairs,
+                                                         uint8_t* __restrict__ packed,
+                                                         float* __restrict__ scale) {
+  const int64_t p = blockIdx.x * 256ll + threadIdx.x;
+  const bool valid = p < pairs;  // pairs is a multiple of 32: a whole block is valid or not
+  const float2 v = reinterpret_cast<const float2*>(w)[valid ? p : 0];
+  const uint32_t a0 = __float_as_uint(v.x) & 0x7FFFFFFFu;
+  const uint32_t a1 = __float_as_uint(v.y) & 0x7FFFFFFFu;
+  if (valid && (a0 >= 0x7F800000u || a1 >= 0x7F800000u)) g_w4_nonfinite = 1;
+  uint32_t m = a0 > a1 ? a0 : a1;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)m, off);
+    m = o > m ? o : m;
+  }
+  const float s32 = (float)((double)__uint_as_float(m) / 6.0);
+  const double s = (double)s32;
+  uint32_t n0 = 0, n1 = 0;
+  if (s != 0.0) {
+    n0 = fp4_magnitude(fabs((double)v.x) / s) | (v.x < 0.0f ? 8u : 0u);
+    n1 = fp4_magnitude(fabs((double)v.y) / s) | (v.y < 0.0f ? 8u : 0u);
+  }
+  if (valid) {
+    packed[p] = (uint8_t)((n0 << 4) | n1);
+    if ((threadIdx.x & 31) == 0) scale[p >> 5] = s32;
+  }
+}
+
 }  // namespace
 
 hipError_t quantize_error_reset(hipStream_t s) {
@@ -122,6 +163,15 @@ hipError_t launch_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* pa
   const int64_t blocks = (pairs + 255) / 256;
   hipLaunchKernelGGL(quant_nf4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, pairs, packed,
                      absmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp4(const float* w, int64_t n, int64_t k, uint8_t* packed, float* scale,
+                               hipStream_t s) {
+  const int64_t pairs = n * (k / 2);
+  const int64_t blocks = (pairs + 255) / 256;
+  hipLaunchKernelGGL(quant_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, pairs, packed,
+                     scale);
   return hipGetLastError();
 }
 

@@ -8,14 +8,15 @@
 // path.
 //
 // The decoded weights are materialized in fp16 for both activation types: for INT4,
-// (q - 8) * s is exact in fp16 whenever it is in fp16 range; for NF4, code * absmax is rounded
-// once to fp16 (relative error <= 2^-11, inside the acceptance bound).  bf16 would not be.
+// (q - 8) * s is exact in fp16 whenever it is in fp16 range; for NF4 and FP4, code * scale is
+// rounded once to fp16 (relative error <= 2^-11, inside the acceptance bound).  bf16 would not be.
 #include "w4_common.h"
 
 namespace w4 {
 namespace {
 
 __constant__ uint32_t c_nf4_code_bits2[16] = W4_NF4_CODE_BITS;
+__constant__ uint32_t c_fp4_code_bits2[16] = W4_FP4_CODE_BITS;
 
 template <int FMT>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint4* __restrict__ packed,
@@ -26,7 +27,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint4* __restrict__ 
     const int64_t row = c / cpr;
     const int cr = (int)(c - row * cpr);
     float s;
-    if (FMT == kNF4) {
+    if (FMT != kINT4) {
       s = reinterpret_cast<const float*>(scales)[row * (k >> 6) + (cr >> 1)];
     } else {
       s = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(scales)[row * (k >> 7) + (cr >> 2)] << 16);
@@ -44,6 +45,9 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint4* __restrict__ 
         if (FMT == kNF4) {
           vh = __uint_as_float(c_nf4_code_bits2[hi]) * s;
           vl = __uint_as_float(c_nf4_code_bits2[lo]) * s;
+        } else if (FMT == kFP4) {
+          vh = __uint_as_float(c_fp4_code_bits2[hi]) * s;
+          vl = __uint_as_float(c_fp4_code_bits2[lo]) * s;
         } else {
           vh = (float)((int)hi - 8) * s;
           vl = (float)((int)lo - 8) * s;
@@ -123,7 +127,11 @@ hipError_t launch_dequant_f16(int fmt, const uint8_t* packed, const void* scales
   const int64_t chunks = n * cpr;
   int64_t blocks = (chunks + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  if (fmt_weight(fmt) == kNF4) {
+  if (fmt_weight(fmt) == kFP4) {
+    hipLaunchKernelGGL(dequant_kernel<kFP4>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const uint4*>(packed), scales, chunks, cpr, k,
+                       reinterpret_cast<uint4*>(w_hat));
+  } else if (fmt_weight(fmt) == kNF4) {
     hipLaunchKernelGGL(dequant_kernel<kNF4>, dim3((unsigned)blocks), dim3(256), 0, s,
                        reinterpret_cast<const uint4*>(packed), scales, chunks, cpr, k,
                        reinterpret_cast<uint4*>(w_hat));

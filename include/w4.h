@@ -36,18 +36,24 @@ extern "C" {
  *         scales = float[N, K/64]  (LLM Quantization on RTX 4060, "Standard Expectation from
  *         Quantization").
  *   INT4: symmetric, stored nibble = q + 8 (My Triton Kernel Ties bitsandbytes, "The kernels"),
- *         groups of 128 along K, scales = bf16 bit patterns uint16[N, K/128]. */
+ *         groups of 128 along K, scales = bf16 bit patterns uint16[N, K/128].
+ *   FP4 : E2M1 codes through a 16-entry table (nibble bit 3 = sign, bits 0-2 index the
+ *         magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; LLM Compressor 0.14, "Details worth
+ *         knowing"), blocks of 64 along K, one fp32 scale absmax / 6 per block,
+ *         scales = float[N, K/64]; decoded weight = table[nibble] * scale. */
 typedef enum {
   W4_NF4_X_F16 = 1,
   W4_NF4_X_BF16 = 2,
   W4_INT4_X_F16 = 3,
-  W4_INT4_X_BF16 = 4
+  W4_INT4_X_BF16 = 4,
+  W4_FP4_X_F16 = 5,
+  W4_FP4_X_BF16 = 6
 } w4_format_t;
 
 typedef enum {
   W4_OK = 0,
   W4_ERR_NULL = -1,      /* a required pointer is NULL                                        */
-  W4_ERR_SHAPE = -2,     /* N, K or B out of range, or K not a multiple of 64 (NF4) / 128 (INT4) */
+  W4_ERR_SHAPE = -2,     /* N, K or B out of range, or K not a multiple of 64 (NF4, FP4) / 128 (INT4) */
   W4_ERR_ALIGN = -3,     /* packed or x not 16-byte aligned, scales or y not element aligned  */
   W4_ERR_FORMAT = -4,    /* unknown w4_format_t                                               */
   W4_ERR_NONFINITE = -5, /* quantize met a NaN or Inf weight (outputs are then meaningless)   */
@@ -111,6 +117,19 @@ int w4_quantize_nf4(const float* w, int64_t N, int64_t K, uint8_t* packed, float
  * Synchronizes `stream`.  Returns W4_ERR_NONFINITE if any weight is NaN or Inf. */
 int w4_quantize_int4(const float* w, int64_t N, int64_t K, uint8_t* packed, uint16_t* scale_bf16,
                      void* stream);
+
+/* w4_quantize_fp4: FP4 (E2M1) quantization, blocks of 64 along K (LLM Compressor 0.14: GPTQ's 15x
+ * speedup is one fused loop, "Details worth knowing": the ladder of thresholds onto
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6}, alternating <= and < so that ties go to the even code).
+ *   w      device float[N, K] (fp32), read only; 8-byte aligned
+ *   N, K   N >= 1, K a positive multiple of 64
+ *   packed device uint8[N, K/2], written; 16-byte aligned; element 2i in the high nibble
+ *   scale  device float[N, K/64], written: s = fp32(absmax / 6) of each block (0 for an all-zero
+ *          block, whose nibbles are all 0); 4-byte aligned
+ * Nibble of w: sign bit (w < 0) | ladder index of |w| / s, the quotient taken in fp64.
+ * Synchronizes `stream`.  Returns W4_ERR_NONFINITE if any weight is NaN or Inf. */
+int w4_quantize_fp4(const float* w, int64_t N, int64_t K, uint8_t* packed, float* scale,
+                    void* stream);
 
 /* -------------------------------------------------------------------------- matmul --------- */
 

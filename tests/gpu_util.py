@@ -6,8 +6,10 @@ import numpy as np
 
 import oracle
 
-WFMT = {"nf4_f16": "nf4", "nf4_bf16": "nf4", "int4_f16": "int4", "int4_bf16": "int4"}
-XDT = {"nf4_f16": "f16", "nf4_bf16": "bf16", "int4_f16": "f16", "int4_bf16": "bf16"}
+WFMT = {"nf4_f16": "nf4", "nf4_bf16": "nf4", "int4_f16": "int4", "int4_bf16": "int4",
+        "fp4_f16": "fp4", "fp4_bf16": "fp4"}
+XDT = {"nf4_f16": "f16", "nf4_bf16": "bf16", "int4_f16": "f16", "int4_bf16": "bf16",
+       "fp4_f16": "f16", "fp4_bf16": "bf16"}
 
 
 def device():
@@ -36,15 +38,19 @@ def gpu_quantize(fmt: str, w_dev):
 
     if WFMT[fmt] == "nf4":
         return w4.quantize_nf4(w_dev)
+    if WFMT[fmt] == "fp4":
+        return w4.quantize_fp4(w_dev)
     return w4.quantize_int4(w_dev)
 
 
 def scales_to_np(fmt: str, s_dev) -> np.ndarray:
     s = s_dev.cpu().numpy()
-    return s if WFMT[fmt] == "nf4" else s.view(np.uint16)
+    return s if WFMT[fmt] in ("nf4", "fp4") else s.view(np.uint16)
 
 
 def oracle_quantize(fmt: str, w: np.ndarray):
+    if WFMT[fmt] == "fp4":
+        return oracle.quantize_fp4(w)
     return oracle.quantize_nf4(w) if WFMT[fmt] == "nf4" else oracle.quantize_int4(w)
 
 

@@ -29,7 +29,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for required in ("w4_quantize_nf4", "w4_quantize_int4", "w4_gemv", "w4_gemm_smallbatch",
+    for required in ("w4_quantize_nf4", "w4_quantize_int4", "w4_quantize_fp4", "w4_gemv",
+                     "w4_gemm_smallbatch",
                      "w4_matmul_ex", "w4_workspace_bytes"):
         assert required in names
 
@@ -67,7 +68,7 @@ def test_host_validation_codes():
     assert _gemv(L, x=0) == -1
     assert _gemv(L, y=0) == -1
     assert _gemv(L, fmt=0) == -4
-    assert _gemv(L, fmt=5) == -4
+    assert _gemv(L, fmt=7) == -4  # 5, 6 are FP4
     assert _gemv(L, n=0) == -2
     assert _gemv(L, k=96) == -2  # NF4 needs K % 64
     assert _gemv(L, fmt=3, k=192) == -2  # INT4 needs K % 128
@@ -88,6 +89,11 @@ def test_host_validation_codes():
     assert L.w4_quantize_nf4(None, 4, 64, vp(FAKE), vp(FAKE * 2), None) == -1
     assert L.w4_quantize_nf4(vp(FAKE), 4, 96, vp(FAKE * 8), vp(FAKE * 9), None) == -2
     assert L.w4_quantize_int4(vp(FAKE), 4, 64, vp(FAKE * 8), vp(FAKE * 9), None) == -2
+    assert L.w4_quantize_fp4(None, 4, 64, vp(FAKE), vp(FAKE * 2), None) == -1
+    assert L.w4_quantize_fp4(vp(FAKE), 4, 96, vp(FAKE * 8), vp(FAKE * 9), None) == -2  # K % 64
+    assert L.w4_quantize_fp4(vp(FAKE), 4, 64, vp(FAKE * 8 + 4), vp(FAKE * 9), None) == -3
+    assert _gemv(L, fmt=5, k=96) == -2  # FP4 needs K % 64
+    assert _gemv(L, fmt=6, s=FAKE * 3 + 2) == -3  # FP4 scales are fp32
     assert L.w4_probe_read(vp(FAKE), 24, vp(FAKE * 2), None) == -2
 
 

@@ -12,7 +12,7 @@ from tests import gpu_util as g
 
 pytestmark = pytest.mark.gpu
 
-ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16"]
+ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16"]
 
 
 def _case(fmt, n, k, b, seed, sigma=0.02):
@@ -38,6 +38,17 @@ def test_gemv_parity(fmt, n, k, b):
     import bit_weight_only_w4_amd as w4
 
     x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n + k + b)
+    y = w4.gemv(xd, p, s, fmt)
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "nf4_bf16", "fp4_f16", "fp4_bf16"])
+@pytest.mark.parametrize("n,k,b", [(70, 192, 1), (129, 320, 2), (33, 64, 1), (300, 1472, 3)])
+def test_gemv_odd_block_count(fmt, n, k, b):
+    """64-weight-block formats with an odd number of blocks per row (K % 128 == 64)."""
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n + 3 * k + b)
     y = w4.gemv(xd, p, s, fmt)
     g.assert_y_close(fmt, y, x, pr, sr)
 
@@ -132,8 +143,10 @@ def test_one_hot_and_zero_activations(fmt):
     w_hat = oracle.dequant(g.WFMT[fmt], pr, sr)
     assert np.all(y[1] == 0)
     # decoded codes: fp16 rounding for NF4 x fp16 (<= 3.3e-4 relative), a two-term bf16 split
-    # for NF4 x bf16 (<= 2^-16 relative), exact (q - 8) for INT4
-    rtol = {"nf4_f16": 3.5e-4, "nf4_bf16": 2.0 ** -16}.get(fmt, 0.0)
+    # for NF4 x bf16 (<= 2^-16 relative), exact (q - 8) for INT4; FP4 codes are exact in both
+    # activation types and only the fp32 product code * scale rounds (<= 2^-24 relative)
+    rtol = {"nf4_f16": 3.5e-4, "nf4_bf16": 2.0 ** -16, "fp4_f16": 2.0 ** -23,
+            "fp4_bf16": 2.0 ** -23}.get(fmt, 0.0)
     assert np.allclose(y[0], w_hat[:, 700], rtol=rtol, atol=0)
     assert torch.isfinite(torch.as_tensor(y)).all()
 

@@ -6,7 +6,7 @@ from tests import gpu_util as g
 
 pytestmark = pytest.mark.gpu
 
-ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16"]
+ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16"]
 
 
 def _case(fmt, n, k, b, seed):
@@ -26,6 +26,17 @@ def test_mfma_parity(fmt, n, k, b):
     import bit_weight_only_w4_amd as w4
 
     x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n * 7 + b)
+    y = w4.matmul_ex(xd, p, s, fmt, path="mfma")
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "nf4_bf16", "fp4_f16", "fp4_bf16"])
+@pytest.mark.parametrize("n,k,b", [(70, 192, 16), (129, 320, 33), (40, 64, 4)])
+def test_mfma_odd_block_count(fmt, n, k, b):
+    """64-weight-block formats with an odd number of blocks per row (K % 128 == 64)."""
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n * 5 + k + b)
     y = w4.matmul_ex(xd, p, s, fmt, path="mfma")
     g.assert_y_close(fmt, y, x, pr, sr)
 
@@ -56,7 +67,8 @@ def test_mfma_deterministic(fmt):
 
 @pytest.mark.parametrize("fmt,n,k,b", [("nf4_f16", 151936, 1536, 8), ("nf4_bf16", 151936, 1536, 128),
                                        ("int4_f16", 1536, 8960, 8), ("int4_bf16", 8960, 1536, 32),
-                                       ("nf4_f16", 28672, 8192, 16)])
+                                       ("nf4_f16", 28672, 8192, 16), ("fp4_f16", 8960, 1536, 32),
+                                       ("fp4_bf16", 151936, 1536, 8)])
 def test_mfma_full_size_sampled(fmt, n, k, b):
     """Full-size matrices (persistent grids with several row tiles per workgroup, K groups, x
     windows in several phases): weights drawn on the GPU, quantized there, and 160 sampled rows

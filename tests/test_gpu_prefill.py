@@ -7,7 +7,7 @@ from tests import gpu_util as g
 
 pytestmark = pytest.mark.gpu
 
-ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16"]
+ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16"]
 
 
 def _case(fmt, n, k, b, seed):
@@ -33,9 +33,9 @@ def test_tiled_parity(fmt, n, k, b):
     g.assert_y_close(fmt, y, x, pr, sr)
 
 
-@pytest.mark.parametrize("fmt", ["nf4_f16", "nf4_bf16"])
+@pytest.mark.parametrize("fmt", ["nf4_f16", "nf4_bf16", "fp4_f16", "fp4_bf16"])
 def test_tiled_odd_block_count(fmt):
-    """K = 320: five NF4 blocks, so the block loop ends on its remainder step."""
+    """K = 320: five 64-weight blocks (NF4, FP4), so the block loop ends on its remainder step."""
     import bit_weight_only_w4_amd as w4
 
     x, xd, p, s, pr, sr = _case(fmt, 200, 320, 150, seed=9)
@@ -64,7 +64,7 @@ def test_tiled_scale_range_fallback(fmt):
     g.assert_y_close(fmt, y, x, pr, sr)
 
 
-@pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
+@pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16", "fp4_bf16"])
 def test_prefill_entry_auto_and_determinism(fmt):
     """w4_gemm_prefill, the explicit tiled path and the automatic path at B >= W4_TILED_FROM_BATCH
     give bitwise the same y; a second call repeats it bitwise."""
@@ -84,7 +84,8 @@ def test_prefill_entry_auto_and_determinism(fmt):
 
 @pytest.mark.parametrize("fmt,n,k,b", [("nf4_f16", 151936, 1536, 512), ("int4_bf16", 151936, 1536, 512),
                                        ("nf4_bf16", 1536, 8960, 512), ("int4_f16", 28672, 8192, 512),
-                                       ("nf4_f16", 8960, 1536, 4096)])
+                                       ("nf4_f16", 8960, 1536, 4096), ("fp4_bf16", 8960, 1536, 512),
+                                       ("fp4_f16", 28672, 8192, 512)])
 def test_tiled_full_size_sampled(fmt, n, k, b):
     """Full-size prefill matrices at 512 tokens (and 4096, the largest batch): weights drawn on the
     GPU, quantized there, and 160 sampled rows (the first and the last among them) checked

@@ -8,7 +8,7 @@ from tests import gpu_util as g
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["nf4_f16", "int4_f16"]
+FMTS = ["nf4_f16", "int4_f16", "fp4_f16"]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -22,7 +22,8 @@ def test_quantize_bitexact_gaussian(fmt, n, k, seed):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_quantize_edge_values(fmt):
-    """Zero blocks, -0.0, denormals, huge magnitudes, constant blocks, exact ties."""
+    """Zero blocks, -0.0, denormals, huge magnitudes, constant blocks, exact ties (NF4, INT4 and
+    FP4 midpoints)."""
     rng = np.random.default_rng(21)
     w = (rng.standard_normal((12, 256)) * 0.02).astype(np.float32)
     w[0] = 0.0
@@ -41,6 +42,15 @@ def test_quantize_edge_values(fmt):
     w[6, 129:137] = [0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 6.5]
     w[7] = rng.integers(-7, 8, 256).astype(np.float32) * np.float32(2.0 ** -5)
     w[7, ::128] = 7 * 2.0 ** -5
+    # FP4 ties: absmax 6 gives s = 1, so the ladder's midpoints are exact ties; absmax 3 gives
+    # s = 0.5 and the same ties at half the size
+    w[8] = 0.0
+    w[8, 0] = 6.0
+    w[8, 1:8] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    w[8, 8:15] = [-0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0]
+    w[8, 64] = -3.0
+    w[8, 65:72] = [0.125, 0.375, 0.625, 0.875, 1.25, 1.75, 2.5]
+    w = np.ascontiguousarray(w)
     p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
     g.assert_quant_equal(fmt, p, s, *g.oracle_quantize(fmt, w))
 
