@@ -32,7 +32,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--fmt", default="nf4_f16", choices=["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16"])
+    ap.add_argument("--fmt", default="nf4_f16",
+                    choices=["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16"])
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,7 +65,7 @@ def log(*a):
 
 def algorithmic_bytes(fmt: str, n: int, k: int, b: int) -> int:
     """Bytes the method itself must move for one GEMV: packed weights + scales + x + y."""
-    scale_bytes = n * k // 16 if fmt.startswith("nf4") else n * k // 64
+    scale_bytes = n * k // 64 if fmt.startswith("int4") else n * k // 16
     return n * k // 2 + scale_bytes + 2 * b * k + 4 * b * n
 
 
@@ -117,7 +118,7 @@ class Step:
                 seed = 1000 + 8 * layer + j
             g = torch.Generator(device=dev).manual_seed(seed)
             w = torch.randn(n, k, generator=g, device=dev) * synth_inputs.QWEN15_SIGMA
-            packed, scales = (w4.quantize_nf4(w) if fmt.startswith("nf4") else w4.quantize_int4(w))
+            packed, scales = w4.quantize(fmt, w)
             del w
             self.mats.append((packed, scales))
             self.ys.append(torch.empty(b, n, device=dev))
@@ -178,7 +179,7 @@ class Step:
 
 
 def _gemv_name(fmt, b, iters, threads, grouped):
-    fmt_i = 0 if fmt.startswith("nf4") else 1
+    fmt_i = {"nf4": 0, "int4": 1, "fp4": 2}[fmt.split("_")[0]]
     xt = 0 if fmt.endswith("_f16") else 1
     return f"gemv_kernel<{fmt_i}, {xt}, {b}, {iters}, {threads}, {'true' if grouped else 'false'}>"
 
@@ -473,13 +474,13 @@ def cpu_baseline(fmt, b, seconds):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
         threads = 1
-    wf = "nf4" if fmt.startswith("nf4") else "int4"
+    wf = fmt.split("_")[0]
     xd = "f16" if fmt.endswith("_f16") else "bf16"
     sample = [("q", 1536, 1536, 1000), ("gate", 8960, 1536, 1004), ("down", 1536, 8960, 1006)]
     mats = []
     for name, n, k, seed in sample:
         w = synth_inputs.weights(n, k, seed=seed)
-        q = oracle.quantize_nf4(w) if wf == "nf4" else oracle.quantize_int4(w)
+        q = {"nf4": oracle.quantize_nf4, "int4": oracle.quantize_int4, "fp4": oracle.quantize_fp4}[wf](w)
         mats.append((q, synth_inputs.activations(b, k, xd, seed=7)))
     sample_weights = sum(n * k for _, n, k, _ in sample)
     t0 = time.perf_counter()
@@ -489,7 +490,7 @@ def cpu_baseline(fmt, b, seconds):
             oracle.gemv_reference(x, xd, oracle.dequant(wf, p, s))
         passes += 1
         el = time.perf_counter() - t0
-        if el >= seconds or passes >= 50:
+        if el >= seconds or passes >= 1000:
             break
     per_pass = el / passes
     step_weights = sum(n * k for _, n, k in synth_inputs.decode_step_shapes())
@@ -519,14 +520,14 @@ def time_shape(fmt, n, k, b, path, split_k, dev, min_bytes=600 << 20, reps=5):
 
     import bit_weight_only_w4_amd as w4
 
-    wb = n * k // 2 + (n * k // 16 if fmt.startswith("nf4") else n * k // 64)
+    wb = n * k // 2 + (n * k // 64 if fmt.startswith("int4") else n * k // 16)
     copies = max(1, min(4096, -(-min_bytes // wb)))
     xdt = torch.float16 if fmt.endswith("_f16") else torch.bfloat16
     gen = torch.Generator(device=dev).manual_seed(n * 31 + k)
     mats = []
     for c in range(copies):
         w = torch.randn(n, k, generator=gen, device=dev) * 0.02
-        mats.append(w4.quantize_nf4(w) if fmt.startswith("nf4") else w4.quantize_int4(w))
+        mats.append(w4.quantize(fmt, w))
         del w
     x = torch.randn(b, k, generator=gen, device=dev).to(xdt)
     y = torch.empty(b, n, device=dev)
@@ -590,7 +591,8 @@ def time_read_probe(nbytes, dev, min_bytes=600 << 20, reps=5):
 
 
 # Decode steps besides the benchmark line's: (format, batch).
-OTHER_STEPS = [("int4_bf16", 1), ("int4_bf16", 8), ("nf4_f16", 8), ("nf4_bf16", 1), ("int4_f16", 1)]
+OTHER_STEPS = [("int4_bf16", 1), ("int4_bf16", 8), ("nf4_f16", 8), ("nf4_bf16", 1), ("int4_f16", 1),
+               ("fp4_f16", 1), ("fp4_bf16", 1), ("fp4_f16", 8)]
 
 
 def steps_suite(args, dev):
@@ -622,7 +624,7 @@ def steps_suite(args, dev):
 
 
 PREFILL_TOKENS = 512
-PREFILL_FMTS = ("nf4_f16", "int4_bf16", "nf4_bf16", "int4_f16")
+PREFILL_FMTS = ("nf4_f16", "int4_bf16", "nf4_bf16", "int4_f16", "fp4_f16", "fp4_bf16")
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 
 
@@ -789,7 +791,7 @@ def counters_suite(dev):
     for name, fmt, n, k, b, path in COUNTER_CASES:
         gen = torch.Generator(device=dev).manual_seed(n + k)
         w = torch.randn(n, k, generator=gen, device=dev) * 0.02
-        p, sc = w4.quantize_nf4(w) if fmt.startswith("nf4") else w4.quantize_int4(w)
+        p, sc = w4.quantize(fmt, w)
         del w
         xdt = torch.float16 if fmt.endswith("_f16") else torch.bfloat16
         x = torch.randn(b, k, generator=gen, device=dev).to(xdt)
@@ -1003,7 +1005,7 @@ def main():
         "config": {
             "workload": (f"Qwen2.5-1.5B decode step: 197 distinct GEMVs (28x q,k,v,o,gate,"
                          f"up,down + lm_head) in {len(units)} launches, {wfmt} "
-                         f"{'bs64 fp32 absmax' if wfmt == 'NF4' else 'g128 bf16 scale'}, "
+                         f"{ {'NF4': 'bs64 fp32 absmax', 'INT4': 'g128 bf16 scale', 'FP4': 'E2M1 bs64 fp32 absmax/6'}[wfmt]}, "
                          f"{args.fmt.split('_')[1]} x, batch {args.batch}, fp32 accumulate/output"),
             "format": args.fmt,
             "batch": args.batch,

@@ -141,7 +141,6 @@ def quantize_nf4(w, stream=None):
     return packed, absmax
 
 
-
 def quantize_fp4(w, stream=None):
     """fp32 [N, K] device weights -> (packed uint8 [N, K/2], scale fp32 [N, K/64]) in FP4 (E2M1)."""
     import torch
@@ -156,6 +155,7 @@ def quantize_fp4(w, stream=None):
           "w4_quantize_fp4")
     return packed, scale
 
+
 def quantize_int4(w, stream=None):
     """fp32 [N, K] device weights -> (packed uint8 [N, K/2], bf16 scale bits int16 [N, K/128])."""
     import torch
@@ -169,6 +169,20 @@ def quantize_int4(w, stream=None):
     check(lib().w4_quantize_int4(_ptr(w), n, k, _ptr(packed), _ptr(scale), _stream(stream)),
           "w4_quantize_int4")
     return packed, scale
+
+
+def weight_format(fmt: str) -> str:
+    """"nf4", "int4" or "fp4": the weight encoding of a format name such as "fp4_bf16"."""
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt!r}")
+    return fmt.split("_")[0]
+
+
+def quantize(fmt: str, w, stream=None):
+    """Quantize fp32 [N, K] device weights in the weight encoding of `fmt` (activation type aside):
+    the packed nibbles and the scales that the matmul entry points take for that format."""
+    q = {"nf4": quantize_nf4, "int4": quantize_int4, "fp4": quantize_fp4}[weight_format(fmt)]
+    return q(w, stream)
 
 
 def _mm_shapes(x, packed):

@@ -13,6 +13,12 @@ def test_codebook_is_the_signed_e2m1_grid():
     assert c.dtype == np.float32 and c.shape == (16,)
     assert list(c[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
     assert np.array_equal(c[8:], -c[:8]) and np.signbit(c[8])
+    # E2M1 read from the bits of each nibble: sign, two exponent bits with bias 1, one mantissa
+    # bit, exponent 0 subnormal (0.m x 2^0)
+    for n in range(16):
+        sign, e, m = n >> 3, (n >> 1) & 3, n & 1
+        mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+        assert c[n] == (-mag if sign else mag) and bool(np.signbit(c[n])) == bool(sign)
     # every entry is exact in fp16 and in bf16 (two significant bits at most)
     assert np.array_equal(c.astype(np.float16).astype(np.float32), c)
     assert np.array_equal((c.view(np.uint32) & 0xFFFF0000).view(np.float32), c)
