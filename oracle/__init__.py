@@ -15,6 +15,9 @@ What it computes (all in numpy fp64 unless a storage format fixes the precision)
 * ``quantize_int4``  -- symmetric INT4 with a +8 zero point (My Triton Kernel Ties bitsandbytes,
   section "The kernels", first bug), one bf16 scale per 128-column group, round half to even
   (LLM Compressor 0.14, section "Details worth knowing").
+* ``quantize_int4_asym`` -- asymmetric INT4: unsigned codes 0..15 with a zero point per group,
+  one bf16 scale per 128-column group, code = rint(clamp(w / s + z, 0, 15)) (LLM Compressor
+  0.14, sections "The fused kernel" and "What those numbers leave out").
 * ``quantize_fp4``   -- FP4 (E2M1) codes through a 16-entry table, block 64, fp32 scale
   absmax / 6, the pages' ladder of thresholds with ties to the even code (LLM Compressor 0.14,
   section "Details worth knowing"; the FP4-named fused kernel of My Triton Kernel Ties
@@ -31,6 +34,7 @@ Pins: every function is checked against facts fixed by the pages or by mathemati
 from .bits import bf16_bits_to_f64, f16_bits_to_f64, f32_to_bf16_rne_bits, x_bits_to_f64
 from .nf4 import NF4_BLOCK, dequant_nf4, nf4_codebook, nf4_midpoints, quantize_nf4
 from .int4 import INT4_GROUP, dequant_int4, quantize_int4
+from .int4_asym import INT4A_GROUP, dequant_int4_asym, int4_asym_scale_zero, quantize_int4_asym
 from .fp4 import FP4_BLOCK, FP4_GRID, dequant_fp4, fp4_codebook, fp4_magnitude_index, quantize_fp4
 from .gemv import accept, dequant, gemv_reference, unpack_nibbles, violation_ratio
 
@@ -38,6 +42,7 @@ __all__ = [
     "NF4_BLOCK", "INT4_GROUP",
     "nf4_codebook", "nf4_midpoints", "quantize_nf4", "dequant_nf4",
     "quantize_int4", "dequant_int4",
+    "INT4A_GROUP", "int4_asym_scale_zero", "quantize_int4_asym", "dequant_int4_asym",
     "FP4_BLOCK", "FP4_GRID", "fp4_codebook", "fp4_magnitude_index", "quantize_fp4", "dequant_fp4",
     "unpack_nibbles", "dequant", "gemv_reference", "accept", "violation_ratio",
     "f16_bits_to_f64", "bf16_bits_to_f64", "x_bits_to_f64", "f32_to_bf16_rne_bits",

@@ -33,7 +33,7 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
 
 
 def dequant(fmt: str, packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Decoded fp64 weights for ``fmt`` in {"nf4", "int4", "fp4"}."""
+    """Decoded fp64 weights for ``fmt`` in {"nf4", "int4", "int4a", "fp4"}."""
     if fmt == "nf4":
         from .nf4 import dequant_nf4
 
@@ -42,6 +42,10 @@ def dequant(fmt: str, packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
         from .int4 import dequant_int4
 
         return dequant_int4(packed, scales)
+    if fmt == "int4a":
+        from .int4_asym import dequant_int4_asym
+
+        return dequant_int4_asym(packed, scales)
     if fmt == "fp4":
         from .fp4 import dequant_fp4
 
