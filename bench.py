@@ -33,7 +33,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--fmt", default="nf4_f16",
-                    choices=["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16"])
+                    choices=["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16",
+                             "int4a_f16", "int4a_bf16"])
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -65,7 +66,8 @@ def log(*a):
 
 def algorithmic_bytes(fmt: str, n: int, k: int, b: int) -> int:
     """Bytes the method itself must move for one GEMV: packed weights + scales + x + y."""
-    scale_bytes = n * k // 64 if fmt.startswith("int4") else n * k // 16
+    scale_bytes = {"nf4": n * k // 16, "fp4": n * k // 16, "int4": n * k // 64,
+                   "int4a": n * k // 32}[fmt.split("_")[0]]
     return n * k // 2 + scale_bytes + 2 * b * k + 4 * b * n
 
 
@@ -179,7 +181,7 @@ class Step:
 
 
 def _gemv_name(fmt, b, iters, threads, grouped):
-    fmt_i = {"nf4": 0, "int4": 1, "fp4": 2}[fmt.split("_")[0]]
+    fmt_i = {"nf4": 0, "int4": 1, "fp4": 2, "int4a": 3}[fmt.split("_")[0]]
     xt = 0 if fmt.endswith("_f16") else 1
     return f"gemv_kernel<{fmt_i}, {xt}, {b}, {iters}, {threads}, {'true' if grouped else 'false'}>"
 
@@ -480,7 +482,8 @@ def cpu_baseline(fmt, b, seconds):
     mats = []
     for name, n, k, seed in sample:
         w = synth_inputs.weights(n, k, seed=seed)
-        q = {"nf4": oracle.quantize_nf4, "int4": oracle.quantize_int4, "fp4": oracle.quantize_fp4}[wf](w)
+        q = {"nf4": oracle.quantize_nf4, "int4": oracle.quantize_int4, "fp4": oracle.quantize_fp4,
+             "int4a": oracle.quantize_int4_asym}[wf](w)
         mats.append((q, synth_inputs.activations(b, k, xd, seed=7)))
     sample_weights = sum(n * k for _, n, k, _ in sample)
     t0 = time.perf_counter()
@@ -520,7 +523,7 @@ def time_shape(fmt, n, k, b, path, split_k, dev, min_bytes=600 << 20, reps=5):
 
     import bit_weight_only_w4_amd as w4
 
-    wb = n * k // 2 + (n * k // 64 if fmt.startswith("int4") else n * k // 16)
+    wb = algorithmic_bytes(fmt, n, k, 0)
     copies = max(1, min(4096, -(-min_bytes // wb)))
     xdt = torch.float16 if fmt.endswith("_f16") else torch.bfloat16
     gen = torch.Generator(device=dev).manual_seed(n * 31 + k)
@@ -1005,7 +1008,7 @@ def main():
         "config": {
             "workload": (f"Qwen2.5-1.5B decode step: 197 distinct GEMVs (28x q,k,v,o,gate,"
                          f"up,down + lm_head) in {len(units)} launches, {wfmt} "
-                         f"{ {'NF4': 'bs64 fp32 absmax', 'INT4': 'g128 bf16 scale', 'FP4': 'E2M1 bs64 fp32 absmax/6'}[wfmt]}, "
+                         f"{ {'NF4': 'bs64 fp32 absmax', 'INT4': 'g128 bf16 scale', 'FP4': 'E2M1 bs64 fp32 absmax/6', 'INT4A': 'asymmetric g128 bf16 scale + zero point'}[wfmt]}, "
                          f"{args.fmt.split('_')[1]} x, batch {args.batch}, fp32 accumulate/output"),
             "format": args.fmt,
             "batch": args.batch,

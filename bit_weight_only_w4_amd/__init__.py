@@ -16,7 +16,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4.so")
 
-FORMATS = {"nf4_f16": 1, "nf4_bf16": 2, "int4_f16": 3, "int4_bf16": 4, "fp4_f16": 5, "fp4_bf16": 6}
+FORMATS = {"nf4_f16": 1, "nf4_bf16": 2, "int4_f16": 3, "int4_bf16": 4, "fp4_f16": 5, "fp4_bf16": 6,
+           "int4a_f16": 7, "int4a_bf16": 8}
 PATHS = {"auto": 0, "gemv": 1, "splitk": 2, "mfma": 3, "twopass": 4, "tiled": 5}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 STATUS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "FORMAT", -5: "NONFINITE",
@@ -52,6 +53,7 @@ def lib() -> ctypes.CDLL:
         L.w4_quantize_nf4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.w4_quantize_int4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.w4_quantize_fp4.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.w4_quantize_int4_asym.argtypes = [vp, i64, i64, vp, vp, vp]
         L.w4_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_smallbatch.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_prefill.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
@@ -71,9 +73,9 @@ def lib() -> ctypes.CDLL:
         L.w4_gemv_grouped_plan.argtypes = [ci, ci, ctypes.POINTER(i64), i64, i64, ip, ip, ip, ip, ip]
         L.w4_probe_read.argtypes = [vp, sz, vp, vp]
         L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
-        for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_quantize_fp4", "w4_gemv",
-                     "w4_gemm_smallbatch",
-                     "w4_matmul_ex", "w4_auto_path", "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
+        for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_quantize_fp4", "w4_quantize_int4_asym",
+                     "w4_gemv", "w4_gemm_smallbatch", "w4_matmul_ex", "w4_auto_path",
+                     "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
                      "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped",
                      "w4_gemm_prefill"):
             getattr(L, name).restype = ci
@@ -171,8 +173,24 @@ def quantize_int4(w, stream=None):
     return packed, scale
 
 
+def quantize_int4_asym(w, stream=None):
+    """fp32 [N, K] device weights -> (packed uint8 [N, K/2], words int32 [N, K/128]) in asymmetric
+    INT4: each word holds the group's bf16 scale bits (bits 0-15) and zero point (bits 16-19)."""
+    import torch
+
+    _need_cuda(w)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    words = torch.empty((n, max(k // 128, 1)), dtype=torch.int32, device=w.device)
+    check(lib().w4_quantize_int4_asym(_ptr(w), n, k, _ptr(packed), _ptr(words), _stream(stream)),
+          "w4_quantize_int4_asym")
+    return packed, words
+
+
 def weight_format(fmt: str) -> str:
-    """"nf4", "int4" or "fp4": the weight encoding of a format name such as "fp4_bf16"."""
+    """"nf4", "int4", "int4a" or "fp4": the weight encoding of a format name such as "fp4_bf16"."""
     if fmt not in FORMATS:
         raise ValueError(f"unknown format {fmt!r}")
     return fmt.split("_")[0]
@@ -181,7 +199,8 @@ def weight_format(fmt: str) -> str:
 def quantize(fmt: str, w, stream=None):
     """Quantize fp32 [N, K] device weights in the weight encoding of `fmt` (activation type aside):
     the packed nibbles and the scales that the matmul entry points take for that format."""
-    q = {"nf4": quantize_nf4, "int4": quantize_int4, "fp4": quantize_fp4}[weight_format(fmt)]
+    q = {"nf4": quantize_nf4, "int4": quantize_int4, "int4a": quantize_int4_asym,
+         "fp4": quantize_fp4}[weight_format(fmt)]
     return q(w, stream)
 
 

@@ -37,7 +37,8 @@ const CodebookInit g_codebook;
 
 bool valid_fmt(int fmt) {
   return fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_BF16 || fmt == W4_INT4_X_F16 ||
-         fmt == W4_INT4_X_BF16 || fmt == W4_FP4_X_F16 || fmt == W4_FP4_X_BF16;
+         fmt == W4_INT4_X_BF16 || fmt == W4_FP4_X_F16 || fmt == W4_FP4_X_BF16 ||
+         fmt == W4_INT4A_X_F16 || fmt == W4_INT4A_X_BF16;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -377,6 +378,23 @@ int w4_quantize_fp4(const float* w, int64_t n, int64_t k, uint8_t* packed, float
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
   if (launch_quantize_fp4(w, n, k, packed, scale, s) != hipSuccess) return W4_ERR_HIP;
+  int flag = 0;
+  if (quantize_error_read(&flag, s) != hipSuccess) return W4_ERR_HIP;
+  return flag ? W4_ERR_NONFINITE : W4_OK;
+}
+
+int w4_quantize_int4_asym(const float* w, int64_t n, int64_t k, uint8_t* packed, uint32_t* words,
+                          void* stream) {
+  if (!w || !packed || !words) return W4_ERR_NULL;
+  if (n < 1 || k < 128 || k % 128 != 0 || n >= kMaxDim || k >= kMaxDim) return W4_ERR_SHAPE;
+  if (!aligned(w, 8) || !aligned(packed, 16) || !aligned(words, 4)) return W4_ERR_ALIGN;
+  if (overlaps(w, (size_t)(n * k) * 4, packed, (size_t)(n * k / 2)) ||
+      overlaps(w, (size_t)(n * k) * 4, words, (size_t)(n * k / 128) * 4) ||
+      overlaps(packed, (size_t)(n * k / 2), words, (size_t)(n * k / 128) * 4))
+    return W4_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
+  if (launch_quantize_int4_asym(w, n, k, packed, words, s) != hipSuccess) return W4_ERR_HIP;
   int flag = 0;
   if (quantize_error_read(&flag, s) != hipSuccess) return W4_ERR_HIP;
   return flag ? W4_ERR_NONFINITE : W4_OK;

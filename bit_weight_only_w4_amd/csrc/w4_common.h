@@ -80,19 +80,29 @@ __device__ inline uint32_t buffer_load16bit(__amdgpu_buffer_rsrc_t r, uint32_t o
 }
 
 // Weight formats.  NF4 and FP4 share the layout (blocks of 64, fp32 scale) and differ only in the
-// 16-entry table; INT4 has groups of 128 with a bf16 scale.
-enum Fmt { kNF4 = 0, kINT4 = 1, kFP4 = 2 };
+// 16-entry table; INT4 has groups of 128 with a bf16 scale; asymmetric INT4 (INT4A) has the same
+// groups with a 32-bit word per group (bf16 scale in bits 0-15, zero point z in bits 16-19).
+// INT4A decodes through INT4's table (codes q - 8), and the kernels subtract (z - 8) * s * sum(x)
+// per group: (q - z) s = (q - 8) s - (z - 8) s.
+enum Fmt { kNF4 = 0, kINT4 = 1, kFP4 = 2, kINT4A = 3 };
 enum XType { kF16 = 0, kBF16 = 1 };
 
+// Formats with groups of 128 along K and a bf16 scale.
+__host__ __device__ constexpr bool is_g128(int f) { return f == kINT4 || f == kINT4A; }
+
 inline int fmt_weight(int fmt) {
-  return (fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_BF16)   ? kNF4
-         : (fmt == W4_FP4_X_F16 || fmt == W4_FP4_X_BF16) ? kFP4
-                                                         : kINT4;
+  return (fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_BF16)       ? kNF4
+         : (fmt == W4_FP4_X_F16 || fmt == W4_FP4_X_BF16)     ? kFP4
+         : (fmt == W4_INT4A_X_F16 || fmt == W4_INT4A_X_BF16) ? kINT4A
+                                                             : kINT4;
 }
 inline int fmt_xtype(int fmt) {
-  return (fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16 || fmt == W4_FP4_X_F16) ? kF16 : kBF16;
+  return (fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16 || fmt == W4_FP4_X_F16 ||
+          fmt == W4_INT4A_X_F16)
+             ? kF16
+             : kBF16;
 }
-inline int64_t fmt_group(int fmt) { return fmt_weight(fmt) == kINT4 ? 128 : 64; }
+inline int64_t fmt_group(int fmt) { return is_g128(fmt_weight(fmt)) ? 128 : 64; }
 inline size_t fmt_scale_bytes(int fmt) { return fmt_weight(fmt) == kINT4 ? 2 : 4; }
 
 // Shape of one fused-GEMV launch (host-chosen; see plan_gemv in w4_api.cpp).
@@ -113,7 +123,7 @@ constexpr int kMaxGroup = W4_MAX_GROUP;
 
 struct GemvMember {
   const uint8_t* packed;  // [N_g, K/2]
-  const void* scales;     // NF4 float[N_g, K/64] | INT4 uint16[N_g, K/128]
+  const void* scales;     // NF4, FP4 float[N_g, K/64] | INT4 uint16[N_g, K/128] | INT4A uint32
   float* out;             // y [B, N_g] (splits == 1) or partials [splits, B, N_g]
   uint32_t n;             // rows N_g
   uint32_t nrb;           // row blocks of this member = ceil(N_g / rows per workgroup)
@@ -157,6 +167,8 @@ hipError_t launch_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* pa
                                float* absmax, hipStream_t s);
 hipError_t launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* packed,
                                 uint16_t* scale, hipStream_t s);
+hipError_t launch_quantize_int4_asym(const float* w, int64_t n, int64_t k, uint8_t* packed,
+                                     uint32_t* words, hipStream_t s);
 hipError_t launch_quantize_fp4(const float* w, int64_t n, int64_t k, uint8_t* packed, float* scale,
                                hipStream_t s);
 hipError_t quantize_error_reset(hipStream_t s);

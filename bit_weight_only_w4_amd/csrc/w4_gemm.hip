@@ -18,7 +18,8 @@
 //     [8 g, 8 g + 8) of the row's 32-byte block, one 8-byte load per row tile, decoded pairwise
 //     through the byte -> pair table in LDS.  Both steps lie inside one scale block, so the block
 //     scale is applied exactly, in fp32, to the block's fresh partial sums: acc += scale * D.
-//     INT4 groups of 128 are two such blocks under one scale.
+//     INT4 groups of 128 are two such blocks under one scale.  Asymmetric INT4 decodes q - 8 as
+//     INT4 and adds one MFMA per step whose A rows hold -(z - 8): D becomes the sum of (q - z) x.
 //   * B operand (32 k x 16 activation rows): lane l = 16 g + r takes activation row r of the
 //     column tile and the same 8 k positions, one ds_read_b128 from the x stage in LDS.
 //   * x stages: the tile's TM activation rows x 64 k (128 bytes per row, padded to 144 so that
@@ -39,7 +40,7 @@ namespace w4 {
 struct GemmArgs {
   const uint16_t* x;      // [M, K] activations (bits)
   const uint8_t* packed;  // [N, K/2]
-  const void* scales;     // NF4 float[N, K/64] | INT4 uint16[N, K/128]
+  const void* scales;     // NF4, FP4 float[N, K/64] | INT4 uint16 / INT4A uint32 [N, K/128]
   float* y;               // [M, N]
   uint32_t m, n, k;
   uint32_t mt;            // activation-row tiles (TM rows each)
@@ -68,7 +69,7 @@ template <int FMT, int XT, int WN, int WM, int KW>
 __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a) {
   constexpr int TN = 32 * WN, TM = 32 * WM;
   constexpr bool kSplit = FMT == kNF4 && XT == kBF16;
-  constexpr int SB = FMT != kINT4 ? 4 : 2;  // bytes per scale
+  constexpr int SB = FMT == kINT4 ? 2 : 4;  // bytes per scale (INT4A: its 32-bit word)
   // LDS: the decode table (static, at address 0, so a lookup address needs no base), then the two
   // x stages of each K group (dynamic), reused at the end for the K groups' sums.
   __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
@@ -95,7 +96,7 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   const uint32_t kbase = (uint32_t)kg * steps;
   const uint32_t cnt = kbase < nb ? min(steps, nb - kbase) : 0u;
   const uint32_t pitch = k >> 1;     // packed bytes per weight row
-  const uint32_t spitch = (k / (FMT != kINT4 ? 64 : 128)) * SB;
+  const uint32_t spitch = (k / (is_g128(FMT) ? 128 : 64)) * SB;
 
   // Buffer resources: this wave's WN * 16 weight rows (rows past N read as zero), and the
   // workgroup's TM activation rows (rows past M read as zero).
@@ -124,8 +125,10 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
 #pragma unroll
     for (int t = 0; t < WN; ++t) {
       const uint32_t row = soff + (uint32_t)t * 16u * spitch;
-      if constexpr (FMT != kINT4) {
+      if constexpr (!is_g128(FMT)) {
         d.s[t] = buffer_load32(rs, offset_or_oob(have, row + kb * 4u));
+      } else if constexpr (FMT == kINT4A) {
+        d.s[t] = buffer_load32(rs, offset_or_oob(have, row + (kb >> 1) * 4u));
       } else {
         d.s[t] = buffer_load16bit(rs, offset_or_oob(have, row + (kb >> 1) * 2u));
       }
@@ -195,6 +198,16 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
 #pragma unroll
     for (int t = 0; t < WN; ++t) {
       float4_t dd[WM];
+      // INT4A: A operand whose row r is -(z_r - 8) everywhere (the word of row r sits in lane
+      // 16 (r >> 2) + (r & 3)); its product adds -(z - 8) * sum(x) to D: codes q - 8 become q - z.
+      uint4 zrow = make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (FMT == kINT4A) {
+        const uint32_t word = (uint32_t)__shfl((int)d.s[t], 16 * (r >> 2) + (r & 3));
+        const float zn = (float)(8 - (int)((word >> 16) & 15u));
+        const uint32_t h = XT == kF16 ? f16_bits(zn) : (__float_as_uint(zn) >> 16);
+        const uint32_t hh = h | (h << 16);
+        zrow = make_uint4(hh, hh, hh, hh);
+      }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         uint32_t p1[4], p2[4];
@@ -217,9 +230,10 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
         for (int j = 0; j < WM; ++j) {
           dd[j] = mfma<XT>(a1, bf[s][j], s == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : dd[j]);
           if (kSplit) dd[j] = mfma<XT>(make_uint4(p2[0], p2[1], p2[2], p2[3]), bf[s][j], dd[j]);
+          if (FMT == kINT4A) dd[j] = mfma<XT>(zrow, bf[s][j], dd[j]);
         }
       }
-      const uint32_t sraw = FMT != kINT4 ? d.s[t] : d.s[t] << 16;
+      const uint32_t sraw = !is_g128(FMT) ? d.s[t] : d.s[t] << 16;
       const float sc[4] = {row_bcast<0>(sraw), row_bcast<1>(sraw), row_bcast<2>(sraw),
                            row_bcast<3>(sraw)};
 #pragma unroll
@@ -364,6 +378,8 @@ hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const 
     case W4_INT4_X_BF16: return launch_fx<kINT4, kBF16>(a, wn, wm, kw, s);
     case W4_FP4_X_F16: return launch_fx<kFP4, kF16>(a, wn, wm, kw, s);
     case W4_FP4_X_BF16: return launch_fx<kFP4, kBF16>(a, wn, wm, kw, s);
+    case W4_INT4A_X_F16: return launch_fx<kINT4A, kF16>(a, wn, wm, kw, s);
+    case W4_INT4A_X_BF16: return launch_fx<kINT4A, kBF16>(a, wn, wm, kw, s);
   }
   return hipErrorInvalidValue;
 }

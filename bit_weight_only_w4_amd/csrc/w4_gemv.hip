@@ -27,6 +27,14 @@ hipError_t launch_gemv_fp4_f16_grouped(int b, const GemvArgs& a, int groups, con
                                        hipStream_t s);
 hipError_t launch_gemv_fp4_bf16_grouped(int b, const GemvArgs& a, int groups, const GemvPlan& p,
                                         hipStream_t s);
+hipError_t launch_gemv_int4a_f16(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                 hipStream_t s);
+hipError_t launch_gemv_int4a_bf16(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                  hipStream_t s);
+hipError_t launch_gemv_int4a_f16_grouped(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                         hipStream_t s);
+hipError_t launch_gemv_int4a_bf16_grouped(int b, const GemvArgs& a, int groups, const GemvPlan& p,
+                                          hipStream_t s);
 
 namespace {
 
@@ -54,6 +62,8 @@ hipError_t launch_gemv(int fmt, int b, const GemvArgs& a, int groups, const Gemv
       case W4_INT4_X_BF16: return launch_gemv_int4_bf16_grouped(b, a, groups, p, s);
       case W4_FP4_X_F16: return launch_gemv_fp4_f16_grouped(b, a, groups, p, s);
       case W4_FP4_X_BF16: return launch_gemv_fp4_bf16_grouped(b, a, groups, p, s);
+      case W4_INT4A_X_F16: return launch_gemv_int4a_f16_grouped(b, a, groups, p, s);
+      case W4_INT4A_X_BF16: return launch_gemv_int4a_bf16_grouped(b, a, groups, p, s);
     }
     return hipErrorInvalidValue;
   }
@@ -64,6 +74,8 @@ hipError_t launch_gemv(int fmt, int b, const GemvArgs& a, int groups, const Gemv
     case W4_INT4_X_BF16: return launch_gemv_int4_bf16(b, a, groups, p, s);
     case W4_FP4_X_F16: return launch_gemv_fp4_f16(b, a, groups, p, s);
     case W4_FP4_X_BF16: return launch_gemv_fp4_bf16(b, a, groups, p, s);
+    case W4_INT4A_X_F16: return launch_gemv_int4a_f16(b, a, groups, p, s);
+    case W4_INT4A_X_BF16: return launch_gemv_int4a_bf16(b, a, groups, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -25,7 +25,10 @@
 //   * Multiply: v_dot2_f32_f16 / v_dot2_f32_bf16 of the decoded pair with the activation pair
 //     into fp32 (products of two 16-bit values are exact in fp32), then one fp32 FMA per chunk with
 //     the block scale.  NF4 with bf16 activations splits each code into two bf16 terms (8-byte
-//     entries, 32 copies): a single bf16 code is not accurate enough.
+//     entries, 32 copies): a single bf16 code is not accurate enough.  Asymmetric INT4 decodes
+//     q - 8 through INT4's table and subtracts (z - 8) * sum(x) per chunk before the scale FMA:
+//     the lane's activation sums are fixed for the launch, so the zero point costs one FMA per
+//     chunk.
 //   * Reduction over a team: DPP within 16 lanes, cross-row shuffles up to 64, and an LDS exchange
 //     between the waves of a team wider than one wave.
 #pragma once
@@ -135,18 +138,23 @@ __device__ inline float team_sum_wave(float v, int team) {
 }
 
 // Bytes of one row's scales, and the byte offset of chunk `chunk`'s scale within the row.
+// INT4A keeps its 32-bit word (bf16 scale | zero point << 16) in the float slot, decoded when used.
 template <int FMT>
 __device__ inline uint32_t scale_pitch(int64_t k) {
-  return FMT != kINT4 ? (uint32_t)(k >> 6) * 4u : (uint32_t)(k >> 7) * 2u;
+  return FMT == kINT4A ? (uint32_t)(k >> 7) * 4u
+         : FMT == kINT4 ? (uint32_t)(k >> 7) * 2u
+                        : (uint32_t)(k >> 6) * 4u;
 }
 template <int FMT>
 __device__ inline uint32_t scale_offset(int chunk) {
-  return FMT != kINT4 ? (uint32_t)(chunk >> 1) * 4u : (uint32_t)(chunk >> 2) * 2u;
+  return FMT == kINT4A ? (uint32_t)(chunk >> 2) * 4u
+         : FMT == kINT4 ? (uint32_t)(chunk >> 2) * 2u
+                        : (uint32_t)(chunk >> 1) * 4u;
 }
 template <int FMT>
 __device__ inline float load_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if (FMT != kINT4) return __uint_as_float(buffer_load32(r, off));
-  return __uint_as_float(buffer_load16bit(r, off) << 16);  // bf16 bits -> fp32, exact
+  if (FMT == kINT4) return __uint_as_float(buffer_load16bit(r, off) << 16);  // bf16 -> fp32, exact
+  return __uint_as_float(buffer_load32(r, off));
 }
 
 template <int FMT, int XT, int B, int ITM, int NT, bool GROUPED>
@@ -264,6 +272,31 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   fill_table<FMT, XT, NT>(tab);
   __syncthreads();
 
+  // INT4A: the sum of each chunk's 32 activations (per batch row), for the zero-point term
+  // -(z - 8) * s * sum(x) of every row this lane meets; computed once per launch.
+  float xsum[FMT == kINT4A ? ITM : 1][B];
+  if constexpr (FMT == kINT4A) {
+    constexpr uint32_t kOnes = XT == kF16 ? 0x3C003C00u : 0x3F803F80u;
+#pragma unroll
+    for (int i = 0; i < ITM; ++i) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float t = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          if (XT == kF16) {
+            t = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, xr[i][b][m]),
+                                       __builtin_bit_cast(half2_t, kOnes), t, false);
+          } else {
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, xr[i][b][m]),
+                                                __builtin_bit_cast(bf162_t, kOnes), t, false);
+          }
+        }
+        xsum[i][b] = t;
+      }
+    }
+  }
+
   constexpr bool kSplitCode = (FMT == kNF4 && XT == kBF16);
   const uint32_t laneoff = kSplitCode ? (uint32_t)(lane & 31) * 8u : (uint32_t)lane * 4u;
   const char* tabc = reinterpret_cast<const char*>(tab);
@@ -314,8 +347,17 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
             }
           }
         }
+        if constexpr (FMT == kINT4A) {
+          // (q - z) s = (q - 8) s - (z - 8) s: the decoded codes were q - 8
+          const uint32_t word = __float_as_uint(sc[i]);
+          const float s = __uint_as_float(word << 16);
+          const float zc = (float)((int)((word >> 16) & 15u) - 8);
 #pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(d[b], sc[i], acc[b]);
+          for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(__builtin_fmaf(-zc, xsum[i][b], d[b]), s, acc[b]);
+        } else {
+#pragma unroll
+          for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(d[b], sc[i], acc[b]);
+        }
       }
     }
 

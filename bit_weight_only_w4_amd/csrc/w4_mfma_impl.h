@@ -30,7 +30,8 @@
 //   * K groups end by adding their results in LDS in the fixed order kg = 0, 1, ..., KW - 1, so the
 //     output is bitwise reproducible.
 //   * NF4 x bf16 uses the two-term bf16 split of each code (two MFMAs per step); INT4 codes q - 8
-//     are exact in both 16-bit types.
+//     are exact in both 16-bit types.  Asymmetric INT4 decodes q - 8 the same way and adds one
+//     MFMA per step whose A rows hold -(z - 8), which makes D the block's sum of (q - z) x.
 #pragma once
 #include <string.h>
 
@@ -44,7 +45,7 @@ namespace w4 {
 // numbered one after another, member g owning tiles [tile0, tile0 + its tiles).
 struct MfmaMember {
   const uint8_t* packed;  // [N_g, K/2]
-  const void* scales;     // NF4 float[N_g, K/64] | INT4 uint16[N_g, K/128]
+  const void* scales;     // NF4, FP4 float[N_g, K/64] | INT4 uint16 / INT4A uint32 [N_g, K/128]
   float* y;               // [B, N_g]
   uint32_t n;             // N_g
   uint32_t tile0;
@@ -88,9 +89,9 @@ constexpr int kMaxTiles = 8;        // up to 128 activation rows per launch
 //   for L >= 2, i.e. the 16 weights from 32 (L & 1) + 16 (L >> 1) of each block.
 template <int FMT>
 struct Quad {
-  static constexpr int QC = FMT != kINT4 ? 4 : 2;  // scale blocks per quad
+  static constexpr int QC = is_g128(FMT) ? 2 : 4;  // scale blocks per quad
   uint32_t w[2][4];
-  uint32_t s[QC];  // fp32 bits (INT4: bf16 bits in the low half)
+  uint32_t s[QC];  // fp32 bits (INT4: bf16 bits in the low half; INT4A: its word)
 };
 
 // Waves per SIMD the kernel is compiled for: four (two workgroups per CU, <= 128 VGPRs) for one
@@ -100,10 +101,10 @@ constexpr int min_waves(int t) { return t == 1 ? 4 : 2; }
 template <int FMT, int XT, int T, int KW, bool GROUPED>
 __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a) {
   constexpr int RW = 8 / KW;
-  constexpr int KC = FMT != kINT4 ? 64 : 128;  // weights per scale block
+  constexpr int KC = is_g128(FMT) ? 128 : 64;  // weights per scale block
   constexpr int QC = kQuad / KC;              // blocks per quad
   constexpr int STEPS = KC / 32;              // MFMA steps per block
-  constexpr int SB = FMT != kINT4 ? 4 : 2;     // bytes per scale
+  constexpr int SB = FMT == kINT4 ? 2 : 4;     // bytes per scale
   constexpr bool kSplit = (FMT == kNF4 && XT == kBF16);
   // LDS: the decode table (static, at address 0, so a lookup address needs no base), then the
   // dynamic part: the K-group reduction area and the x window.
@@ -198,7 +199,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
     // multiplied (inside the matrix their bytes are the next row's; zeroing them here would make
     // the loop wait for the load).  INT4: two bf16 scales, 2-byte aligned, two loads, moved to the
     // high half when multiplied (for the same reason).
-    if constexpr (FMT != kINT4) {
+    if constexpr (!is_g128(FMT)) {
       const uint4 sv = buffer_load16(cur.rs, offset_or_oob(qb < nblocks, sbase));
       d.s[0] = sv.x;
       d.s[1] = sv.y;
@@ -208,7 +209,8 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
         const bool have = qb + c < nblocks;
-        d.s[c] = buffer_load16bit(cur.rs, offset_or_oob(have, sbase) + (uint32_t)(c * SB));
+        const uint32_t off = offset_or_oob(have, sbase) + (uint32_t)(c * SB);
+        d.s[c] = FMT == kINT4A ? buffer_load32(cur.rs, off) : buffer_load16bit(cur.rs, off);
       }
     }
   };
@@ -281,7 +283,9 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   const uint8_t* xw = xs + (uint32_t)kg * (seg * 16u);  // this K group's part of the window
 
   // k offset (in the block) of the first of this lane's weights for MFMA step 0 (see Quad).
-  const int klane = FMT != kINT4 ? 32 * (g & 1) + 16 * (g >> 1) : 32 * g;
+  const int klane = !is_g128(FMT) ? 32 * (g & 1) + 16 * (g >> 1) : 32 * g;
+  // INT4A: the lane holding the scale word of A row m (scale words sit with D rows 4 g + (m & 3)).
+  const int zsrc = 16 * (m >> 2) + (m & 3);
 
   // Multiply the quad held in d: quad q of the K group, wq = its index inside the current window.
   auto compute = [&](int q, int wq, const Quad<FMT>& d) __attribute__((always_inline)) {
@@ -296,7 +300,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
       wh[1][i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0x128, 0xF, 0xF, false);  // row_ror:8
     }
     uint32_t wb[QC][STEPS];
-    if constexpr (FMT != kINT4) {
+    if constexpr (!is_g128(FMT)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const auto s0 = __builtin_amdgcn_permlane32_swap(wh[h][0], wh[h][2], false, false);
@@ -327,6 +331,16 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
       float4_t dd[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) dd[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+      // INT4A: A operand whose row m is -(z_m - 8) everywhere; its product with the block's x adds
+      // -(z - 8) * sum(x) to D, turning the decoded codes q - 8 into q - z.
+      uint4 zrow = make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (FMT == kINT4A) {
+        const uint32_t word = (uint32_t)__shfl((int)d.s[c], zsrc);
+        const float zn = (float)(8 - (int)((word >> 16) & 15u));
+        const uint32_t h = XT == kF16 ? f16_bits(zn) : (__float_as_uint(zn) >> 16);
+        const uint32_t hh = h | (h << 16);
+        zrow = make_uint4(hh, hh, hh, hh);
+      }
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
         uint32_t p1[4], p2[4];
@@ -350,12 +364,13 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
           const uint4 bv = *reinterpret_cast<const uint4*>(xq + xrowoff[t] + (c * KC + s * 8) * 2);
           dd[t] = mfma<XT>(a1, bv, dd[t]);
           if (kSplit) dd[t] = mfma<XT>(make_uint4(p2[0], p2[1], p2[2], p2[3]), bv, dd[t]);
+          if (FMT == kINT4A) dd[t] = mfma<XT>(zrow, bv, dd[t]);
         }
         // With 8 tiles, keep each step's B fragments from being fetched ahead of the previous
         // step (they would not fit the registers left by the accumulators).
         if constexpr (T == 8) __builtin_amdgcn_sched_barrier(0);
       }
-      const uint32_t sraw = FMT != kINT4 ? ((c > 0 && qb + c >= nblocks) ? 0u : d.s[c]) : d.s[c] << 16;
+      const uint32_t sraw = !is_g128(FMT) ? ((c > 0 && qb + c >= nblocks) ? 0u : d.s[c]) : d.s[c] << 16;
       const float sc[4] = {row_bcast<0>(sraw), row_bcast<1>(sraw), row_bcast<2>(sraw),
                            row_bcast<3>(sraw)};
 #pragma unroll
@@ -528,6 +543,8 @@ hipError_t dispatch(int op, int fmt, const MfmaArgs& a, int tiles, int kw, int l
     case W4_INT4_X_BF16: return dispatch_fx<kINT4, kBF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
     case W4_FP4_X_F16: return dispatch_fx<kFP4, kF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
     case W4_FP4_X_BF16: return dispatch_fx<kFP4, kBF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
+    case W4_INT4A_X_F16: return dispatch_fx<kINT4A, kF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
+    case W4_INT4A_X_BF16: return dispatch_fx<kINT4A, kBF16, GROUPED>(op, a, tiles, kw, lds, grid, slices, out, s);
   }
   return hipErrorInvalidValue;
 }

@@ -12,6 +12,12 @@
 // -8, 7) against the rounded s, nibble = q + 8.  fp32(A / 7) is taken as the fp64 quotient rounded
 // to fp32, which equals the correctly rounded fp32 quotient (53 >= 2 * 24 + 2).
 //
+// Asymmetric INT4 (LLM Compressor 0.14, "The fused kernel": divide by the scale, add the zero
+// point, clamp, round; "Details worth knowing": rint): groups of 128, lo = min(min w, 0),
+// hi = max(max w, 0), s = bf16_RNE(fp32(fp32(hi - lo) / 15)), z = clamp(rint(-lo / s), 0, 15),
+// q = rint(clamp(w / s + z, 0, 15)), quotients in fp64 against the rounded s; the group's word is
+// the bf16 bits of s | z << 16.
+//
 // FP4 (LLM Compressor 0.14, "Details worth knowing": a ladder of thresholds onto the magnitudes
 // {0, 0.5, 1, 1.5, 2, 3, 4, 6}, alternating <= and < so that ties go to the even code): blocks of
 // 64, s = fp32(A / 6) (the fp64 quotient rounded to fp32, as for INT4), magnitude index = the
@@ -20,7 +26,8 @@
 //
 // One lane handles one pair of weights (one output byte): element 2i goes to the high nibble.
 // Absmax is an integer max over |bits| (the order of non-negative floats), reduced across the 32
-// lanes of an NF4 block or the 64 lanes of an INT4 group with cross-lane shuffles.
+// lanes of an NF4 block or the 64 lanes of an INT4 group with cross-lane shuffles (asymmetric
+// INT4: fp32 min and max the same way).
 #include "w4_common.h"
 
 namespace w4 {
@@ -107,6 +114,45 @@ __global__ void __launch_bounds__(256) quant_int4_kernel(const float* __restrict
   }
 }
 
+__global__ void __launch_bounds__(256) quant_int4_asym_kernel(const float* __restrict__ w,
+                                                               int64_t pairs,
+                                                               uint8_t* __restrict__ packed,
+                                                               uint32_t* __restrict__ words) {
+  const int64_t p = blockIdx.x * 256ll + threadIdx.x;
+  const bool valid = p < pairs;  // pairs is a multiple of 64: a whole group is valid or not
+  const float2 v = reinterpret_cast<const float2*>(w)[valid ? p : 0];
+  const uint32_t a0 = __float_as_uint(v.x) & 0x7FFFFFFFu;
+  const uint32_t a1 = __float_as_uint(v.y) & 0x7FFFFFFFu;
+  if (valid && (a0 >= 0x7F800000u || a1 >= 0x7F800000u)) g_w4_nonfinite = 1;
+  // the range with 0 in it: lo <= 0 <= hi
+  float lo = fminf(fminf(v.x, v.y), 0.0f), hi = fmaxf(fmaxf(v.x, v.y), 0.0f);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off));
+    hi = fmaxf(hi, __shfl_xor(hi, off));
+  }
+  const float span = hi - lo;  // one IEEE fp32 subtraction
+  const float s32 = (float)((double)span / 15.0);
+  const uint32_t u = __float_as_uint(s32);
+  const uint32_t sb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // bf16, nearest even
+  const double s = (double)__uint_as_float(sb << 16);
+  uint32_t n0 = 0, n1 = 0, z = 0;
+  if (s != 0.0) {
+    double zf = rint(-(double)lo / s);
+    zf = zf < 0.0 ? 0.0 : (zf > 15.0 ? 15.0 : zf);
+    z = (uint32_t)zf;
+    double q0 = (double)v.x / s + zf, q1 = (double)v.y / s + zf;  // divide, add the zero point
+    q0 = rint(q0 < 0.0 ? 0.0 : (q0 > 15.0 ? 15.0 : q0));        // clamp, round
+    q1 = rint(q1 < 0.0 ? 0.0 : (q1 > 15.0 ? 15.0 : q1));
+    n0 = (uint32_t)q0;
+    n1 = (uint32_t)q1;
+  }
+  if (valid) {
+    packed[p] = (uint8_t)((n0 << 4) | n1);
+    if ((threadIdx.x & 63) == 0) words[p >> 6] = sb | (z << 16);
+  }
+}
+
 // FP4 magnitude index of y = |w| / s >= 0: one step past each threshold crossed; a value on
 // 0.25, 1.25, 2.5 or 5 stays below, one on 0.75, 1.75 or 3.5 goes above (the even index).
 __device__ inline uint32_t fp4_magnitude(double y) {
@@ -172,6 +218,15 @@ hipError_t launch_quantize_fp4(const float* w, int64_t n, int64_t k, uint8_t* pa
   const int64_t blocks = (pairs + 255) / 256;
   hipLaunchKernelGGL(quant_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, pairs, packed,
                      scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int4_asym(const float* w, int64_t n, int64_t k, uint8_t* packed,
+                                     uint32_t* words, hipStream_t s) {
+  const int64_t pairs = n * (k / 2);
+  const int64_t blocks = (pairs + 255) / 256;
+  hipLaunchKernelGGL(quant_int4_asym_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, pairs,
+                     packed, words);
   return hipGetLastError();
 }
 

@@ -8,7 +8,8 @@
 // path.
 //
 // The decoded weights are materialized in fp16 for both activation types: for INT4,
-// (q - 8) * s is exact in fp16 whenever it is in fp16 range; for NF4 and FP4, code * scale is
+// (q - 8) * s is exact in fp16 whenever it is in fp16 range; for INT4A, (q - z) * s has up to
+// 12 significant bits and is rounded once to fp16; for NF4 and FP4, code * scale is
 // rounded once to fp16 (relative error <= 2^-11, inside the acceptance bound).  bf16 would not be.
 #include "w4_common.h"
 
@@ -27,7 +28,12 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint4* __restrict__ 
     const int64_t row = c / cpr;
     const int cr = (int)(c - row * cpr);
     float s;
-    if (FMT != kINT4) {
+    int zp = 8;  // the stored nibble's offset: 8 (INT4), the group's zero point (INT4A)
+    if (FMT == kINT4A) {
+      const uint32_t word = reinterpret_cast<const uint32_t*>(scales)[row * (k >> 7) + (cr >> 2)];
+      s = __uint_as_float(word << 16);
+      zp = (int)((word >> 16) & 15u);
+    } else if (!is_g128(FMT)) {
       s = reinterpret_cast<const float*>(scales)[row * (k >> 6) + (cr >> 1)];
     } else {
       s = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(scales)[row * (k >> 7) + (cr >> 2)] << 16);
@@ -49,8 +55,8 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint4* __restrict__ 
           vh = __uint_as_float(c_fp4_code_bits2[hi]) * s;
           vl = __uint_as_float(c_fp4_code_bits2[lo]) * s;
         } else {
-          vh = (float)((int)hi - 8) * s;
-          vl = (float)((int)lo - 8) * s;
+          vh = (float)((int)hi - zp) * s;
+          vl = (float)((int)lo - zp) * s;
         }
         const uint32_t h16 = __builtin_bit_cast(uint16_t, (_Float16)vh);
         const uint32_t l16 = __builtin_bit_cast(uint16_t, (_Float16)vl);
@@ -133,6 +139,10 @@ hipError_t launch_dequant_f16(int fmt, const uint8_t* packed, const void* scales
                        reinterpret_cast<uint4*>(w_hat));
   } else if (fmt_weight(fmt) == kNF4) {
     hipLaunchKernelGGL(dequant_kernel<kNF4>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const uint4*>(packed), scales, chunks, cpr, k,
+                       reinterpret_cast<uint4*>(w_hat));
+  } else if (fmt_weight(fmt) == kINT4A) {
+    hipLaunchKernelGGL(dequant_kernel<kINT4A>, dim3((unsigned)blocks), dim3(256), 0, s,
                        reinterpret_cast<const uint4*>(packed), scales, chunks, cpr, k,
                        reinterpret_cast<uint4*>(w_hat));
   } else {

@@ -40,20 +40,27 @@ extern "C" {
  *   FP4 : E2M1 codes through a 16-entry table (nibble bit 3 = sign, bits 0-2 index the
  *         magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; LLM Compressor 0.14, "Details worth
  *         knowing"), blocks of 64 along K, one fp32 scale absmax / 6 per block,
- *         scales = float[N, K/64]; decoded weight = table[nibble] * scale. */
+ *         scales = float[N, K/64]; decoded weight = table[nibble] * scale.
+ *   INT4A: asymmetric INT4 (LLM Compressor 0.14, "The fused kernel": divide by the scale, add
+ *         the zero point, clamp, round; "What those numbers leave out": INT4 symmetric and
+ *         asymmetric, grouped): nibble = unsigned code q in 0..15, groups of 128 along K,
+ *         scales = uint32[N, K/128] words, bf16 scale bits in bits 0-15 and the zero point z
+ *         (0..15) in bits 16-19, bits 20-31 zero; decoded weight = (q - z) * scale. */
 typedef enum {
   W4_NF4_X_F16 = 1,
   W4_NF4_X_BF16 = 2,
   W4_INT4_X_F16 = 3,
   W4_INT4_X_BF16 = 4,
   W4_FP4_X_F16 = 5,
-  W4_FP4_X_BF16 = 6
+  W4_FP4_X_BF16 = 6,
+  W4_INT4A_X_F16 = 7,
+  W4_INT4A_X_BF16 = 8
 } w4_format_t;
 
 typedef enum {
   W4_OK = 0,
   W4_ERR_NULL = -1,      /* a required pointer is NULL                                        */
-  W4_ERR_SHAPE = -2,     /* N, K or B out of range, or K not a multiple of 64 (NF4, FP4) / 128 (INT4) */
+  W4_ERR_SHAPE = -2,     /* N, K or B out of range, or K not a multiple of 64 (NF4, FP4) / 128 (INT4, INT4A) */
   W4_ERR_ALIGN = -3,     /* packed or x not 16-byte aligned, scales or y not element aligned  */
   W4_ERR_FORMAT = -4,    /* unknown w4_format_t                                               */
   W4_ERR_NONFINITE = -5, /* quantize met a NaN or Inf weight (outputs are then meaningless)   */
@@ -117,6 +124,20 @@ int w4_quantize_nf4(const float* w, int64_t N, int64_t K, uint8_t* packed, float
  * Synchronizes `stream`.  Returns W4_ERR_NONFINITE if any weight is NaN or Inf. */
 int w4_quantize_int4(const float* w, int64_t N, int64_t K, uint8_t* packed, uint16_t* scale_bf16,
                      void* stream);
+
+/* w4_quantize_int4_asym: asymmetric INT4 (LLM Compressor 0.14, "The fused kernel": a code is the
+ * weight divided by the scale, plus the zero point, clamped and rounded; "Details worth knowing":
+ * rint).  Per row and 128-group: lo = min(min w, 0), hi = max(max w, 0);
+ * s = bf16_RNE(fp32(fp32(hi - lo) / 15)); z = clamp(rint(-lo / s), 0, 15);
+ * q = rint(clamp(w / s + z, 0, 15)), the quotients in fp64 against the rounded s; a group whose
+ * s is 0 stores word 0 and nibbles 0.
+ *   w       device float[N, K], read only; 8-byte aligned
+ *   N, K    N >= 1, K >= 128, K % 128 == 0
+ *   packed  device uint8[N, K/2], written; 16-byte aligned; element 2i in the high nibble
+ *   words   device uint32[N, K/128], written: bf16 bits of s | z << 16; 4-byte aligned
+ * Synchronizes `stream`.  Returns W4_ERR_NONFINITE if any weight is NaN or Inf. */
+int w4_quantize_int4_asym(const float* w, int64_t N, int64_t K, uint8_t* packed, uint32_t* words,
+                          void* stream);
 
 /* w4_quantize_fp4: FP4 (E2M1) quantization, blocks of 64 along K (LLM Compressor 0.14: GPTQ's 15x
  * speedup is one fused loop, "Details worth knowing": the ladder of thresholds onto

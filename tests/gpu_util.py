@@ -7,9 +7,8 @@ import numpy as np
 import oracle
 
 WFMT = {"nf4_f16": "nf4", "nf4_bf16": "nf4", "int4_f16": "int4", "int4_bf16": "int4",
-        "fp4_f16": "fp4", "fp4_bf16": "fp4"}
-XDT = {"nf4_f16": "f16", "nf4_bf16": "bf16", "int4_f16": "f16", "int4_bf16": "bf16",
-       "fp4_f16": "f16", "fp4_bf16": "bf16"}
+        "fp4_f16": "fp4", "fp4_bf16": "fp4", "int4a_f16": "int4a", "int4a_bf16": "int4a"}
+XDT = {f: f.split("_")[1] for f in WFMT}
 
 
 def device():
@@ -36,22 +35,19 @@ def to_dev_x(x_bits: np.ndarray, xdt: str):
 def gpu_quantize(fmt: str, w_dev):
     import bit_weight_only_w4_amd as w4
 
-    if WFMT[fmt] == "nf4":
-        return w4.quantize_nf4(w_dev)
-    if WFMT[fmt] == "fp4":
-        return w4.quantize_fp4(w_dev)
-    return w4.quantize_int4(w_dev)
+    return w4.quantize(fmt, w_dev)
 
 
 def scales_to_np(fmt: str, s_dev) -> np.ndarray:
     s = s_dev.cpu().numpy()
+    if WFMT[fmt] == "int4a":
+        return s.view(np.uint32)
     return s if WFMT[fmt] in ("nf4", "fp4") else s.view(np.uint16)
 
 
 def oracle_quantize(fmt: str, w: np.ndarray):
-    if WFMT[fmt] == "fp4":
-        return oracle.quantize_fp4(w)
-    return oracle.quantize_nf4(w) if WFMT[fmt] == "nf4" else oracle.quantize_int4(w)
+    return {"nf4": oracle.quantize_nf4, "int4": oracle.quantize_int4, "fp4": oracle.quantize_fp4,
+            "int4a": oracle.quantize_int4_asym}[WFMT[fmt]](w)
 
 
 def assert_quant_equal(fmt, packed_dev, scales_dev, packed_ref, scales_ref, rows=None):
@@ -62,8 +58,8 @@ def assert_quant_equal(fmt, packed_dev, scales_dev, packed_ref, scales_ref, rows
     assert p.shape == packed_ref.shape
     bad = np.argwhere(p != packed_ref)
     assert bad.size == 0, f"{len(bad)} packed bytes differ, first at {bad[:5].tolist()}"
-    sv = s.view(np.uint32) if s.dtype == np.float32 else s
-    rv = scales_ref.view(np.uint32) if scales_ref.dtype == np.float32 else scales_ref
+    sv = s.view(np.uint32) if s.dtype in (np.float32, np.int32) else s
+    rv = scales_ref.view(np.uint32) if scales_ref.dtype in (np.float32, np.int32) else scales_ref
     bad = np.argwhere(sv != rv)
     assert bad.size == 0, f"{len(bad)} scales differ, first at {bad[:5].tolist()}"
 

@@ -29,7 +29,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for required in ("w4_quantize_nf4", "w4_quantize_int4", "w4_quantize_fp4", "w4_gemv",
+    for required in ("w4_quantize_nf4", "w4_quantize_int4", "w4_quantize_fp4",
+                     "w4_quantize_int4_asym", "w4_gemv",
                      "w4_gemm_smallbatch",
                      "w4_matmul_ex", "w4_workspace_bytes"):
         assert required in names
@@ -68,7 +69,7 @@ def test_host_validation_codes():
     assert _gemv(L, x=0) == -1
     assert _gemv(L, y=0) == -1
     assert _gemv(L, fmt=0) == -4
-    assert _gemv(L, fmt=7) == -4  # 5, 6 are FP4
+    assert _gemv(L, fmt=9) == -4  # 5, 6 are FP4, 7, 8 asymmetric INT4
     assert _gemv(L, n=0) == -2
     assert _gemv(L, k=96) == -2  # NF4 needs K % 64
     assert _gemv(L, fmt=3, k=192) == -2  # INT4 needs K % 128
@@ -93,6 +94,11 @@ def test_host_validation_codes():
     assert L.w4_quantize_fp4(vp(FAKE), 4, 96, vp(FAKE * 8), vp(FAKE * 9), None) == -2  # K % 64
     assert L.w4_quantize_fp4(vp(FAKE), 4, 64, vp(FAKE * 8 + 4), vp(FAKE * 9), None) == -3
     assert _gemv(L, fmt=5, k=96) == -2  # FP4 needs K % 64
+    assert _gemv(L, fmt=7, k=192) == -2  # asymmetric INT4 needs K % 128
+    assert _gemv(L, fmt=8, s=FAKE * 3 + 2) == -3  # its scale words are 4-byte
+    assert L.w4_quantize_int4_asym(None, 4, 128, vp(FAKE), vp(FAKE * 2), None) == -1
+    assert L.w4_quantize_int4_asym(vp(FAKE), 4, 64, vp(FAKE * 8), vp(FAKE * 9), None) == -2
+    assert L.w4_quantize_int4_asym(vp(FAKE), 4, 128, vp(FAKE * 8), vp(FAKE * 9 + 2), None) == -3
     assert _gemv(L, fmt=6, s=FAKE * 3 + 2) == -3  # FP4 scales are fp32
     assert L.w4_probe_read(vp(FAKE), 24, vp(FAKE * 2), None) == -2
 
@@ -173,7 +179,7 @@ def test_grouped_validation_codes():
     assert _grouped(L, n=(64, 0, 32)) == -2
     assert _grouped(L, k=96) == -2
     assert _grouped(L, b=9) == -2
-    assert _grouped(L, fmt=7) == -4
+    assert _grouped(L, fmt=9) == -4
     assert _grouped(L, p=[FAKE * 10, FAKE * 11 + 4, FAKE * 12]) == -3
     # y of member 1 overlaps y of member 0 (64 rows x 4 bytes from FAKE * 30)
     assert _grouped(L, y=[FAKE * 30, FAKE * 30 + 128, FAKE * 32]) == -9
@@ -195,7 +201,7 @@ def test_grouped_smallbatch_validation_codes():
     assert _grouped(L, n=(64, 0, 32), b=32, entry=e) == -2
     assert _grouped(L, k=96, b=32, entry=e) == -2
     assert _grouped(L, b=4097, entry=e) == -2
-    assert _grouped(L, fmt=7, b=32, entry=e) == -4
+    assert _grouped(L, fmt=9, b=32, entry=e) == -4
     assert _grouped(L, y=[FAKE * 30, FAKE * 30 + 128, FAKE * 32], b=1, entry=e) == -9
     # with B = 32 each y_g is 32 rows: y_1 placed inside y_0
     assert _grouped(L, y=[FAKE * 30, FAKE * 30 + 64 * 4 * 8, FAKE * 32], b=32, entry=e) == -9

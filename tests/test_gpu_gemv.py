@@ -12,7 +12,8 @@ from tests import gpu_util as g
 
 pytestmark = pytest.mark.gpu
 
-ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16"]
+ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16", "int4a_f16",
+            "int4a_bf16"]
 
 
 def _case(fmt, n, k, b, seed, sigma=0.02):

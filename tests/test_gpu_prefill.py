@@ -7,7 +7,8 @@ from tests import gpu_util as g
 
 pytestmark = pytest.mark.gpu
 
-ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16"]
+ALL_FMTS = ["nf4_f16", "nf4_bf16", "int4_f16", "int4_bf16", "fp4_f16", "fp4_bf16", "int4a_f16",
+            "int4a_bf16"]
 
 
 def _case(fmt, n, k, b, seed):
@@ -85,7 +86,8 @@ def test_prefill_entry_auto_and_determinism(fmt):
 @pytest.mark.parametrize("fmt,n,k,b", [("nf4_f16", 151936, 1536, 512), ("int4_bf16", 151936, 1536, 512),
                                        ("nf4_bf16", 1536, 8960, 512), ("int4_f16", 28672, 8192, 512),
                                        ("nf4_f16", 8960, 1536, 4096), ("fp4_bf16", 8960, 1536, 512),
-                                       ("fp4_f16", 28672, 8192, 512)])
+                                       ("fp4_f16", 28672, 8192, 512), ("int4a_bf16", 151936, 1536, 512),
+                                       ("int4a_f16", 8960, 1536, 1024)])
 def test_tiled_full_size_sampled(fmt, n, k, b):
     """Full-size prefill matrices at 512 tokens (and 4096, the largest batch): weights drawn on the
     GPU, quantized there, and 160 sampled rows (the first and the last among them) checked

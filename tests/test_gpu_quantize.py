@@ -8,7 +8,7 @@ from tests import gpu_util as g
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["nf4_f16", "int4_f16", "fp4_f16"]
+FMTS = ["nf4_f16", "int4_f16", "fp4_f16", "int4a_f16"]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -23,7 +23,7 @@ def test_quantize_bitexact_gaussian(fmt, n, k, seed):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_quantize_edge_values(fmt):
     """Zero blocks, -0.0, denormals, huge magnitudes, constant blocks, exact ties (NF4, INT4 and
-    FP4 midpoints)."""
+    FP4 midpoints; asymmetric INT4 codes and zero points), one-signed groups."""
     rng = np.random.default_rng(21)
     w = (rng.standard_normal((12, 256)) * 0.02).astype(np.float32)
     w[0] = 0.0
@@ -50,6 +50,13 @@ def test_quantize_edge_values(fmt):
     w[8, 8:15] = [-0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0]
     w[8, 64] = -3.0
     w[8, 65:72] = [0.125, 0.375, 0.625, 0.875, 1.25, 1.75, 2.5]
+    # asymmetric INT4: all-positive and all-negative groups (zero points 0 and 15), and zero-point
+    # ties: ranges [-2.5 s, 12.5 s] and [-3.5 s, 11.5 s] with s = 2^-4
+    w[9, :128] = np.abs(w[9, :128]) + np.float32(0.01)
+    w[9, 128:] = -np.abs(w[9, 128:]) - np.float32(0.01)
+    w[10] = 0.0
+    w[10, 0], w[10, 1], w[10, 2:10] = -2.5 / 16, 12.5 / 16, np.arange(8) / 16 + 1 / 32
+    w[10, 128], w[10, 129], w[10, 130:138] = -3.5 / 16, 11.5 / 16, -np.arange(8) / 16 - 1 / 32
     w = np.ascontiguousarray(w)
     p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
     g.assert_quant_equal(fmt, p, s, *g.oracle_quantize(fmt, w))
