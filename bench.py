@@ -595,7 +595,8 @@ def time_read_probe(nbytes, dev, min_bytes=600 << 20, reps=5):
 
 # Decode steps besides the benchmark line's: (format, batch).
 OTHER_STEPS = [("int4_bf16", 1), ("int4_bf16", 8), ("nf4_f16", 8), ("nf4_bf16", 1), ("int4_f16", 1),
-               ("fp4_f16", 1), ("fp4_bf16", 1), ("fp4_f16", 8)]
+               ("fp4_f16", 1), ("fp4_bf16", 1), ("fp4_f16", 8), ("int4a_bf16", 1), ("int4a_f16", 1),
+               ("int4a_bf16", 8)]
 
 
 def steps_suite(args, dev):
@@ -627,7 +628,8 @@ def steps_suite(args, dev):
 
 
 PREFILL_TOKENS = 512
-PREFILL_FMTS = ("nf4_f16", "int4_bf16", "nf4_bf16", "int4_f16", "fp4_f16", "fp4_bf16")
+PREFILL_FMTS = ("nf4_f16", "int4_bf16", "nf4_bf16", "int4_f16", "fp4_f16", "fp4_bf16", "int4a_f16",
+                "int4a_bf16")
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 
 
