@@ -22,6 +22,10 @@ What it computes (all in numpy fp64 unless a storage format fixes the precision)
   absmax / 6, the pages' ladder of thresholds with ties to the even code (LLM Compressor 0.14,
   section "Details worth knowing"; the FP4-named fused kernel of My Triton Kernel Ties
   bitsandbytes, section "The kernels").
+* ``gptq``           -- GPTQ's column loop with lazy blocks (module ``oracle.gptq``): dampening, the
+  upper Cholesky factor of H^-1, per-column quantize with error feedback, the lazy update (LLM
+  Compressor 0.14, sections "The problem GPTQ solves" to "The fused kernel"), in fp64 for the
+  algorithm's checks or fp32 with a fixed order of operations for parity with the GPU kernels.
 * ``dequant_*``      -- the decoded weights, exact in fp64.
 * ``gemv_reference`` -- y = x . W_hat^T and T = |x| . |W_hat|^T in fp64: the fused kernel only moves
   where dequantization happens (LLM Quantization on RTX 4060, section "Kernel Implementation"), so

@@ -1,0 +1,132 @@
+"""Pins of the oracle's GPTQ column loop (CPU only), against what the LLM Compressor 0.14 page
+fixes: lazy blocks change no grid point ("Three checks": block sizes 1, 8, 128, 512 agree), the
+Cholesky form is the Optimal Brain Surgeon update (explicit Equation 2 updates with Gaussian
+elimination of H^-1 pick the same grid points), dampening makes a rank-deficient H factorizable,
+GPTQ with a diagonal H is round-to-nearest, and the error feedback lowers the layer's output
+error on correlated inputs against rounding alone."""
+import numpy as np
+import pytest
+
+from oracle import gptq as G
+
+
+def _layer(rows, cols, tokens, corr, seed):
+    """W ~ N(0, 1) and calibration inputs X [cols x tokens] whose channels share a common factor
+    (correlation ~corr), H = X X^T; a per-row absmax INT4 grid (s = absmax / 7, z = 0)."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((rows, cols))
+    common = rng.standard_normal((1, tokens))
+    x = np.sqrt(corr) * common + np.sqrt(1 - corr) * rng.standard_normal((cols, tokens))
+    x *= rng.uniform(0.5, 2.0, (cols, 1))
+    h = x @ x.T
+    s = np.abs(w).max(axis=1, keepdims=True) / 7.0
+    return w, h, s, np.zeros_like(s), x
+
+
+def _obs(w, h, s, z, qmin, qmax, percdamp=0.01):
+    """Explicit OBS: quantize column j, spread (w_j - q_j) / [H_F^-1]_jj along row j of H_F^-1 to
+    the columns not yet quantized, then remove j from H_F^-1 by one Gaussian elimination step."""
+    w = np.array(w, dtype=np.float64, copy=True)
+    hd, _ = G.dampen(h, percdamp)
+    hinv = np.linalg.inv(hd)
+    codes = np.zeros(w.shape, dtype=np.int64)
+    for j in range(w.shape[1]):
+        qh, codes[:, j] = G.quantize_column(w[:, j], s[:, 0], z[:, 0], qmin, qmax, np.float64)
+        err = (w[:, j] - qh) / hinv[j, j]
+        w[:, j + 1:] -= np.outer(err, hinv[j, j + 1:])
+        hinv = hinv - np.outer(hinv[:, j], hinv[j, :]) / hinv[j, j]
+    return codes
+
+
+def test_u_is_the_upper_cholesky_factor_of_the_dampened_inverse():
+    w, h, s, z, _ = _layer(8, 48, 256, 0.5, 0)
+    u = G.inv_chol_upper(h)
+    hd, _ = G.dampen(h)
+    assert np.allclose(np.triu(u), u)
+    assert np.all(np.diag(u) > 0)
+    assert np.allclose(u.T @ u, np.linalg.inv(hd), rtol=1e-9, atol=1e-12)
+    # the rows of U are the eliminated inverses' rows scaled by 1 / sqrt of their diagonal
+    hinv = np.linalg.inv(hd)
+    j = 5
+    for k in range(j):
+        hinv = hinv - np.outer(hinv[:, k], hinv[k, :]) / hinv[k, k]
+    assert np.allclose(u[j, j:], hinv[j, j:] / np.sqrt(hinv[j, j]), rtol=1e-8)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_lazy_blocks_are_exact(seed):
+    w, h, s, z, _ = _layer(64, 256, 1024, 0.6, seed)
+    u = G.inv_chol_upper(h)
+    ref = G.gptq(w, u, s, z, -8, 7, block=256)["codes"]
+    for b in (1, 8, 128):
+        assert np.array_equal(G.gptq(w, u, s, z, -8, 7, block=b)["codes"], ref), b
+
+
+def test_cholesky_form_is_the_obs_update():
+    w, h, s, z, _ = _layer(32, 96, 512, 0.7, 3)
+    u = G.inv_chol_upper(h)
+    assert np.array_equal(G.gptq(w, u, s, z, -8, 7, block=32)["codes"], _obs(w, h, s, z, -8, 7))
+
+
+def test_diagonal_h_is_round_to_nearest():
+    rng = np.random.default_rng(4)
+    w = rng.standard_normal((16, 64))
+    h = np.diag(rng.uniform(0.5, 3.0, 64))
+    s = np.abs(w).max(axis=1, keepdims=True) / 7.0
+    z = np.zeros_like(s)
+    out = G.gptq(w, G.inv_chol_upper(h), s, z, -8, 7, block=16)
+    q_rtn, c_rtn = G.rtn(w, s, z, -8, 7)
+    assert np.array_equal(out["codes"], c_rtn)
+    assert np.array_equal(out["q_hat"], q_rtn)
+
+
+def test_error_feedback_beats_rounding_on_correlated_inputs():
+    w, h, s, z, x = _layer(64, 128, 2048, 0.9, 5)
+    out = G.gptq(w, G.inv_chol_upper(h), s, z, -8, 7)
+    q_rtn, _ = G.rtn(w, s, z, -8, 7)
+    assert G.proxy_loss(w, out["q_hat"], h) < 0.8 * G.proxy_loss(w, q_rtn, h)
+    # some grid points differ from rounding, all codes on the grid
+    assert np.any(out["codes"] != G.rtn(w, s, z, -8, 7)[1])
+    assert out["codes"].min() >= 0 and out["codes"].max() <= 15
+
+
+def test_dampening_makes_rank_deficient_h_factorizable():
+    w, h, s, z, _ = _layer(16, 256, 64, 0.3, 6)   # 64 tokens for 256 channels: rank 64
+    with pytest.raises(np.linalg.LinAlgError):
+        G.inv_chol_upper(h, percdamp=0.0)
+    u = G.inv_chol_upper(h, percdamp=0.01)
+    out = G.gptq(w, u, s, z, -8, 7)
+    assert np.all(np.isfinite(out["q_hat"]))
+
+
+def test_dead_channels():
+    w, h, s, z, _ = _layer(8, 32, 256, 0.4, 7)
+    h[5, :] = 0
+    h[:, 5] = 0
+    hd, dead = G.dampen(h)
+    assert dead.tolist() == [i == 5 for i in range(32)]
+    d = np.diag(h).copy()
+    d[5] = 1.0
+    assert hd[5, 5] == 1.0 + 0.01 * np.mean(d)
+    assert np.array_equal(np.diag(hd), d + 0.01 * np.mean(d))
+    out = G.gptq(w, G.inv_chol_upper(h), s, z, -8, 7, dead=dead)
+    assert np.all(out["q_hat"][:, 5] == 0)
+
+
+def test_quantize_column_rules():
+    # divide, add the zero point, clamp, round (half to even), dequantize; code = q - qmin
+    w = np.array([0.5, 1.5, 2.5, -0.5, 100.0, -100.0, 0.0, 0.7])
+    s = np.array([1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 0.0, 0.5])
+    z = np.array([0.0, 0.0, 0.0, 3.0, 0.0, 0.0, 2.0, 1.0])
+    qh, code = G.quantize_column(w, s, z, -8, 7, np.float64)
+    assert code.tolist() == [8, 10, 10, 10, 15, 0, 10, 10]
+    assert qh.tolist() == [0.0, 2.0, 2.0, -1.0, 7.0, -8.0, 0.0, 0.5]
+
+
+def test_fp32_loop_tracks_fp64():
+    w, h, s, z, _ = _layer(128, 256, 1024, 0.6, 8)
+    u = G.inv_chol_upper(h)
+    c64 = G.gptq(w, u, s, z, -8, 7)["codes"]
+    out32 = G.gptq(w, u, s, z, -8, 7, dtype=np.float32)
+    assert out32["q_hat"].dtype == np.float32
+    assert np.mean(out32["codes"] == c64) > 0.995
