@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.w4_quantize_int4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.w4_quantize_fp4.argtypes = [vp, i64, i64, vp, vp, vp]
         L.w4_quantize_int4_asym.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.w4_gptq_block_update.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, i64, i64, vp, vp,
+                                           vp, vp]
+        L.w4_gptq_lazy_update.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
+        L.w4_gptq_quantize.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, i64, vp, vp, vp, vp]
         L.w4_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_smallbatch.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_prefill.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
@@ -77,7 +81,8 @@ def lib() -> ctypes.CDLL:
                      "w4_gemv", "w4_gemm_smallbatch", "w4_matmul_ex", "w4_auto_path",
                      "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
                      "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped",
-                     "w4_gemm_prefill"):
+                     "w4_gemm_prefill", "w4_gptq_block_update", "w4_gptq_lazy_update",
+                     "w4_gptq_quantize"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -348,3 +353,59 @@ def probe_copy(src, dst, stream=None):
     _need_cuda(src, dst)
     check(lib().w4_probe_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
                               _stream(stream)), "w4_probe_copy")
+
+
+def _gptq_args(w, u, scale, zero, group):
+    import torch
+
+    _need_cuda(w, u, scale, zero)
+    for t in (w, u, scale, zero):
+        if t.dtype != torch.float32 or t.dim() != 2:
+            raise ValueError("w, u, scale and zero must be 2-D float32 tensors")
+    rows, cols = w.shape
+    if tuple(u.shape) != (cols, cols):
+        raise ValueError("u must be [cols, cols]")
+    group = cols if group is None else int(group)
+    if group < 1 or cols % group or tuple(scale.shape) != (rows, cols // group) or \
+            tuple(zero.shape) != (rows, cols // group):
+        raise ValueError("scale and zero must be [rows, cols // group]")
+    return rows, cols, group
+
+
+def gptq_outputs(w):
+    """Empty (q_hat fp32, codes uint8, err fp32) buffers shaped like w."""
+    import torch
+
+    return (torch.empty_like(w), torch.empty(w.shape, dtype=torch.uint8, device=w.device),
+            torch.empty_like(w))
+
+
+def gptq_quantize(w, u, scale, zero, qmin, qmax, group=None, block=128, stream=None):
+    """GPTQ's column loop on w [rows, cols] (fp32, updated in place) with U the upper Cholesky
+    factor of the dampened inverse Hessian [cols, cols], grid scale/zero [rows, cols // group],
+    codes in [qmin, qmax], lazy blocks of `block` columns.  Returns (q_hat, codes, err)."""
+    rows, cols, group = _gptq_args(w, u, scale, zero, group)
+    q_hat, codes, err = gptq_outputs(w)
+    check(lib().w4_gptq_quantize(_ptr(w), _ptr(u), _ptr(scale), _ptr(zero), rows, cols, group,
+                                 int(qmin), int(qmax), int(block), _ptr(q_hat), _ptr(codes),
+                                 _ptr(err), _stream(stream)), "w4_gptq_quantize")
+    return q_hat, codes, err
+
+
+def gptq_block_update(w, u, scale, zero, qmin, qmax, col0, bcols, q_hat, codes, err, group=None,
+                      stream=None):
+    """One lazy block [col0, col0 + bcols) of the column loop (outputs written in place)."""
+    rows, cols, group = _gptq_args(w, u, scale, zero, group)
+    _need_cuda(q_hat, codes, err)
+    check(lib().w4_gptq_block_update(_ptr(w), _ptr(u), _ptr(scale), _ptr(zero), rows, cols, group,
+                                     int(qmin), int(qmax), int(col0), int(bcols), _ptr(q_hat),
+                                     _ptr(codes), _ptr(err), _stream(stream)),
+          "w4_gptq_block_update")
+
+
+def gptq_lazy_update(w, u, err, col0, bcols, stream=None):
+    """W[:, col0 + bcols:] -= E[:, col0:col0 + bcols] U[col0:col0 + bcols, col0 + bcols:]."""
+    _need_cuda(w, u, err)
+    rows, cols = w.shape
+    check(lib().w4_gptq_lazy_update(_ptr(w), _ptr(u), _ptr(err), rows, cols, int(col0), int(bcols),
+                                    _stream(stream)), "w4_gptq_lazy_update")

@@ -601,4 +601,95 @@ int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
              : W4_ERR_HIP;
 }
 
+namespace {
+
+// Shared checks of the GPTQ calls; 0 when the arguments are usable.
+int gptq_check(const float* w, const float* u, const float* scale, const float* zero, int64_t rows,
+               int64_t cols, int64_t group, int qmin, int qmax, const float* q_hat,
+               const uint8_t* codes, const float* err) {
+  if (!w || !u || !scale || !zero || !q_hat || !codes || !err) return W4_ERR_NULL;
+  if (rows < 1 || cols < 1 || rows >= kMaxDim || cols >= ((int64_t)1 << 22)) return W4_ERR_SHAPE;
+  if (group < 1 || cols % group != 0 || cols / group >= kMaxDim) return W4_ERR_SHAPE;
+  if (qmin >= qmax || qmax - qmin > 255 || qmin < -32767 || qmax > 32767) return W4_ERR_SHAPE;
+  if (!aligned(w, 4) || !aligned(u, 4) || !aligned(scale, 4) || !aligned(zero, 4) ||
+      !aligned(q_hat, 4) || !aligned(err, 4))
+    return W4_ERR_ALIGN;
+  const size_t wb = (size_t)rows * (size_t)cols * 4, cb = (size_t)rows * (size_t)cols;
+  const size_t ub = (size_t)cols * (size_t)cols * 4, sb = (size_t)rows * (size_t)(cols / group) * 4;
+  const void* outs[3] = {q_hat, codes, err};
+  const size_t outb[3] = {wb, cb, wb};
+  const void* ins[4] = {w, u, scale, zero};
+  const size_t inb[4] = {wb, ub, sb, sb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outs[i], outb[i], ins[j], inb[j])) return W4_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outb[i], outs[j], outb[j])) return W4_ERR_ALIAS;
+  }
+  for (int j = 1; j < 4; ++j)
+    if (overlaps(w, wb, ins[j], inb[j])) return W4_ERR_ALIAS;
+  return W4_OK;
+}
+
+int gptq_block(float* w, const float* u, const float* scale, const float* zero, int64_t rows,
+               int64_t cols, int64_t group, int qmin, int qmax, int64_t col0, int64_t bcols,
+               float* q_hat, uint8_t* codes, float* err, hipStream_t s) {
+  const int64_t ng = cols / group;
+  const hipError_t e = launch_gptq_block(
+      w + col0, cols, u + col0 * cols + col0, cols, scale, zero, ng, (int)group,
+      (int)col0, qmin, qmax, rows, (int)bcols, q_hat + col0, cols, codes + col0, cols, err + col0,
+      cols, s);
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+int gptq_lazy(float* w, const float* u, const float* err, int64_t rows, int64_t cols, int64_t col0,
+              int64_t bcols, hipStream_t s) {
+  const int64_t i2 = col0 + bcols;
+  if (i2 >= cols) return W4_OK;
+  const hipError_t e = launch_gptq_lazy(w + i2, cols, err + col0, cols, u + col0 * cols + i2, cols,
+                                        rows, cols - i2, (int)bcols, s);
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+}  // namespace
+
+int w4_gptq_block_update(float* w, const float* u, const float* scale, const float* zero,
+                         int64_t rows, int64_t cols, int64_t group, int qmin, int qmax,
+                         int64_t col0, int64_t bcols, float* q_hat, uint8_t* codes, float* err,
+                         void* stream) {
+  const int st = gptq_check(w, u, scale, zero, rows, cols, group, qmin, qmax, q_hat, codes, err);
+  if (st != W4_OK) return st;
+  if (col0 < 0 || bcols < 1 || bcols > 128 || col0 + bcols > cols) return W4_ERR_SHAPE;
+  return gptq_block(w, u, scale, zero, rows, cols, group, qmin, qmax, col0, bcols, q_hat, codes,
+                    err, reinterpret_cast<hipStream_t>(stream));
+}
+
+int w4_gptq_lazy_update(float* w, const float* u, const float* err, int64_t rows, int64_t cols,
+                        int64_t col0, int64_t bcols, void* stream) {
+  if (!w || !u || !err) return W4_ERR_NULL;
+  if (rows < 1 || cols < 1 || rows >= kMaxDim || cols >= ((int64_t)1 << 22)) return W4_ERR_SHAPE;
+  if (col0 < 0 || bcols < 1 || bcols > 128 || col0 + bcols > cols) return W4_ERR_SHAPE;
+  if (!aligned(w, 4) || !aligned(u, 4) || !aligned(err, 4)) return W4_ERR_ALIGN;
+  const size_t wb = (size_t)rows * (size_t)cols * 4, ub = (size_t)cols * (size_t)cols * 4;
+  if (overlaps(w, wb, u, ub) || overlaps(w, wb, err, wb)) return W4_ERR_ALIAS;
+  return gptq_lazy(w, u, err, rows, cols, col0, bcols, reinterpret_cast<hipStream_t>(stream));
+}
+
+int w4_gptq_quantize(float* w, const float* u, const float* scale, const float* zero, int64_t rows,
+                     int64_t cols, int64_t group, int qmin, int qmax, int64_t block, float* q_hat,
+                     uint8_t* codes, float* err, void* stream) {
+  const int st = gptq_check(w, u, scale, zero, rows, cols, group, qmin, qmax, q_hat, codes, err);
+  if (st != W4_OK) return st;
+  if (block < 1 || block > 128) return W4_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int64_t c0 = 0; c0 < cols; c0 += block) {
+    const int64_t bc = std::min(block, cols - c0);
+    int r = gptq_block(w, u, scale, zero, rows, cols, group, qmin, qmax, c0, bc, q_hat, codes, err, s);
+    if (r != W4_OK) return r;
+    r = gptq_lazy(w, u, err, rows, cols, c0, bc, s);
+    if (r != W4_OK) return r;
+  }
+  return W4_OK;
+}
+
 }  // extern "C"

@@ -184,6 +184,12 @@ hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uin
                                int64_t k, int64_t b, hipStream_t s);
 hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
                        int64_t n, int64_t k, int64_t m, float* y, hipStream_t s);
+hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu, const float* scale,
+                             const float* zero, int64_t lds, int group, int i1, int qmin, int qmax,
+                             int64_t rows, int bc, float* q_hat, int64_t ldq, uint8_t* codes,
+                             int64_t ldc, float* err, int64_t lde, hipStream_t s);
+hipError_t launch_gptq_lazy(float* w, int64_t ldw, const float* err, int64_t lde, const float* u,
+                            int64_t ldu, int64_t rows, int64_t cols, int bc, hipStream_t s);
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 

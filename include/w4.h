@@ -271,6 +271,51 @@ const char* w4_status_string(int status);
 /* Library ABI version (this header: 1). */
 int w4_version(void);
 
+/* ------------------------------------------------------------------ GPTQ column loop ------- */
+
+/* GPTQ quantizes a layer W [rows x cols] column by column onto a grid fixed beforehand, feeding
+ * each column's rounding error forward through U, the upper Cholesky factor of the dampened
+ * inverse Hessian (H^-1 = U^T U), in lazy blocks of up to 128 columns (LLM Compressor 0.14: GPTQ's
+ * 15x speedup is one fused loop, "Three changes that make it fast", "The fused kernel").  Forming
+ * H, dampening it and factorizing stay outside these calls, as on that page: U is an input.
+ *
+ * Common arguments (all device pointers, row-major, 4-byte aligned unless stated):
+ *   w       float[rows, cols], read and updated in place: column j ends holding the value it was
+ *           quantized from (every earlier column's update applied)
+ *   u       float[cols, cols]; only the upper triangle j <= c is read; U_jj > 0
+ *   scale, zero  float[rows, cols / group]: the grid of row r, column j is scale[r, j / group],
+ *           zero[r, j / group]; group >= 1 divides cols
+ *   qmin, qmax   integer code range, qmin < qmax, qmax - qmin <= 255, |qmin|, |qmax| <= 32767
+ *   q_hat   float[rows, cols] written: (q - z) * s
+ *   codes   uint8[rows, cols] written: q - qmin (for the W4 formats the stored nibble: qmin = -8
+ *           symmetric, qmin = 0 asymmetric)
+ *   err     float[rows, cols] written: column j's e = (w_j - q_hat_j) / U_jj
+ *   rows, cols   1 <= rows < 2^31, 1 <= cols < 2^22
+ * Column j, per row: q = rint(clamp(w_j / s + z, qmin, qmax)) (w_j / s taken as 0 when s == 0),
+ * q_hat = (q - z) s, e = (w_j - q_hat) / U_jj, then w_c -= e U_jc for the block's columns c > j.
+ * Every operation is fp32, rounded on its own in that order (products rounded before the
+ * subtraction; no fused multiply-add; divisions correctly rounded).  The outputs must not overlap
+ * each other or the inputs.  Asynchronous on `stream`; no allocation. */
+
+/* One lazy block: columns [col0, col0 + bcols), 1 <= bcols <= 128, col0 + bcols <= cols.  Rows
+ * run in parallel (a 16-lane team per row), the block's columns in sequence. */
+int w4_gptq_block_update(float* w, const float* u, const float* scale, const float* zero,
+                         int64_t rows, int64_t cols, int64_t group, int qmin, int qmax,
+                         int64_t col0, int64_t bcols, float* q_hat, uint8_t* codes, float* err,
+                         void* stream);
+
+/* The lazy update after block [col0, col0 + bcols): W[:, i2:] -= E[:, col0:i2] U[col0:i2, i2:],
+ * i2 = col0 + bcols, each element's sum over the block's columns taken in column order (products
+ * rounded, then added), then subtracted.  Reads err's block columns; a no-op when i2 == cols. */
+int w4_gptq_lazy_update(float* w, const float* u, const float* err, int64_t rows, int64_t cols,
+                        int64_t col0, int64_t bcols, void* stream);
+
+/* The whole column loop: for each block of `block` columns (1..128; the last one may be
+ * narrower), w4_gptq_block_update then w4_gptq_lazy_update. */
+int w4_gptq_quantize(float* w, const float* u, const float* scale, const float* zero, int64_t rows,
+                     int64_t cols, int64_t group, int qmin, int qmax, int64_t block, float* q_hat,
+                     uint8_t* codes, float* err, void* stream);
+
 /* ------------------------------------------------------------------ measurement probes ------ */
 
 /* Streaming-read ceiling probe: reads `bytes` (multiple of 16) from device `src` with 128-bit

@@ -92,3 +92,15 @@ def single_gemv_case(seed: int = 0, n: int = 256, k: int = 1536, dtype: str = "f
     w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(QWEN15_SIGMA)
     x = to_storage_bits(rng.standard_normal((1, k), dtype=np.float32), dtype)
     return w, x
+
+
+def upper_factor(cols: int, seed: int, off_sigma: float = 0.3) -> np.ndarray:
+    """A seeded random upper-triangular fp32 matrix [cols, cols]: diagonal ~ U(0.5, 1.5),
+    entries above it ~ N(0, off_sigma^2 / cols), zeros below.  Any such matrix U is the upper
+    Cholesky factor of the inverse of the symmetric positive definite matrix (U^T U)^-1, so it
+    stands for the factor that GPTQ's column loop takes as input."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((cols, cols), dtype=np.float32) * np.float32(off_sigma / np.sqrt(cols))
+    u = np.triu(u, 1)
+    u[np.diag_indices(cols)] = rng.uniform(0.5, 1.5, cols).astype(np.float32)
+    return u

@@ -226,3 +226,44 @@ def test_grouped_plan_logic():
     with pytest.raises(ValueError):
         w4.gemv_grouped_plan("nf4_f16", [64, 0], 256, 1)
     assert L.w4_gemv_grouped_plan(1, 2, None, 256, 1, None, None, None, None, None) == -1
+
+
+G_SP = 1 << 24  # spacing of the fake GPTQ buffers: large enough that none overlaps another
+
+
+def _gptq(L, w=G_SP, u=G_SP * 2, s=G_SP * 3, z=G_SP * 4, rows=64, cols=256, group=128, qmin=-8,
+          qmax=7, block=128, q=G_SP * 5, c=G_SP * 6, e=G_SP * 7):
+    vp = ctypes.c_void_p
+    return L.w4_gptq_quantize(vp(w), vp(u), vp(s), vp(z), rows, cols, group, qmin, qmax, block,
+                              vp(q), vp(c), vp(e), None)
+
+
+def test_gptq_validation_codes():
+    """The GPTQ calls check shapes, the code range, alignment and overlaps on the host (every
+    case here fails validation, before any launch)."""
+    _, L = _lib()
+    vp = ctypes.c_void_p
+    assert _gptq(L, w=0) == -1
+    assert _gptq(L, e=0) == -1
+    assert _gptq(L, rows=0) == -2
+    assert _gptq(L, cols=1 << 22) == -2
+    assert _gptq(L, group=100) == -2          # does not divide cols
+    assert _gptq(L, block=0) == -2
+    assert _gptq(L, block=129) == -2
+    assert _gptq(L, qmin=7, qmax=7) == -2
+    assert _gptq(L, qmin=0, qmax=256) == -2   # codes are bytes
+    assert _gptq(L, s=G_SP * 3 + 2) == -3
+    assert _gptq(L, q=G_SP + 64) == -9        # q_hat overlaps w
+    assert _gptq(L, c=G_SP * 5 + 8) == -9     # codes overlap q_hat
+    assert _gptq(L, u=G_SP + 4096) == -9      # u overlaps w
+    # one block: col0 + bcols within cols, 1 <= bcols <= 128
+    blk = L.w4_gptq_block_update
+    args = [vp(G_SP), vp(G_SP * 2), vp(G_SP * 3), vp(G_SP * 4), 64, 256, 128, -8, 7]
+    outs = [vp(G_SP * 5), vp(G_SP * 6), vp(G_SP * 7), None]
+    assert blk(*args, 200, 64, *outs) == -2
+    assert blk(*args, 0, 0, *outs) == -2
+    assert blk(*args, 0, 129, *outs) == -2
+    lazy = L.w4_gptq_lazy_update
+    assert lazy(vp(G_SP), vp(G_SP * 2), None, 64, 256, 0, 128, None) == -1
+    assert lazy(vp(G_SP), vp(G_SP * 2), vp(G_SP * 7), 64, 256, 192, 128, None) == -2
+    assert lazy(vp(G_SP), vp(G_SP + 8), vp(G_SP * 7), 64, 256, 0, 128, None) == -9
