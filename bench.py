@@ -39,7 +39,8 @@ def parse_args():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--suite", default="decode", choices=["decode", "shapes", "counters", "steps", "prefill"],
+    ap.add_argument("--suite", default="decode",
+                    choices=["decode", "shapes", "counters", "steps", "prefill", "gptq"],
                     help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table; "
                          "counters: a few launches of each path, for rocprofv3 --pmc runs; "
                          "steps: the decode step in the other formats and at batch 8; "
@@ -703,6 +704,130 @@ def prefill_suite(args, dev):
     return out
 
 
+GPTQ_BLOCK = 128
+GPTQ_GROUP = 128
+# fp32 multiply and add as separate VALU instructions (no FMA, no packed fp32): one flop per lane
+# per cycle, 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+VALU_FP32_UNFUSED_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def gptq_suite(args, dev):
+    """GPTQ's column loop over the seven matrices of one Qwen2.5-1.5B decoder layer (LLM Compressor
+    0.14, "The fused kernel"): INT4 codes -8..7 on a symmetric grid fixed beforehand (absmax / 7 per
+    group of 128), lazy blocks of 128 columns, U a seeded random upper factor per input width
+    (q, k, v, gate and up share one: they read the same activations).  The layer's launches (one
+    fused block kernel and one lazy update per block) are captured as one HIP graph; also graphs
+    of only the block kernels and only the lazy updates, for their per-launch times.  Returns a
+    dict of the figures."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+    import synth_inputs
+
+    L = w4.lib()
+    vp = ctypes.c_void_p
+    gen = torch.Generator(device=dev).manual_seed(5)
+    ufac = {}
+    mats = []
+    for name, n, k in synth_inputs.QWEN15_LAYER:
+        key = name if name in ("o", "down") else "x"
+        if key not in ufac:
+            ufac[key] = torch.from_numpy(synth_inputs.upper_factor(k, seed=k + len(ufac))).to(dev)
+        w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+        s = (w.abs().view(n, k // GPTQ_GROUP, GPTQ_GROUP).amax(dim=2) / 7.0).contiguous()
+        z = torch.zeros_like(s)
+        mats.append((name, n, k, w, ufac[key], s, z, *w4.gptq_outputs(w)))
+
+    def launches(kind):
+        out = []
+        for name, n, k, w, u, s, z, q, c, e in mats:
+            for c0 in range(0, k, GPTQ_BLOCK):
+                bc = min(GPTQ_BLOCK, k - c0)
+                if kind in ("all", "block"):
+                    out.append(("block", name, n, k, c0, bc, (w, u, s, z, q, c, e)))
+                if kind in ("all", "lazy") and c0 + bc < k:
+                    out.append(("lazy", name, n, k, c0, bc, (w, u, s, z, q, c, e)))
+        return out
+
+    def launch(item, stream):
+        kind, name, n, k, c0, bc, (w, u, s, z, q, c, e) = item
+        if kind == "block":
+            st = L.w4_gptq_block_update(vp(w.data_ptr()), vp(u.data_ptr()), vp(s.data_ptr()),
+                                        vp(z.data_ptr()), n, k, GPTQ_GROUP, -8, 7, c0, bc,
+                                        vp(q.data_ptr()), vp(c.data_ptr()), vp(e.data_ptr()), vp(stream))
+        else:
+            st = L.w4_gptq_lazy_update(vp(w.data_ptr()), vp(u.data_ptr()), vp(e.data_ptr()), n, k, c0,
+                                       bc, vp(stream))
+        w4.check(st, kind)
+
+    def graph_of(items):
+        s0 = torch.cuda.Stream(device=dev)
+        s0.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s0):
+            for it in items:
+                launch(it, s0.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s0):
+            for it in items:
+                launch(it, s0.cuda_stream)
+        torch.cuda.synchronize()
+        return g
+
+    reps, warm = max(3, args.steps // 20), 2
+    res = {"block": GPTQ_BLOCK, "group": GPTQ_GROUP, "matrices": []}
+    layer_cols = sum(k for _, _, k in synth_inputs.QWEN15_LAYER)
+    items = launches("all")
+    g = graph_of(items)
+    ms = time_replays(g, reps, warm)
+    del g
+    res["layer"] = {"ms": round(ms, 4), "launches": len(items), "columns": layer_cols,
+                    "us_per_column": round(ms * 1e3 / layer_cols, 3)}
+    log(f"[gptq] layer: {ms:.3f} ms, {len(items)} launches, {ms * 1e3 / layer_cols:.2f} us per column")
+    for kind in ("block", "lazy"):
+        its = launches(kind)
+        g = graph_of(its)
+        ms_k = time_replays(g, reps, warm)
+        del g
+        flops = 0.0
+        for _, _, n, k, c0, bc, _ in its:
+            if kind == "lazy":
+                flops += 2.0 * n * (k - c0 - bc) * bc
+            else:
+                flops += 2.0 * n * bc * (bc - 1) / 2
+        tf = flops / (ms_k / 1e3) / 1e12
+        res[kind] = {"ms": round(ms_k, 4), "launches": len(its),
+                     "us_per_launch": round(ms_k * 1e3 / len(its), 3),
+                     "flop": flops, "tflops": round(tf, 2),
+                     "frac_unfused_fp32_peak": round(tf / VALU_FP32_UNFUSED_PEAK_TFLOPS, 4)}
+        log(f"[gptq] {kind} kernels: {ms_k:.3f} ms over {len(its)} launches, {tf:.1f} TFLOP/s")
+    for name, n, k, *_ in mats:
+        its = [it for it in items if it[1] == name]
+        g = graph_of(its)
+        ms_m = time_replays(g, reps, warm)
+        del g
+        res["matrices"].append({"name": name, "rows": n, "cols": k, "ms": round(ms_m, 4),
+                                "us_per_column": round(ms_m * 1e3 / k, 3)})
+        log(f"[gptq] {name} {n}x{k}: {ms_m:.3f} ms")
+    # the oracle's fp32 loop on the q matrix (the same arithmetic, numpy on the host), for scale
+    name, n, k = synth_inputs.QWEN15_LAYER[0]
+    from oracle import gptq as G
+
+    w = synth_inputs.weights(n, k, seed=1)
+    u = synth_inputs.upper_factor(k, seed=2)
+    sg = (np.abs(w.reshape(n, k // GPTQ_GROUP, GPTQ_GROUP)).max(axis=2) / np.float32(7)).astype(np.float32)
+    t0 = time.perf_counter()
+    G.gptq(w, u, sg, np.zeros_like(sg), -8, 7, group=GPTQ_GROUP, block=GPTQ_BLOCK, dtype=np.float32)
+    cpu_s = time.perf_counter() - t0
+    res["cpu_oracle_q"] = {"seconds": round(cpu_s, 3), "us_per_column": round(cpu_s * 1e6 / k, 1),
+                           "threads": 1}
+    log(f"[gptq] oracle fp32 loop on q {n}x{k} (host): {cpu_s:.2f} s")
+    return res
+
+
 def shapes_suite(args, dev):
     """Per-shape table for the other workloads: INT4 decode steps (B = 1, 8) and split-K vs one
     pass on down; small-batch GEMM on gate / down / lm_head at B = 1, 8, 32, 128 for the GEMV,
@@ -926,6 +1051,16 @@ def main():
                 json.dump(res, f, indent=1)
         print(json.dumps({"metric": "prefill step (512 tokens) and per-shape GEMM table",
                           "steps": res["steps"]}), flush=True)
+        return
+    if args.suite == "gptq":
+        import torch
+
+        res = gptq_suite(args, torch.device("cuda:0"))
+        if args.report:
+            with open(args.report, "w") as f:
+                json.dump(res, f, indent=1)
+        print(json.dumps({"metric": "GPTQ column loop, one Qwen2.5-1.5B layer", **res["layer"]}),
+              flush=True)
         return
     if args.suite == "shapes":
         import torch

@@ -19,7 +19,7 @@
 // block's columns t, t + 16, ..., t + 112 in registers.  Column j belongs to lane j % 16, which
 // quantizes it; its error goes to the team by a DPP row broadcast, and every lane updates its own
 // columns right of j with U[j, c] read from LDS (the block of U transposed to [j][t][m], zero
-// where c <= j).  16 rows per 256-thread workgroup.
+// where c <= j).  32 rows per 512-thread workgroup; two workgroups fit a CU's LDS.
 //
 // Lazy-update kernel: 64 x 64 output tiles, each of 256 threads computing 4 x 4 outputs from the
 // block's errors and U's rows staged in LDS.
@@ -35,7 +35,8 @@ namespace {
 constexpr int kBlockMax = 128;
 constexpr int kTeam = 16;
 constexpr int kSlots = kBlockMax / kTeam;  // columns per lane
-constexpr int kRowsPerWg = 256 / kTeam;
+constexpr int kBlockThreads = 512;
+constexpr int kRowsPerWg = kBlockThreads / kTeam;
 
 __device__ inline float div_rn(float a, float b) { return __fdiv_rn(a, b); }
 
@@ -58,6 +59,8 @@ struct GptqBlockArgs {
 // One row's state in the block kernel: this lane's 8 columns and their results.
 struct ColState {
   float w[kSlots], s[kSlots], z[kSlots], qh[kSlots], ee[kSlots];
+  float d[kSlots];  // U_cc of the lane's columns c (the divisor when the lane owns the column)
+  float4 u0, u1;    // row J of the transposed U block for this lane, read one column ahead
   uint32_t code[kSlots];
   int t, bc, qmin;
   float fqmin, fqmax;
@@ -72,29 +75,34 @@ template <int J>
 __device__ __forceinline__ void column_step(ColState& st) {
   constexpr int o = J & 15, mj = J >> 4;
   if (J >= st.bc) return;  // uniform
+  // this column's U row (read during the previous column), and the next one's, read now so that
+  // its LDS latency overlaps this column's divisions
+  const float4 u0 = st.u0, u1 = st.u1;
+  if constexpr (J + 1 < kBlockMax) {
+    st.u0 = *reinterpret_cast<const float4*>(&st.ut[(((J + 1) << 4) + st.t) * kSlots]);
+    st.u1 = *reinterpret_cast<const float4*>(&st.ut[(((J + 1) << 4) + st.t) * kSlots + 4]);
+  }
   const float wj = st.w[mj];
   float v = st.s[mj] != 0.0f ? div_rn(wj, st.s[mj]) : 0.0f;
   v = v + st.z[mj];
   v = fminf(fmaxf(v, st.fqmin), st.fqmax);
   const float q = rintf(v);
   const float qhat = (q - st.z[mj]) * st.s[mj];
-  const float e_own = div_rn(wj - qhat, st.ud[J]);
-  if (st.t == o) {
-    st.qh[mj] = qhat;
-    st.ee[mj] = e_own;
-    st.code[mj] = (uint32_t)((int)q - st.qmin);
-  }
+  const float e_own = div_rn(wj - qhat, st.d[mj]);
+  const bool own = st.t == o;
+  st.qh[mj] = own ? qhat : st.qh[mj];
+  st.ee[mj] = own ? e_own : st.ee[mj];
+  st.code[mj] = own ? (uint32_t)((int)q - st.qmin) : st.code[mj];
   // DPP row broadcast of lane o of each 16-lane row: the owner's error to its team
   const float e = __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, e_own), 0x150 + o, 0xF, 0xF, false));
-  const float4 u0 = *reinterpret_cast<const float4*>(&st.ut[((J << 4) + st.t) * kSlots]);
-  const float4 u1 = *reinterpret_cast<const float4*>(&st.ut[((J << 4) + st.t) * kSlots + 4]);
   const float uu[kSlots] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
   for (int m = mj; m < kSlots; ++m) {
     const float p = e * uu[m];
+    const float wn = st.w[m] - p;
     // in slot mj the columns c <= J (lanes t <= o) keep their value
-    if (m > mj || st.t > o) st.w[m] = st.w[m] - p;
+    st.w[m] = (m > mj || st.t > o) ? wn : st.w[m];
   }
 }
 
@@ -103,22 +111,35 @@ __device__ __forceinline__ void run_columns(std::integer_sequence<int, J...>, Co
   (column_step<J>(st), ...);
 }
 
-__global__ void __launch_bounds__(256) gptq_block_kernel(GptqBlockArgs a) {
+__global__ void __launch_bounds__(kBlockThreads, 2) gptq_block_kernel(GptqBlockArgs a) {
   // U block, transposed: ut[(j * 16 + t) * 8 + m] = U[i1 + j, i1 + t + 16 m] for t + 16 m > j,
   // else 0; ud[j] = U[i1 + j, i1 + j].
   __shared__ __align__(16) float ut[kBlockMax * kTeam * kSlots];
   __shared__ float ud[kBlockMax];
   const int tid = threadIdx.x;
   const int bc = a.bc;
-  for (int e = tid; e < kBlockMax * kBlockMax; e += 256) {
-    const int j = e >> 7, c = e & 127;
-    float v = 0.0f;
-    if (j < bc && c < bc && c >= j) v = a.u[(int64_t)j * a.ldu + c];
-    if (c == j) {
-      ud[j] = v;
-      v = 0.0f;
+  // Thread tid fills column c = tid & 127 of rows j = (tid >> 7) + 4 i, i = 0..31: every load is
+  // issued unconditionally (indices clamped into the block) before the first LDS write, so the 32
+  // loads are in flight together; values outside the upper triangle are then replaced by 0.
+  constexpr int kFill = kBlockMax * kBlockMax / kBlockThreads;
+  constexpr int kJStep = kBlockThreads / kBlockMax;
+  {
+    const int c = tid & 127, j0 = tid >> 7;
+    const int cl = c < bc ? c : bc - 1;
+    float uv[kFill];
+#pragma unroll
+    for (int i = 0; i < kFill; ++i) {
+      const int j = j0 + kJStep * i;
+      const int jl = j < bc ? j : bc - 1;
+      uv[i] = a.u[(int64_t)jl * a.ldu + cl];
     }
-    ut[((j << 4) + (c & 15)) * kSlots + (c >> 4)] = v;
+#pragma unroll
+    for (int i = 0; i < kFill; ++i) {
+      const int j = j0 + kJStep * i;
+      const bool upper = j < bc && c < bc && c > j;
+      if (c == j) ud[j] = j < bc ? uv[i] : 0.0f;
+      ut[((j << 4) + (c & 15)) * kSlots + (c >> 4)] = upper ? uv[i] : 0.0f;
+    }
   }
 
   const int t = tid & (kTeam - 1);
@@ -130,8 +151,10 @@ __global__ void __launch_bounds__(256) gptq_block_kernel(GptqBlockArgs a) {
   for (int m = 0; m < kSlots; ++m) {
     const int c = t + kTeam * m;
     const bool in = c < bc;
-    w[m] = in ? a.w[rr * a.ldw + c] : 0.0f;
-    const int64_t g = (int64_t)((a.i1 + (in ? c : 0)) / a.group);
+    const int cl = in ? c : bc - 1;  // every load in bounds and unconditional
+    const float wv = a.w[rr * a.ldw + cl];
+    w[m] = in ? wv : 0.0f;
+    const int64_t g = (int64_t)((a.i1 + cl) / a.group);
     s[m] = a.scale[rr * a.lds + g];
     z[m] = a.zero[rr * a.lds + g];
   }
@@ -152,6 +175,10 @@ __global__ void __launch_bounds__(256) gptq_block_kernel(GptqBlockArgs a) {
     st.ee[m] = 0.0f;
     st.code[m] = 0u;
   }
+#pragma unroll
+  for (int m = 0; m < kSlots; ++m) st.d[m] = ud[t + kTeam * m];
+  st.u0 = *reinterpret_cast<const float4*>(&ut[t * kSlots]);
+  st.u1 = *reinterpret_cast<const float4*>(&ut[t * kSlots + 4]);
   st.fqmin = (float)a.qmin;
   st.fqmax = (float)a.qmax;
   // one copy of the column step per column (slot and owner lane are constants in each), so that
@@ -182,23 +209,45 @@ struct GptqLazyArgs {
 };
 
 constexpr int kTile = 64;
-constexpr int kEPitch = kBlockMax + 1;
+constexpr int kEPitch = kTile + 4;  // es row pitch (floats): 16-byte rows, writes spread over banks
 
 __global__ void __launch_bounds__(256) gptq_lazy_kernel(GptqLazyArgs a) {
-  __shared__ float es[kTile * kEPitch];       // es[row * kEPitch + kk] = E[r0 + row, kk]
+  __shared__ __align__(16) float es[kBlockMax * kEPitch];  // es[kk * kEPitch + row] = E[r0 + row, kk]
   __shared__ __align__(16) float us[kBlockMax * kTile];  // us[kk * 64 + col] = U[kk, c0 + col]
   const int tid = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.x * kTile, c0 = (int64_t)blockIdx.y * kTile;
   const int bc = a.bc;
-  for (int e = tid; e < kTile * kBlockMax; e += 256) {
-    const int row = e >> 7, kk = e & 127;
-    const int64_t r = r0 + row;
-    es[row * kEPitch + kk] = (kk < bc && r < a.rows) ? a.err[r * a.lde + kk] : 0.0f;
+  // Loads unconditional (indices clamped into range) and all issued before the LDS writes.
+  {
+    const int kk = tid & 127, row0 = tid >> 7;
+    const int kkl = kk < bc ? kk : bc - 1;
+    float ev[kTile / 2];
+#pragma unroll
+    for (int i = 0; i < kTile / 2; ++i) {
+      const int64_t r = r0 + row0 + 2 * i;
+      ev[i] = a.err[(r < a.rows ? r : a.rows - 1) * a.lde + kkl];
+    }
+#pragma unroll
+    for (int i = 0; i < kTile / 2; ++i) {
+      const int row = row0 + 2 * i;
+      es[kk * kEPitch + row] = (kk < bc && r0 + row < a.rows) ? ev[i] : 0.0f;
+    }
   }
-  for (int e = tid; e < kBlockMax * kTile; e += 256) {
-    const int kk = e >> 6, col = e & 63;
+  {
+    const int col = tid & 63, kk0 = tid >> 6;
     const int64_t c = c0 + col;
-    us[kk * kTile + col] = (kk < bc && c < a.cols) ? a.u[(int64_t)kk * a.ldu + c] : 0.0f;
+    const int64_t cl = c < a.cols ? c : a.cols - 1;
+    float uv[kBlockMax / 4];
+#pragma unroll
+    for (int i = 0; i < kBlockMax / 4; ++i) {
+      const int kk = kk0 + 4 * i;
+      uv[i] = a.u[(int64_t)(kk < bc ? kk : bc - 1) * a.ldu + cl];
+    }
+#pragma unroll
+    for (int i = 0; i < kBlockMax / 4; ++i) {
+      const int kk = kk0 + 4 * i;
+      us[kk * kTile + col] = (kk < bc && c < a.cols) ? uv[i] : 0.0f;
+    }
   }
   __syncthreads();
   const int tr = (tid >> 4) * 4, tc = (tid & 15) * 4;
@@ -208,15 +257,18 @@ __global__ void __launch_bounds__(256) gptq_lazy_kernel(GptqLazyArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) acc[i][jj] = 0.0f;
   }
+  // the block's columns in order kk = 0, 1, ...: each product rounded, then added
+#pragma unroll 4
   for (int kk = 0; kk < bc; ++kk) {
     const float4 uv = *reinterpret_cast<const float4*>(&us[kk * kTile + tc]);
+    const float4 evv = *reinterpret_cast<const float4*>(&es[kk * kEPitch + tr]);
     const float ub[4] = {uv.x, uv.y, uv.z, uv.w};
+    const float eb[4] = {evv.x, evv.y, evv.z, evv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float ev = es[(tr + i) * kEPitch + kk];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float p = ev * ub[jj];
+        const float p = eb[i] * ub[jj];
         acc[i][jj] = acc[i][jj] + p;
       }
     }
@@ -245,7 +297,7 @@ hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu,
   GptqBlockArgs a{w, u, scale, zero, q_hat, codes, err, ldw, ldu, lds, ldq, ldc, lde, rows, bc, i1,
                   group, qmin, qmax};
   const int64_t grid = (rows + kRowsPerWg - 1) / kRowsPerWg;
-  hipLaunchKernelGGL(gptq_block_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(gptq_block_kernel, dim3((unsigned)grid), dim3(kBlockThreads), 0, s, a);
   return hipGetLastError();
 }
 
