@@ -26,6 +26,10 @@ What it computes (all in numpy fp64 unless a storage format fixes the precision)
   upper Cholesky factor of H^-1, per-column quantize with error feedback, the lazy update (LLM
   Compressor 0.14, sections "The problem GPTQ solves" to "The fused kernel"), in fp64 for the
   algorithm's checks or fp32 with a fixed order of operations for parity with the GPU kernels.
+* ``sparse24``       -- 2:4 structured sparsity (module ``oracle.sparse24``): two kept 16-bit
+  values per group of four, position codes two per byte, and the dense matrix they stand for (Do
+  Quantization and Sparsity make LLM Inference Faster?, "Library 2:4 sparsity" and "Custom CUDA
+  2:4 GEMV").
 * ``dequant_*``      -- the decoded weights, exact in fp64.
 * ``gemv_reference`` -- y = x . W_hat^T and T = |x| . |W_hat|^T in fp64: the fused kernel only moves
   where dequantization happens (LLM Quantization on RTX 4060, section "Kernel Implementation"), so
