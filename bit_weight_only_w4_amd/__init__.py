@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
                                            vp, vp]
         L.w4_gptq_lazy_update.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
         L.w4_gptq_quantize.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, i64, vp, vp, vp, vp]
+        L.w4_sparse24_compress.argtypes = [vp, i64, i64, ci, vp, vp, vp]
+        L.w4_sparse24_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_smallbatch.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_prefill.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
@@ -82,7 +84,7 @@ def lib() -> ctypes.CDLL:
                      "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
                      "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped",
                      "w4_gemm_prefill", "w4_gptq_block_update", "w4_gptq_lazy_update",
-                     "w4_gptq_quantize"):
+                     "w4_gptq_quantize", "w4_sparse24_compress", "w4_sparse24_gemv"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -409,3 +411,38 @@ def gptq_lazy_update(w, u, err, col0, bcols, stream=None):
     rows, cols = w.shape
     check(lib().w4_gptq_lazy_update(_ptr(w), _ptr(u), _ptr(err), rows, cols, int(col0), int(bcols),
                                     _stream(stream)), "w4_gptq_lazy_update")
+
+
+S24_TYPES = {"f16": 0, "bf16": 1}
+
+
+def sparse24_compress(w, xtype="f16", stream=None):
+    """fp32 [N, K] device weights -> (values int16 [N, K/2] (16-bit bits of `xtype`), codes uint8
+    [N, K/8]) in the 2:4 format: the two largest magnitudes of every group of four kept."""
+    import torch
+
+    _need_cuda(w)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    n, k = w.shape
+    values = torch.empty((n, k // 2), dtype=torch.int16, device=w.device)
+    meta = torch.empty((n, max(k // 8, 1)), dtype=torch.uint8, device=w.device)
+    check(lib().w4_sparse24_compress(_ptr(w), n, k, S24_TYPES[xtype], _ptr(values), _ptr(meta),
+                                     _stream(stream)), "w4_sparse24_compress")
+    return values, meta
+
+
+def sparse24_gemv(x, values, meta, y=None, stream=None):
+    """y [B, N] fp32 = x [B, K] (fp16 or bf16) times the 2:4 matrix (values of x's type)."""
+    import torch
+
+    _need_cuda(x, values, meta)
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    xtype = {torch.float16: "f16", torch.bfloat16: "bf16"}[x2.dtype]
+    b, k = x2.shape
+    n = values.shape[0]
+    if y is None:
+        y = torch.empty((b, n), dtype=torch.float32, device=x.device)
+    check(lib().w4_sparse24_gemv(_ptr(x2), _ptr(values), _ptr(meta), S24_TYPES[xtype], n, k, b,
+                                 _ptr(y), _stream(stream)), "w4_sparse24_gemv")
+    return y

@@ -692,4 +692,38 @@ int w4_gptq_quantize(float* w, const float* u, const float* scale, const float* 
   return W4_OK;
 }
 
+int w4_sparse24_compress(const float* w, int64_t n, int64_t k, int xtype, uint16_t* values,
+                         uint8_t* meta, void* stream) {
+  if (!w || !values || !meta) return W4_ERR_NULL;
+  if (xtype != W4_S24_F16 && xtype != W4_S24_BF16) return W4_ERR_FORMAT;
+  if (n < 1 || k < 32 || k % 32 != 0 || k > 16384 || n >= kMaxDim) return W4_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(values, 16) || !aligned(meta, 4)) return W4_ERR_ALIGN;
+  const size_t wb = (size_t)(n * k) * 4, vb = (size_t)(n * k), mb = (size_t)(n * k / 8);
+  if (overlaps(w, wb, values, vb) || overlaps(w, wb, meta, mb) || overlaps(values, vb, meta, mb))
+    return W4_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (sparse24_error_reset(s) != hipSuccess) return W4_ERR_HIP;
+  if (launch_sparse24_compress(xtype, w, n, k, values, meta, s) != hipSuccess) return W4_ERR_HIP;
+  int flag = 0;
+  if (sparse24_error_read(&flag, s) != hipSuccess) return W4_ERR_HIP;
+  return flag ? W4_ERR_NONFINITE : W4_OK;
+}
+
+int w4_sparse24_gemv(const uint16_t* x, const uint16_t* values, const uint8_t* meta, int xtype,
+                     int64_t n, int64_t k, int64_t b, float* y, void* stream) {
+  if (!x || !values || !meta || !y) return W4_ERR_NULL;
+  if (xtype != W4_S24_F16 && xtype != W4_S24_BF16) return W4_ERR_FORMAT;
+  if (n < 1 || k < 32 || k % 32 != 0 || k > 16384 || n >= kMaxDim || b < 1 || b > 8)
+    return W4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(values, 16) || !aligned(meta, 4) || !aligned(y, 4))
+    return W4_ERR_ALIGN;
+  const size_t yb = (size_t)(b * n) * 4;
+  if (overlaps(y, yb, x, (size_t)(b * k) * 2) || overlaps(y, yb, values, (size_t)(n * k)) ||
+      overlaps(y, yb, meta, (size_t)(n * k / 8)))
+    return W4_ERR_ALIAS;
+  const hipError_t e = launch_sparse24_gemv(xtype, x, reinterpret_cast<const uint8_t*>(values),
+                                            meta, n, k, b, y, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
 }  // extern "C"

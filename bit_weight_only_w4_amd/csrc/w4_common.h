@@ -190,6 +190,14 @@ hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu,
                              int64_t ldc, float* err, int64_t lde, hipStream_t s);
 hipError_t launch_gptq_lazy(float* w, int64_t ldw, const float* err, int64_t lde, const float* u,
                             int64_t ldu, int64_t rows, int64_t cols, int bc, hipStream_t s);
+bool sparse24_plan(int64_t k, int* team, int* itm);
+hipError_t launch_sparse24_gemv(int xt, const uint16_t* x, const uint8_t* values,
+                                const uint8_t* meta, int64_t n, int64_t k, int64_t b, float* y,
+                                hipStream_t s);
+hipError_t launch_sparse24_compress(int xt, const float* w, int64_t n, int64_t k, uint16_t* values,
+                                    uint8_t* meta, hipStream_t s);
+hipError_t sparse24_error_reset(hipStream_t s);
+hipError_t sparse24_error_read(int* flag, hipStream_t s);
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 

@@ -316,6 +316,36 @@ int w4_gptq_quantize(float* w, const float* u, const float* scale, const float* 
                      int64_t cols, int64_t group, int qmin, int qmax, int64_t block, float* q_hat,
                      uint8_t* codes, float* err, void* stream);
 
+/* ------------------------------------------------------------------ 2:4 sparse GEMV -------- */
+
+/* 2:4 structured sparsity (Do Quantization and Sparsity make LLM Inference Faster?, "Library 2:4
+ * sparsity", "Custom CUDA 2:4 GEMV"): of every group of four weights along K two 16-bit values
+ * are kept, with a 4-bit code per group holding their positions (i0 | i1 << 2, i0 < i1); stored
+ * bytes are 56.25% of dense fp16.  Layout per row: values uint16[K/2] (the kept pair of group g at
+ * 2g, 2g + 1), codes uint8[K/8] (group g in byte g/2, even groups in the low nibble).  The values
+ * have the activations' 16-bit type. */
+typedef enum { W4_S24_F16 = 0, W4_S24_BF16 = 1 } w4_s24_type_t;
+
+/* w4_sparse24_compress: keep the two largest magnitudes of every group of four (the lower
+ * position on equal magnitudes), rounded to nearest even to `xtype`.
+ *   w       device float[N, K], read only; 16-byte aligned
+ *   N, K    N >= 1; K a positive multiple of 32, K <= 16384
+ *   values  device uint16[N, K/2], written; 16-byte aligned
+ *   meta    device uint8[N, K/8], written; 4-byte aligned
+ * Synchronizes `stream`.  Returns W4_ERR_NONFINITE if any weight is NaN or Inf. */
+int w4_sparse24_compress(const float* w, int64_t N, int64_t K, int xtype, uint16_t* values,
+                         uint8_t* meta, void* stream);
+
+/* w4_sparse24_gemv: y[b, n] = sum over groups of v0 x[b, 4g + i0] + v1 x[b, 4g + i1], fp32
+ * accumulation and output; the removed weights are never rebuilt.
+ *   x       device [B, K] activations of `xtype` (bits), 16-byte aligned
+ *   values, meta  as written by w4_sparse24_compress (alignment as there)
+ *   N, K    as there; 1 <= B <= 8 (each activation row streams the weights again)
+ *   y       device float[B, N], written, 4-byte aligned; must not overlap an input
+ * Asynchronous on `stream`; no allocation. */
+int w4_sparse24_gemv(const uint16_t* x, const uint16_t* values, const uint8_t* meta, int xtype,
+                     int64_t N, int64_t K, int64_t B, float* y, void* stream);
+
 /* ------------------------------------------------------------------ measurement probes ------ */
 
 /* Streaming-read ceiling probe: reads `bytes` (multiple of 16) from device `src` with 128-bit

@@ -267,3 +267,28 @@ def test_gptq_validation_codes():
     assert lazy(vp(G_SP), vp(G_SP * 2), None, 64, 256, 0, 128, None) == -1
     assert lazy(vp(G_SP), vp(G_SP * 2), vp(G_SP * 7), 64, 256, 192, 128, None) == -2
     assert lazy(vp(G_SP), vp(G_SP + 8), vp(G_SP * 7), 64, 256, 0, 128, None) == -9
+
+
+def test_sparse24_validation_codes():
+    _, L = _lib()
+    vp = ctypes.c_void_p
+    S = 1 << 24
+
+    def gemv(x=S, v=2 * S, m=3 * S, xt=0, n=64, k=256, b=1, y=4 * S):
+        return L.w4_sparse24_gemv(vp(x), vp(v), vp(m), xt, n, k, b, vp(y), None)
+
+    assert gemv(x=0) == -1
+    assert gemv(xt=2) == -4
+    assert gemv(k=48) == -2            # K % 32
+    assert gemv(k=16384 + 32) == -2    # longest row 16384
+    assert gemv(b=9) == -2
+    assert gemv(b=0) == -2
+    assert gemv(x=S + 8) == -3
+    assert gemv(m=3 * S + 2) == -3
+    assert gemv(y=2 * S + 64) == -9    # y overlaps the values
+    comp = L.w4_sparse24_compress
+    assert comp(None, 4, 64, 0, vp(2 * S), vp(3 * S), None) == -1
+    assert comp(vp(S), 4, 64, 5, vp(2 * S), vp(3 * S), None) == -4
+    assert comp(vp(S), 4, 40, 0, vp(2 * S), vp(3 * S), None) == -2
+    assert comp(vp(S + 4), 4, 64, 0, vp(2 * S), vp(3 * S), None) == -3
+    assert comp(vp(S), 4, 64, 0, vp(S + 16), vp(3 * S), None) == -9
