@@ -40,7 +40,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--suite", default="decode",
-                    choices=["decode", "shapes", "counters", "steps", "prefill", "gptq"],
+                    choices=["decode", "shapes", "counters", "steps", "prefill", "gptq", "sparse24"],
                     help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table; "
                          "counters: a few launches of each path, for rocprofv3 --pmc runs; "
                          "steps: the decode step in the other formats and at batch 8; "
@@ -828,6 +828,106 @@ def gptq_suite(args, dev):
     return res
 
 
+def sparse24_suite(args, dev):
+    """The 197-GEMV decode step at batch 1 with 2:4 sparse fp16 weights (Do Quantization and
+    Sparsity make LLM Inference Faster?, "Custom CUDA 2:4 GEMV"): every matrix compressed on the
+    GPU from N(0, 0.02) draws, the step captured as one HIP graph of 197 w4_sparse24_gemv
+    launches; per shape, the sparse GEMV against the fused NF4 GEMV and a dense fp16 GEMV of the
+    same shape (torch.matmul, for context), each timed as a graph over weight copies that exceed
+    the last-level cache.  Algorithmic bytes per sparse GEMV: 1.125 B per weight + x + y."""
+    import ctypes
+
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+    import synth_inputs
+
+    L = w4.lib()
+    vp = ctypes.c_void_p
+    shapes = synth_inputs.decode_step_shapes()
+    gen = torch.Generator(device=dev).manual_seed(7)
+    mats = []
+    for i, (name, n, k) in enumerate(shapes):
+        w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+        mats.append((n, k, *w4.sparse24_compress(w, "f16")))
+        del w
+    xs = {k: torch.randn(1, k, generator=gen, device=dev).to(torch.float16) for k in {k for _, _, k in shapes}}
+    ys = [torch.empty((1, n), device=dev) for _, n, _ in shapes]
+
+    def launch(i, stream):
+        n, k, v, m = mats[i]
+        w4.check(L.w4_sparse24_gemv(vp(xs[k].data_ptr()), vp(v.data_ptr()), vp(m.data_ptr()), 0, n,
+                                    k, 1, vp(ys[i].data_ptr()), vp(stream)), "w4_sparse24_gemv")
+
+    def graph_of(fn, count):
+        s0 = torch.cuda.Stream(device=dev)
+        s0.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s0):
+            for i in range(count):
+                fn(i, s0.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s0):
+            for i in range(count):
+                fn(i, s0.cuda_stream)
+        torch.cuda.synchronize()
+        return g
+
+    total = sum(n * k * 9 // 8 + 2 * k + 4 * n for _, n, k in shapes)
+    g = graph_of(launch, len(shapes))
+    ms = time_replays(g, args.steps, args.warmup)
+    del g
+    res = {"step": {"ms": round(ms, 5), "tok_s": round(1e3 / ms, 2), "launches": len(shapes),
+                    "algorithmic_bytes": total, "gbs": round(total / (ms / 1e3) / 1e9, 1)},
+           "shapes": []}
+    log(f"[s24] decode step (197 sparse GEMVs, B = 1): {ms * 1e3:.1f} us, {1e3 / ms:.1f} tok/s, "
+        f"{total / (ms / 1e3) / 1e9:.0f} GB/s")
+    del mats, ys
+    torch.cuda.empty_cache()
+    for name, n, k in [("q/o", 1536, 1536), ("k/v", 256, 1536), ("gate/up", 8960, 1536),
+                       ("down", 1536, 8960), ("lm_head", 151936, 1536)]:
+        per = n * k * 9 // 8
+        copies = max(2, min(64, (600 << 20) // per))
+        row = {"shape": name, "n": n, "k": k, "copies": copies}
+        sm = [w4.sparse24_compress(torch.randn(n, k, generator=gen, device=dev) * 0.02, "f16")
+              for _ in range(copies)]
+        x = xs[k]
+        yb = torch.empty((1, n), device=dev)
+
+        def ls(i, stream, sm=sm, n=n, k=k, x=x, yb=yb):
+            v, m = sm[i]
+            w4.check(L.w4_sparse24_gemv(vp(x.data_ptr()), vp(v.data_ptr()), vp(m.data_ptr()), 0, n, k,
+                                        1, vp(yb.data_ptr()), vp(stream)), "w4_sparse24_gemv")
+        g = graph_of(ls, copies)
+        us = time_replays(g, 20, 3) * 1e3 / copies
+        del g, sm
+        byt = per + 2 * k + 4 * n
+        row["sparse24_us"] = round(us, 3)
+        row["sparse24_gbs"] = round(byt / us / 1e3, 1)
+        t_nf4, _ = time_shape("nf4_f16", n, k, 1, "gemv", 0, dev, min_bytes=256 << 20, reps=3)
+        row["nf4_gemv_us"] = round(t_nf4, 3) if t_nf4 else None
+        dcopies = max(2, min(32, (600 << 20) // (n * k * 2)))
+        dw = [torch.randn(n, k, generator=gen, device=dev).to(torch.float16) for _ in range(dcopies)]
+        for _ in range(3):
+            for d in dw:
+                torch.matmul(x, d.t())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            for d in dw:
+                torch.matmul(x, d.t())
+        e1.record()
+        torch.cuda.synchronize()
+        row["fp16_dense_torch_us"] = round(e0.elapsed_time(e1) * 1e3 / (5 * dcopies), 3)
+        del dw
+        torch.cuda.empty_cache()
+        res["shapes"].append(row)
+        log(f"[s24] {name} {n}x{k}: sparse {row['sparse24_us']} us ({row['sparse24_gbs']} GB/s), "
+            f"NF4 GEMV {row['nf4_gemv_us']} us, fp16 dense {row['fp16_dense_torch_us']} us")
+    return res
+
+
 def shapes_suite(args, dev):
     """Per-shape table for the other workloads: INT4 decode steps (B = 1, 8) and split-K vs one
     pass on down; small-batch GEMM on gate / down / lm_head at B = 1, 8, 32, 128 for the GEMV,
@@ -1051,6 +1151,16 @@ def main():
                 json.dump(res, f, indent=1)
         print(json.dumps({"metric": "prefill step (512 tokens) and per-shape GEMM table",
                           "steps": res["steps"]}), flush=True)
+        return
+    if args.suite == "sparse24":
+        import torch
+
+        res = sparse24_suite(args, torch.device("cuda:0"))
+        if args.report:
+            with open(args.report, "w") as f:
+                json.dump(res, f, indent=1)
+        print(json.dumps({"metric": "2:4 sparse decode step (197 GEMVs, B=1)", **res["step"]}),
+              flush=True)
         return
     if args.suite == "gptq":
         import torch
