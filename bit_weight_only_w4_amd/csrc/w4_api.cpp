@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "w4_common.h"
 
@@ -651,6 +652,40 @@ int gptq_lazy(float* w, const float* u, const float* err, int64_t rows, int64_t 
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
+// The lazy update of block [col0, col0 + bcols) restricted to columns [c_begin, c_end).
+int gptq_lazy_range(float* w, const float* u, const float* err, int64_t rows, int64_t cols,
+                    int64_t col0, int64_t bcols, int64_t c_begin, int64_t c_end, hipStream_t s) {
+  if (c_begin >= c_end) return W4_OK;
+  const hipError_t e = launch_gptq_lazy(w + c_begin, cols, err + col0, cols, u + col0 * cols + c_begin,
+                                        cols, rows, c_end - c_begin, (int)bcols, s);
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+// Helper stream and events of w4_gptq_quantize on one device, created on the first call made
+// outside stream capture (default priority, non-blocking).
+struct GptqHelper {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false;
+};
+std::mutex g_gptq_mu;
+GptqHelper g_gptq_helper[64];
+
+GptqHelper* gptq_helper(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  GptqHelper& h = g_gptq_helper[dev];
+  if (h.ok) return &h;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (hipStreamCreateWithFlags(&h.side, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&h.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h.join, hipEventDisableTiming) != hipSuccess)
+    return nullptr;
+  h.ok = true;
+  return &h;
+}
+
 }  // namespace
 
 int w4_gptq_block_update(float* w, const float* u, const float* scale, const float* zero,
@@ -682,13 +717,48 @@ int w4_gptq_quantize(float* w, const float* u, const float* scale, const float* 
   if (st != W4_OK) return st;
   if (block < 1 || block > 128) return W4_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_gptq_mu);
+  // Small layers keep one stream: the extra launches and the stream hand-offs cost more than the
+  // overlap gains there (measured: q 1536 x 1536 and k 256 x 1536 slower, gate 8960 x 1536 and
+  // down 1536 x 8960 faster with the helper stream).
+  GptqHelper* h = rows * cols >= ((int64_t)1 << 23) ? gptq_helper(s) : nullptr;
+  if (!h) {
+    // one stream: each block, then its whole lazy update
+    for (int64_t c0 = 0; c0 < cols; c0 += block) {
+      const int64_t bc = std::min(block, cols - c0);
+      int r = gptq_block(w, u, scale, zero, rows, cols, group, qmin, qmax, c0, bc, q_hat, codes, err, s);
+      if (r != W4_OK) return r;
+      r = gptq_lazy(w, u, err, rows, cols, c0, bc, s);
+      if (r != W4_OK) return r;
+    }
+    return W4_OK;
+  }
+  // Two streams.  After block b, `s` updates only the next block's columns and goes on with the
+  // next block's kernel, while the helper stream updates the columns beyond: the latency-bound
+  // block kernel runs beside the lazy update.  Each column still takes the blocks' updates in
+  // block order (`s` waits for the helper's previous update before its next narrow update), and
+  // each update's arithmetic is unchanged, so the results are the same bits as on one stream.
+  bool pending = false;  // a helper update not yet waited for
   for (int64_t c0 = 0; c0 < cols; c0 += block) {
     const int64_t bc = std::min(block, cols - c0);
+    const int64_t i2 = c0 + bc, i3 = std::min(i2 + block, cols);
     int r = gptq_block(w, u, scale, zero, rows, cols, group, qmin, qmax, c0, bc, q_hat, codes, err, s);
     if (r != W4_OK) return r;
-    r = gptq_lazy(w, u, err, rows, cols, c0, bc, s);
+    if (i2 >= cols) break;
+    if (pending && hipStreamWaitEvent(s, h->join, 0) != hipSuccess) return W4_ERR_HIP;
+    pending = false;
+    if (i3 < cols) {
+      if (hipEventRecord(h->fork, s) != hipSuccess || hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
+        return W4_ERR_HIP;
+      r = gptq_lazy_range(w, u, err, rows, cols, c0, bc, i3, cols, h->side);
+      if (r != W4_OK) return r;
+      if (hipEventRecord(h->join, h->side) != hipSuccess) return W4_ERR_HIP;
+      pending = true;
+    }
+    r = gptq_lazy_range(w, u, err, rows, cols, c0, bc, i2, i3, s);
     if (r != W4_OK) return r;
   }
+  if (pending && hipStreamWaitEvent(s, h->join, 0) != hipSuccess) return W4_ERR_HIP;
   return W4_OK;
 }
 

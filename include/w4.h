@@ -311,7 +311,13 @@ int w4_gptq_lazy_update(float* w, const float* u, const float* err, int64_t rows
                         int64_t col0, int64_t bcols, void* stream);
 
 /* The whole column loop: for each block of `block` columns (1..128; the last one may be
- * narrower), w4_gptq_block_update then w4_gptq_lazy_update. */
+ * narrower), w4_gptq_block_update then w4_gptq_lazy_update.  For layers of 2^23 weights and more,
+ * after each block only the next block's columns are updated on `stream` and the columns beyond
+ * on a helper stream of the library, joined back into `stream` before the next narrow update and
+ * at the end (same results, bit for bit).  The helper stream and two events are created once per
+ * device on the first such call made outside stream capture (no device memory is allocated);
+ * until then, and for smaller layers, everything runs on `stream`.  Calls from several host
+ * threads are serialized while they enqueue. */
 int w4_gptq_quantize(float* w, const float* u, const float* scale, const float* zero, int64_t rows,
                      int64_t cols, int64_t group, int qmin, int qmax, int64_t block, float* q_hat,
                      uint8_t* codes, float* err, void* stream);

@@ -136,3 +136,44 @@ def test_gptq_codes_pack_into_the_int4_format():
 
     assert np.array_equal(oracle.dequant("int4", packed, sb), q_hat.cpu().numpy().astype(np.float64))
     assert torch.isfinite(y).all()
+
+
+def test_gptq_quantize_in_a_graph_replays_bitwise():
+    """w4_gptq_quantize captured in a HIP graph (its helper stream joins the capture) and replayed
+    three times, with eager work and synchronizations between replays: every replay gives the
+    eager call's bits."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    rows, cols, group = 4096, 2048, 128  # 2^23 weights: the two-stream schedule
+    w = synth_inputs.weights(rows, cols, seed=21)
+    u = synth_inputs.upper_factor(cols, seed=22)
+    s, z, qmin, qmax = _grid(w, group, True)
+    ud, sd, zd = _dev(u), _dev(s), _dev(z)
+    w_eager = _dev(w)
+    ref = w4.gptq_quantize(w_eager, ud, sd, zd, qmin, qmax, group=group, block=128)
+    pristine = _dev(w)
+    wg = pristine.clone()
+    q_hat, codes, err = w4.gptq_outputs(wg)
+    dev = g.device()
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        w4.check(w4.lib().w4_gptq_quantize(
+            w4._ptr(wg), w4._ptr(ud), w4._ptr(sd), w4._ptr(zd), rows, cols, group, qmin, qmax, 128,
+            w4._ptr(q_hat), w4._ptr(codes), w4._ptr(err), stream.cuda_stream), "capture")
+    for i in range(3):
+        wg.copy_(pristine)
+        q_hat.fill_(float("nan"))
+        err.fill_(float("nan"))
+        codes.fill_(255)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((q_hat, codes, err, wg), (*ref, w_eager)):
+            assert torch.equal(a, b), i
+        junk = torch.randn(1024, 1024, device=dev) @ torch.randn(1024, 1024, device=dev)
+        torch.cuda.synchronize()
+        del junk
