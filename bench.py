@@ -881,14 +881,31 @@ def sparse24_suite(args, dev):
         return g
 
     total = sum(n * k * 9 // 8 + 2 * k + 4 * n for _, n, k in shapes)
-    g = graph_of(launch, len(shapes))
-    ms = time_replays(g, args.steps, args.warmup)
-    del g
-    res = {"step": {"ms": round(ms, 5), "tok_s": round(1e3 / ms, 2), "launches": len(shapes),
-                    "algorithmic_bytes": total, "gbs": round(total / (ms / 1e3) / 1e9, 1)},
-           "shapes": []}
-    log(f"[s24] decode step (197 sparse GEMVs, B = 1): {ms * 1e3:.1f} us, {1e3 / ms:.1f} tok/s, "
-        f"{total / (ms / 1e3) / 1e9:.0f} GB/s")
+    res = {"shapes": []}
+    units = step_units(shapes, "grouped")
+    arr = ctypes.c_void_p
+
+    def launch_unit(j, stream):
+        u = units[j]
+        if len(u) == 1:
+            return launch(u[0], stream)
+        g_ = len(u)
+        k = mats[u[0]][1]
+        w4.check(L.w4_sparse24_gemv_grouped(
+            vp(xs[k].data_ptr()), g_, (arr * g_)(*[mats[i][2].data_ptr() for i in u]),
+            (arr * g_)(*[mats[i][3].data_ptr() for i in u]),
+            (ctypes.c_int64 * g_)(*[mats[i][0] for i in u]), 0, k, 1,
+            (arr * g_)(*[ys[i].data_ptr() for i in u]), vp(stream)), "w4_sparse24_gemv_grouped")
+
+    for sched, fn, count in (("grouped", launch_unit, len(units)), ("serial", launch, len(shapes))):
+        g = graph_of(fn, count)
+        ms = time_replays(g, args.steps, args.warmup)
+        del g
+        res[sched] = {"ms": round(ms, 5), "tok_s": round(1e3 / ms, 2), "launches": count,
+                      "algorithmic_bytes": total, "gbs": round(total / (ms / 1e3) / 1e9, 1)}
+        log(f"[s24] decode step, {sched} ({count} launches, B = 1): {ms * 1e3:.1f} us, "
+            f"{1e3 / ms:.1f} tok/s, {total / (ms / 1e3) / 1e9:.0f} GB/s")
+    res["step"] = res["grouped"]
     del mats, ys
     torch.cuda.empty_cache()
     for name, n, k in [("q/o", 1536, 1536), ("k/v", 256, 1536), ("gate/up", 8960, 1536),

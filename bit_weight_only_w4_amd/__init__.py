@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         L.w4_gptq_quantize.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, i64, vp, vp, vp, vp]
         L.w4_sparse24_compress.argtypes = [vp, i64, i64, ci, vp, vp, vp]
         L.w4_sparse24_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
+        L.w4_sparse24_gemv_grouped.argtypes = [vp, ci, vp, vp, vp, ci, i64, i64, vp, vp]
         L.w4_gemv.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_smallbatch.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
         L.w4_gemm_prefill.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, vp]
@@ -84,7 +85,8 @@ def lib() -> ctypes.CDLL:
                      "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
                      "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped",
                      "w4_gemm_prefill", "w4_gptq_block_update", "w4_gptq_lazy_update",
-                     "w4_gptq_quantize", "w4_sparse24_compress", "w4_sparse24_gemv"):
+                     "w4_gptq_quantize", "w4_sparse24_compress", "w4_sparse24_gemv",
+                     "w4_sparse24_gemv_grouped"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -446,3 +448,23 @@ def sparse24_gemv(x, values, meta, y=None, stream=None):
     check(lib().w4_sparse24_gemv(_ptr(x2), _ptr(values), _ptr(meta), S24_TYPES[xtype], n, k, b,
                                  _ptr(y), _stream(stream)), "w4_sparse24_gemv")
     return y
+
+
+def sparse24_gemv_grouped(x, values, meta, ys=None, stream=None):
+    """Several 2:4 matrices sharing x in one launch: returns [y_g] (fp32 [B, N_g])."""
+    import torch
+
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    _need_cuda(x2, *values, *meta)
+    xtype = {torch.float16: "f16", torch.bfloat16: "bf16"}[x2.dtype]
+    b, k = x2.shape
+    ns = [v.shape[0] for v in values]
+    if ys is None:
+        ys = [torch.empty((b, n), dtype=torch.float32, device=x.device) for n in ns]
+    g = len(values)
+    arr = ctypes.c_void_p * g
+    check(lib().w4_sparse24_gemv_grouped(
+        _ptr(x2), g, arr(*[v.data_ptr() for v in values]), arr(*[m.data_ptr() for m in meta]),
+        (ctypes.c_int64 * g)(*ns), S24_TYPES[xtype], k, b, arr(*[y.data_ptr() for y in ys]),
+        _stream(stream)), "w4_sparse24_gemv_grouped")
+    return ys

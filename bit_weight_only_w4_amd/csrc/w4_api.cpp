@@ -791,8 +791,42 @@ int w4_sparse24_gemv(const uint16_t* x, const uint16_t* values, const uint8_t* m
   if (overlaps(y, yb, x, (size_t)(b * k) * 2) || overlaps(y, yb, values, (size_t)(n * k)) ||
       overlaps(y, yb, meta, (size_t)(n * k / 8)))
     return W4_ERR_ALIAS;
-  const hipError_t e = launch_sparse24_gemv(xtype, x, reinterpret_cast<const uint8_t*>(values),
-                                            meta, n, k, b, y, reinterpret_cast<hipStream_t>(stream));
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(values);
+  const hipError_t e = launch_sparse24_gemv(xtype, x, 1, &vp, &meta, &n, &y, k, b,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+int w4_sparse24_gemv_grouped(const uint16_t* x, int groups, const uint16_t* const* values,
+                             const uint8_t* const* meta, const int64_t* N, int xtype, int64_t k,
+                             int64_t b, float* const* y, void* stream) {
+  if (!x || !values || !meta || !N || !y) return W4_ERR_NULL;
+  if (groups < 1 || groups > W4_MAX_GROUP) return W4_ERR_SHAPE;
+  if (xtype != W4_S24_F16 && xtype != W4_S24_BF16) return W4_ERR_FORMAT;
+  if (k < 32 || k % 32 != 0 || k > 16384 || b < 1 || b > 8) return W4_ERR_SHAPE;
+  if (!aligned(x, 16)) return W4_ERR_ALIGN;
+  int64_t total = 0;
+  const uint8_t* vps[W4_MAX_GROUP];
+  for (int g = 0; g < groups; ++g) {
+    if (!values[g] || !meta[g] || !y[g]) return W4_ERR_NULL;
+    if (N[g] < 1) return W4_ERR_SHAPE;
+    total += N[g];
+    if (!aligned(values[g], 16) || !aligned(meta[g], 4) || !aligned(y[g], 4)) return W4_ERR_ALIGN;
+    vps[g] = reinterpret_cast<const uint8_t*>(values[g]);
+  }
+  if (total >= kMaxDim) return W4_ERR_SHAPE;
+  for (int g = 0; g < groups; ++g) {
+    const size_t yb = (size_t)(b * N[g]) * 4;
+    if (overlaps(y[g], yb, x, (size_t)(b * k) * 2)) return W4_ERR_ALIAS;
+    for (int h = 0; h < groups; ++h) {
+      if (overlaps(y[g], yb, values[h], (size_t)(N[h] * k)) ||
+          overlaps(y[g], yb, meta[h], (size_t)(N[h] * k / 8)))
+        return W4_ERR_ALIAS;
+      if (h != g && overlaps(y[g], yb, y[h], (size_t)(b * N[h]) * 4)) return W4_ERR_ALIAS;
+    }
+  }
+  const hipError_t e = launch_sparse24_gemv(xtype, x, groups, vps, meta, N, y, k, b,
+                                            reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 

@@ -191,9 +191,9 @@ hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu,
 hipError_t launch_gptq_lazy(float* w, int64_t ldw, const float* err, int64_t lde, const float* u,
                             int64_t ldu, int64_t rows, int64_t cols, int bc, hipStream_t s);
 bool sparse24_plan(int64_t k, int* team, int* itm);
-hipError_t launch_sparse24_gemv(int xt, const uint16_t* x, const uint8_t* values,
-                                const uint8_t* meta, int64_t n, int64_t k, int64_t b, float* y,
-                                hipStream_t s);
+hipError_t launch_sparse24_gemv(int xt, const uint16_t* x, int groups, const uint8_t* const* values,
+                                const uint8_t* const* meta, const int64_t* ns, float* const* y,
+                                int64_t k, int64_t b, hipStream_t s);
 hipError_t launch_sparse24_compress(int xt, const float* w, int64_t n, int64_t k, uint16_t* values,
                                     uint8_t* meta, hipStream_t s);
 hipError_t sparse24_error_reset(hipStream_t s);

@@ -15,7 +15,8 @@
 // activations, whose selector is built from the 4-bit code, and one v_dot2 multiplies it with the
 // kept pair into fp32.  Team sums by DPP and cross-row shuffles; lane 0 of the team stores.
 // Activation row b of a batch is slice blockIdx.y: batches re-stream the weights (the page's
-// kernel is batch 1).
+// kernel is batch 1).  Up to four matrices that read the same activations run in one launch,
+// their row blocks numbered one after another.
 //
 // Compression: one thread per two groups (eight weights) keeps the two largest magnitudes of each
 // group (ties to the lower position), rounds them to the 16-bit type (nearest even) and writes
@@ -112,16 +113,26 @@ __device__ inline float s24_team_sum(float v, int team) {
   return v;
 }
 
+// One matrix of a launch; the members of a grouped launch share x and K, and their row blocks
+// are numbered one after another (member g owns row blocks [rb0_g, rb0_g + its row blocks)).
+struct S24Member {
+  const uint8_t* values;  // [N_g, K] bytes (K/2 16-bit values per row)
+  const uint8_t* meta;    // [N_g, K/8]
+  float* y;               // [B, N_g]
+  int64_t n;
+  int64_t rb0;
+};
+
 struct S24Args {
-  const uint16_t* x;    // [B, K]
-  const uint8_t* values;  // [N, K] bytes (K/2 16-bit values per row)
-  const uint8_t* meta;    // [N, K/8]
-  float* y;               // [B, N]
-  int64_t n, k;
+  S24Member m[kMaxGroup];
+  const uint16_t* x;      // [B, K]
+  int64_t k;
+  int64_t nrb;            // row blocks of all members
+  int groups;
   int team;
 };
 
-template <int XT, int ITM>
+template <int XT, int ITM, bool GROUPED>
 __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int team = a.team;
@@ -132,8 +143,19 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
   const int64_t k = a.k;
   const int cpr = (int)(k >> 5);  // 32-weight chunks per row
   const uint32_t vpitch = (uint32_t)k, mpitch = (uint32_t)(k >> 3);
-  const int64_t nrb = (a.n + rows_per_wg - 1) / rows_per_wg;
+  const int64_t nrb = a.nrb;
   const int b = blockIdx.y;
+  // The member owning row block rb (uniform), by selects over the fixed member slots.
+  auto member = [&](int64_t rb) {
+    S24Member r = a.m[0];
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int g = 1; g < kMaxGroup; ++g) {
+        if (g < a.groups && rb >= a.m[g].rb0) r = a.m[g];
+      }
+    }
+    return r;
+  };
 
   // this lane's activations: chunk c = tl + team * i, 32 values = 16 dwords each
   uint32_t xr[ITM][16];
@@ -159,12 +181,13 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
   // Row block rb's values and codes for this lane, through resources spanning the block's
   // existing rows (rows past N and chunks past the row read as zero).
   auto load = [&](int64_t rb, Buf& d) {
-    const int64_t row0 = rb * rows_per_wg;
-    const int64_t left = row0 < a.n ? a.n - row0 : 0;
+    const S24Member mm = member(rb);
+    const int64_t row0 = (rb - mm.rb0) * rows_per_wg;
+    const int64_t left = rb < nrb && row0 < mm.n ? mm.n - row0 : 0;
     const uint32_t rows = (uint32_t)(left < rows_per_wg ? left : rows_per_wg);
-    const int64_t r0 = row0 < a.n ? row0 : 0;
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.values + r0 * vpitch, rows * vpitch);
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + r0 * mpitch, rows * mpitch);
+    const int64_t r0 = left > 0 ? row0 : 0;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(mm.values + r0 * vpitch, rows * vpitch);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mm.meta + r0 * mpitch, rows * mpitch);
 #pragma unroll
     for (int i = 0; i < ITM; ++i) {
       const int c = tl + team * i;
@@ -199,8 +222,9 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
       }
     }
     acc = s24_team_sum(acc, team);
-    const int64_t row = rb * rows_per_wg + team_id;
-    if (tl == 0 && row < a.n) a.y[(int64_t)b * a.n + row] = acc;
+    const S24Member mm = member(rb);
+    const int64_t row = (rb - mm.rb0) * rows_per_wg + team_id;
+    if (tl == 0 && row < mm.n) mm.y[(int64_t)b * mm.n + row] = acc;
   };
 
   (void)lane;
@@ -217,11 +241,11 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
   }
 }
 
-template <int XT>
+template <int XT, bool GROUPED>
 hipError_t launch_itm(int itm, const S24Args& a, dim3 grid, hipStream_t s) {
   switch (itm) {
 #define W4_S24(I) \
-  case I: hipLaunchKernelGGL((s24_gemv_kernel<XT, I>), grid, dim3(kS24Threads), 0, s, a); break;
+  case I: hipLaunchKernelGGL((s24_gemv_kernel<XT, I, GROUPED>), grid, dim3(kS24Threads), 0, s, a); break;
     W4_S24(1) W4_S24(2) W4_S24(3) W4_S24(4) W4_S24(5) W4_S24(6) W4_S24(7) W4_S24(8)
 #undef W4_S24
     default: return hipErrorInvalidValue;
@@ -254,18 +278,30 @@ bool sparse24_plan(int64_t k, int* team, int* itm) {
   return true;
 }
 
-hipError_t launch_sparse24_gemv(int xt, const uint16_t* x, const uint8_t* values,
-                                const uint8_t* meta, int64_t n, int64_t k, int64_t b, float* y,
-                                hipStream_t s) {
+hipError_t launch_sparse24_gemv(int xt, const uint16_t* x, int groups, const uint8_t* const* values,
+                                const uint8_t* const* meta, const int64_t* ns, float* const* y,
+                                int64_t k, int64_t b, hipStream_t s) {
   int team = 0, itm = 0;
-  if (!sparse24_plan(k, &team, &itm)) return hipErrorInvalidValue;
+  if (groups < 1 || groups > kMaxGroup || !sparse24_plan(k, &team, &itm)) return hipErrorInvalidValue;
   const int64_t rows_per_wg = kS24Threads / team;
-  const int64_t nrb = (n + rows_per_wg - 1) / rows_per_wg;
+  S24Args a{};
+  int64_t nrb = 0;
+  for (int g = 0; g < groups; ++g) {
+    a.m[g] = S24Member{values[g], meta[g], y[g], ns[g], nrb};
+    nrb += (ns[g] + rows_per_wg - 1) / rows_per_wg;
+  }
+  for (int g = groups; g < kMaxGroup; ++g) a.m[g] = a.m[0];
+  a.x = x;
+  a.k = k;
+  a.nrb = nrb;
+  a.groups = groups;
+  a.team = team;
   const int64_t cap = (int64_t)device_cu_count() * 8;
   const int64_t gx = nrb < cap ? nrb : cap;
-  S24Args a{x, values, meta, y, n, k, team};
   const dim3 grid((unsigned)gx, (unsigned)b);
-  return xt == kF16 ? launch_itm<kF16>(itm, a, grid, s) : launch_itm<kBF16>(itm, a, grid, s);
+  if (groups > 1)
+    return xt == kF16 ? launch_itm<kF16, true>(itm, a, grid, s) : launch_itm<kBF16, true>(itm, a, grid, s);
+  return xt == kF16 ? launch_itm<kF16, false>(itm, a, grid, s) : launch_itm<kBF16, false>(itm, a, grid, s);
 }
 
 hipError_t launch_sparse24_compress(int xt, const float* w, int64_t n, int64_t k, uint16_t* values,

@@ -352,6 +352,22 @@ int w4_sparse24_compress(const float* w, int64_t N, int64_t K, int xtype, uint16
 int w4_sparse24_gemv(const uint16_t* x, const uint16_t* values, const uint8_t* meta, int xtype,
                      int64_t N, int64_t K, int64_t B, float* y, void* stream);
 
+/* w4_sparse24_gemv_grouped: G 2:4 matrices that read the same activations (a layer's q, k and v,
+ * or gate and up) in one launch, their row blocks one after another: y_g = x . W_g^T, each y_g
+ * bitwise what w4_sparse24_gemv gives on member g alone (the same per-row arithmetic and launch
+ * shape).  Fewer, fuller launches, as for w4_gemv_grouped.
+ *   x         device [B, K] of `xtype`, shared; 16-byte aligned
+ *   groups    G, 1 <= G <= W4_MAX_GROUP
+ *   values, meta, y   host arrays of G device pointers (member g: [N_g, K/2], [N_g, K/8],
+ *             float[B, N_g]; alignment as for w4_sparse24_gemv); no y_g may overlap another y_h or
+ *             any input
+ *   N         host array of G row counts, N_g >= 1, sum < 2^31
+ *   xtype, K, B   as for w4_sparse24_gemv, shared
+ * The host arrays are read during the call only.  Asynchronous on `stream`; no allocation. */
+int w4_sparse24_gemv_grouped(const uint16_t* x, int groups, const uint16_t* const* values,
+                             const uint8_t* const* meta, const int64_t* N, int xtype, int64_t K,
+                             int64_t B, float* const* y, void* stream);
+
 /* ------------------------------------------------------------------ measurement probes ------ */
 
 /* Streaming-read ceiling probe: reads `bytes` (multiple of 16) from device `src` with 128-bit

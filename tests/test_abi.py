@@ -292,3 +292,20 @@ def test_sparse24_validation_codes():
     assert comp(vp(S), 4, 40, 0, vp(2 * S), vp(3 * S), None) == -2
     assert comp(vp(S + 4), 4, 64, 0, vp(2 * S), vp(3 * S), None) == -3
     assert comp(vp(S), 4, 64, 0, vp(S + 16), vp(3 * S), None) == -9
+
+
+def test_sparse24_grouped_validation_codes():
+    _, L = _lib()
+    S = 1 << 24
+    arr = ctypes.c_void_p * 2
+    vals, meta, ys = arr(2 * S, 3 * S), arr(4 * S, 5 * S), arr(6 * S, 7 * S)
+    ns = (ctypes.c_int64 * 2)(64, 32)
+    f = L.w4_sparse24_gemv_grouped
+    vp = ctypes.c_void_p
+    assert f(vp(S), 0, vals, meta, ns, 0, 256, 1, ys, None) == -2
+    assert f(vp(S), 5, vals, meta, ns, 0, 256, 1, ys, None) == -2
+    assert f(vp(S), 2, vals, meta, ns, 3, 256, 1, ys, None) == -4
+    assert f(vp(S), 2, vals, meta, ns, 0, 250, 1, ys, None) == -2
+    assert f(vp(S), 2, arr(2 * S, 0), meta, ns, 0, 256, 1, ys, None) == -1
+    assert f(vp(S), 2, vals, meta, (ctypes.c_int64 * 2)(64, 0), 0, 256, 1, ys, None) == -2
+    assert f(vp(S), 2, vals, meta, ns, 0, 256, 1, arr(6 * S, 6 * S + 64), None) == -9  # y overlap

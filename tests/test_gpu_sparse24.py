@@ -131,3 +131,27 @@ def test_deterministic_and_overwrites():
     w4.sparse24_gemv(xd, v, m, y=y1)
     w4.sparse24_gemv(xd, v, m, y=y2)
     assert torch.equal(y1, y2) and not torch.isnan(y1).any()
+
+
+@pytest.mark.parametrize("xdt", XTYPES)
+@pytest.mark.parametrize("ns,k,b", [((1536, 256, 256), 1536, 1), ((8960, 8960), 1536, 1),
+                                    ((1, 7, 300, 65), 384, 2), ((129, 33), 8960, 1),
+                                    ((500,), 1024, 3)])
+def test_grouped_bitwise_equals_solo(xdt, ns, k, b):
+    """Each member of a grouped launch is bitwise the single-matrix call (same per-row arithmetic
+    and launch shape) and within the bound of the oracle; y buffers pre-filled with NaN."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    x = synth_inputs.activations(b, k, xdt, seed=k + b)
+    xd = g.to_dev_x(x, xdt)
+    members = []
+    for i, n in enumerate(ns):
+        w = synth_inputs.weights(n, k, seed=31 * i + n)
+        members.append(_compress_both(w, xdt))
+    ys = [torch.full((b, n), float("nan"), device=g.device()) for n in ns]
+    w4.sparse24_gemv_grouped(xd, [m[0] for m in members], [m[1] for m in members], ys=ys)
+    for (v, m, vr, mr), y in zip(members, ys):
+        assert torch.equal(y, w4.sparse24_gemv(xd, v, m))
+        _check_y(y, x, xdt, vr, mr)
