@@ -14,8 +14,10 @@
 // group one v_perm_b32 gathers the activation pair (x[i0], x[i1]) from the group's four
 // activations, whose selector is built from the 4-bit code, and one v_dot2 multiplies it with the
 // kept pair into fp32.  Team sums by DPP and cross-row shuffles; lane 0 of the team stores.
-// Activation row b of a batch is slice blockIdx.y: batches re-stream the weights (the page's
-// kernel is batch 1).  Up to four matrices that read the same activations run in one launch,
+// A lane holds BT activation rows (1, 2, 4 or 8, as its registers allow for the row length) and
+// multiplies each loaded weight group with all of them; slice blockIdx.y takes activation rows
+// [BT y, BT y + BT), so only batches larger than BT stream the weights again (the page's kernel
+// is batch 1).  Up to four matrices that read the same activations run in one launch,
 // their row blocks numbered one after another.
 //
 // Compression: one thread per two groups (eight weights) keeps the two largest magnitudes of each
@@ -127,12 +129,13 @@ struct S24Args {
   S24Member m[kMaxGroup];
   const uint16_t* x;      // [B, K]
   int64_t k;
+  int64_t b;              // activation rows; slice blockIdx.y takes rows [BT y, BT y + BT)
   int64_t nrb;            // row blocks of all members
   int groups;
   int team;
 };
 
-template <int XT, int ITM, bool GROUPED>
+template <int XT, int ITM, int BT, bool GROUPED>
 __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int team = a.team;
@@ -144,7 +147,8 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
   const int cpr = (int)(k >> 5);  // 32-weight chunks per row
   const uint32_t vpitch = (uint32_t)k, mpitch = (uint32_t)(k >> 3);
   const int64_t nrb = a.nrb;
-  const int b = blockIdx.y;
+  const int64_t b0 = (int64_t)blockIdx.y * BT;                  // this slice's first activation row
+  const int64_t nb = a.b - b0 < BT ? a.b - b0 : BT;             // its rows (1..BT)
   // The member owning row block rb (uniform), by selects over the fixed member slots.
   auto member = [&](int64_t rb) {
     S24Member r = a.m[0];
@@ -157,20 +161,24 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
     return r;
   };
 
-  // this lane's activations: chunk c = tl + team * i, 32 values = 16 dwords each
-  uint32_t xr[ITM][16];
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (int64_t)b * k, (uint32_t)(k * 2));
+  // this lane's activations: chunk c = tl + team * i of each of the slice's rows, 32 values =
+  // 16 dwords each (rows past B read as zero)
+  uint32_t xr[ITM][BT][16];
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + b0 * k, (uint32_t)(nb * k * 2));
 #pragma unroll
   for (int i = 0; i < ITM; ++i) {
     const int c = tl + team * i;
-    const uint32_t off = offset_or_oob(c < cpr, (uint32_t)c * 64u);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = buffer_load16(rx, off + 16u * q);
-      xr[i][4 * q] = v.x;
-      xr[i][4 * q + 1] = v.y;
-      xr[i][4 * q + 2] = v.z;
-      xr[i][4 * q + 3] = v.w;
+    for (int r = 0; r < BT; ++r) {
+      const uint32_t off = offset_or_oob(c < cpr, (uint32_t)(r * k + c * 32) * 2u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = buffer_load16(rx, off + 16u * q);
+        xr[i][r][4 * q] = v.x;
+        xr[i][r][4 * q + 1] = v.y;
+        xr[i][r][4 * q + 2] = v.z;
+        xr[i][r][4 * q + 3] = v.w;
+      }
     }
   }
 
@@ -199,7 +207,9 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
     }
   };
   auto compute_store = [&](int64_t rb, const Buf& d) {
-    float acc = 0.0f;
+    float acc[BT];
+#pragma unroll
+    for (int r = 0; r < BT; ++r) acc[r] = 0.0f;
 #pragma unroll
     for (int i = 0; i < ITM; ++i) {
       const uint32_t vals[8] = {d.v0[i].x, d.v0[i].y, d.v0[i].z, d.v0[i].w,
@@ -211,20 +221,26 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
         const uint32_t c = (md >> (4 * j)) & 15u;
         const uint32_t spread = ((c << 1) & 6u) | ((c << 15) & 0x60000u);
         const uint32_t sel = spread * 0x101u + 0x01000100u;
-        const uint32_t xp = __builtin_amdgcn_perm(xr[i][2 * j + 1], xr[i][2 * j], sel);
-        if (XT == kF16) {
-          acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(s24_half2, vals[j]),
-                                       __builtin_bit_cast(s24_half2, xp), acc, false);
-        } else {
-          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s24_bf162, vals[j]),
-                                                __builtin_bit_cast(s24_bf162, xp), acc, false);
+#pragma unroll
+        for (int r = 0; r < BT; ++r) {
+          const uint32_t xp = __builtin_amdgcn_perm(xr[i][r][2 * j + 1], xr[i][r][2 * j], sel);
+          if (XT == kF16) {
+            acc[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(s24_half2, vals[j]),
+                                            __builtin_bit_cast(s24_half2, xp), acc[r], false);
+          } else {
+            acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s24_bf162, vals[j]),
+                                                     __builtin_bit_cast(s24_bf162, xp), acc[r], false);
+          }
         }
       }
     }
-    acc = s24_team_sum(acc, team);
     const S24Member mm = member(rb);
     const int64_t row = (rb - mm.rb0) * rows_per_wg + team_id;
-    if (tl == 0 && row < mm.n) mm.y[(int64_t)b * mm.n + row] = acc;
+#pragma unroll
+    for (int r = 0; r < BT; ++r) {
+      const float v = s24_team_sum(acc[r], team);
+      if (tl == 0 && row < mm.n && r < nb) mm.y[(b0 + r) * mm.n + row] = v;
+    }
   };
 
   (void)lane;
@@ -241,30 +257,47 @@ __global__ void __launch_bounds__(kS24Threads) s24_gemv_kernel(S24Args a) {
   }
 }
 
-template <int XT, bool GROUPED>
+// Instantiations with ITM x BT <= 8 (activations in at most 128 registers per lane).
+template <int XT, int BT, bool GROUPED>
 hipError_t launch_itm(int itm, const S24Args& a, dim3 grid, hipStream_t s) {
   switch (itm) {
-#define W4_S24(I) \
-  case I: hipLaunchKernelGGL((s24_gemv_kernel<XT, I, GROUPED>), grid, dim3(kS24Threads), 0, s, a); break;
+#define W4_S24(I)                                                                              \
+  case I:                                                                                      \
+    if constexpr (I * BT <= kS24MaxItm) {                                                      \
+      hipLaunchKernelGGL((s24_gemv_kernel<XT, I, BT, GROUPED>), grid, dim3(kS24Threads), 0, s, a); \
+      return hipGetLastError();                                                                \
+    }                                                                                          \
+    break;
     W4_S24(1) W4_S24(2) W4_S24(3) W4_S24(4) W4_S24(5) W4_S24(6) W4_S24(7) W4_S24(8)
 #undef W4_S24
-    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
+}
+
+template <int XT, bool GROUPED>
+hipError_t launch_bt(int bt, int itm, const S24Args& a, dim3 grid, hipStream_t s) {
+  switch (bt) {
+    case 1: return launch_itm<XT, 1, GROUPED>(itm, a, grid, s);
+    case 2: return launch_itm<XT, 2, GROUPED>(itm, a, grid, s);
+    case 4: return launch_itm<XT, 4, GROUPED>(itm, a, grid, s);
+    case 8: return launch_itm<XT, 8, GROUPED>(itm, a, grid, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Team size and chunks per lane for a row of K weights: the team (16, 32, 64 lanes) whose chunk
-// slots (team x chunks per lane, at most 8 per lane) waste the fewest, the smaller team on ties.
-// Returns false when K needs more than 64 x 8 chunks.
-bool sparse24_plan(int64_t k, int* team, int* itm) {
+// Team size and chunks per lane for a row of K weights when a lane holds `bt` activation rows:
+// the team (16, 32, 64 lanes) whose chunk slots (team x chunks per lane, at most 8 / bt per lane)
+// waste the fewest, the smaller team on ties.  Returns false when K needs more slots.
+bool sparse24_plan_bt(int64_t k, int bt, int* team, int* itm) {
   const int64_t cpr = k / 32;
+  const int64_t max_itm = kS24MaxItm / bt;
   int best_t = 0, best_i = 0;
   int64_t best_waste = -1;
   for (int t = 16; t <= 64; t *= 2) {
     const int64_t i = (cpr + t - 1) / t;
-    if (i > kS24MaxItm) continue;
+    if (i > max_itm) continue;
     const int64_t waste = t * i - cpr;
     if (best_waste < 0 || waste < best_waste) {
       best_waste = waste;
@@ -278,11 +311,17 @@ bool sparse24_plan(int64_t k, int* team, int* itm) {
   return true;
 }
 
+bool sparse24_plan(int64_t k, int* team, int* itm) { return sparse24_plan_bt(k, 1, team, itm); }
+
 hipError_t launch_sparse24_gemv(int xt, const uint16_t* x, int groups, const uint8_t* const* values,
                                 const uint8_t* const* meta, const int64_t* ns, float* const* y,
                                 int64_t k, int64_t b, hipStream_t s) {
-  int team = 0, itm = 0;
-  if (groups < 1 || groups > kMaxGroup || !sparse24_plan(k, &team, &itm)) return hipErrorInvalidValue;
+  // activation rows per slice: the largest power of two <= B whose registers leave a plan
+  int team = 0, itm = 0, bt = 8;
+  while (bt > b) bt >>= 1;
+  while (bt > 1 && !sparse24_plan_bt(k, bt, &team, &itm)) bt >>= 1;
+  if (groups < 1 || groups > kMaxGroup || !sparse24_plan_bt(k, bt, &team, &itm))
+    return hipErrorInvalidValue;
   const int64_t rows_per_wg = kS24Threads / team;
   S24Args a{};
   int64_t nrb = 0;
@@ -293,15 +332,16 @@ hipError_t launch_sparse24_gemv(int xt, const uint16_t* x, int groups, const uin
   for (int g = groups; g < kMaxGroup; ++g) a.m[g] = a.m[0];
   a.x = x;
   a.k = k;
+  a.b = b;
   a.nrb = nrb;
   a.groups = groups;
   a.team = team;
   const int64_t cap = (int64_t)device_cu_count() * 8;
   const int64_t gx = nrb < cap ? nrb : cap;
-  const dim3 grid((unsigned)gx, (unsigned)b);
+  const dim3 grid((unsigned)gx, (unsigned)((b + bt - 1) / bt));
   if (groups > 1)
-    return xt == kF16 ? launch_itm<kF16, true>(itm, a, grid, s) : launch_itm<kBF16, true>(itm, a, grid, s);
-  return xt == kF16 ? launch_itm<kF16, false>(itm, a, grid, s) : launch_itm<kBF16, false>(itm, a, grid, s);
+    return xt == kF16 ? launch_bt<kF16, true>(bt, itm, a, grid, s) : launch_bt<kBF16, true>(bt, itm, a, grid, s);
+  return xt == kF16 ? launch_bt<kF16, false>(bt, itm, a, grid, s) : launch_bt<kBF16, false>(bt, itm, a, grid, s);
 }
 
 hipError_t launch_sparse24_compress(int xt, const float* w, int64_t n, int64_t k, uint16_t* values,

@@ -346,7 +346,9 @@ int w4_sparse24_compress(const float* w, int64_t N, int64_t K, int xtype, uint16
  * accumulation and output; the removed weights are never rebuilt.
  *   x       device [B, K] activations of `xtype` (bits), 16-byte aligned
  *   values, meta  as written by w4_sparse24_compress (alignment as there)
- *   N, K    as there; 1 <= B <= 8 (each activation row streams the weights again)
+ *   N, K    as there; 1 <= B <= 8 (a lane multiplies each weight group with up to 8, 4, 2 or 1
+ *           activation rows as its registers allow for the row length; larger batches stream the
+ *           weights once per such slice)
  *   y       device float[B, N], written, 4-byte aligned; must not overlap an input
  * Asynchronous on `stream`; no allocation. */
 int w4_sparse24_gemv(const uint16_t* x, const uint16_t* values, const uint8_t* meta, int xtype,
