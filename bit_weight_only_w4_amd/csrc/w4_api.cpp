@@ -678,10 +678,18 @@ GptqHelper* gptq_helper(hipStream_t s) {
   if (h.ok) return &h;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  if (hipStreamCreateWithFlags(&h.side, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  if (hipEventCreateWithFlags(&h.fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h.join, hipEventDisableTiming) != hipSuccess)
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (hipStreamCreateWithFlags(&side, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+    if (fork) (void)hipEventDestroy(fork);
+    (void)hipStreamDestroy(side);
     return nullptr;
+  }
+  h.side = side;
+  h.fork = fork;
+  h.join = join;
   h.ok = true;
   return &h;
 }
@@ -739,24 +747,30 @@ int w4_gptq_quantize(float* w, const float* u, const float* scale, const float* 
   // block order (`s` waits for the helper's previous update before its next narrow update), and
   // each update's arithmetic is unchanged, so the results are the same bits as on one stream.
   bool pending = false;  // a helper update not yet waited for
+  // on an error, `stream` still joins the helper's pending work (a capture stays well formed)
+  auto fail = [&](int code) {
+    if (pending) (void)hipStreamWaitEvent(s, h->join, 0);
+    return code;
+  };
   for (int64_t c0 = 0; c0 < cols; c0 += block) {
     const int64_t bc = std::min(block, cols - c0);
     const int64_t i2 = c0 + bc, i3 = std::min(i2 + block, cols);
     int r = gptq_block(w, u, scale, zero, rows, cols, group, qmin, qmax, c0, bc, q_hat, codes, err, s);
-    if (r != W4_OK) return r;
+    if (r != W4_OK) return fail(r);
     if (i2 >= cols) break;
-    if (pending && hipStreamWaitEvent(s, h->join, 0) != hipSuccess) return W4_ERR_HIP;
+    if (pending && hipStreamWaitEvent(s, h->join, 0) != hipSuccess) return fail(W4_ERR_HIP);
     pending = false;
     if (i3 < cols) {
       if (hipEventRecord(h->fork, s) != hipSuccess || hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
-        return W4_ERR_HIP;
+        return fail(W4_ERR_HIP);
       r = gptq_lazy_range(w, u, err, rows, cols, c0, bc, i3, cols, h->side);
-      if (r != W4_OK) return r;
+      // the helper has work from here on (even if this launch failed, the wait below is needed)
       if (hipEventRecord(h->join, h->side) != hipSuccess) return W4_ERR_HIP;
       pending = true;
+      if (r != W4_OK) return fail(r);
     }
     r = gptq_lazy_range(w, u, err, rows, cols, c0, bc, i2, i3, s);
-    if (r != W4_OK) return r;
+    if (r != W4_OK) return fail(r);
   }
   if (pending && hipStreamWaitEvent(s, h->join, 0) != hipSuccess) return W4_ERR_HIP;
   return W4_OK;
