@@ -1212,8 +1212,8 @@ def main():
                           "measured": len(ok), "report": args.report}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
-              "the multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (--gpus {args.gpus} requested); "
+              "multi-GPU sharding is described, not measured", file=sys.stderr)
         sys.exit(2)
     import torch
 
