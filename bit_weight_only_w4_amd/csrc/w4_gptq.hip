@@ -68,8 +68,8 @@ struct ColState {
   const float* ud;
 };
 
-// Column J of the block: quantize it in its owner lane (divide, add the zero point, clamp, round,
-// dequantize; e = (w - q_hat) / U_JJ), broadcast e over the 16-lane team, and subtract e U[J, c]
+// Column J of the block: quantize it in its owner lane (q = rint(clamp(w / s + z)),
+// q_hat = (q - z) s; e = (w - q_hat) / U_JJ), broadcast e over the 16-lane team, and subtract e U[J, c]
 // (product rounded, then the subtraction) from the lane's columns c > J.
 template <int J>
 __device__ __forceinline__ void column_step(ColState& st) {

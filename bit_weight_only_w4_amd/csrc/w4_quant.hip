@@ -12,14 +12,15 @@
 // -8, 7) against the rounded s, nibble = q + 8.  fp32(A / 7) is taken as the fp64 quotient rounded
 // to fp32, which equals the correctly rounded fp32 quotient (53 >= 2 * 24 + 2).
 //
-// Asymmetric INT4 (LLM Compressor 0.14, "The fused kernel": divide by the scale, add the zero
-// point, clamp, round; "Details worth knowing": rint): groups of 128, lo = min(min w, 0),
-// hi = max(max w, 0), s = bf16_RNE(fp32(fp32(hi - lo) / 15)), z = clamp(rint(-lo / s), 0, 15),
+// Asymmetric INT4 (LLM Compressor 0.14, "The fused kernel": a code is the clamped, rounded sum
+// of the scale quotient and the zero point; "Details worth knowing": rint): groups of 128,
+// lo = min(min w, 0), hi = max(max w, 0), s = bf16_RNE(fp32(fp32(hi - lo) / 15)), z = clamp(rint(-lo / s), 0, 15),
 // q = rint(clamp(w / s + z, 0, 15)), quotients in fp64 against the rounded s; the group's word is
 // the bf16 bits of s | z << 16.
 //
-// FP4 (LLM Compressor 0.14, "Details worth knowing": a ladder of thresholds onto the magnitudes
-// {0, 0.5, 1, 1.5, 2, 3, 4, 6}, alternating <= and < so that ties go to the even code): blocks of
+// FP4 (LLM Compressor 0.14, "Details worth knowing": rounding onto the magnitudes
+// {0, 0.5, 1, 1.5, 2, 3, 4, 6} by threshold comparisons whose <= and < alternate, exact ties
+// landing on even codes): blocks of
 // 64, s = fp32(A / 6) (the fp64 quotient rounded to fp32, as for INT4), magnitude index = the
 // ladder applied to the fp64 quotient |w| / s, sign bit = (w < 0); the thresholds are dyadic, so
 // the fp64 quotient of two fp32 values is on the same side of each as the exact ratio.
@@ -141,7 +142,7 @@ __global__ void __launch_bounds__(256) quant_int4_asym_kernel(const float* __res
     double zf = rint(-(double)lo / s);
     zf = zf < 0.0 ? 0.0 : (zf > 15.0 ? 15.0 : zf);
     z = (uint32_t)zf;
-    double q0 = (double)v.x / s + zf, q1 = (double)v.y / s + zf;  // divide, add the zero point
+    double q0 = (double)v.x / s + zf, q1 = (double)v.y / s + zf;  // w / s + z
     q0 = rint(q0 < 0.0 ? 0.0 : (q0 > 15.0 ? 15.0 : q0));        // clamp, round
     q1 = rint(q1 < 0.0 ? 0.0 : (q1 > 15.0 ? 15.0 : q1));
     n0 = (uint32_t)q0;

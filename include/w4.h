@@ -41,9 +41,9 @@ extern "C" {
  *         magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; LLM Compressor 0.14, "Details worth
  *         knowing"), blocks of 64 along K, one fp32 scale absmax / 6 per block,
  *         scales = float[N, K/64]; decoded weight = table[nibble] * scale.
- *   INT4A: asymmetric INT4 (LLM Compressor 0.14, "The fused kernel": divide by the scale, add
- *         the zero point, clamp, round; "What those numbers leave out": INT4 symmetric and
- *         asymmetric, grouped): nibble = unsigned code q in 0..15, groups of 128 along K,
+ *   INT4A: asymmetric INT4 (LLM Compressor 0.14, "The fused kernel": a code is the scale
+ *         quotient plus the zero point, clamped and rounded; "What those numbers leave out":
+ *         INT4 in symmetric and asymmetric grouped forms): nibble = unsigned code q in 0..15, groups of 128 along K,
  *         scales = uint32[N, K/128] words, bf16 scale bits in bits 0-15 and the zero point z
  *         (0..15) in bits 16-19, bits 20-31 zero; decoded weight = (q - z) * scale. */
 typedef enum {
@@ -140,8 +140,8 @@ int w4_quantize_int4_asym(const float* w, int64_t N, int64_t K, uint8_t* packed,
                           void* stream);
 
 /* w4_quantize_fp4: FP4 (E2M1) quantization, blocks of 64 along K (LLM Compressor 0.14: GPTQ's 15x
- * speedup is one fused loop, "Details worth knowing": the ladder of thresholds onto
- * {0, 0.5, 1, 1.5, 2, 3, 4, 6}, alternating <= and < so that ties go to the even code).
+ * speedup is one fused loop, "Details worth knowing": threshold comparisons onto
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6} whose <= and < alternate, so exact ties land on even codes).
  *   w      device float[N, K] (fp32), read only; 8-byte aligned
  *   N, K   N >= 1, K a positive multiple of 64
  *   packed device uint8[N, K/2], written; 16-byte aligned; element 2i in the high nibble

@@ -19,7 +19,7 @@ What it computes (all in numpy fp64 unless a storage format fixes the precision)
   one bf16 scale per 128-column group, code = rint(clamp(w / s + z, 0, 15)) (LLM Compressor
   0.14, sections "The fused kernel" and "What those numbers leave out").
 * ``quantize_fp4``   -- FP4 (E2M1) codes through a 16-entry table, block 64, fp32 scale
-  absmax / 6, the pages' ladder of thresholds with ties to the even code (LLM Compressor 0.14,
+  absmax / 6, the pages' threshold rounding with exact ties on even codes (LLM Compressor 0.14,
   section "Details worth knowing"; the FP4-named fused kernel of My Triton Kernel Ties
   bitsandbytes, section "The kernels").
 * ``gptq``           -- GPTQ's column loop with lazy blocks (module ``oracle.gptq``): dampening, the

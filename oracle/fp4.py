@@ -4,8 +4,8 @@ Test infrastructure only (see the package docstring).
 
 Sources:
   * LLM Compressor 0.14: GPTQ's 15x speedup is one fused loop, section "Details worth knowing"
-    (rounding per format): FP4 rounds through a ladder of thresholds onto the magnitudes
-    {0, 0.5, 1, 1.5, 2, 3, 4, 6}, the comparisons alternating <= and < so that a value exactly
+    (rounding per format): FP4 rounds onto the magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6} by
+    comparisons against fixed thresholds whose <= and < alternate, so that a value exactly
     between two magnitudes goes to the even code.
   * My Triton Kernel Ties bitsandbytes, section "The kernels": the fused kernel named for FP4
     decodes through a 16-entry fp32 codebook, code[nibble] times the block's scale, the same

@@ -16,9 +16,9 @@ Source: LLM Compressor 0.14: GPTQ's 15x speedup is one fused loop.
     those updates inside the block, collect the block's errors in E [rows x B], and then update
     the columns to the right once, W[:, i2:] -= E U[i1:i2, i2:]; dampening adds 1% of the mean
     diagonal to H, dead channels get diagonal 1 and zero weights.
-  * "The fused kernel": one program per (row tile) walks the block's columns: divide by the scale,
-    add the zero point, clamp, round, dequantize, e = (w - q) / U_jj, store q and e, subtract
-    e U_j,: from the columns to the right.  "Details worth knowing": INT rounding is rint, and the
+  * "The fused kernel": one program per row tile walks the block's columns; each column is
+    quantized (scale quotient plus zero point, clamped and rounded, then dequantized), its error
+    e = (w - q) / U_jj is kept with q, and e U_j,: comes off the columns to its right.  "Details worth knowing": INT rounding is rint, and the
     kernel avoids fused multiply-adds so that it matches the unfused eager loop bit for bit.
 
 Readings where the pages are silent (each listed in the design notes):
@@ -57,7 +57,7 @@ def inv_chol_upper(h: np.ndarray, percdamp: float = 0.01):
 
 
 def quantize_column(w, s, z, qmin, qmax, dtype):
-    """Divide by the scale, add the zero point, clamp, round, dequantize (all in ``dtype``).
+    """q = rint(clamp(w / s + z, qmin, qmax)) and q_hat = (q - z) s, every step in ``dtype``.
     Returns (q_hat, code) with code = q - qmin."""
     w = np.asarray(w, dtype=dtype)
     s = np.asarray(s, dtype=dtype)

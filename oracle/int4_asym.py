@@ -5,7 +5,7 @@ Test infrastructure only (see the package docstring).
 
 Sources:
   * LLM Compressor 0.14: GPTQ's 15x speedup is one fused loop, section "The fused kernel": a code
-    is made by dividing by the scale, adding the zero point, clamping and rounding, and decoded
+    is the clamped, rounded sum of the scale quotient and the zero point, and it is decoded
     from the same scale and zero point; section "Details worth knowing": INT rounding is ``rint``
     (round half to even); section "What those numbers leave out": INT4 is tested symmetric and
     asymmetric, grouped.
@@ -62,7 +62,7 @@ def quantize_int4_asym(w: np.ndarray):
     s_bits, z = int4_asym_scale_zero(lo, hi)
     s64 = bf16_bits_to_f64(s_bits)[..., None]
     safe = np.where(s64 > 0.0, s64, 1.0)
-    # divide by the scale, add the zero point, clamp, round
+    # w / s + z, clamped to the code range, then rounded half to even
     v = groups.astype(np.float64) / safe + z[..., None].astype(np.float64)
     q = np.rint(np.clip(v, 0.0, 15.0))
     q[np.broadcast_to(s64 == 0.0, q.shape)] = 0

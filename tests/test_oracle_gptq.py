@@ -114,7 +114,7 @@ def test_dead_channels():
 
 
 def test_quantize_column_rules():
-    # divide, add the zero point, clamp, round (half to even), dequantize; code = q - qmin
+    # q = rint(clamp(w / s + z)) (half to even), q_hat = (q - z) s; code = q - qmin
     w = np.array([0.5, 1.5, 2.5, -0.5, 100.0, -100.0, 0.0, 0.7])
     s = np.array([1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 0.0, 0.5])
     z = np.array([0.0, 0.0, 0.0, 3.0, 0.0, 0.0, 2.0, 1.0])

@@ -1,7 +1,7 @@
 """Pins of the oracle's asymmetric INT4 quantizer (CPU only).
 
-What the pages fix: a code is made by dividing by the scale, adding the zero point, clamping and
-rounding (LLM Compressor 0.14, section "The fused kernel"), integer rounding is rint, ties to even
+What the pages fix: a code is the scale quotient plus the zero point, clamped and rounded (LLM
+Compressor 0.14, section "The fused kernel"), integer rounding is rint, ties to even
 (same page, "Details worth knowing"), and INT4 comes symmetric and asymmetric, grouped (same page,
 "What those numbers leave out").  The rest is pinned by an exact-rational re-derivation that picks
 the nearest grid point by distance (a different formulation from the oracle's divide-add-round),
