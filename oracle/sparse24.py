@@ -6,8 +6,8 @@ Test infrastructure only (see the package docstring).
 Source: Do Quantization and Sparsity make LLM Inference Faster?, sections "Library 2:4 sparsity:
 fewer values, but too much overhead" and "Custom CUDA 2:4 GEMV" with its optional kernel
 walk-through:
-  * only two values of every group of four weights are kept, and metadata records their
-    positions; values and metadata take 56.25% of the dense fp16 bytes;
+  * each group of four weights keeps two values, with a small code giving the two positions;
+    values and codes together are 56.25% of the dense fp16 bytes;
   * per row the kept values are stored consecutively, two per group (K/2 16-bit values), and each
     group has a 4-bit code whose low two bits are the first kept position and next two bits the
     second; two codes share a byte, the even group in the low nibble (K/8 bytes per row);
