@@ -135,3 +135,32 @@ def test_grouped_at_prefill_batch(fmt):
     assert torch.equal(ys[0], w4.gemm_prefill(xd, packed[0], scales[0], fmt))
     for y, (pr, sr) in zip(ys, refs):
         g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("path,b", [("mfma", 16), ("mfma", 40), ("tiled", 128), ("tiled", 200)])
+def test_one_hot_columns_matrix_core_paths(fmt, path, b):
+    """Activation row i = e_{c_i}: y[i] is column c_i of the decoded matrix, up to the rounding of
+    the decoded code (fp16 NF4 codes: 3.3e-4 relative; the two-term bf16 split: 2^-16) and of the
+    fp32 product with the scale (2^-24); INT4 and asymmetric INT4 come out exact."""
+    import numpy as np
+
+    import oracle
+
+    import bit_weight_only_w4_amd as w4
+
+    n, k = 300, 1024
+    w = synth_inputs.weights(n, k, seed=77)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    w_hat = oracle.dequant(g.WFMT[fmt], pr, sr)
+    one = 0x3C00 if g.XDT[fmt] == "f16" else 0x3F80
+    cols = [(37 * i + 5) % k for i in range(b)]
+    x = np.zeros((b, k), dtype=np.uint16)
+    for i, c in enumerate(cols):
+        x[i, c] = one
+    y = w4.matmul_ex(g.to_dev_x(x, g.XDT[fmt]), p, s, fmt, path=path).cpu().numpy().astype(np.float64)
+    rtol = {"nf4_f16": 3.5e-4, "nf4_bf16": 2.0 ** -16 + 2.0 ** -23, "fp4_f16": 2.0 ** -23,
+            "fp4_bf16": 2.0 ** -23}.get(fmt, 0.0)
+    for i, c in enumerate(cols):
+        assert np.allclose(y[i], w_hat[:, c], rtol=rtol, atol=0), (i, c)
