@@ -96,7 +96,9 @@ def step_units(shapes, schedule):
 class Step:
     """The 197 GEMVs with their inputs resident in HBM and prebuilt C-ABI arguments."""
 
-    def __init__(self, fmt, b, path, dev):
+    def __init__(self, fmt, b, path, dev, layers=None, on_weight=None):
+        """`layers` decoder layers (all 28 by default) plus lm_head.  `on_weight(i, name, w)`, if
+        given, sees each fp32 weight matrix on the device before it is quantized and freed."""
         import ctypes
 
         import torch
@@ -105,7 +107,8 @@ class Step:
         import synth_inputs
 
         self.w4, self.fmt, self.b, self.path = w4, fmt, b, path
-        self.shapes = synth_inputs.decode_step_shapes()
+        self.shapes = synth_inputs.decode_step_shapes(
+            synth_inputs.QWEN15_LAYERS if layers is None else layers)
         self.fmt_id = w4.FORMATS[fmt]
         xdt = torch.float16 if fmt.endswith("_f16") else torch.bfloat16
         gen = torch.Generator(device=dev).manual_seed(7)
@@ -121,6 +124,8 @@ class Step:
                 seed = 1000 + 8 * layer + j
             g = torch.Generator(device=dev).manual_seed(seed)
             w = torch.randn(n, k, generator=g, device=dev) * synth_inputs.QWEN15_SIGMA
+            if on_weight is not None:
+                on_weight(i, name, w)
             packed, scales = w4.quantize(fmt, w)
             del w
             self.mats.append((packed, scales))

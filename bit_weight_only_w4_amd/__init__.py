@@ -80,13 +80,17 @@ def lib() -> ctypes.CDLL:
         L.w4_gemv_grouped_plan.argtypes = [ci, ci, ctypes.POINTER(i64), i64, i64, ip, ip, ip, ip, ip]
         L.w4_probe_read.argtypes = [vp, sz, vp, vp]
         L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
+        L.w4_set_path.argtypes = [ci]
+        L.w4_get_path.argtypes = []
+        L.w4_set_workspace.argtypes = [vp, sz]
         for name in ("w4_quantize_nf4", "w4_quantize_int4", "w4_quantize_fp4", "w4_quantize_int4_asym",
                      "w4_gemv", "w4_gemm_smallbatch", "w4_matmul_ex", "w4_auto_path",
                      "w4_gemv_plan", "w4_version", "w4_probe_read", "w4_probe_copy",
                      "w4_gemv_grouped", "w4_gemv_grouped_plan", "w4_gemm_smallbatch_grouped",
                      "w4_gemm_prefill", "w4_gptq_block_update", "w4_gptq_lazy_update",
                      "w4_gptq_quantize", "w4_sparse24_compress", "w4_sparse24_gemv",
-                     "w4_sparse24_gemv_grouped"):
+                     "w4_sparse24_gemv_grouped", "w4_set_path", "w4_get_path",
+                     "w4_set_workspace"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -345,6 +349,29 @@ def matmul_ex(x, packed, scales, fmt, path="auto", split_k=0, workspace=None, y=
                              PATHS[path], int(split_k), _ptr(workspace), wbytes, _stream(stream)),
           f"w4_matmul_ex[{path}]")
     return y
+
+
+def set_path(path) -> None:
+    """Override the automatic path of w4_gemv / w4_gemm_smallbatch ("auto" removes it)."""
+    check(lib().w4_set_path(PATHS[path] if isinstance(path, str) else int(path)), "w4_set_path")
+
+
+def get_path() -> str:
+    """The current override's name; raises if W4_FORCE_PATH held an unknown value."""
+    r = lib().w4_get_path()
+    if r < 0:
+        check(r, "w4_get_path")
+    return PATH_NAMES[r]
+
+
+def set_workspace(ws=None) -> None:
+    """Register a device tensor (or None to unregister) as the current device's workspace for
+    w4_gemv / w4_gemm_smallbatch.  The caller keeps the tensor alive while it is registered."""
+    if ws is None:
+        check(lib().w4_set_workspace(None, 0), "w4_set_workspace")
+    else:
+        _need_cuda(ws)
+        check(lib().w4_set_workspace(_ptr(ws), ws.numel() * ws.element_size()), "w4_set_workspace")
 
 
 def probe_read(src, sink, stream=None):

@@ -1,6 +1,7 @@
 // C ABI of the W4 library: host-side validation, path and launch-shape selection, dispatch.
 // Every check runs before any launch; nothing here allocates device memory or synchronizes a
 // stream except the quantizers (which read back the device-side non-finite flag).
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -36,6 +37,66 @@ struct CodebookInit {
 };
 const CodebookInit g_codebook;
 
+// The quantizers and the 2:4 compression report non-finite weights through one device-side word
+// each (per device), which a call resets, lets its kernel set, and reads back after synchronizing
+// its stream.  Calls on different streams would otherwise interleave those three steps and lose or
+// misattribute a flag, so the whole sequence runs under this lock (the calls synchronize anyway).
+std::mutex g_flag_mu;
+
+// Library settings that steer the automatic choices of w4_gemv and w4_gemm_smallbatch: a path
+// override (w4_set_path, or W4_FORCE_PATH read once when the library loads) and a workspace
+// registered per device (w4_set_workspace).  Guarded by g_settings_mu.
+constexpr int kMaxDevices = 64;
+struct Settings {
+  int path = W4_PATH_AUTO;  // W4_PATH_AUTO = no override
+  bool env_bad = false;     // W4_FORCE_PATH named no path: steered calls fail with W4_ERR_PATH
+  void* ws[kMaxDevices] = {};
+  size_t ws_bytes[kMaxDevices] = {};
+};
+std::mutex g_settings_mu;
+Settings g_settings;
+
+int parse_path_name(const char* v) {
+  static const char* const names[] = {"auto", "gemv", "splitk", "mfma", "twopass", "tiled"};
+  for (int i = 0; i < 6; ++i)
+    if (strcmp(v, names[i]) == 0) return i;
+  if (v[0] >= '0' && v[0] <= '5' && v[1] == 0) return v[0] - '0';
+  return -1;
+}
+
+struct EnvInit {
+  EnvInit() {
+    const char* v = getenv("W4_FORCE_PATH");
+    if (!v || !*v) return;
+    const int p = parse_path_name(v);
+    if (p < 0) {
+      g_settings.env_bad = true;
+    } else {
+      g_settings.path = p;
+    }
+  }
+};
+const EnvInit g_env_init;
+
+// The override and this device's registered workspace, read under the lock.
+struct Steer {
+  int path;
+  bool bad;
+  void* ws;
+  size_t ws_bytes;
+};
+Steer current_steer() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  std::lock_guard<std::mutex> lock(g_settings_mu);
+  Steer st{g_settings.path, g_settings.env_bad, nullptr, 0};
+  if (dev >= 0) {
+    st.ws = g_settings.ws[dev];
+    st.ws_bytes = g_settings.ws_bytes[dev];
+  }
+  return st;
+}
+
 bool valid_fmt(int fmt) {
   return fmt == W4_NF4_X_F16 || fmt == W4_NF4_X_BF16 || fmt == W4_INT4_X_F16 ||
          fmt == W4_INT4_X_BF16 || fmt == W4_FP4_X_F16 || fmt == W4_FP4_X_BF16 ||
@@ -69,6 +130,15 @@ int validate(const void* x, const uint8_t* packed, const void* scales, int fmt, 
       overlaps(y, ybytes, scales, sbytes))
     return W4_ERR_ALIAS;
   return W4_OK;
+}
+
+// Whether the `used` bytes a path writes into the workspace overlap x, the packed weights or the
+// scales (those kernels write partials or decoded weights while other workgroups still read them).
+bool workspace_overlaps_inputs(const void* ws, size_t used, const void* x, const uint8_t* packed,
+                               const void* scales, int fmt, int64_t n, int64_t k, int64_t b) {
+  const size_t sbytes = (size_t)(n * (k / fmt_group(fmt))) * fmt_scale_bytes(fmt);
+  return overlaps(ws, used, x, (size_t)(b * k) * 2) || overlaps(ws, used, packed, (size_t)(n * k / 2)) ||
+         overlaps(ws, used, scales, sbytes);
 }
 
 int next_pow2(int v) {
@@ -360,6 +430,7 @@ int w4_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* packed, float
       overlaps(packed, (size_t)(n * k / 2), absmax, (size_t)(n * k / 64) * 4))
     return W4_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_flag_mu);
   if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
   if (launch_quantize_nf4(w, n, k, packed, absmax, s) != hipSuccess) return W4_ERR_HIP;
   int flag = 0;
@@ -377,6 +448,7 @@ int w4_quantize_fp4(const float* w, int64_t n, int64_t k, uint8_t* packed, float
       overlaps(packed, (size_t)(n * k / 2), scale, (size_t)(n * k / 64) * 4))
     return W4_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_flag_mu);
   if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
   if (launch_quantize_fp4(w, n, k, packed, scale, s) != hipSuccess) return W4_ERR_HIP;
   int flag = 0;
@@ -394,6 +466,7 @@ int w4_quantize_int4_asym(const float* w, int64_t n, int64_t k, uint8_t* packed,
       overlaps(packed, (size_t)(n * k / 2), words, (size_t)(n * k / 128) * 4))
     return W4_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_flag_mu);
   if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
   if (launch_quantize_int4_asym(w, n, k, packed, words, s) != hipSuccess) return W4_ERR_HIP;
   int flag = 0;
@@ -411,6 +484,7 @@ int w4_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* packed, uint
       overlaps(packed, (size_t)(n * k / 2), scale, (size_t)(n * k / 128) * 2))
     return W4_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_flag_mu);
   if (quantize_error_reset(s) != hipSuccess) return W4_ERR_HIP;
   if (launch_quantize_int4(w, n, k, packed, scale, s) != hipSuccess) return W4_ERR_HIP;
   int flag = 0;
@@ -520,7 +594,10 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
       if (b > kMaxGemvBatch) return W4_ERR_PATH;
       if (split_k == 0) split_k = 4;
       if (split_k < 2 || split_k > W4_MAX_SPLIT_K || split_k > k / 32) return W4_ERR_PATH;
-      if (!workspace || workspace_bytes < splitk_bytes(n, b, split_k)) return W4_ERR_WORKSPACE;
+      const size_t used = splitk_bytes(n, b, split_k);
+      if (!workspace || workspace_bytes < used) return W4_ERR_WORKSPACE;
+      if (workspace_overlaps_inputs(workspace, used, x, packed, scales, fmt, n, k, b))
+        return W4_ERR_ALIAS;
       return run_gemv(x, packed, scales, fmt, n, k, b, y, split_k, workspace, s);
     }
     case W4_PATH_MFMA:
@@ -528,9 +605,9 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
     case W4_PATH_TILED:
       return run_tiled(x, packed, scales, fmt, n, k, b, y, s);
     case W4_PATH_TWOPASS: {
-      if (!workspace || workspace_bytes < (size_t)n * (size_t)k * 2) return W4_ERR_WORKSPACE;
-      if (overlaps(workspace, workspace_bytes, x, (size_t)(b * k) * 2) ||
-          overlaps(workspace, workspace_bytes, packed, (size_t)(n * k / 2)))
+      const size_t used = (size_t)n * (size_t)k * 2;
+      if (!workspace || workspace_bytes < used) return W4_ERR_WORKSPACE;
+      if (workspace_overlaps_inputs(workspace, used, x, packed, scales, fmt, n, k, b))
         return W4_ERR_ALIAS;
       return run_twopass(x, packed, scales, fmt, n, k, b, y, workspace, s);
     }
@@ -543,6 +620,11 @@ int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, i
   int st = validate(x, packed, scales, fmt, n, k, b, y);
   if (st != W4_OK) return st;
   if (b > kMaxGemvBatch) return W4_ERR_SHAPE;
+  const Steer steer = current_steer();
+  if (steer.bad) return W4_ERR_PATH;
+  if (steer.path != W4_PATH_AUTO)
+    return w4_matmul_ex(x, packed, scales, fmt, n, k, b, y, steer.path, 0, steer.ws, steer.ws_bytes,
+                        stream);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   GemvPlan p;
   if (!plan_gemv(n, k, (int)b, 1, &p)) return run_mfma(x, packed, scales, fmt, n, k, b, y, s);
@@ -573,7 +655,34 @@ int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* 
 
 int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
                        int64_t k, int64_t b, float* y, void* stream) {
-  return w4_matmul_ex(x, packed, scales, fmt, n, k, b, y, W4_PATH_AUTO, 0, nullptr, 0, stream);
+  const Steer steer = current_steer();
+  if (steer.bad) return W4_ERR_PATH;
+  return w4_matmul_ex(x, packed, scales, fmt, n, k, b, y, steer.path, 0, steer.ws, steer.ws_bytes,
+                      stream);
+}
+
+int w4_set_path(int path) {
+  if (path < W4_PATH_AUTO || path > W4_PATH_TILED) return W4_ERR_PATH;
+  std::lock_guard<std::mutex> lock(g_settings_mu);
+  g_settings.path = path;
+  g_settings.env_bad = false;
+  return W4_OK;
+}
+
+int w4_get_path(void) {
+  std::lock_guard<std::mutex> lock(g_settings_mu);
+  return g_settings.env_bad ? W4_ERR_PATH : g_settings.path;
+}
+
+int w4_set_workspace(void* workspace, size_t bytes) {
+  if (!workspace && bytes != 0) return W4_ERR_NULL;
+  if (workspace && !aligned(workspace, 16)) return W4_ERR_ALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W4_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_settings_mu);
+  g_settings.ws[dev] = workspace;
+  g_settings.ws_bytes[dev] = workspace ? bytes : 0;
+  return W4_OK;
 }
 
 int w4_gemm_prefill(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
@@ -786,6 +895,7 @@ int w4_sparse24_compress(const float* w, int64_t n, int64_t k, int xtype, uint16
   if (overlaps(w, wb, values, vb) || overlaps(w, wb, meta, mb) || overlaps(values, vb, meta, mb))
     return W4_ERR_ALIAS;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_flag_mu);
   if (sparse24_error_reset(s) != hipSuccess) return W4_ERR_HIP;
   if (launch_sparse24_compress(xtype, w, n, k, values, meta, s) != hipSuccess) return W4_ERR_HIP;
   int flag = 0;

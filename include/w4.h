@@ -18,8 +18,18 @@
  *     as W4_ERR_HIP.
  *   - Packed weights: uint8 [N, K/2]; byte i of a row holds element 2i in its high nibble and
  *     element 2i+1 in its low nibble (same page, "Kernel Implementation").
- *   - The library has no global mutable state except the quantizers' device-side error word;
- *     calls on different streams may run concurrently as long as their buffers do not overlap.
+ *   - Library state (everything that outlives a call):
+ *       . a path override and one registered workspace per device (w4_set_path, w4_set_workspace,
+ *         and the environment variable W4_FORCE_PATH, read once when the library is loaded); they
+ *         steer only w4_gemv and w4_gemm_smallbatch and are read under a lock at each call;
+ *       . one device-side non-finite flag word for the quantizers and one for the 2:4 compression
+ *         (per device); a call resets its word, launches, synchronizes and reads it back under a
+ *         host lock, so concurrent quantize or compress calls are serialized by the library;
+ *       . a helper stream and two events per device for w4_gptq_quantize on large layers,
+ *         created on first use and kept until the process ends;
+ *       . a cache of each device's compute-unit count (launch shapes).
+ *     Matmul calls on different streams may run concurrently as long as their buffers (and
+ *     workspaces) do not overlap.
  */
 #ifndef W4_H
 #define W4_H
@@ -154,6 +164,38 @@ int w4_quantize_fp4(const float* w, int64_t N, int64_t K, uint8_t* packed, float
 
 /* -------------------------------------------------------------------------- matmul --------- */
 
+/* ---------------------------------------------------------------- settings ----------------- */
+
+/* w4_set_path: a path override for the automatic choice of w4_gemv and w4_gemm_smallbatch (the
+ * wrapper's checks of LLM Quantization on RTX 4060, "Kernel Implementation", turned into a knob
+ * for tests and ablations; My Triton Kernel Ties bitsandbytes, "The kernels", bug 2: compare paths
+ * explicitly rather than trusting an automatic pick).  path = W4_PATH_AUTO removes the override.
+ * While an override is set, those two calls run w4_matmul_ex with that path, split_k = 0 and the
+ * workspace registered for the current device; a path that cannot run the arguments returns
+ * W4_ERR_PATH, a split-K or two-pass override without a large enough registered workspace returns
+ * W4_ERR_WORKSPACE.  Other entry points ignore the override.  The environment variable
+ * W4_FORCE_PATH (auto, gemv, splitk, mfma, twopass, tiled, or the digit 0-5) sets the same
+ * override once, when the library is loaded; an unknown value makes the steered calls return
+ * W4_ERR_PATH until w4_set_path is called.  Process-wide, not per thread: set it before launching
+ * work from other threads.  Returns W4_OK, or W4_ERR_PATH for an unknown path.  Host only; no
+ * allocation, no device call. */
+int w4_set_path(int path);
+
+/* The current override (a w4_path_t), or W4_ERR_PATH when W4_FORCE_PATH held an unknown value. */
+int w4_get_path(void);
+
+/* w4_set_workspace: registers caller-owned device memory for the current device, used by w4_gemv
+ * and w4_gemm_smallbatch when a path needs scratch (split-K partials, two-pass decoded weights).
+ *   workspace  device memory, 16-byte aligned, or NULL with bytes = 0 to unregister
+ *   bytes      its size
+ * The library keeps the pointer (it never frees it); the caller keeps the memory alive and unused
+ * by anything else while steered calls may run, and calls that share it must not overlap in time.
+ * Returns W4_OK, W4_ERR_NULL (NULL with bytes > 0), W4_ERR_ALIGN or W4_ERR_HIP (no current device).
+ * Host only; no allocation. */
+int w4_set_workspace(void* workspace, size_t bytes);
+
+/* ---------------------------------------------------------------- matmul ------------------- */
+
 /* w4_gemv: fused dequantize-and-multiply, y = x . W_hat^T, B <= 8 (decode; LLM Quantization on
  * RTX 4060, "Kernel Implementation": unpack, codebook, block scale, fp32 accumulation).
  *   x       device [B, K] fp16 or bf16 (per fmt) bit patterns; 16-byte aligned
@@ -162,7 +204,8 @@ int w4_quantize_fp4(const float* w, int64_t N, int64_t K, uint8_t* packed, float
  *   fmt     w4_format_t
  *   N, K, B N >= 1; K as for the format; 1 <= B <= 8
  *   y       device float[B, N]; fully overwritten, never accumulated into; must not overlap inputs
- * Single pass, no workspace.  Asynchronous on `stream`. */
+ * Single pass, no workspace (unless w4_set_path steers it to another path).  Asynchronous on
+ * `stream`. */
 int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t N,
             int64_t K, int64_t B, float* y, void* stream);
 
@@ -195,7 +238,8 @@ int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
  * batches").  Picks the fused GEMV for small B, the MFMA path (weights decoded on chip into
  * the matrix-core operands) for larger B, and the tiled GEMM from B = W4_TILED_FROM_BATCH when
  * N >= W4_TILED_FROM_ROWS; never materializes W_hat.  Arguments as for w4_gemv, with 1 <= B <= W4_MAX_BATCH.
- * No workspace.  Asynchronous. */
+ * No workspace unless one is registered (w4_set_workspace) and a path that needs it is chosen
+ * or forced (w4_set_path).  Asynchronous. */
 int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales, int fmt,
                        int64_t N, int64_t K, int64_t B, float* y, void* stream);
 
@@ -224,6 +268,8 @@ int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* 
 
 /* w4_matmul_ex: the same operation with an explicit path, split count and workspace (tests and
  * the ablation benchmark).  path = W4_PATH_AUTO also considers split-K when a workspace is given.
+ * The bytes a path writes into the workspace must not overlap x, packed, scales or y
+ * (W4_ERR_ALIAS).
  *   split_k          number of K ranges for W4_PATH_SPLITK (2..W4_MAX_SPLIT_K); 0 = library choice;
  *                    ignored by the other paths
  *   workspace        device memory of at least w4_workspace_bytes(...) bytes, 16-byte aligned;

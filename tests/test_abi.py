@@ -309,3 +309,76 @@ def test_sparse24_grouped_validation_codes():
     assert f(vp(S), 2, arr(2 * S, 0), meta, ns, 0, 256, 1, ys, None) == -1
     assert f(vp(S), 2, vals, meta, (ctypes.c_int64 * 2)(64, 0), 0, 256, 1, ys, None) == -2
     assert f(vp(S), 2, vals, meta, ns, 0, 256, 1, arr(6 * S, 6 * S + 64), None) == -9  # y overlap
+
+
+def test_path_override_and_workspace_registration():
+    """w4_set_path / w4_get_path / w4_set_workspace on the host: unknown paths are rejected, the
+    override steers w4_gemv and w4_gemm_smallbatch into w4_matmul_ex's checks (a forced split-K
+    or two-pass without a registered workspace fails before any launch), and registration checks
+    its pointer."""
+    w4, L = _lib()
+    vp = ctypes.c_void_p
+    try:
+        assert L.w4_set_path(9) == -7
+        assert L.w4_set_path(-1) == -7
+        for path in range(6):
+            assert L.w4_set_path(path) == 0
+            assert L.w4_get_path() == path
+        assert L.w4_set_path(2) == 0  # split-K, nothing registered on this host
+        assert _gemv(L) == -6
+        assert _gemv(L, x=0) == -1  # validation still comes first
+        assert L.w4_gemm_smallbatch(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 1,
+                                    vp(FAKE * 4), None) == -6
+        assert L.w4_set_path(4) == 0  # two-pass, no workspace
+        assert _gemv(L) == -6
+        assert L.w4_set_path(1) == 0  # the GEMV path has no launch shape for B = 9
+        assert L.w4_gemm_smallbatch(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 9,
+                                    vp(FAKE * 64), None) == -7
+        w4.set_path("auto")
+        assert w4.get_path() == "auto"
+        assert L.w4_set_workspace(None, 16) == -1
+        assert L.w4_set_workspace(vp(FAKE + 8), 64) == -3
+        # a registration needs a current device: W4_ERR_HIP on a host without one
+        st = L.w4_set_workspace(vp(FAKE), 64)
+        assert st in (0, -8)
+        assert L.w4_set_workspace(None, 0) in (0, -8)
+    finally:
+        L.w4_set_path(0)
+
+
+@pytest.mark.parametrize("value,expect", [("mfma", "3"), ("splitk", "2"), ("5", "5"),
+                                          ("bogus", "-7")])
+def test_force_path_environment_read_at_load(value, expect):
+    """W4_FORCE_PATH is read once when the library loads; an unknown name leaves every steered
+    call failing with W4_ERR_PATH (no silent default) until w4_set_path is called."""
+    import subprocess
+    import sys
+
+    code = ("import ctypes, bit_weight_only_w4_amd as w4; L = w4.lib(); vp = ctypes.c_void_p; "
+            "print(L.w4_get_path()); "
+            "print(L.w4_gemv(vp(0x10000), vp(0x20000), vp(0x30000), 1, 64, 256, 1, vp(0x40000), None)); "
+            "L.w4_set_path(0); print(L.w4_get_path())")
+    env = dict(os.environ, W4_FORCE_PATH=value)
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                         text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    got, gemv_status, after = out.stdout.split()
+    assert got == expect
+    if value == "bogus":
+        assert gemv_status == "-7"
+    assert after == "0"
+
+
+def test_workspace_must_not_overlap_inputs():
+    """A workspace that a path writes into may not overlap x, the packed weights or the scales."""
+    _, L = _lib()
+    vp = ctypes.c_void_p
+    x, p, s, y = FAKE, FAKE * 2, FAKE * 3, FAKE * 4  # n = 64, k = 256, b = 1: scales 1 KiB
+    splitk = 4 * 64 * 4
+    for ws in (x, p + 4096, s + 512):
+        assert L.w4_matmul_ex(vp(x), vp(p), vp(s), 1, 64, 256, 1, vp(y), 2, 4, vp(ws), splitk,
+                              None) == -9
+    twopass = 64 * 256 * 2
+    for ws in (s - twopass + 16, x - twopass + 16):
+        assert L.w4_matmul_ex(vp(x), vp(p), vp(s), 1, 64, 256, 1, vp(y), 4, 0, vp(ws), twopass,
+                              None) == -9

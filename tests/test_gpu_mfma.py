@@ -70,7 +70,8 @@ def test_mfma_deterministic(fmt):
                                        ("int4_f16", 1536, 8960, 8), ("int4_bf16", 8960, 1536, 32),
                                        ("nf4_f16", 28672, 8192, 16), ("fp4_f16", 8960, 1536, 32),
                                        ("fp4_bf16", 151936, 1536, 8), ("int4a_f16", 8960, 1536, 64),
-                                       ("int4a_bf16", 1536, 8960, 8)])
+                                       ("int4a_bf16", 1536, 8960, 8), ("int4_f16", 28672, 8192, 4),
+                                       ("int4a_bf16", 28672, 8192, 16)])
 def test_mfma_full_size_sampled(fmt, n, k, b):
     """Full-size matrices (persistent grids with several row tiles per workgroup, K groups, x
     windows in several phases): weights drawn on the GPU, quantized there, and 160 sampled rows

@@ -45,10 +45,10 @@ def test_tiled_odd_block_count(fmt):
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
-def test_tiled_scale_range_fallback(fmt):
-    """Rows whose block scales fall outside the range where fp16 holds every scaled code (tiny,
-    huge, and zero rows) next to ordinary rows: with fp16 activations their blocks take the exact
-    fp32 form, the others the folded fp16 form; all within the bound."""
+def test_tiled_scale_range(fmt):
+    """Rows whose block scales are tiny, huge or zero next to ordinary rows: the tiled kernel
+    applies every block scale in fp32 to that block's fresh partial sums, so the scale's range
+    never meets a 16-bit operand; all rows within the bound."""
     import numpy as np
 
     import bit_weight_only_w4_amd as w4
