@@ -3,110 +3,135 @@
 Test infrastructure only (see the package docstring).
 
 Source: LLM Compressor 0.14: GPTQ's 15x speedup is one fused loop.
-  * "The problem GPTQ solves": a layer W [rows x cols] is quantized onto a grid fixed beforehand
-    (a scale per row or per group), choosing grid points so as to keep the layer's output on the
-    calibration inputs X; the data enters only through H = X X^T.
-  * "One weight at a time: the Optimal Brain Surgeon update": rounding one weight, the other
-    weights not yet quantized absorb the error along the column of the inverse Hessian, divided by
-    its diagonal entry; the inverse then loses that row and column by one step of Gaussian
-    elimination.
-  * "Three changes that make it fast": one column order (left to right) for every row; the rows of
-    the eliminated inverses are the rows of U, the upper Cholesky factor of H^-1, so column j's
-    step is e = (w_j - q_j) / U_jj and w_{j+1:} -= e U_{j, j+1:}; lazy blocks of B columns apply
-    those updates inside the block, collect the block's errors in E [rows x B], and then update
-    the columns to the right once, W[:, i2:] -= E U[i1:i2, i2:]; dampening adds 1% of the mean
-    diagonal to H, dead channels get diagonal 1 and zero weights.
-  * "The fused kernel": one program per row tile walks the block's columns; each column is
-    quantized (scale quotient plus zero point, clamped and rounded, then dequantized), its error
-    e = (w - q) / U_jj is kept with q, and e U_j,: comes off the columns to its right.  "Details worth knowing": INT rounding is rint, and the
-    kernel avoids fused multiply-adds so that it matches the unfused eager loop bit for bit.
+  * "The problem GPTQ solves": a layer W [rows x cols] is rounded onto a grid fixed beforehand (a
+    scale per row or per group) so as to keep the layer's output on calibration inputs X; the data
+    enters only through H = X X^T.
+  * "One weight at a time: the Optimal Brain Surgeon update": after one weight is rounded, the
+    weights not yet rounded absorb its error along that weight's row of the inverse Hessian,
+    divided by the row's diagonal entry, and the inverse loses that row and column by one step of
+    Gaussian elimination.
+  * "Three changes that make it fast": every row takes the columns in one order (left to right);
+    the successive eliminated inverses' rows, divided by the square root of their diagonal, are
+    the rows of U, the upper triangular factor with H^-1 = U^T U, so column j's error is
+    (w_j - q_j) / U_jj and column c > j takes that error times U_jc off its weight; within a lazy
+    block those updates are applied one column at a time, and each block's errors reach the
+    columns to its right in one accumulated update; dampening adds 1% of the mean diagonal to H,
+    and dead channels (diagonal 0) get diagonal 1 and zero weights.
+  * "The fused kernel" gives the order of one column's steps (scale quotient, zero point, clamp,
+    rounding, dequantization, error); "Details worth knowing": integer rounding is rint, and the
+    fused kernel avoids fused multiply-adds so that its bits match the unfused loop.
 
 Readings where the pages are silent (each listed in the design notes):
   * The grid is given per row and group: scale s[r, g] and zero point z[r, g] (fp), integer range
-    [qmin, qmax]; group g of column j is j // group.  q = rint(clamp(w / s + z, qmin, qmax)),
+    [qmin, qmax]; column j belongs to group j // group.  q = rint(clamp(w / s + z, qmin, qmax)),
     q_hat = (q - z) * s; the stored code is q - qmin.  A group with s == 0 takes w / s as 0.
-  * ``dtype`` fixes the arithmetic of the column loop: float64 for the algorithm-level checks,
-    float32 for parity with the GPU kernels, which take every rounding decision in fp32 with the
-    same order of operations (each product rounded, then the subtraction; no fused multiply-add).
-  * The lazy update's sum over the block's columns runs in column order:
-    t = sum_{c = i1 .. i2-1} E[:, c] U[c, i2:] (each product rounded, then added), W -= t.
+  * ``dtype`` fixes the arithmetic: float64 for the algorithm-level checks, float32 for parity
+    with the GPU kernels, which round every product before subtracting it (no fused multiply-add).
+  * Order of the subtractions reaching column c (inside block k): first one correction per earlier
+    block, in block order, each the sum over that block's columns in column order (every product
+    rounded, the sum started from +0 and rounded after each addition); then the corrections of
+    block k's earlier columns one at a time, in column order.
+
+Structure: ``inverse_factor`` builds U by the Gaussian elimination the OBS section describes;
+``grid_point`` is one quantization step; ``gptq`` walks the blocks, solving each block column by
+column from the left (each column gathers the corrections of the block's earlier columns just before
+it is rounded) and then handing the block's accumulated correction to every column to its right.
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def dampen(h: np.ndarray, percdamp: float = 0.01):
-    """H plus percdamp times its mean diagonal on the diagonal; dead channels (diagonal 0) get
-    diagonal 1.  Returns (H_damped, dead mask)."""
-    h = np.array(h, dtype=np.float64, copy=True)
-    dead = np.diag(h) == 0
-    h[dead, dead] = 1.0
-    h[np.diag_indices_from(h)] += percdamp * np.mean(np.diag(h))
-    return h, dead
+def dampened(h: np.ndarray, damp: float = 0.01):
+    """(H with dead channels set to diagonal 1 and ``damp`` times the mean diagonal added to the
+    diagonal, dead-channel mask), fp64."""
+    hd = np.array(h, dtype=np.float64, copy=True)
+    diag = np.diagonal(hd).copy()
+    dead = diag == 0
+    diag[dead] = 1.0
+    diag = diag + damp * float(np.mean(diag))
+    np.fill_diagonal(hd, diag)
+    return hd, dead
 
 
-def inv_chol_upper(h: np.ndarray, percdamp: float = 0.01):
-    """U, the upper Cholesky factor of the inverse of the dampened H (H^-1 = U^T U), in fp64.
-    Raises numpy.linalg.LinAlgError when the dampened H is not positive definite."""
-    hd, _ = dampen(h, percdamp)
-    lower = np.linalg.cholesky(hd)                # H = L L^T
-    linv = np.linalg.inv(lower)
-    hinv = linv.T @ linv                           # H^-1 = L^-T L^-1
-    return np.linalg.cholesky(hinv).T              # upper: H^-1 = U^T U
+def inverse_factor(h: np.ndarray, damp: float = 0.01) -> np.ndarray:
+    """U [cols x cols], upper triangular with H_d^-1 = U^T U (H_d = the dampened H), built as the
+    OBS section states it: row j of U is row j of the inverse after eliminating columns 0..j-1,
+    from column j on, divided by the square root of its diagonal entry.  fp64.  Raises
+    numpy.linalg.LinAlgError when H_d is not positive definite (its smallest eigenvalue at most
+    cols * eps times its largest) or an eliminated diagonal is not positive."""
+    hd, _ = dampened(h, damp)
+    eig = np.linalg.eigvalsh(hd)
+    if not eig[0] > hd.shape[0] * np.finfo(np.float64).eps * eig[-1]:
+        raise np.linalg.LinAlgError("dampened H is not positive definite")
+    cur = np.linalg.inv(hd)
+    n = cur.shape[0]
+    out = np.zeros_like(cur)
+    for j in range(n):
+        pivot = cur[j, j]
+        if not pivot > 0:
+            raise np.linalg.LinAlgError(f"eliminated inverse not positive definite at column {j}")
+        out[j, j:] = cur[j, j:] / np.sqrt(pivot)
+        # drop column j from the inverse: one step of Gaussian elimination
+        cur = cur - np.outer(cur[:, j], cur[j, :]) / pivot
+    return out
 
 
-def quantize_column(w, s, z, qmin, qmax, dtype):
-    """q = rint(clamp(w / s + z, qmin, qmax)) and q_hat = (q - z) s, every step in ``dtype``.
-    Returns (q_hat, code) with code = q - qmin."""
+def grid_point(w, s, z, qmin, qmax, dtype):
+    """One quantization step in ``dtype``: v = w / s (0 where s == 0), v + z, clamped to
+    [qmin, qmax], rounded half to even; q_hat = (q - z) * s.  Returns (q_hat, code = q - qmin)."""
     w = np.asarray(w, dtype=dtype)
     s = np.asarray(s, dtype=dtype)
     z = np.asarray(z, dtype=dtype)
-    safe = np.where(s != 0, s, dtype(1))
-    v = np.where(s != 0, w / safe, dtype(0))
-    v = v + z
-    v = np.minimum(np.maximum(v, dtype(qmin)), dtype(qmax))
-    q = np.rint(v)
+    ratio = np.divide(w, s, out=np.zeros_like(w), where=(s != 0))
+    shifted = np.clip(ratio + z, dtype(qmin), dtype(qmax))
+    q = np.rint(shifted)
     q_hat = (q - z) * s
     return q_hat.astype(dtype), (q - qmin).astype(np.int64)
 
 
 def gptq(w, u, scale, zero, qmin, qmax, group=None, block=128, dtype=np.float64, dead=None):
-    """Quantize W [rows x cols] column by column with error feedback through U (upper, cols x cols),
-    lazy blocks of ``block`` columns.  scale, zero: [rows, cols // group] (group defaults to cols:
-    one grid per row).  Returns dict(q_hat, codes, err, w_final) where err[:, j] is column j's
-    e = (w_j - q_j) / U_jj and w_final the weights after every update."""
-    dtype = np.dtype(dtype).type
-    w = np.array(w, dtype=dtype, copy=True)
-    u = np.asarray(u, dtype=dtype)
-    rows, cols = w.shape
+    """Round W [rows x cols] column by column with error feedback through U (upper, cols x cols),
+    in lazy blocks of ``block`` columns.  scale, zero: [rows, cols // group] (group defaults to
+    cols: one grid per row).  Returns dict(q_hat, codes, err, w_final): err[:, j] = (v_j - q_hat_j)
+    / U_jj where v_j is column j as it stands when it is rounded, and w_final[:, j] = v_j."""
+    dt = np.dtype(dtype).type
+    cur = np.array(w, dtype=dt, copy=True)  # columns not yet rounded receive corrections here
+    u = np.asarray(u, dtype=dt)
+    rows, cols = cur.shape
     group = cols if group is None else group
-    scale = np.asarray(scale, dtype=dtype).reshape(rows, -1)
-    zero = np.asarray(zero, dtype=dtype).reshape(rows, -1)
-    if scale.shape[1] != cols // group or cols % group:
+    if cols % group:
+        raise ValueError("cols must be a multiple of group")
+    scale = np.asarray(scale, dtype=dt).reshape(rows, -1)
+    zero = np.asarray(zero, dtype=dt).reshape(rows, -1)
+    if scale.shape[1] != cols // group or zero.shape != scale.shape:
         raise ValueError("scale / zero must be [rows, cols // group]")
     if dead is not None:
-        w[:, dead] = 0
-    q_hat = np.zeros_like(w)
+        cur[:, np.asarray(dead, dtype=bool)] = 0
+    q_hat = np.zeros_like(cur)
     codes = np.zeros((rows, cols), dtype=np.int64)
-    err = np.zeros_like(w)
-    for i1 in range(0, cols, block):
-        i2 = min(i1 + block, cols)
-        for j in range(i1, i2):
-            g = j // group
-            q_hat[:, j], codes[:, j] = quantize_column(w[:, j], scale[:, g], zero[:, g], qmin, qmax,
-                                                       dtype)
-            e = (w[:, j] - q_hat[:, j]) / u[j, j]
-            err[:, j] = e
-            # rank-one update of the block's columns to the right (product rounded, then the
-            # subtraction)
-            w[:, j + 1:i2] = w[:, j + 1:i2] - np.outer(e, u[j, j + 1:i2])
-        if i2 < cols:
-            t = np.zeros((rows, cols - i2), dtype=dtype)
-            for c in range(i1, i2):
-                t = t + np.outer(err[:, c], u[c, i2:])
-            w[:, i2:] = w[:, i2:] - t
-    return {"q_hat": q_hat, "codes": codes, "err": err, "w_final": w}
+    err = np.zeros_like(cur)
+
+    for start in range(0, cols, block):
+        stop = min(start + block, cols)
+        # inside the block: each column takes the corrections of the block's earlier columns, one
+        # at a time in column order, then is rounded and yields its own error
+        for c in range(start, stop):
+            v = cur[:, c]
+            for prev in range(start, c):
+                v = v - err[:, prev] * u[prev, c]
+            cur[:, c] = v
+            gi = c // group
+            q_hat[:, c], codes[:, c] = grid_point(v, scale[:, gi], zero[:, gi], qmin, qmax, dt)
+            err[:, c] = (v - q_hat[:, c]) / u[c, c]
+        # the block's correction of every column to its right, summed over the block's columns
+        # in column order from +0, subtracted once
+        if stop < cols:
+            corr = np.zeros((rows, cols - stop), dtype=dt)
+            for prev in range(start, stop):
+                corr = corr + err[:, prev:prev + 1] * u[prev:prev + 1, stop:]
+            cur[:, stop:] = cur[:, stop:] - corr
+    return {"q_hat": q_hat, "codes": codes, "err": err, "w_final": cur}
 
 
 def rtn(w, scale, zero, qmin, qmax, group=None, dtype=np.float64):
@@ -116,8 +141,8 @@ def rtn(w, scale, zero, qmin, qmax, group=None, dtype=np.float64):
     group = cols if group is None else group
     scale = np.asarray(scale, dtype=dtype).reshape(rows, -1)
     zero = np.asarray(zero, dtype=dtype).reshape(rows, -1)
-    g = np.arange(cols) // group
-    return quantize_column(w, scale[:, g], zero[:, g], qmin, qmax, np.dtype(dtype).type)
+    gi = np.arange(cols) // group
+    return grid_point(w, scale[:, gi], zero[:, gi], qmin, qmax, np.dtype(dtype).type)
 
 
 def proxy_loss(w, q_hat, h):

@@ -23,15 +23,15 @@ def _layer(rows, cols, tokens, corr, seed):
     return w, h, s, np.zeros_like(s), x
 
 
-def _obs(w, h, s, z, qmin, qmax, percdamp=0.01):
+def _obs(w, h, s, z, qmin, qmax, damp=0.01):
     """Explicit OBS: quantize column j, spread (w_j - q_j) / [H_F^-1]_jj along row j of H_F^-1 to
     the columns not yet quantized, then remove j from H_F^-1 by one Gaussian elimination step."""
     w = np.array(w, dtype=np.float64, copy=True)
-    hd, _ = G.dampen(h, percdamp)
+    hd, _ = G.dampened(h, damp)
     hinv = np.linalg.inv(hd)
     codes = np.zeros(w.shape, dtype=np.int64)
     for j in range(w.shape[1]):
-        qh, codes[:, j] = G.quantize_column(w[:, j], s[:, 0], z[:, 0], qmin, qmax, np.float64)
+        qh, codes[:, j] = G.grid_point(w[:, j], s[:, 0], z[:, 0], qmin, qmax, np.float64)
         err = (w[:, j] - qh) / hinv[j, j]
         w[:, j + 1:] -= np.outer(err, hinv[j, j + 1:])
         hinv = hinv - np.outer(hinv[:, j], hinv[j, :]) / hinv[j, j]
@@ -40,23 +40,20 @@ def _obs(w, h, s, z, qmin, qmax, percdamp=0.01):
 
 def test_u_is_the_upper_cholesky_factor_of_the_dampened_inverse():
     w, h, s, z, _ = _layer(8, 48, 256, 0.5, 0)
-    u = G.inv_chol_upper(h)
-    hd, _ = G.dampen(h)
+    u = G.inverse_factor(h)
+    hd, _ = G.dampened(h)
     assert np.allclose(np.triu(u), u)
     assert np.all(np.diag(u) > 0)
     assert np.allclose(u.T @ u, np.linalg.inv(hd), rtol=1e-9, atol=1e-12)
-    # the rows of U are the eliminated inverses' rows scaled by 1 / sqrt of their diagonal
-    hinv = np.linalg.inv(hd)
-    j = 5
-    for k in range(j):
-        hinv = hinv - np.outer(hinv[:, k], hinv[k, :]) / hinv[k, k]
-    assert np.allclose(u[j, j:], hinv[j, j:] / np.sqrt(hinv[j, j]), rtol=1e-8)
+    # the factor is unique: it equals the transposed lower Cholesky factor of the inverse that a
+    # library routine computes by a different algorithm
+    assert np.allclose(u, np.linalg.cholesky(np.linalg.inv(hd)).T, rtol=1e-8, atol=1e-12)
 
 
 @pytest.mark.parametrize("seed", [1, 2])
 def test_lazy_blocks_are_exact(seed):
     w, h, s, z, _ = _layer(64, 256, 1024, 0.6, seed)
-    u = G.inv_chol_upper(h)
+    u = G.inverse_factor(h)
     ref = G.gptq(w, u, s, z, -8, 7, block=256)["codes"]
     for b in (1, 8, 128):
         assert np.array_equal(G.gptq(w, u, s, z, -8, 7, block=b)["codes"], ref), b
@@ -64,7 +61,7 @@ def test_lazy_blocks_are_exact(seed):
 
 def test_cholesky_form_is_the_obs_update():
     w, h, s, z, _ = _layer(32, 96, 512, 0.7, 3)
-    u = G.inv_chol_upper(h)
+    u = G.inverse_factor(h)
     assert np.array_equal(G.gptq(w, u, s, z, -8, 7, block=32)["codes"], _obs(w, h, s, z, -8, 7))
 
 
@@ -74,7 +71,7 @@ def test_diagonal_h_is_round_to_nearest():
     h = np.diag(rng.uniform(0.5, 3.0, 64))
     s = np.abs(w).max(axis=1, keepdims=True) / 7.0
     z = np.zeros_like(s)
-    out = G.gptq(w, G.inv_chol_upper(h), s, z, -8, 7, block=16)
+    out = G.gptq(w, G.inverse_factor(h), s, z, -8, 7, block=16)
     q_rtn, c_rtn = G.rtn(w, s, z, -8, 7)
     assert np.array_equal(out["codes"], c_rtn)
     assert np.array_equal(out["q_hat"], q_rtn)
@@ -82,7 +79,7 @@ def test_diagonal_h_is_round_to_nearest():
 
 def test_error_feedback_beats_rounding_on_correlated_inputs():
     w, h, s, z, x = _layer(64, 128, 2048, 0.9, 5)
-    out = G.gptq(w, G.inv_chol_upper(h), s, z, -8, 7)
+    out = G.gptq(w, G.inverse_factor(h), s, z, -8, 7)
     q_rtn, _ = G.rtn(w, s, z, -8, 7)
     assert G.proxy_loss(w, out["q_hat"], h) < 0.8 * G.proxy_loss(w, q_rtn, h)
     # some grid points differ from rounding, all codes on the grid
@@ -93,8 +90,8 @@ def test_error_feedback_beats_rounding_on_correlated_inputs():
 def test_dampening_makes_rank_deficient_h_factorizable():
     w, h, s, z, _ = _layer(16, 256, 64, 0.3, 6)   # 64 tokens for 256 channels: rank 64
     with pytest.raises(np.linalg.LinAlgError):
-        G.inv_chol_upper(h, percdamp=0.0)
-    u = G.inv_chol_upper(h, percdamp=0.01)
+        G.inverse_factor(h, damp=0.0)
+    u = G.inverse_factor(h, damp=0.01)
     out = G.gptq(w, u, s, z, -8, 7)
     assert np.all(np.isfinite(out["q_hat"]))
 
@@ -103,13 +100,13 @@ def test_dead_channels():
     w, h, s, z, _ = _layer(8, 32, 256, 0.4, 7)
     h[5, :] = 0
     h[:, 5] = 0
-    hd, dead = G.dampen(h)
+    hd, dead = G.dampened(h)
     assert dead.tolist() == [i == 5 for i in range(32)]
     d = np.diag(h).copy()
     d[5] = 1.0
     assert hd[5, 5] == 1.0 + 0.01 * np.mean(d)
     assert np.array_equal(np.diag(hd), d + 0.01 * np.mean(d))
-    out = G.gptq(w, G.inv_chol_upper(h), s, z, -8, 7, dead=dead)
+    out = G.gptq(w, G.inverse_factor(h), s, z, -8, 7, dead=dead)
     assert np.all(out["q_hat"][:, 5] == 0)
 
 
@@ -118,14 +115,14 @@ def test_quantize_column_rules():
     w = np.array([0.5, 1.5, 2.5, -0.5, 100.0, -100.0, 0.0, 0.7])
     s = np.array([1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 0.0, 0.5])
     z = np.array([0.0, 0.0, 0.0, 3.0, 0.0, 0.0, 2.0, 1.0])
-    qh, code = G.quantize_column(w, s, z, -8, 7, np.float64)
+    qh, code = G.grid_point(w, s, z, -8, 7, np.float64)
     assert code.tolist() == [8, 10, 10, 10, 15, 0, 10, 10]
     assert qh.tolist() == [0.0, 2.0, 2.0, -1.0, 7.0, -8.0, 0.0, 0.5]
 
 
 def test_fp32_loop_tracks_fp64():
     w, h, s, z, _ = _layer(128, 256, 1024, 0.6, 8)
-    u = G.inv_chol_upper(h)
+    u = G.inverse_factor(h)
     c64 = G.gptq(w, u, s, z, -8, 7)["codes"]
     out32 = G.gptq(w, u, s, z, -8, 7, dtype=np.float32)
     assert out32["q_hat"].dtype == np.float32
@@ -135,7 +132,7 @@ def test_fp32_loop_tracks_fp64():
 def test_lazy_blocks_are_exact_up_to_512():
     """The page's block sizes 1, 8, 128 and 512 on a 512-column layer give the same grid points."""
     w, h, s, z, _ = _layer(32, 512, 2048, 0.6, 9)
-    u = G.inv_chol_upper(h)
+    u = G.inverse_factor(h)
     ref = G.gptq(w, u, s, z, -8, 7, block=512)["codes"]
     for b in (1, 8, 128):
         assert np.array_equal(G.gptq(w, u, s, z, -8, 7, block=b)["codes"], ref), b
@@ -156,7 +153,7 @@ def test_held_out_output_error_beats_rounding():
     h = x_cal @ x_cal.T
     s = np.abs(w).max(axis=1, keepdims=True) / 7.0
     z = np.zeros_like(s)
-    q_gptq = G.gptq(w, G.inv_chol_upper(h), s, z, -8, 7)["q_hat"]
+    q_gptq = G.gptq(w, G.inverse_factor(h), s, z, -8, 7)["q_hat"]
     q_rtn, _ = G.rtn(w, s, z, -8, 7)
     err = lambda q: float(np.mean(((w - q) @ x_test) ** 2))  # noqa: E731
     assert err(q_gptq) < 0.9 * err(q_rtn)
