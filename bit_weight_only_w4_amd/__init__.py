@@ -26,6 +26,7 @@ MAX_BATCH = 4096
 TILED_FROM_BATCH = 128
 TILED_FROM_ROWS = 4096
 MAX_SPLIT_K = 64
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 _lib = None
 
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.w4_gemv_grouped_plan.argtypes = [ci, ci, ctypes.POINTER(i64), i64, i64, ip, ip, ip, ip, ip]
         L.w4_probe_read.argtypes = [vp, sz, vp, vp]
         L.w4_probe_copy.argtypes = [vp, vp, sz, vp]
+        L.w4_matmul_splitk_noalloc.argtypes = [vp, vp, vp, ci, i64, i64, i64, vp, ci, vp]
         L.w4_set_path.argtypes = [ci]
         L.w4_get_path.argtypes = []
         L.w4_set_workspace.argtypes = [vp, sz]
@@ -90,6 +92,7 @@ def lib() -> ctypes.CDLL:
                      "w4_gemm_prefill", "w4_gptq_block_update", "w4_gptq_lazy_update",
                      "w4_gptq_quantize", "w4_sparse24_compress", "w4_sparse24_gemv",
                      "w4_sparse24_gemv_grouped", "w4_set_path", "w4_get_path",
+                     "w4_matmul_splitk_noalloc",
                      "w4_set_workspace"):
             getattr(L, name).restype = ci
         _lib = L

@@ -631,6 +631,20 @@ int w4_gemv(const void* x, const uint8_t* packed, const void* scales, int fmt, i
   return run_gemv(x, packed, scales, fmt, n, k, b, y, 1, nullptr, s);
 }
 
+int w4_matmul_splitk_noalloc(const void* x, const uint8_t* packed, const void* scales, int fmt,
+                             int64_t n, int64_t k, int64_t b, float* y, int split_k, void* stream) {
+  const int st = validate(x, packed, scales, fmt, n, k, b, y);
+  if (st != W4_OK) return st;
+  if (b > kMaxGemvBatch) return W4_ERR_PATH;
+  if (split_k == 0) split_k = 4;
+  if (split_k < 2 || split_k > W4_MAX_SPLIT_K || split_k > k / 32) return W4_ERR_PATH;
+  if (splitk_bytes(n, b, split_k) > (size_t)W4_NOALLOC_SCRATCH_BYTES) return W4_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (splitk_scratch(&ws) != hipSuccess) return W4_ERR_HIP;
+  return run_gemv(x, packed, scales, fmt, n, k, b, y, split_k, ws,
+                  reinterpret_cast<hipStream_t>(stream));
+}
+
 int w4_gemv_grouped(const void* x, int groups, const uint8_t* const* packed,
                     const void* const* scales, const int64_t* n, float* const* y, int fmt,
                     int64_t k, int64_t b, void* stream) {

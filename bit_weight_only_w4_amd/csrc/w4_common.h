@@ -163,6 +163,9 @@ hipError_t launch_gemv(int fmt, int b, const GemvArgs& a, int groups, const Gemv
                        hipStream_t s);
 hipError_t launch_splitk_reduce(const float* partial, float* y, int64_t count, int splits,
                                 hipStream_t s);
+// Device address of the current device's static split-K scratch (W4_NOALLOC_SCRATCH_BYTES),
+// looked up once per device.
+hipError_t splitk_scratch(void** ptr);
 hipError_t launch_quantize_nf4(const float* w, int64_t n, int64_t k, uint8_t* packed,
                                float* absmax, hipStream_t s);
 hipError_t launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* packed,

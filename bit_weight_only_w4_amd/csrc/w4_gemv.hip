@@ -1,7 +1,40 @@
-// Format dispatch of the fused GEMV and the fixed-order split-K reduction.
+// Format dispatch of the fused GEMV, the fixed-order split-K reduction, and the static split-K
+// scratch of the no-allocation entry point.
+#include <mutex>
+
 #include "w4_common.h"
 
 namespace w4 {
+
+// Split-K partials of w4_matmul_splitk_noalloc: a file-scope device array, so that the call needs
+// no allocation.  Every device the library runs on holds its own copy (W4_NOALLOC_SCRATCH_BYTES)
+// until the process ends; all calls on one device share it, which is why calls that overlap in
+// time on one device race.  Host code never passes `scratch` itself to a kernel (on the host the
+// name is a stand-in, not a device address): it passes the address hipGetSymbolAddress reports
+// for the current device.
+static __device__ __align__(256) float scratch[W4_NOALLOC_SCRATCH_BYTES / 4];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64] = {};
+}  // namespace
+
+hipError_t splitk_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy, with it current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_gemv_nf4_f16(int b, const GemvArgs& a, int groups, const GemvPlan& p,
                                hipStream_t s);

@@ -27,7 +27,9 @@
  *         host lock, so concurrent quantize or compress calls are serialized by the library;
  *       . a helper stream and two events per device for w4_gptq_quantize on large layers,
  *         created on first use and kept until the process ends;
- *       . a cache of each device's compute-unit count (launch shapes).
+ *       . a cache of each device's compute-unit count (launch shapes);
+ *       . the split-K scratch of w4_matmul_splitk_noalloc: a static device array per device and
+ *         its looked-up address per device.
  *     Matmul calls on different streams may run concurrently as long as their buffers (and
  *     workspaces) do not overlap.
  */
@@ -107,6 +109,7 @@ typedef enum {
 #define W4_TILED_FROM_ROWS 4096
 #define W4_MAX_SPLIT_K 64
 #define W4_MAX_GROUP 4
+#define W4_NOALLOC_SCRATCH_BYTES (8 << 20) /* static split-K scratch of w4_matmul_splitk_noalloc */
 
 /* ---------------------------------------------------------------- quantizers (offline) ----- */
 
@@ -279,6 +282,22 @@ int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* 
 int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t N,
                  int64_t K, int64_t B, float* y, int path, int split_k, void* workspace,
                  size_t workspace_bytes, void* stream);
+
+/* w4_matmul_splitk_noalloc: w4_matmul_ex with path = W4_PATH_SPLITK, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the split-K partials go to a static device array of W4_NOALLOC_SCRATCH_BYTES held by the library
+ * on each device it runs on (until the process ends) instead of a caller's workspace.  Same
+ * kernels, hence the same bits as w4_matmul_ex with the same split_k.
+ *   x, packed, scales, fmt, N, K, B, y   as for w4_gemv (B <= 8)
+ *   split_k  2..W4_MAX_SPLIT_K (at most K/32); 0 = 4
+ * Returns W4_ERR_WORKSPACE when 4 * split_k * B * N bytes exceed W4_NOALLOC_SCRATCH_BYTES,
+ * W4_ERR_PATH for a split count or batch the split-K path cannot run, W4_ERR_HIP when the scratch
+ * address cannot be looked up (first call on a device).  Calls no allocating routine.  The scratch
+ * is fully rewritten by each call before it is read (nothing needs clearing), but every call on
+ * one device shares it: two such calls that overlap in time on one device (two streams, two
+ * threads) race and may corrupt each other's y.  Asynchronous on `stream`. */
+int w4_matmul_splitk_noalloc(const void* x, const uint8_t* packed, const void* scales, int fmt,
+                             int64_t N, int64_t K, int64_t B, float* y, int split_k, void* stream);
 
 /* Bytes of workspace w4_matmul_ex needs for (fmt, N, K, B, path, split_k): split-K needs
  * 4 * S * B * N, two-pass 2 * N * K, the single-pass paths 0; W4_PATH_AUTO reports the split-K
