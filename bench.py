@@ -38,14 +38,21 @@ def parse_args():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "splitk", "twopass", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-table", action="store_true", help="skip the per-shape table")
+    ap.add_argument("--no-large", action="store_true",
+                    help="leave the hidden-8192 shapes out of the per-shape table")
+    ap.add_argument("--trace-from", metavar="KT_DIR", default=None,
+                    help="turn a rocprofv3 --kernel-trace run of this script into the stored "
+                         "per-kernel traced durations, then exit")
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="cap on the CPU time of the oracle's decode step")
     ap.add_argument("--suite", default="decode",
                     choices=["decode", "shapes", "counters", "steps", "prefill", "gptq", "sparse24"],
                     help="decode: the 197-GEMV step (the benchmark line); shapes: per-shape table; "
                          "counters: a few launches of each path, for rocprofv3 --pmc runs; "
                          "steps: the decode step in the other formats and at batch 8; "
                          "prefill: the 197 GEMMs of a 512-token prompt and a per-shape GEMM table")
-    ap.add_argument("--kernel-reps", type=int, default=50,
+    ap.add_argument("--kernel-reps", type=int, default=20,
                     help="graph replays per kernel class / shape kind when timing launches")
     ap.add_argument("--schedule", default="grouped", choices=["serial", "grouped", "dag"],
                     help="serial: one chain of 197 launches; grouped: one chain of 113 launches, "
@@ -167,6 +174,37 @@ class Step:
         r = self.w4.lib().w4_gemm_smallbatch_grouped(*self.group_args[unit], stream_handle)
         if r != 0:
             self.w4.check(r, f"grouped gemv {[self.shapes[i][0] for i in unit]}")
+
+    def launcher(self, unit, mats=None):
+        """A callable(stream_handle) that launches `unit` exactly as launch_unit does, but on the
+        matrices `mats` (a list of (packed, scales), one per member; default the step's own): the
+        rotated timings launch clones of the step's matrices this way."""
+        if mats is None:
+            mats = [self.mats[i] for i in unit]
+        L = self.w4.lib()
+        if len(unit) == 1:
+            import ctypes
+
+            a = list(self.args[unit[0]])
+            a[1] = ctypes.c_void_p(mats[0][0].data_ptr())
+            a[2] = ctypes.c_void_p(mats[0][1].data_ptr())
+            a = tuple(a)
+
+            def run(stream_handle):
+                r = L.w4_matmul_ex(*a, stream_handle)
+                if r != 0:
+                    self.w4.check(r, f"gemv {self.shapes[unit[0]][0]}")
+            return run
+        k = self.shapes[unit[0]][2]
+        arrays = self.w4.grouped_args(self.x[k], [m[0] for m in mats], [m[1] for m in mats],
+                                      [self.ys[i] for i in unit])
+        a = (self.args[unit[0]][0], len(unit)) + arrays + (self.fmt_id, k, self.b)
+
+        def run_group(stream_handle):
+            r = L.w4_gemm_smallbatch_grouped(*a, stream_handle)
+            if r != 0:
+                self.w4.check(r, f"grouped gemv {[self.shapes[i][0] for i in unit]}")
+        return run_group
 
     def unit_key(self, unit):
         """Name of the kernel instantiation a launch unit runs (the profiler's kernel names)."""
@@ -320,6 +358,79 @@ def traffic_from_counters(fetch_dir, write_dir, fmt, b, path, schedule, out):
     return rec
 
 
+def trace_path(fmt, b, path, schedule):
+    root = os.path.dirname(os.path.abspath(__file__))
+    return os.path.join(root, "profiles", f"trace_decode_{fmt}_b{b}_{path}_{schedule}.json")
+
+
+def trace_from(kt_dir, fmt, b, path, schedule, out):
+    """Turn a rocprofv3 --kernel-trace run of this script into per-kernel execution times of the
+    decode step's kernels: for every kernel and grid size of the step's launch mix, the count,
+    mean and median of End - Start over all its traced dispatches (every bench phase that ran
+    it), and per kernel the mean of those medians weighted by how often the step launches each
+    grid.  CPU-only."""
+    import collections
+    import csv
+    import statistics
+
+    import bit_weight_only_w4_amd as w4
+
+    durs = collections.defaultdict(list)
+    with open(os.path.join(kt_dir, "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            durs[(r["Kernel_Name"], grid)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    mix = step_launch_mix(w4, fmt, b, path, schedule)
+    kernels = {}
+    for key in sorted({m[0] for m in mix}):
+        launches = [m for m in mix if m[0] == key]
+        by_grid = {}
+        for grid in sorted({m[1] for m in launches}):
+            d = [v for (n, g), vs in durs.items() if key in n and g == grid for v in vs]
+            if not d:
+                raise SystemExit(f"trace: no dispatch of {key} at grid {grid}")
+            by_grid[str(grid)] = {"count": len(d), "mean_ns": round(statistics.fmean(d), 1),
+                                  "median_ns": float(statistics.median(d)),
+                                  "launches_per_step": sum(1 for m in launches if m[1] == grid)}
+        w = sum(v["launches_per_step"] for v in by_grid.values())
+        kernels[key] = {"by_grid": by_grid,
+                        "step_weighted_median_ns": round(sum(
+                            v["median_ns"] * v["launches_per_step"] for v in by_grid.values()) / w, 1),
+                        "algorithmic_bytes": round(sum(m[2] for m in launches) / len(launches))}
+    rec = {"workload": f"decode step {fmt} batch {b} path {path} schedule {schedule}",
+           "sources_sha256": kernel_source_digest(), "kernels": kernels}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def stored_trace(fmt, b, path, schedule):
+    """The stored kernel-trace summary of this configuration, or None when there is none or the
+    library's sources have changed since it was taken."""
+    p = trace_path(fmt, b, path, schedule)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    return rec if rec.get("sources_sha256") == kernel_source_digest() else None
+
+
+def traced_entry(rec, key, dom):
+    """The dominant kernel's traced execution time (no launch gaps) beside the live figure."""
+    k = rec["kernels"].get(key)
+    if not k:
+        return None
+    us = k["step_weighted_median_ns"] / 1e3
+    gbs = dom["bytes"] / (us / 1e6) / 1e9
+    return {"avg_launch_us": round(us, 3), "achieved": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "source": "rocprofv3 --kernel-trace of the default bench command: median End - Start "
+                      "per grid size, weighted by the step's launches (kernel execution only, no "
+                      "gap between graph nodes)",
+            "by_grid": k["by_grid"]}
+
+
 def stored_traffic(fmt, b, path, schedule, key):
     """HBM bytes per launch of kernel `key` from the stored counter reading, or None when there is
     none or the library's sources have changed since it was taken."""
@@ -399,40 +510,84 @@ def time_replays(graph, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-def time_kernel_classes(step, dev, units, reps=50):
-    """Average launch time of every kernel instantiation the step uses, measured the way the step
-    runs: a graph holding only that kernel's launches, in step order, timed with HIP events over
-    `reps` replays.  Returns {kernel: {"launches", "us", "bytes"}} per step."""
-    classes = {}
-    for u in units:
-        classes.setdefault(step.unit_key(u), []).append(u)
-    out = {}
-    for key, us in classes.items():
-        g = capture(step, dev, us, "serial")
-        ms = time_replays(g, reps, 5)
-        out[key] = {"launches": len(us), "us": ms * 1e3 / len(us),
-                    "bytes": sum(step.unit_bytes(u) for u in us) / len(us)}
-        del g
-    return out
+def graph_time(launchers, dev, reps):
+    """us per launch of the launch closures `launchers`, captured in order as one HIP graph on a
+    side stream (each launch depends on the previous one, as in the step) and replayed `reps`
+    times between two HIP events on the stream the kernels run on."""
+    import torch
+
+    s0 = torch.cuda.Stream(device=dev)
+    s0.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s0):
+        for f in launchers:
+            f(s0.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s0):
+        for f in launchers:
+            f(s0.cuda_stream)
+    torch.cuda.synchronize()
+    ms = time_replays(g, reps, 2)
+    del g
+    return ms * 1e3 / len(launchers)
 
 
-def time_shape_kinds(step, dev, units, reps=50):
-    """Average launch time per launch kind (q, k, ..., lm_head, or q|k|v and gate|up when grouped)
-    inside the step, from a graph of that kind's launches only."""
+ROTATE_BYTES = 600 << 20  # > 2 x the 256 MB last-level cache
+
+
+def time_kinds_rotated(step, dev, units, reps=10, min_bytes=ROTATE_BYTES):
+    """Average launch time of every launch kind of the step (q|k|v, o, gate|up, down, lm_head, or
+    one per projection when ungrouped), measured as the step runs it but on weights that stream
+    from HBM: a graph of that kind's launches over the step's own distinct matrices, followed by
+    launches on clones of them until the graph has read more than `min_bytes` (twice the
+    last-level cache), timed with HIP events.  Returns {kind: {...}}."""
+    import torch
+
     kinds = {}
     for u in units:
         kinds.setdefault(step.unit_kind(u), []).append(u)
     out = {}
     for kind, us in kinds.items():
-        g = capture(step, dev, us, "serial")
-        ms = time_replays(g, reps, 5)
+        launchers = [step.launcher(u) for u in us]
+        total = sum(step.unit_bytes(u) for u in us)
+        clones = []
+        j = 0
+        while total < min_bytes:
+            u = us[j % len(us)]
+            mats = [(step.mats[i][0].clone(), step.mats[i][1].clone()) for i in u]
+            clones.append(mats)
+            launchers.append(step.launcher(u, mats))
+            total += step.unit_bytes(u)
+            j += 1
+        t = graph_time(launchers, dev, reps)
         u0 = us[0]
+        ab = step.unit_bytes(u0)
         out[kind] = {"n": sum(step.shapes[i][1] for i in u0), "k": step.shapes[u0[0]][2],
-                     "count": len(us), "us": ms * 1e3 / len(us), "bytes": step.unit_bytes(u0),
+                     "count": len(us), "graph_launches": len(launchers), "us": t, "bytes": ab,
+                     "gbs": ab / (t / 1e6) / 1e9,
                      "path": "grouped" if len(u0) > 1 else step.plans[u0[0]][0],
                      "kernel": step.unit_key(u0)}
-        out[kind]["gbs"] = out[kind]["bytes"] / (out[kind]["us"] / 1e6) / 1e9
-        del g
+        del clones, launchers
+        torch.cuda.empty_cache()
+    return out
+
+
+def kernel_classes(step, units, kinds):
+    """Per kernel instantiation of the step: launches per step, average launch time (the
+    launch-weighted mean of its kinds' rotated times) and average algorithmic bytes per launch."""
+    out = {}
+    for u in units:
+        kd = kinds[step.unit_kind(u)]
+        c = out.setdefault(step.unit_key(u), {"launches": 0, "us_sum": 0.0, "bytes_sum": 0.0,
+                                             "kinds": []})
+        c["launches"] += 1
+        c["us_sum"] += kd["us"]
+        c["bytes_sum"] += step.unit_bytes(u)
+        if step.unit_kind(u) not in c["kinds"]:
+            c["kinds"].append(step.unit_kind(u))
+    for c in out.values():
+        c["us"] = c.pop("us_sum") / c["launches"]
+        c["bytes"] = c.pop("bytes_sum") / c["launches"]
     return out
 
 
@@ -468,9 +623,14 @@ def measure_ceilings(dev, nbytes=2 << 30, reps=10):
 
 
 def cpu_baseline(fmt, b, seconds):
-    """The oracle (fp64 dequantize + dot products) timed on the host cores on a bounded sample of
-    the decode step -- layer 0's q, gate and down matrices -- scaled to a whole step by weight
-    count.  Weights are drawn and quantized on the CPU (untimed); only dequant + GEMV is timed."""
+    """The oracle (fp64 dequantize + dot products) timed on the host cores: the single 256 x 1536
+    GEMV (W ~ N(0, 0.02), seed 0, quantized by the oracle), then one whole 197-GEMV decode step --
+    every matrix, lm_head included, in chunks of at most 8192 rows to bound host memory.  The
+    step's packed bytes and scales are random storage bits from synth_inputs (drawn untimed, one
+    matrix at a time): the oracle's cost does not depend on the values.  The per-shape times are
+    those of layer 0's matrices and lm_head within the step.  `seconds` caps the step: when the
+    time runs out, the remaining matrices are scaled from the measured ones by weight count (the
+    sample string says so)."""
     import numpy as np
 
     import oracle
@@ -484,26 +644,38 @@ def cpu_baseline(fmt, b, seconds):
         threads = 1
     wf = fmt.split("_")[0]
     xd = "f16" if fmt.endswith("_f16") else "bf16"
-    sample = [("q", 1536, 1536, 1000), ("gate", 8960, 1536, 1004), ("down", 1536, 8960, 1006)]
-    mats = []
-    for name, n, k, seed in sample:
-        w = synth_inputs.weights(n, k, seed=seed)
-        q = {"nf4": oracle.quantize_nf4, "int4": oracle.quantize_int4, "fp4": oracle.quantize_fp4,
-             "int4a": oracle.quantize_int4_asym}[wf](w)
-        mats.append((q, synth_inputs.activations(b, k, xd, seed=7)))
-    sample_weights = sum(n * k for _, n, k, _ in sample)
+    quant = {"nf4": oracle.quantize_nf4, "int4": oracle.quantize_int4, "fp4": oracle.quantize_fp4,
+             "int4a": oracle.quantize_int4_asym}[wf]
+    # the single-GEMV workload
+    w0, x0 = synth_inputs.single_gemv_case(seed=0, dtype=xd)
+    p0, s0 = quant(w0)
     t0 = time.perf_counter()
-    passes = 0
-    while True:
-        for (p, s), x in mats:
-            oracle.gemv_reference(x, xd, oracle.dequant(wf, p, s))
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or passes >= 1000:
-            break
-    per_pass = el / passes
-    step_weights = sum(n * k for _, n, k in synth_inputs.decode_step_shapes())
-    step_s = per_pass * step_weights / sample_weights
+    reps = 0
+    while reps < 20 or time.perf_counter() - t0 < 0.5:
+        oracle.gemv_reference(x0, xd, oracle.dequant(wf, p0, s0))
+        reps += 1
+    single_us = (time.perf_counter() - t0) / reps * 1e6
+    # one decode step, matrix by matrix
+    xs = {k: synth_inputs.activations(b, k, xd, seed=7) for k in (1536, 8960)}
+    shapes = synth_inputs.decode_step_shapes()
+    per_shape, done_s, done_w, total_w = {}, 0.0, 0, sum(n * k for _, n, k in shapes)
+    chunk = 8192
+    for i, (name, n, k) in enumerate(shapes):
+        if done_s >= seconds and name != "lm_head":
+            continue
+        p, sc = synth_inputs.random_packed(wf, n, k, seed=5000 + i)
+        t = time.perf_counter()
+        for r0 in range(0, n, chunk):
+            oracle.gemv_reference(xs[k], xd, oracle.dequant(wf, p[r0:r0 + chunk], sc[r0:r0 + chunk]))
+        el = time.perf_counter() - t
+        done_s += el
+        done_w += n * k
+        short = name.split(".")[-1]
+        if name.startswith("L1.") or name == "lm_head":
+            per_shape[short] = round(el * 1e6, 1)
+        del p, sc
+    step_s = done_s * total_w / done_w
+    full = done_w == total_w
     try:
         model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
     except Exception:
@@ -513,31 +685,53 @@ def cpu_baseline(fmt, b, seconds):
         "unit": "tok/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"layer-0 q 1536x1536, gate 8960x1536, down 1536x8960 ({sample_weights} weights), "
-                   f"{passes} passes in {el:.1f}s, scaled by weight count to the 197-GEMV step "
-                   f"({step_weights} weights): {step_s:.2f} s/step; CPU {model}"),
+        "sample": (f"the 197-GEMV decode step at batch {b}, "
+                   + ("every matrix timed" if full else
+                      f"{done_w} of {total_w} weights timed, the rest scaled by weight count")
+                   + f" (row chunks of {chunk}; random packed bytes and scales, value-independent "
+                   f"cost): {step_s:.2f} s/step; the 256x1536 single GEMV {single_us:.0f} us; "
+                   f"CPU {model}"),
+        "step_s": round(step_s, 3),
+        "single_gemv_256x1536_us": round(single_us, 1),
+        "per_shape_us": per_shape,
     }
 
 
-def time_shape(fmt, n, k, b, path, split_k, dev, min_bytes=600 << 20, reps=5):
+def rotated_mats(fmt, n, k, dev, min_bytes=ROTATE_BYTES, seed=None):
+    """One [n, k] matrix W ~ N(0, 0.02) drawn and quantized on the device, plus clones of it until
+    the copies together exceed `min_bytes` (so that launches rotating over them stream their
+    weights from HBM; the kernels' cost does not depend on the values)."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    wb = algorithmic_bytes(fmt, n, k, 0)
+    copies = max(2, min(4096, -(-min_bytes // wb)))
+    gen = torch.Generator(device=dev).manual_seed(n * 31 + k if seed is None else seed)
+    w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+    p, s = w4.quantize(fmt, w)
+    del w
+    mats = [(p, s)] + [(p.clone(), s.clone()) for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    return mats
+
+
+def time_shape(fmt, n, k, b, path, split_k, dev, mats=None, reps=5):
     """Average launch time of one (format, N, K, B, path) over rotated weight copies (together
-    larger than the last-level cache, so the weights stream from HBM), as a HIP graph of launches
-    timed with events.  Returns (us per launch, None) or (None, error text)."""
+    larger than twice the last-level cache, so the weights stream from HBM), as a HIP graph of
+    launches timed with events.  Returns (us per launch, None) or (None, error text)."""
     import ctypes
 
     import torch
 
     import bit_weight_only_w4_amd as w4
 
-    wb = algorithmic_bytes(fmt, n, k, 0)
-    copies = max(1, min(4096, -(-min_bytes // wb)))
+    own = mats is None
+    if own:
+        mats = rotated_mats(fmt, n, k, dev)
+    copies = len(mats)
     xdt = torch.float16 if fmt.endswith("_f16") else torch.bfloat16
-    gen = torch.Generator(device=dev).manual_seed(n * 31 + k)
-    mats = []
-    for c in range(copies):
-        w = torch.randn(n, k, generator=gen, device=dev) * 0.02
-        mats.append(w4.quantize(fmt, w))
-        del w
+    gen = torch.Generator(device=dev).manual_seed(b * 7 + k)
     x = torch.randn(b, k, generator=gen, device=dev).to(xdt)
     y = torch.empty(b, n, device=dev)
     wsb = w4.workspace_bytes(fmt, n, k, b, path, split_k) if path in ("splitk", "twopass") else 0
@@ -545,30 +739,30 @@ def time_shape(fmt, n, k, b, path, split_k, dev, min_bytes=600 << 20, reps=5):
     launches = max(copies, 16)
     vp = ctypes.c_void_p
     L = w4.lib()
+    err = []
 
-    def run(stream):
-        for r in range(launches):
-            p_, s_ = mats[r % copies]
-            st = L.w4_matmul_ex(vp(x.data_ptr()), vp(p_.data_ptr()), vp(s_.data_ptr()), w4.FORMATS[fmt],
-                                n, k, b, vp(y.data_ptr()), w4.PATHS[path], split_k,
-                                vp(ws.data_ptr()), ws.numel(), stream.cuda_stream)
+    def make(r):
+        p_, s_ = mats[r % copies]
+        a = (vp(x.data_ptr()), vp(p_.data_ptr()), vp(s_.data_ptr()), w4.FORMATS[fmt], n, k, b,
+             vp(y.data_ptr()), w4.PATHS[path], split_k, vp(ws.data_ptr()), ws.numel())
+
+        def run(stream_handle):
+            st = L.w4_matmul_ex(*a, stream_handle)
             if st != 0:
-                return w4.status_string(st)
-        return None
+                err.append(w4.status_string(st))
+                raise RuntimeError(err[-1])
+        return run
 
-    s0 = torch.cuda.Stream(device=dev)
-    s0.wait_stream(torch.cuda.current_stream())
-    err = run(s0)
-    torch.cuda.synchronize()
-    if err:
-        return None, err
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s0):
-        run(s0)
-    ms = time_replays(g, reps, 2)
-    del g, mats, ws
-    torch.cuda.empty_cache()
-    return ms * 1e3 / launches, None
+    try:
+        us = graph_time([make(r) for r in range(launches)], dev, reps)
+    except RuntimeError:
+        return None, err[-1] if err else "launch failed"
+    finally:
+        del ws
+        if own:
+            del mats
+        torch.cuda.empty_cache()
+    return us, None
 
 
 def time_read_probe(nbytes, dev, min_bytes=600 << 20, reps=5):
@@ -597,6 +791,52 @@ def time_read_probe(nbytes, dev, min_bytes=600 << 20, reps=5):
     del g, bufs
     torch.cuda.empty_cache()
     return ms * 1e3 / launches
+
+
+# The per-shape table of the default run: the Qwen2.5-1.5B decode shapes at batches 1, 8, 32 and
+# 128, the hidden-8192 model's shapes at 1, 4, 16 (its own batches) and 8, 32, 128, and the single
+# 256 x 1536 GEMV, all on the automatic path over rotated copies.
+TABLE_QWEN = (("q/o", 1536, 1536), ("k/v", 256, 1536), ("gate/up", 8960, 1536),
+              ("down", 1536, 8960), ("lm_head", 151936, 1536))
+TABLE_LARGE = (("q", 8192, 8192), ("kv", 1024, 8192), ("gate/up", 28672, 8192),
+               ("down", 8192, 28672), ("lm_head", 128256, 8192))
+
+
+def shape_table(fmt, dev, read_gbs, large=True):
+    """Rows of (shape, B, path, us, GB/s, fractions of 8 TB/s and of the measured read ceiling,
+    TFLOP/s and the fraction of the 2.5 PFLOP/s dense fp16/bf16 matrix-core peak from B = 32)."""
+    import bit_weight_only_w4_amd as w4
+
+    plan = [("single", "256x1536", 256, 1536, (1,))]
+    plan += [("qwen2.5-1.5b", nm, n, k, (1, 8, 32, 128)) for nm, n, k in TABLE_QWEN]
+    if large:
+        plan += [("hidden-8192", nm, n, k, (1, 4, 8, 16, 32, 128)) for nm, n, k in TABLE_LARGE]
+    rows = []
+    for group, name, n, k, bs in plan:
+        mats = rotated_mats(fmt, n, k, dev)
+        for b in bs:
+            path, sk = w4.auto_path(fmt, n, k, b, 0)
+            us, err = time_shape(fmt, n, k, b, "auto", 0, dev, mats=mats)
+            ab = algorithmic_bytes(fmt, n, k, b)
+            r = {"group": group, "shape": name, "n": n, "k": k, "b": b, "path": path}
+            if us is None:
+                r["error"] = err
+            else:
+                gbs = ab / us / 1e3
+                tf = 2.0 * n * k * b / us / 1e6
+                r.update({"us": round(us, 3), "gbs": round(gbs, 1),
+                          "frac_8tbs": round(gbs / HBM_PEAK_GBS, 4),
+                          "frac_read_ceiling": round(gbs / read_gbs, 4),
+                          "tflops": round(tf, 2)})
+                if b >= 32:
+                    r["frac_mfma_peak"] = round(tf / MFMA_FP16_PEAK_TFLOPS, 4)
+            rows.append(r)
+            log(f"[table] {group:12s} {name:9s} {n:6d}x{k:5d} B={b:3d} {path:6s} "
+                + (f"{r['us']:9.2f} us {r['gbs']:7.0f} GB/s ({100 * r['frac_8tbs']:5.1f}% of 8 TB/s, "
+                   f"{100 * r['frac_read_ceiling']:5.1f}% of read ceiling) {r['tflops']:7.1f} TFLOP/s"
+                   if us else f"ERR {err}"))
+        del mats
+    return rows
 
 
 # Decode steps besides the benchmark line's: (format, batch).
@@ -679,7 +919,8 @@ def prefill_suite(args, dev):
             row = {"format": fmt, "shape": name, "n": n, "k": k, "b": b,
                    "auto": w4.auto_path(fmt, n, k, b)[0]}
             for path in ("tiled", "mfma"):
-                us, err = time_shape(fmt, n, k, b, path, 0, dev, min_bytes=256 << 20, reps=3)
+                us, err = time_shape(fmt, n, k, b, path, 0, dev,
+                                     mats=rotated_mats(fmt, n, k, dev, min_bytes=256 << 20), reps=3)
                 if us is None:
                     row[path] = {"error": err}
                     continue
@@ -933,7 +1174,8 @@ def sparse24_suite(args, dev):
         byt = per + 2 * k + 4 * n
         row["sparse24_us"] = round(us, 3)
         row["sparse24_gbs"] = round(byt / us / 1e3, 1)
-        t_nf4, _ = time_shape("nf4_f16", n, k, 1, "gemv", 0, dev, min_bytes=256 << 20, reps=3)
+        t_nf4, _ = time_shape("nf4_f16", n, k, 1, "gemv", 0, dev,
+                              mats=rotated_mats("nf4_f16", n, k, dev, min_bytes=256 << 20), reps=3)
         row["nf4_gemv_us"] = round(t_nf4, 3) if t_nf4 else None
         dcopies = max(2, min(32, (600 << 20) // (n * k * 2)))
         dw = [torch.randn(n, k, generator=gen, device=dev).to(torch.float16) for _ in range(dcopies)]
@@ -1138,6 +1380,12 @@ def main():
         path, out = counters_from(args.counters_from)
         print(json.dumps({"counters": path, "cases": len(out)}))
         return
+    if args.trace_from:
+        out = trace_path(args.fmt, args.batch, args.path, args.schedule)
+        rec = trace_from(args.trace_from, args.fmt, args.batch, args.path, args.schedule, out)
+        print(json.dumps({"trace": out, "kernels": {k: v["step_weighted_median_ns"]
+                                                    for k, v in rec["kernels"].items()}}))
+        return
     if args.traffic_from:
         out = traffic_path(args.fmt, args.batch, args.path, args.schedule)
         rec = traffic_from_counters(*args.traffic_from, args.fmt, args.batch, args.path,
@@ -1247,11 +1495,14 @@ def main():
         f"{step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
 
     units = step_units(step.shapes, args.schedule)
-    kernels = time_kernel_classes(step, dev, units, args.kernel_reps)
-    shapes = time_shape_kinds(step, dev, units, args.kernel_reps)
+    shapes = time_kinds_rotated(step, dev, units, args.kernel_reps)
+    kernels = kernel_classes(step, units, shapes)
     for kind, r in shapes.items():
         log(f"[bench] {kind:10s} {r['n']:6d}x{r['k']:5d} {r['path']:7s} {r['us']:8.2f} us/launch "
-            f"{r['gbs']:8.0f} GB/s  [{r['kernel']}]")
+            f"{r['gbs']:8.0f} GB/s  ({r['graph_launches']} rotated launches) [{r['kernel']}]")
+    kinds_sum_us = sum(shapes[step.unit_kind(u)]["us"] for u in units)
+    log(f"[bench] sum over the step's launches of their kinds' rotated times: {kinds_sum_us:.1f} us "
+        f"(step {ms * 1e3:.1f} us)")
     for key, d in sorted(kernels.items(), key=lambda kv: -kv[1]["us"] * kv[1]["launches"]):
         log(f"[bench] kernel {key}: {d['launches']} launches/step, {d['us']:.2f} us/launch, "
             f"{d['bytes'] / (d['us'] / 1e6) / 1e9:.0f} GB/s")
@@ -1261,6 +1512,10 @@ def main():
 
     read_gbs, copy_gbs = measure_ceilings(dev)
     log(f"[bench] ceilings: streaming read {read_gbs:.0f} GB/s, copy {copy_gbs:.0f} GB/s")
+    table = None
+    if not args.no_table:
+        table = shape_table(args.fmt, dev, read_gbs, large=not args.no_large)
+    traced = stored_trace(args.fmt, args.batch, args.path, args.schedule)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -1301,6 +1556,13 @@ def main():
             "measured_copy_ceiling_gbs": round(copy_gbs, 1),
             "step_frac_of_measured_read": round(step_gbs / read_gbs, 4),
             "per_shape_us": {kk: round(r["us"], 3) for kk, r in shapes.items()},
+            "per_shape_timing": (f"HIP events over graph replays of each launch kind, rotated over "
+                                 f"more than {ROTATE_BYTES >> 20} MiB of distinct weights (the "
+                                 f"step's own matrices, then clones), launch to launch"),
+            "sum_of_kind_times_us": round(kinds_sum_us, 1),
+            "single_gemv_256x1536_us": (next((r["us"] for r in table or [] if r["group"] == "single"
+                                              and "us" in r), None)),
+            "shape_table": table,
         },
         "roofline": {
             "bound": "hbm",
@@ -1312,6 +1574,14 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": stored_traffic(args.fmt, args.batch, args.path, args.schedule, dom_key),
+            "timing": "HIP events, rotated graph replays of the kernel's launch kinds, launch to launch",
+            "per_kind": {kd: {"launches_per_step": shapes[kd]["count"],
+                              "avg_launch_us": round(shapes[kd]["us"], 3),
+                              "bytes": shapes[kd]["bytes"],
+                              "achieved": round(shapes[kd]["gbs"], 1),
+                              "frac": round(shapes[kd]["gbs"] / HBM_PEAK_GBS, 4)}
+                         for kd in dom["kinds"]},
+            "traced": traced_entry(traced, dom_key, dom) if traced else None,
         },
         "cpu_baseline": cpu,
     }

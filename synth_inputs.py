@@ -94,6 +94,26 @@ def single_gemv_case(seed: int = 0, n: int = 256, k: int = 1536, dtype: str = "f
     return w, x
 
 
+def random_packed(fmt: str, n: int, k: int, seed: int):
+    """Storage arrays of an [n, k] 4-bit matrix filled with random bits, for timing code whose cost
+    does not depend on the values: packed bytes uniform over 0..255 ([n, k/2] uint8) and per-block
+    scales in the format's storage type -- fp32 [n, k/64] for "nf4" and "fp4", bf16 bit patterns
+    [n, k/128] for "int4", and for "int4a" uint32 words [n, k/128] holding bf16 scale bits in bits
+    0-15 and a random zero point 0..15 in bits 16-19.  Scales are drawn from U(0.004, 0.006)."""
+    rng = np.random.default_rng(seed)
+    packed = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    if fmt in ("nf4", "fp4"):
+        scales = rng.uniform(0.004, 0.006, size=(n, k // 64)).astype(np.float32)
+    elif fmt == "int4":
+        scales = _f32_to_bf16_bits(rng.uniform(0.004, 0.006, size=(n, k // 128)))
+    elif fmt == "int4a":
+        bits = _f32_to_bf16_bits(rng.uniform(0.004, 0.006, size=(n, k // 128))).astype(np.uint32)
+        scales = bits | (rng.integers(0, 16, size=bits.shape, dtype=np.uint32) << np.uint32(16))
+    else:
+        raise ValueError(f"unknown weight format {fmt!r}")
+    return packed, scales
+
+
 def upper_factor(cols: int, seed: int, off_sigma: float = 0.3) -> np.ndarray:
     """A seeded random upper-triangular fp32 matrix [cols, cols]: diagonal ~ U(0.5, 1.5),
     entries above it ~ N(0, off_sigma^2 / cols), zeros below.  Any such matrix U is the upper
