@@ -21,7 +21,9 @@
 //     value of the low nibble) in the activation's 16-bit type; one ds_read_b32 decodes two
 //     weights.  The table holds 64 copies of each entry, copy c in bank c, and lane L reads copy L,
 //     so the lookups of a wave never conflict.  Its LDS address, byte value * 256 + lane * 4, is
-//     built by one v_perm_b32.  The table is written while the first loads are in flight.
+//     built by one v_perm_b32.  The table is written while the first loads are in flight.  FP4
+//     needs no table: gfx950 converts a byte of two E2M1 codes to a 16-bit pair in one
+//     instruction (the pair comes out odd k first, so FP4 holds its activation pairs swapped).
 //   * Multiply: v_dot2_f32_f16 / v_dot2_f32_bf16 of the decoded pair with the activation pair
 //     into fp32 (products of two 16-bit values are exact in fp32), then one fp32 FMA per chunk with
 //     the block scale.  NF4 with bf16 activations splits each code into two bf16 terms (8-byte
@@ -157,10 +159,34 @@ __device__ inline float load_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __uint_as_float(buffer_load32(r, off));
 }
 
+// FP4 is decoded without the LDS table, through gfx950's E2M1 -> 16-bit conversion
+// (v_cvt_scalef32_pk_{f16,bf16}_fp4 with scale 1: exact, one instruction per packed byte); no
+// table fill, no lookups.  (Decoding INT4 x fp16 without the table by fp16 bit arithmetic -- the
+// fp16 number with bit pattern 0x6400 | q is 1024 + q, one packed subtraction of 1032 gives
+// q - 8 -- is exact too, but its 4.25 VALU instructions per packed byte measured slower than the
+// table on the larger matrices.)
+template <int FMT, int XT>
+constexpr bool table_free() {
+  return FMT == kFP4;
+}
+
+// The two FP4 weights of byte KB of packed dword w as one activation-type pair.  The conversion
+// returns the low nibble's value (odd k) in the low half, so FP4 keeps its activation pairs swapped
+// (odd k low) to match.
+template <int XT, int KB>
+__device__ inline uint32_t fp4_pair(uint32_t w) {
+  if constexpr (XT == kF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, KB));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, KB));
+  }
+}
+
 template <int FMT, int XT, int B, int ITM, int NT, bool GROUPED>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
-  __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
+  constexpr bool kTable = !table_free<FMT, XT>();
+  __shared__ __align__(16) uint32_t tab[kTable ? kTableBytes / 4 : 4];
   __shared__ float xwave[NT / 64][B];
 
   const int tid = threadIdx.x;
@@ -258,7 +284,12 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
       const uint32_t xo = offset_or_oob(have, (uint32_t)(b * k + (int64_t)(c0 + c) * 32) * 2u);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = buffer_load16(rx, xo + 16u * q);
+        uint4 v = buffer_load16(rx, xo + 16u * q);
+        if constexpr (FMT == kFP4) {
+          // the hardware FP4 conversion yields (odd k, even k) pairs: swap each activation pair
+          v = make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
+                         __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
+        }
         xr[i][b][4 * q + 0] = v.x;
         xr[i][b][4 * q + 1] = v.y;
         xr[i][b][4 * q + 2] = v.z;
@@ -269,8 +300,10 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   load_rb(rb0 + grid, pB, sB);
 
   // --- decode table, written while the loads above are in flight
-  fill_table<FMT, XT, NT>(tab);
-  __syncthreads();
+  if constexpr (kTable) {
+    fill_table<FMT, XT, NT>(tab);
+    __syncthreads();
+  }
 
   // INT4A: the sum of each chunk's 32 activations (per batch row), for the zero-point term
   // -(z - 8) * s * sum(x) of every row this lane meets; computed once per launch.
@@ -319,10 +352,28 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
+            const int m = 4 * j + kb;  // byte index in the chunk = activation pair index
+            if constexpr (!kTable) {
+              const uint32_t t = kb == 0   ? fp4_pair<XT, 0>(wv[j])
+                                 : kb == 1 ? fp4_pair<XT, 1>(wv[j])
+                                 : kb == 2 ? fp4_pair<XT, 2>(wv[j])
+                                           : fp4_pair<XT, 3>(wv[j]);
+#pragma unroll
+              for (int b = 0; b < B; ++b) {
+                if (XT == kF16) {
+                  d[b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, t),
+                                                __builtin_bit_cast(half2_t, xr[i][b][m]), d[b], false);
+                } else {
+                  d[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, t),
+                                                         __builtin_bit_cast(bf162_t, xr[i][b][m]),
+                                                         d[b], false);
+                }
+              }
+              continue;
+            }
             // LDS byte address: lane offset in byte 0, the packed byte in byte 1.
             const uint32_t addr =
                 __builtin_amdgcn_perm(wv[j], laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb) << 8));
-            const int m = 4 * j + kb;  // byte index in the chunk = activation pair index
             if (kSplitCode) {
               const uint2 t = *reinterpret_cast<const uint2*>(tabc + addr);
 #pragma unroll
