@@ -28,10 +28,28 @@ bool plan_slice(const int64_t* ns, int groups, int64_t k, int64_t b, int t, Mfma
   const int slices = (int)((b + 16 * t - 1) / (16 * t));
   const int64_t rows_held = std::min<int64_t>(16 * t, b);
   int kw = 1;
-  for (int c = 1; c <= max_kw(t); c *= 2) {
-    if (c > quads) break;
-    kw = c;
-    if (member_tiles(ns, groups, 16 * (8 / c)) * slices >= cus) break;
+  if (quads <= 12) {
+    // Rows of at most 3072 weights (measured on MI355X over the 1536-wide decode shapes at
+    // B = 4..32): with one batch tile, eight K groups (one quad per wave, idle groups past K
+    // reading zeros) beat fewer on every matrix that does not keep each resident workgroup busy
+    // for two row tiles at one K group, where one K group is best (lm_head); with two or more
+    // batch tiles (one workgroup per CU), the most K groups whose tiles still fit one round of
+    // resident workgroups (a second, partial round costs more than the shorter waves save).
+    if (t == 1) {
+      kw = member_tiles(ns, groups, 16 * 8) * slices >= 2 * 2 * cus ? 1 : 8;
+    } else {
+      for (int c = max_kw(t); c >= 1; c /= 2) {
+        kw = c;
+        if (member_tiles(ns, groups, 16 * (8 / c)) * slices <= cus) break;
+      }
+    }
+  } else {
+    // Longer rows: the fewest K groups that give every CU a row tile.
+    for (int c = 1; c <= max_kw(t); c *= 2) {
+      if (c > quads) break;
+      kw = c;
+      if (member_tiles(ns, groups, 16 * (8 / c)) * slices >= cus) break;
+    }
   }
   const int64_t qpk = (quads + kw - 1) / kw;
   const int64_t red = kw > 1 ? (int64_t)(kw - 1) * (8 / kw) * t * 1024 : 0;
