@@ -734,7 +734,7 @@ def time_shape(fmt, n, k, b, path, split_k, dev, mats=None, reps=5):
     gen = torch.Generator(device=dev).manual_seed(b * 7 + k)
     x = torch.randn(b, k, generator=gen, device=dev).to(xdt)
     y = torch.empty(b, n, device=dev)
-    wsb = w4.workspace_bytes(fmt, n, k, b, path, split_k) if path in ("splitk", "twopass") else 0
+    wsb = w4.workspace_bytes(fmt, n, k, b, path, split_k) if path != "gemv" else 0
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     launches = max(copies, 16)
     vp = ctypes.c_void_p
@@ -800,6 +800,11 @@ TABLE_QWEN = (("q/o", 1536, 1536), ("k/v", 256, 1536), ("gate/up", 8960, 1536),
               ("down", 1536, 8960), ("lm_head", 151936, 1536))
 TABLE_LARGE = (("q", 8192, 8192), ("kv", 1024, 8192), ("gate/up", 28672, 8192),
                ("down", 8192, 28672), ("lm_head", 128256, 8192))
+# One GPU's share of the hidden-8192 model and of the Qwen lm_head under 8-way tensor
+# parallelism: column-parallel matrices split N (q, gate/up, lm_head), the row-parallel down
+# projection splits K.
+TABLE_SHARD = (("q/8", 1024, 8192), ("gate/up/8", 3584, 8192), ("down/8", 8192, 3584),
+               ("lm_head/8", 16032, 8192), ("qwen-lm/8", 18992, 1536))
 
 
 def shape_table(fmt, dev, read_gbs, large=True):
@@ -811,14 +816,18 @@ def shape_table(fmt, dev, read_gbs, large=True):
     plan += [("qwen2.5-1.5b", nm, n, k, (1, 8, 32, 128)) for nm, n, k in TABLE_QWEN]
     if large:
         plan += [("hidden-8192", nm, n, k, (1, 4, 8, 16, 32, 128)) for nm, n, k in TABLE_LARGE]
+        plan += [("tp8-shard", nm, n, k, (1, 8, 32)) for nm, n, k in TABLE_SHARD]
     rows = []
     for group, name, n, k, bs in plan:
         mats = rotated_mats(fmt, n, k, dev)
         for b in bs:
-            path, sk = w4.auto_path(fmt, n, k, b, 0)
+            # the automatic choice given the workspace it asks for (time_shape passes it)
+            path, sk = w4.auto_path(fmt, n, k, b, w4.workspace_bytes(fmt, n, k, b))
             us, err = time_shape(fmt, n, k, b, "auto", 0, dev, mats=mats)
             ab = algorithmic_bytes(fmt, n, k, b)
-            r = {"group": group, "shape": name, "n": n, "k": k, "b": b, "path": path}
+            r = {"group": group, "shape": name, "n": n, "k": k, "b": b, "path": path,
+                 "split_k": sk}
+            path = path + (f"/S{sk}" if sk > 1 else "")
             if us is None:
                 r["error"] = err
             else:
@@ -831,7 +840,7 @@ def shape_table(fmt, dev, read_gbs, large=True):
                 if b >= 32:
                     r["frac_mfma_peak"] = round(tf / MFMA_FP16_PEAK_TFLOPS, 4)
             rows.append(r)
-            log(f"[table] {group:12s} {name:9s} {n:6d}x{k:5d} B={b:3d} {path:6s} "
+            log(f"[table] {group:12s} {name:9s} {n:6d}x{k:5d} B={b:3d} {path:8s} "
                 + (f"{r['us']:9.2f} us {r['gbs']:7.0f} GB/s ({100 * r['frac_8tbs']:5.1f}% of 8 TB/s, "
                    f"{100 * r['frac_read_ceiling']:5.1f}% of read ceiling) {r['tflops']:7.1f} TFLOP/s"
                    if us else f"ERR {err}"))

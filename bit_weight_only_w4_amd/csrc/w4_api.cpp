@@ -204,6 +204,34 @@ int auto_splits(int64_t, int64_t, int) { return 1; }
 
 size_t splitk_bytes(int64_t n, int64_t b, int s) { return (size_t)s * (size_t)b * (size_t)n * 4; }
 
+int pow2_at_least(int64_t v) {
+  int p = 1;
+  while (p < v && p < (1 << 30)) p *= 2;
+  return p;
+}
+
+// Split count of the automatic MFMA path (used when the caller's workspace holds the partial
+// sums).  Rows of at most 12 quads (3072 weights) never split, nor matrices with two 128-row
+// tiles per CU (128256 x 8192 at B = 32: 205 us split 4 ways against 195 unsplit, the partial
+// sums adding 12% to the traffic).  Longer rows split K into the
+// smallest power of two of ranges that (a) keeps one range's activation window, held rows x K / S
+// x 2 bytes, within 128 KiB, and (b) gives matrices of few rows two row tiles of 16 rows per CU;
+// at most 16 ranges, each of at least two quads.  Measured on MI355X (NF4 x fp16, rotated
+// weights, every S from 1 to 16): the rule's S is the best or within 6% of it on 1536 x 8960 at
+// B = 4..32 (14.9 -> 11.8 us at B = 32), 8192 x 28672 at B = 4..32 (72.3 -> 45.2 us at B = 32),
+// 8192 x 8192 at B = 4..32 and 1024 x 8192 at B = 8 and 32; 28672 x 8192 at B = 32 gets 56.4 us
+// against 59.3 unsplit (49.1 at S = 8).  Non-power-of-two counts measured slower throughout.
+int auto_mfma_splits(int64_t n, int64_t k, int64_t b) {
+  const int64_t quads = (k + 255) / 256;
+  if (quads <= 12 || (n + 127) / 128 >= 2 * device_cu_count()) return 1;
+  const int64_t rows = std::min<int64_t>(b, 128);
+  const int sx = pow2_at_least((rows * k * 2 + 131071) / 131072);
+  const int sp = pow2_at_least((2 * device_cu_count() * 16 + n - 1) / n);
+  int s = std::min(std::max(sx, sp), 16);
+  while (s > 1 && quads / s < 2) s /= 2;
+  return s;
+}
+
 // Launch shape of one fused-GEMV launch over `groups` members that share K: the plan of their
 // summed rows, each member's row blocks, and each member's workgroups along x (its share of the
 // grid cap, at most its row blocks; grouped launches give the members consecutive ranges of x, so
@@ -287,9 +315,9 @@ int run_twopass(const void* x, const uint8_t* packed, const void* scales, int fm
 }
 
 int run_mfma(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
-             int64_t k, int64_t b, float* y, hipStream_t st) {
+             int64_t k, int64_t b, float* y, hipStream_t st, int splits = 1, void* ws = nullptr) {
   const hipError_t e = launch_mfma(fmt, reinterpret_cast<const uint16_t*>(x), packed, scales, n, k,
-                                   b, y, st);
+                                   b, y, st, splits, reinterpret_cast<float*>(ws));
   if (e == hipErrorNotSupported) return W4_ERR_PATH;
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
@@ -498,11 +526,12 @@ size_t w4_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b, int path, in
   if (n < 1 || k < g || k % g || b < 1 || b > W4_MAX_BATCH || n >= kMaxDim || k >= kMaxDim) return 0;
   switch (path) {
     case W4_PATH_SPLITK: return splitk_bytes(n, b, split_k > 1 ? split_k : 4);
+    case W4_PATH_MFMA: return split_k > 1 ? splitk_bytes(n, b, split_k) : 0;
     case W4_PATH_TWOPASS: return (size_t)n * (size_t)k * 2;
     case W4_PATH_AUTO: {
-      if (b > kMaxGemvBatch) return 0;
-      const int s = auto_splits(n, k, (int)b);
-      return s > 1 ? splitk_bytes(n, b, s) : 0;
+      int sk = 1;
+      const int p = w4_auto_path(fmt, n, k, b, SIZE_MAX, &sk);
+      return (p == W4_PATH_SPLITK || p == W4_PATH_MFMA) && sk > 1 ? splitk_bytes(n, b, sk) : 0;
     }
     default: return 0;
   }
@@ -560,6 +589,8 @@ int w4_auto_path(int fmt, int64_t n, int64_t k, int64_t b, size_t workspace_byte
     path = W4_PATH_TILED;
   } else if (prefer_mfma(n, k, b) || !plan_gemv(n, k, (int)b, 1, &p)) {
     path = W4_PATH_MFMA;
+    s = auto_mfma_splits(n, k, b);
+    if (s > 1 && workspace_bytes < splitk_bytes(n, b, s)) s = 1;
   } else {
     s = auto_splits(n, k, (int)b);
     if (s > 1 && workspace_bytes >= splitk_bytes(n, b, s)) {
@@ -600,8 +631,15 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
         return W4_ERR_ALIAS;
       return run_gemv(x, packed, scales, fmt, n, k, b, y, split_k, workspace, s);
     }
-    case W4_PATH_MFMA:
-      return run_mfma(x, packed, scales, fmt, n, k, b, y, s);
+    case W4_PATH_MFMA: {
+      if (split_k <= 1) return run_mfma(x, packed, scales, fmt, n, k, b, y, s);
+      if (split_k > W4_MAX_SPLIT_K) return W4_ERR_PATH;
+      const size_t used = splitk_bytes(n, b, split_k);
+      if (!workspace || workspace_bytes < used) return W4_ERR_WORKSPACE;
+      if (workspace_overlaps_inputs(workspace, used, x, packed, scales, fmt, n, k, b))
+        return W4_ERR_ALIAS;
+      return run_mfma(x, packed, scales, fmt, n, k, b, y, s, split_k, workspace);
+    }
     case W4_PATH_TILED:
       return run_tiled(x, packed, scales, fmt, n, k, b, y, s);
     case W4_PATH_TWOPASS: {

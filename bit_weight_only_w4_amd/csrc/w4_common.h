@@ -180,11 +180,17 @@ hipError_t launch_dequant_f16(int fmt, const uint8_t* packed, const void* scales
                               int64_t k, uint16_t* w_hat, hipStream_t s);
 hipError_t launch_dense_gemv(int fmt, const uint16_t* x, const uint16_t* w_hat, int64_t n,
                              int64_t k, int64_t b, float* y, hipStream_t s);
+// MFMA path.  splits > 1 (one member only): K in `splits` ranges of whole quads (fewer when the
+// quads do not fill them), each range's partial sums in ws[split][B][N] (fp32), then the
+// fixed-order reduction into y; mfma_splits_used gives the number of ranges (0: no plan).
 hipError_t launch_mfma(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
-                       int64_t n, int64_t k, int64_t b, float* y, hipStream_t s);
+                       int64_t n, int64_t k, int64_t b, float* y, hipStream_t s, int splits = 1,
+                       float* ws = nullptr);
 hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
                                const void* const* scales, const int64_t* ns, float* const* y,
-                               int64_t k, int64_t b, hipStream_t s);
+                               int64_t k, int64_t b, hipStream_t s, int splits = 1,
+                               float* ws = nullptr);
+int mfma_splits_used(int64_t n, int64_t k, int64_t b, int splits);
 hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
                        int64_t n, int64_t k, int64_t m, float* y, hipStream_t s);
 hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu, const float* scale,

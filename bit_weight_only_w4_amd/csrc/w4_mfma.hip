@@ -12,7 +12,7 @@ namespace w4 {
 // the runtime's occupancy for the LDS in use), and a workgroup walks several row tiles when there
 // are more tiles than that.
 struct MfmaPlan {
-  int tiles, kw, qpk, qpp, xrow, red, lds, ntiles, slices;
+  int tiles, kw, qpk, qpp, xrow, red, lds, ntiles, slices, qps, splits;
 };
 
 // Row tiles of `rows` rows over the members of a launch.
@@ -22,13 +22,17 @@ int64_t member_tiles(const int64_t* ns, int groups, int64_t rows) {
   return t;
 }
 
-bool plan_slice(const int64_t* ns, int groups, int64_t k, int64_t b, int t, MfmaPlan* p) {
-  const int64_t quads = (k + kQuad - 1) / kQuad;
+bool plan_slice(const int64_t* ns, int groups, int64_t k, int64_t b, int t, int splits,
+                MfmaPlan* p) {
+  // With split-K the rules below see one split's quads and count every split's workgroups.
+  const int64_t quads_all = (k + kQuad - 1) / kQuad;
+  splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, quads_all));
+  const int64_t quads = (quads_all + splits - 1) / splits;
   const int64_t cus = device_cu_count();
-  const int slices = (int)((b + 16 * t - 1) / (16 * t));
+  const int slices = (int)((b + 16 * t - 1) / (16 * t)) * splits;
   const int64_t rows_held = std::min<int64_t>(16 * t, b);
   int kw = 1;
-  if (quads <= 12) {
+  if (quads <= 12 && splits == 1) {
     // Rows of at most 3072 weights (measured on MI355X over the 1536-wide decode shapes at
     // B = 4..32): with one batch tile, eight K groups (one quad per wave, idle groups past K
     // reading zeros) beat fewer on every matrix that does not keep each resident workgroup busy
@@ -44,7 +48,9 @@ bool plan_slice(const int64_t* ns, int groups, int64_t k, int64_t b, int t, Mfma
       }
     }
   } else {
-    // Longer rows: the fewest K groups that give every CU a row tile.
+    // Longer rows, or split-K (whose splits already supply the parallelism): the fewest K groups
+    // that give every CU a row tile, which keeps row tiles tall and each activation loaded into
+    // the window serving the most weight rows.
     for (int c = 1; c <= max_kw(t); c *= 2) {
       if (c > quads) break;
       kw = c;
@@ -73,14 +79,18 @@ bool plan_slice(const int64_t* ns, int groups, int64_t k, int64_t b, int t, Mfma
   p->red = (int)red;
   p->lds = (int)(red + window(qpp));  // dynamic LDS
   p->ntiles = (int)member_tiles(ns, groups, 16 * (8 / kw));
-  p->slices = slices;
+  p->slices = slices / splits;
+  // Split z owns quads [z qps, (z + 1) qps); the last one may run past K (reads zeros), none is
+  // empty.
+  p->qps = splits > 1 ? (int)(kw * qpk) : 0;
+  p->splits = splits > 1 ? (int)((quads_all + p->qps - 1) / p->qps) : 1;
   return true;
 }
 
 // Batch tiles per slice: the largest T (8, 4, 2, 1; at most what B needs) whose launch has at
 // least half a row tile per CU; slices beyond the first re-read the weights (mostly from L2).
 // Offsets are 32-bit: a slice's activations (16 T K 2 bytes) and K itself are bounded below.
-bool plan_mfma(const int64_t* ns, int groups, int64_t k, int64_t b, MfmaPlan* out) {
+bool plan_mfma(const int64_t* ns, int groups, int64_t k, int64_t b, int splits, MfmaPlan* out) {
   int64_t n_total = 0;
   for (int g = 0; g < groups; ++g) n_total += ns[g];
   if (b < 1 || b > W4_MAX_BATCH || k >= ((int64_t)1 << 22) || n_total >= ((int64_t)1 << 31) ||
@@ -93,12 +103,12 @@ bool plan_mfma(const int64_t* ns, int groups, int64_t k, int64_t b, MfmaPlan* ou
   MfmaPlan best{};
   for (int t = tmax; t >= 1; t /= 2) {
     MfmaPlan p;
-    if (!plan_slice(ns, groups, k, b, t, &p)) continue;
+    if (!plan_slice(ns, groups, k, b, t, splits, &p)) continue;
     if (!found || (int64_t)p.ntiles * p.slices > (int64_t)best.ntiles * best.slices) {
       best = p;
       found = true;
     }
-    if ((int64_t)p.ntiles * p.slices * 2 >= cus) {
+    if ((int64_t)p.ntiles * p.slices * p.splits * 2 >= cus) {
       best = p;
       break;
     }
@@ -111,10 +121,11 @@ bool plan_mfma(const int64_t* ns, int groups, int64_t k, int64_t b, MfmaPlan* ou
 // row tiles of every member on grid.x.
 hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
                                const void* const* scales, const int64_t* ns, float* const* y,
-                               int64_t k, int64_t b, hipStream_t s) {
+                               int64_t k, int64_t b, hipStream_t s, int splits, float* ws) {
   if (groups < 1 || groups > kMaxGroup) return hipErrorInvalidValue;
+  if (splits > 1 && (groups != 1 || ws == nullptr)) return hipErrorInvalidValue;
   MfmaPlan p;
-  if (!plan_mfma(ns, groups, k, b, &p)) return hipErrorNotSupported;
+  if (!plan_mfma(ns, groups, k, b, splits, &p)) return hipErrorNotSupported;
   MfmaArgs a;
   memset(&a, 0, sizeof(a));
   const int64_t rows = 16 * (8 / p.kw);
@@ -122,7 +133,7 @@ hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uin
   for (int g = 0; g < groups; ++g) {
     a.m[g].packed = packed[g];
     a.m[g].scales = scales[g];
-    a.m[g].y = y[g];
+    a.m[g].y = p.splits > 1 ? ws : y[g];
     a.m[g].n = (uint32_t)ns[g];
     a.m[g].tile0 = tile0;
     tile0 += (uint32_t)((ns[g] + rows - 1) / rows);
@@ -136,6 +147,8 @@ hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uin
   a.xrow = (uint32_t)p.xrow;
   a.red_bytes = (uint32_t)p.red;
   a.tiles = (uint32_t)p.ntiles;
+  a.qps = (uint32_t)p.qps;
+  a.ysplit = p.splits > 1 ? (uint32_t)(b * ns[0]) : 0u;
   // One member runs the instantiations without member selection (fewer live scalar registers).
   auto run = [&](int op, int grid, int* out) {
     return groups > 1 ? mfma_dispatch_grouped(op, fmt, a, p.tiles, p.kw, p.lds, grid, p.slices, out, s)
@@ -145,16 +158,28 @@ hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uin
   hipError_t e = run(0, 0, &resident);
   if (e != hipSuccess) return e;
   if (resident < 1) return hipErrorNotSupported;
-  const int64_t fit = std::max<int64_t>(1, (int64_t)device_cu_count() * resident / p.slices);
+  const int64_t fit =
+      std::max<int64_t>(1, (int64_t)device_cu_count() * resident / (p.slices * p.splits));
   const int grid = (int)std::min<int64_t>(p.ntiles, fit);
   a.tiles_base = (uint32_t)(p.ntiles / grid);
   a.tiles_rem = (uint32_t)(p.ntiles % grid);
-  return run(1, grid, nullptr);
+  e = run(1, grid, nullptr);
+  if (e != hipSuccess || p.splits == 1) return e;
+  // the splits' partial sums, added in split order (bitwise reproducible), overwrite y
+  return launch_splitk_reduce(ws, y[0], b * ns[0], p.splits, s);
 }
 
 hipError_t launch_mfma(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
-                       int64_t n, int64_t k, int64_t b, float* y, hipStream_t s) {
-  return launch_mfma_members(fmt, x, 1, &packed, &scales, &n, &y, k, b, s);
+                       int64_t n, int64_t k, int64_t b, float* y, hipStream_t s, int splits,
+                       float* ws) {
+  return launch_mfma_members(fmt, x, 1, &packed, &scales, &n, &y, k, b, s, splits, ws);
+}
+
+int mfma_splits_used(int64_t n, int64_t k, int64_t b, int splits) {
+  if (splits <= 1) return 1;
+  MfmaPlan p;
+  if (!plan_mfma(&n, 1, k, b, splits, &p)) return 0;
+  return p.splits;
 }
 
 }  // namespace w4

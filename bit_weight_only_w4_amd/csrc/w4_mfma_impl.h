@@ -64,6 +64,9 @@ struct MfmaArgs {
   uint32_t tiles;      // row tiles (16 RW rows each) in all
   uint32_t tiles_base;  // tiles per workgroup: tiles_base, plus one for blockIdx.x < tiles_rem
   uint32_t tiles_rem;
+  uint32_t qps;        // split-K (grid.z > 1): quads per split, KW * qpk; split z owns quads
+                       // [z qps, (z + 1) qps) and writes its partial sums to y + z * ysplit
+  uint32_t ysplit;     // floats between the partial planes of consecutive splits (B * N)
 };
 
 namespace {
@@ -126,6 +129,8 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   const uint32_t b0 = blockIdx.y * 16u * T;
   const uint32_t bsl = min(16u * T, a.b - b0);
   const uint16_t* xsl = a.x + (size_t)b0 * k;
+  // Split-K: this workgroup's first quad of K (0 without a split).
+  const uint32_t zq = blockIdx.z * a.qps;
   const __amdgpu_buffer_rsrc_t rx_ = make_rsrc(xsl, bsl * k * 2u);
 
   // The workgroup's row tiles: blockIdx.x, blockIdx.x + gridDim.x, ... (ntiles of them).
@@ -178,11 +183,12 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
       set_tile(c);
     }
   };
-  // The quad at the cursor: blocks qb .. qb + QC - 1 of the K group, qb = (kg * qpk + q) * QC.
+  // The quad at the cursor: blocks qb .. qb + QC - 1 of the K group,
+// qb = (z qps + kg * qpk + q) * QC.
   // Blocks past K read as zero (their weights and scales), which adds nothing.  Each lane's 16
   // bytes lie inside one block.
   auto load_quad = [&](const Cursor& cur, Quad<FMT>& d) __attribute__((always_inline)) {
-    const uint32_t qb = ((uint32_t)kg * a.qpk + (uint32_t)cur.q) * QC;
+    const uint32_t qb = (zq + (uint32_t)kg * a.qpk + (uint32_t)cur.q) * QC;
     const uint32_t wq = qb * (KC / 2);  // byte offset of the quad segment in a row
     const uint32_t sbase = slane + qb * SB;
 #pragma unroll
@@ -216,7 +222,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   };
 
   // x window of phase p: for every batch row r < bsl and K group kk, the quads
-  // kk * qpk + p * qpp .. + qpp - 1 that the K group has (other pieces read as zero).  The window
+  // z qps + kk * qpk + p * qpp .. + qpp - 1 that the K group has (other pieces read as zero).  The window
   // is copied straight from global memory into LDS (buffer loads with the LDS destination): the
   // 16-byte slot s = base + tid receives thread tid's load, so slot s holds piece
   // col = s % P of row r = s / P, P = KW * seg + 1 pieces per row, the last one padding (it puts
@@ -241,7 +247,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
       const uint32_t kk = (uint32_t)(((float)col + 0.5f) * inv_seg);
       const uint32_t pc = col - kk * seg;
       const uint32_t ql = q0 + (pc >> 5);  // quad inside the K group
-      const uint32_t kpos = (kk * a.qpk + ql) * kQuad + (pc & 31u) * 8u;
+      const uint32_t kpos = (zq + kk * a.qpk + ql) * kQuad + (pc & 31u) * 8u;
       const bool have = sl < slots && kk < (uint32_t)KW && ql < a.qpk && kpos < k;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx_, (__attribute__((address_space(3))) void*)(xs + (base + (uint32_t)wave * 64u) * 16u), 16,
@@ -289,7 +295,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
 
   // Multiply the quad held in d: quad q of the K group, wq = its index inside the current window.
   auto compute = [&](int q, int wq, const Quad<FMT>& d) __attribute__((always_inline)) {
-    const uint32_t qb = ((uint32_t)kg * a.qpk + (uint32_t)q) * QC;  // its first scale block
+    const uint32_t qb = (zq + (uint32_t)kg * a.qpk + (uint32_t)q) * QC;  // its first scale block
     // this lane's 2 (NF4) or 4 (INT4) dwords of packed bytes per block
     // Chunks g and g + 4 of row m: keep the own one, take the partner's by a rotation of 8 lanes.
     uint32_t wh[2][4];
@@ -388,7 +394,7 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
     const MfmaMember mm = member(tg);
     const uint32_t n = mm.n;
     const uint32_t row_d = ((tg - mm.tile0) * RW + rg) * 16u + 4u * g;
-    float* ysl = mm.y + (size_t)b0 * n;
+    float* ysl = mm.y + (size_t)blockIdx.z * a.ysplit + (size_t)b0 * n;
     if constexpr (KW > 1) {
       __syncthreads();  // the previous tile's sums have been read
       if (kg > 0) {
@@ -493,8 +499,11 @@ int resident_kw(int lds) {
 
 template <int FMT, int XT, int T, int KW, bool GROUPED>
 hipError_t launch_kw(const MfmaArgs& a, int lds, int grid, int slices, hipStream_t s) {
-  hipLaunchKernelGGL((mfma_kernel<FMT, XT, T, KW, GROUPED>), dim3((unsigned)grid, (unsigned)slices),
-                     dim3(kThreads), (unsigned)lds, s, a);
+  const uint32_t quads = (a.k + kQuad - 1) / kQuad;
+  const uint32_t splits = a.qps ? (quads + a.qps - 1) / a.qps : 1u;
+  hipLaunchKernelGGL((mfma_kernel<FMT, XT, T, KW, GROUPED>),
+                     dim3((unsigned)grid, (unsigned)slices, (unsigned)splits), dim3(kThreads),
+                     (unsigned)lds, s, a);
   return hipGetLastError();
 }
 

@@ -91,7 +91,12 @@ typedef enum {
                           My Triton Kernel Ties bitsandbytes, "The kernels", v3 and its
                           stale-output bug)                                                  */
   W4_PATH_MFMA = 3,    /* decode W on chip, MFMA against x, 1 <= B <= W4_MAX_BATCH (W4_PATH_AUTO
-                          takes it from B = 4, or B = 3 for matrices of 64 MiB and more)   */
+                          takes it from B = 4, or B = 3 for matrices of 64 MiB and more).
+                          With split_k >= 2: K in split_k ranges of whole 256-weight quads
+                          (fewer when the quads do not fill them), each range's partial sums
+                          into an fp32 workspace, then the same fixed-order sum as
+                          W4_PATH_SPLITK; W4_PATH_AUTO splits rows longer than 3072 weights
+                          when the workspace holds the partials                              */
   W4_PATH_TWOPASS = 4, /* ablation: dequantize W to fp16 in the workspace, then a dense GEMV/GEMM
                           (the out-of-place path of LLM Quantization on RTX 4060, "The
                           Quantization Tax: A Byte-Accounting Model")                        */
@@ -270,11 +275,13 @@ int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* 
                                int fmt, int64_t K, int64_t B, void* stream);
 
 /* w4_matmul_ex: the same operation with an explicit path, split count and workspace (tests and
- * the ablation benchmark).  path = W4_PATH_AUTO also considers split-K when a workspace is given.
+ * the ablation benchmark).  path = W4_PATH_AUTO also considers split-K (fused GEMV or MFMA) when a
+ * workspace is given: w4_workspace_bytes(..., W4_PATH_AUTO, 0) is the size that lets it.
  * The bytes a path writes into the workspace must not overlap x, packed, scales or y
  * (W4_ERR_ALIAS).
- *   split_k          number of K ranges for W4_PATH_SPLITK (2..W4_MAX_SPLIT_K); 0 = library choice;
- *                    ignored by the other paths
+ *   split_k          number of K ranges for W4_PATH_SPLITK (2..W4_MAX_SPLIT_K; 0 = 4) and for
+ *                    W4_PATH_MFMA (2..W4_MAX_SPLIT_K; 0 or 1 = one pass); ignored by the other
+ *                    paths.  Either split path needs 4 * split_k * B * N workspace bytes.
  *   workspace        device memory of at least w4_workspace_bytes(...) bytes, 16-byte aligned;
  *                    may be NULL when that size is 0.  Its contents are scratch on entry and exit.
  *                    Two calls in flight must not share one workspace.
@@ -299,9 +306,10 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
 int w4_matmul_splitk_noalloc(const void* x, const uint8_t* packed, const void* scales, int fmt,
                              int64_t N, int64_t K, int64_t B, float* y, int split_k, void* stream);
 
-/* Bytes of workspace w4_matmul_ex needs for (fmt, N, K, B, path, split_k): split-K needs
- * 4 * S * B * N, two-pass 2 * N * K, the single-pass paths 0; W4_PATH_AUTO reports the split-K
- * size it would use.  Returns 0 for invalid arguments. */
+/* Bytes of workspace w4_matmul_ex needs for (fmt, N, K, B, path, split_k): split-K (the GEMV's,
+ * or the MFMA path's with split_k >= 2) needs 4 * S * B * N, two-pass 2 * N * K, the single-pass
+ * paths 0; W4_PATH_AUTO reports the split-K size it would use given that much workspace.
+ * Returns 0 for invalid arguments. */
 size_t w4_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t B, int path, int split_k);
 
 /* The path (w4_path_t) and split count W4_PATH_AUTO would run for these arguments when given

@@ -157,6 +157,31 @@ def test_workspace_and_plan_logic():
     assert w4.workspace_bytes("nf4_f16", 8960, 1536, 512, "tiled") == 0
 
 
+def test_mfma_split_rule():
+    """The automatic MFMA split-K count (host logic; the CU count falls back to MI355X's 256 where
+    no GPU is visible): rows of at most 3072 weights never split; longer rows take the smallest
+    power of two that keeps held rows x K / S x 2 bytes within 128 KiB and gives two 16-row tiles
+    per CU, at most 16, each range at least two quads; only with a large enough workspace."""
+    w4, _ = _lib()
+    big = 1 << 30
+    assert w4.auto_path("nf4_f16", 1536, 8960, 8) == ("mfma", 1)  # no workspace: one pass
+    assert w4.auto_path("nf4_f16", 1536, 8960, 8, big) == ("mfma", 8)  # 2 by x, 8 by the tiles
+    assert w4.auto_path("nf4_f16", 1536, 8960, 8, 8 * 8 * 1536 * 4 - 1) == ("mfma", 1)
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 8) == 8 * 8 * 1536 * 4
+    assert w4.auto_path("nf4_f16", 8192, 28672, 32, big) == ("mfma", 16)  # x: 32*28672*2/128Ki = 14
+    assert w4.auto_path("nf4_f16", 8192, 8192, 8, big) == ("mfma", 1)  # exactly 128 KiB
+    assert w4.auto_path("nf4_f16", 8192, 8192, 16, big) == ("mfma", 2)
+    assert w4.auto_path("int4_bf16", 1024, 8192, 4, big) == ("mfma", 8)
+    assert w4.auto_path("nf4_f16", 8960, 1536, 32, big) == ("mfma", 1)  # 6 quads: never
+    assert w4.auto_path("nf4_f16", 1536, 3072, 8, big) == ("mfma", 1)  # 12 quads: never
+    assert w4.auto_path("nf4_f16", 64, 3328, 8, big) == ("mfma", 4)  # 13 quads: >= 2 per range
+    assert w4.workspace_bytes("nf4_f16", 8960, 1536, 8) == 0
+    assert w4.auto_path("nf4_f16", 128256, 8192, 32, big) == ("mfma", 1)  # 1002 tiles of 128 rows
+    assert w4.auto_path("nf4_f16", 28672, 8192, 32, big) == ("mfma", 4)
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 8, "mfma", 4) == 4 * 8 * 1536 * 4
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 8, "mfma", 1) == 0
+
+
 def _grouped(L, n=(64, 32, 32), x=FAKE, p=None, s=None, y=None, fmt=1, k=256, b=1, groups=None,
              entry="w4_gemv_grouped"):
     vp = ctypes.c_void_p

@@ -33,7 +33,8 @@ def _workspace(nbytes):
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("n,k,b", [(256, 1536, 1), (37, 384, 1), (1, 128, 1), (300, 1536, 2),
-                                   (129, 8960, 1), (77, 8192, 3), (64, 28672, 1), (200, 1536, 4),
+                                   (129, 8960, 1), (129, 8960, 2), (77, 8192, 3), (64, 28672, 1),
+                                   (200, 1536, 4),
                                    (45, 1024, 5), (96, 2048, 8), (33, 640, 7), (250, 256, 6)])
 def test_gemv_parity(fmt, n, k, b):
     import bit_weight_only_w4_amd as w4

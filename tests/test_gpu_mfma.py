@@ -140,3 +140,39 @@ def test_smallbatch_grouped_below_threshold_is_the_grouped_gemv():
     c = w4.gemv_grouped(xd, packed, scales, fmt)
     for ya, yc in zip(a, c):
         assert torch.equal(ya, yc)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("n,k,b,splits", [(130, 8960, 8, 5), (96, 1536, 16, 2), (70, 2048, 33, 3),
+                                          (40, 384, 4, 8), (200, 8192, 8, 4), (17, 1024, 129, 2)])
+def test_mfma_splitk_parity(fmt, n, k, b, splits):
+    """MFMA split-K (K in ranges of whole 256-weight quads, partial sums in the workspace, then the
+    fixed-order reduction) against the oracle; y pre-filled with NaN and the workspace dirty, so a
+    result that misses a split or accumulates into y fails.  Includes more splits than quads."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n + k + b + splits)
+    wsb = w4.workspace_bytes(fmt, n, k, b, "mfma", splits)
+    assert wsb == splits * b * n * 4
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device=xd.device)
+    y = torch.full((b, n), float("nan"), device=xd.device)
+    w4.matmul_ex(xd, p, s, fmt, path="mfma", split_k=splits, workspace=ws, y=y)
+    g.assert_y_close(fmt, y, x, pr, sr)
+    y2 = w4.matmul_ex(xd, p, s, fmt, path="mfma", split_k=splits, workspace=ws)
+    assert torch.equal(y, y2)
+
+
+def test_mfma_splitk_needs_workspace():
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    fmt, n, k, b = "nf4_f16", 64, 2048, 8
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=9)
+    small = torch.empty(4 * b * n * 4 - 16, dtype=torch.uint8, device=xd.device)
+    with pytest.raises(RuntimeError, match="workspace"):
+        w4.matmul_ex(xd, p, s, fmt, path="mfma", split_k=4, workspace=small)
+    with pytest.raises(RuntimeError, match="workspace"):
+        w4.matmul_ex(xd, p, s, fmt, path="mfma", split_k=4)
