@@ -211,9 +211,10 @@ int pow2_at_least(int64_t v) {
 }
 
 // Split count of the automatic MFMA path (used when the caller's workspace holds the partial
-// sums).  Rows of at most 12 quads (3072 weights) never split, nor matrices with two 128-row
-// tiles per CU (128256 x 8192 at B = 32: 205 us split 4 ways against 195 unsplit, the partial
-// sums adding 12% to the traffic).  Longer rows split K into the
+// sums).  Rows of at most 12 quads (3072 weights) never split, nor batches above 64 (1536 x 8960
+// at B = 128: 25.3 us split 16 ways against 24.5 unsplit), nor matrices with two 128-row tiles
+// per CU (128256 x 8192 at B = 32: 205 us split 4 ways against 195 unsplit, the partial sums
+// adding 12% to the traffic).  Longer rows split K into the
 // smallest power of two of ranges that (a) keeps one range's activation window, held rows x K / S
 // x 2 bytes, within 128 KiB, and (b) gives matrices of few rows two row tiles of 16 rows per CU;
 // at most 16 ranges, each of at least two quads.  Measured on MI355X (NF4 x fp16, rotated
@@ -223,7 +224,7 @@ int pow2_at_least(int64_t v) {
 // against 59.3 unsplit (49.1 at S = 8).  Non-power-of-two counts measured slower throughout.
 int auto_mfma_splits(int64_t n, int64_t k, int64_t b) {
   const int64_t quads = (k + 255) / 256;
-  if (quads <= 12 || (n + 127) / 128 >= 2 * device_cu_count()) return 1;
+  if (quads <= 12 || b > 64 || (n + 127) / 128 >= 2 * device_cu_count()) return 1;
   const int64_t rows = std::min<int64_t>(b, 128);
   const int sx = pow2_at_least((rows * k * 2 + 131071) / 131072);
   const int sp = pow2_at_least((2 * device_cu_count() * 16 + n - 1) / n);

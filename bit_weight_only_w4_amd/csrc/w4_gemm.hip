@@ -340,6 +340,7 @@ hipError_t launch_wm(const GemmArgs& a, hipStream_t s) {
 template <int FMT, int XT>
 hipError_t launch_fx(const GemmArgs& a, int wn, int wm, int kw, hipStream_t s) {
   if (wn == 2 && wm == 4 && kw == 2) return launch_wm<FMT, XT, 2, 4, 2>(a, s);
+  if (wn == 2 && wm == 4 && kw == 1) return launch_wm<FMT, XT, 2, 4, 1>(a, s);
   if (wn == 4 && wm == 4 && kw == 1) return launch_wm<FMT, XT, 4, 4, 1>(a, s);
   return hipErrorInvalidValue;
 }
@@ -355,10 +356,16 @@ hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const 
   const int64_t cus = device_cu_count();
   const int wm = 4;
   const int64_t mt = (m + 32 * wm - 1) / (32 * wm);
-  // Two workgroups of 128 x 128 per CU when there are that many tiles; else 64 x 128 tiles with
-  // two K groups (twice the waves per tile, half the blocks per wave).
+  // Two workgroups of 128 x 128 per CU when there are that many tiles; else 64 x 128 tiles, with
+  // one K group when those make two workgroups per CU, two K groups (twice the waves per tile,
+  // half the blocks per wave) when they do not.  Measured on MI355X at 512 activation rows (NF4 x
+  // fp16): 8960 x 1536 takes 41.7 us with 64 x 128 tiles and one K group against 47.2 with two and
+  // 47.0 with 128 x 128 tiles; 1536 x 8960 71.9 us with two K groups against 85.5 with one;
+  // 151936 x 1536 and 28672 x 8192 are fastest with 128 x 128 tiles (431 and 410 us).  Larger
+  // tiles (128 x 256 or 256 x 128 per workgroup, one wave per SIMD) measured 1.4-5x slower.
   const bool full = ((n + 127) / 128) * mt >= 2 * cus;
-  const int wn = full ? 4 : 2, kw = full ? 1 : 2;
+  const bool half = !full && ((n + 63) / 64) * mt >= 2 * cus;
+  const int wn = full ? 4 : 2, kw = full || half ? 1 : 2;
   const int64_t nt = (n + 32 * wn - 1) / (32 * wn);
   if (nt * mt >= ((int64_t)1 << 31)) return hipErrorNotSupported;
   GemmArgs a;

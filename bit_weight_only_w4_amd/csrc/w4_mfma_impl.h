@@ -262,15 +262,18 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   ld.ti = 0;
   ld.q = 0;
   set_tile(ld);
-  // Two quads go out before the window and the table, the other two after the barrier (which
-  // waits for every load in flight): the prologue's loads stay few.
+  // Two quads go out before the table and the window, the other two after the barrier (which
+  // waits for every load in flight): the prologue's loads stay few.  The table is written before
+  // the window's buffer-to-LDS loads are issued: written after them, its LDS stores had to wait
+  // for every load in flight (the compiler cannot tell the two LDS areas apart), which put the
+  // fill behind a full memory round trip (0.1 us on the 1536-wide shapes at B = 8).
   Quad<FMT> P0, P1, P2, P3;
   load_quad(ld, P0);
   advance(ld);
   load_quad(ld, P1);
   advance(ld);
-  load_x(0);
   fill_table<FMT, XT, kThreads>(tab);
+  load_x(0);
   __syncthreads();
   if constexpr (R == 4) {
     load_quad(ld, P2);

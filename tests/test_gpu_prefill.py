@@ -87,7 +87,8 @@ def test_prefill_entry_auto_and_determinism(fmt):
                                        ("nf4_bf16", 1536, 8960, 512), ("int4_f16", 28672, 8192, 512),
                                        ("nf4_f16", 8960, 1536, 4096), ("fp4_bf16", 8960, 1536, 512),
                                        ("fp4_f16", 28672, 8192, 512), ("int4a_bf16", 151936, 1536, 512),
-                                       ("int4a_f16", 8960, 1536, 1024)])
+                                       ("int4a_f16", 8960, 1536, 1024), ("nf4_f16", 8960, 1536, 512),
+                                       ("nf4_bf16", 8960, 1536, 512), ("int4a_bf16", 8960, 1536, 512)])
 def test_tiled_full_size_sampled(fmt, n, k, b):
     """Full-size prefill matrices at 512 tokens (and 4096, the largest batch): weights drawn on the
     GPU, quantized there, and 160 sampled rows (the first and the last among them) checked
