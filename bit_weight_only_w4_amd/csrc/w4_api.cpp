@@ -291,6 +291,17 @@ int run_gemv_members(const void* x, int groups, const uint8_t* const* packed,
   a.cps = p.cps;
   a.team = p.team;
   a.iters = p.iters;
+  // The small decode table (a quarter of the 64 KiB fill, lookups with up to 4-way bank
+  // conflicts) for 4-byte entries always: measured on MI355X (NF4 x fp16 decode step, rotated
+  // per-kind times) it is faster on every launch kind, q|k|v 3.27 -> 3.10 us, gate|up 6.86 ->
+  // 6.59, down 5.50 -> 5.03, lm_head 24.6 -> 24.3, step 535 -> 509 us: the fill's stores and its
+  // barrier sit on each workgroup's critical path, the lookups' conflicts mostly do not.  NF4 x
+  // bf16's 8-byte entries (8 copies in the small table) only where each workgroup streams one row
+  // block of one chunk per lane or runs 256 threads: there q|k|v 3.38 -> 3.18 us and down 5.89 ->
+  // 5.57, while gate|up (7.56 -> 8.06) and lm_head (26.8 -> 35.3) lose to the conflicts.
+  bool one_trip = p.iters == 1;
+  for (int g = 0; g < groups; ++g) one_trip = one_trip && nrb[g] <= grid_g[g];
+  a.small_table = fmt != W4_NF4_X_BF16 || one_trip || p.threads == 256 ? 1 : 0;
   if (launch_gemv(fmt, (int)b, a, groups, p, st) != hipSuccess) return W4_ERR_HIP;
   if (splits > 1) {
     if (launch_splitk_reduce(reinterpret_cast<const float*>(ws), y[0], b * n[0], splits, st) !=

@@ -144,6 +144,8 @@ struct GemvArgsT {
   int cps;            // chunks per split
   int team;
   int iters;
+  int small_table;    // 1: the decode table holds 16 copies of each entry (4-byte entries; 8 of
+                      // the 8-byte ones), written 4x faster, read with up to 4-way conflicts
 };
 using GemvArgs = GemvArgsT<kMaxGroup>;
 

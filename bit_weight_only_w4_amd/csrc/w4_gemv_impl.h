@@ -19,9 +19,12 @@
 //     to valid ones and skipped by index when computing), so no branch joins force early waits.
 //   * Decode (NF4): a 256-entry table in LDS maps a packed byte to the pair (value of the high
 //     nibble, value of the low nibble) in the activation's 16-bit type; one ds_read_b32 decodes two
-//     weights.  The table holds 64 copies of each entry, copy c in bank c, and lane L reads copy L,
-//     so the lookups of a wave never conflict.  Its LDS address, byte value * 256 + lane * 4, is
-//     built by one v_perm_b32.  The table is written while the first loads are in flight.  FP4
+//     weights.  Each entry owns 256 bytes of LDS.  The full table holds 64 copies of each entry,
+//     copy c in bank c, lane L reading copy L, so the lookups of a wave never conflict; the small
+//     one holds 16 copies (lane L reads copy L & 15; lanes 16 apart share a bank) and takes a
+//     quarter of the stores to write, which the host prefers where the fill costs more than the
+//     conflicts.  The LDS address, byte value * 256 + lane offset, is built by one v_perm_b32.
+//     The table is written while the first loads are in flight.  FP4
 //     needs no table: gfx950 converts a byte of two E2M1 codes to a 16-bit pair in one
 //     instruction (the pair comes out odd k first, so FP4 holds its activation pairs swapped).
 //     INT4 and asymmetric INT4 skip it where that measured faster (see table_free): a nibble q
@@ -94,11 +97,16 @@ __device__ inline void lane_decode(uint32_t& v1, uint32_t& v2) {
   }
 }
 
-// Write the 64 KiB table.  Thread t writes 16-byte slots t, t + NT, ...; slot i belongs to entry
-// i >> 4, whose high nibble (i >> 8) is the same for the whole wave (read with v_readlane) and
-// whose low nibble ((i >> 4) & 15) is fixed per lane when NT >= 256.
-template <int FMT, int XT, int NT>
+// Write the table.  Each entry has 256 bytes of LDS; the full table fills all of them (64 copies
+// of a 4-byte entry, 32 of an 8-byte one: 16 slots of 16 bytes), the small one the first 64
+// bytes (SPE = 4 slots: 16 or 8 copies), a quarter of the stores for launches whose workgroups
+// look up too few bytes to notice the conflicts (lanes L, L + 16, L + 32, L + 48 then share a
+// bank).  Thread t writes slots t, t + NT, ...; slot i belongs to entry i / SPE, whose high nibble
+// (i / 16 SPE) is the same for the whole wave (read with v_readlane) and whose low nibble
+// ((i / SPE) & 15) is fixed per lane when NT >= 256.
+template <int FMT, int XT, int NT, int SPE>
 __device__ inline void fill_table(uint32_t* tab) {
+  constexpr int kShift = SPE == 16 ? 4 : 2;  // log2(SPE)
   uint32_t v1, v2;
   lane_decode<FMT, XT>(v1, v2);
   constexpr bool kSplit = (FMT == kNF4 && XT == kBF16);
@@ -106,23 +114,24 @@ __device__ inline void fill_table(uint32_t* tab) {
   const int tid = threadIdx.x;
   uint32_t lo1 = 0, lo2 = 0;
   if (NT >= 256) {
-    lo1 = (uint32_t)__shfl((int)v1, (tid >> 4) & 15) << 16;
-    if (kSplit) lo2 = (uint32_t)__shfl((int)v2, (tid >> 4) & 15) << 16;
+    lo1 = (uint32_t)__shfl((int)v1, (tid >> kShift) & 15) << 16;
+    if (kSplit) lo2 = (uint32_t)__shfl((int)v2, (tid >> kShift) & 15) << 16;
   }
 #pragma unroll 4
-  for (int j = 0; j < kTableBytes / 16 / NT; ++j) {
+  for (int j = 0; j < 256 * SPE / NT; ++j) {
     const int i = tid + NT * j;
-    const int hi = __builtin_amdgcn_readfirstlane(i >> 8);
+    const int hi = __builtin_amdgcn_readfirstlane(i >> (kShift + 4));
     if (NT < 256) {
-      lo1 = (uint32_t)__shfl((int)v1, (i >> 4) & 15) << 16;
-      if (kSplit) lo2 = (uint32_t)__shfl((int)v2, (i >> 4) & 15) << 16;
+      lo1 = (uint32_t)__shfl((int)v1, (i >> kShift) & 15) << 16;
+      if (kSplit) lo2 = (uint32_t)__shfl((int)v2, (i >> kShift) & 15) << 16;
     }
     const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane((int)v1, hi) | lo1;
+    const int slot = SPE == 16 ? i : ((i >> 2) << 4) | (i & 3);
     if (kSplit) {
       const uint32_t p2 = (uint32_t)__builtin_amdgcn_readlane((int)v2, hi) | lo2;
-      t4[i] = make_uint4(p1, p2, p1, p2);
+      t4[slot] = make_uint4(p1, p2, p1, p2);
     } else {
-      t4[i] = make_uint4(p1, p1, p1, p1);
+      t4[slot] = make_uint4(p1, p1, p1, p1);
     }
   }
 }
@@ -158,10 +167,27 @@ __device__ inline uint32_t scale_offset(int chunk) {
          : FMT == kINT4 ? (uint32_t)(chunk >> 2) * 2u
                         : (uint32_t)(chunk >> 1) * 4u;
 }
+// The scale slot of a chunk as loaded: fp32 (NF4, FP4), the 32-bit word (INT4A, as float bits),
+// or the 16 bf16 bits (INT4), widened to fp32 only where the scale is used (scale_value).  Widened
+// at load time, the conversion of every prefetched row block's scales waited for their loads
+// right away (0.2 us per small launch).
 template <int FMT>
-__device__ inline float load_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if (FMT == kINT4) return __uint_as_float(buffer_load16bit(r, off) << 16);  // bf16 -> fp32, exact
-  return __uint_as_float(buffer_load32(r, off));
+using ScaleSlot = typename std::conditional<FMT == kINT4, uint16_t, float>::type;
+template <int FMT>
+__device__ inline ScaleSlot<FMT> load_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (FMT == kINT4) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+  } else {
+    return __uint_as_float(buffer_load32(r, off));
+  }
+}
+template <int FMT>
+__device__ inline float scale_value(ScaleSlot<FMT> slot) {
+  if constexpr (FMT == kINT4) {
+    return __uint_as_float((uint32_t)slot << 16);  // bf16 -> fp32, exact
+  } else {
+    return slot;
+  }
 }
 
 // Launches decoded without the LDS table (no fill, no lookups): FP4 always, through gfx950's
@@ -287,7 +313,7 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   // without touching memory, and need no clamping or branch.
   const uint32_t pitch = (uint32_t)(k >> 1);  // packed bytes per row
   const uint32_t spitch = scale_pitch<FMT>(k);
-  auto load_rb = [&](uint32_t rbv, uint4 (&p)[ITM], float (&s)[ITM]) {
+  auto load_rb = [&](uint32_t rbv, uint4 (&p)[ITM], ScaleSlot<FMT> (&s)[ITM]) {
     // A prefetch past this workgroup's last row block re-reads that block (an L2 hit) rather
     // than switching the resource off, which would need a per-block select of its size.
     const Where w = where(rbv < rb_last ? rbv : rb_last);
@@ -309,7 +335,7 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
 
   // --- first row block, then this lane's activations, then the second row block
   uint4 pA[ITM], pB[ITM], pC[ITM];
-  float sA[ITM], sB[ITM], sC[ITM];
+  ScaleSlot<FMT> sA[ITM], sB[ITM], sC[ITM];
   load_rb(rb0, pA, sA);
   uint32_t xr[ITM][B][16];
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(B * k * 2));
@@ -341,7 +367,11 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
 
   // --- decode table, written while the loads above are in flight
   if constexpr (kTable) {
-    fill_table<FMT, XT, NT>(tab);
+    if (a.small_table) {
+      fill_table<FMT, XT, NT, 4>(tab);
+    } else {
+      fill_table<FMT, XT, NT, 16>(tab);
+    }
     __syncthreads();
   }
 
@@ -373,12 +403,14 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   }
 
   constexpr bool kSplitCode = (FMT == kNF4 && XT == kBF16);
-  const uint32_t laneoff = kSplitCode ? (uint32_t)(lane & 31) * 8u : (uint32_t)lane * 4u;
+  // copy of this lane (see fill_table): 64 / 32 copies, or 16 / 8 in the small table
+  const uint32_t cmask = a.small_table ? (kSplitCode ? 7u : 15u) : (kSplitCode ? 31u : 63u);
+  const uint32_t laneoff = ((uint32_t)lane & cmask) * (kSplitCode ? 8u : 4u);
   const char* tabc = reinterpret_cast<const char*>(tab);
   const int wave = tid >> 6;
   const int waves_per_team = team > 64 ? team >> 6 : 1;
 
-  auto compute_store = [&](uint32_t rbv, const uint4 (&pk)[ITM], const float (&sc)[ITM]) {
+  auto compute_store = [&](uint32_t rbv, const uint4 (&pk)[ITM], const ScaleSlot<FMT> (&sc)[ITM]) {
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
@@ -458,11 +490,13 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
         } else if constexpr (kIntTf) {
           // (q - 8) s = ((M + q) - (M + 8)) s
           constexpr float zc = int4_magic_value<XT>() + 8.0f;
+          const float s = scale_value<FMT>(sc[i]);
 #pragma unroll
-          for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(__builtin_fmaf(-zc, xsum[i][b], d[b]), sc[i], acc[b]);
+          for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(__builtin_fmaf(-zc, xsum[i][b], d[b]), s, acc[b]);
         } else {
+          const float s = scale_value<FMT>(sc[i]);
 #pragma unroll
-          for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(d[b], sc[i], acc[b]);
+          for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(d[b], s, acc[b]);
         }
       }
     }
@@ -525,6 +559,7 @@ hipError_t launch_one(const GemvArgs& full, int groups, const GemvPlan& p, hipSt
   a.cps = full.cps;
   a.team = full.team;
   a.iters = full.iters;
+  a.small_table = full.small_table;
   for (int g = 0; g < G; ++g) a.m[g] = full.m[g];
   (void)groups;
   const dim3 grid(p.grid_x, p.splits, 1);
