@@ -143,13 +143,21 @@ __device__ inline float dpp_f(float v) {
 }
 
 // Sum over a team of `team` (16..64) lanes inside one wave; every lane of the team gets the total.
+// Within a row of 16 lanes by DPP; across rows by gfx950's lane swaps (v_permlane16_swap: rows 0
+// and 1, 2 and 3; v_permlane32_swap: the two halves), VALU operations instead of LDS shuffles.
 __device__ inline float team_sum_wave(float v, int team) {
   v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_f<0x141>(v);  // row_half_mirror
   v += dpp_f<0x140>(v);  // row_mirror: all 16 lanes of a row hold the row sum
-  if (team >= 32) v += __shfl_xor(v, 16);
-  if (team >= 64) v += __shfl_xor(v, 32);
+  if (team >= 32) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(s[0]) + __uint_as_float(s[1]);  // row r: r + (r ^ 1)
+  }
+  if (team >= 64) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(s[0]) + __uint_as_float(s[1]);  // lane l: l + (l ^ 32)
+  }
   return v;
 }
 
