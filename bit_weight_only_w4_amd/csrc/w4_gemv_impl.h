@@ -388,6 +388,19 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   // computed once per launch.
   constexpr bool kXsum = FMT == kINT4A || kIntTf;
   float xsum[kXsum ? ITM : 1][B];
+  if constexpr (kXsum && kTable) {
+    // Keep the sums behind the barrier: computed before it, they made every wave wait for its
+    // activations (and the row block loaded ahead of them) before the barrier, which then waited
+    // for the slowest wave's loads (0.3 us per small launch).
+#pragma unroll
+    for (int i = 0; i < ITM; ++i) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) asm volatile("" : "+v"(xr[i][b][m]));
+      }
+    }
+  }
   if constexpr (kXsum) {
     constexpr uint32_t kOnes = XT == kF16 ? 0x3C003C00u : 0x3F803F80u;
 #pragma unroll
