@@ -342,17 +342,22 @@ int run_tiled(const void* x, const uint8_t* packed, const void* scales, int fmt,
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
-// Batch size from which the automatic path prefers the MFMA kernel: 4, or 3 for matrices of 64 MiB
-// of packed bytes and more.  Measured on MI355X (NF4 x fp16, INT4 x bf16): the MFMA kernel's time
-// hardly moves between B = 1 and 16, the GEMV's grows with B (one dot2 per weight pair and
-// activation row); on 8960 x 1536 the GEMV is still faster at B = 3 and slower from B = 4, on
-// 151936 x 1536 slower from B = 3.
+// Batch size from which the automatic path prefers the MFMA kernel: 4; 3 for matrices of 64 MiB
+// of packed bytes and more; 5 for matrices under 4 MiB.  Measured on MI355X (NF4 x fp16, INT4 x
+// bf16): the MFMA kernel's time hardly moves between B = 1 and 16, the GEMV's grows with B (one
+// dot2 per weight pair and activation row); on 8960 x 1536 the GEMV is still faster at B = 3 and
+// slower from B = 4, on 151936 x 1536 slower from B = 3; on the small launches (256, 1536 and
+// 2048 rows x 1536) it is still 0.1-0.3 us faster at B = 4 (q 4.29 against 4.43 us, INT4 k/v
+// 3.91 against 4.25) and slower from B = 6.
 constexpr int64_t kMfmaFromBatch = 4;
 constexpr int64_t kMfmaFromBatchLarge = 3;
+constexpr int64_t kMfmaFromBatchSmall = 5;
 
 bool prefer_mfma(int64_t n, int64_t k, int64_t b) {
-  const bool large = n * (k / 2) >= ((int64_t)64 << 20);
-  return b >= (large ? kMfmaFromBatchLarge : kMfmaFromBatch);
+  const int64_t bytes = n * (k / 2);
+  const bool large = bytes >= ((int64_t)64 << 20);
+  const bool small = bytes < ((int64_t)4 << 20);
+  return b >= (large ? kMfmaFromBatchLarge : small ? kMfmaFromBatchSmall : kMfmaFromBatch);
 }
 
 // The tiled GEMM from W4_TILED_FROM_BATCH activation rows, for matrices of W4_TILED_FROM_ROWS rows

@@ -262,25 +262,26 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
   ld.ti = 0;
   ld.q = 0;
   set_tile(ld);
-  // Two quads go out before the table and the window, the other two after the barrier (which
-  // waits for every load in flight): the prologue's loads stay few.  The table is written before
-  // the window's buffer-to-LDS loads are issued: written after them, its LDS stores had to wait
-  // for every load in flight (the compiler cannot tell the two LDS areas apart), which put the
-  // fill behind a full memory round trip (0.1 us on the 1536-wide shapes at B = 8).
+  // Prologue order: the window's buffer-to-LDS loads first, then the weight quads, then the
+  // table, then the barrier.  Memory operations complete in issue order, so what waits for the
+  // window (the table's LDS stores, which the compiler cannot tell apart from the window's, and
+  // the barrier) waits for it alone, not for the weights behind it: no wave holds the barrier for
+  // its own HBM loads, and all four quads are in flight across it.  (Weights first and the window
+  // last made the barrier wait for every load in flight; the table first delayed the weights.)
   Quad<FMT> P0, P1, P2, P3;
+  load_x(0);
   load_quad(ld, P0);
   advance(ld);
   load_quad(ld, P1);
   advance(ld);
   fill_table<FMT, XT, kThreads>(tab);
-  load_x(0);
-  __syncthreads();
   if constexpr (R == 4) {
     load_quad(ld, P2);
     advance(ld);
     load_quad(ld, P3);
     advance(ld);
   }
+  __syncthreads();
 
   float4_t acc[T];
 #pragma unroll

@@ -91,7 +91,8 @@ typedef enum {
                           My Triton Kernel Ties bitsandbytes, "The kernels", v3 and its
                           stale-output bug)                                                  */
   W4_PATH_MFMA = 3,    /* decode W on chip, MFMA against x, 1 <= B <= W4_MAX_BATCH (W4_PATH_AUTO
-                          takes it from B = 4, or B = 3 for matrices of 64 MiB and more).
+                          takes it from B = 4; from B = 3 for matrices of 64 MiB and more,
+                          from B = 5 for matrices under 4 MiB).
                           With split_k >= 2: K in split_k ranges of whole 256-weight quads
                           (fewer when the quads do not fill them), each range's partial sums
                           into an fp32 workspace, then the same fixed-order sum as

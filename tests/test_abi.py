@@ -146,6 +146,8 @@ def test_workspace_and_plan_logic():
     assert w4.auto_path("nf4_f16", 8960, 1536, 1) == ("gemv", 1)
     assert w4.auto_path("nf4_f16", 8960, 1536, 3)[0] == "gemv"
     assert w4.auto_path("nf4_f16", 8960, 1536, 4)[0] == "mfma"
+    assert w4.auto_path("nf4_f16", 1536, 1536, 4)[0] == "gemv"  # under 4 MiB: MFMA from B = 5
+    assert w4.auto_path("nf4_f16", 1536, 1536, 5)[0] == "mfma"
     assert w4.auto_path("nf4_f16", 8960, 1536, 64)[0] == "mfma"
     assert w4.auto_path("nf4_f16", 151936, 1536, 2)[0] == "gemv"  # 116 MB: MFMA from B = 3
     assert w4.auto_path("nf4_f16", 151936, 1536, 3)[0] == "mfma"
