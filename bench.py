@@ -243,7 +243,11 @@ def plan_kernel(w4, fmt, n, k, b, path, sk):
 
 
 def grouped_kernel(w4, fmt, ns, k, b):
-    """(kernel name, grid size in work-items) of one grouped launch over members of ns rows."""
+    """(kernel name, grid size in work-items) of one grouped launch over members of ns rows: the
+    grouped fused GEMV where the automatic choice for the summed rows is the GEMV, else the MFMA
+    kernel (from the tiled batch on, members of 4096 rows and more as tiled launches)."""
+    if b > 8 or w4.auto_path(fmt, sum(ns), k, b)[0] != "gemv":
+        return ("tiled|mfma" if b >= 128 else "mfma"), None
     plan = w4.gemv_grouped_plan(fmt, ns, k, b)
     return (_gemv_name(fmt, b, plan["iters"], plan["threads"], True),
             plan["grid_x"] * plan["grid_z"] * plan["threads"])
@@ -925,17 +929,21 @@ def prefill_suite(args, dev):
                                              if nm != "up"]
     for fmt in ("nf4_f16", "int4_bf16"):
         for name, n, k in shapes:
-            row = {"format": fmt, "shape": name, "n": n, "k": k, "b": b,
-                   "auto": w4.auto_path(fmt, n, k, b)[0]}
-            for path in ("tiled", "mfma"):
-                us, err = time_shape(fmt, n, k, b, path, 0, dev,
-                                     mats=rotated_mats(fmt, n, k, dev, min_bytes=256 << 20), reps=3)
+            ap, sk = w4.auto_path(fmt, n, k, b, w4.workspace_bytes(fmt, n, k, b))
+            row = {"format": fmt, "shape": name, "n": n, "k": k, "b": b, "auto": ap,
+                   "auto_split": sk}
+            mats = rotated_mats(fmt, n, k, dev, min_bytes=256 << 20)
+            # "auto": the automatic path with the workspace it asks for (the tiled GEMM over K
+            # ranges where its tiles alone do not fill the CUs); "tiled", "mfma": one pass each
+            for path in ("auto", "tiled", "mfma"):
+                us, err = time_shape(fmt, n, k, b, path, 0, dev, mats=mats, reps=3)
                 if us is None:
                     row[path] = {"error": err}
                     continue
                 tf = 2.0 * n * k * b / us / 1e6
                 row[path] = {"us": round(us, 2), "tflops": round(tf, 1),
                              "frac_fp16_mfma_peak": round(tf / MFMA_FP16_PEAK_TFLOPS, 4)}
+            del mats
             if fmt == "nf4_f16":
                 w = torch.randn(n, k, device=dev, dtype=torch.float16)
                 x = torch.randn(b, k, device=dev, dtype=torch.float16)
@@ -953,8 +961,8 @@ def prefill_suite(args, dev):
                 del w, x, y
                 torch.cuda.empty_cache()
             out["shapes"].append(row)
-            log(f"[prefill] {fmt} {name} {n}x{k} B={b}: " +
-                ", ".join(f"{p} {row[p]['us']} us" for p in ("tiled", "mfma", "fp16_dense_torch")
+            log(f"[prefill] {fmt} {name} {n}x{k} B={b} (auto {ap}, S={sk}): " +
+                ", ".join(f"{p} {row[p]['us']} us" for p in ("auto", "tiled", "mfma", "fp16_dense_torch")
                           if p in row and "us" in row[p]))
     return out
 
@@ -1420,6 +1428,7 @@ def main():
         w4.lib()
         rows = steps_suite(args, torch.device("cuda:0"))
         if args.report:
+            os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
             with open(args.report, "w") as f:
                 json.dump(rows, f, indent=1)
         print(json.dumps({"metric": "decode step in other formats and batches", "rows": rows}),
@@ -1433,6 +1442,7 @@ def main():
         w4.lib()
         res = prefill_suite(args, torch.device("cuda:0"))
         if args.report:
+            os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
             with open(args.report, "w") as f:
                 json.dump(res, f, indent=1)
         print(json.dumps({"metric": "prefill step (512 tokens) and per-shape GEMM table",
@@ -1443,6 +1453,7 @@ def main():
 
         res = sparse24_suite(args, torch.device("cuda:0"))
         if args.report:
+            os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
             with open(args.report, "w") as f:
                 json.dump(res, f, indent=1)
         print(json.dumps({"metric": "2:4 sparse decode step (197 GEMVs, B=1)", **res["step"]}),
@@ -1453,6 +1464,7 @@ def main():
 
         res = gptq_suite(args, torch.device("cuda:0"))
         if args.report:
+            os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
             with open(args.report, "w") as f:
                 json.dump(res, f, indent=1)
         print(json.dumps({"metric": "GPTQ column loop, one Qwen2.5-1.5B layer", **res["layer"]}),
@@ -1467,6 +1479,7 @@ def main():
         dev = torch.device("cuda:0")
         rows = shapes_suite(args, dev)
         if args.report:
+            os.makedirs(os.path.dirname(os.path.abspath(args.report)), exist_ok=True)
             with open(args.report, "w") as f:
                 json.dump(rows, f, indent=1)
         ok = [r for r in rows if "us" in r]

@@ -233,6 +233,25 @@ int auto_mfma_splits(int64_t n, int64_t k, int64_t b) {
   return s;
 }
 
+// Split count of the automatic tiled GEMM (used when the caller's workspace holds the partial
+// sums): the smallest power of two S for which ceil(N / 64) * ceil(B / 128) * S, the workgroups
+// of 64-row tiles over all K ranges, reaches three quarters of the CUs, with at least 16 blocks
+// of 64 weights per range and at most 16 ranges.  Measured on MI355X (NF4 x fp16, rotated weights,
+// S = 1..16 at B = 128, 256, 512): the rule's S is the best or within 10% of it on 1536 x 8960
+// (72.6 -> 45.5 us at B = 512, 73.3 -> 27.0 at 256, 74.4 -> 21.0 at 128), 1024 x 8192 (63.7 ->
+// 25.9, 64.4 -> 18.9, 64.2 -> 18.7) and 8192 x 8192 at B = 128 (65.2 -> 45.4); rows of 1536
+// weights and matrices with enough tiles stay whole (8960 x 1536 at B = 128: 17.6 us unsplit,
+// 28.7 split in two; 151936 x 1536 slower with every split).  It gives up to 10% on 8192 x 28672
+// at B = 512 (444 us against 400 at S = 2).
+int auto_tiled_splits(int64_t n, int64_t k, int64_t b) {
+  const int64_t tiles = ((n + 63) / 64) * ((b + 127) / 128);
+  const int64_t nb = k / 64;
+  const int64_t want = (3 * (int64_t)device_cu_count() + 3) / 4;
+  int s = 1;
+  while (s < 16 && tiles * s < want && nb / (2 * s) >= 16) s *= 2;
+  return s;
+}
+
 // Launch shape of one fused-GEMV launch over `groups` members that share K: the plan of their
 // summed rows, each member's row blocks, and each member's workgroups along x (its share of the
 // grid cap, at most its row blocks; grouped launches give the members consecutive ranges of x, so
@@ -335,9 +354,9 @@ int run_mfma(const void* x, const uint8_t* packed, const void* scales, int fmt, 
 }
 
 int run_tiled(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
-              int64_t k, int64_t b, float* y, hipStream_t st) {
+              int64_t k, int64_t b, float* y, hipStream_t st, int splits = 1, void* ws = nullptr) {
   const hipError_t e = launch_gemm(fmt, reinterpret_cast<const uint16_t*>(x), packed, scales, n, k,
-                                   b, y, st);
+                                   b, y, st, splits, reinterpret_cast<float*>(ws));
   if (e == hipErrorNotSupported) return W4_ERR_PATH;
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
@@ -363,9 +382,24 @@ bool prefer_mfma(int64_t n, int64_t k, int64_t b) {
 // The tiled GEMM from W4_TILED_FROM_BATCH activation rows, for matrices of W4_TILED_FROM_ROWS rows
 // and more.  Measured on MI355X at 512 activation rows (NF4 x fp16, INT4 x bf16): tiled against
 // MFMA 48 / 57 us on 8960 x 1536, 437 / 500 us on 151936 x 1536, 403 / 519 us on 28672 x 8192;
-// with 1536 or 2048 rows the tiles do not fill the CUs and the MFMA path is faster (17 / 14 us on
-// 1536 x 1536, 66 / 57 us on 1536 x 8960).
+// with 1536 or 2048 rows the tiles of one pass do not fill the CUs and the MFMA path is faster
+// (17 / 14 us on 1536 x 1536, 66 / 57 us on 1536 x 8960) unless K splits (below).
 bool prefer_tiled(int64_t n, int64_t b) { return b >= W4_TILED_FROM_BATCH && n >= W4_TILED_FROM_ROWS; }
+
+// Fewer rows from W4_TILED_FROM_BATCH: the tiled GEMM over K ranges when the rule above splits K
+// and the workspace holds the partial sums (1536 x 8960 at 512 / 256 / 128 activation rows: 45.5 /
+// 27.0 / 21.0 us against the MFMA path's 56.9 / 47.2 / 24.5; 1024 x 8192: 25.9 / 18.9 / 18.7
+// against 51.3 / 23.2 / 22.3), else the MFMA path.
+bool prefer_tiled_split(int64_t n, int64_t k, int64_t b, size_t workspace_bytes, int* splits) {
+  if (b < W4_TILED_FROM_BATCH) return false;
+  const int s = auto_tiled_splits(n, k, b);
+  const int ranges = s > 1 ? gemm_splits_used(k, s) : 1;
+  if (ranges > 1 && workspace_bytes >= splitk_bytes(n, b, ranges)) {
+    *splits = s;
+    return true;
+  }
+  return false;
+}
 
 // Arguments of a grouped call: every member valid on its own, the members' summed rows in range,
 // and no member's y overlapping another member's y, packed bytes or scales.
@@ -544,10 +578,15 @@ size_t w4_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b, int path, in
   switch (path) {
     case W4_PATH_SPLITK: return splitk_bytes(n, b, split_k > 1 ? split_k : 4);
     case W4_PATH_MFMA: return split_k > 1 ? splitk_bytes(n, b, split_k) : 0;
+    case W4_PATH_TILED: {
+      const int ranges = split_k > 1 && split_k <= W4_MAX_SPLIT_K ? gemm_splits_used(k, split_k) : 1;
+      return ranges > 1 ? splitk_bytes(n, b, ranges) : 0;
+    }
     case W4_PATH_TWOPASS: return (size_t)n * (size_t)k * 2;
     case W4_PATH_AUTO: {
       int sk = 1;
       const int p = w4_auto_path(fmt, n, k, b, SIZE_MAX, &sk);
+      if (p == W4_PATH_TILED) return sk > 1 ? splitk_bytes(n, b, gemm_splits_used(k, sk)) : 0;
       return (p == W4_PATH_SPLITK || p == W4_PATH_MFMA) && sk > 1 ? splitk_bytes(n, b, sk) : 0;
     }
     default: return 0;
@@ -604,6 +643,10 @@ int w4_auto_path(int fmt, int64_t n, int64_t k, int64_t b, size_t workspace_byte
   GemvPlan p;
   if (prefer_tiled(n, b)) {
     path = W4_PATH_TILED;
+    int st = 1;
+    if (prefer_tiled_split(n, k, b, workspace_bytes, &st)) s = st;
+  } else if (prefer_tiled_split(n, k, b, workspace_bytes, &s)) {
+    path = W4_PATH_TILED;
   } else if (prefer_mfma(n, k, b) || !plan_gemv(n, k, (int)b, 1, &p)) {
     path = W4_PATH_MFMA;
     s = auto_mfma_splits(n, k, b);
@@ -657,8 +700,17 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
         return W4_ERR_ALIAS;
       return run_mfma(x, packed, scales, fmt, n, k, b, y, s, split_k, workspace);
     }
-    case W4_PATH_TILED:
-      return run_tiled(x, packed, scales, fmt, n, k, b, y, s);
+    case W4_PATH_TILED: {
+      if (split_k <= 1) return run_tiled(x, packed, scales, fmt, n, k, b, y, s);
+      if (split_k > W4_MAX_SPLIT_K) return W4_ERR_PATH;
+      const int ranges = gemm_splits_used(k, split_k);
+      if (ranges <= 1) return run_tiled(x, packed, scales, fmt, n, k, b, y, s);
+      const size_t used = splitk_bytes(n, b, ranges);
+      if (!workspace || workspace_bytes < used) return W4_ERR_WORKSPACE;
+      if (workspace_overlaps_inputs(workspace, used, x, packed, scales, fmt, n, k, b))
+        return W4_ERR_ALIAS;
+      return run_tiled(x, packed, scales, fmt, n, k, b, y, s, ranges, workspace);
+    }
     case W4_PATH_TWOPASS: {
       const size_t used = (size_t)n * (size_t)k * 2;
       if (!workspace || workspace_bytes < used) return W4_ERR_WORKSPACE;

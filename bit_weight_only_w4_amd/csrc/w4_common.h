@@ -193,8 +193,13 @@ hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uin
                                int64_t k, int64_t b, hipStream_t s, int splits = 1,
                                float* ws = nullptr);
 int mfma_splits_used(int64_t n, int64_t k, int64_t b, int splits);
+// Tiled GEMM.  splits > 1: K in up to `splits` ranges of whole 64-weight blocks on grid.y
+// (gemm_splits_used gives how many), each range's partial sums in ws[range][M][N] (fp32), then the
+// fixed-order reduction into y.
 hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
-                       int64_t n, int64_t k, int64_t m, float* y, hipStream_t s);
+                       int64_t n, int64_t k, int64_t m, float* y, hipStream_t s, int splits = 1,
+                       float* ws = nullptr);
+int gemm_splits_used(int64_t k, int splits);
 hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu, const float* scale,
                              const float* zero, int64_t lds, int group, int i1, int qmin, int qmax,
                              int64_t rows, int bc, float* q_hat, int64_t ldq, uint8_t* codes,

@@ -33,6 +33,8 @@
 //   * Workgroups are numbered so that the ones the dispatcher places on one XCD (every eighth)
 //     take consecutive tiles, the activation-row tiles of one weight-row tile first: a weight tile
 //     is read from HBM once and then served by that XCD's L2.
+#include <algorithm>
+
 #include "w4_mfma_common.h"
 
 namespace w4 {
@@ -41,10 +43,13 @@ struct GemmArgs {
   const uint16_t* x;      // [M, K] activations (bits)
   const uint8_t* packed;  // [N, K/2]
   const void* scales;     // NF4, FP4 float[N, K/64] | INT4 uint16 / INT4A uint32 [N, K/128]
-  float* y;               // [M, N]
+  float* y;               // [M, N], or the partial sums [S, M, N] of a split K
   uint32_t m, n, k;
   uint32_t mt;            // activation-row tiles (TM rows each)
   uint32_t tiles;         // mt * weight-row tiles
+  uint32_t bps;           // 64-weight blocks per K range: range z = blockIdx.y owns blocks
+                          // [z bps, min((z + 1) bps, K / 64)) and writes y + z * ysplit
+  uint32_t ysplit;        // floats between the partial planes of consecutive ranges (M * N)
 };
 
 namespace {
@@ -89,12 +94,16 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   const uint32_t n0 = tn * TN, m0 = tm * TM;
 
   const uint32_t k = a.k;
-  const uint32_t nb = k / 64;        // 64-weight blocks along K
+  // This workgroup's K range: blocks [kb0, kb0 + nbz) of 64 weights (all of K without a split;
+  // the host makes every range non-empty).
+  const uint32_t kb0 = blockIdx.y * a.bps;
+  const uint32_t nbz = min(a.bps, k / 64u - kb0);
   // K group kg takes blocks [kbase, kbase + cnt); every group runs `steps` block steps (the
   // barriers are shared), the ones past its range on zero-filled loads, which add nothing.
-  const uint32_t steps = (nb + KW - 1) / KW;
-  const uint32_t kbase = (uint32_t)kg * steps;
-  const uint32_t cnt = kbase < nb ? min(steps, nb - kbase) : 0u;
+  const uint32_t steps = (nbz + KW - 1) / KW;
+  const uint32_t kfirst = (uint32_t)kg * steps;
+  const uint32_t kbase = kb0 + kfirst;
+  const uint32_t cnt = kfirst < nbz ? min(steps, nbz - kfirst) : 0u;
   const uint32_t pitch = k >> 1;     // packed bytes per weight row
   const uint32_t spitch = (k / (is_g128(FMT) ? 128 : 64)) * SB;
 
@@ -300,13 +309,15 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
     }
   }
 
-  // Stores: lane (g, r) holds y[m0 + wm * 16 WM + 16 j + r][wrow0 + 16 t + 4 g + i].
+  // Stores: lane (g, r) holds y[m0 + wm * 16 WM + 16 j + r][wrow0 + 16 t + 4 g + i] (of this K
+  // range's plane of partial sums when K is split).
   const uint32_t n = a.n;
+  float* yz = a.y + (size_t)blockIdx.y * a.ysplit;
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
     const uint32_t mrow = m0 + (uint32_t)wm * 16u * WM + 16u * j + (uint32_t)r;
     if (mrow >= a.m) continue;
-    float* yr = a.y + (size_t)mrow * n;
+    float* yr = yz + (size_t)mrow * n;
 #pragma unroll
     for (int t = 0; t < WN; ++t) {
       const uint32_t col = wrow0 + 16u * t + 4u * (uint32_t)g;
@@ -332,8 +343,8 @@ hipError_t launch_wm(const GemmArgs& a, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     raised = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<FMT, XT, WN, WM, KW>), dim3(a.tiles), dim3(kGroupThreads * KW),
-                     lds, s, a);
+  hipLaunchKernelGGL((gemm_kernel<FMT, XT, WN, WM, KW>), dim3(a.tiles, (a.k / 64 + a.bps - 1) / a.bps),
+                     dim3(kGroupThreads * KW), lds, s, a);
   return hipGetLastError();
 }
 
@@ -345,26 +356,42 @@ hipError_t launch_fx(const GemmArgs& a, int wn, int wm, int kw, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// K ranges of a split over `nb` 64-weight blocks when `splits` are requested: ceil(nb / bps)
+// with bps = ceil(nb / splits) blocks each (every range non-empty).
+int gemm_ranges(int64_t nb, int splits, int64_t* bps) {
+  const int64_t s = std::max<int64_t>(1, std::min<int64_t>(splits, nb));
+  const int64_t per = (nb + s - 1) / s;
+  if (bps) *bps = per;
+  return (int)((nb + per - 1) / per);
+}
+
 }  // namespace
 
+int gemm_splits_used(int64_t k, int splits) { return gemm_ranges(k / 64, splits, nullptr); }
+
 hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
-                       int64_t n, int64_t k, int64_t m, float* y, hipStream_t s) {
+                       int64_t n, int64_t k, int64_t m, float* y, hipStream_t s, int splits,
+                       float* ws) {
   if (m < 1 || n < 1 || k < 64 || k % 64 != 0) return hipErrorInvalidValue;
   // 32-bit offsets inside the buffer resources: 128 activation rows and 64 weight rows of K.
   if (128 * k * 2 >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31) || m >= ((int64_t)1 << 31))
     return hipErrorNotSupported;
+  int64_t bps = 0;
+  const int ranges = gemm_ranges(k / 64, splits, &bps);
+  if (ranges > 1 && (!ws || (int64_t)m * n >= ((int64_t)1 << 32))) return hipErrorInvalidValue;
   const int64_t cus = device_cu_count();
   const int wm = 4;
   const int64_t mt = (m + 32 * wm - 1) / (32 * wm);
-  // Two workgroups of 128 x 128 per CU when there are that many tiles; else 64 x 128 tiles, with
-  // one K group when those make two workgroups per CU, two K groups (twice the waves per tile,
-  // half the blocks per wave) when they do not.  Measured on MI355X at 512 activation rows (NF4 x
-  // fp16): 8960 x 1536 takes 41.7 us with 64 x 128 tiles and one K group against 47.2 with two and
-  // 47.0 with 128 x 128 tiles; 1536 x 8960 71.9 us with two K groups against 85.5 with one;
-  // 151936 x 1536 and 28672 x 8192 are fastest with 128 x 128 tiles (431 and 410 us).  Larger
-  // tiles (128 x 256 or 256 x 128 per workgroup, one wave per SIMD) measured 1.4-5x slower.
-  const bool full = ((n + 127) / 128) * mt >= 2 * cus;
-  const bool half = !full && ((n + 63) / 64) * mt >= 2 * cus;
+  // Two workgroups of 128 x 128 per CU when there are that many tiles (counting every K range's);
+  // else 64 x 128 tiles, with one K group when those make two workgroups per CU, two K groups
+  // (twice the waves per tile, half the blocks per wave) when they do not.  Measured on MI355X at
+  // 512 activation rows (NF4 x fp16): 8960 x 1536 takes 41.7 us with 64 x 128 tiles and one K
+  // group against 47.2 with two and 47.0 with 128 x 128 tiles; 1536 x 8960 71.9 us with two K
+  // groups against 85.5 with one; 151936 x 1536 and 28672 x 8192 are fastest with 128 x 128 tiles
+  // (431 and 410 us).  Larger tiles (128 x 256 or 256 x 128 per workgroup, one wave per SIMD)
+  // measured 1.4-5x slower.
+  const bool full = ((n + 127) / 128) * mt * ranges >= 2 * cus;
+  const bool half = !full && ((n + 63) / 64) * mt * ranges >= 2 * cus;
   const int wn = full ? 4 : 2, kw = full || half ? 1 : 2;
   const int64_t nt = (n + 32 * wn - 1) / (32 * wn);
   if (nt * mt >= ((int64_t)1 << 31)) return hipErrorNotSupported;
@@ -372,23 +399,28 @@ hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const 
   a.x = x;
   a.packed = packed;
   a.scales = scales;
-  a.y = y;
+  a.y = ranges > 1 ? ws : y;
   a.m = (uint32_t)m;
   a.n = (uint32_t)n;
   a.k = (uint32_t)k;
   a.mt = (uint32_t)mt;
   a.tiles = (uint32_t)(nt * mt);
+  a.bps = (uint32_t)bps;
+  a.ysplit = ranges > 1 ? (uint32_t)(m * n) : 0u;
+  hipError_t e = hipErrorInvalidValue;
   switch (fmt) {
-    case W4_NF4_X_F16: return launch_fx<kNF4, kF16>(a, wn, wm, kw, s);
-    case W4_NF4_X_BF16: return launch_fx<kNF4, kBF16>(a, wn, wm, kw, s);
-    case W4_INT4_X_F16: return launch_fx<kINT4, kF16>(a, wn, wm, kw, s);
-    case W4_INT4_X_BF16: return launch_fx<kINT4, kBF16>(a, wn, wm, kw, s);
-    case W4_FP4_X_F16: return launch_fx<kFP4, kF16>(a, wn, wm, kw, s);
-    case W4_FP4_X_BF16: return launch_fx<kFP4, kBF16>(a, wn, wm, kw, s);
-    case W4_INT4A_X_F16: return launch_fx<kINT4A, kF16>(a, wn, wm, kw, s);
-    case W4_INT4A_X_BF16: return launch_fx<kINT4A, kBF16>(a, wn, wm, kw, s);
+    case W4_NF4_X_F16: e = launch_fx<kNF4, kF16>(a, wn, wm, kw, s); break;
+    case W4_NF4_X_BF16: e = launch_fx<kNF4, kBF16>(a, wn, wm, kw, s); break;
+    case W4_INT4_X_F16: e = launch_fx<kINT4, kF16>(a, wn, wm, kw, s); break;
+    case W4_INT4_X_BF16: e = launch_fx<kINT4, kBF16>(a, wn, wm, kw, s); break;
+    case W4_FP4_X_F16: e = launch_fx<kFP4, kF16>(a, wn, wm, kw, s); break;
+    case W4_FP4_X_BF16: e = launch_fx<kFP4, kBF16>(a, wn, wm, kw, s); break;
+    case W4_INT4A_X_F16: e = launch_fx<kINT4A, kF16>(a, wn, wm, kw, s); break;
+    case W4_INT4A_X_BF16: e = launch_fx<kINT4A, kBF16>(a, wn, wm, kw, s); break;
   }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || ranges == 1) return e;
+  // the ranges' partial sums, added in range order into y
+  return launch_splitk_reduce(ws, y, m * n, ranges, s);
 }
 
 }  // namespace w4

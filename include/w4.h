@@ -106,8 +106,13 @@ typedef enum {
                           into the matrix-core operands (LLM Quantization on RTX 4060, "Why Only
                           16%", item 3: prefill needs a GEMM, not a GEMV per token); any B.
                           W4_PATH_AUTO takes it from B = W4_TILED_FROM_BATCH for matrices of
-                          N >= W4_TILED_FROM_ROWS (fewer rows leave too few tiles: the MFMA path
-                          is faster there)                                                   */
+                          N >= W4_TILED_FROM_ROWS, and for fewer rows when K splits (below) and
+                          the workspace holds the partials (else the MFMA path is faster there).
+                          With split_k >= 2 K runs in ranges of whole 64-weight blocks on
+                          separate workgroups, partial sums in the workspace, then the fixed-order
+                          reduction; W4_PATH_AUTO, given a workspace, splits K into the smallest
+                          power of two of ranges that gives three quarters of the CUs a 64-row
+                          tile, each range at least 16 blocks, at most 16 ranges                */
 } w4_path_t;
 
 #define W4_MAX_BATCH 4096
@@ -276,13 +281,16 @@ int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* 
                                int fmt, int64_t K, int64_t B, void* stream);
 
 /* w4_matmul_ex: the same operation with an explicit path, split count and workspace (tests and
- * the ablation benchmark).  path = W4_PATH_AUTO also considers split-K (fused GEMV or MFMA) when a
- * workspace is given: w4_workspace_bytes(..., W4_PATH_AUTO, 0) is the size that lets it.
+ * the ablation benchmark).  path = W4_PATH_AUTO also considers split-K (fused GEMV, MFMA or tiled
+ * GEMM) when a workspace is given: w4_workspace_bytes(..., W4_PATH_AUTO, 0) is the size that lets
+ * it.
  * The bytes a path writes into the workspace must not overlap x, packed, scales or y
  * (W4_ERR_ALIAS).
- *   split_k          number of K ranges for W4_PATH_SPLITK (2..W4_MAX_SPLIT_K; 0 = 4) and for
- *                    W4_PATH_MFMA (2..W4_MAX_SPLIT_K; 0 or 1 = one pass); ignored by the other
- *                    paths.  Either split path needs 4 * split_k * B * N workspace bytes.
+ *   split_k          number of K ranges for W4_PATH_SPLITK (2..W4_MAX_SPLIT_K; 0 = 4), for
+ *                    W4_PATH_MFMA and for W4_PATH_TILED (2..W4_MAX_SPLIT_K; 0 or 1 = one pass);
+ *                    ignored by the other paths.  The GEMV and MFMA splits need 4 * split_k * B * N
+ *                    workspace bytes; the tiled GEMM makes R = ceil(K/64 / ceil(K/64 / split_k))
+ *                    ranges of whole 64-weight blocks (R <= split_k) and needs 4 * R * B * N.
  *   workspace        device memory of at least w4_workspace_bytes(...) bytes, 16-byte aligned;
  *                    may be NULL when that size is 0.  Its contents are scratch on entry and exit.
  *                    Two calls in flight must not share one workspace.
@@ -308,8 +316,9 @@ int w4_matmul_splitk_noalloc(const void* x, const uint8_t* packed, const void* s
                              int64_t N, int64_t K, int64_t B, float* y, int split_k, void* stream);
 
 /* Bytes of workspace w4_matmul_ex needs for (fmt, N, K, B, path, split_k): split-K (the GEMV's,
- * or the MFMA path's with split_k >= 2) needs 4 * S * B * N, two-pass 2 * N * K, the single-pass
- * paths 0; W4_PATH_AUTO reports the split-K size it would use given that much workspace.
+ * or the MFMA path's with split_k >= 2) needs 4 * S * B * N, the tiled GEMM's 4 * R * B * N (R its
+ * ranges, see w4_matmul_ex), two-pass 2 * N * K, the single-pass paths 0; W4_PATH_AUTO reports the
+ * split-K size it would use given that much workspace.
  * Returns 0 for invalid arguments. */
 size_t w4_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t B, int path, int split_k);
 

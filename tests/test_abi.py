@@ -184,6 +184,35 @@ def test_mfma_split_rule():
     assert w4.workspace_bytes("nf4_f16", 1536, 8960, 8, "mfma", 1) == 0
 
 
+def test_tiled_split_rule():
+    """The automatic tiled GEMM's split-K count (host logic, 256 CUs where no GPU is visible): from
+    B = 128 the smallest power of two S with ceil(N / 64) * ceil(B / 128) * S >= 192, at least 16
+    blocks of 64 weights per range, at most 16 ranges; matrices under 4096 rows take the tiled GEMM
+    only when K splits and the workspace holds the partials, else the MFMA path."""
+    w4, _ = _lib()
+    big = 1 << 30
+    assert w4.auto_path("nf4_f16", 1536, 8960, 512) == ("mfma", 1)  # no workspace
+    assert w4.auto_path("nf4_f16", 1536, 8960, 512, big) == ("tiled", 2)  # 96 tiles
+    assert w4.auto_path("nf4_f16", 1536, 8960, 256, big) == ("tiled", 4)  # 48 tiles
+    assert w4.auto_path("nf4_f16", 1536, 8960, 128, big) == ("tiled", 8)  # 140 / 16 >= 8
+    assert w4.auto_path("int4_bf16", 1024, 8192, 512, big) == ("tiled", 4)
+    assert w4.auto_path("int4_bf16", 1024, 8192, 128, big) == ("tiled", 8)  # 128 / 16 < 16
+    assert w4.auto_path("nf4_f16", 8192, 8192, 128, big) == ("tiled", 2)
+    assert w4.auto_path("nf4_f16", 8192, 8192, 512, big) == ("tiled", 1)  # 512 tiles
+    assert w4.auto_path("nf4_f16", 8960, 1536, 128, big) == ("tiled", 1)  # 24 blocks: no split
+    assert w4.auto_path("nf4_f16", 1536, 1536, 512, big) == ("mfma", 1)
+    assert w4.auto_path("nf4_f16", 1536, 8960, 64, big) == ("mfma", 16)  # below the tiled batch
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512) == 2 * 512 * 1536 * 4
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 128) == 8 * 128 * 1536 * 4
+    assert w4.auto_path("nf4_f16", 1536, 8960, 512, 2 * 512 * 1536 * 4 - 1) == ("mfma", 1)
+    assert w4.workspace_bytes("nf4_f16", 8192, 8192, 512) == 0
+    # explicit splits: ceil(K / 64 / ceil(K / 64 / S)) ranges, 4 * ranges * B * N bytes
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512, "tiled", 8) == 8 * 512 * 1536 * 4
+    assert w4.workspace_bytes("nf4_f16", 64, 192, 130, "tiled", 2) == 2 * 130 * 64 * 4  # 3 blocks
+    assert w4.workspace_bytes("nf4_f16", 64, 192, 130, "tiled", 16) == 3 * 130 * 64 * 4
+    assert w4.workspace_bytes("nf4_f16", 64, 192, 130, "tiled", 1) == 0
+
+
 def _grouped(L, n=(64, 32, 32), x=FAKE, p=None, s=None, y=None, fmt=1, k=256, b=1, groups=None,
              entry="w4_gemv_grouped"):
     vp = ctypes.c_void_p

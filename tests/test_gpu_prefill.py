@@ -113,6 +113,83 @@ def test_tiled_full_size_sampled(fmt, n, k, b):
     g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
 
 
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("n,k,b,splits", [(130, 8960, 200, 8), (37, 1024, 129, 2), (300, 2048, 512, 4),
+                                          (64, 384, 130, 3), (96, 256, 257, 16), (65, 8192, 33, 5)])
+def test_tiled_splitk_parity(fmt, n, k, b, splits):
+    """Tiled GEMM over K ranges of whole 64-weight blocks (partial sums in the workspace, then the
+    fixed-order reduction) against the oracle; y pre-filled with NaN and the workspace dirty, so a
+    result that misses a range or accumulates into y fails.  Includes more splits than blocks
+    (K = 256: four ranges of one block) and uneven ranges (140 blocks in 8, 128 in 5)."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n + k + b + splits)
+    nb = k // 64
+    per = -(-nb // min(splits, nb))
+    ranges = -(-nb // per)
+    wsb = w4.workspace_bytes(fmt, n, k, b, "tiled", splits)
+    assert wsb == ranges * b * n * 4
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device=xd.device)
+    y = torch.full((b, n), float("nan"), device=xd.device)
+    w4.matmul_ex(xd, p, s, fmt, path="tiled", split_k=splits, workspace=ws, y=y)
+    g.assert_y_close(fmt, y, x, pr, sr)
+    y2 = w4.matmul_ex(xd, p, s, fmt, path="tiled", split_k=splits, workspace=ws)
+    assert torch.equal(y, y2)
+
+
+def test_tiled_splitk_needs_workspace():
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    fmt, n, k, b = "nf4_f16", 64, 2048, 130
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=9)
+    small = torch.empty(4 * b * n * 4 - 16, dtype=torch.uint8, device=xd.device)
+    with pytest.raises(RuntimeError, match="workspace"):
+        w4.matmul_ex(xd, p, s, fmt, path="tiled", split_k=4, workspace=small)
+    with pytest.raises(RuntimeError, match="workspace"):
+        w4.matmul_ex(xd, p, s, fmt, path="tiled", split_k=4)
+    # one range needs none: bitwise the unsplit launch
+    y1 = w4.matmul_ex(xd, p, s, fmt, path="tiled", split_k=1)
+    assert torch.equal(y1, w4.gemm_prefill(xd, p, s, fmt))
+
+
+@pytest.mark.parametrize("fmt,n,k,b", [("nf4_f16", 1536, 8960, 512), ("int4_bf16", 1024, 8192, 128),
+                                       ("int4a_f16", 1536, 8960, 256), ("fp4_bf16", 8192, 8192, 128)])
+def test_tiled_splitk_auto_full_size_sampled(fmt, n, k, b):
+    """The automatic path with a workspace at prefill batches: the tiled GEMM split over K for the
+    matrices whose tiles do not fill the CUs (the 1536 x 8960 down projection, the 1024 x 8192 k/v
+    projection, 8192 x 8192 at 128 rows), bitwise equal to the explicit call with its split count;
+    160 sampled rows against the oracle over every activation row."""
+    import numpy as np
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    dev = g.device()
+    gen = torch.Generator(device=dev).manual_seed(n + 3 * k + b)
+    w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+    p, s = g.gpu_quantize(fmt, w)
+    rng = np.random.default_rng(n + k + b)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 158, replace=False)]))
+    w_rows = w[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    del w
+    pr, sr = g.oracle_quantize(fmt, w_rows)
+    g.assert_quant_equal(fmt, p, s, pr, sr, rows=rows)
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=b + 13)
+    xd = g.to_dev_x(x, g.XDT[fmt])
+    wsb = w4.workspace_bytes(fmt, n, k, b)
+    path, sk = w4.auto_path(fmt, n, k, b, wsb)
+    assert path == "tiled" and sk > 1 and wsb > 0
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device=dev)
+    y = torch.full((b, n), float("nan"), device=dev)
+    w4.matmul_ex(xd, p, s, fmt, workspace=ws, y=y)
+    assert torch.equal(y, w4.matmul_ex(xd, p, s, fmt, path="tiled", split_k=sk, workspace=ws))
+    g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
+
+
 @pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
 def test_grouped_at_prefill_batch(fmt):
     """w4_gemm_smallbatch_grouped from W4_TILED_FROM_BATCH on: members of W4_TILED_FROM_ROWS rows
