@@ -275,7 +275,9 @@ def gemv_grouped(x, packed, scales, fmt, ys=None, stream=None):
 
 def gemm_smallbatch_grouped(x, packed, scales, fmt, ys=None, stream=None):
     """gemv_grouped for batches up to W4_MAX_BATCH: one launch of the kernel the automatic path
-    picks for the members' summed rows (the fused GEMV, or the MFMA kernel for larger batches)."""
+    picks for the members' summed rows (the fused GEMV, or the MFMA kernel for larger batches);
+    from W4_TILED_FROM_BATCH rows one tiled launch over the members of TILED_FROM_ROWS rows and
+    more, one MFMA launch over the others."""
     return _grouped_call("w4_gemm_smallbatch_grouped", x, packed, scales, fmt, ys, stream)
 
 

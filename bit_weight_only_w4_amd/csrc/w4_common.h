@@ -200,6 +200,12 @@ hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const 
                        int64_t n, int64_t k, int64_t m, float* y, hipStream_t s, int splits = 1,
                        float* ws = nullptr);
 int gemm_splits_used(int64_t k, int splits);
+// One tiled launch over `groups` members that share x and K (their tiles one after another);
+// splits > 1 only with one member.
+hipError_t launch_gemm_members(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
+                               const void* const* scales, const int64_t* ns, float* const* y,
+                               int64_t k, int64_t m, hipStream_t s, int splits = 1,
+                               float* ws = nullptr);
 hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu, const float* scale,
                              const float* zero, int64_t lds, int group, int i1, int qmin, int qmax,
                              int64_t rows, int bc, float* q_hat, int64_t ldq, uint8_t* codes,

@@ -39,14 +39,23 @@
 
 namespace w4 {
 
+// One matrix of a launch.  The matrices of a grouped launch share x and K; their tiles are
+// numbered one after another, member g owning tiles [tile0, tile0 + mt * its weight-row tiles).
+struct GemmMember {
+  const uint8_t* packed;  // [N_g, K/2]
+  const void* scales;     // NF4, FP4 float[N_g, K/64] | INT4 uint16 / INT4A uint32 [N_g, K/128]
+  float* y;               // [M, N_g], or the partial sums [S, M, N] of a split K (one member)
+  uint32_t n;             // N_g
+  uint32_t tile0;
+};
+
 struct GemmArgs {
+  GemmMember mb[kMaxGroup];
   const uint16_t* x;      // [M, K] activations (bits)
-  const uint8_t* packed;  // [N, K/2]
-  const void* scales;     // NF4, FP4 float[N, K/64] | INT4 uint16 / INT4A uint32 [N, K/128]
-  float* y;               // [M, N], or the partial sums [S, M, N] of a split K
-  uint32_t m, n, k;
+  uint32_t groups;
+  uint32_t m, k;
   uint32_t mt;            // activation-row tiles (TM rows each)
-  uint32_t tiles;         // mt * weight-row tiles
+  uint32_t tiles;         // tiles of all members
   uint32_t bps;           // 64-weight blocks per K range: range z = blockIdx.y owns blocks
                           // [z bps, min((z + 1) bps, K / 64)) and writes y + z * ysplit
   uint32_t ysplit;        // floats between the partial planes of consecutive ranges (M * N)
@@ -70,7 +79,7 @@ struct Block {
   uint32_t s[WN];
 };
 
-template <int FMT, int XT, int WN, int WM, int KW>
+template <int FMT, int XT, int WN, int WM, int KW, bool GROUPED>
 __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a) {
   constexpr int TN = 32 * WN, TM = 32 * WM;
   constexpr bool kSplit = FMT == kNF4 && XT == kBF16;
@@ -90,7 +99,17 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   const uint32_t id = blockIdx.x, tiles = a.tiles;
   const uint32_t xcd = id % kXcds, per = tiles / kXcds, extra = tiles % kXcds;
   const uint32_t tile = xcd * per + min(xcd, extra) + id / kXcds;
-  const uint32_t tn = tile / a.mt, tm = tile - tn * a.mt;
+  // Its member, by selects over the fixed member slots (the argument block is never indexed by a
+  // computed value).
+  GemmMember mm = a.mb[0];
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int i = 1; i < kMaxGroup; ++i) {
+      if ((uint32_t)i < a.groups && tile >= a.mb[i].tile0) mm = a.mb[i];
+    }
+  }
+  const uint32_t lt = tile - mm.tile0;
+  const uint32_t tn = lt / a.mt, tm = lt - tn * a.mt;
   const uint32_t n0 = tn * TN, m0 = tm * TM;
 
   const uint32_t k = a.k;
@@ -110,10 +129,10 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   // Buffer resources: this wave's WN * 16 weight rows (rows past N read as zero), and the
   // workgroup's TM activation rows (rows past M read as zero).
   const uint32_t wrow0 = n0 + (uint32_t)wn * 16u * WN;
-  const uint32_t wrows = wrow0 < a.n ? min(16u * WN, a.n - wrow0) : 0u;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.packed + (size_t)wrow0 * pitch, wrows * pitch);
+  const uint32_t wrows = wrow0 < mm.n ? min(16u * WN, mm.n - wrow0) : 0u;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(mm.packed + (size_t)wrow0 * pitch, wrows * pitch);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(reinterpret_cast<const char*>(a.scales) + (size_t)wrow0 * spitch, wrows * spitch);
+      make_rsrc(reinterpret_cast<const char*>(mm.scales) + (size_t)wrow0 * spitch, wrows * spitch);
   const uint32_t xrows = min((uint32_t)TM, a.m - m0);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)m0 * k, xrows * k * 2u);
 
@@ -311,8 +330,8 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
 
   // Stores: lane (g, r) holds y[m0 + wm * 16 WM + 16 j + r][wrow0 + 16 t + 4 g + i] (of this K
   // range's plane of partial sums when K is split).
-  const uint32_t n = a.n;
-  float* yz = a.y + (size_t)blockIdx.y * a.ysplit;
+  const uint32_t n = mm.n;
+  float* yz = mm.y + (size_t)blockIdx.y * a.ysplit;
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
     const uint32_t mrow = m0 + (uint32_t)wm * 16u * WM + 16u * j + (uint32_t)r;
@@ -333,27 +352,33 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   }
 }
 
-template <int FMT, int XT, int WN, int WM, int KW>
+template <int FMT, int XT, int WN, int WM, int KW, bool GROUPED>
 hipError_t launch_wm(const GemmArgs& a, hipStream_t s) {
   static bool raised = false;
   constexpr int lds = KW * 2 * stage_bytes<WM>();
   static_assert(KW == 1 || (KW - 1) * 4 * WN * WM * 64 * 16 <= lds, "K-group sums fit the stages");
   if (!raised) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<FMT, XT, WN, WM, KW>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<FMT, XT, WN, WM, KW, GROUPED>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     raised = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<FMT, XT, WN, WM, KW>), dim3(a.tiles, (a.k / 64 + a.bps - 1) / a.bps),
-                     dim3(kGroupThreads * KW), lds, s, a);
+  hipLaunchKernelGGL((gemm_kernel<FMT, XT, WN, WM, KW, GROUPED>),
+                     dim3(a.tiles, (a.k / 64 + a.bps - 1) / a.bps), dim3(kGroupThreads * KW), lds, s, a);
   return hipGetLastError();
+}
+
+template <int FMT, int XT, bool GROUPED>
+hipError_t launch_plan(const GemmArgs& a, int wn, int wm, int kw, hipStream_t s) {
+  if (wn == 2 && wm == 4 && kw == 2) return launch_wm<FMT, XT, 2, 4, 2, GROUPED>(a, s);
+  if (wn == 2 && wm == 4 && kw == 1) return launch_wm<FMT, XT, 2, 4, 1, GROUPED>(a, s);
+  if (wn == 4 && wm == 4 && kw == 1) return launch_wm<FMT, XT, 4, 4, 1, GROUPED>(a, s);
+  return hipErrorInvalidValue;
 }
 
 template <int FMT, int XT>
 hipError_t launch_fx(const GemmArgs& a, int wn, int wm, int kw, hipStream_t s) {
-  if (wn == 2 && wm == 4 && kw == 2) return launch_wm<FMT, XT, 2, 4, 2>(a, s);
-  if (wn == 2 && wm == 4 && kw == 1) return launch_wm<FMT, XT, 2, 4, 1>(a, s);
-  if (wn == 4 && wm == 4 && kw == 1) return launch_wm<FMT, XT, 4, 4, 1>(a, s);
-  return hipErrorInvalidValue;
+  return a.groups > 1 ? launch_plan<FMT, XT, true>(a, wn, wm, kw, s)
+                      : launch_plan<FMT, XT, false>(a, wn, wm, kw, s);
 }
 
 // K ranges of a split over `nb` 64-weight blocks when `splits` are requested: ceil(nb / bps)
@@ -369,44 +394,63 @@ int gemm_ranges(int64_t nb, int splits, int64_t* bps) {
 
 int gemm_splits_used(int64_t k, int splits) { return gemm_ranges(k / 64, splits, nullptr); }
 
-hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
-                       int64_t n, int64_t k, int64_t m, float* y, hipStream_t s, int splits,
-                       float* ws) {
-  if (m < 1 || n < 1 || k < 64 || k % 64 != 0) return hipErrorInvalidValue;
+hipError_t launch_gemm_members(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
+                               const void* const* scales, const int64_t* ns, float* const* y,
+                               int64_t k, int64_t m, hipStream_t s, int splits, float* ws) {
+  if (groups < 1 || groups > kMaxGroup || m < 1 || k < 64 || k % 64 != 0)
+    return hipErrorInvalidValue;
+  int64_t n_total = 0;
+  for (int g = 0; g < groups; ++g) {
+    if (ns[g] < 1) return hipErrorInvalidValue;
+    n_total += ns[g];
+  }
   // 32-bit offsets inside the buffer resources: 128 activation rows and 64 weight rows of K.
-  if (128 * k * 2 >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31) || m >= ((int64_t)1 << 31))
+  if (128 * k * 2 >= ((int64_t)1 << 31) || n_total >= ((int64_t)1 << 31) || m >= ((int64_t)1 << 31))
     return hipErrorNotSupported;
   int64_t bps = 0;
   const int ranges = gemm_ranges(k / 64, splits, &bps);
-  if (ranges > 1 && (!ws || (int64_t)m * n >= ((int64_t)1 << 32))) return hipErrorInvalidValue;
+  if (ranges > 1 && (groups > 1 || !ws || m * ns[0] >= ((int64_t)1 << 32)))
+    return hipErrorInvalidValue;
   const int64_t cus = device_cu_count();
   const int wm = 4;
   const int64_t mt = (m + 32 * wm - 1) / (32 * wm);
-  // Two workgroups of 128 x 128 per CU when there are that many tiles (counting every K range's);
-  // else 64 x 128 tiles, with one K group when those make two workgroups per CU, two K groups
-  // (twice the waves per tile, half the blocks per wave) when they do not.  Measured on MI355X at
-  // 512 activation rows (NF4 x fp16): 8960 x 1536 takes 41.7 us with 64 x 128 tiles and one K
-  // group against 47.2 with two and 47.0 with 128 x 128 tiles; 1536 x 8960 71.9 us with two K
-  // groups against 85.5 with one; 151936 x 1536 and 28672 x 8192 are fastest with 128 x 128 tiles
-  // (431 and 410 us).  Larger tiles (128 x 256 or 256 x 128 per workgroup, one wave per SIMD)
-  // measured 1.4-5x slower.
-  const bool full = ((n + 127) / 128) * mt * ranges >= 2 * cus;
-  const bool half = !full && ((n + 63) / 64) * mt * ranges >= 2 * cus;
+  auto tiles_of = [&](int64_t rows) {
+    int64_t t = 0;
+    for (int g = 0; g < groups; ++g) t += (ns[g] + rows - 1) / rows;
+    return t * mt;
+  };
+  // Two workgroups of 128 x 128 per CU when there are that many tiles (counting every member's
+  // and every K range's); else 64 x 128 tiles, with one K group when those make two workgroups
+  // per CU, two K groups (twice the waves per tile, half the blocks per wave) when they do not.
+  // Measured on MI355X at 512 activation rows (NF4 x fp16): 8960 x 1536 takes 41.7 us with
+  // 64 x 128 tiles and one K group against 47.2 with two and 47.0 with 128 x 128 tiles; 1536 x
+  // 8960 71.9 us with two K groups against 85.5 with one; 151936 x 1536 and 28672 x 8192 are
+  // fastest with 128 x 128 tiles (431 and 410 us).  Larger tiles (128 x 256 or 256 x 128 per
+  // workgroup, one wave per SIMD) measured 1.4-5x slower.
+  const bool full = tiles_of(128) * ranges >= 2 * cus;
+  const bool half = !full && tiles_of(64) * ranges >= 2 * cus;
   const int wn = full ? 4 : 2, kw = full || half ? 1 : 2;
-  const int64_t nt = (n + 32 * wn - 1) / (32 * wn);
-  if (nt * mt >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  const int64_t tiles = tiles_of(32 * wn);
+  if (tiles >= ((int64_t)1 << 31)) return hipErrorNotSupported;
   GemmArgs a;
+  int64_t tile0 = 0;
+  for (int g = 0; g < kMaxGroup; ++g) {
+    const bool use = g < groups;
+    a.mb[g].packed = use ? packed[g] : packed[0];
+    a.mb[g].scales = use ? scales[g] : scales[0];
+    a.mb[g].y = use ? (ranges > 1 ? ws : y[g]) : nullptr;
+    a.mb[g].n = use ? (uint32_t)ns[g] : 0u;
+    a.mb[g].tile0 = use ? (uint32_t)tile0 : 0xFFFFFFFFu;
+    if (use) tile0 += ((ns[g] + 32 * wn - 1) / (32 * wn)) * mt;
+  }
   a.x = x;
-  a.packed = packed;
-  a.scales = scales;
-  a.y = ranges > 1 ? ws : y;
+  a.groups = (uint32_t)groups;
   a.m = (uint32_t)m;
-  a.n = (uint32_t)n;
   a.k = (uint32_t)k;
   a.mt = (uint32_t)mt;
-  a.tiles = (uint32_t)(nt * mt);
+  a.tiles = (uint32_t)tiles;
   a.bps = (uint32_t)bps;
-  a.ysplit = ranges > 1 ? (uint32_t)(m * n) : 0u;
+  a.ysplit = ranges > 1 ? (uint32_t)(m * ns[0]) : 0u;
   hipError_t e = hipErrorInvalidValue;
   switch (fmt) {
     case W4_NF4_X_F16: e = launch_fx<kNF4, kF16>(a, wn, wm, kw, s); break;
@@ -420,7 +464,13 @@ hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const 
   }
   if (e != hipSuccess || ranges == 1) return e;
   // the ranges' partial sums, added in range order into y
-  return launch_splitk_reduce(ws, y, m * n, ranges, s);
+  return launch_splitk_reduce(ws, y[0], m * ns[0], ranges, s);
+}
+
+hipError_t launch_gemm(int fmt, const uint16_t* x, const uint8_t* packed, const void* scales,
+                       int64_t n, int64_t k, int64_t m, float* y, hipStream_t s, int splits,
+                       float* ws) {
+  return launch_gemm_members(fmt, x, 1, &packed, &scales, &n, &y, k, m, s, splits, ws);
 }
 
 }  // namespace w4

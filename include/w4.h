@@ -271,9 +271,10 @@ int w4_gemm_prefill(const void* x, const uint8_t* packed, const void* scales, in
  * launch of the kernel w4_gemm_smallbatch would pick for a matrix of sum-of-N_g rows: the fused
  * GEMV (as w4_gemv_grouped) for small B, the MFMA kernel over the row tiles of every member for
  * larger B (LLM Compressor 0.14: GPTQ's 15x speedup is one fused loop, section "Batching
- * layers").  From B = W4_TILED_FROM_BATCH each member of N_g >= W4_TILED_FROM_ROWS runs as its
- * own tiled-GEMM launch (bitwise equal to w4_gemm_prefill on it) and the others share one MFMA
- * launch.  Arguments, ownership and errors as for w4_gemv_grouped, with B up to
+ * layers").  From B = W4_TILED_FROM_BATCH the members of N_g >= W4_TILED_FROM_ROWS share one
+ * tiled-GEMM launch (their tiles one after another; each y_g is bitwise equal to w4_gemm_prefill
+ * on that member when both launches run the same number of K groups per tile: one when a launch
+ * has at least two 64 x 128 tiles per CU, two below) and the others share one MFMA launch.  Arguments, ownership and errors as for w4_gemv_grouped, with B up to
  * W4_MAX_BATCH.  Each y_g meets w4_gemm_smallbatch's accuracy bound on that member.  No
  * workspace.  Asynchronous on `stream`. */
 int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* packed,

@@ -193,8 +193,8 @@ def test_tiled_splitk_auto_full_size_sampled(fmt, n, k, b):
 @pytest.mark.parametrize("fmt", ["nf4_f16", "int4_bf16"])
 def test_grouped_at_prefill_batch(fmt):
     """w4_gemm_smallbatch_grouped from W4_TILED_FROM_BATCH on: members of W4_TILED_FROM_ROWS rows
-    and more through the tiled GEMM (bitwise equal to w4_gemm_prefill on them), the others in one
-    MFMA launch; every member against the oracle."""
+    and more through the tiled GEMM (one member: bitwise equal to w4_gemm_prefill on it), the
+    others in one MFMA launch; every member against the oracle."""
     import torch
 
     import bit_weight_only_w4_amd as w4
@@ -213,6 +213,73 @@ def test_grouped_at_prefill_batch(fmt):
     assert torch.equal(ys[0], w4.gemm_prefill(xd, packed[0], scales[0], fmt))
     for y, (pr, sr) in zip(ys, refs):
         g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_grouped_tiled_members(fmt):
+    """Several members of W4_TILED_FROM_ROWS rows and more share one tiled launch (their tiles one
+    after another, ragged row counts, an MFMA member beside them): every member against the oracle,
+    bitwise equal to w4_gemm_prefill on it (both launches take the same tile plan here: 64 x 128
+    tiles, two K groups), and repeatable bitwise; y pre-filled with NaN."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    k, b = 1024, 160
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=81)
+    xd = g.to_dev_x(x, g.XDT[fmt])
+    ns = (w4.TILED_FROM_ROWS + 33, 300, w4.TILED_FROM_ROWS + 1000, w4.TILED_FROM_ROWS)
+    packed, scales, refs = [], [], []
+    for i, n in enumerate(ns):
+        w = synth_inputs.weights(n, k, seed=90 + i)
+        p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+        packed.append(p)
+        scales.append(s)
+        refs.append(g.oracle_quantize(fmt, w))
+    ys = [torch.full((b, n), float("nan"), device=xd.device) for n in ns]
+    w4.gemm_smallbatch_grouped(xd, packed, scales, fmt, ys=ys)
+    for i, (y, (pr, sr)) in enumerate(zip(ys, refs)):
+        g.assert_y_close(fmt, y, x, pr, sr)
+        if ns[i] >= w4.TILED_FROM_ROWS:
+            assert torch.equal(y, w4.gemm_prefill(xd, packed[i], scales[i], fmt))
+    again = w4.gemm_smallbatch_grouped(xd, packed, scales, fmt)
+    for y, y2 in zip(ys, again):
+        assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("fmt", ["nf4_f16", "int4a_bf16"])
+def test_grouped_tiled_gate_up_full_size(fmt):
+    """The gate and up projections (8960 x 1536 each) of a 512-token prompt in one grouped call:
+    one tiled launch over both (128 x 128 tiles), bitwise equal to w4_gemm_prefill on each (64 x
+    128 tiles: the same per-block accumulation order with one K group); 160 sampled rows of each
+    against the oracle."""
+    import numpy as np
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    dev = g.device()
+    n, k, b = 8960, 1536, 512
+    x = synth_inputs.activations(b, k, g.XDT[fmt], seed=515)
+    xd = g.to_dev_x(x, g.XDT[fmt])
+    packed, scales, checks = [], [], []
+    for i in range(2):
+        gen = torch.Generator(device=dev).manual_seed(4242 + i)
+        w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+        p, s = g.gpu_quantize(fmt, w)
+        rng = np.random.default_rng(77 + i)
+        rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 158, replace=False)]))
+        w_rows = w[torch.as_tensor(rows, device=dev)].cpu().numpy()
+        del w
+        pr, sr = g.oracle_quantize(fmt, w_rows)
+        g.assert_quant_equal(fmt, p, s, pr, sr, rows=rows)
+        packed.append(p)
+        scales.append(s)
+        checks.append((rows, pr, sr))
+    ys = w4.gemm_smallbatch_grouped(xd, packed, scales, fmt)
+    for i, (y, (rows, pr, sr)) in enumerate(zip(ys, checks)):
+        assert torch.equal(y, w4.gemm_prefill(xd, packed[i], scales[i], fmt))
+        g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
