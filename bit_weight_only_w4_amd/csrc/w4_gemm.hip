@@ -419,15 +419,19 @@ hipError_t launch_gemm_members(int fmt, const uint16_t* x, int groups, const uin
     for (int g = 0; g < groups; ++g) t += (ns[g] + rows - 1) / rows;
     return t * mt;
   };
-  // Two workgroups of 128 x 128 per CU when there are that many tiles (counting every member's
-  // and every K range's); else 64 x 128 tiles, with one K group when those make two workgroups
-  // per CU, two K groups (twice the waves per tile, half the blocks per wave) when they do not.
-  // Measured on MI355X at 512 activation rows (NF4 x fp16): 8960 x 1536 takes 41.7 us with
-  // 64 x 128 tiles and one K group against 47.2 with two and 47.0 with 128 x 128 tiles; 1536 x
-  // 8960 71.9 us with two K groups against 85.5 with one; 151936 x 1536 and 28672 x 8192 are
-  // fastest with 128 x 128 tiles (431 and 410 us).  Larger tiles (128 x 256 or 256 x 128 per
-  // workgroup, one wave per SIMD) measured 1.4-5x slower.
-  const bool full = tiles_of(128) * ranges >= 2 * cus;
+  // 128 x 128 tiles (one K group) when there are enough of them, counting every member's and
+  // every K range's: 1.5 per CU for rows of at least 4096 weights, 4 per CU for shorter rows;
+  // else 64 x 128 tiles, with one K group when those make two workgroups per CU, two K groups
+  // (twice the waves per tile, half the blocks per wave) when they do not.  The larger tile halves
+  // the activation traffic per weight; the smaller one fills the CUs more evenly, which matters
+  // most for short rows (few blocks per tile).  Measured on MI355X (NF4 x fp16, 128 x 128 against
+  // 64 x 128 tiles): 16032 x 8192 at 512 activation rows (504 tiles of 128 x 128) 218 against
+  // 245 us, 2 x 28672 x 8192 at 256 (448) 429 against 443, 8192 x 8192 at 512 (256) 133 against
+  // 129; 2 x 8960 x 1536 at 512 (560) 76.3 against 68.9, at 1024 (1120) 120.8 against 120.1,
+  // 151936 x 1536 at 128 (1187) 145 against 151; at 512 activation rows 1536 x 8960 takes 71.9 us
+  // with two K groups against 85.5 with one.  Larger tiles (128 x 256 or 256 x 128 per workgroup,
+  // one wave per SIMD) measured 1.4-5x slower.
+  const bool full = tiles_of(128) * ranges >= (k >= 4096 ? 3 * cus / 2 : 4 * cus);
   const bool half = !full && tiles_of(64) * ranges >= 2 * cus;
   const int wn = full ? 4 : 2, kw = full || half ? 1 : 2;
   const int64_t tiles = tiles_of(32 * wn);

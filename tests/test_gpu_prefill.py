@@ -250,9 +250,9 @@ def test_grouped_tiled_members(fmt):
 @pytest.mark.parametrize("fmt", ["nf4_f16", "int4a_bf16"])
 def test_grouped_tiled_gate_up_full_size(fmt):
     """The gate and up projections (8960 x 1536 each) of a 512-token prompt in one grouped call:
-    one tiled launch over both (128 x 128 tiles), bitwise equal to w4_gemm_prefill on each (64 x
-    128 tiles: the same per-block accumulation order with one K group); 160 sampled rows of each
-    against the oracle."""
+    one tiled launch over both, bitwise equal to w4_gemm_prefill on each (both launches run one K
+    group per tile, hence the same per-block accumulation order); 160 sampled rows of each against
+    the oracle."""
     import numpy as np
     import torch
 
