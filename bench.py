@@ -930,7 +930,7 @@ def prefill_suite(args, dev):
     for fmt in ("nf4_f16", "int4_bf16"):
         for name, n, k in shapes:
             ap, sk = w4.auto_path(fmt, n, k, b, w4.workspace_bytes(fmt, n, k, b))
-            row = {"format": fmt, "shape": name, "n": n, "k": k, "b": b, "auto": ap,
+            row = {"format": fmt, "shape": name, "n": n, "k": k, "b": b, "auto_path": ap,
                    "auto_split": sk}
             mats = rotated_mats(fmt, n, k, dev, min_bytes=256 << 20)
             # "auto": the automatic path with the workspace it asks for (the tiled GEMM over K
@@ -1293,9 +1293,12 @@ COUNTER_CASES = [
     ("mfma nf4 lm_head B=32", "nf4_f16", 151936, 1536, 32, "mfma"),
     ("mfma nf4 lm_head B=128", "nf4_f16", 151936, 1536, 128, "mfma"),
     ("twopass nf4 gate B=1", "nf4_f16", 8960, 1536, 1, "twopass"),
+    ("tiled nf4 gate B=512", "nf4_f16", 8960, 1536, 512, "tiled"),
+    ("tiled nf4 lm_head B=512", "nf4_f16", 151936, 1536, 512, "tiled"),
+    ("tiled nf4 L.gate B=512", "nf4_f16", 28672, 8192, 512, "tiled"),
 ]
 COUNTER_LAUNCHES = 3
-COUNTER_KERNELS = ("gemv_kernel", "mfma_kernel", "dequant", "dense")
+COUNTER_KERNELS = ("gemv_kernel", "mfma_kernel", "gemm_kernel", "dequant", "dense")
 
 
 def counters_suite(dev):
