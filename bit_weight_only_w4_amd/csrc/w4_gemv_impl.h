@@ -275,13 +275,20 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   // along x, found by selects over the member slots (every slot is fetched in the one batch of
   // scalar loads; indexing the slots by a loaded value would add a second, dependent batch).
   GemvMember mm = a.m[0];
+  if constexpr (!GROUPED) {
+    // (Taking these fields here makes the compiler fetch the whole argument block in one batch
+    // with one wait; the decode-table switch otherwise came in a late second batch whose wait
+    // delayed the table fill by a scalar-memory round trip.)
+    asm volatile("" ::"s"(mm.packed), "s"(mm.n), "s"(mm.nrb), "s"(mm.grid), "s"(a.x),
+                 "s"(a.small_table), "s"(a.team));
+  }
   if constexpr (GROUPED) {
     // (The empty asm statements take every slot's fields first, so that the compiler fetches them
     // in one batch instead of loading the chosen slot after comparing.)
 #pragma unroll
     for (int i = 0; i < (GROUPED ? kMaxGroup : 1); ++i) {
       asm volatile("" ::"s"(a.m[i].packed), "s"(a.m[i].scales), "s"(a.m[i].out), "s"(a.m[i].n),
-                   "s"(a.m[i].nrb), "s"(a.m[i].wg0), "s"(a.m[i].grid));
+                   "s"(a.m[i].nrb), "s"(a.m[i].wg0), "s"(a.m[i].grid), "s"(a.x), "s"(a.small_table));
     }
 #pragma unroll
     for (int i = 1; i < (GROUPED ? kMaxGroup : 1); ++i) {
@@ -298,10 +305,12 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   // 32-bit index arithmetic for row blocks (the host guarantees N < 2^31); one 32-bit division
   // gives this workgroup's trip count.
   const uint32_t nrb = mm.nrb;
-  const uint32_t grid = GROUPED ? mm.grid : gridDim.x;
+  const uint32_t grid = mm.grid;  // = gridDim.x for one member (read with the other arguments)
   const uint32_t rb0 = GROUPED ? blockIdx.x - mm.wg0 : blockIdx.x;
-  const uint32_t count = (nrb - 1u - rb0) / grid + 1u;  // row blocks of this workgroup (>= 1)
-  const uint32_t rb_last = rb0 + grid * (count - 1u);
+  // Row blocks of this workgroup (>= 1) and the last of them; computed after the first row
+  // block's and the activations' loads are issued (those need neither), so that the division
+  // does not delay them.
+  uint32_t count = 1u, rb_last = rb0;
 
   // Chunk index of slot i for this lane within the split, and whether the lane has that chunk.
   auto chunk_at = [&](int i) { return tl + (i << tshift); };
@@ -321,10 +330,12 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   // without touching memory, and need no clamping or branch.
   const uint32_t pitch = (uint32_t)(k >> 1);  // packed bytes per row
   const uint32_t spitch = scale_pitch<FMT>(k);
-  auto load_rb = [&](uint32_t rbv, uint4 (&p)[ITM], ScaleSlot<FMT> (&s)[ITM]) {
+  auto load_rb = [&](uint32_t rbv, uint4 (&p)[ITM], ScaleSlot<FMT> (&s)[ITM], bool clamp = true) {
     // A prefetch past this workgroup's last row block re-reads that block (an L2 hit) rather
-    // than switching the resource off, which would need a per-block select of its size.
-    const Where w = where(rbv < rb_last ? rbv : rb_last);
+    // than switching the resource off, which would need a per-block select of its size.  The
+    // first row block needs no clamp (rb0 <= rb_last), so its loads do not wait for the trip
+    // count's division.
+    const Where w = where(!clamp || rbv < rb_last ? rbv : rb_last);
     uint32_t rows = w.n - w.row0;  // w.row0 < w.n: every row block up to rb_last exists
     rows = rows < (uint32_t)teams_per_wg ? rows : (uint32_t)teams_per_wg;
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(w.packed + (int64_t)w.row0 * pitch, rows * pitch);
@@ -344,7 +355,7 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
   // --- first row block, then this lane's activations, then the second row block
   uint4 pA[ITM], pB[ITM], pC[ITM];
   ScaleSlot<FMT> sA[ITM], sB[ITM], sC[ITM];
-  load_rb(rb0, pA, sA);
+  load_rb(rb0, pA, sA, false);
   uint32_t xr[ITM][B][16];
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(B * k * 2));
 #pragma unroll
@@ -356,14 +367,7 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
       const uint32_t xo = offset_or_oob(have, (uint32_t)(b * k + (int64_t)(c0 + c) * 32) * 2u);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint4 v = buffer_load16(rx, xo + 16u * q);
-        if constexpr (FMT == kFP4) {
-          // the hardware FP4 conversion yields (odd k, even k) pairs: swap each activation pair
-          v = make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
-                         __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
-        } else if constexpr (kIntTf) {
-          v = int4_x_order(v);  // the pairs the nibble decode makes: (k1, k5), (k0, k4), ...
-        }
+        const uint4 v = buffer_load16(rx, xo + 16u * q);
         xr[i][b][4 * q + 0] = v.x;
         xr[i][b][4 * q + 1] = v.y;
         xr[i][b][4 * q + 2] = v.z;
@@ -371,7 +375,36 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
       }
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  count = (nrb - 1u - rb0) / grid + 1u;
+  rb_last = rb0 + grid * (count - 1u);
   load_rb(rb0 + grid, pB, sB);
+  // Activation pairs in the order the table-free decodes make them (after the loads above, which
+  // these rearrangements would otherwise wait for).
+  if constexpr (FMT == kFP4 || kIntTf) {
+#pragma unroll
+    for (int i = 0; i < ITM; ++i) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint4 v = make_uint4(xr[i][b][4 * q], xr[i][b][4 * q + 1], xr[i][b][4 * q + 2],
+                               xr[i][b][4 * q + 3]);
+          if constexpr (FMT == kFP4) {
+            // the hardware FP4 conversion yields (odd k, even k) pairs: swap each pair
+            v = make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
+                           __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
+          } else {
+            v = int4_x_order(v);  // the pairs the nibble decode makes: (k1, k5), (k0, k4), ...
+          }
+          xr[i][b][4 * q + 0] = v.x;
+          xr[i][b][4 * q + 1] = v.y;
+          xr[i][b][4 * q + 2] = v.z;
+          xr[i][b][4 * q + 3] = v.w;
+        }
+      }
+    }
+  }
 
   // --- decode table, written while the loads above are in flight
   if constexpr (kTable) {
