@@ -367,7 +367,14 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
       const uint32_t xo = offset_or_oob(have, (uint32_t)(b * k + (int64_t)(c0 + c) * 32) * 2u);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = buffer_load16(rx, xo + 16u * q);
+        uint4 v = buffer_load16(rx, xo + 16u * q);
+        if constexpr (FMT == kFP4) {
+          // the hardware FP4 conversion yields (odd k, even k) pairs: swap each activation pair
+          v = make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
+                         __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
+        } else if constexpr (kIntTf) {
+          v = int4_x_order(v);  // the pairs the nibble decode makes: (k1, k5), (k0, k4), ...
+        }
         xr[i][b][4 * q + 0] = v.x;
         xr[i][b][4 * q + 1] = v.y;
         xr[i][b][4 * q + 2] = v.z;
@@ -375,36 +382,14 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
       }
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
+  // (Table launches: the division after the loads above.  The table-free ones rearrange their
+  // activation pairs as they arrive; a scheduling barrier here would make those rearrangements
+  // wait for the loads before the next row block is requested, 1% slower per step.)
+  if constexpr (kTable) __builtin_amdgcn_sched_barrier(0);
   count = (nrb - 1u - rb0) / grid + 1u;
   rb_last = rb0 + grid * (count - 1u);
   load_rb(rb0 + grid, pB, sB);
-  // Activation pairs in the order the table-free decodes make them (after the loads above, which
-  // these rearrangements would otherwise wait for).
-  if constexpr (FMT == kFP4 || kIntTf) {
-#pragma unroll
-    for (int i = 0; i < ITM; ++i) {
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint4 v = make_uint4(xr[i][b][4 * q], xr[i][b][4 * q + 1], xr[i][b][4 * q + 2],
-                               xr[i][b][4 * q + 3]);
-          if constexpr (FMT == kFP4) {
-            // the hardware FP4 conversion yields (odd k, even k) pairs: swap each pair
-            v = make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
-                           __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
-          } else {
-            v = int4_x_order(v);  // the pairs the nibble decode makes: (k1, k5), (k0, k4), ...
-          }
-          xr[i][b][4 * q + 0] = v.x;
-          xr[i][b][4 * q + 1] = v.y;
-          xr[i][b][4 * q + 2] = v.z;
-          xr[i][b][4 * q + 3] = v.w;
-        }
-      }
-    }
-  }
+
 
   // --- decode table, written while the loads above are in flight
   if constexpr (kTable) {
