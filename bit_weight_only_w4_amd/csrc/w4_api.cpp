@@ -391,7 +391,7 @@ bool prefer_tiled(int64_t n, int64_t b) { return b >= W4_TILED_FROM_BATCH && n >
 // 27.0 / 21.0 us against the MFMA path's 56.9 / 47.2 / 24.5; 1024 x 8192: 25.9 / 18.9 / 18.7
 // against 51.3 / 23.2 / 22.3), else the MFMA path.
 bool prefer_tiled_split(int64_t n, int64_t k, int64_t b, size_t workspace_bytes, int* splits) {
-  if (b < W4_TILED_FROM_BATCH) return false;
+  if (b < W4_TILED_FROM_BATCH || b * n >= ((int64_t)1 << 32)) return false;
   const int s = auto_tiled_splits(n, k, b);
   const int ranges = s > 1 ? gemm_splits_used(k, s) : 1;
   if (ranges > 1 && workspace_bytes >= splitk_bytes(n, b, ranges)) {

@@ -409,8 +409,8 @@ hipError_t launch_gemm_members(int fmt, const uint16_t* x, int groups, const uin
     return hipErrorNotSupported;
   int64_t bps = 0;
   const int ranges = gemm_ranges(k / 64, splits, &bps);
-  if (ranges > 1 && (groups > 1 || !ws || m * ns[0] >= ((int64_t)1 << 32)))
-    return hipErrorInvalidValue;
+  if (ranges > 1 && (groups > 1 || !ws)) return hipErrorInvalidValue;
+  if (ranges > 1 && m * ns[0] >= ((int64_t)1 << 32)) return hipErrorNotSupported;  // 32-bit planes
   const int64_t cus = device_cu_count();
   const int wm = 4;
   const int64_t mt = (m + 32 * wm - 1) / (32 * wm);

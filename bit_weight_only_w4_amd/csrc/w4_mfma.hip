@@ -124,6 +124,7 @@ hipError_t launch_mfma_members(int fmt, const uint16_t* x, int groups, const uin
                                int64_t k, int64_t b, hipStream_t s, int splits, float* ws) {
   if (groups < 1 || groups > kMaxGroup) return hipErrorInvalidValue;
   if (splits > 1 && (groups != 1 || ws == nullptr)) return hipErrorInvalidValue;
+  if (splits > 1 && b * ns[0] >= ((int64_t)1 << 32)) return hipErrorNotSupported;  // 32-bit planes
   MfmaPlan p;
   if (!plan_mfma(ns, groups, k, b, splits, &p)) return hipErrorNotSupported;
   MfmaArgs a;
