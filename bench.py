@@ -852,6 +852,52 @@ def shape_table(fmt, dev, read_gbs, large=True):
     return rows
 
 
+# Steps and the split-K table the default run also records (the grouped schedule; compact).
+LINE_STEPS = [("int4_bf16", 1), ("int4_bf16", 8), ("nf4_f16", 8)]
+LINE_SPLITK = [("int4_bf16", 1, "splitk"), ("int4_bf16", 8, "mfma")]
+
+
+def line_extras(args, dev):
+    """The decode step in INT4 x bf16 at B = 1 and 8 and in NF4 x fp16 at B = 8 (grouped schedule,
+    automatic paths), and the down projection 1536 x 8960 in INT4 x bf16 at B = 1 (fused GEMV
+    split-K) and B = 8 (MFMA split-K) for S = 1, 2, 4, 8, 16 against the automatic choice, each
+    timed over rotated weights: the records the benchmark line carries besides its own step."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    steps = []
+    for fmt, b in LINE_STEPS:
+        step = Step(fmt, b, "auto", dev)
+        total = sum(step.bytes)
+        g = capture(step, dev, step_units(step.shapes, "grouped"), "grouped")
+        ms = time_replays(g, args.steps, max(args.warmup, 500))  # clocks settle over ~0.3 s
+        del g
+        steps.append({"format": fmt, "batch": b, "paths": sorted({p for p, _ in step.plans}),
+                      "ms_per_step": round(ms, 5), "tok_s": round(b * 1e3 / ms, 2),
+                      "gbs": round(total / (ms / 1e3) / 1e9, 1)})
+        log(f"[extras] step {fmt} B={b} grouped: {ms * 1e3:.1f} us/step, {b * 1e3 / ms:.1f} tok/s")
+        del step
+        torch.cuda.empty_cache()
+    splitk = []
+    n, k = 1536, 8960
+    for fmt, b, path in LINE_SPLITK:
+        mats = rotated_mats(fmt, n, k, dev)
+        ap, ask = w4.auto_path(fmt, n, k, b, w4.workspace_bytes(fmt, n, k, b))
+        row = {"format": fmt, "n": n, "k": k, "b": b, "split_path": path, "auto": [ap, ask], "us": {}}
+        for s in (1, 2, 4, 8, 16):
+            p = ("gemv" if path == "splitk" else "mfma") if s == 1 else path
+            us, err = time_shape(fmt, n, k, b, p, s if s > 1 else 0, dev, mats=mats)
+            row["us"][str(s)] = round(us, 3) if us is not None else err
+        us, err = time_shape(fmt, n, k, b, "auto", 0, dev, mats=mats)
+        row["us"]["auto"] = round(us, 3) if us is not None else err
+        splitk.append(row)
+        log(f"[extras] down {fmt} B={b} {path}: " + ", ".join(f"S={s} {v}" for s, v in row["us"].items()))
+        del mats
+        torch.cuda.empty_cache()
+    return {"steps": steps, "down_splitk": splitk}
+
+
 # Decode steps besides the benchmark line's: (format, batch).
 OTHER_STEPS = [("int4_bf16", 1), ("int4_bf16", 8), ("nf4_f16", 8), ("nf4_bf16", 1), ("int4_f16", 1),
                ("fp4_f16", 1), ("fp4_bf16", 1), ("fp4_f16", 8), ("int4a_bf16", 1), ("int4a_f16", 1),
@@ -1537,6 +1583,11 @@ def main():
 
     read_gbs, copy_gbs = measure_ceilings(dev)
     log(f"[bench] ceilings: streaming read {read_gbs:.0f} GB/s, copy {copy_gbs:.0f} GB/s")
+    del step  # its 197 matrices: the other steps below allocate their own
+    torch.cuda.empty_cache()
+    extras = None
+    if not args.no_table and args.batch == 1:
+        extras = line_extras(args, dev)
     table = None
     if not args.no_table:
         table = shape_table(args.fmt, dev, read_gbs, large=not args.no_large)
@@ -1588,6 +1639,8 @@ def main():
             "single_gemv_256x1536_us": (next((r["us"] for r in table or [] if r["group"] == "single"
                                               and "us" in r), None)),
             "shape_table": table,
+            "other_steps": extras["steps"] if extras else None,
+            "down_splitk_us": extras["down_splitk"] if extras else None,
         },
         "roofline": {
             "bound": "hbm",
