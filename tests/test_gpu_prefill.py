@@ -309,3 +309,45 @@ def test_one_hot_columns_matrix_core_paths(fmt, path, b):
             "fp4_bf16": 2.0 ** -23}.get(fmt, 0.0)
     for i, c in enumerate(cols):
         assert np.allclose(y[i], w_hat[:, c], rtol=rtol, atol=0), (i, c)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shapes_matrix_core_paths(seed):
+    """Seeded random shapes through the automatic path with its workspace (which may split K on the
+    tiled GEMM or the MFMA kernel), an explicit tiled split and a grouped call of two to four
+    members: format, N (1..2500), K (a multiple of the format's group up to 4096) and B (1..700)
+    drawn from the seed; y pre-filled with NaN; every result against the oracle."""
+    import numpy as np
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    rng = np.random.default_rng(9000 + seed)
+    fmt = ALL_FMTS[int(rng.integers(len(ALL_FMTS)))]
+    grp = 128 if fmt.startswith("int4") else 64
+    k = grp * int(rng.integers(1, 4096 // grp + 1))
+    b = int(rng.choice([int(rng.integers(1, 9)), int(rng.integers(9, 128)), int(rng.integers(128, 701))]))
+    n = int(rng.integers(1, 2501))
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=seed * 7 + 3)
+    wsb = w4.workspace_bytes(fmt, n, k, b)
+    ws = torch.full((max(wsb, 16),), 0x7F, dtype=torch.uint8, device=xd.device)
+    y = torch.full((b, n), float("nan"), device=xd.device)
+    w4.matmul_ex(xd, p, s, fmt, workspace=ws, y=y)
+    g.assert_y_close(fmt, y, x, pr, sr)
+    splits = int(rng.integers(2, 17))
+    wst = w4.workspace_bytes(fmt, n, k, b, "tiled", splits)
+    wt = torch.full((max(wst, 16),), 0x7F, dtype=torch.uint8, device=xd.device)
+    yt = torch.full((b, n), float("nan"), device=xd.device)
+    w4.matmul_ex(xd, p, s, fmt, path="tiled", split_k=splits, workspace=wt, y=yt)
+    g.assert_y_close(fmt, yt, x, pr, sr)
+    # a grouped call: this matrix and one to three more of random row counts sharing x
+    members = [(p, s, pr, sr)]
+    for j in range(int(rng.integers(1, 4))):
+        nj = int(rng.integers(1, 2501))
+        w = synth_inputs.weights(nj, k, seed=seed * 31 + j)
+        pj, sj = g.gpu_quantize(fmt, g.to_dev_f32(w))
+        members.append((pj, sj) + tuple(g.oracle_quantize(fmt, w)))
+    ys = [torch.full((b, m[0].shape[0]), float("nan"), device=xd.device) for m in members]
+    w4.gemm_smallbatch_grouped(xd, [m[0] for m in members], [m[1] for m in members], fmt, ys=ys)
+    for yg, m in zip(ys, members):
+        g.assert_y_close(fmt, yg, x, m[2], m[3])
