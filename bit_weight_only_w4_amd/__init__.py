@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libw4.so")
 
 FORMATS = {"nf4_f16": 1, "nf4_bf16": 2, "int4_f16": 3, "int4_bf16": 4, "fp4_f16": 5, "fp4_bf16": 6,
            "int4a_f16": 7, "int4a_bf16": 8}
-PATHS = {"auto": 0, "gemv": 1, "splitk": 2, "mfma": 3, "twopass": 4, "tiled": 5}
+PATHS = {"auto": 0, "gemv": 1, "splitk": 2, "mfma": 3, "twopass": 4, "tiled": 5, "tiled_f16": 6}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 STATUS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "FORMAT", -5: "NONFINITE",
           -6: "WORKSPACE", -7: "PATH", -8: "HIP", -9: "ALIAS"}

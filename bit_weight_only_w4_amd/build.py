@@ -24,7 +24,7 @@ SOURCES = ["w4_api.cpp", "w4_gemv.hip",
            "w4_gemv_fp4_f16_grouped.hip", "w4_gemv_fp4_bf16_grouped.hip",
            "w4_gemv_int4a_f16.hip", "w4_gemv_int4a_bf16.hip", "w4_gemv_int4a_f16_grouped.hip",
            "w4_gemv_int4a_bf16_grouped.hip",
-           "w4_quant.hip", "w4_twopass.hip", "w4_mfma.hip", "w4_mfma_grouped.hip", "w4_gemm.hip",
+           "w4_quant.hip", "w4_twopass.hip", "w4_mfma.hip", "w4_mfma_grouped.hip", "w4_gemm.hip", "w4_gemm_fold.hip",
            "w4_gptq.hip", "w4_sparse24.hip", "w4_probe.hip"]
 ARCH = "gfx950"
 

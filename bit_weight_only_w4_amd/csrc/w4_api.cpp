@@ -57,10 +57,11 @@ std::mutex g_settings_mu;
 Settings g_settings;
 
 int parse_path_name(const char* v) {
-  static const char* const names[] = {"auto", "gemv", "splitk", "mfma", "twopass", "tiled"};
-  for (int i = 0; i < 6; ++i)
+  static const char* const names[] = {"auto", "gemv", "splitk", "mfma", "twopass", "tiled",
+                                      "tiled_f16"};
+  for (int i = 0; i < 7; ++i)
     if (strcmp(v, names[i]) == 0) return i;
-  if (v[0] >= '0' && v[0] <= '5' && v[1] == 0) return v[0] - '0';
+  if (v[0] >= '0' && v[0] <= '6' && v[1] == 0) return v[0] - '0';
   return -1;
 }
 
@@ -349,6 +350,19 @@ int run_mfma(const void* x, const uint8_t* packed, const void* scales, int fmt, 
              int64_t k, int64_t b, float* y, hipStream_t st, int splits = 1, void* ws = nullptr) {
   const hipError_t e = launch_mfma(fmt, reinterpret_cast<const uint16_t*>(x), packed, scales, n, k,
                                    b, y, st, splits, reinterpret_cast<float*>(ws));
+  if (e == hipErrorNotSupported) return W4_ERR_PATH;
+  return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+// The folded-scale GEMM on one matrix: the automatic tile rows, or 128-row tiles where the
+// automatic choice would take the block-scale kernel.
+int run_tiled_f16(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
+                  int64_t k, int64_t b, float* y, hipStream_t st) {
+  if (!gemm_fold_format(fmt)) return W4_ERR_PATH;
+  int rows = gemm_fold_tile_rows(fmt, &n, 1, k, b);
+  if (rows == 0) rows = 128;
+  const hipError_t e = launch_gemm_fold(fmt, reinterpret_cast<const uint16_t*>(x), 1, &packed,
+                                        &scales, &n, &y, k, b, rows, st);
   if (e == hipErrorNotSupported) return W4_ERR_PATH;
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
@@ -726,6 +740,9 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
         return W4_ERR_ALIAS;
       return run_tiled(x, packed, scales, fmt, n, k, b, y, s, ranges, workspace);
     }
+    case W4_PATH_TILED_F16:
+      if (split_k > 1) return W4_ERR_PATH;
+      return run_tiled_f16(x, packed, scales, fmt, n, k, b, y, s);
     case W4_PATH_TWOPASS: {
       const size_t used = (size_t)n * (size_t)k * 2;
       if (!workspace || workspace_bytes < used) return W4_ERR_WORKSPACE;
@@ -798,7 +815,7 @@ int w4_gemm_smallbatch(const void* x, const uint8_t* packed, const void* scales,
 }
 
 int w4_set_path(int path) {
-  if (path < W4_PATH_AUTO || path > W4_PATH_TILED) return W4_ERR_PATH;
+  if (path < W4_PATH_AUTO || path > W4_PATH_TILED_F16) return W4_ERR_PATH;
   std::lock_guard<std::mutex> lock(g_settings_mu);
   g_settings.path = path;
   g_settings.env_bad = false;

@@ -206,6 +206,14 @@ hipError_t launch_gemm_members(int fmt, const uint16_t* x, int groups, const uin
                                const void* const* scales, const int64_t* ns, float* const* y,
                                int64_t k, int64_t m, hipStream_t s, int splits = 1,
                                float* ws = nullptr);
+// Folded-scale GEMM for fp16 activations (w4_gemm_fold.hip): whether a format can run it, the
+// weight rows per tile the automatic choice gives a launch (0: the block-scale kernel is faster),
+// and one launch over `groups` members that share x and K with tiles of `tile_rows` (128 or 256).
+bool gemm_fold_format(int fmt);
+int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m);
+hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
+                            const void* const* scales, const int64_t* ns, float* const* y,
+                            int64_t k, int64_t m, int tile_rows, hipStream_t s);
 hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu, const float* scale,
                              const float* zero, int64_t lds, int group, int i1, int qmin, int qmax,
                              int64_t rows, int bc, float* q_hat, int64_t ldq, uint8_t* codes,

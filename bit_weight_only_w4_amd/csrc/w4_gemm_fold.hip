@@ -1,0 +1,464 @@
+// Prefill-size GEMM for fp16 activations with the block scale folded into the decoded weights:
+// y[m, n] = sum_k x[m, k] * W_hat[n, k], W_hat[n, k] = code(q[n, k]) * s[n, block(k)].
+//
+// Prefill needs a GEMM, not a GEMV per token (LLM Quantization on RTX 4060, "Why Only 16%", item
+// 3).  The block-scale kernel (w4_gemm.hip) multiplies the raw codes on the matrix cores and
+// rescales every block's fresh fp32 partial sums by the block scale: one FMA per output per 64
+// weights, about as many vector instructions as the matrix cores spend cycles.  With fp16
+// activations the decoded weight itself can be formed in fp16 instead: the table gives the code in
+// fp16, one packed multiply per pair applies the fp16-rounded scale, and the matrix cores then
+// accumulate x * W_hat across all blocks directly.  The rounding stays inside the accuracy bound
+// (|y - y_exact| <= 2e-3 sum_k |x w_hat| + 1e-5): code, scale and product each round to fp16
+// (at most 2^-11 relative each), so a folded NF4 weight is within 3 * 2^-11 = 1.5e-3 of W_hat,
+// an FP4 weight (exact code) within 2 * 2^-11, and an INT4 weight, (q - 8) s with a bf16 scale
+// (at most 3 + 8 significant bits), is exact.  The products with fp16 x are exact in fp32.
+//
+// A folded weight must stay a normal, finite fp16 number: a block whose scale s satisfies
+// lo <= |s| <= hi (or s == 0) is folded, with [lo, hi] = [2^-10, 2^15] for NF4 (smallest nonzero
+// |code| 0.0796), [2^-13, 2^13] for FP4 (codes 0.5 .. 6), [2^-14, 2^12] for INT4 (|q - 8| <= 8).
+// Every wave checks all block scales of its rows once, in its prologue; a wave that meets one
+// outside that range (tiny, huge, infinite or NaN scales) runs all of K through the block-scale
+// route instead: raw codes on the matrix cores, fp32 rescaling of each block's partial sums.
+//
+// Work layout.  A workgroup has 4 waves and an output tile of TN = 128 NT weight rows x TM = 128
+// activation rows; wave w owns weight rows [32 NT w, 32 NT (w + 1)) of the tile and all TM
+// activation rows, so every weight is decoded once per tile.  Matrix step: v_mfma_f32_32x32x16_f16
+// with the activations as the A operand and the weights as the B operand:
+//   * A (32 activation rows x 16 k): lane l = 32 h + c takes row c and 8 consecutive k.
+//   * B (16 k x 32 weight rows): lane l = 32 h + c takes weight row c and the same 8 k.
+//   * D (32 x 32 fp32, 16 registers): lane l = 32 h + c holds weight row c, activation rows
+//     8 (e / 4) + 4 h + e % 4 (register e).  Each lane's outputs share one weight row, so a block
+//     scale reaches them without any cross-lane broadcast.
+// K runs one 64-weight block per step (an NF4/FP4 block, half an INT4 group).  Lane (h, c) loads
+// bytes [16 h, 16 h + 16) of its row's 32-byte block: weights 32 h .. 32 h + 31, of which matrix
+// step q (0 .. 3) takes 32 h + 8 q .. + 7; the A lanes read the same k positions of x.
+//   * Activations: ST stages of TM rows x 64 k in LDS (16 KiB each), copied straight from global
+//     memory by buffer loads with the LDS destination (no register round trip), ST - 1 blocks
+//     ahead; 16-byte slot S of a stage holds row S / 8 and chunk (S % 8) XOR (row % 8), which puts
+//     the eight rows a group of lanes reads into distinct banks.
+//   * Weights and scales: DP blocks ahead in rotating register sets.
+//   * Decode: the byte -> pair table of w4_mfma_common.h (32 copies, one LDS read per two weights).
+//   * Tiles are numbered so that the workgroups one XCD receives (every eighth) take consecutive
+//     tiles, the activation-row tiles of a weight tile first: the weight tile then comes from that
+//     XCD's L2 after its first read.
+#include <algorithm>
+
+#include "w4_mfma_common.h"
+
+namespace w4 {
+
+struct FoldMember {
+  const uint8_t* packed;  // [N_g, K/2]
+  const void* scales;     // NF4, FP4 float[N_g, K/64] | INT4 uint16 (bf16) [N_g, K/128]
+  float* y;               // [M, N_g]
+  uint32_t n;             // N_g
+  uint32_t tile0;         // first tile of this member
+};
+
+struct FoldArgs {
+  FoldMember mb[kMaxGroup];
+  const uint16_t* x;  // [M, K] fp16 bits
+  uint32_t groups;
+  uint32_t m, k;
+  uint32_t mt;     // activation-row tiles (128 rows each)
+  uint32_t tiles;  // tiles of all members
+};
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kFoldThreads = 256;
+constexpr int kFoldMT = 4;  // 32-row activation tiles per wave: TM = 128
+
+__device__ inline f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                 __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+// The fold range of a block scale (see the top of this file), and the scale as fp32.
+template <int FMT>
+__device__ inline bool foldable(float s) {
+  const float a = __builtin_fabsf(s);
+  constexpr float lo = FMT == kNF4 ? 0x1p-10f : FMT == kFP4 ? 0x1p-13f : 0x1p-14f;
+  constexpr float hi = FMT == kNF4 ? 0x1p15f : FMT == kFP4 ? 0x1p13f : 0x1p12f;
+  return s == 0.0f || (a >= lo && a <= hi);
+}
+template <int FMT>
+__device__ inline float scale_f32(uint32_t raw) {
+  return FMT == kINT4 ? __uint_as_float(raw << 16) : __uint_as_float(raw);
+}
+
+// The block-scale route of one wave, for rows that hold a scale outside the fold range: raw codes
+// on the matrix cores, each block's partial sums rescaled in fp32 (exact scale, any range), then
+// the wave's stores.  It walks the same stages with the same barriers as the folded loop (the
+// stages are filled by every wave of the workgroup) but loads each block's weights when it needs
+// them.  Kept out of line, with accumulators of its own: the folded loop's registers are then
+// allocated as if this route did not exist (inlined, it cost the folded route 8-30%).
+template <int FMT, int NT, int ST>
+__device__ __attribute__((noinline)) void fold_block_scale_wave(
+    __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rx,
+    const char* tabc, uint4* xst0, float* y, uint32_t n, uint32_t m, uint32_t m0, uint32_t wrow0,
+    uint32_t k) {
+  constexpr int MT = kFoldMT;
+  constexpr int SLOTS = 32 * MT * 8;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, c = lane & 31;
+  const uint32_t nkb = k / 64u, pitch = k >> 1;
+  constexpr uint32_t kSB = FMT == kINT4 ? 2u : 4u;
+  const uint32_t spitch = (k / (FMT == kINT4 ? 128u : 64u)) * kSB;
+  const uint32_t laneoff = (uint32_t)c * 8u;
+  f32x16 acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][j][e] = 0.f;
+  for (uint32_t kb = 0; kb < nkb; ++kb) {
+    const uint32_t b = kb % (uint32_t)ST;
+    __syncthreads();
+    {
+      const uint32_t kn = kb + ST - 1, bn = (b + ST - 1) % ST;
+      const bool have = kn < nkb;
+#pragma unroll
+      for (int j = 0; j < SLOTS / kFoldThreads; ++j) {
+        const uint32_t sl = (uint32_t)(j * kFoldThreads + tid);
+        const uint32_t mr = sl >> 3, cc = (sl & 7u) ^ (mr & 7u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void*)(xst0 + bn * SLOTS + j * kFoldThreads + wave * 64),
+            16, (int)offset_or_oob(have, (mr * k + kn * 64u + cc * 8u) * 2u), 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t row = (uint32_t)(32 * t + c);
+      const uint4 w = buffer_load16_stream(rw, row * pitch + kb * 32u + 16u * (uint32_t)h);
+      const uint32_t raw = FMT == kINT4 ? buffer_load16bit(rs, row * spitch + (kb >> 1) * 2u)
+                                        : buffer_load32(rs, row * spitch + kb * 4u);
+      const float sf = scale_f32<FMT>(raw);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      uint4 bu[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t pr[4];
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+          const uint32_t addr =
+              __builtin_amdgcn_perm(wd[q], laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb4) << 8)) >> 1;
+          pr[kb4] = *reinterpret_cast<const uint32_t*>(tabc + addr);
+        }
+        bu[q] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+      }
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        f32x16 dd;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dd[e] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t mr = (uint32_t)(32 * j + c), cc = (uint32_t)(4 * h + q);
+          dd = mfma32(xst0[b * SLOTS + mr * 8u + (cc ^ (mr & 7u))], bu[q], dd);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][j][e] = __builtin_fmaf(dd[e], sf, acc[t][j][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint32_t col = wrow0 + 32u * t + (uint32_t)c;
+    if (col >= n) continue;
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t mr = m0 + 32u * j + 8u * (uint32_t)(e >> 2) + 4u * (uint32_t)h + (uint32_t)(e & 3);
+        if (mr < m) y[(size_t)mr * n + col] = acc[t][j][e];
+      }
+    }
+  }
+}
+
+template <int FMT, int NT, int ST, int DP, bool GROUPED>
+__global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
+  constexpr int MT = kFoldMT;
+  constexpr int TN = 4 * 32 * NT, TM = 32 * MT;
+  constexpr int SLOTS = TM * 8;  // 16-byte slots of one stage (64 k per row)
+  __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
+  __shared__ __align__(16) uint4 xst[ST][SLOTS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, c = lane & 31;
+
+  const uint32_t id = blockIdx.x, tiles = a.tiles;
+  const uint32_t xcd = id % 8u, per = tiles / 8u, extra = tiles % 8u;
+  const uint32_t tile = xcd * per + min(xcd, extra) + id / 8u;
+  FoldMember mm = a.mb[0];
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int i = 1; i < kMaxGroup; ++i) {
+      if ((uint32_t)i < a.groups && tile >= a.mb[i].tile0) mm = a.mb[i];
+    }
+  }
+  const uint32_t lt = tile - mm.tile0;
+  const uint32_t tn = lt / a.mt, tm = lt - tn * a.mt;
+  const uint32_t m0 = tm * TM;
+  const uint32_t k = a.k, nkb = k / 64u;
+  const uint32_t pitch = k >> 1;
+  constexpr uint32_t kSB = FMT == kINT4 ? 2u : 4u;
+  const uint32_t spitch = (k / (FMT == kINT4 ? 128u : 64u)) * kSB;
+  const uint32_t wrow0 = tn * TN + (uint32_t)wave * 32u * NT;
+  const uint32_t wbase = wrow0 < mm.n ? wrow0 : 0u;
+  const uint32_t wrows = wrow0 < mm.n ? min(32u * NT, mm.n - wrow0) : 0u;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(mm.packed + (size_t)wbase * pitch, wrows * pitch);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(reinterpret_cast<const char*>(mm.scales) + (size_t)wbase * spitch, wrows * spitch);
+  const uint32_t xrows = min((uint32_t)TM, a.m - m0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)m0 * k, xrows * k * 2u);
+
+  // Block kb's packed bytes (row 32 t + c, bytes [16 h, 16 h + 16) of the block) and raw scale
+  // of this lane's rows; blocks past K and rows past N read as zero.
+  uint4 W[DP][NT];
+  uint32_t S[DP][NT];
+  auto load_w = [&](uint32_t kb, uint4 (&w)[NT], uint32_t (&s)[NT]) __attribute__((always_inline)) {
+    const bool have = kb < nkb;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t row = (uint32_t)(32 * t + c);
+      w[t] = buffer_load16_stream(rw, offset_or_oob(have, row * pitch + kb * 32u + 16u * (uint32_t)h));
+      if constexpr (FMT == kINT4) {
+        s[t] = buffer_load16bit(rs, offset_or_oob(have, row * spitch + (kb >> 1) * 2u));
+      } else {
+        s[t] = buffer_load32(rs, offset_or_oob(have, row * spitch + kb * 4u));
+      }
+    }
+  };
+  // Stage of block kb into buffer b (every thread moves SLOTS / 256 slots).
+  auto load_x = [&](uint32_t kb, int b) __attribute__((always_inline)) {
+    const bool have = kb < nkb;
+#pragma unroll
+    for (int j = 0; j < SLOTS / kFoldThreads; ++j) {
+      const uint32_t sl = (uint32_t)(j * kFoldThreads + tid);
+      const uint32_t mr = sl >> 3, cc = (sl & 7u) ^ (mr & 7u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(&xst[b][j * kFoldThreads + wave * 64]), 16,
+          (int)offset_or_oob(have, (mr * k + kb * 64u + cc * 8u) * 2u), 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < ST - 1; ++i) load_x((uint32_t)i, i);
+#pragma unroll
+  for (int i = 0; i < DP; ++i) load_w((uint32_t)i, W[i], S[i]);
+  fill_table<FMT, kF16, kFoldThreads>(tab);
+
+  f32x16 acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][j][e] = 0.f;
+
+  // LDS byte address of a lookup = byte * 128 + lane copy offset: the perm builds byte * 256 +
+  // 2 * copy offset (the packed byte into byte 1), halved by the shift.
+  const uint32_t laneoff = (uint32_t)c * 8u;
+  const char* tabc = reinterpret_cast<const char*>(tab);
+  auto lookup4 = [&](uint32_t wd, uint32_t (&p)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      const uint32_t addr =
+          __builtin_amdgcn_perm(wd, laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb4) << 8)) >> 1;
+      p[kb4] = *reinterpret_cast<const uint32_t*>(tabc + addr);
+    }
+  };
+  auto afrag = [&](int b, int j, int q) __attribute__((always_inline)) {
+    const uint32_t mr = (uint32_t)(32 * j + c), cc = (uint32_t)(4 * h + q);
+    return xst[b][mr * 8u + (cc ^ (mr & 7u))];
+  };
+
+  // Block kb of the folded route: the barrier completes stage b (every wave's copies) and ends
+  // the reads of the stage the next copy overwrites; then that copy, the decode with the scale
+  // folded in, the weight refill DP blocks ahead, the matrix steps.
+  auto step = [&](uint32_t kb, int b, uint4 (&w)[NT], uint32_t (&s)[NT]) __attribute__((always_inline)) {
+    __syncthreads();
+    load_x(kb + ST - 1, (b + ST - 1) % ST);
+    uint4 bw[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const _Float16 sh = (_Float16)scale_f32<FMT>(s[t]);
+      const half2_t s2 = {sh, sh};
+      const uint32_t wd[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t p[4];
+        lookup4(wd[q], p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p[e]) * s2);
+        bw[t][q] = make_uint4(p[0], p[1], p[2], p[3]);
+      }
+    }
+    load_w(kb + DP, w, s);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        const uint4 af = afrag(b, j, q);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][j] = mfma32(af, bw[t][q], acc[t][j]);
+      }
+    }
+  };
+
+  // Every block scale of this wave's rows over the whole of K, checked once: lane (h, c) reads
+  // scales h, h + 2, ... of row 32 t + c, one load per scale (rows past N read as zero, which
+  // folds).  The loads go out after the first weights and stages, so the check adds no round trip
+  // before the first block.
+  bool fold = true;
+  {
+    const uint32_t nsc = k / (FMT == kINT4 ? 128u : 64u);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t row = (uint32_t)(32 * t + c);
+      for (uint32_t i = (uint32_t)h; i < nsc; i += 2u) {
+        const uint32_t raw = FMT == kINT4 ? buffer_load16bit(rs, row * spitch + i * 2u)
+                                          : buffer_load32(rs, row * spitch + i * 4u);
+        fold = fold && foldable<FMT>(scale_f32<FMT>(raw));
+      }
+    }
+  }
+  const bool fold_wave = __builtin_amdgcn_ballot_w64(!fold) == 0;
+
+  if (fold_wave) {
+    constexpr int UNR = DP > ST ? DP : ST;
+    static_assert(UNR % DP == 0 && UNR % ST == 0, "register sets and stages rotate together");
+    uint32_t kb = 0;
+    for (; kb + UNR <= nkb; kb += UNR) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) step(kb + u, (int)((kb + u) % ST), W[u % DP], S[u % DP]);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR - 1; ++u) {
+      if (kb + u < nkb) step(kb + u, (int)((kb + u) % ST), W[u % DP], S[u % DP]);
+    }
+  } else {
+    // every wave runs the same number of barriers on either route
+    fold_block_scale_wave<FMT, NT, ST>(rw, rs, rx, reinterpret_cast<const char*>(tab), &xst[0][0],
+                                       mm.y, mm.n, a.m, m0, wrow0, k);
+    return;
+  }
+
+  // y[m0 + 32 j + 8 (e / 4) + 4 h + e % 4][wrow0 + 32 t + c]: for each register, 32 lanes write
+  // 32 consecutive floats of one row of y.
+  const uint32_t n = mm.n;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint32_t col = wrow0 + 32u * t + (uint32_t)c;
+    if (col >= n) continue;
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t mr = m0 + 32u * j + 8u * (uint32_t)(e >> 2) + 4u * (uint32_t)h + (uint32_t)(e & 3);
+        if (mr < a.m) mm.y[(size_t)mr * n + col] = acc[t][j][e];
+      }
+    }
+  }
+}
+
+template <int FMT, int NT, bool GROUPED>
+hipError_t launch_nt(const FoldArgs& a, hipStream_t s) {
+  // Two activation stages and two blocks of weights in flight with 256-row tiles; three stages
+  // and three blocks with 128-row tiles (measured on MI355X, NF4 x fp16 at 512 activation rows).
+  constexpr int ST = NT == 2 ? 2 : 3, DP = NT == 2 ? 2 : 3;
+  hipLaunchKernelGGL((fold_kernel<FMT, NT, ST, DP, GROUPED>), dim3(a.tiles), dim3(kFoldThreads), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const FoldArgs& a, int nt, hipStream_t s) {
+  if (nt == 2) return a.groups > 1 ? launch_nt<FMT, 2, true>(a, s) : launch_nt<FMT, 2, false>(a, s);
+  return a.groups > 1 ? launch_nt<FMT, 1, true>(a, s) : launch_nt<FMT, 1, false>(a, s);
+}
+
+int64_t fold_tiles(const int64_t* ns, int groups, int64_t m, int64_t tn) {
+  int64_t t = 0;
+  for (int g = 0; g < groups; ++g) t += (ns[g] + tn - 1) / tn;
+  return t * ((m + 32 * kFoldMT - 1) / (32 * kFoldMT));
+}
+
+}  // namespace
+
+bool gemm_fold_format(int fmt) {
+  return fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16 || fmt == W4_FP4_X_F16;
+}
+
+// Weight rows per tile of the folded kernel for this launch (256 or 128), or 0 when the block-scale
+// kernel is the faster one.  Measured on MI355X (rotated weights, against the block-scale kernel's
+// automatic launch): at 512 activation rows, 256-row tiles where they number two per CU (one per
+// CU for rows of 4096+ weights): NF4 151936 x 1536 378 against 426 us (INT4 x fp16 325), 28672 x
+// 8192 359 against 402; else 128-row tiles from one per CU for rows shorter than 8192 weights and
+// two per CU for longer ones: 8960 x 1536 34 against 45 us (the two gate/up matrices of a grouped
+// launch: the same as the block-scale kernel's 64 x 128 tiles), while 8192 x 28672 with one
+// 128-row tile per CU (493 against 429) and 8192 x 8192 (129 against 130) stay with the block-scale
+// kernel.  Below 256 activation rows the folded kernel's prologue and tile count cost more than
+// its decode saves (NF4 151936 x 1536 at 128 rows: 152 against 124 us).
+int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m) {
+  if (!gemm_fold_format(fmt) || m < 256 || k < 64 || k % 64 != 0) return 0;
+  const int64_t cus = device_cu_count();
+  if (fold_tiles(ns, groups, m, 256) >= (k >= 4096 ? cus : 2 * cus)) return 256;
+  if (fold_tiles(ns, groups, m, 128) >= (k >= 8192 ? 2 * cus : cus)) return 128;
+  return 0;
+}
+
+hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
+                            const void* const* scales, const int64_t* ns, float* const* y,
+                            int64_t k, int64_t m, int tile_rows, hipStream_t s) {
+  if (!gemm_fold_format(fmt) || groups < 1 || groups > kMaxGroup || m < 1 || k < 64 || k % 64 != 0)
+    return hipErrorInvalidValue;
+  if (fmt == W4_INT4_X_F16 && k % 128 != 0) return hipErrorInvalidValue;
+  if (tile_rows != 128 && tile_rows != 256) return hipErrorInvalidValue;
+  int64_t n_total = 0;
+  for (int g = 0; g < groups; ++g) {
+    if (ns[g] < 1) return hipErrorInvalidValue;
+    n_total += ns[g];
+  }
+  // 32-bit offsets inside the buffer resources: 128 activation rows and 64 weight rows of K.
+  if (128 * k * 2 >= ((int64_t)1 << 31) || n_total >= ((int64_t)1 << 31) || m >= ((int64_t)1 << 31))
+    return hipErrorNotSupported;
+  const int64_t mt = (m + 32 * kFoldMT - 1) / (32 * kFoldMT);
+  const int64_t tiles = fold_tiles(ns, groups, m, tile_rows);
+  if (tiles >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  FoldArgs a;
+  int64_t tile0 = 0;
+  for (int g = 0; g < kMaxGroup; ++g) {
+    const bool use = g < groups;
+    a.mb[g].packed = use ? packed[g] : packed[0];
+    a.mb[g].scales = use ? scales[g] : scales[0];
+    a.mb[g].y = use ? y[g] : nullptr;
+    a.mb[g].n = use ? (uint32_t)ns[g] : 0u;
+    a.mb[g].tile0 = use ? (uint32_t)tile0 : 0xFFFFFFFFu;
+    if (use) tile0 += ((ns[g] + tile_rows - 1) / tile_rows) * mt;
+  }
+  a.x = x;
+  a.groups = (uint32_t)groups;
+  a.m = (uint32_t)m;
+  a.k = (uint32_t)k;
+  a.mt = (uint32_t)mt;
+  a.tiles = (uint32_t)tiles;
+  const int nt = tile_rows / 128;
+  switch (fmt) {
+    case W4_NF4_X_F16: return launch_fmt<kNF4>(a, nt, s);
+    case W4_INT4_X_F16: return launch_fmt<kINT4>(a, nt, s);
+    case W4_FP4_X_F16: return launch_fmt<kFP4>(a, nt, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w4

@@ -101,7 +101,7 @@ typedef enum {
   W4_PATH_TWOPASS = 4, /* ablation: dequantize W to fp16 in the workspace, then a dense GEMV/GEMM
                           (the out-of-place path of LLM Quantization on RTX 4060, "The
                           Quantization Tax: A Byte-Accounting Model")                        */
-  W4_PATH_TILED = 5    /* prefill-size GEMM: output tiles of 128 weight rows x 128 activation
+  W4_PATH_TILED = 5,   /* prefill-size GEMM: output tiles of 128 weight rows x 128 activation
                           rows, K walked one 64-weight block at a time, weights decoded on chip
                           into the matrix-core operands (LLM Quantization on RTX 4060, "Why Only
                           16%", item 3: prefill needs a GEMM, not a GEMV per token); any B.
@@ -112,7 +112,25 @@ typedef enum {
                           separate workgroups, partial sums in the workspace, then the fixed-order
                           reduction; W4_PATH_AUTO, given a workspace, splits K into the smallest
                           power of two of ranges that gives three quarters of the CUs a 64-row
-                          tile, each range at least 16 blocks, at most 16 ranges                */
+                          tile, each range at least 16 blocks, at most 16 ranges.  For fp16
+                          activations (W4_NF4_X_F16, W4_INT4_X_F16, W4_FP4_X_F16) a one-pass tiled
+                          launch with enough tiles runs the folded kernel of W4_PATH_TILED_F16
+                          instead (see there)                                                   */
+  W4_PATH_TILED_F16 = 6 /* prefill-size GEMM for fp16 activations with each block scale folded into
+                          the decoded fp16 weights (one packed multiply per weight pair), so the
+                          matrix cores accumulate x * W_hat over all of K: tiles of 256 or 128
+                          weight rows x 128 activation rows, 32x32x16 matrix steps; any B, no
+                          split (split_k <= 1), no workspace.  W4_NF4_X_F16, W4_INT4_X_F16 and
+                          W4_FP4_X_F16 only (other formats: W4_ERR_PATH).  A folded weight is
+                          within 3 * 2^-11 of W_hat (NF4; FP4 2 * 2^-11; INT4 exact); a wave whose
+                          rows hold a block scale outside the range where every folded weight is a
+                          normal, finite fp16 number (NF4 [2^-10, 2^15], FP4 [2^-13, 2^13], INT4
+                          [2^-14, 2^12], or zero) runs all of K with the scale applied in fp32 per
+                          block instead.  W4_PATH_AUTO and W4_PATH_TILED take it for those
+                          formats from 256 activation rows, with 256-row tiles when those number
+                          at least two per CU (one per CU for K >= 4096), else with 128-row
+                          tiles when those number at least one per CU (two per CU for
+                          K >= 8192)                                                             */
 } w4_path_t;
 
 #define W4_MAX_BATCH 4096
@@ -188,7 +206,7 @@ int w4_quantize_fp4(const float* w, int64_t N, int64_t K, uint8_t* packed, float
  * workspace registered for the current device; a path that cannot run the arguments returns
  * W4_ERR_PATH, a split-K or two-pass override without a large enough registered workspace returns
  * W4_ERR_WORKSPACE.  Other entry points ignore the override.  The environment variable
- * W4_FORCE_PATH (auto, gemv, splitk, mfma, twopass, tiled, or the digit 0-5) sets the same
+ * W4_FORCE_PATH (auto, gemv, splitk, mfma, twopass, tiled, tiled_f16, or the digit 0-6) sets the same
  * override once, when the library is loaded; an unknown value makes the steered calls return
  * W4_ERR_PATH until w4_set_path is called.  Process-wide, not per thread: set it before launching
  * work from other threads.  Returns W4_OK, or W4_ERR_PATH for an unknown path.  Host only; no

@@ -367,6 +367,20 @@ def test_sparse24_grouped_validation_codes():
     assert f(vp(S), 2, vals, meta, ns, 0, 256, 1, arr(6 * S, 6 * S + 64), None) == -9  # y overlap
 
 
+def test_tiled_f16_host_checks():
+    """W4_PATH_TILED_F16 runs fp16 activations with NF4, INT4 or FP4 weights and no split: other
+    formats and split_k > 1 fail with W4_ERR_PATH before any launch; it asks for no workspace."""
+    w4, L = _lib()
+    vp = ctypes.c_void_p
+    for fmt in (2, 4, 6, 7, 8):
+        assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), fmt, 64, 256, 200, vp(FAKE * 64),
+                              6, 0, None, 0, None) == -7
+    assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 200, vp(FAKE * 64), 6, 2,
+                          None, 0, None) == -7
+    for fmt in ("nf4_f16", "int4_f16", "fp4_f16"):
+        assert w4.workspace_bytes(fmt, 8960, 1536, 512, "tiled_f16") == 0
+
+
 def test_path_override_and_workspace_registration():
     """w4_set_path / w4_get_path / w4_set_workspace on the host: unknown paths are rejected, the
     override steers w4_gemv and w4_gemm_smallbatch into w4_matmul_ex's checks (a forced split-K
@@ -376,8 +390,9 @@ def test_path_override_and_workspace_registration():
     vp = ctypes.c_void_p
     try:
         assert L.w4_set_path(9) == -7
+        assert L.w4_set_path(7) == -7
         assert L.w4_set_path(-1) == -7
-        for path in range(6):
+        for path in range(7):
             assert L.w4_set_path(path) == 0
             assert L.w4_get_path() == path
         assert L.w4_set_path(2) == 0  # split-K, nothing registered on this host
@@ -387,6 +402,9 @@ def test_path_override_and_workspace_registration():
                                     vp(FAKE * 4), None) == -6
         assert L.w4_set_path(4) == 0  # two-pass, no workspace
         assert _gemv(L) == -6
+        assert L.w4_set_path(6) == 0  # the folded GEMM runs fp16 activations only
+        assert L.w4_gemm_smallbatch(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 2, 64, 256, 200,
+                                    vp(FAKE * 64), None) == -7
         assert L.w4_set_path(1) == 0  # the GEMV path has no launch shape for B = 9
         assert L.w4_gemm_smallbatch(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 9,
                                     vp(FAKE * 64), None) == -7

@@ -1,0 +1,171 @@
+"""Folded-scale prefill GEMM (W4_PATH_TILED_F16, fp16 activations) against the oracle's fp64
+reference, per element within 2e-3 T + 1e-5 (T = sum over k of |x * w_hat|), as for every other
+path; its fp32 block-scale loop for scales outside the fold range; the automatic choice inside the
+tiled path."""
+import numpy as np
+import pytest
+
+import synth_inputs
+from tests import gpu_util as g
+
+pytestmark = pytest.mark.gpu
+
+F16_FMTS = ["nf4_f16", "int4_f16", "fp4_f16"]
+
+
+def _case(fmt, n, k, b, seed, w=None):
+    if w is None:
+        w = synth_inputs.weights(n, k, seed=seed)
+    x = synth_inputs.activations(b, k, "f16", seed=seed + 17)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    g.assert_quant_equal(fmt, p, s, pr, sr)
+    return x, g.to_dev_x(x, "f16"), p, s, pr, sr
+
+
+# Tiles are 128 weight rows x 128 activation rows over 64-weight blocks of K, three blocks per
+# unrolled trip: one block (NF4, FP4), five and ten blocks (a remainder of two and one), ragged N
+# and B in both tile directions, B = 1, several tiles.
+@pytest.mark.parametrize("fmt", F16_FMTS)
+@pytest.mark.parametrize("n,k,b", [(64, 128, 128), (37, 384, 130), (300, 1536, 512), (129, 8960, 200),
+                                   (1000, 2048, 257), (96, 1024, 1), (65, 64, 33), (260, 320, 300),
+                                   (33, 640, 129)])
+def test_tiled_f16_parity(fmt, n, k, b):
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    if fmt.startswith("int4") and k % 128:
+        pytest.skip("INT4 groups are 128 weights")
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n * 7 + b)
+    y = torch.full((b, n), float("nan"), device=xd.device)
+    w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", y=y)
+    g.assert_y_close(fmt, y, x, pr, sr)
+    assert torch.equal(y, w4.matmul_ex(xd, p, s, fmt, path="tiled_f16"))
+
+
+@pytest.mark.parametrize("fmt", F16_FMTS)
+def test_tiled_f16_scale_range(fmt):
+    """Groups of 32 rows (one wave's rows) with ordinary scales, with one block per row scaled far
+    below the fold range, with whole rows scaled far above it, and with zero rows: the waves that
+    meet an unfoldable scale run all of K with the block scale applied in fp32, the others fold;
+    every row within the bound, across the 128-row tiles of one launch."""
+    import bit_weight_only_w4_amd as w4
+
+    n, k, b = 512, 1536, 160
+    grp = 128 if fmt.startswith("int4") else 64
+    w = synth_inputs.weights(n, k, seed=41).astype(np.float64)
+    rows = np.arange(n)
+    kind = (rows // 32) % 4
+    w[kind == 1, 3 * grp:4 * grp] *= 1e-7       # one block per row below the fold range
+    w[kind == 2, :] *= 1e6                       # whole rows above it
+    w[(kind == 3) & (rows % 2 == 0), :] = 0.0    # zero rows (scale 0 folds)
+    w = w.astype(np.float32)
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=42, w=w)
+    y = w4.matmul_ex(xd, p, s, fmt, path="tiled_f16")
+    g.assert_y_close(fmt, y, x, pr, sr)
+
+
+@pytest.mark.parametrize("fmt", F16_FMTS)
+@pytest.mark.parametrize("b", [128, 200])
+def test_tiled_f16_one_hot_columns(fmt, b):
+    """Activation row i = e_{c_i}: y[i] is column c_i of the decoded matrix up to the fp16
+    rounding of the folded weight: exact for INT4 ((q - 8) s with a bf16 scale fits fp16), within
+    2 * 2^-11 for FP4 (scale and product rounded), 3 * 2^-11 for NF4 (code, scale and product)."""
+    import oracle
+
+    import bit_weight_only_w4_amd as w4
+
+    n, k = 300, 1024
+    w = synth_inputs.weights(n, k, seed=78)
+    p, s = g.gpu_quantize(fmt, g.to_dev_f32(w))
+    pr, sr = g.oracle_quantize(fmt, w)
+    w_hat = oracle.dequant(g.WFMT[fmt], pr, sr)
+    cols = [(41 * i + 3) % k for i in range(b)]
+    x = np.zeros((b, k), dtype=np.uint16)
+    for i, c in enumerate(cols):
+        x[i, c] = 0x3C00
+    y = w4.matmul_ex(g.to_dev_x(x, "f16"), p, s, fmt, path="tiled_f16").cpu().numpy()
+    y = y.astype(np.float64)
+    rtol = {"nf4_f16": 3 * 2.0 ** -11 + 2.0 ** -20, "fp4_f16": 2 * 2.0 ** -11 + 2.0 ** -20,
+            "int4_f16": 0.0}[fmt]
+    for i, c in enumerate(cols):
+        assert np.allclose(y[i], w_hat[:, c], rtol=rtol, atol=0), (i, c)
+
+
+@pytest.mark.parametrize("fmt,n,k", [("nf4_f16", 33000, 320), ("fp4_f16", 33000, 320),
+                                     ("int4_f16", 33000, 640)])
+def test_tiled_f16_wide_tiles_sampled(fmt, n, k):
+    """256-row tiles (chosen from two per CU) with a remainder step (five blocks of K: two per
+    unrolled trip) and a ragged last tile: 160 sampled rows against the oracle; the explicit path,
+    the tiled path and the automatic path agree bitwise (the automatic choice is this kernel)."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    dev = g.device()
+    b = 512
+    gen = torch.Generator(device=dev).manual_seed(n + k)
+    w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+    p, s = g.gpu_quantize(fmt, w)
+    rng = np.random.default_rng(n + 3)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 158, replace=False)]))
+    w_rows = w[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    del w
+    pr, sr = g.oracle_quantize(fmt, w_rows)
+    g.assert_quant_equal(fmt, p, s, pr, sr, rows=rows)
+    x = synth_inputs.activations(b, k, "f16", seed=b + 5)
+    xd = g.to_dev_x(x, "f16")
+    y = w4.matmul_ex(xd, p, s, fmt, path="tiled_f16")
+    g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
+    assert torch.equal(y, w4.matmul_ex(xd, p, s, fmt, path="tiled"))
+    assert torch.equal(y, w4.gemm_prefill(xd, p, s, fmt))
+
+
+@pytest.mark.parametrize("fmt", F16_FMTS)
+def test_tiled_f16_grouped_members(fmt):
+    """Three members of a 512-token grouped call large enough for the folded kernel (their tiles
+    one after another in one launch): each bitwise equal to the folded kernel on that member
+    alone and within the bound on sampled rows; y pre-filled with NaN."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    dev = g.device()
+    k, b = 1536, 512
+    ns = (8960, 4100, 5000)
+    x = synth_inputs.activations(b, k, "f16", seed=301)
+    xd = g.to_dev_x(x, "f16")
+    packed, scales, checks = [], [], []
+    for i, n in enumerate(ns):
+        gen = torch.Generator(device=dev).manual_seed(700 + i)
+        w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+        p, s = g.gpu_quantize(fmt, w)
+        rng = np.random.default_rng(31 + i)
+        rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 78, replace=False)]))
+        w_rows = w[torch.as_tensor(rows, device=dev)].cpu().numpy()
+        del w
+        pr, sr = g.oracle_quantize(fmt, w_rows)
+        packed.append(p)
+        scales.append(s)
+        checks.append((rows, pr, sr))
+    ys = [torch.full((b, n), float("nan"), device=dev) for n in ns]
+    w4.gemm_smallbatch_grouped(xd, packed, scales, fmt, ys=ys)
+    for y, p, s, (rows, pr, sr) in zip(ys, packed, scales, checks):
+        assert torch.equal(y, w4.matmul_ex(xd, p, s, fmt, path="tiled_f16"))
+        g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=y.device)], x, pr, sr)
+
+
+def test_tiled_f16_rejects_other_formats():
+    """Formats with bf16 activations (and asymmetric INT4) have no folded kernel: W4_ERR_PATH, y
+    untouched."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    for fmt in ("nf4_bf16", "int4_bf16", "fp4_bf16", "int4a_f16", "int4a_bf16"):
+        x, xd, p, s, pr, sr = _case(fmt, 64, 256, 128, seed=3)
+        y = torch.full((128, 64), 7.0, device=xd.device)
+        with pytest.raises(ValueError):
+            w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", y=y)
+        assert bool((y == 7.0).all())
