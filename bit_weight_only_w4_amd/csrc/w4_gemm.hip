@@ -150,19 +150,38 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
       d.w[t][0] = v.x;
       d.w[t][1] = v.y;
     }
+    if constexpr (is_g128(FMT)) {
 #pragma unroll
-    for (int t = 0; t < WN; ++t) {
-      const uint32_t row = soff + (uint32_t)t * 16u * spitch;
-      if constexpr (!is_g128(FMT)) {
-        d.s[t] = buffer_load32(rs, offset_or_oob(have, row + kb * 4u));
-      } else if constexpr (FMT == kINT4A) {
-        d.s[t] = buffer_load32(rs, offset_or_oob(have, row + (kb >> 1) * 4u));
-      } else {
-        d.s[t] = buffer_load16bit(rs, offset_or_oob(have, row + (kb >> 1) * 2u));
+      for (int t = 0; t < WN; ++t) {
+        const uint32_t row = soff + (uint32_t)t * 16u * spitch;
+        if constexpr (FMT == kINT4A) {
+          d.s[t] = buffer_load32(rs, offset_or_oob(have, row + (kb >> 1) * 4u));
+        } else {
+          d.s[t] = buffer_load16bit(rs, offset_or_oob(have, row + (kb >> 1) * 2u));
+        }
       }
     }
   };
-
+  // NF4 and FP4: the fp32 scales of QS consecutive blocks i .. i + QS - 1 (of this K group) in one
+  // load per row tile every QS blocks (four blocks, 16 bytes; two, 8 bytes, with 128 x 128 tiles,
+  // whose registers hold no more).  A dword per block touched one cache line per row for 4 useful
+  // bytes; words past the group's blocks belong to later blocks or the next row (or read zero past
+  // the rows), and only ever meet blocks past the range, whose weights read as zero.
+  constexpr int QS = WN >= 4 ? 2 : 4;
+  auto load_sq = [&](uint32_t i, uint4 (&sq)[WN]) __attribute__((always_inline)) {
+    const bool have = i < cnt;
+#pragma unroll
+    for (int t = 0; t < WN; ++t) {
+      const uint32_t row = soff + (uint32_t)t * 16u * spitch;
+      const uint32_t off = offset_or_oob(have, row + (kbase + i) * 4u);
+      if constexpr (QS == 4) {
+        sq[t] = buffer_load16(rs, off);
+      } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0);
+        sq[t] = make_uint4(v.x, v.y, 0u, 0u);
+      }
+    }
+  };
   // x stage of the group's block i: group thread gt moves 16-byte chunks c = gt + 256 j (row
   // c / 8, chunk c % 8) into the group's own two stages.
   uint8_t* xg = xs + (uint32_t)kg * 2u * stage_bytes<WM>();
@@ -190,6 +209,8 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   // kDepth - 1), so that the waits the compiler derives for the loop entry match its back edge.
   Block<WN> D[kDepth];
   uint4 X0[WM], X1[WM];
+  uint4 SQ[2][WN];  // NF4, FP4: scale sets of QS blocks (load_sq), alternating
+  if constexpr (!is_g128(FMT)) load_sq(0, SQ[0]);
 #pragma unroll
   for (int i = 0; i < kDepth - 1; ++i) load_block((uint32_t)i, D[i]);
   load_x(0, X0);
@@ -214,7 +235,7 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   // This lane's B fragment offset inside a stage: activation row wm * 16 WM + r, bytes 32 g.
   const uint32_t xoff = ((uint32_t)wm * 16u * WM + (uint32_t)r) * kXPitch + 32u * (uint32_t)g;
 
-  auto compute = [&](int buf, const Block<WN>& d) __attribute__((always_inline)) {
+  auto compute = [&](int buf, const Block<WN>& d, const uint32_t (&sw)[WN]) __attribute__((always_inline)) {
     const uint8_t* st = xg + buf * stage_bytes<WM>() + xoff;
     uint4 bf[2][WM];
 #pragma unroll
@@ -261,7 +282,7 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
           if (FMT == kINT4A) dd[j] = mfma<XT>(zrow, bf[s][j], dd[j]);
         }
       }
-      const uint32_t sraw = !is_g128(FMT) ? d.s[t] : d.s[t] << 16;
+      const uint32_t sraw = !is_g128(FMT) ? sw[t] : d.s[t] << 16;
       const float sc[4] = {row_bcast<0>(sraw), row_bcast<1>(sraw), row_bcast<2>(sraw),
                            row_bcast<3>(sraw)};
 #pragma unroll
@@ -278,27 +299,60 @@ __global__ void __launch_bounds__(kGroupThreads * KW, 2) gemm_kernel(GemmArgs a)
   // barrier ends the reads of stage kb % 2 and makes stage kb + 1 visible.  The x loads are kept
   // ahead of the weight loads (the scheduler would otherwise mix them, and the wait before the LDS
   // store would then also wait for weights fetched later).
-  auto step = [&](uint32_t kb, Block<WN>& d, uint4 (&xn)[WM], const uint4 (&xp)[WM])
-                  __attribute__((always_inline)) {
+  auto step = [&](uint32_t kb, Block<WN>& d, uint4 (&xn)[WM], const uint4 (&xp)[WM],
+                  const uint32_t (&sw)[WN]) __attribute__((always_inline)) {
     load_x(kb + 2, xn);
     __builtin_amdgcn_sched_barrier(0);
-    compute((int)(kb & 1u), d);
+    compute((int)(kb & 1u), d, sw);
     store_x((int)((kb + 1) & 1u), xp);
     __builtin_amdgcn_sched_barrier(0);
     load_block(kb + kDepth, d);
     __syncthreads();
   };
+  // Block kb = kb0 + u of a trip (kb0 a multiple of its length): register set u % 4, activation
+  // stage parity u % 2, scale set (u / QS) % 2, whose successor is requested at u % QS == 0.
+  auto unit = [&](uint32_t kb0, int u) __attribute__((always_inline)) {
+    const uint32_t kb = kb0 + (uint32_t)u;
+    uint32_t sw[WN] = {};
+    if constexpr (!is_g128(FMT)) {
+      uint4 (&sq)[WN] = SQ[(u / QS) & 1];
+      if (u % QS == 0) load_sq(kb + QS, SQ[(u / QS + 1) & 1]);
+      const int e = u % QS;
+#pragma unroll
+      for (int t = 0; t < WN; ++t)
+        sw[t] = e == 0 ? sq[t].x : e == 1 ? sq[t].y : e == 2 ? sq[t].z : sq[t].w;
+    }
+    if (u & 1) {
+      step(kb, D[u & 3], X1, X0, sw);
+    } else {
+      step(kb, D[u & 3], X0, X1, sw);
+    }
+  };
 
   uint32_t kb = 0;
-  for (; kb + 4 <= steps; kb += 4) {
-    step(kb, D[0], X0, X1);
-    step(kb + 1, D[1], X1, X0);
-    step(kb + 2, D[2], X0, X1);
-    step(kb + 3, D[3], X1, X0);
+  if constexpr (is_g128(FMT)) {
+    // Four blocks per trip, the register sets rotating (the scales travel with the weights).
+    const uint32_t sw0[WN] = {};
+    for (; kb + 4 <= steps; kb += 4) {
+      step(kb, D[0], X0, X1, sw0);
+      step(kb + 1, D[1], X1, X0, sw0);
+      step(kb + 2, D[2], X0, X1, sw0);
+      step(kb + 3, D[3], X1, X0, sw0);
+    }
+    if (kb < steps) step(kb, D[0], X0, X1, sw0);
+    if (kb + 1 < steps) step(kb + 1, D[1], X1, X0, sw0);
+    if (kb + 2 < steps) step(kb + 2, D[2], X0, X1, sw0);
+  } else {
+    // Eight blocks per trip: the scale sets alternate as well.
+    for (; kb + 8 <= steps; kb += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) unit(kb, u);
+    }
+#pragma unroll
+    for (int u = 0; u < 7; ++u) {
+      if (kb + u < steps) unit(kb, u);
+    }
   }
-  if (kb < steps) step(kb, D[0], X0, X1);
-  if (kb + 1 < steps) step(kb + 1, D[1], X1, X0);
-  if (kb + 2 < steps) step(kb + 2, D[2], X0, X1);
 
   // K groups 1 .. KW - 1 hand their sums to group 0 through LDS (the x stages are free after the
   // last barrier), which adds them in the fixed order kg = 1, 2, ...: bitwise reproducible.

@@ -220,20 +220,34 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   const uint32_t xrows = min((uint32_t)TM, a.m - m0);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)m0 * k, xrows * k * 2u);
 
-  // Block kb's packed bytes (row 32 t + c, bytes [16 h, 16 h + 16) of the block) and raw scale
-  // of this lane's rows; blocks past K and rows past N read as zero.
+  // Block kb's packed bytes for this lane: row 32 t + c, bytes [16 h, 16 h + 16) of the block;
+  // blocks past K and rows past N read as zero.
   uint4 W[DP][NT];
-  uint32_t S[DP][NT];
-  auto load_w = [&](uint32_t kb, uint4 (&w)[NT], uint32_t (&s)[NT]) __attribute__((always_inline)) {
+  auto load_w = [&](uint32_t kb, uint4 (&w)[NT]) __attribute__((always_inline)) {
     const bool have = kb < nkb;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const uint32_t row = (uint32_t)(32 * t + c);
       w[t] = buffer_load16_stream(rw, offset_or_oob(have, row * pitch + kb * 32u + 16u * (uint32_t)h));
+    }
+  };
+  // The scales of blocks 4 q .. 4 q + 3 of this lane's rows in one load per row: four fp32 words
+  // (NF4, FP4; 16 bytes at a 4-byte aligned offset) or two bf16 group scales (INT4).
+  // One load per row per four blocks instead of one per block (two for INT4): each such load
+  // touches one cache line per row, whatever its width.  Words past the row's scales read the next row's (or zero
+  // past the wave's rows), which only ever meets blocks past K, whose weights are zero.
+  uint4 SQ[2][NT];
+  auto load_sq = [&](uint32_t q, uint4 (&sq)[NT]) __attribute__((always_inline)) {
+    const bool have = 4u * q < nkb;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t row = (uint32_t)(32 * t + c);
       if constexpr (FMT == kINT4) {
-        s[t] = buffer_load16bit(rs, offset_or_oob(have, row * spitch + (kb >> 1) * 2u));
+        const uint32_t off = offset_or_oob(have, row * spitch + q * 4u);  // 2-byte aligned
+        const uint32_t g0 = buffer_load16bit(rs, off) << 16, g1 = buffer_load16bit(rs, off + 2u) << 16;
+        sq[t] = make_uint4(g0, g0, g1, g1);
       } else {
-        s[t] = buffer_load32(rs, offset_or_oob(have, row * spitch + kb * 4u));
+        sq[t] = buffer_load16(rs, offset_or_oob(have, row * spitch + q * 16u));
       }
     }
   };
@@ -252,8 +266,9 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
 
 #pragma unroll
   for (int i = 0; i < ST - 1; ++i) load_x((uint32_t)i, i);
+  load_sq(0, SQ[0]);
 #pragma unroll
-  for (int i = 0; i < DP; ++i) load_w((uint32_t)i, W[i], S[i]);
+  for (int i = 0; i < DP; ++i) load_w((uint32_t)i, W[i]);
   fill_table<FMT, kF16, kFoldThreads>(tab);
 
   f32x16 acc[NT][MT];
@@ -284,13 +299,13 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   // Block kb of the folded route: the barrier completes stage b (every wave's copies) and ends
   // the reads of the stage the next copy overwrites; then that copy, the decode with the scale
   // folded in, the weight refill DP blocks ahead, the matrix steps.
-  auto step = [&](uint32_t kb, int b, uint4 (&w)[NT], uint32_t (&s)[NT]) __attribute__((always_inline)) {
+  auto step = [&](uint32_t kb, int b, uint4 (&w)[NT], const uint32_t (&s)[NT]) __attribute__((always_inline)) {
     __syncthreads();
     load_x(kb + ST - 1, (b + ST - 1) % ST);
     uint4 bw[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const _Float16 sh = (_Float16)scale_f32<FMT>(s[t]);
+      const _Float16 sh = (_Float16)__uint_as_float(s[t]);
       const half2_t s2 = {sh, sh};
       const uint32_t wd[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
 #pragma unroll
@@ -303,7 +318,7 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
         bw[t][q] = make_uint4(p[0], p[1], p[2], p[3]);
       }
     }
-    load_w(kb + DP, w, s);
+    load_w(kb + DP, w);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -335,16 +350,27 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   const bool fold_wave = __builtin_amdgcn_ballot_w64(!fold) == 0;
 
   if (fold_wave) {
-    constexpr int UNR = DP > ST ? DP : ST;
+    // Eight blocks per trip: two scale quads alternate, and stages and weight sets rotate with it.
+    constexpr int UNR = 8;
     static_assert(UNR % DP == 0 && UNR % ST == 0, "register sets and stages rotate together");
+    auto unit = [&](uint32_t kb0, int u) __attribute__((always_inline)) {
+      const uint32_t kb = kb0 + (uint32_t)u;
+      uint4 (&sq)[NT] = SQ[(u >> 2) & 1];
+      if ((u & 3) == 0) load_sq(kb / 4u + 1u, SQ[((u >> 2) + 1) & 1]);
+      uint32_t sw[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        sw[t] = (u & 3) == 0 ? sq[t].x : (u & 3) == 1 ? sq[t].y : (u & 3) == 2 ? sq[t].z : sq[t].w;
+      step(kb, u % ST, W[u % DP], sw);  // kb0 is a multiple of UNR, hence of ST
+    };
     uint32_t kb = 0;
     for (; kb + UNR <= nkb; kb += UNR) {
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) step(kb + u, (int)((kb + u) % ST), W[u % DP], S[u % DP]);
+      for (int u = 0; u < UNR; ++u) unit(kb, u);
     }
 #pragma unroll
     for (int u = 0; u < UNR - 1; ++u) {
-      if (kb + u < nkb) step(kb + u, (int)((kb + u) % ST), W[u % DP], S[u % DP]);
+      if (kb + u < nkb) unit(kb, u);
     }
   } else {
     // every wave runs the same number of barriers on either route
@@ -373,9 +399,9 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
 
 template <int FMT, int NT, bool GROUPED>
 hipError_t launch_nt(const FoldArgs& a, hipStream_t s) {
-  // Two activation stages and two blocks of weights in flight with 256-row tiles; three stages
-  // and three blocks with 128-row tiles (measured on MI355X, NF4 x fp16 at 512 activation rows).
-  constexpr int ST = NT == 2 ? 2 : 3, DP = NT == 2 ? 2 : 3;
+  // Two activation stages and four blocks of weights in flight (eight blocks per unrolled trip,
+  // two quads of scales): measured on MI355X against three stages and three blocks.
+  constexpr int ST = 2, DP = 4;
   hipLaunchKernelGGL((fold_kernel<FMT, NT, ST, DP, GROUPED>), dim3(a.tiles), dim3(kFoldThreads), 0,
                      s, a);
   return hipGetLastError();
@@ -402,18 +428,18 @@ bool gemm_fold_format(int fmt) {
 // Weight rows per tile of the folded kernel for this launch (256 or 128), or 0 when the block-scale
 // kernel is the faster one.  Measured on MI355X (rotated weights, against the block-scale kernel's
 // automatic launch): at 512 activation rows, 256-row tiles where they number two per CU (one per
-// CU for rows of 4096+ weights): NF4 151936 x 1536 378 against 426 us (INT4 x fp16 325), 28672 x
-// 8192 359 against 402; else 128-row tiles from one per CU for rows shorter than 8192 weights and
-// two per CU for longer ones: 8960 x 1536 34 against 45 us (the two gate/up matrices of a grouped
-// launch: the same as the block-scale kernel's 64 x 128 tiles), while 8192 x 28672 with one
-// 128-row tile per CU (493 against 429) and 8192 x 8192 (129 against 130) stay with the block-scale
-// kernel.  Below 256 activation rows the folded kernel's prologue and tile count cost more than
-// its decode saves (NF4 151936 x 1536 at 128 rows: 152 against 124 us).
+// CU for rows of 4096+ weights): NF4 151936 x 1536 330 against 426 us (INT4 x fp16 303), 28672 x
+// 8192 289 against 402; else 128-row tiles from one per CU for rows shorter than 16384 weights
+// and two per CU for longer ones: 8960 x 1536 34 against 45 us, 8192 x 8192 117 against 129 (the
+// two gate/up matrices of a grouped launch: the same as the block-scale kernel's 64 x 128 tiles),
+// while 8192 x 28672 with one 128-row tile per CU (448 against 424) stays with the block-scale
+// kernel.  Below 256 activation rows the two kernels tie (151936 x 1536 at 128 rows: 123.5
+// against 124 us) and the block-scale one keeps them.
 int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m) {
   if (!gemm_fold_format(fmt) || m < 256 || k < 64 || k % 64 != 0) return 0;
   const int64_t cus = device_cu_count();
   if (fold_tiles(ns, groups, m, 256) >= (k >= 4096 ? cus : 2 * cus)) return 256;
-  if (fold_tiles(ns, groups, m, 128) >= (k >= 8192 ? 2 * cus : cus)) return 128;
+  if (fold_tiles(ns, groups, m, 128) >= (k >= 16384 ? 2 * cus : cus)) return 128;
   return 0;
 }
 

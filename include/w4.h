@@ -130,7 +130,7 @@ typedef enum {
                           formats from 256 activation rows, with 256-row tiles when those number
                           at least two per CU (one per CU for K >= 4096), else with 128-row
                           tiles when those number at least one per CU (two per CU for
-                          K >= 8192)                                                             */
+                          K >= 16384)                                                            */
 } w4_path_t;
 
 #define W4_MAX_BATCH 4096
