@@ -23,9 +23,10 @@ def _case(fmt, n, k, b, seed, w=None):
     return x, g.to_dev_x(x, "f16"), p, s, pr, sr
 
 
-# Tiles are 128 weight rows x 128 activation rows over 64-weight blocks of K, three blocks per
-# unrolled trip: one block (NF4, FP4), five and ten blocks (a remainder of two and one), ragged N
-# and B in both tile directions, B = 1, several tiles.
+# Tiles are 128 weight rows x 128 activation rows over 64-weight blocks of K, eight blocks (two
+# quads of scales) per unrolled trip: one block (NF4, FP4), five (no whole trip), six and ten (a
+# remainder of two), 24 and 140 (three and four trips), ragged N and B in both tile directions,
+# B = 1, several tiles.
 @pytest.mark.parametrize("fmt", F16_FMTS)
 @pytest.mark.parametrize("n,k,b", [(64, 128, 128), (37, 384, 130), (300, 1536, 512), (129, 8960, 200),
                                    (1000, 2048, 257), (96, 1024, 1), (65, 64, 33), (260, 320, 300),
@@ -96,8 +97,8 @@ def test_tiled_f16_one_hot_columns(fmt, b):
 @pytest.mark.parametrize("fmt,n,k", [("nf4_f16", 33000, 320), ("fp4_f16", 33000, 320),
                                      ("int4_f16", 33000, 640)])
 def test_tiled_f16_wide_tiles_sampled(fmt, n, k):
-    """256-row tiles (chosen from two per CU) with a remainder step (five blocks of K: two per
-    unrolled trip) and a ragged last tile: 160 sampled rows against the oracle; the explicit path,
+    """256-row tiles (chosen from two per CU) with K shorter than one unrolled trip (five blocks of
+    64; INT4 ten) and a ragged last tile: 160 sampled rows against the oracle; the explicit path,
     the tiled path and the automatic path agree bitwise (the automatic choice is this kernel)."""
     import torch
 
@@ -169,3 +170,25 @@ def test_tiled_f16_rejects_other_formats():
         with pytest.raises(ValueError):
             w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", y=y)
         assert bool((y == 7.0).all())
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_tiled_f16_random_shapes(seed):
+    """Seeded random shapes on the folded kernel, forced: format, N (1..3000), K (a multiple of the
+    format's group up to 4096) and B (1..700) drawn from the seed; y pre-filled with NaN; every
+    element against the oracle; 128-row tiles (the forced path's choice below the automatic
+    thresholds)."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    rng = np.random.default_rng(5000 + seed)
+    fmt = F16_FMTS[int(rng.integers(len(F16_FMTS)))]
+    grp = 128 if fmt.startswith("int4") else 64
+    k = grp * int(rng.integers(1, 4096 // grp + 1))
+    b = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 257)), int(rng.integers(257, 701))]))
+    n = int(rng.integers(1, 3001))
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=seed * 11 + 1)
+    y = torch.full((b, n), float("nan"), device=xd.device)
+    w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", y=y)
+    g.assert_y_close(fmt, y, x, pr, sr)
