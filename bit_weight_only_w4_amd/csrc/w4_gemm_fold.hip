@@ -96,11 +96,12 @@ __device__ inline float scale_f32(uint32_t raw) {
 // stages are filled by every wave of the workgroup) but loads each block's weights when it needs
 // them.  Kept out of line, with accumulators of its own: the folded loop's registers are then
 // allocated as if this route did not exist (inlined, it cost the folded route 8-30%).
-template <int FMT, int NT, int ST>
+template <int FMT, int NT>
 __device__ __attribute__((noinline)) void fold_block_scale_wave(
     __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rx,
-    const char* tabc, uint4* xst0, float* y, uint32_t n, uint32_t m, uint32_t m0, uint32_t wrow0,
-    uint32_t k) {
+    const char* tabc, uint4* xs0, uint4* xs1, float* y, uint32_t n, uint32_t m, uint32_t m0,
+    uint32_t wrow0, uint32_t k) {
+  constexpr int ST = 2;
   constexpr int MT = kFoldMT;
   constexpr int SLOTS = 32 * MT * 8;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -119,6 +120,8 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
       for (int e = 0; e < 16; ++e) acc[t][j][e] = 0.f;
   for (uint32_t kb = 0; kb < nkb; ++kb) {
     const uint32_t b = kb % (uint32_t)ST;
+    uint4* const xst = b ? xs1 : xs0;
+    wait_own_stage_copies(xst + tid);
     __syncthreads();
     {
       const uint32_t kn = kb + ST - 1, bn = (b + ST - 1) % ST;
@@ -128,7 +131,7 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
         const uint32_t sl = (uint32_t)(j * kFoldThreads + tid);
         const uint32_t mr = sl >> 3, cc = (sl & 7u) ^ (mr & 7u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (__attribute__((address_space(3))) void*)(xst0 + bn * SLOTS + j * kFoldThreads + wave * 64),
+            rx, (__attribute__((address_space(3))) void*)((bn ? xs1 : xs0) + j * kFoldThreads + wave * 64),
             16, (int)offset_or_oob(have, (mr * k + kn * 64u + cc * 8u) * 2u), 0, 0, 0);
       }
     }
@@ -160,7 +163,7 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t mr = (uint32_t)(32 * j + c), cc = (uint32_t)(4 * h + q);
-          dd = mfma32(xst0[b * SLOTS + mr * 8u + (cc ^ (mr & 7u))], bu[q], dd);
+          dd = mfma32(xst[mr * 8u + (cc ^ (mr & 7u))], bu[q], dd);
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[t][j][e] = __builtin_fmaf(dd[e], sf, acc[t][j][e]);
@@ -188,7 +191,14 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   constexpr int TN = 4 * 32 * NT, TM = 32 * MT;
   constexpr int SLOTS = TM * 8;  // 16-byte slots of one stage (64 k per row)
   __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
-  __shared__ __align__(16) uint4 xst[ST][SLOTS];
+  // The two stages are separate LDS objects and every access names one of them statically: the
+  // compiler then tells a stage's reads from the copies into the other stage (and from the table)
+  // and waits only for the copies a read depends on.  As one array indexed by stage, every LDS read
+  // (table lookups included) waited for all copies in flight, the next stage's too: one round trip
+  // per block.
+  static_assert(ST == 2, "two stages, each its own LDS object");
+  __shared__ __align__(16) uint4 xs0[SLOTS];
+  __shared__ __align__(16) uint4 xs1[SLOTS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -259,7 +269,7 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
       const uint32_t sl = (uint32_t)(j * kFoldThreads + tid);
       const uint32_t mr = sl >> 3, cc = (sl & 7u) ^ (mr & 7u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void*)(&xst[b][j * kFoldThreads + wave * 64]), 16,
+          rx, (__attribute__((address_space(3))) void*)((b ? xs1 : xs0) + j * kFoldThreads + wave * 64), 16,
           (int)offset_or_oob(have, (mr * k + kb * 64u + cc * 8u) * 2u), 0, 0, 0);
     }
   };
@@ -293,13 +303,14 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   };
   auto afrag = [&](int b, int j, int q) __attribute__((always_inline)) {
     const uint32_t mr = (uint32_t)(32 * j + c), cc = (uint32_t)(4 * h + q);
-    return xst[b][mr * 8u + (cc ^ (mr & 7u))];
+    return (b ? xs1 : xs0)[mr * 8u + (cc ^ (mr & 7u))];
   };
 
   // Block kb of the folded route: the barrier completes stage b (every wave's copies) and ends
   // the reads of the stage the next copy overwrites; then that copy, the decode with the scale
   // folded in, the weight refill DP blocks ahead, the matrix steps.
   auto step = [&](uint32_t kb, int b, uint4 (&w)[NT], const uint32_t (&s)[NT]) __attribute__((always_inline)) {
+    wait_own_stage_copies((b ? xs1 : xs0) + tid);
     __syncthreads();
     load_x(kb + ST - 1, (b + ST - 1) % ST);
     uint4 bw[NT][4];
@@ -374,8 +385,8 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
     }
   } else {
     // every wave runs the same number of barriers on either route
-    fold_block_scale_wave<FMT, NT, ST>(rw, rs, rx, reinterpret_cast<const char*>(tab), &xst[0][0],
-                                       mm.y, mm.n, a.m, m0, wrow0, k);
+    fold_block_scale_wave<FMT, NT>(rw, rs, rx, reinterpret_cast<const char*>(tab), xs0, xs1, mm.y,
+                                   mm.n, a.m, m0, wrow0, k);
     return;
   }
 

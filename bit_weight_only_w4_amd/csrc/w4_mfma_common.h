@@ -100,5 +100,27 @@ __device__ inline float row_bcast(uint32_t v) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + I, 0xF, 0xF, true));
 }
 
+// Stages in LDS filled by buffer loads with the LDS destination: each wave's copies are counted
+// by that wave's vmcnt, and a barrier does not wait for them, so before the barrier after which
+// other waves read the stage, every wave waits for its own copies.
+//
+// wait_own_stage_copies reads one slot of the stage that this thread's copies filled.  The
+// compiler makes an LDS read wait for the latest copy into the LDS object that holds it (all
+// copies, if it cannot tell objects apart), and copies complete in issue order, so after the read
+// every copy this wave issued into that object has landed.  The stage must be an LDS object of its
+// own: waits are then only as long as this stage needs (the loads issued after its copies stay in
+// flight).
+__device__ inline void wait_own_stage_copies(const uint4* own_slot) {
+  const uint4 v = *own_slot;
+  asm volatile("" ::"v"(v.x));
+}
+
+// s_waitcnt vmcnt(0), the other counters left alone: for a stage whose copies are this wave's
+// latest loads, where nothing is gained by naming the stage.
+__device__ inline void wait_all_vector_loads() {
+  // gfx9 encoding: vmcnt in bits 3:0 and 15:14 (0), expcnt 6:4 (7 = no wait), lgkmcnt 11:8 (15).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 }  // namespace
 }  // namespace w4

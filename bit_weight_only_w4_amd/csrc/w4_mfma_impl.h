@@ -447,6 +447,9 @@ __global__ void __launch_bounds__(kThreads, min_waves(T)) mfma_kernel(MfmaArgs a
     if (nphase > 1 && (cq > 0 || ct > 0) && cq % a.qpp == 0) {
       __syncthreads();  // every wave is done with the old window
       load_x((uint32_t)cq / a.qpp);
+      // The window's copies are this wave's last loads: wait for all of them, since the barrier
+      // does not wait for the copies of other waves.
+      wait_all_vector_loads();
       __syncthreads();
     }
     compute(cq, nphase > 1 ? cq % (int)a.qpp : cq, d);
