@@ -3,9 +3,10 @@
 Test infrastructure only (see the package docstring).
 
 Source: LLM Quantization on RTX 4060: Where 4-bit Decode Falls Behind FP16, section "Kernel
-Implementation": each output row is the sum over the input of decoded weight times activation,
-accumulated in FP32 because FP16 accumulation over 1536 steps is not accurate enough; the fused
-kernel does not change the arithmetic, only where dequantization happens.  So the reference is
+Implementation": an output row is the dot product of the decoded weight row with the activation
+row, and the kernel there keeps its running sums in fp32, since a dot product 1536 terms long loses
+too much in a 16-bit accumulator; fusing the dequantization into the product moves where the
+decode happens, not what is summed.  So the reference is
 the plain definition y[b, n] = sum_k x[b, k] * W_hat[n, k], taken here in fp64 on the exact
 decoded weights and the exact activation values.
 
