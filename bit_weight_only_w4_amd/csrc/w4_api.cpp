@@ -235,7 +235,8 @@ int auto_mfma_splits(int64_t n, int64_t k, int64_t b) {
 }
 
 // Split count of the automatic tiled GEMM (used when the caller's workspace holds the partial
-// sums): the smallest power of two S for which ceil(N / 64) * ceil(B / 128) * S, the workgroups
+// sums).  NF4, INT4 and FP4 with fp16 activations from 256 rows run the folded-scale kernel, whose
+// own rule gives S (gemm_fold_auto_splits).  Otherwise the smallest power of two S for which ceil(N / 64) * ceil(B / 128) * S, the workgroups
 // of 64-row tiles over all K ranges, reaches three quarters of the CUs, with at least 16 blocks
 // of 64 weights per range and at most 16 ranges.  Measured on MI355X (NF4 x fp16, rotated weights,
 // S = 1..16 at B = 128, 256, 512): the rule's S is the best or within 10% of it on 1536 x 8960
@@ -244,7 +245,9 @@ int auto_mfma_splits(int64_t n, int64_t k, int64_t b) {
 // weights and matrices with enough tiles stay whole (8960 x 1536 at B = 128: 17.6 us unsplit,
 // 28.7 split in two; 151936 x 1536 slower with every split).  It gives up to 10% on 8192 x 28672
 // at B = 512 (444 us against 400 at S = 2).
-int auto_tiled_splits(int64_t n, int64_t k, int64_t b) {
+int auto_tiled_splits(int fmt, int64_t n, int64_t k, int64_t b) {
+  const int fold = gemm_fold_auto_splits(fmt, n, k, b);  // fp16 activations: the folded kernel's
+  if (fold > 0) return fold;
   const int64_t tiles = ((n + 63) / 64) * ((b + 127) / 128);
   const int64_t nb = k / 64;
   const int64_t want = (3 * (int64_t)device_cu_count() + 3) / 4;
@@ -354,15 +357,16 @@ int run_mfma(const void* x, const uint8_t* packed, const void* scales, int fmt, 
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
-// The folded-scale GEMM on one matrix: the automatic tile rows, or 128-row tiles where the
-// automatic choice would take the block-scale kernel.
+// The folded-scale GEMM on one matrix: unsplit, the automatic tile rows, or 128-row tiles where
+// the automatic choice would take the block-scale kernel; over K ranges, 128-row tiles.
 int run_tiled_f16(const void* x, const uint8_t* packed, const void* scales, int fmt, int64_t n,
-                  int64_t k, int64_t b, float* y, hipStream_t st) {
+                  int64_t k, int64_t b, float* y, hipStream_t st, int splits = 1, void* ws = nullptr) {
   if (!gemm_fold_format(fmt)) return W4_ERR_PATH;
-  int rows = gemm_fold_tile_rows(fmt, &n, 1, k, b);
+  int rows = splits > 1 ? 0 : gemm_fold_tile_rows(fmt, &n, 1, k, b);
   if (rows == 0) rows = 128;
   const hipError_t e = launch_gemm_fold(fmt, reinterpret_cast<const uint16_t*>(x), 1, &packed,
-                                        &scales, &n, &y, k, b, rows, st);
+                                        &scales, &n, &y, k, b, rows, st, splits,
+                                        reinterpret_cast<float*>(ws));
   if (e == hipErrorNotSupported) return W4_ERR_PATH;
   return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
@@ -404,9 +408,10 @@ bool prefer_tiled(int64_t n, int64_t b) { return b >= W4_TILED_FROM_BATCH && n >
 // and the workspace holds the partial sums (1536 x 8960 at 512 / 256 / 128 activation rows: 45.5 /
 // 27.0 / 21.0 us against the MFMA path's 56.9 / 47.2 / 24.5; 1024 x 8192: 25.9 / 18.9 / 18.7
 // against 51.3 / 23.2 / 22.3), else the MFMA path.
-bool prefer_tiled_split(int64_t n, int64_t k, int64_t b, size_t workspace_bytes, int* splits) {
+bool prefer_tiled_split(int fmt, int64_t n, int64_t k, int64_t b, size_t workspace_bytes,
+                        int* splits) {
   if (b < W4_TILED_FROM_BATCH || b * n >= ((int64_t)1 << 32)) return false;
-  const int s = auto_tiled_splits(n, k, b);
+  const int s = auto_tiled_splits(fmt, n, k, b);
   const int ranges = s > 1 ? gemm_splits_used(k, s) : 1;
   if (ranges > 1 && workspace_bytes >= splitk_bytes(n, b, ranges)) {
     *splits = s;
@@ -611,6 +616,12 @@ size_t w4_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t b, int path, in
       const int ranges = split_k > 1 && split_k <= W4_MAX_SPLIT_K ? gemm_splits_used(k, split_k) : 1;
       return ranges > 1 ? splitk_bytes(n, b, ranges) : 0;
     }
+    case W4_PATH_TILED_F16: {
+      if (!gemm_fold_format(fmt)) return 0;
+      const int ranges =
+          split_k > 1 && split_k <= W4_MAX_SPLIT_K ? gemm_fold_ranges(fmt, k, split_k, nullptr) : 1;
+      return ranges > 1 ? splitk_bytes(n, b, ranges) : 0;
+    }
     case W4_PATH_TWOPASS: return (size_t)n * (size_t)k * 2;
     case W4_PATH_AUTO: {
       int sk = 1;
@@ -673,8 +684,8 @@ int w4_auto_path(int fmt, int64_t n, int64_t k, int64_t b, size_t workspace_byte
   if (prefer_tiled(n, b)) {
     path = W4_PATH_TILED;
     int st = 1;
-    if (prefer_tiled_split(n, k, b, workspace_bytes, &st)) s = st;
-  } else if (prefer_tiled_split(n, k, b, workspace_bytes, &s)) {
+    if (prefer_tiled_split(fmt, n, k, b, workspace_bytes, &st)) s = st;
+  } else if (prefer_tiled_split(fmt, n, k, b, workspace_bytes, &s)) {
     path = W4_PATH_TILED;
   } else if (prefer_mfma(n, k, b) || !plan_gemv(n, k, (int)b, 1, &p)) {
     path = W4_PATH_MFMA;
@@ -740,9 +751,16 @@ int w4_matmul_ex(const void* x, const uint8_t* packed, const void* scales, int f
         return W4_ERR_ALIAS;
       return run_tiled(x, packed, scales, fmt, n, k, b, y, s, ranges, workspace);
     }
-    case W4_PATH_TILED_F16:
-      if (split_k > 1) return W4_ERR_PATH;
-      return run_tiled_f16(x, packed, scales, fmt, n, k, b, y, s);
+    case W4_PATH_TILED_F16: {
+      if (!gemm_fold_format(fmt) || split_k > W4_MAX_SPLIT_K) return W4_ERR_PATH;
+      const int ranges = split_k > 1 ? gemm_fold_ranges(fmt, k, split_k, nullptr) : 1;
+      if (ranges <= 1) return run_tiled_f16(x, packed, scales, fmt, n, k, b, y, s);
+      const size_t used = splitk_bytes(n, b, ranges);
+      if (!workspace || workspace_bytes < used) return W4_ERR_WORKSPACE;
+      if (workspace_overlaps_inputs(workspace, used, x, packed, scales, fmt, n, k, b))
+        return W4_ERR_ALIAS;
+      return run_tiled_f16(x, packed, scales, fmt, n, k, b, y, s, split_k, workspace);
+    }
     case W4_PATH_TWOPASS: {
       const size_t used = (size_t)n * (size_t)k * 2;
       if (!workspace || workspace_bytes < used) return W4_ERR_WORKSPACE;

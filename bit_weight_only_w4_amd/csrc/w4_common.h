@@ -207,13 +207,21 @@ hipError_t launch_gemm_members(int fmt, const uint16_t* x, int groups, const uin
                                int64_t k, int64_t m, hipStream_t s, int splits = 1,
                                float* ws = nullptr);
 // Folded-scale GEMM for fp16 activations (w4_gemm_fold.hip): whether a format can run it, the
-// weight rows per tile the automatic choice gives a launch (0: the block-scale kernel is faster),
-// and one launch over `groups` members that share x and K with tiles of `tile_rows` (128 or 256).
+// weight rows per tile the automatic choice gives an unsplit launch (0: the block-scale kernel is
+// faster), the K ranges (and blocks per range) that `splits` give it, the automatic split count
+// of the tiled path on one matrix (0: not this kernel), whether split tiled launches take it, and
+// one launch over `groups`
+// members that share x and K with tiles of `tile_rows` (128 or 256); with more than one K range
+// (one member only) the partial sums go to ws ([ranges, M, N] floats) and are added into y.
 bool gemm_fold_format(int fmt);
 int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m);
+int gemm_fold_ranges(int fmt, int64_t k, int splits, int64_t* bps);
+int gemm_fold_auto_splits(int fmt, int64_t n, int64_t k, int64_t m);
+bool gemm_fold_split(int fmt, int groups, int64_t m);
 hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
                             const void* const* scales, const int64_t* ns, float* const* y,
-                            int64_t k, int64_t m, int tile_rows, hipStream_t s);
+                            int64_t k, int64_t m, int tile_rows, hipStream_t s, int splits = 1,
+                            float* ws = nullptr);
 hipError_t launch_gptq_block(float* w, int64_t ldw, const float* u, int64_t ldu, const float* scale,
                              const float* zero, int64_t lds, int group, int i1, int qmin, int qmax,
                              int64_t rows, int bc, float* q_hat, int64_t ldq, uint8_t* codes,

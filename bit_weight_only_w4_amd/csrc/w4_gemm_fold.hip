@@ -41,6 +41,10 @@
 //   * Tiles are numbered so that the workgroups one XCD receives (every eighth) take consecutive
 //     tiles, the activation-row tiles of a weight tile first: the weight tile then comes from that
 //     XCD's L2 after its first read.
+//   * K may be split into ranges of whole blocks (grid.y; an even number of blocks for INT4, so a
+//     range starts on a group): a workgroup addresses the weights, scales and activations from its
+//     range's first block on, with the matrix's row pitches, and writes fp32 partial sums to its
+//     range's plane; a second kernel adds the planes in range order (fixed-order, reproducible).
 #include <algorithm>
 
 #include "w4_mfma_common.h"
@@ -62,6 +66,9 @@ struct FoldArgs {
   uint32_t m, k;
   uint32_t mt;     // activation-row tiles (128 rows each)
   uint32_t tiles;  // tiles of all members
+  uint32_t bps;    // 64-weight blocks per K range: range z = blockIdx.y owns blocks
+                   // [z bps, min((z + 1) bps, K / 64)) and writes y + z * ysplit
+  uint32_t ysplit; // floats between the partial planes of consecutive ranges (M * N; one member)
 };
 
 namespace {
@@ -100,14 +107,14 @@ template <int FMT, int NT>
 __device__ __attribute__((noinline)) void fold_block_scale_wave(
     __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rx,
     const char* tabc, uint4* xs0, uint4* xs1, float* y, uint32_t n, uint32_t m, uint32_t m0,
-    uint32_t wrow0, uint32_t k) {
+    uint32_t wrow0, uint32_t k, uint32_t nkb) {
   constexpr int ST = 2;
   constexpr int MT = kFoldMT;
   constexpr int SLOTS = 32 * MT * 8;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c = lane & 31;
-  const uint32_t nkb = k / 64u, pitch = k >> 1;
+  const uint32_t pitch = k >> 1;  // k: the row pitch; nkb: the blocks of this K range
   constexpr uint32_t kSB = FMT == kINT4 ? 2u : 4u;
   const uint32_t spitch = (k / (FMT == kINT4 ? 128u : 64u)) * kSB;
   const uint32_t laneoff = (uint32_t)c * 8u;
@@ -217,18 +224,26 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   const uint32_t lt = tile - mm.tile0;
   const uint32_t tn = lt / a.mt, tm = lt - tn * a.mt;
   const uint32_t m0 = tm * TM;
-  const uint32_t k = a.k, nkb = k / 64u;
+  // This workgroup's K range, blocks [kb_lo, kb_lo + nkb): weights, scales and activations are
+  // addressed from block kb_lo on (block kb below is block kb_lo + kb of the row); k stays the
+  // row pitch.  Each resource ends where the matrix does.
+  const uint32_t k = a.k, kb_lo = blockIdx.y * a.bps, nkb = min(a.bps, k / 64u - kb_lo);
   const uint32_t pitch = k >> 1;
   constexpr uint32_t kSB = FMT == kINT4 ? 2u : 4u;
   const uint32_t spitch = (k / (FMT == kINT4 ? 128u : 64u)) * kSB;
+  const uint32_t soff = FMT == kINT4 ? kb_lo : kb_lo * 4u;  // scale bytes before block kb_lo
   const uint32_t wrow0 = tn * TN + (uint32_t)wave * 32u * NT;
   const uint32_t wbase = wrow0 < mm.n ? wrow0 : 0u;
   const uint32_t wrows = wrow0 < mm.n ? min(32u * NT, mm.n - wrow0) : 0u;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(mm.packed + (size_t)wbase * pitch, wrows * pitch);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(mm.packed + (size_t)wbase * pitch + kb_lo * 32u,
+                                              wrows ? wrows * pitch - kb_lo * 32u : 0u);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(reinterpret_cast<const char*>(mm.scales) + (size_t)wbase * spitch, wrows * spitch);
+      make_rsrc(reinterpret_cast<const char*>(mm.scales) + (size_t)wbase * spitch + soff,
+                wrows ? wrows * spitch - soff : 0u);
   const uint32_t xrows = min((uint32_t)TM, a.m - m0);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)m0 * k, xrows * k * 2u);
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(a.x + (size_t)m0 * k + kb_lo * 64u, xrows * k * 2u - kb_lo * 128u);
+  float* const yz = mm.y + (size_t)blockIdx.y * a.ysplit;
 
   // Block kb's packed bytes for this lane: row 32 t + c, bytes [16 h, 16 h + 16) of the block;
   // blocks past K and rows past N read as zero.
@@ -341,13 +356,13 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
     }
   };
 
-  // Every block scale of this wave's rows over the whole of K, checked once: lane (h, c) reads
+  // Every block scale of this wave's rows over its K range, checked once: lane (h, c) reads
   // scales h, h + 2, ... of row 32 t + c, one load per scale (rows past N read as zero, which
   // folds).  The loads go out after the first weights and stages, so the check adds no round trip
   // before the first block.
   bool fold = true;
   {
-    const uint32_t nsc = k / (FMT == kINT4 ? 128u : 64u);
+    const uint32_t nsc = FMT == kINT4 ? nkb / 2u : nkb;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const uint32_t row = (uint32_t)(32 * t + c);
@@ -385,8 +400,8 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
     }
   } else {
     // every wave runs the same number of barriers on either route
-    fold_block_scale_wave<FMT, NT>(rw, rs, rx, reinterpret_cast<const char*>(tab), xs0, xs1, mm.y,
-                                   mm.n, a.m, m0, wrow0, k);
+    fold_block_scale_wave<FMT, NT>(rw, rs, rx, reinterpret_cast<const char*>(tab), xs0, xs1, yz,
+                                   mm.n, a.m, m0, wrow0, k, nkb);
     return;
   }
 
@@ -402,26 +417,27 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t mr = m0 + 32u * j + 8u * (uint32_t)(e >> 2) + 4u * (uint32_t)h + (uint32_t)(e & 3);
-        if (mr < a.m) mm.y[(size_t)mr * n + col] = acc[t][j][e];
+        if (mr < a.m) yz[(size_t)mr * n + col] = acc[t][j][e];
       }
     }
   }
 }
 
 template <int FMT, int NT, bool GROUPED>
-hipError_t launch_nt(const FoldArgs& a, hipStream_t s) {
+hipError_t launch_nt(const FoldArgs& a, int ranges, hipStream_t s) {
   // Two activation stages and four blocks of weights in flight (eight blocks per unrolled trip,
   // two quads of scales): measured on MI355X against three stages and three blocks.
   constexpr int ST = 2, DP = 4;
-  hipLaunchKernelGGL((fold_kernel<FMT, NT, ST, DP, GROUPED>), dim3(a.tiles), dim3(kFoldThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL((fold_kernel<FMT, NT, ST, DP, GROUPED>), dim3(a.tiles, ranges),
+                     dim3(kFoldThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_fmt(const FoldArgs& a, int nt, hipStream_t s) {
-  if (nt == 2) return a.groups > 1 ? launch_nt<FMT, 2, true>(a, s) : launch_nt<FMT, 2, false>(a, s);
-  return a.groups > 1 ? launch_nt<FMT, 1, true>(a, s) : launch_nt<FMT, 1, false>(a, s);
+hipError_t launch_fmt(const FoldArgs& a, int nt, int ranges, hipStream_t s) {
+  if (nt == 2)
+    return a.groups > 1 ? launch_nt<FMT, 2, true>(a, ranges, s) : launch_nt<FMT, 2, false>(a, ranges, s);
+  return a.groups > 1 ? launch_nt<FMT, 1, true>(a, ranges, s) : launch_nt<FMT, 1, false>(a, ranges, s);
 }
 
 int64_t fold_tiles(const int64_t* ns, int groups, int64_t m, int64_t tn) {
@@ -432,31 +448,72 @@ int64_t fold_tiles(const int64_t* ns, int groups, int64_t m, int64_t tn) {
 
 }  // namespace
 
+// K ranges of the folded kernel when `splits` are requested over K: blocks per range as for the
+// block-scale kernel (ceil(blocks / splits)), rounded up to an even count for INT4 (a range then
+// starts on a 128-weight group), so never more ranges than that kernel's.
+int gemm_fold_ranges(int fmt, int64_t k, int splits, int64_t* bps) {
+  const int64_t nb = k / 64;
+  const int64_t sp = std::max<int64_t>(1, std::min<int64_t>(splits, nb));
+  int64_t per = (nb + sp - 1) / sp;
+  if (fmt == W4_INT4_X_F16) per += per & 1;
+  if (bps) *bps = per;
+  return (int)((nb + per - 1) / per);
+}
+
 bool gemm_fold_format(int fmt) {
   return fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16 || fmt == W4_FP4_X_F16;
 }
 
-// Weight rows per tile of the folded kernel for this launch (256 or 128), or 0 when the block-scale
-// kernel is the faster one.  Measured on MI355X (rotated weights, against the block-scale kernel's
-// automatic launch): at 512 activation rows, 256-row tiles where they number two per CU (one per
-// CU for rows of 4096+ weights): NF4 151936 x 1536 330 against 426 us (INT4 x fp16 303), 28672 x
-// 8192 289 against 402; else 128-row tiles from one per CU for rows shorter than 16384 weights
-// and two per CU for longer ones: 8960 x 1536 34 against 45 us, 8192 x 8192 117 against 129 (the
-// two gate/up matrices of a grouped launch: the same as the block-scale kernel's 64 x 128 tiles),
-// while 8192 x 28672 with one 128-row tile per CU (448 against 424) stays with the block-scale
-// kernel.  Below 256 activation rows the two kernels tie (151936 x 1536 at 128 rows: 123.5
-// against 124 us) and the block-scale one keeps them.
+// Weight rows per tile of the folded kernel for an unsplit launch (256 or 128), or 0 when the
+// block-scale kernel is the faster one.  Measured on MI355X (rotated weights, against the
+// block-scale kernel's automatic launch): at 512 activation rows, 256-row tiles where they number
+// two per CU (one per CU for rows of 4096+ weights): NF4 151936 x 1536 334 against 426 us (INT4 x
+// fp16 315), 28672 x 8192 289 against 402; else 128-row tiles from one per CU: 8960 x 1536 35
+// against 45 us, 8192 x 8192 106 against 129, 8192 x 28672 363 against 423 (the two gate/up
+// matrices of a grouped launch: the same as the block-scale kernel's 64 x 128 tiles).  Below 256
+// activation rows the two kernels tie (151936 x 1536 at 128 rows: 123.5 against 124 us) and the
+// block-scale one keeps them.
 int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m) {
   if (!gemm_fold_format(fmt) || m < 256 || k < 64 || k % 64 != 0) return 0;
   const int64_t cus = device_cu_count();
   if (fold_tiles(ns, groups, m, 256) >= (k >= 4096 ? cus : 2 * cus)) return 256;
-  if (fold_tiles(ns, groups, m, 128) >= (k >= 16384 ? 2 * cus : cus)) return 128;
+  if (fold_tiles(ns, groups, m, 128) >= cus) return 128;
   return 0;
+}
+
+// K ranges the automatic tiled path gives the folded kernel (128-row tiles) on one matrix, 1 for
+// none, or 0 where the kernel does not apply.  With T tiles below one per CU and rows of 4096+
+// weights: S = min(16, CUs / T, K / 64 / 12) ranges (at least 12 blocks each) when that is 2 or
+// more, about one workgroup per CU; from one to two tiles per CU with rows of 16384+ weights: two
+// ranges (two workgroups per CU).  Measured on MI355X (NF4 x fp16, rotated weights; INT4 within 5%): 1536 x
+// 8960 at 512 activation rows (48 tiles) 120 us unsplit, 67.8 / 50.1 / 41.6 / 36.7 / 40.3 / 39.8 /
+// 36.9 at S = 2 / 3 / 4 / 5 / 6 / 8 / 10 (the block-scale kernel's split: 44.4); at 256 rows (24
+// tiles) 38.6 / 32.7 / 26.9 / 24.3 / 28.2 at S = 4 / 5 / 8 / 10 / 16 (27.4); 1024 x 8192 at 512
+// (32 tiles) 34.7 / 28.1 / 26.1 / 29.3 at S = 4 / 6 / 8 / 10 (25.5); 8192 x 28672 at 512 (256
+// tiles) 363 / 339 / 354 at S = 1 / 2 / 3; 8192 x 8192 at 512 106 / 105 at S = 1 / 2 (not
+// split); 1536 x 1536 at 512 (24 blocks) 18.5 at best, against the MFMA path's 12.4 (not split).
+int gemm_fold_auto_splits(int fmt, int64_t n, int64_t k, int64_t m) {
+  if (!gemm_fold_format(fmt) || m < 256 || k < 64 || k % 64 != 0) return 0;
+  const int64_t cus = device_cu_count();
+  const int64_t nb = k / 64;
+  const int64_t tiles = fold_tiles(&n, 1, m, 128);
+  if (tiles < cus) {
+    if (nb < 64) return 1;
+    const int64_t s = std::min<int64_t>(std::min<int64_t>(16, cus / tiles), nb / 12);
+    return s >= 2 ? (int)s : 1;
+  }
+  return tiles < 2 * cus && nb >= 256 ? 2 : 1;
+}
+
+// Split tiled launches (one member) of the formats and sizes the folded kernel runs: it does.
+bool gemm_fold_split(int fmt, int groups, int64_t m) {
+  return gemm_fold_format(fmt) && groups == 1 && m >= 256;
 }
 
 hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
                             const void* const* scales, const int64_t* ns, float* const* y,
-                            int64_t k, int64_t m, int tile_rows, hipStream_t s) {
+                            int64_t k, int64_t m, int tile_rows, hipStream_t s, int splits,
+                            float* ws) {
   if (!gemm_fold_format(fmt) || groups < 1 || groups > kMaxGroup || m < 1 || k < 64 || k % 64 != 0)
     return hipErrorInvalidValue;
   if (fmt == W4_INT4_X_F16 && k % 128 != 0) return hipErrorInvalidValue;
@@ -469,6 +526,10 @@ hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_
   // 32-bit offsets inside the buffer resources: 128 activation rows and 64 weight rows of K.
   if (128 * k * 2 >= ((int64_t)1 << 31) || n_total >= ((int64_t)1 << 31) || m >= ((int64_t)1 << 31))
     return hipErrorNotSupported;
+  int64_t bps = 0;
+  const int ranges = gemm_fold_ranges(fmt, k, splits, &bps);
+  if (ranges > 1 && (groups > 1 || !ws)) return hipErrorInvalidValue;
+  if (ranges > 1 && m * ns[0] >= ((int64_t)1 << 32)) return hipErrorNotSupported;  // 32-bit planes
   const int64_t mt = (m + 32 * kFoldMT - 1) / (32 * kFoldMT);
   const int64_t tiles = fold_tiles(ns, groups, m, tile_rows);
   if (tiles >= ((int64_t)1 << 31)) return hipErrorNotSupported;
@@ -478,7 +539,7 @@ hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_
     const bool use = g < groups;
     a.mb[g].packed = use ? packed[g] : packed[0];
     a.mb[g].scales = use ? scales[g] : scales[0];
-    a.mb[g].y = use ? y[g] : nullptr;
+    a.mb[g].y = use ? (ranges > 1 ? ws : y[g]) : nullptr;
     a.mb[g].n = use ? (uint32_t)ns[g] : 0u;
     a.mb[g].tile0 = use ? (uint32_t)tile0 : 0xFFFFFFFFu;
     if (use) tile0 += ((ns[g] + tile_rows - 1) / tile_rows) * mt;
@@ -489,13 +550,18 @@ hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_
   a.k = (uint32_t)k;
   a.mt = (uint32_t)mt;
   a.tiles = (uint32_t)tiles;
+  a.bps = (uint32_t)bps;
+  a.ysplit = ranges > 1 ? (uint32_t)(m * ns[0]) : 0u;
   const int nt = tile_rows / 128;
+  hipError_t e = hipErrorInvalidValue;
   switch (fmt) {
-    case W4_NF4_X_F16: return launch_fmt<kNF4>(a, nt, s);
-    case W4_INT4_X_F16: return launch_fmt<kINT4>(a, nt, s);
-    case W4_FP4_X_F16: return launch_fmt<kFP4>(a, nt, s);
+    case W4_NF4_X_F16: e = launch_fmt<kNF4>(a, nt, ranges, s); break;
+    case W4_INT4_X_F16: e = launch_fmt<kINT4>(a, nt, ranges, s); break;
+    case W4_FP4_X_F16: e = launch_fmt<kFP4>(a, nt, ranges, s); break;
   }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || ranges == 1) return e;
+  // the ranges' partial sums, added in range order into y
+  return launch_splitk_reduce(ws, y[0], m * ns[0], ranges, s);
 }
 
 }  // namespace w4

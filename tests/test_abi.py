@@ -185,32 +185,56 @@ def test_mfma_split_rule():
 
 
 def test_tiled_split_rule():
-    """The automatic tiled GEMM's split-K count (host logic, 256 CUs where no GPU is visible): from
-    B = 128 the smallest power of two S with ceil(N / 64) * ceil(B / 128) * S >= 192, at least 16
-    blocks of 64 weights per range, at most 16 ranges; matrices under 4096 rows take the tiled GEMM
-    only when K splits and the workspace holds the partials, else the MFMA path."""
+    """The automatic tiled GEMM's split-K count (host logic, 256 CUs where no GPU is visible).
+    Block-scale kernel (bf16 activations, and fp16 below 256 rows): from B = 128 the smallest power
+    of two S with ceil(N / 64) * ceil(B / 128) * S >= 192, at least 16 blocks of 64 weights per
+    range, at most 16 ranges.  Matrices under 4096 rows take the tiled GEMM only when K splits and
+    the workspace holds the partials, else the MFMA path."""
     w4, _ = _lib()
     big = 1 << 30
-    assert w4.auto_path("nf4_f16", 1536, 8960, 512) == ("mfma", 1)  # no workspace
-    assert w4.auto_path("nf4_f16", 1536, 8960, 512, big) == ("tiled", 2)  # 96 tiles
-    assert w4.auto_path("nf4_f16", 1536, 8960, 256, big) == ("tiled", 4)  # 48 tiles
+    assert w4.auto_path("nf4_bf16", 1536, 8960, 512) == ("mfma", 1)  # no workspace
+    assert w4.auto_path("nf4_bf16", 1536, 8960, 512, big) == ("tiled", 2)  # 96 tiles
+    assert w4.auto_path("nf4_bf16", 1536, 8960, 256, big) == ("tiled", 4)  # 48 tiles
     assert w4.auto_path("nf4_f16", 1536, 8960, 128, big) == ("tiled", 8)  # 140 / 16 >= 8
     assert w4.auto_path("int4_bf16", 1024, 8192, 512, big) == ("tiled", 4)
     assert w4.auto_path("int4_bf16", 1024, 8192, 128, big) == ("tiled", 8)  # 128 / 16 < 16
     assert w4.auto_path("nf4_f16", 8192, 8192, 128, big) == ("tiled", 2)
-    assert w4.auto_path("nf4_f16", 8192, 8192, 512, big) == ("tiled", 1)  # 512 tiles
+    assert w4.auto_path("nf4_bf16", 8192, 8192, 512, big) == ("tiled", 1)  # 512 tiles
     assert w4.auto_path("nf4_f16", 8960, 1536, 128, big) == ("tiled", 1)  # 24 blocks: no split
-    assert w4.auto_path("nf4_f16", 1536, 1536, 512, big) == ("mfma", 1)
+    assert w4.auto_path("nf4_bf16", 1536, 1536, 512, big) == ("mfma", 1)
     assert w4.auto_path("nf4_f16", 1536, 8960, 64, big) == ("mfma", 16)  # below the tiled batch
-    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512) == 2 * 512 * 1536 * 4
+    assert w4.workspace_bytes("nf4_bf16", 1536, 8960, 512) == 2 * 512 * 1536 * 4
     assert w4.workspace_bytes("nf4_f16", 1536, 8960, 128) == 8 * 128 * 1536 * 4
-    assert w4.auto_path("nf4_f16", 1536, 8960, 512, 2 * 512 * 1536 * 4 - 1) == ("mfma", 1)
+    assert w4.auto_path("nf4_bf16", 1536, 8960, 512, 2 * 512 * 1536 * 4 - 1) == ("mfma", 1)
     assert w4.workspace_bytes("nf4_f16", 8192, 8192, 512) == 0
     # explicit splits: ceil(K / 64 / ceil(K / 64 / S)) ranges, 4 * ranges * B * N bytes
     assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512, "tiled", 8) == 8 * 512 * 1536 * 4
     assert w4.workspace_bytes("nf4_f16", 64, 192, 130, "tiled", 2) == 2 * 130 * 64 * 4  # 3 blocks
     assert w4.workspace_bytes("nf4_f16", 64, 192, 130, "tiled", 16) == 3 * 130 * 64 * 4
     assert w4.workspace_bytes("nf4_f16", 64, 192, 130, "tiled", 1) == 0
+
+
+def test_tiled_split_rule_folded():
+    """NF4, INT4 and FP4 with fp16 activations from 256 rows (the folded-scale kernel, 128-row
+    tiles, T tiles): below one tile per CU with rows of 4096+ weights, S = min(16, 256 / T,
+    K / 64 / 12) when that is 2 or more; from one to two tiles per CU with rows of 16384+ weights,
+    S = 2; otherwise one pass (and shorter rows keep the MFMA path under 4096 matrix rows)."""
+    w4, _ = _lib()
+    big = 1 << 30
+    for fmt in ("nf4_f16", "int4_f16", "fp4_f16"):
+        assert w4.auto_path(fmt, 1536, 8960, 512, big) == ("tiled", 5)  # 48 tiles
+        assert w4.auto_path(fmt, 1536, 8960, 256, big) == ("tiled", 10)  # 24 tiles
+        assert w4.auto_path(fmt, 1024, 8192, 512, big) == ("tiled", 8)  # 32 tiles
+        assert w4.auto_path(fmt, 200, 8192, 512, big) == ("tiled", 10)  # 8 tiles; 128 / 12 blocks
+        assert w4.auto_path(fmt, 8192, 28672, 512, big) == ("tiled", 2)  # 256 tiles, long rows
+        assert w4.auto_path(fmt, 8192, 28672, 512) == ("tiled", 1)  # no workspace: one pass
+        assert w4.auto_path(fmt, 8192, 8192, 512, big) == ("tiled", 1)  # 256 tiles
+        assert w4.auto_path(fmt, 16384, 28672, 512, big) == ("tiled", 1)  # 512 tiles
+        assert w4.auto_path(fmt, 1536, 1536, 512, big) == ("mfma", 1)  # 24 blocks: no split
+        assert w4.auto_path(fmt, 1536, 2048, 512, big) == ("mfma", 1)  # 32 blocks: no split
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512) == 5 * 512 * 1536 * 4
+    assert w4.workspace_bytes("int4_f16", 1536, 8960, 256) == 10 * 256 * 1536 * 4
+    assert w4.workspace_bytes("fp4_f16", 8192, 28672, 512) == 2 * 512 * 8192 * 4
 
 
 def _grouped(L, n=(64, 32, 32), x=FAKE, p=None, s=None, y=None, fmt=1, k=256, b=1, groups=None,
@@ -368,17 +392,26 @@ def test_sparse24_grouped_validation_codes():
 
 
 def test_tiled_f16_host_checks():
-    """W4_PATH_TILED_F16 runs fp16 activations with NF4, INT4 or FP4 weights and no split: other
-    formats and split_k > 1 fail with W4_ERR_PATH before any launch; it asks for no workspace."""
+    """W4_PATH_TILED_F16 runs fp16 activations with NF4, INT4 or FP4 weights: other formats fail
+    with W4_ERR_PATH before any launch; unsplit it asks for no workspace; split over K it needs one
+    fp32 plane per K range (W4_ERR_WORKSPACE without one, W4_ERR_PATH past W4_MAX_SPLIT_K), with
+    ceil(K/64 / S) blocks per range, an even count for INT4 (fewer ranges where that rounds up)."""
     w4, L = _lib()
     vp = ctypes.c_void_p
     for fmt in (2, 4, 6, 7, 8):
         assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), fmt, 64, 256, 200, vp(FAKE * 64),
                               6, 0, None, 0, None) == -7
     assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 200, vp(FAKE * 64), 6, 2,
+                          None, 0, None) == -6
+    assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 200, vp(FAKE * 64), 6, 65,
                           None, 0, None) == -7
     for fmt in ("nf4_f16", "int4_f16", "fp4_f16"):
         assert w4.workspace_bytes(fmt, 8960, 1536, 512, "tiled_f16") == 0
+        assert w4.workspace_bytes(fmt, 1536, 8960, 512, "tiled_f16", 5) == 5 * 512 * 1536 * 4
+    # 140 blocks, S = 11: 13 blocks per range (11 ranges); INT4 rounds to 14 (10 ranges)
+    assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512, "tiled_f16", 11) == 11 * 512 * 1536 * 4
+    assert w4.workspace_bytes("int4_f16", 1536, 8960, 512, "tiled_f16", 11) == 10 * 512 * 1536 * 4
+    assert w4.workspace_bytes("nf4_bf16", 1536, 8960, 512, "tiled_f16", 4) == 0
 
 
 def test_path_override_and_workspace_registration():

@@ -192,3 +192,51 @@ def test_tiled_f16_random_shapes(seed):
     y = torch.full((b, n), float("nan"), device=xd.device)
     w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", y=y)
     g.assert_y_close(fmt, y, x, pr, sr)
+
+
+# K split into ranges of whole blocks (their partial sums added in range order): ragged last
+# ranges, ranges shorter than one unrolled trip of eight blocks, INT4 ranges rounded to an even
+# block count (k = 640: S = 4 gives ranges of 4, 4 and 2 blocks), a range of one block.
+@pytest.mark.parametrize("fmt", F16_FMTS)
+@pytest.mark.parametrize("n,k,b,splits", [(300, 8960, 300, 5), (129, 4096, 512, 3), (64, 1536, 256, 7),
+                                          (37, 640, 130, 4), (200, 1024, 129, 16), (1536, 2048, 40, 2)])
+def test_tiled_f16_split_k(fmt, n, k, b, splits):
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    if fmt.startswith("int4") and k % 128:
+        pytest.skip("INT4 groups are 128 weights")
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=n * 5 + splits)
+    wsb = w4.workspace_bytes(fmt, n, k, b, "tiled_f16", splits)
+    assert wsb > 0
+    ws = torch.full((wsb // 4,), float("nan"), device=xd.device).view(torch.uint8)
+    y = torch.full((b, n), float("nan"), device=xd.device)
+    w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", split_k=splits, workspace=ws, y=y)
+    g.assert_y_close(fmt, y, x, pr, sr)
+    y2 = w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", split_k=splits, workspace=ws)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("fmt", F16_FMTS)
+def test_tiled_f16_split_k_scale_range(fmt):
+    """The scale-range rows of the unsplit test, K split in three: a wave whose range holds an
+    unfoldable scale takes the fp32 route for that range only; every row within the bound."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    n, k, b = 512, 1536, 160
+    grp = 128 if fmt.startswith("int4") else 64
+    w = synth_inputs.weights(n, k, seed=41).astype(np.float64)
+    rows = np.arange(n)
+    kind = (rows // 32) % 4
+    w[kind == 1, 3 * grp:4 * grp] *= 1e-7
+    w[kind == 2, :] *= 1e6
+    w[(kind == 3) & (rows % 2 == 0), :] = 0.0
+    w = w.astype(np.float32)
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=42, w=w)
+    ws = torch.empty(w4.workspace_bytes(fmt, n, k, b, "tiled_f16", 3), dtype=torch.uint8,
+                     device=xd.device)
+    y = w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", split_k=3, workspace=ws)
+    g.assert_y_close(fmt, y, x, pr, sr)
