@@ -113,24 +113,31 @@ typedef enum {
                           reduction; W4_PATH_AUTO, given a workspace, splits K into the smallest
                           power of two of ranges that gives three quarters of the CUs a 64-row
                           tile, each range at least 16 blocks, at most 16 ranges.  For fp16
-                          activations (W4_NF4_X_F16, W4_INT4_X_F16, W4_FP4_X_F16) a one-pass tiled
-                          launch with enough tiles runs the folded kernel of W4_PATH_TILED_F16
-                          instead (see there)                                                   */
+                          activations (W4_NF4_X_F16, W4_INT4_X_F16, W4_FP4_X_F16) from 256
+                          activation rows the folded kernel of W4_PATH_TILED_F16 runs instead: a
+                          one-pass launch with enough tiles, and every split launch, with that
+                          kernel's split rule for W4_PATH_AUTO (see there)                      */
   W4_PATH_TILED_F16 = 6 /* prefill-size GEMM for fp16 activations with each block scale folded into
                           the decoded fp16 weights (one packed multiply per weight pair), so the
                           matrix cores accumulate x * W_hat over all of K: tiles of 256 or 128
-                          weight rows x 128 activation rows, 32x32x16 matrix steps; any B, no
-                          split (split_k <= 1), no workspace.  W4_NF4_X_F16, W4_INT4_X_F16 and
+                          weight rows x 128 activation rows, 32x32x16 matrix steps; any B; no
+                          workspace in one pass (split_k <= 1), else K in ranges of whole
+                          64-weight blocks (128-row tiles; an even number of blocks per range
+                          for INT4), partial sums in the workspace, the fixed-order reduction.
+                          W4_NF4_X_F16, W4_INT4_X_F16 and
                           W4_FP4_X_F16 only (other formats: W4_ERR_PATH).  A folded weight is
                           within 3 * 2^-11 of W_hat (NF4; FP4 2 * 2^-11; INT4 exact); a wave whose
                           rows hold a block scale outside the range where every folded weight is a
                           normal, finite fp16 number (NF4 [2^-10, 2^15], FP4 [2^-13, 2^13], INT4
                           [2^-14, 2^12], or zero) runs all of K with the scale applied in fp32 per
                           block instead.  W4_PATH_AUTO and W4_PATH_TILED take it for those
-                          formats from 256 activation rows, with 256-row tiles when those number
-                          at least two per CU (one per CU for K >= 4096), else with 128-row
-                          tiles when those number at least one per CU (two per CU for
-                          K >= 16384)                                                            */
+                          formats from 256 activation rows: in one pass with 256-row tiles when
+                          those number at least two per CU (one per CU for K >= 4096), else with
+                          128-row tiles when those number at least one per CU; split launches
+                          always.  W4_PATH_AUTO with a workspace splits K for it when its T
+                          128-row tiles number under one per CU and K >= 4096, into
+                          min(16, CUs / T, K / 64 / 12) ranges if that is at least 2, and into
+                          two ranges when 1 <= T / CUs < 2 and K >= 16384                       */
 } w4_path_t;
 
 #define W4_MAX_BATCH 4096
@@ -306,10 +313,12 @@ int w4_gemm_smallbatch_grouped(const void* x, int groups, const uint8_t* const* 
  * The bytes a path writes into the workspace must not overlap x, packed, scales or y
  * (W4_ERR_ALIAS).
  *   split_k          number of K ranges for W4_PATH_SPLITK (2..W4_MAX_SPLIT_K; 0 = 4), for
- *                    W4_PATH_MFMA and for W4_PATH_TILED (2..W4_MAX_SPLIT_K; 0 or 1 = one pass);
- *                    ignored by the other paths.  The GEMV and MFMA splits need 4 * split_k * B * N
- *                    workspace bytes; the tiled GEMM makes R = ceil(K/64 / ceil(K/64 / split_k))
- *                    ranges of whole 64-weight blocks (R <= split_k) and needs 4 * R * B * N.
+ *                    W4_PATH_MFMA, W4_PATH_TILED and W4_PATH_TILED_F16 (2..W4_MAX_SPLIT_K; 0 or
+ *                    1 = one pass); ignored by the other paths.  The GEMV and MFMA splits need
+ *                    4 * split_k * B * N workspace bytes; the tiled GEMM makes
+ *                    R = ceil(K/64 / ceil(K/64 / split_k)) ranges of whole 64-weight blocks
+ *                    (R <= split_k) and needs 4 * R * B * N (the folded kernel rounds the blocks
+ *                    per range up to an even count for W4_INT4_X_F16, which never adds ranges).
  *   workspace        device memory of at least w4_workspace_bytes(...) bytes, 16-byte aligned;
  *                    may be NULL when that size is 0.  Its contents are scratch on entry and exit.
  *                    Two calls in flight must not share one workspace.
