@@ -37,7 +37,8 @@
 //     ahead; 16-byte slot S of a stage holds row S / 8 and chunk (S % 8) XOR (row % 8), which puts
 //     the eight rows a group of lanes reads into distinct banks.
 //   * Weights and scales: DP blocks ahead in rotating register sets.
-//   * Decode: the byte -> pair table of w4_mfma_common.h (32 copies, one LDS read per two weights).
+//   * Decode: the byte -> pair table of w4_mfma_common.h (32 copies, one LDS read per two weights);
+//     FP4 converts in registers instead (gfx950 E2M1 conversion, no table).
 //   * Tiles are numbered so that the workgroups one XCD receives (every eighth) take consecutive
 //     tiles, the activation-row tiles of a weight tile first: the weight tile then comes from that
 //     XCD's L2 after its first read.
@@ -97,6 +98,30 @@ __device__ inline float scale_f32(uint32_t raw) {
   return FMT == kINT4 ? __uint_as_float(raw << 16) : __uint_as_float(raw);
 }
 
+// The four weight pairs of packed dword wd (byte j: weight 2j in the high nibble, 2j + 1 in the
+// low one) as unscaled fp16 codes, weight 2j in the low half.  NF4 and INT4 through the LDS table:
+// one read per byte at byte * 128 + the lane's copy offset (the perm builds byte * 256 + 2 * copy
+// offset, the packed byte into byte 1, halved by the shift).  FP4 through gfx950's E2M1
+// conversion instead (one instruction per byte, exact, no table): it puts the low nibble in the
+// low half, so the nibbles of every byte are swapped first.
+template <int FMT>
+__device__ inline void decode4(uint32_t wd, const char* tabc, uint32_t laneoff, uint32_t (&p)[4]) {
+  if constexpr (FMT == kFP4) {
+    const uint32_t sw = ((wd >> 4) & 0x0F0F0F0Fu) | ((wd & 0x0F0F0F0Fu) << 4);
+    p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(sw, 1.0f, 0));
+    p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(sw, 1.0f, 1));
+    p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(sw, 1.0f, 2));
+    p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(sw, 1.0f, 3));
+  } else {
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      const uint32_t addr =
+          __builtin_amdgcn_perm(wd, laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb4) << 8)) >> 1;
+      p[kb4] = *reinterpret_cast<const uint32_t*>(tabc + addr);
+    }
+  }
+}
+
 // The block-scale route of one wave, for rows that hold a scale outside the fold range: raw codes
 // on the matrix cores, each block's partial sums rescaled in fp32 (exact scale, any range), then
 // the wave's stores.  It walks the same stages with the same barriers as the folded loop (the
@@ -154,12 +179,7 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t pr[4];
-#pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-          const uint32_t addr =
-              __builtin_amdgcn_perm(wd[q], laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb4) << 8)) >> 1;
-          pr[kb4] = *reinterpret_cast<const uint32_t*>(tabc + addr);
-        }
+        decode4<FMT>(wd[q], tabc, laneoff, pr);
         bu[q] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
       }
 #pragma unroll
@@ -197,7 +217,8 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   constexpr int MT = kFoldMT;
   constexpr int TN = 4 * 32 * NT, TM = 32 * MT;
   constexpr int SLOTS = TM * 8;  // 16-byte slots of one stage (64 k per row)
-  __shared__ __align__(16) uint32_t tab[kTableBytes / 4];
+  // the byte -> pair table (not used by FP4, which converts in registers)
+  __shared__ __align__(16) uint32_t tab[FMT == kFP4 ? 4 : kTableBytes / 4];
   // The two stages are separate LDS objects and every access names one of them statically: the
   // compiler then tells a stage's reads from the copies into the other stage (and from the table)
   // and waits only for the copies a read depends on.  As one array indexed by stage, every LDS read
@@ -294,7 +315,7 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   load_sq(0, SQ[0]);
 #pragma unroll
   for (int i = 0; i < DP; ++i) load_w((uint32_t)i, W[i]);
-  fill_table<FMT, kF16, kFoldThreads>(tab);
+  if constexpr (FMT != kFP4) fill_table<FMT, kF16, kFoldThreads>(tab);
 
   f32x16 acc[NT][MT];
 #pragma unroll
@@ -304,18 +325,8 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][j][e] = 0.f;
 
-  // LDS byte address of a lookup = byte * 128 + lane copy offset: the perm builds byte * 256 +
-  // 2 * copy offset (the packed byte into byte 1), halved by the shift.
-  const uint32_t laneoff = (uint32_t)c * 8u;
+  const uint32_t laneoff = (uint32_t)c * 8u;  // this lane's table copy
   const char* tabc = reinterpret_cast<const char*>(tab);
-  auto lookup4 = [&](uint32_t wd, uint32_t (&p)[4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4) {
-      const uint32_t addr =
-          __builtin_amdgcn_perm(wd, laneoff, 0x0C0C0000u | ((4u + (uint32_t)kb4) << 8)) >> 1;
-      p[kb4] = *reinterpret_cast<const uint32_t*>(tabc + addr);
-    }
-  };
   auto afrag = [&](int b, int j, int q) __attribute__((always_inline)) {
     const uint32_t mr = (uint32_t)(32 * j + c), cc = (uint32_t)(4 * h + q);
     return (b ? xs1 : xs0)[mr * 8u + (cc ^ (mr & 7u))];
@@ -337,7 +348,7 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t p[4];
-        lookup4(wd[q], p);
+        decode4<FMT>(wd[q], tabc, laneoff, p);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           p[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p[e]) * s2);
