@@ -1342,6 +1342,7 @@ COUNTER_CASES = [
     ("tiled nf4 gate B=512", "nf4_f16", 8960, 1536, 512, "tiled"),
     ("tiled nf4 lm_head B=512", "nf4_f16", 151936, 1536, 512, "tiled"),
     ("tiled nf4 L.gate B=512", "nf4_f16", 28672, 8192, 512, "tiled"),
+    ("tiled fp4 lm_head B=512", "fp4_f16", 151936, 1536, 512, "tiled"),
     ("tiled nf4 bf16 lm_head B=512", "nf4_bf16", 151936, 1536, 512, "tiled"),
     ("tiled int4 bf16 L.gate B=512", "int4_bf16", 28672, 8192, 512, "tiled"),
 ]

@@ -34,8 +34,8 @@
 // step q (0 .. 3) takes 32 h + 8 q .. + 7; the A lanes read the same k positions of x.
 //   * Activations: ST stages of TM rows x 64 k in LDS (16 KiB each), copied straight from global
 //     memory by buffer loads with the LDS destination (no register round trip), ST - 1 blocks
-//     ahead; 16-byte slot S of a stage holds row S / 8 and chunk (S % 8) XOR (row % 8), which puts
-//     the eight rows a group of lanes reads into distinct banks.
+//     ahead; 16-byte slot S of a stage holds row S / 8 and chunk (S % 8) XOR ((row / 2) % 8), which
+//     puts the sixteen rows a 16-lane group reads into distinct banks (see xkey).
 //   * Weights and scales: DP blocks ahead in rotating register sets.
 //   * Decode: the byte -> pair table of w4_mfma_common.h (32 copies, one LDS read per two weights);
 //     FP4 converts in registers instead (gfx950 E2M1 conversion, no table).
@@ -84,6 +84,12 @@ __device__ inline f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
 }
+
+// XOR key of the 16-byte chunks of activation row mr in a stage: (mr / 2) mod 8.  A 128-bit LDS
+// read serves 16 lanes per cycle across 64 banks (16 slots); the 16 lanes of a fragment read take
+// rows r .. r + 15 at one chunk, whose slots must then differ mod 16: row parity gives slot bit 3,
+// the key bits 0-2 (a key of mr mod 8 repeats for rows r and r + 8: two-way conflicts).
+__device__ inline uint32_t xkey(uint32_t mr) { return (mr >> 1) & 7u; }
 
 // The fold range of a block scale (see the top of this file), and the scale as fp32.
 template <int FMT>
@@ -161,7 +167,7 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
 #pragma unroll
       for (int j = 0; j < SLOTS / kFoldThreads; ++j) {
         const uint32_t sl = (uint32_t)(j * kFoldThreads + tid);
-        const uint32_t mr = sl >> 3, cc = (sl & 7u) ^ (mr & 7u);
+        const uint32_t mr = sl >> 3, cc = (sl & 7u) ^ xkey(mr);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rx, (__attribute__((address_space(3))) void*)((bn ? xs1 : xs0) + j * kFoldThreads + wave * 64),
             16, (int)offset_or_oob(have, (mr * k + kn * 64u + cc * 8u) * 2u), 0, 0, 0);
@@ -190,7 +196,7 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t mr = (uint32_t)(32 * j + c), cc = (uint32_t)(4 * h + q);
-          dd = mfma32(xst[mr * 8u + (cc ^ (mr & 7u))], bu[q], dd);
+          dd = mfma32(xst[mr * 8u + (cc ^ xkey(mr))], bu[q], dd);
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[t][j][e] = __builtin_fmaf(dd[e], sf, acc[t][j][e]);
@@ -303,7 +309,7 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
 #pragma unroll
     for (int j = 0; j < SLOTS / kFoldThreads; ++j) {
       const uint32_t sl = (uint32_t)(j * kFoldThreads + tid);
-      const uint32_t mr = sl >> 3, cc = (sl & 7u) ^ (mr & 7u);
+      const uint32_t mr = sl >> 3, cc = (sl & 7u) ^ xkey(mr);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx, (__attribute__((address_space(3))) void*)((b ? xs1 : xs0) + j * kFoldThreads + wave * 64), 16,
           (int)offset_or_oob(have, (mr * k + kb * 64u + cc * 8u) * 2u), 0, 0, 0);
@@ -329,7 +335,7 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   const char* tabc = reinterpret_cast<const char*>(tab);
   auto afrag = [&](int b, int j, int q) __attribute__((always_inline)) {
     const uint32_t mr = (uint32_t)(32 * j + c), cc = (uint32_t)(4 * h + q);
-    return (b ? xs1 : xs0)[mr * 8u + (cc ^ (mr & 7u))];
+    return (b ? xs1 : xs0)[mr * 8u + (cc ^ xkey(mr))];
   };
 
   // Block kb of the folded route: the barrier completes stage b (every wave's copies) and ends
