@@ -66,7 +66,8 @@ struct FoldArgs {
   uint32_t groups;
   uint32_t m, k;
   uint32_t mt;     // activation-row tiles (128 rows each)
-  uint32_t tiles;  // tiles of all members
+  uint32_t tiles;  // workgroups along x: tiles of this launch times the slices of each
+  uint32_t tile_base;  // first tile of this launch (tiles counted over all members)
   uint32_t bps;    // 64-weight blocks per K range: range z = blockIdx.y owns blocks
                    // [z bps, min((z + 1) bps, K / 64)) and writes y + z * ysplit
   uint32_t ysplit; // floats between the partial planes of consecutive ranges (M * N; one member)
@@ -78,7 +79,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kFoldThreads = 256;
-constexpr int kFoldMT = 4;  // 32-row activation tiles per wave: TM = 128
+constexpr int kFoldMT = 4;  // 32-row activation tiles per wave in a full tile: TM = 128
 
 __device__ inline f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
@@ -134,13 +135,12 @@ __device__ inline void decode4(uint32_t wd, const char* tabc, uint32_t laneoff, 
 // stages are filled by every wave of the workgroup) but loads each block's weights when it needs
 // them.  Kept out of line, with accumulators of its own: the folded loop's registers are then
 // allocated as if this route did not exist (inlined, it cost the folded route 8-30%).
-template <int FMT, int NT>
+template <int FMT, int NT, int MT>
 __device__ __attribute__((noinline)) void fold_block_scale_wave(
     __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rx,
     const char* tabc, uint4* xs0, uint4* xs1, float* y, uint32_t n, uint32_t m, uint32_t m0,
     uint32_t wrow0, uint32_t k, uint32_t nkb) {
   constexpr int ST = 2;
-  constexpr int MT = kFoldMT;
   constexpr int SLOTS = 32 * MT * 8;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -218,10 +218,10 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
   }
 }
 
-template <int FMT, int NT, int ST, int DP, bool GROUPED>
+template <int FMT, int NT, int MT, int ST, int DP, bool GROUPED>
 __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
-  constexpr int MT = kFoldMT;
   constexpr int TN = 4 * 32 * NT, TM = 32 * MT;
+  constexpr uint32_t SUBS = kFoldMT / MT;  // slices of TM activation rows per 128-row tile
   constexpr int SLOTS = TM * 8;  // 16-byte slots of one stage (64 k per row)
   // the byte -> pair table (not used by FP4, which converts in registers)
   __shared__ __align__(16) uint32_t tab[FMT == kFP4 ? 4 : kTableBytes / 4];
@@ -238,9 +238,10 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c = lane & 31;
 
-  const uint32_t id = blockIdx.x, tiles = a.tiles;
-  const uint32_t xcd = id % 8u, per = tiles / 8u, extra = tiles % 8u;
-  const uint32_t tile = xcd * per + min(xcd, extra) + id / 8u;
+  const uint32_t id = blockIdx.x, units = a.tiles;
+  const uint32_t xcd = id % 8u, per = units / 8u, extra = units % 8u;
+  const uint32_t unit = xcd * per + min(xcd, extra) + id / 8u;
+  const uint32_t tile = a.tile_base + unit / SUBS, sub = unit % SUBS;
   FoldMember mm = a.mb[0];
   if constexpr (GROUPED) {
 #pragma unroll
@@ -250,7 +251,8 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   }
   const uint32_t lt = tile - mm.tile0;
   const uint32_t tn = lt / a.mt, tm = lt - tn * a.mt;
-  const uint32_t m0 = tm * TM;
+  const uint32_t m0 = tm * (32u * kFoldMT) + sub * TM;
+  if (m0 >= a.m) return;  // a slice past the last activation row: the whole workgroup, no barrier
   // This workgroup's K range, blocks [kb_lo, kb_lo + nkb): weights, scales and activations are
   // addressed from block kb_lo on (block kb below is block kb_lo + kb of the row); k stays the
   // row pitch.  Each resource ends where the matrix does.
@@ -417,7 +419,7 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
     }
   } else {
     // every wave runs the same number of barriers on either route
-    fold_block_scale_wave<FMT, NT>(rw, rs, rx, reinterpret_cast<const char*>(tab), xs0, xs1, yz,
+    fold_block_scale_wave<FMT, NT, MT>(rw, rs, rx, reinterpret_cast<const char*>(tab), xs0, xs1, yz,
                                    mm.n, a.m, m0, wrow0, k, nkb);
     return;
   }
@@ -440,21 +442,33 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   }
 }
 
-template <int FMT, int NT, bool GROUPED>
+template <int FMT, int NT, int MT, bool GROUPED>
 hipError_t launch_nt(const FoldArgs& a, int ranges, hipStream_t s) {
   // Two activation stages and four blocks of weights in flight (eight blocks per unrolled trip,
   // two quads of scales): measured on MI355X against three stages and three blocks.
   constexpr int ST = 2, DP = 4;
-  hipLaunchKernelGGL((fold_kernel<FMT, NT, ST, DP, GROUPED>), dim3(a.tiles, ranges),
+  hipLaunchKernelGGL((fold_kernel<FMT, NT, MT, ST, DP, GROUPED>), dim3(a.tiles, ranges),
                      dim3(kFoldThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t launch_fmt(const FoldArgs& a, int nt, int ranges, hipStream_t s) {
+template <int FMT, int MT>
+hipError_t launch_mt(const FoldArgs& a, int nt, int ranges, hipStream_t s) {
   if (nt == 2)
-    return a.groups > 1 ? launch_nt<FMT, 2, true>(a, ranges, s) : launch_nt<FMT, 2, false>(a, ranges, s);
-  return a.groups > 1 ? launch_nt<FMT, 1, true>(a, ranges, s) : launch_nt<FMT, 1, false>(a, ranges, s);
+    return a.groups > 1 ? launch_nt<FMT, 2, MT, true>(a, ranges, s)
+                        : launch_nt<FMT, 2, MT, false>(a, ranges, s);
+  return a.groups > 1 ? launch_nt<FMT, 1, MT, true>(a, ranges, s)
+                      : launch_nt<FMT, 1, MT, false>(a, ranges, s);
+}
+
+// Full 128-row tiles [tile_base, tile_base + count), or (thin) the same tiles as four 32-row
+// slices each.
+template <int FMT>
+hipError_t launch_fmt(FoldArgs a, int nt, int ranges, int64_t tile_base, int64_t count, bool thin,
+                      hipStream_t s) {
+  a.tile_base = (uint32_t)tile_base;
+  a.tiles = (uint32_t)(thin ? count * kFoldMT : count);
+  return thin ? launch_mt<FMT, 1>(a, nt, ranges, s) : launch_mt<FMT, kFoldMT>(a, nt, ranges, s);
 }
 
 int64_t fold_tiles(const int64_t* ns, int groups, int64_t m, int64_t tn) {
@@ -566,16 +580,24 @@ hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_
   a.m = (uint32_t)m;
   a.k = (uint32_t)k;
   a.mt = (uint32_t)mt;
-  a.tiles = (uint32_t)tiles;
   a.bps = (uint32_t)bps;
   a.ysplit = ranges > 1 ? (uint32_t)(m * ns[0]) : 0u;
   const int nt = tile_rows / 128;
-  hipError_t e = hipErrorInvalidValue;
-  switch (fmt) {
-    case W4_NF4_X_F16: e = launch_fmt<kNF4>(a, nt, ranges, s); break;
-    case W4_INT4_X_F16: e = launch_fmt<kINT4>(a, nt, ranges, s); break;
-    case W4_FP4_X_F16: e = launch_fmt<kFP4>(a, nt, ranges, s); break;
-  }
+  // Two workgroups per CU hold 2 * CUs tiles at once.  One pass whose tiles leave a last round of
+  // at most CUs / 4 tiles (whole rounds before it) runs that round as a second launch of 32-row
+  // slices, four per tile, spread over the CUs: the sums over K take the same order either way.
+  const int64_t slots = 2 * device_cu_count(), rem = tiles % slots;
+  const int64_t tail = ranges == 1 && tiles > slots && 4 * rem <= slots / 2 ? rem : 0;
+  auto run = [&](int64_t base, int64_t count, bool thin) {
+    switch (fmt) {
+      case W4_NF4_X_F16: return launch_fmt<kNF4>(a, nt, ranges, base, count, thin, s);
+      case W4_INT4_X_F16: return launch_fmt<kINT4>(a, nt, ranges, base, count, thin, s);
+      case W4_FP4_X_F16: return launch_fmt<kFP4>(a, nt, ranges, base, count, thin, s);
+    }
+    return hipErrorInvalidValue;
+  };
+  hipError_t e = run(0, tiles - tail, false);
+  if (e == hipSuccess && tail > 0) e = run(tiles - tail, tail, true);
   if (e != hipSuccess || ranges == 1) return e;
   // the ranges' partial sums, added in range order into y
   return launch_splitk_reduce(ws, y[0], m * ns[0], ranges, s);

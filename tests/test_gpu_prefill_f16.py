@@ -240,3 +240,59 @@ def test_tiled_f16_split_k_scale_range(fmt):
                      device=xd.device)
     y = w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", split_k=3, workspace=ws)
     g.assert_y_close(fmt, y, x, pr, sr)
+
+
+def _tail_case(fmt, ns, k, b, seed):
+    """Members drawn on the GPU, quantized there, with rows sampled for the oracle: the last 128-row
+    tiles of the last member (the launch's last round) always among them."""
+    import torch
+
+    dev = g.device()
+    packed, scales, checks = [], [], []
+    for i, n in enumerate(ns):
+        gen = torch.Generator(device=dev).manual_seed(seed + i)
+        w = torch.randn(n, k, generator=gen, device=dev) * 0.02
+        p, s = g.gpu_quantize(fmt, w)
+        rng = np.random.default_rng(seed + 100 + i)
+        last = np.arange(max(0, n - 300), n)
+        rows = np.unique(np.concatenate([[0], rng.choice(n, 60, replace=False), last[::3]]))
+        w_rows = w[torch.as_tensor(rows, device=dev)].cpu().numpy()
+        del w
+        pr, sr = g.oracle_quantize(fmt, w_rows)
+        packed.append(p)
+        scales.append(s)
+        checks.append((rows, pr, sr))
+    return packed, scales, checks
+
+
+# The tiled path runs a one-pass launch whose last round of 128-row tiles holds at most CUs / 4
+# tiles as a second launch of 32-row slices (on 256 CUs: 513..576 tiles, 1025..1088, ...):
+# gate|up as one grouped call at 512 and at 400 activation rows (the last 128-row tile 16 rows:
+# its slices past row 400 do nothing), and one 17000-row matrix (133 x 4 = 532 tiles).  Every
+# output written (y pre-filled with NaN), sampled rows within the bound, the grouped call bitwise
+# equal to its members alone (their launches have no such round), two calls bitwise equal.
+@pytest.mark.parametrize("fmt", F16_FMTS)
+@pytest.mark.parametrize("ns,b", [((8960, 8960), 512), ((8960, 8960), 400), ((17000,), 512)])
+def test_tiled_f16_last_round_slices(fmt, ns, b):
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    k = 1536
+    dev = g.device()
+    x = synth_inputs.activations(b, k, "f16", seed=b + len(ns))
+    xd = g.to_dev_x(x, "f16")
+    packed, scales, checks = _tail_case(fmt, ns, k, b, seed=900 + b)
+    ys = [torch.full((b, n), float("nan"), device=dev) for n in ns]
+    if len(ns) > 1:
+        w4.gemm_smallbatch_grouped(xd, packed, scales, fmt, ys=ys)
+    else:
+        w4.matmul_ex(xd, packed[0], scales[0], fmt, path="tiled", y=ys[0])
+    for y, p, s, (rows, pr, sr) in zip(ys, packed, scales, checks):
+        assert bool(torch.isfinite(y).all())
+        g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=dev)], x, pr, sr)
+        alone = w4.matmul_ex(xd, p, s, fmt, path="tiled_f16")
+        if len(ns) > 1:
+            assert torch.equal(y, alone)
+        else:
+            assert torch.equal(y, w4.matmul_ex(xd, p, s, fmt, path="tiled"))
