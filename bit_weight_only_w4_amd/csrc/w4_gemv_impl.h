@@ -27,14 +27,6 @@
 //     The table is written while the first loads are in flight.  FP4
 //     needs no table: gfx950 converts a byte of two E2M1 codes to a 16-bit pair in one
 //     instruction (the pair comes out odd k first, so FP4 holds its activation pairs swapped).
-//     INT4 and asymmetric INT4 skip it where that measured faster (see table_free): a nibble q
-//     placed in the low mantissa bits of a 16-bit number whose upper bits are those of M (1024 in
-//     fp16, 128 in bf16) is exactly M + q,
-//     so one v_and_or_b32 per pair (and a shift for three of every four) turns a packed dword into
-//     four pairs; the pairs it makes join weights k and k + 4 of the dword's eight, and the
-//     activations are held in that order.  The offset comes off per chunk: sum (M + q) x minus
-//     (M + 8) sum(x) (asymmetric: (M + z) sum(x)), the lane's activation sums being fixed for the
-//     launch.
 //   * Multiply: v_dot2_f32_f16 / v_dot2_f32_bf16 of the decoded pair with the activation pair
 //     into fp32 (products of two 16-bit values are exact in fp32), then one fp32 FMA per chunk with
 //     the block scale.  NF4 with bf16 activations splits each code into two bf16 terms (8-byte
@@ -198,47 +190,16 @@ __device__ inline float scale_value(ScaleSlot<FMT> slot) {
   }
 }
 
-// Launches decoded without the LDS table (no fill, no lookups): FP4 always, through gfx950's
-// E2M1 -> 16-bit conversion (v_cvt_scalef32_pk_{f16,bf16}_fp4 with scale 1: exact, one
-// instruction per packed byte); INT4 and asymmetric INT4 in the 256-thread launches at batch 1
-// and 2, by placing nibbles into the mantissa of M + q (1.75 VALU instructions per packed byte
-// against the table's one plus one LDS read).  The 256-thread plan serves long rows of moderate
-// matrices (two rows per workgroup, e.g. the 1536 x 8960 down projection), where the 64 KiB fill
-// is paid for little work per workgroup.  Measured on MI355X: down 5.41 -> 5.23 us at B = 1
-// (asymmetric INT4 5.63 -> 5.20), 7.04 -> 6.81 us at B = 2; the 512-thread launches stream more
-// rows per fill and are bound by VALU issue (gate|up 6.59 us with the table, 7.09 without), and
-// from B = 3 the per-launch activation sums cost more than the fill (down 9.63 -> 10.26 us).
-template <int FMT, int XT, int B, int NT>
+// Launches decoded without the LDS table (no fill, no lookups): FP4, through gfx950's E2M1 ->
+// 16-bit conversion (v_cvt_scalef32_pk_{f16,bf16}_fp4 with scale 1: exact, one instruction per
+// packed byte).  INT4 and asymmetric INT4 keep the table everywhere: a table-free INT4 decode
+// (nibbles placed in the mantissa of M + q, 1.75 VALU instructions per packed byte, the offset
+// taken off per chunk through the activation sums) paid off only against the 64 KiB fill, and
+// with the 16-copy table it measured slower in every step (INT4 x bf16 at B = 1 490.5 us with the
+// table against 492.3, asymmetric INT4 503.5 against 508.1, INT4 at B = 2 610.6 against 622.7).
+template <int FMT>
 constexpr bool table_free() {
-  return FMT == kFP4 || ((FMT == kINT4 || FMT == kINT4A) && NT == 256 && B <= 2);
-}
-
-// INT4 table-free decode: the 16-bit pattern of M (1024 = 0x6400 in fp16, 128 = 0x4300 in bf16),
-// whose mantissa LSB weighs 1, so that pattern | q is exactly M + q for q < 16.
-template <int XT>
-constexpr uint32_t int4_magic() {
-  return XT == kF16 ? 0x64006400u : 0x43004300u;
-}
-template <int XT>
-constexpr float int4_magic_value() {
-  return XT == kF16 ? 1024.0f : 128.0f;
-}
-
-// The four (M + q) pairs of packed dword w (bytes B0..B3, byte j = weight 2j in the high nibble,
-// 2j + 1 in the low one).  Pair p = (w >> 4 p) & 0x000F000F | magic joins, in its low and high
-// halves: p = 0: k1, k5; p = 1: k0, k4; p = 2: k3, k7; p = 3: k2, k6.
-template <int XT, int P>
-__device__ inline uint32_t int4_pair(uint32_t w) {
-  return ((w >> (4 * P)) & 0x000F000Fu) | int4_magic<XT>();
-}
-
-// Activation pairs in that order, from the dword's activations X0 = (x0, x1), X1 = (x2, x3),
-// X2 = (x4, x5), X3 = (x6, x7) (low half first).
-__device__ inline uint4 int4_x_order(uint4 v) {
-  return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u),   // (x1, x5)
-                    __builtin_amdgcn_perm(v.z, v.x, 0x05040100u),   // (x0, x4)
-                    __builtin_amdgcn_perm(v.w, v.y, 0x07060302u),   // (x3, x7)
-                    __builtin_amdgcn_perm(v.w, v.y, 0x05040100u));  // (x2, x6)
+  return FMT == kFP4;
 }
 
 // The two FP4 weights of byte KB of packed dword w as one activation-type pair.  The conversion
@@ -256,8 +217,7 @@ __device__ inline uint32_t fp4_pair(uint32_t w) {
 template <int FMT, int XT, int B, int ITM, int NT, bool GROUPED>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
-  constexpr bool kTable = !table_free<FMT, XT, B, NT>();
-  constexpr bool kIntTf = !kTable && (FMT == kINT4 || FMT == kINT4A);  // INT4 pairs M + q
+  constexpr bool kTable = !table_free<FMT>();
   __shared__ __align__(16) uint32_t tab[kTable ? kTableBytes / 4 : 4];
   __shared__ float xwave[NT / 64][B];
 
@@ -372,8 +332,6 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
           // the hardware FP4 conversion yields (odd k, even k) pairs: swap each activation pair
           v = make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
                          __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
-        } else if constexpr (kIntTf) {
-          v = int4_x_order(v);  // the pairs the nibble decode makes: (k1, k5), (k0, k4), ...
         }
         xr[i][b][4 * q + 0] = v.x;
         xr[i][b][4 * q + 1] = v.y;
@@ -382,9 +340,9 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
       }
     }
   }
-  // (Table launches: the division after the loads above.  The table-free ones rearrange their
-  // activation pairs as they arrive; a scheduling barrier here would make those rearrangements
-  // wait for the loads before the next row block is requested, 1% slower per step.)
+  // (Table launches: the division after the loads above.  FP4 rearranges its activation pairs
+  // as they arrive; a scheduling barrier here would make those rearrangements wait for the loads
+  // before the next row block is requested, 1% slower per step.)
   if constexpr (kTable) __builtin_amdgcn_sched_barrier(0);
   count = (nrb - 1u - rb0) / grid + 1u;
   rb_last = rb0 + grid * (count - 1u);
@@ -401,10 +359,9 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
     __syncthreads();
   }
 
-  // INT4, INT4A: the sum of each chunk's 32 activations (per batch row), for the offset term
-  // -(M + 8) * s * sum(x) (asymmetric: -(M + z) * s * sum(x)) of every row this lane meets;
-  // computed once per launch.
-  constexpr bool kXsum = FMT == kINT4A || kIntTf;
+  // INT4A: the sum of each chunk's 32 activations (per batch row), for the zero-point term
+  // -(z - 8) * s * sum(x) of every row this lane meets; computed once per launch.
+  constexpr bool kXsum = FMT == kINT4A;
   float xsum[kXsum ? ITM : 1][B];
   if constexpr (kXsum && kTable) {
     // Keep the sums behind the barrier: computed before it, they made every wave wait for its
@@ -467,18 +424,10 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
           for (int kb = 0; kb < 4; ++kb) {
             const int m = 4 * j + kb;  // byte index in the chunk = activation pair index
             if constexpr (!kTable) {
-              uint32_t t;
-              if constexpr (kIntTf) {
-                t = kb == 0   ? int4_pair<XT, 0>(wv[j])
-                    : kb == 1 ? int4_pair<XT, 1>(wv[j])
-                    : kb == 2 ? int4_pair<XT, 2>(wv[j])
-                              : int4_pair<XT, 3>(wv[j]);
-              } else {
-                t = kb == 0   ? fp4_pair<XT, 0>(wv[j])
-                    : kb == 1 ? fp4_pair<XT, 1>(wv[j])
-                    : kb == 2 ? fp4_pair<XT, 2>(wv[j])
-                              : fp4_pair<XT, 3>(wv[j]);
-              }
+              const uint32_t t = kb == 0   ? fp4_pair<XT, 0>(wv[j])
+                                 : kb == 1 ? fp4_pair<XT, 1>(wv[j])
+                                 : kb == 2 ? fp4_pair<XT, 2>(wv[j])
+                                           : fp4_pair<XT, 3>(wv[j]);
 #pragma unroll
               for (int b = 0; b < B; ++b) {
                 if (XT == kF16) {
@@ -520,16 +469,10 @@ gemv_kernel(GemvArgsT<GROUPED ? kMaxGroup : 1> a) {
           }
         }
         if constexpr (FMT == kINT4A) {
-          // (q - z) s = ((M + q) - (M + z)) s without the table, ((q - 8) - (z - 8)) s with it
+          // (q - z) s = ((q - 8) - (z - 8)) s: the table gives q - 8
           const uint32_t word = __float_as_uint(sc[i]);
           const float s = __uint_as_float(word << 16);
-          const float zc = (kIntTf ? int4_magic_value<XT>() : -8.0f) + (float)((word >> 16) & 15u);
-#pragma unroll
-          for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(__builtin_fmaf(-zc, xsum[i][b], d[b]), s, acc[b]);
-        } else if constexpr (kIntTf) {
-          // (q - 8) s = ((M + q) - (M + 8)) s
-          constexpr float zc = int4_magic_value<XT>() + 8.0f;
-          const float s = scale_value<FMT>(sc[i]);
+          const float zc = -8.0f + (float)((word >> 16) & 15u);
 #pragma unroll
           for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(__builtin_fmaf(-zc, xsum[i][b], d[b]), s, acc[b]);
         } else {
