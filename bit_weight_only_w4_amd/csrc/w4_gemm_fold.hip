@@ -21,8 +21,9 @@
 // route instead: raw codes on the matrix cores, fp32 rescaling of each block's partial sums.
 //
 // Work layout.  A workgroup has 4 waves and an output tile of TN = 128 NT weight rows x TM = 128
-// activation rows; wave w owns weight rows [32 NT w, 32 NT (w + 1)) of the tile and all TM
-// activation rows, so every weight is decoded once per tile.  Matrix step: v_mfma_f32_32x32x16_f16
+// activation rows (32 for the slices below); wave w owns weight rows [32 NT w, 32 NT (w + 1)) of
+// the tile and all TM activation rows, so every weight is decoded once per tile.  Matrix step:
+// v_mfma_f32_32x32x16_f16
 // with the activations as the A operand and the weights as the B operand:
 //   * A (32 activation rows x 16 k): lane l = 32 h + c takes row c and 8 consecutive k.
 //   * B (16 k x 32 weight rows): lane l = 32 h + c takes weight row c and the same 8 k.
@@ -46,6 +47,10 @@
 //     range starts on a group): a workgroup addresses the weights, scales and activations from its
 //     range's first block on, with the matrix's row pitches, and writes fp32 partial sums to its
 //     range's plane; a second kernel adds the planes in range order (fixed-order, reproducible).
+//   * A one-pass launch whose tiles leave a sparse last round (see launch_gemm_fold) runs that
+//     round as a second launch of 32-row slices (TM = 32, four workgroups per tile): each weight
+//     of such a tile is decoded four times, but the round spreads over the whole chip, and every
+//     output's sum over K runs in the same order as in a full tile.
 #include <algorithm>
 
 #include "w4_mfma_common.h"
