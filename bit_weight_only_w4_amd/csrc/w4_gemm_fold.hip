@@ -10,12 +10,15 @@
 // accumulate x * W_hat across all blocks directly.  The rounding stays inside the accuracy bound
 // (|y - y_exact| <= 2e-3 sum_k |x w_hat| + 1e-5): code, scale and product each round to fp16
 // (at most 2^-11 relative each), so a folded NF4 weight is within 3 * 2^-11 = 1.5e-3 of W_hat,
-// an FP4 weight (exact code) within 2 * 2^-11, and an INT4 weight, (q - 8) s with a bf16 scale
-// (at most 3 + 8 significant bits), is exact.  The products with fp16 x are exact in fp32.
+// an FP4 weight (exact code) within 2 * 2^-11, an INT4 weight, (q - 8) s with a bf16 scale
+// (at most 3 + 8 significant bits), is exact, and an asymmetric INT4 weight, (q - z) s formed as
+// ((q - 8) + (8 - z)) s (the sum an exact small integer, at most 4 + 8 significant bits in the
+// product), is within 2^-11.  The products with fp16 x are exact in fp32.
 //
 // A folded weight must stay a normal, finite fp16 number: a block whose scale s satisfies
 // lo <= |s| <= hi (or s == 0) is folded, with [lo, hi] = [2^-10, 2^15] for NF4 (smallest nonzero
-// |code| 0.0796), [2^-13, 2^13] for FP4 (codes 0.5 .. 6), [2^-14, 2^12] for INT4 (|q - 8| <= 8).
+// |code| 0.0796), [2^-13, 2^13] for FP4 (codes 0.5 .. 6), [2^-14, 2^12] for INT4 (|q - 8| <= 8)
+// and asymmetric INT4 (|q - z| <= 15: at most 61440).
 // Every wave checks all block scales of its rows once, in its prologue; a wave that meets one
 // outside that range (tiny, huge, infinite or NaN scales) runs all of K through the block-scale
 // route instead: raw codes on the matrix cores, fp32 rescaling of each block's partial sums.
@@ -30,7 +33,8 @@
 //   * D (32 x 32 fp32, 16 registers): lane l = 32 h + c holds weight row c, activation rows
 //     8 (e / 4) + 4 h + e % 4 (register e).  Each lane's outputs share one weight row, so a block
 //     scale reaches them without any cross-lane broadcast.
-// K runs one 64-weight block per step (an NF4/FP4 block, half an INT4 group).  Lane (h, c) loads
+// K runs one 64-weight block per step (an NF4/FP4 block, half an INT4 group).  Asymmetric INT4
+// decodes q - 8 through INT4's table and adds 8 - z (one packed add per pair) before the scale.  Lane (h, c) loads
 // bytes [16 h, 16 h + 16) of its row's 32-byte block: weights 32 h .. 32 h + 31, of which matrix
 // step q (0 .. 3) takes 32 h + 8 q .. + 7; the A lanes read the same k positions of x.
 //   * Activations: ST stages of TM rows x 64 k in LDS (16 KiB each), copied straight from global
@@ -105,9 +109,17 @@ __device__ inline bool foldable(float s) {
   constexpr float hi = FMT == kNF4 ? 0x1p15f : FMT == kFP4 ? 0x1p13f : 0x1p12f;
   return s == 0.0f || (a >= lo && a <= hi);
 }
+// raw: the scale as stored (NF4, FP4: fp32; INT4: bf16 in the low half; asymmetric INT4: the
+// group's 32-bit word, bf16 scale low, zero point in bits 16-19).
 template <int FMT>
 __device__ inline float scale_f32(uint32_t raw) {
-  return FMT == kINT4 ? __uint_as_float(raw << 16) : __uint_as_float(raw);
+  return is_g128(FMT) ? __uint_as_float(raw << 16) : __uint_as_float(raw);
+}
+// Asymmetric INT4: 8 - z as an fp16 pair, which turns the table's q - 8 into q - z (small
+// integers: exact).
+__device__ inline uint32_t zero_shift_pair(uint32_t word) {
+  const _Float16 d = (_Float16)(8.0f - (float)((word >> 16) & 15u));
+  return __builtin_bit_cast(uint32_t, half2_t{d, d});
 }
 
 // The four weight pairs of packed dword wd (byte j: weight 2j in the high nibble, 2j + 1 in the
@@ -152,7 +164,7 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
   const int h = lane >> 5, c = lane & 31;
   const uint32_t pitch = k >> 1;  // k: the row pitch; nkb: the blocks of this K range
   constexpr uint32_t kSB = FMT == kINT4 ? 2u : 4u;
-  const uint32_t spitch = (k / (FMT == kINT4 ? 128u : 64u)) * kSB;
+  const uint32_t spitch = (k / (is_g128(FMT) ? 128u : 64u)) * kSB;
   const uint32_t laneoff = (uint32_t)c * 8u;
   f32x16 acc[NT][MT];
 #pragma unroll
@@ -182,8 +194,9 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
     for (int t = 0; t < NT; ++t) {
       const uint32_t row = (uint32_t)(32 * t + c);
       const uint4 w = buffer_load16_stream(rw, row * pitch + kb * 32u + 16u * (uint32_t)h);
-      const uint32_t raw = FMT == kINT4 ? buffer_load16bit(rs, row * spitch + (kb >> 1) * 2u)
-                                        : buffer_load32(rs, row * spitch + kb * 4u);
+      const uint32_t raw = FMT == kINT4    ? buffer_load16bit(rs, row * spitch + (kb >> 1) * 2u)
+                           : FMT == kINT4A ? buffer_load32(rs, row * spitch + (kb >> 1) * 4u)
+                                           : buffer_load32(rs, row * spitch + kb * 4u);
       const float sf = scale_f32<FMT>(raw);
       const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
       uint4 bu[4];
@@ -191,6 +204,12 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
       for (int q = 0; q < 4; ++q) {
         uint32_t pr[4];
         decode4<FMT>(wd[q], tabc, laneoff, pr);
+        if constexpr (FMT == kINT4A) {
+          const half2_t zz = __builtin_bit_cast(half2_t, zero_shift_pair(raw));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pr[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pr[e]) + zz);
+        }
         bu[q] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
       }
 #pragma unroll
@@ -264,8 +283,9 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   const uint32_t k = a.k, kb_lo = blockIdx.y * a.bps, nkb = min(a.bps, k / 64u - kb_lo);
   const uint32_t pitch = k >> 1;
   constexpr uint32_t kSB = FMT == kINT4 ? 2u : 4u;
-  const uint32_t spitch = (k / (FMT == kINT4 ? 128u : 64u)) * kSB;
-  const uint32_t soff = FMT == kINT4 ? kb_lo : kb_lo * 4u;  // scale bytes before block kb_lo
+  const uint32_t spitch = (k / (is_g128(FMT) ? 128u : 64u)) * kSB;
+  // scale bytes before block kb_lo (an even block for the formats with 128-weight groups)
+  const uint32_t soff = FMT == kINT4 ? kb_lo : FMT == kINT4A ? kb_lo * 2u : kb_lo * 4u;
   const uint32_t wrow0 = tn * TN + (uint32_t)wave * 32u * NT;
   const uint32_t wbase = wrow0 < mm.n ? wrow0 : 0u;
   const uint32_t wrows = wrow0 < mm.n ? min(32u * NT, mm.n - wrow0) : 0u;
@@ -305,6 +325,11 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
         const uint32_t off = offset_or_oob(have, row * spitch + q * 4u);  // 2-byte aligned
         const uint32_t g0 = buffer_load16bit(rs, off) << 16, g1 = buffer_load16bit(rs, off + 2u) << 16;
         sq[t] = make_uint4(g0, g0, g1, g1);
+      } else if constexpr (FMT == kINT4A) {
+        // the two groups' words, kept whole (scale and zero point)
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(
+            rs, (int)offset_or_oob(have, row * spitch + q * 8u), 0, 0);
+        sq[t] = make_uint4(v.x, v.x, v.y, v.y);
       } else {
         sq[t] = buffer_load16(rs, offset_or_oob(have, row * spitch + q * 16u));
       }
@@ -355,16 +380,21 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
     uint4 bw[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const _Float16 sh = (_Float16)__uint_as_float(s[t]);
+      // s[t]: fp32 bits (NF4, FP4, INT4), the group's word (asymmetric INT4)
+      const _Float16 sh = (_Float16)(FMT == kINT4A ? scale_f32<FMT>(s[t]) : __uint_as_float(s[t]));
       const half2_t s2 = {sh, sh};
+      const half2_t zz = __builtin_bit_cast(half2_t, FMT == kINT4A ? zero_shift_pair(s[t]) : 0u);
       const uint32_t wd[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t p[4];
         decode4<FMT>(wd[q], tabc, laneoff, p);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          p[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p[e]) * s2);
+        for (int e = 0; e < 4; ++e) {
+          half2_t v = __builtin_bit_cast(half2_t, p[e]);
+          if constexpr (FMT == kINT4A) v = v + zz;  // q - z, exact
+          p[e] = __builtin_bit_cast(uint32_t, v * s2);
+        }
         bw[t][q] = make_uint4(p[0], p[1], p[2], p[3]);
       }
     }
@@ -386,13 +416,13 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   // before the first block.
   bool fold = true;
   {
-    const uint32_t nsc = FMT == kINT4 ? nkb / 2u : nkb;
+    const uint32_t nsc = is_g128(FMT) ? nkb / 2u : nkb;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const uint32_t row = (uint32_t)(32 * t + c);
       for (uint32_t i = (uint32_t)h; i < nsc; i += 2u) {
         const uint32_t raw = FMT == kINT4 ? buffer_load16bit(rs, row * spitch + i * 2u)
-                                          : buffer_load32(rs, row * spitch + i * 4u);
+                                          : buffer_load32(rs, row * spitch + i * 4u);  // INT4A: word
         fold = fold && foldable<FMT>(scale_f32<FMT>(raw));
       }
     }
@@ -450,8 +480,9 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
 template <int FMT, int NT, int MT, bool GROUPED>
 hipError_t launch_nt(const FoldArgs& a, int ranges, hipStream_t s) {
   // Two activation stages and four blocks of weights in flight (eight blocks per unrolled trip,
-  // two quads of scales): measured on MI355X against three stages and three blocks.
-  constexpr int ST = 2, DP = 4;
+  // two quads of scales): measured on MI355X against three stages and three blocks.  Asymmetric
+  // INT4 with 128-row tiles keeps two (its zero-point pairs would otherwise spill).
+  constexpr int ST = 2, DP = FMT == kINT4A && NT == 1 ? 2 : 4;
   hipLaunchKernelGGL((fold_kernel<FMT, NT, MT, ST, DP, GROUPED>), dim3(a.tiles, ranges),
                      dim3(kFoldThreads), 0, s, a);
   return hipGetLastError();
@@ -491,13 +522,14 @@ int gemm_fold_ranges(int fmt, int64_t k, int splits, int64_t* bps) {
   const int64_t nb = k / 64;
   const int64_t sp = std::max<int64_t>(1, std::min<int64_t>(splits, nb));
   int64_t per = (nb + sp - 1) / sp;
-  if (fmt == W4_INT4_X_F16) per += per & 1;
+  if (fmt == W4_INT4_X_F16 || fmt == W4_INT4A_X_F16) per += per & 1;
   if (bps) *bps = per;
   return (int)((nb + per - 1) / per);
 }
 
 bool gemm_fold_format(int fmt) {
-  return fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16 || fmt == W4_FP4_X_F16;
+  return fmt == W4_NF4_X_F16 || fmt == W4_INT4_X_F16 || fmt == W4_FP4_X_F16 ||
+         fmt == W4_INT4A_X_F16;
 }
 
 // Weight rows per tile of the folded kernel for an unsplit launch (256 or 128), or 0 when the
@@ -552,7 +584,7 @@ hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_
                             float* ws) {
   if (!gemm_fold_format(fmt) || groups < 1 || groups > kMaxGroup || m < 1 || k < 64 || k % 64 != 0)
     return hipErrorInvalidValue;
-  if (fmt == W4_INT4_X_F16 && k % 128 != 0) return hipErrorInvalidValue;
+  if ((fmt == W4_INT4_X_F16 || fmt == W4_INT4A_X_F16) && k % 128 != 0) return hipErrorInvalidValue;
   if (tile_rows != 128 && tile_rows != 256) return hipErrorInvalidValue;
   int64_t n_total = 0;
   for (int g = 0; g < groups; ++g) {
@@ -597,6 +629,7 @@ hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_
     switch (fmt) {
       case W4_NF4_X_F16: return launch_fmt<kNF4>(a, nt, ranges, base, count, thin, s);
       case W4_INT4_X_F16: return launch_fmt<kINT4>(a, nt, ranges, base, count, thin, s);
+      case W4_INT4A_X_F16: return launch_fmt<kINT4A>(a, nt, ranges, base, count, thin, s);
       case W4_FP4_X_F16: return launch_fmt<kFP4>(a, nt, ranges, base, count, thin, s);
     }
     return hipErrorInvalidValue;

@@ -113,7 +113,8 @@ typedef enum {
                           reduction; W4_PATH_AUTO, given a workspace, splits K into the smallest
                           power of two of ranges that gives three quarters of the CUs a 64-row
                           tile, each range at least 16 blocks, at most 16 ranges.  For fp16
-                          activations (W4_NF4_X_F16, W4_INT4_X_F16, W4_FP4_X_F16) from 256
+                          activations (W4_NF4_X_F16, W4_INT4_X_F16, W4_FP4_X_F16,
+                          W4_INT4A_X_F16) from 256
                           activation rows the folded kernel of W4_PATH_TILED_F16 runs instead: a
                           one-pass launch with enough tiles, and every split launch, with that
                           kernel's split rule for W4_PATH_AUTO (see there)                      */
@@ -123,13 +124,15 @@ typedef enum {
                           weight rows x 128 activation rows, 32x32x16 matrix steps; any B; no
                           workspace in one pass (split_k <= 1), else K in ranges of whole
                           64-weight blocks (128-row tiles; an even number of blocks per range
-                          for INT4), partial sums in the workspace, the fixed-order reduction.
-                          W4_NF4_X_F16, W4_INT4_X_F16 and
-                          W4_FP4_X_F16 only (other formats: W4_ERR_PATH).  A folded weight is
-                          within 3 * 2^-11 of W_hat (NF4; FP4 2 * 2^-11; INT4 exact); a wave whose
+                          for INT4 and asymmetric INT4), partial sums in the workspace, the
+                          fixed-order reduction.  W4_NF4_X_F16, W4_INT4_X_F16, W4_FP4_X_F16 and
+                          W4_INT4A_X_F16 only (other formats: W4_ERR_PATH).  A folded weight is
+                          within 3 * 2^-11 of W_hat (NF4; FP4 2 * 2^-11; asymmetric INT4 2^-11;
+                          INT4 exact); a wave whose
                           rows hold a block scale outside the range where every folded weight is a
                           normal, finite fp16 number (NF4 [2^-10, 2^15], FP4 [2^-13, 2^13], INT4
-                          [2^-14, 2^12], or zero) runs all of K with the scale applied in fp32 per
+                          and asymmetric INT4 [2^-14, 2^12], or zero) runs all of K with the
+                          scale applied in fp32 per
                           block instead.  W4_PATH_AUTO and W4_PATH_TILED take it for those
                           formats from 256 activation rows: in one pass with 256-row tiles when
                           those number at least two per CU (one per CU for K >= 4096), else with

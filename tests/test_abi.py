@@ -215,13 +215,13 @@ def test_tiled_split_rule():
 
 
 def test_tiled_split_rule_folded():
-    """NF4, INT4 and FP4 with fp16 activations from 256 rows (the folded-scale kernel, 128-row
+    """NF4, INT4, FP4 and asymmetric INT4 with fp16 activations from 256 rows (the folded-scale kernel, 128-row
     tiles, T tiles): below one tile per CU with rows of 4096+ weights, S = min(16, 256 / T,
     K / 64 / 12) when that is 2 or more; from one to two tiles per CU with rows of 16384+ weights,
     S = 2; otherwise one pass (and shorter rows keep the MFMA path under 4096 matrix rows)."""
     w4, _ = _lib()
     big = 1 << 30
-    for fmt in ("nf4_f16", "int4_f16", "fp4_f16"):
+    for fmt in ("nf4_f16", "int4_f16", "fp4_f16", "int4a_f16"):
         assert w4.auto_path(fmt, 1536, 8960, 512, big) == ("tiled", 5)  # 48 tiles
         assert w4.auto_path(fmt, 1536, 8960, 256, big) == ("tiled", 10)  # 24 tiles
         assert w4.auto_path(fmt, 1024, 8192, 512, big) == ("tiled", 8)  # 32 tiles
@@ -392,13 +392,14 @@ def test_sparse24_grouped_validation_codes():
 
 
 def test_tiled_f16_host_checks():
-    """W4_PATH_TILED_F16 runs fp16 activations with NF4, INT4 or FP4 weights: other formats fail
-    with W4_ERR_PATH before any launch; unsplit it asks for no workspace; split over K it needs one
-    fp32 plane per K range (W4_ERR_WORKSPACE without one, W4_ERR_PATH past W4_MAX_SPLIT_K), with
-    ceil(K/64 / S) blocks per range, an even count for INT4 (fewer ranges where that rounds up)."""
+    """W4_PATH_TILED_F16 runs fp16 activations with NF4, INT4, FP4 or asymmetric INT4 weights:
+    bf16 activations fail with W4_ERR_PATH before any launch; unsplit it asks for no workspace;
+    split over K it needs one fp32 plane per K range (W4_ERR_WORKSPACE without one, W4_ERR_PATH past
+    W4_MAX_SPLIT_K), with ceil(K/64 / S) blocks per range, an even count for the formats with
+    128-weight groups (fewer ranges where that rounds up)."""
     w4, L = _lib()
     vp = ctypes.c_void_p
-    for fmt in (2, 4, 6, 7, 8):
+    for fmt in (2, 4, 6, 8):
         assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), fmt, 64, 256, 200, vp(FAKE * 64),
                               6, 0, None, 0, None) == -7
     assert L.w4_matmul_ex(vp(FAKE), vp(FAKE * 2), vp(FAKE * 3), 1, 64, 256, 200, vp(FAKE * 64), 6, 2,
@@ -411,6 +412,7 @@ def test_tiled_f16_host_checks():
     # 140 blocks, S = 11: 13 blocks per range (11 ranges); INT4 rounds to 14 (10 ranges)
     assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512, "tiled_f16", 11) == 11 * 512 * 1536 * 4
     assert w4.workspace_bytes("int4_f16", 1536, 8960, 512, "tiled_f16", 11) == 10 * 512 * 1536 * 4
+    assert w4.workspace_bytes("int4a_f16", 1536, 8960, 512, "tiled_f16", 11) == 10 * 512 * 1536 * 4
     assert w4.workspace_bytes("nf4_bf16", 1536, 8960, 512, "tiled_f16", 4) == 0
 
 

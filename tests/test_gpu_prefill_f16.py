@@ -10,7 +10,7 @@ from tests import gpu_util as g
 
 pytestmark = pytest.mark.gpu
 
-F16_FMTS = ["nf4_f16", "int4_f16", "fp4_f16"]
+F16_FMTS = ["nf4_f16", "int4_f16", "fp4_f16", "int4a_f16"]
 
 
 def _case(fmt, n, k, b, seed, w=None):
@@ -72,7 +72,8 @@ def test_tiled_f16_scale_range(fmt):
 def test_tiled_f16_one_hot_columns(fmt, b):
     """Activation row i = e_{c_i}: y[i] is column c_i of the decoded matrix up to the fp16
     rounding of the folded weight: exact for INT4 ((q - 8) s with a bf16 scale fits fp16), within
-    2 * 2^-11 for FP4 (scale and product rounded), 3 * 2^-11 for NF4 (code, scale and product)."""
+    2^-11 for asymmetric INT4 ((q - z) s rounded once), 2 * 2^-11 for FP4 (scale and product
+    rounded), 3 * 2^-11 for NF4 (code, scale and product)."""
     import oracle
 
     import bit_weight_only_w4_amd as w4
@@ -89,7 +90,7 @@ def test_tiled_f16_one_hot_columns(fmt, b):
     y = w4.matmul_ex(g.to_dev_x(x, "f16"), p, s, fmt, path="tiled_f16").cpu().numpy()
     y = y.astype(np.float64)
     rtol = {"nf4_f16": 3 * 2.0 ** -11 + 2.0 ** -20, "fp4_f16": 2 * 2.0 ** -11 + 2.0 ** -20,
-            "int4_f16": 0.0}[fmt]
+            "int4_f16": 0.0, "int4a_f16": 2.0 ** -11 + 2.0 ** -20}[fmt]
     for i, c in enumerate(cols):
         assert np.allclose(y[i], w_hat[:, c], rtol=rtol, atol=0), (i, c)
 
@@ -158,13 +159,12 @@ def test_tiled_f16_grouped_members(fmt):
 
 
 def test_tiled_f16_rejects_other_formats():
-    """Formats with bf16 activations (and asymmetric INT4) have no folded kernel: W4_ERR_PATH, y
-    untouched."""
+    """Formats with bf16 activations have no folded kernel: W4_ERR_PATH, y untouched."""
     import torch
 
     import bit_weight_only_w4_amd as w4
 
-    for fmt in ("nf4_bf16", "int4_bf16", "fp4_bf16", "int4a_f16", "int4a_bf16"):
+    for fmt in ("nf4_bf16", "int4_bf16", "fp4_bf16", "int4a_bf16"):
         x, xd, p, s, pr, sr = _case(fmt, 64, 256, 128, seed=3)
         y = torch.full((128, 64), 7.0, device=xd.device)
         with pytest.raises(ValueError):
@@ -296,3 +296,31 @@ def test_tiled_f16_last_round_slices(fmt, ns, b):
             assert torch.equal(y, alone)
         else:
             assert torch.equal(y, w4.matmul_ex(xd, p, s, fmt, path="tiled"))
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_tiled_f16_int4a_zero_points(splits):
+    """Asymmetric INT4 with zero points at the ends of the grid: rows of one sign only (zero
+    point 0 or 15, so the zero-point term carries most of each weight) next to ordinary rows,
+    folded as ((q - 8) + (8 - z)) s; every element within the bound, in one pass and over K
+    ranges."""
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    fmt = "int4a_f16"
+    n, k, b = 384, 2048, 300
+    w = synth_inputs.weights(n, k, seed=77).astype(np.float64)
+    rows = np.arange(n)
+    w[rows % 3 == 1] = np.abs(w[rows % 3 == 1]) + 0.01
+    w[rows % 3 == 2] = -np.abs(w[rows % 3 == 2]) - 0.01
+    w = w.astype(np.float32)
+    x, xd, p, s, pr, sr = _case(fmt, n, k, b, seed=78, w=w)
+    z = (sr >> 16) & 15
+    assert (z[rows % 3 == 1] <= 1).all() and (z[rows % 3 == 2] >= 14).all()
+    ws = None
+    if splits > 1:
+        ws = torch.empty(w4.workspace_bytes(fmt, n, k, b, "tiled_f16", splits), dtype=torch.uint8,
+                         device=xd.device)
+    y = w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", split_k=splits, workspace=ws)
+    g.assert_y_close(fmt, y, x, pr, sr)
