@@ -217,7 +217,7 @@ bool gemm_fold_format(int fmt);
 int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m);
 int gemm_fold_ranges(int fmt, int64_t k, int splits, int64_t* bps);
 int gemm_fold_auto_splits(int fmt, int64_t n, int64_t k, int64_t m);
-bool gemm_fold_split(int fmt, int groups, int64_t m);
+bool gemm_fold_split(int fmt, int groups, const int64_t* ns, int64_t m);
 hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,
                             const void* const* scales, const int64_t* ns, float* const* y,
                             int64_t k, int64_t m, int tile_rows, hipStream_t s, int splits = 1,

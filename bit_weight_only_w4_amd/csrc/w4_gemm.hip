@@ -466,12 +466,12 @@ hipError_t launch_gemm_members(int fmt, const uint16_t* x, int groups, const uin
   if (ranges > 1 && (groups > 1 || !ws)) return hipErrorInvalidValue;
   if (ranges > 1 && m * ns[0] >= ((int64_t)1 << 32)) return hipErrorNotSupported;  // 32-bit planes
   // fp16 activations: the folded-scale kernel in one pass where its tiles fill the CUs, and over
-  // K ranges (128-row tiles) from 256 activation rows
+  // K ranges (128-row tiles) where its split rule takes it
   if (ranges == 1) {
     const int fold_rows = gemm_fold_tile_rows(fmt, ns, groups, k, m);
     if (fold_rows > 0)
       return launch_gemm_fold(fmt, x, groups, packed, scales, ns, y, k, m, fold_rows, s);
-  } else if (gemm_fold_split(fmt, groups, m)) {
+  } else if (gemm_fold_split(fmt, groups, ns, m)) {
     return launch_gemm_fold(fmt, x, groups, packed, scales, ns, y, k, m, 128, s, splits, ws);
   }
   const int64_t cus = device_cu_count();

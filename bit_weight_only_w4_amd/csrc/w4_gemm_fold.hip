@@ -538,44 +538,58 @@ bool gemm_fold_format(int fmt) {
 // two per CU (one per CU for rows of 4096+ weights): NF4 151936 x 1536 334 against 426 us (INT4 x
 // fp16 315), 28672 x 8192 289 against 402; else 128-row tiles from one per CU: 8960 x 1536 35
 // against 45 us, 8192 x 8192 106 against 129, 8192 x 28672 363 against 423 (the two gate/up
-// matrices of a grouped launch: the same as the block-scale kernel's 64 x 128 tiles).  Below 256
-// activation rows the two kernels tie (151936 x 1536 at 128 rows: 123.5 against 124 us) and the
-// block-scale one keeps them.
+// matrices of a grouped launch: the same as the block-scale kernel's 64 x 128 tiles).  From 128
+// activation rows: at 192 rows 151936 x 1536 181 against 208 us, 28672 x 8192 172 against 221,
+// 8960 x 1536 22.2 against 31.0; at 128 rows 151936 x 1536 115 against 127 (128-row tiles), while
+// 8960 x 1536 (70 tiles) stays with the block-scale kernel (22.5 against 17.3).  With one
+// 128-row activation tile (M <= 128) the 256-row tiles lose (151936 x 1536 at 128 rows 127 us
+// against 115 with 128-row tiles); from two, 128-row tiles already win at half a tile per CU
+// (8960 x 1536 at 192 rows, 140 tiles: 22.2 us against the block-scale kernel's 31.0).
 int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m) {
-  if (!gemm_fold_format(fmt) || m < 256 || k < 64 || k % 64 != 0) return 0;
+  if (!gemm_fold_format(fmt) || m < 128 || k < 64 || k % 64 != 0) return 0;
   const int64_t cus = device_cu_count();
-  if (fold_tiles(ns, groups, m, 256) >= (k >= 4096 ? cus : 2 * cus)) return 256;
-  if (fold_tiles(ns, groups, m, 128) >= cus) return 128;
+  if (m > 128 && fold_tiles(ns, groups, m, 256) >= (k >= 4096 ? cus : 2 * cus)) return 256;
+  const int64_t t128 = fold_tiles(ns, groups, m, 128);
+  if (t128 >= cus || (m > 128 && 2 * t128 >= cus)) return 128;
   return 0;
 }
 
 // K ranges the automatic tiled path gives the folded kernel (128-row tiles) on one matrix, 1 for
-// none, or 0 where the kernel does not apply.  With T tiles below one per CU and rows of 4096+
-// weights: S = min(16, CUs / T, K / 64 / 12) ranges (at least 12 blocks each) when that is 2 or
-// more, about one workgroup per CU; from one to two tiles per CU with rows of 16384+ weights: two
-// ranges (two workgroups per CU).  Measured on MI355X (NF4 x fp16, rotated weights; INT4 within 5%): 1536 x
+// none, or 0 where the kernel does not apply (below 256 activation rows, fewer than 32 tiles:
+// the block-scale kernel's split is faster there).  With T tiles below one per CU and rows of
+// 4096+ weights: S = min(16, CUs / T, K / 64 / 12) ranges (at least 12 blocks each), at least 2
+// from half a tile per CU, when that is 2 or more: about one or two workgroups per CU; from one
+// to two tiles per CU with rows of 16384+ weights: two ranges (two workgroups per CU).  Measured on MI355X (NF4 x fp16, rotated weights; INT4 within 5%): 1536 x
 // 8960 at 512 activation rows (48 tiles) 120 us unsplit, 67.8 / 50.1 / 41.6 / 36.7 / 40.3 / 39.8 /
 // 36.9 at S = 2 / 3 / 4 / 5 / 6 / 8 / 10 (the block-scale kernel's split: 44.4); at 256 rows (24
 // tiles) 38.6 / 32.7 / 26.9 / 24.3 / 28.2 at S = 4 / 5 / 8 / 10 / 16 (27.4); 1024 x 8192 at 512
 // (32 tiles) 34.7 / 28.1 / 26.1 / 29.3 at S = 4 / 6 / 8 / 10 (25.5); 8192 x 28672 at 512 (256
 // tiles) 363 / 339 / 354 at S = 1 / 2 / 3; 8192 x 8192 at 512 106 / 105 at S = 1 / 2 (not
 // split); 1536 x 1536 at 512 (24 blocks) 18.5 at best, against the MFMA path's 12.4 (not split).
+// At 128 activation rows: 28672 x 8192 (224 tiles) 112 us over two ranges against 119 unsplit and
+// the block-scale kernel's 127; 8192 x 28672 (64 tiles) 118 / 112 over four / eight against 131;
+// 8192 x 8192 (64) 42.0 over four against 42.5; 1536 x 8960 (12 tiles) 25.7 over eight against the
+// block-scale kernel's 21.4 (hence its share below 32 tiles).
 int gemm_fold_auto_splits(int fmt, int64_t n, int64_t k, int64_t m) {
-  if (!gemm_fold_format(fmt) || m < 256 || k < 64 || k % 64 != 0) return 0;
+  if (!gemm_fold_format(fmt) || m < 128 || k < 64 || k % 64 != 0) return 0;
   const int64_t cus = device_cu_count();
   const int64_t nb = k / 64;
   const int64_t tiles = fold_tiles(&n, 1, m, 128);
+  if (m < 256 && tiles < 32) return 0;
   if (tiles < cus) {
     if (nb < 64) return 1;
-    const int64_t s = std::min<int64_t>(std::min<int64_t>(16, cus / tiles), nb / 12);
+    int64_t s = std::min<int64_t>(std::min<int64_t>(16, cus / tiles), nb / 12);
+    if (2 * tiles >= cus) s = std::max<int64_t>(s, std::min<int64_t>(2, nb / 12));
     return s >= 2 ? (int)s : 1;
   }
   return tiles < 2 * cus && nb >= 256 ? 2 : 1;
 }
 
-// Split tiled launches (one member) of the formats and sizes the folded kernel runs: it does.
-bool gemm_fold_split(int fmt, int groups, int64_t m) {
-  return gemm_fold_format(fmt) && groups == 1 && m >= 256;
+// Split tiled launches (one member) of the formats and sizes the folded kernel runs: from 256
+// activation rows, and from 128 with at least 32 tiles of 128 rows (the split rule above).
+bool gemm_fold_split(int fmt, int groups, const int64_t* ns, int64_t m) {
+  return gemm_fold_format(fmt) && groups == 1 &&
+         (m >= 256 || (m >= 128 && fold_tiles(ns, 1, m, 128) >= 32));
 }
 
 hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_t* const* packed,

@@ -114,10 +114,10 @@ typedef enum {
                           power of two of ranges that gives three quarters of the CUs a 64-row
                           tile, each range at least 16 blocks, at most 16 ranges.  For fp16
                           activations (W4_NF4_X_F16, W4_INT4_X_F16, W4_FP4_X_F16,
-                          W4_INT4A_X_F16) from 256
-                          activation rows the folded kernel of W4_PATH_TILED_F16 runs instead: a
-                          one-pass launch with enough tiles, and every split launch, with that
-                          kernel's split rule for W4_PATH_AUTO (see there)                      */
+                          W4_INT4A_X_F16) from 128
+                          activation rows the folded kernel of W4_PATH_TILED_F16 runs instead
+                          where its rules take it (see there), with that kernel's split rule for
+                          W4_PATH_AUTO                                                          */
   W4_PATH_TILED_F16 = 6 /* prefill-size GEMM for fp16 activations with each block scale folded into
                           the decoded fp16 weights (one packed multiply per weight pair), so the
                           matrix cores accumulate x * W_hat over all of K: tiles of 256 or 128
@@ -134,13 +134,16 @@ typedef enum {
                           and asymmetric INT4 [2^-14, 2^12], or zero) runs all of K with the
                           scale applied in fp32 per
                           block instead.  W4_PATH_AUTO and W4_PATH_TILED take it for those
-                          formats from 256 activation rows: in one pass with 256-row tiles when
-                          those number at least two per CU (one per CU for K >= 4096), else with
-                          128-row tiles when those number at least one per CU; split launches
-                          always.  W4_PATH_AUTO with a workspace splits K for it when its T
-                          128-row tiles number under one per CU and K >= 4096, into
-                          min(16, CUs / T, K / 64 / 12) ranges if that is at least 2, and into
-                          two ranges when 1 <= T / CUs < 2 and K >= 16384                       */
+                          formats from 128 activation rows: in one pass with 256-row tiles when
+                          B > 128 and those number at least two per CU (one per CU for
+                          K >= 4096), else with 128-row tiles when those number at least one per
+                          CU (half a tile per CU when B > 128); split launches from 256 rows,
+                          and from 128 with at least 32 tiles of 128 rows.  W4_PATH_AUTO with a
+                          workspace splits K for it when its T 128-row tiles number under one
+                          per CU and K >= 4096 (below 256 rows: T >= 32), into
+                          min(16, CUs / T, K / 64 / 12) ranges (at least 2 when T >= CUs / 2) if
+                          that is at least 2, and into two ranges when 1 <= T / CUs < 2 and
+                          K >= 16384                                                            */
 } w4_path_t;
 
 #define W4_MAX_BATCH 4096

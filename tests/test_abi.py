@@ -198,7 +198,7 @@ def test_tiled_split_rule():
     assert w4.auto_path("nf4_f16", 1536, 8960, 128, big) == ("tiled", 8)  # 140 / 16 >= 8
     assert w4.auto_path("int4_bf16", 1024, 8192, 512, big) == ("tiled", 4)
     assert w4.auto_path("int4_bf16", 1024, 8192, 128, big) == ("tiled", 8)  # 128 / 16 < 16
-    assert w4.auto_path("nf4_f16", 8192, 8192, 128, big) == ("tiled", 2)
+    assert w4.auto_path("nf4_bf16", 8192, 8192, 128, big) == ("tiled", 2)
     assert w4.auto_path("nf4_bf16", 8192, 8192, 512, big) == ("tiled", 1)  # 512 tiles
     assert w4.auto_path("nf4_f16", 8960, 1536, 128, big) == ("tiled", 1)  # 24 blocks: no split
     assert w4.auto_path("nf4_bf16", 1536, 1536, 512, big) == ("mfma", 1)
@@ -218,7 +218,9 @@ def test_tiled_split_rule_folded():
     """NF4, INT4, FP4 and asymmetric INT4 with fp16 activations from 256 rows (the folded-scale kernel, 128-row
     tiles, T tiles): below one tile per CU with rows of 4096+ weights, S = min(16, 256 / T,
     K / 64 / 12) when that is 2 or more; from one to two tiles per CU with rows of 16384+ weights,
-    S = 2; otherwise one pass (and shorter rows keep the MFMA path under 4096 matrix rows)."""
+    S = 2; otherwise one pass (and shorter rows keep the MFMA path under 4096 matrix rows).  From
+    128 rows: below 256 only with at least 32 tiles, and at least 2 ranges from half a tile per
+    CU."""
     w4, _ = _lib()
     big = 1 << 30
     for fmt in ("nf4_f16", "int4_f16", "fp4_f16", "int4a_f16"):
@@ -232,6 +234,12 @@ def test_tiled_split_rule_folded():
         assert w4.auto_path(fmt, 16384, 28672, 512, big) == ("tiled", 1)  # 512 tiles
         assert w4.auto_path(fmt, 1536, 1536, 512, big) == ("mfma", 1)  # 24 blocks: no split
         assert w4.auto_path(fmt, 1536, 2048, 512, big) == ("mfma", 1)  # 32 blocks: no split
+        # from 128 rows; below 256 only with at least 32 tiles (else the block-scale rule)
+        assert w4.auto_path(fmt, 8192, 8192, 128, big) == ("tiled", 4)  # 64 tiles
+        assert w4.auto_path(fmt, 28672, 8192, 128, big) == ("tiled", 2)  # 224 tiles: half per CU
+        assert w4.auto_path(fmt, 8192, 28672, 192, big) == ("tiled", 2)  # 128 tiles, 448 blocks
+        assert w4.auto_path(fmt, 1536, 8960, 128, big) == ("tiled", 8)  # 12 tiles: block-scale rule
+        assert w4.auto_path(fmt, 151936, 1536, 128, big) == ("tiled", 1)
     assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512) == 5 * 512 * 1536 * 4
     assert w4.workspace_bytes("int4_f16", 1536, 8960, 256) == 10 * 256 * 1536 * 4
     assert w4.workspace_bytes("fp4_f16", 8192, 28672, 512) == 2 * 512 * 8192 * 4

@@ -219,8 +219,12 @@ def test_grouped_at_prefill_batch(fmt):
 def test_grouped_tiled_members(fmt):
     """Several members of W4_TILED_FROM_ROWS rows and more share one tiled launch (their tiles one
     after another, ragged row counts, an MFMA member beside them): every member against the oracle,
-    bitwise equal to w4_gemm_prefill on it (both launches take the same tile plan here: 64 x 128
-    tiles, two K groups), and repeatable bitwise; y pre-filled with NaN."""
+    bitwise equal to the same kernel on that member alone, and repeatable bitwise; y pre-filled
+    with NaN.  bf16 activations: the block-scale kernel, as w4_gemm_prefill runs it on one member
+    (64 x 128 tiles, two K groups both times).  fp16 activations: the launch's 210 tiles of 128
+    rows at 160 activation rows take the folded kernel (from half a tile per CU), a member alone
+    too few, so the reference is the folded kernel forced on the member (128-row tiles both
+    times)."""
     import torch
 
     import bit_weight_only_w4_amd as w4
@@ -241,7 +245,11 @@ def test_grouped_tiled_members(fmt):
     for i, (y, (pr, sr)) in enumerate(zip(ys, refs)):
         g.assert_y_close(fmt, y, x, pr, sr)
         if ns[i] >= w4.TILED_FROM_ROWS:
-            assert torch.equal(y, w4.gemm_prefill(xd, packed[i], scales[i], fmt))
+            if fmt.endswith("_f16"):
+                alone = w4.matmul_ex(xd, packed[i], scales[i], fmt, path="tiled_f16")
+            else:
+                alone = w4.gemm_prefill(xd, packed[i], scales[i], fmt)
+            assert torch.equal(y, alone)
     again = w4.gemm_smallbatch_grouped(xd, packed, scales, fmt)
     for y, y2 in zip(ys, again):
         assert torch.equal(y, y2)
