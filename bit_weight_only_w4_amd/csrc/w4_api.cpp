@@ -235,8 +235,9 @@ int auto_mfma_splits(int64_t n, int64_t k, int64_t b) {
 }
 
 // Split count of the automatic tiled GEMM (used when the caller's workspace holds the partial
-// sums).  NF4, INT4 and FP4 with fp16 activations from 256 rows run the folded-scale kernel, whose
-// own rule gives S (gemm_fold_auto_splits).  Otherwise the smallest power of two S for which ceil(N / 64) * ceil(B / 128) * S, the workgroups
+// sums).  Where the folded-scale kernel's own rule applies (fp16 activations with NF4, INT4, FP4
+// or asymmetric INT4 weights from 128 rows, gemm_fold_auto_splits), it gives S.  Otherwise the
+// smallest power of two S for which ceil(N / 64) * ceil(B / 128) * S, the workgroups
 // of 64-row tiles over all K ranges, reaches three quarters of the CUs, with at least 16 blocks
 // of 64 weights per range and at most 16 ranges.  Measured on MI355X (NF4 x fp16, rotated weights,
 // S = 1..16 at B = 128, 256, 512): the rule's S is the best or within 10% of it on 1536 x 8960

@@ -215,12 +215,12 @@ def test_tiled_split_rule():
 
 
 def test_tiled_split_rule_folded():
-    """NF4, INT4, FP4 and asymmetric INT4 with fp16 activations from 256 rows (the folded-scale kernel, 128-row
+    """NF4, INT4, FP4 and asymmetric INT4 with fp16 activations (the folded-scale kernel, 128-row
     tiles, T tiles): below one tile per CU with rows of 4096+ weights, S = min(16, 256 / T,
-    K / 64 / 12) when that is 2 or more; from one to two tiles per CU with rows of 16384+ weights,
-    S = 2; otherwise one pass (and shorter rows keep the MFMA path under 4096 matrix rows).  From
-    128 rows: below 256 only with at least 32 tiles, and at least 2 ranges from half a tile per
-    CU."""
+    K / 64 / 12), at least 2 from half a tile per CU, when that is 2 or more; from one to two
+    tiles per CU with rows of 16384+ weights, S = 2; otherwise one pass (and shorter rows keep the
+    MFMA path under 4096 matrix rows).  From 256 activation rows, and from 128 with at least 32
+    tiles (fewer: the block-scale kernel's rule)."""
     w4, _ = _lib()
     big = 1 << 30
     for fmt in ("nf4_f16", "int4_f16", "fp4_f16", "int4a_f16"):
