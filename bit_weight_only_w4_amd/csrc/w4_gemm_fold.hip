@@ -543,23 +543,30 @@ bool gemm_fold_format(int fmt) {
 // 8960 x 1536 22.2 against 31.0; at 128 rows 151936 x 1536 115 against 127 (128-row tiles), while
 // 8960 x 1536 (70 tiles) stays with the block-scale kernel (22.5 against 17.3).  With one
 // 128-row activation tile (M <= 128) the 256-row tiles lose (151936 x 1536 at 128 rows 127 us
-// against 115 with 128-row tiles); from two, 128-row tiles already win at half a tile per CU
-// (8960 x 1536 at 192 rows, 140 tiles: 22.2 us against the block-scale kernel's 31.0).
+// against 115 with 128-row tiles); from two, 128-row tiles already win at half a tile per CU on
+// rows shorter than 4096 weights (8960 x 1536 at 192 rows, 140 tiles: 22.2 us against the
+// block-scale kernel's 31.0), not on longer ones, whose few workgroups then carry hundreds of
+// blocks each (8192 x 8192 at 192 rows, 128 tiles: 95 against 62.5; 8192 x 28672 352 against
+// 207: split over K, the folded kernel wins again).
 int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m) {
   if (!gemm_fold_format(fmt) || m < 128 || k < 64 || k % 64 != 0) return 0;
   const int64_t cus = device_cu_count();
   if (m > 128 && fold_tiles(ns, groups, m, 256) >= (k >= 4096 ? cus : 2 * cus)) return 256;
   const int64_t t128 = fold_tiles(ns, groups, m, 128);
-  if (t128 >= cus || (m > 128 && 2 * t128 >= cus)) return 128;
+  if (t128 >= cus || (m > 128 && k < 4096 && 2 * t128 >= cus)) return 128;
   return 0;
 }
 
 // K ranges the automatic tiled path gives the folded kernel (128-row tiles) on one matrix, 1 for
 // none, or 0 where the kernel does not apply (below 256 activation rows, fewer than 32 tiles:
 // the block-scale kernel's split is faster there).  With T tiles below one per CU and rows of
-// 4096+ weights: S = min(16, CUs / T, K / 64 / 12) ranges (at least 12 blocks each), at least 2
-// from half a tile per CU, when that is 2 or more: about one or two workgroups per CU; from one
-// to two tiles per CU with rows of 16384+ weights: two ranges (two workgroups per CU).  Measured on MI355X (NF4 x fp16, rotated weights; INT4 within 5%): 1536 x
+// 4096+ weights: S = min(16, 2 CUs / T) (about two workgroups per CU) when that leaves 32+ blocks
+// per range, else S = min(16, CUs / T, K / 64 / 12) (at least 12 blocks each), at least 2 from
+// half a tile per CU, when that is 2 or more; from one to two tiles per CU with rows of 16384+
+// weights: two ranges (two workgroups per CU).  Long rows gain from the second workgroup per CU
+// (8192 x 8192 at 192 rows: 57.5 us over four ranges against 61.9 over two; 8192 x 28672 at 128
+// rows 112 over eight against 118 over four, at 192 rows 183 over four against 194 over two),
+// short ones do not (1536 x 8960 at 512 rows over ten ranges 36.9 against 36.7 over five).  Measured on MI355X (NF4 x fp16, rotated weights; INT4 within 5%): 1536 x
 // 8960 at 512 activation rows (48 tiles) 120 us unsplit, 67.8 / 50.1 / 41.6 / 36.7 / 40.3 / 39.8 /
 // 36.9 at S = 2 / 3 / 4 / 5 / 6 / 8 / 10 (the block-scale kernel's split: 44.4); at 256 rows (24
 // tiles) 38.6 / 32.7 / 26.9 / 24.3 / 28.2 at S = 4 / 5 / 8 / 10 / 16 (27.4); 1024 x 8192 at 512
@@ -578,6 +585,9 @@ int gemm_fold_auto_splits(int fmt, int64_t n, int64_t k, int64_t m) {
   if (m < 256 && tiles < 32) return 0;
   if (tiles < cus) {
     if (nb < 64) return 1;
+    // about two workgroups per CU while the ranges keep 32+ blocks, else about one
+    const int64_t s2 = std::min<int64_t>(16, 2 * cus / tiles);
+    if (s2 >= 2 && nb / s2 >= 32) return (int)s2;
     int64_t s = std::min<int64_t>(std::min<int64_t>(16, cus / tiles), nb / 12);
     if (2 * tiles >= cus) s = std::max<int64_t>(s, std::min<int64_t>(2, nb / 12));
     return s >= 2 ? (int)s : 1;

@@ -137,13 +137,14 @@ typedef enum {
                           formats from 128 activation rows: in one pass with 256-row tiles when
                           B > 128 and those number at least two per CU (one per CU for
                           K >= 4096), else with 128-row tiles when those number at least one per
-                          CU (half a tile per CU when B > 128); split launches from 256 rows,
-                          and from 128 with at least 32 tiles of 128 rows.  W4_PATH_AUTO with a
-                          workspace splits K for it when its T 128-row tiles number under one
-                          per CU and K >= 4096 (below 256 rows: T >= 32), into
-                          min(16, CUs / T, K / 64 / 12) ranges (at least 2 when T >= CUs / 2) if
-                          that is at least 2, and into two ranges when 1 <= T / CUs < 2 and
-                          K >= 16384                                                            */
+                          CU (half a tile per CU when B > 128 and K < 4096); split launches from
+                          256 rows, and from 128 with at least 32 tiles of 128 rows.
+                          W4_PATH_AUTO with a workspace splits K for it when its T 128-row tiles
+                          number under one per CU and K >= 4096 (below 256 rows: T >= 32): into
+                          min(16, 2 CUs / T) ranges when each keeps at least 32 blocks of 64
+                          weights, else min(16, CUs / T, K / 64 / 12) (at least 2 when
+                          T >= CUs / 2) if that is at least 2; and into two ranges when
+                          1 <= T / CUs < 2 and K >= 16384                                       */
 } w4_path_t;
 
 #define W4_MAX_BATCH 4096

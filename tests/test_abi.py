@@ -216,8 +216,9 @@ def test_tiled_split_rule():
 
 def test_tiled_split_rule_folded():
     """NF4, INT4, FP4 and asymmetric INT4 with fp16 activations (the folded-scale kernel, 128-row
-    tiles, T tiles): below one tile per CU with rows of 4096+ weights, S = min(16, 256 / T,
-    K / 64 / 12), at least 2 from half a tile per CU, when that is 2 or more; from one to two
+    tiles, T tiles): below one tile per CU with rows of 4096+ weights, S = min(16, 512 / T) when
+    that leaves 32+ blocks per range, else S = min(16, 256 / T, K / 64 / 12), at least 2 from half
+    a tile per CU, when that is 2 or more; from one to two
     tiles per CU with rows of 16384+ weights, S = 2; otherwise one pass (and shorter rows keep the
     MFMA path under 4096 matrix rows).  From 256 activation rows, and from 128 with at least 32
     tiles (fewer: the block-scale kernel's rule)."""
@@ -237,7 +238,9 @@ def test_tiled_split_rule_folded():
         # from 128 rows; below 256 only with at least 32 tiles (else the block-scale rule)
         assert w4.auto_path(fmt, 8192, 8192, 128, big) == ("tiled", 4)  # 64 tiles
         assert w4.auto_path(fmt, 28672, 8192, 128, big) == ("tiled", 2)  # 224 tiles: half per CU
-        assert w4.auto_path(fmt, 8192, 28672, 192, big) == ("tiled", 2)  # 128 tiles, 448 blocks
+        assert w4.auto_path(fmt, 8192, 28672, 192, big) == ("tiled", 4)  # 128 tiles: 2 per CU
+        assert w4.auto_path(fmt, 8192, 28672, 128, big) == ("tiled", 8)  # 64 tiles, 56 blocks each
+        assert w4.auto_path(fmt, 8192, 8192, 192, big) == ("tiled", 4)  # 32 blocks per range
         assert w4.auto_path(fmt, 1536, 8960, 128, big) == ("tiled", 8)  # 12 tiles: block-scale rule
         assert w4.auto_path(fmt, 151936, 1536, 128, big) == ("tiled", 1)
     assert w4.workspace_bytes("nf4_f16", 1536, 8960, 512) == 5 * 512 * 1536 * 4
