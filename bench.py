@@ -59,6 +59,11 @@ def parse_args():
                          "q|k|v and gate|up each in one grouped launch; dag: 197 launches with "
                          "q|k|v and gate|up as graph branches")
     ap.add_argument("--report", default=None, help="write a detailed JSON report here")
+    ap.add_argument("--prefill-rows", default="512",
+                    help="--suite prefill: activation-row counts of the per-shape table (comma list; "
+                         "the step itself is always the 512-token prompt)")
+    ap.add_argument("--prefill-steps", type=int, default=1,
+                    help="--suite prefill: 0 skips the step timings (per-shape table only)")
     ap.add_argument("--counters-from", nargs="+", metavar="PMC_DIR", default=None,
                     help="CPU only: turn rocprofv3 --pmc runs of --suite counters into per-path "
                          "instruction counts (profiles/counters_paths.json), then exit")
@@ -531,7 +536,10 @@ def graph_time(launchers, dev, reps):
         for f in launchers:
             f(s0.cuda_stream)
     torch.cuda.synchronize()
-    ms = time_replays(g, reps, 2)
+    # Replay for about 20 ms before timing, so that the first shape of a table is not timed while
+    # the clocks still ramp up from an idle device.
+    warm = time_replays(g, 1, 1)
+    ms = time_replays(g, reps, max(2, int(20.0 / max(warm, 1e-3))))
     del g
     return ms * 1e3 / len(launchers)
 
@@ -952,7 +960,7 @@ def prefill_suite(args, dev):
 
     b = PREFILL_TOKENS
     out = {"tokens": b, "steps": [], "shapes": []}
-    for fmt in PREFILL_FMTS:
+    for fmt in (PREFILL_FMTS if args.prefill_steps else ()):
         step = Step(fmt, b, "auto", dev)
         flops = sum(2.0 * n * k * b for _, n, k in step.shapes)
         r = {"format": fmt, "tokens": b, "flop_per_step": flops,
@@ -973,7 +981,8 @@ def prefill_suite(args, dev):
     shapes = [("q/o", 1536, 1536), ("k/v", 256, 1536), ("gate/up", 8960, 1536), ("down", 1536, 8960),
               ("lm_head", 151936, 1536)] + [(f"L.{nm}", n, k) for nm, n, k in synth_inputs.LARGE_SHAPES
                                              if nm != "up"]
-    for fmt in ("nf4_f16", "int4_bf16"):
+    rows_list = [int(v) for v in str(args.prefill_rows).split(",") if v]
+    for fmt, b in [(f, r) for r in rows_list for f in ("nf4_f16", "int4_bf16")]:
         for name, n, k in shapes:
             ap, sk = w4.auto_path(fmt, n, k, b, w4.workspace_bytes(fmt, n, k, b))
             row = {"format": fmt, "shape": name, "n": n, "k": k, "b": b, "auto_path": ap,
