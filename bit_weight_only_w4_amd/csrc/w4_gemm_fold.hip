@@ -89,6 +89,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kFoldThreads = 256;
 constexpr int kFoldMT = 4;  // 32-row activation tiles per wave in a full tile: TM = 128
+constexpr int kWideMT = 6;  // the 192-row tile, for 129 to 192 activation rows
 
 __device__ inline f32x16 mfma32(const uint4& a, const uint4& b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
@@ -245,7 +246,9 @@ __device__ __attribute__((noinline)) void fold_block_scale_wave(
 template <int FMT, int NT, int MT, int ST, int DP, bool GROUPED>
 __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   constexpr int TN = 4 * 32 * NT, TM = 32 * MT;
-  constexpr uint32_t SUBS = kFoldMT / MT;  // slices of TM activation rows per 128-row tile
+  // activation rows of the tile grid: 128 (whole tiles or slices of them), or 192 in one tile
+  constexpr int FULL = MT > kFoldMT ? MT : kFoldMT;
+  constexpr uint32_t SUBS = FULL / MT;  // slices of TM activation rows per tile of the grid
   constexpr int SLOTS = TM * 8;  // 16-byte slots of one stage (64 k per row)
   // the byte -> pair table (not used by FP4, which converts in registers)
   __shared__ __align__(16) uint32_t tab[FMT == kFP4 ? 4 : kTableBytes / 4];
@@ -275,7 +278,7 @@ __global__ void __launch_bounds__(kFoldThreads, 2) fold_kernel(FoldArgs a) {
   }
   const uint32_t lt = tile - mm.tile0;
   const uint32_t tn = lt / a.mt, tm = lt - tn * a.mt;
-  const uint32_t m0 = tm * (32u * kFoldMT) + sub * TM;
+  const uint32_t m0 = tm * (32u * FULL) + sub * TM;
   if (m0 >= a.m) return;  // a slice past the last activation row: the whole workgroup, no barrier
   // This workgroup's K range, blocks [kb_lo, kb_lo + nkb): weights, scales and activations are
   // addressed from block kb_lo on (block kb below is block kb_lo + kb of the row); k stays the
@@ -498,12 +501,15 @@ hipError_t launch_mt(const FoldArgs& a, int nt, int ranges, hipStream_t s) {
 }
 
 // Full 128-row tiles [tile_base, tile_base + count), or (thin) the same tiles as four 32-row
-// slices each.
+// slices each, or (wide: 128-weight-row tiles only) 192-row tiles.
 template <int FMT>
 hipError_t launch_fmt(FoldArgs a, int nt, int ranges, int64_t tile_base, int64_t count, bool thin,
-                      hipStream_t s) {
+                      bool wide, hipStream_t s) {
   a.tile_base = (uint32_t)tile_base;
   a.tiles = (uint32_t)(thin ? count * kFoldMT : count);
+  if (wide)
+    return a.groups > 1 ? launch_nt<FMT, 1, kWideMT, true>(a, ranges, s)
+                        : launch_nt<FMT, 1, kWideMT, false>(a, ranges, s);
   return thin ? launch_mt<FMT, 1>(a, nt, ranges, s) : launch_mt<FMT, kFoldMT>(a, nt, ranges, s);
 }
 
@@ -551,6 +557,10 @@ bool gemm_fold_format(int fmt) {
 int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m) {
   if (!gemm_fold_format(fmt) || m < 128 || k < 64 || k % 64 != 0) return 0;
   const int64_t cus = device_cu_count();
+  // 129 to 192 rows: 192-row tiles over 128 weight rows wherever they give every CU one
+  if (m > 128 && m <= 32 * kWideMT && 32 * kWideMT * k * 2 < ((int64_t)1 << 31) &&
+      fold_tiles(ns, groups, 1, 128) >= cus)
+    return 128;
   if (m > 128 && fold_tiles(ns, groups, m, 256) >= (k >= 4096 ? cus : 2 * cus)) return 256;
   const int64_t t128 = fold_tiles(ns, groups, m, 128);
   if (t128 >= cus || (m > 128 && k < 4096 && 2 * t128 >= cus)) return 128;
@@ -622,8 +632,14 @@ hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_
   const int ranges = gemm_fold_ranges(fmt, k, splits, &bps);
   if (ranges > 1 && (groups > 1 || !ws)) return hipErrorInvalidValue;
   if (ranges > 1 && m * ns[0] >= ((int64_t)1 << 32)) return hipErrorNotSupported;  // 32-bit planes
-  const int64_t mt = (m + 32 * kFoldMT - 1) / (32 * kFoldMT);
-  const int64_t tiles = fold_tiles(ns, groups, m, tile_rows);
+  // 129 to 192 activation rows in one 192-row tile instead of two 128-row ones (the second a
+  // half padding), for unsplit 128-weight-row tiles that still give every CU one tile: each
+  // weight is then decoded once, and a quarter fewer matrix steps run.
+  const int64_t cus = device_cu_count();
+  const bool wide = ranges == 1 && tile_rows == 128 && m > 128 && m <= 32 * kWideMT &&
+                    32 * kWideMT * k * 2 < ((int64_t)1 << 31) && fold_tiles(ns, groups, 1, 128) >= cus;
+  const int64_t mt = wide ? 1 : (m + 32 * kFoldMT - 1) / (32 * kFoldMT);
+  const int64_t tiles = wide ? fold_tiles(ns, groups, 1, 128) : fold_tiles(ns, groups, m, tile_rows);
   if (tiles >= ((int64_t)1 << 31)) return hipErrorNotSupported;
   FoldArgs a;
   int64_t tile0 = 0;
@@ -647,14 +663,14 @@ hipError_t launch_gemm_fold(int fmt, const uint16_t* x, int groups, const uint8_
   // Two workgroups per CU hold 2 * CUs tiles at once.  One pass whose tiles leave a last round of
   // at most CUs / 4 tiles (whole rounds before it) runs that round as a second launch of 32-row
   // slices, four per tile, spread over the CUs: the sums over K take the same order either way.
-  const int64_t slots = 2 * device_cu_count(), rem = tiles % slots;
-  const int64_t tail = ranges == 1 && tiles > slots && 4 * rem <= slots / 2 ? rem : 0;
+  const int64_t slots = 2 * cus, rem = tiles % slots;
+  const int64_t tail = !wide && ranges == 1 && tiles > slots && 4 * rem <= slots / 2 ? rem : 0;
   auto run = [&](int64_t base, int64_t count, bool thin) {
     switch (fmt) {
-      case W4_NF4_X_F16: return launch_fmt<kNF4>(a, nt, ranges, base, count, thin, s);
-      case W4_INT4_X_F16: return launch_fmt<kINT4>(a, nt, ranges, base, count, thin, s);
-      case W4_INT4A_X_F16: return launch_fmt<kINT4A>(a, nt, ranges, base, count, thin, s);
-      case W4_FP4_X_F16: return launch_fmt<kFP4>(a, nt, ranges, base, count, thin, s);
+      case W4_NF4_X_F16: return launch_fmt<kNF4>(a, nt, ranges, base, count, thin, wide, s);
+      case W4_INT4_X_F16: return launch_fmt<kINT4>(a, nt, ranges, base, count, thin, wide, s);
+      case W4_INT4A_X_F16: return launch_fmt<kINT4A>(a, nt, ranges, base, count, thin, wide, s);
+      case W4_FP4_X_F16: return launch_fmt<kFP4>(a, nt, ranges, base, count, thin, wide, s);
     }
     return hipErrorInvalidValue;
   };

@@ -134,7 +134,9 @@ typedef enum {
                           and asymmetric INT4 [2^-14, 2^12], or zero) runs all of K with the
                           scale applied in fp32 per
                           block instead.  W4_PATH_AUTO and W4_PATH_TILED take it for those
-                          formats from 128 activation rows: in one pass with 256-row tiles when
+                          formats from 128 activation rows: in one pass over 128 weight rows
+                          by 192 activation rows per tile when 128 < B <= 192 and the matrix
+                          has at least 128 weight rows per CU; else with 256-row tiles when
                           B > 128 and those number at least two per CU (one per CU for
                           K >= 4096), else with 128-row tiles when those number at least one per
                           CU (half a tile per CU when B > 128 and K < 4096); split launches from

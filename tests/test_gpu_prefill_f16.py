@@ -324,3 +324,32 @@ def test_tiled_f16_int4a_zero_points(splits):
                          device=xd.device)
     y = w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", split_k=splits, workspace=ws)
     g.assert_y_close(fmt, y, x, pr, sr)
+
+
+# 129 to 192 activation rows over at least one 128-weight-row tile per CU run as one 192-row tile
+# per weight tile (33000 rows: 258 tiles): ragged B inside the tile, every output written (y
+# pre-filled with NaN), sampled rows within the bound, and the rows bitwise equal to the same rows
+# computed as 128 + (b - 128) rows in two calls (128-row tiles; the sums over K take the same
+# order in either tile), and to the automatic path.
+@pytest.mark.parametrize("fmt", F16_FMTS)
+@pytest.mark.parametrize("b", [129, 160, 192])
+def test_tiled_f16_192_row_tiles(fmt, b):
+    import torch
+
+    import bit_weight_only_w4_amd as w4
+
+    n, k = 33000, 640
+    dev = g.device()
+    packed, scales, checks = _tail_case(fmt, (n,), k, b, seed=700 + b)
+    p, s, (rows, pr, sr) = packed[0], scales[0], checks[0]
+    x = synth_inputs.activations(b, k, "f16", seed=b + 11)
+    xd = g.to_dev_x(x, "f16")
+    y = torch.full((b, n), float("nan"), device=dev)
+    w4.matmul_ex(xd, p, s, fmt, path="tiled_f16", y=y)
+    assert bool(torch.isfinite(y).all())
+    g.assert_y_close(fmt, y[:, torch.as_tensor(rows, device=dev)], x, pr, sr)
+    top = w4.matmul_ex(xd[:128].contiguous(), p, s, fmt, path="tiled_f16")
+    rest = w4.matmul_ex(xd[128:].contiguous(), p, s, fmt, path="tiled_f16")
+    assert torch.equal(y[:128], top)
+    assert torch.equal(y[128:], rest)
+    assert torch.equal(y, w4.gemm_prefill(xd, p, s, fmt))
