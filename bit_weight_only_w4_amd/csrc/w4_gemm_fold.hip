@@ -553,7 +553,10 @@ bool gemm_fold_format(int fmt) {
 // rows shorter than 4096 weights (8960 x 1536 at 192 rows, 140 tiles: 22.2 us against the
 // block-scale kernel's 31.0), not on longer ones, whose few workgroups then carry hundreds of
 // blocks each (8192 x 8192 at 192 rows, 128 tiles: 95 against 62.5; 8192 x 28672 352 against
-// 207: split over K, the folded kernel wins again).
+// 207: split over K, the folded kernel wins again).  From 129 to 192 rows a matrix with at least
+// one 128-weight-row tile per CU takes 128-row tiles, which the launch runs as 192-row activation
+// tiles: ahead of the 256-row ones (192 rows: 151936 x 1536 131 us against 169, 128256 x 8192
+// 524 against 720).
 int gemm_fold_tile_rows(int fmt, const int64_t* ns, int groups, int64_t k, int64_t m) {
   if (!gemm_fold_format(fmt) || m < 128 || k < 64 || k % 64 != 0) return 0;
   const int64_t cus = device_cu_count();
